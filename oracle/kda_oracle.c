@@ -1,0 +1,336 @@
+/*
+ * Plain CPU oracle for the Kimi Delta Attention (KDA) forward.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link or
+ * call this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline use it.  It shares no code with the HIP library.
+ *
+ * Everything is computed token by token, in fp64, after an exact upcast of the
+ * fp32 (or bf16-valued) inputs.  No chunking, no blocking, no fusion.
+ *
+ * Sources (the pages give the interface; the recurrence is the KDA definition):
+ *  - call contract of chunk_kda (q, k, v, gate, beta, a_log, dt_bias, scale,
+ *    lower_bound, initial_state, output_final_state, in-kernel q/k L2 norm,
+ *    in-kernel gate, in-kernel beta sigmoid): hyper_parallel coverage page for
+ *    context_parallel/kimi_delta_attention.py, `_run_local_kda` and the
+ *    `chunk_kda` call inside `_eager_kda_state_p2p`;
+ *  - tensor shapes q,k [B,T,H,K], v [B,T,HV,V], gate [B,T,HV,K], beta [B,T,HV],
+ *    a_log HV values, dt_bias HV*K values: same page, `_validate_projected_inputs`;
+ *  - fp32 recurrent state of shape (B, HV, K, V): same page,
+ *    `_RecvKDAInitialState.forward` and the state_shape built in
+ *    `_eager_kda_state_p2p`;
+ *  - affine state summary (state_ext, transition) and its application to an
+ *    optional initial state: same page, `_eager_kda_state_p2p`
+ *    (torch_kda_state_summary / torch_apply_kda_state_summary);
+ *  - document resets through cu_seqlens: NeMo AutoModel page
+ *    "nemo_automodel.components.models.kimi_k3.cp", module introduction and
+ *    `doc_ids_from_cu_seqlens` / `segment_cu_seqlens`;
+ *  - two gate activations (unbounded and lower-bounded): torchtitan PR #4025
+ *    "[kimi k3] add eager reference model with FSDP2", the follow-up commit
+ *    note on chunk_kda with the gate activation fused into the kernel.
+ *
+ * Definition (per sequence n and head h, state S of shape K x V, row = key
+ * channel, column = value channel):
+ *     q^ = q / sqrt(sum q^2 + 1e-6),  k^ likewise
+ *     g_c = -exp(a_log[h]) * softplus(gate_c + dt_bias[h,c])          (no bound)
+ *     g_c = lb * sigmoid(exp(a_log[h]) * (gate_c + dt_bias[h,c]))     (bound lb<0)
+ *     beta = sigmoid(beta_logit)
+ *     S_t  = (I - beta k^ k^T) Diag(exp g) S_{t-1} + beta k^ v^T
+ *     o_t  = scale * S_t^T q^
+ * The gate formula is not printed on the pages; the two forms above are the
+ * reading this oracle takes.  A third, alternative reading of the bound (a hard
+ * clamp max(lb, -exp(a_log) softplus(.))) is available as gate mode 2.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_EPS 1e-6
+
+enum { GATE_SOFTPLUS = 0, GATE_SIGMOID_BOUND = 1, GATE_CLAMP_BOUND = 2 };
+
+static double softplus(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+/* L2 normalisation of one head vector (in-kernel q/k norm). */
+static void l2norm(const float* x, int n, double* out) {
+  double ss = 0.0;
+  for (int i = 0; i < n; ++i) ss += (double)x[i] * (double)x[i];
+  double r = 1.0 / sqrt(ss + ORACLE_EPS);
+  for (int i = 0; i < n; ++i) out[i] = (double)x[i] * r;
+}
+
+/* Per-key-channel log-decay built from the raw gate logits (in-kernel gate). */
+static void gate_row(const float* gate, const float* dt_bias_h, double a_log_h, int K, int mode,
+                     double lb, double* g) {
+  double A = exp(a_log_h);
+  for (int c = 0; c < K; ++c) {
+    double x = (double)gate[c] + (double)dt_bias_h[c];
+    if (mode == GATE_SOFTPLUS) {
+      g[c] = -A * softplus(x);
+    } else if (mode == GATE_SIGMOID_BOUND) {
+      g[c] = lb * sigmoid(A * x);
+    } else {
+      g[c] = fmax(lb, -A * softplus(x));
+    }
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Public: prologue only (q^, k^, g, beta) for every token and head.         */
+/* ------------------------------------------------------------------------ */
+int oracle_prologue(int B, int T, int H, int K, const float* q, const float* k, const float* gate,
+                    const float* beta, const float* a_log, const float* dt_bias, int gate_mode,
+                    double lower_bound, double* qn, double* kn, double* g, double* b) {
+  if (B < 0 || T < 0 || H <= 0 || K <= 0) return 1;
+  for (long bt = 0; bt < (long)B * T; ++bt) {
+    for (int h = 0; h < H; ++h) {
+      long th = bt * H + h;
+      l2norm(q + th * K, K, qn + th * K);
+      l2norm(k + th * K, K, kn + th * K);
+      gate_row(gate + th * K, dt_bias + (long)h * K, (double)a_log[h], K, gate_mode, lower_bound,
+               g + th * K);
+      b[th] = sigmoid((double)beta[th]);
+    }
+  }
+  return 0;
+}
+
+/* One token of the recurrence on state S (K x V, row-major). */
+static void recur_step(double* S, int K, int V, const double* qn, const double* kn, const double* g,
+                       double bt, const float* v, double scale, double* u, double* o_out) {
+  /* S <- Diag(exp g) S */
+  for (int c = 0; c < K; ++c) {
+    double d = exp(g[c]);
+    double* row = S + (long)c * V;
+    for (int j = 0; j < V; ++j) row[j] *= d;
+  }
+  /* u = S^T k^  (the value the state currently predicts for k^) */
+  for (int j = 0; j < V; ++j) u[j] = 0.0;
+  for (int c = 0; c < K; ++c) {
+    const double* row = S + (long)c * V;
+    for (int j = 0; j < V; ++j) u[j] += row[j] * kn[c];
+  }
+  /* S <- S + beta k^ (v - u)^T, which equals (I - beta k^ k^T) S + beta k^ v^T */
+  for (int c = 0; c < K; ++c) {
+    double* row = S + (long)c * V;
+    double bk = bt * kn[c];
+    for (int j = 0; j < V; ++j) row[j] += bk * ((double)v[j] - u[j]);
+  }
+  /* o = scale * S^T q^ */
+  if (o_out) {
+    for (int j = 0; j < V; ++j) o_out[j] = 0.0;
+    for (int c = 0; c < K; ++c) {
+      const double* row = S + (long)c * V;
+      for (int j = 0; j < V; ++j) o_out[j] += row[j] * qn[c];
+    }
+    for (int j = 0; j < V; ++j) o_out[j] *= scale;
+  }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Threaded driver over independent (sequence, head) pairs.                 */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  int B, T, H, K, V;
+  const float *q, *k, *v, *gate, *beta, *a_log, *dt_bias;
+  /* pre-normalised inputs (recurrence-only entry); NULL when raw is used */
+  const double *qn, *kn, *g, *bb;
+  int gate_mode;
+  double lb, scale;
+  int N;
+  const int32_t* cu;
+  const float* init;
+  double* o;
+  double* fin;
+  double* trans; /* summary mode: transition [N,H,K,K] */
+  int summary;
+  int next; /* work counter */
+  pthread_mutex_t mu;
+} job_t;
+
+static int take(job_t* J) {
+  pthread_mutex_lock(&J->mu);
+  int w = J->next++;
+  pthread_mutex_unlock(&J->mu);
+  return w;
+}
+
+static void seq_range(const job_t* J, int n, long* row, long* t0, long* t1) {
+  if (J->cu) {
+    *row = 0;
+    *t0 = J->cu[n];
+    *t1 = J->cu[n + 1];
+  } else {
+    *row = n;
+    *t0 = 0;
+    *t1 = J->T;
+  }
+}
+
+static void* worker(void* arg) {
+  job_t* J = (job_t*)arg;
+  int K = J->K, V = J->V, H = J->H;
+  double* S = (double*)malloc(sizeof(double) * (size_t)K * V);
+  double* P = J->summary ? (double*)malloc(sizeof(double) * (size_t)K * K) : NULL;
+  double* u = (double*)malloc(sizeof(double) * (size_t)(K > V ? K : V));
+  double* qn = (double*)malloc(sizeof(double) * K);
+  double* kn = (double*)malloc(sizeof(double) * K);
+  double* g = (double*)malloc(sizeof(double) * K);
+  float* zeros = (float*)calloc((size_t)(K > V ? K : V), sizeof(float));
+  for (;;) {
+    int w = take(J);
+    if (w >= J->N * H) break;
+    int n = w / H, h = w % H;
+    long row, t0, t1;
+    seq_range(J, n, &row, &t0, &t1);
+    long sidx = ((long)n * H + h) * (long)K * V;
+    for (long i = 0; i < (long)K * V; ++i) S[i] = J->init ? (double)J->init[sidx + i] : 0.0;
+    if (P) {
+      for (int i = 0; i < K; ++i)
+        for (int j = 0; j < K; ++j) P[(long)i * K + j] = (i == j) ? 1.0 : 0.0;
+    }
+    for (long t = t0; t < t1; ++t) {
+      long th = ((row * J->T) + t) * H + h;
+      const double *pq, *pk, *pg;
+      double bt;
+      if (J->qn) {
+        pq = J->qn + th * K;
+        pk = J->kn + th * K;
+        pg = J->g + th * K;
+        bt = J->bb[th];
+      } else {
+        l2norm(J->q + th * K, K, qn);
+        l2norm(J->k + th * K, K, kn);
+        gate_row(J->gate + th * K, J->dt_bias + (long)h * K, (double)J->a_log[h], K, J->gate_mode,
+                 J->lb, g);
+        bt = sigmoid((double)J->beta[th]);
+        pq = qn;
+        pk = kn;
+        pg = g;
+      }
+      recur_step(S, K, V, pq, pk, pg, bt, J->v + th * V, J->scale, u,
+                 J->o ? J->o + th * V : NULL);
+      if (P) /* the same factor applied to the transition, with zero values */
+        recur_step(P, K, K, pq, pk, pg, bt, zeros, 0.0, u, NULL);
+    }
+    if (J->fin)
+      for (long i = 0; i < (long)K * V; ++i) J->fin[sidx + i] = S[i];
+    if (P) {
+      long pidx = ((long)n * H + h) * (long)K * K;
+      memcpy(J->trans + pidx, P, sizeof(double) * (size_t)K * K);
+    }
+  }
+  free(S);
+  free(P);
+  free(u);
+  free(qn);
+  free(kn);
+  free(g);
+  free(zeros);
+  return NULL;
+}
+
+static int run_job(job_t* J, int threads) {
+  if (threads < 1) threads = 1;
+  if (threads > 256) threads = 256;
+  pthread_mutex_init(&J->mu, NULL);
+  J->next = 0;
+  pthread_t tid[256];
+  int started = 0;
+  for (int i = 1; i < threads; ++i)
+    if (pthread_create(&tid[started], NULL, worker, J) == 0) ++started;
+  worker(J);
+  for (int i = 0; i < started; ++i) pthread_join(tid[i], NULL);
+  pthread_mutex_destroy(&J->mu);
+  return 0;
+}
+
+static int check_cu(int B, int T, int N, const int32_t* cu) {
+  if (!cu) return N == B ? 0 : 2;
+  if (B != 1 || cu[0] != 0 || cu[N] != T) return 2;
+  for (int n = 0; n < N; ++n)
+    if (cu[n + 1] < cu[n]) return 2;
+  return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Public: full forward from raw inputs.                                     */
+/*   o [B,T,H,V] (may be NULL), final_state [N,H,K,V] (may be NULL).         */
+/* ------------------------------------------------------------------------ */
+int oracle_kda_fwd(int B, int T, int H, int K, int V, const float* q, const float* k,
+                   const float* v, const float* gate, const float* beta, const float* a_log,
+                   const float* dt_bias, double scale, int gate_mode, double lower_bound, int N,
+                   const int32_t* cu_seqlens, const float* initial_state, double* o,
+                   double* final_state, int threads) {
+  if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return 1;
+  if (check_cu(B, T, N, cu_seqlens)) return 2;
+  job_t J;
+  memset(&J, 0, sizeof(J));
+  J.B = B; J.T = T; J.H = H; J.K = K; J.V = V;
+  J.q = q; J.k = k; J.v = v; J.gate = gate; J.beta = beta; J.a_log = a_log; J.dt_bias = dt_bias;
+  J.gate_mode = gate_mode; J.lb = lower_bound; J.scale = scale;
+  J.N = N; J.cu = cu_seqlens; J.init = initial_state; J.o = o; J.fin = final_state;
+  return run_job(&J, threads);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Public: recurrence only, from already normalised q^, k^, log-decay g and  */
+/* beta (all [B,T,H,*] fp64).  v and initial_state are fp32 as above.        */
+/* ------------------------------------------------------------------------ */
+int oracle_recurrence(int B, int T, int H, int K, int V, const double* qn, const double* kn,
+                      const float* v, const double* g, const double* b, double scale, int N,
+                      const int32_t* cu_seqlens, const float* initial_state, double* o,
+                      double* final_state, int threads) {
+  if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return 1;
+  if (check_cu(B, T, N, cu_seqlens)) return 2;
+  job_t J;
+  memset(&J, 0, sizeof(J));
+  J.B = B; J.T = T; J.H = H; J.K = K; J.V = V;
+  J.qn = qn; J.kn = kn; J.g = g; J.bb = b; J.v = v; J.scale = scale;
+  J.N = N; J.cu = cu_seqlens; J.init = initial_state; J.o = o; J.fin = final_state;
+  return run_job(&J, threads);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Public: affine state summary of each row (no document resets).           */
+/*   state_ext  [B,H,K,V] = final state of the row started from zero        */
+/*   transition [B,H,K,K] = ordered product of the per-token factors        */
+/*                          (I - beta k^ k^T) Diag(exp g), later on the left */
+/* so that final_state = transition . initial_state + state_ext.            */
+/* ------------------------------------------------------------------------ */
+int oracle_state_summary(int B, int T, int H, int K, int V, const float* q, const float* k,
+                         const float* v, const float* gate, const float* beta, const float* a_log,
+                         const float* dt_bias, int gate_mode, double lower_bound,
+                         double* state_ext, double* transition, int threads) {
+  if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return 1;
+  job_t J;
+  memset(&J, 0, sizeof(J));
+  J.B = B; J.T = T; J.H = H; J.K = K; J.V = V;
+  J.q = q; J.k = k; J.v = v; J.gate = gate; J.beta = beta; J.a_log = a_log; J.dt_bias = dt_bias;
+  J.gate_mode = gate_mode; J.lb = lower_bound; J.scale = 1.0;
+  J.N = B; J.fin = state_ext; J.trans = transition; J.summary = 1;
+  return run_job(&J, threads);
+}
+
+/* Public: final = transition . initial + state_ext (initial may be NULL). */
+int oracle_apply_state_summary(int B, int H, int K, int V, const double* state_ext,
+                               const double* transition, const double* initial_state,
+                               double* final_state) {
+  for (long bh = 0; bh < (long)B * H; ++bh) {
+    const double* E = state_ext + bh * K * V;
+    const double* P = transition + bh * K * K;
+    const double* S0 = initial_state ? initial_state + bh * K * V : NULL;
+    double* F = final_state + bh * K * V;
+    for (int i = 0; i < K; ++i)
+      for (int j = 0; j < V; ++j) {
+        double acc = E[(long)i * V + j];
+        if (S0)
+          for (int c = 0; c < K; ++c) acc += P[(long)i * K + c] * S0[(long)c * V + j];
+        F[(long)i * V + j] = acc;
+      }
+  }
+  return 0;
+}
