@@ -1,0 +1,238 @@
+#!/usr/bin/env python3
+"""Benchmark of the KDA chunked forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload 3]
+
+One step is one kda_fwd over the whole batch of the throughput workload
+(B=4 rows x T=16384 tokens, H=32 heads, dk=dv=128, bf16 inputs, fp32 state,
+chunk 64, one document per row, no lower bound), with every input already
+resident in HBM.  W untimed steps, then exactly K timed steps between two
+device synchronisations; rank 0 prints one JSON line.
+
+Besides the throughput it reports
+  * "roofline": the dominant kernel's algorithmic bytes per launch divided by
+    its average duration, timed live with HIP events recorded by the library
+    around each stage on the kernel's own stream (kda_fwd_profiled);
+  * "cpu_baseline": the CPU oracle, as it stands, timed on this host on a
+    bounded sample of the same workload (a few heads of one row).
+Only one GPU is used: --gpus above 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from gated_delta_rule_43_amd import kda, synthetic  # noqa: E402
+
+METRIC = "KDA chunked fwd Mtokens/s at H=32,dk=dv=128 bf16; MFMA util % of peak"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+
+
+def _hip():
+    """The HIP runtime torch already loaded (same soname as libkda.so's)."""
+    try:
+        return ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+    except OSError:
+        return ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
+
+
+class StageEvents:
+    """2*NUM_STAGES hipEvents per timed step, read back after the timed region."""
+
+    def __init__(self, steps):
+        self.hip = _hip()
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        n = 2 * kda.NUM_STAGES
+        self.arrays = []
+        for _ in range(steps):
+            arr = (ctypes.c_void_p * n)()
+            for i in range(n):
+                ev = ctypes.c_void_p()
+                rc = self.hip.hipEventCreate(ctypes.byref(ev))
+                if rc != 0:
+                    raise RuntimeError("hipEventCreate failed (%d)" % rc)
+                arr[i] = ev.value
+            self.arrays.append(arr)
+
+    def stage_ms(self):
+        """Average duration (ms) of each stage over the recorded steps."""
+        out = np.zeros(kda.NUM_STAGES)
+        for arr in self.arrays:
+            for s in range(kda.NUM_STAGES):
+                ms = ctypes.c_float(0.0)
+                rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), arr[2 * s], arr[2 * s + 1])
+                if rc != 0:
+                    raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+                out[s] += ms.value
+        return out / max(1, len(self.arrays))
+
+    def close(self):
+        for arr in self.arrays:
+            for ev in arr:
+                self.hip.hipEventDestroy(ev)
+
+
+def algorithmic(w):
+    """Algorithmic bytes and FLOPs of the whole forward, per token-head (bf16
+    inputs/outputs, triangular savings counted; see the measurement notes)."""
+    K, V, C = w.K, w.V, w.chunk_size
+    elt = 2 if w.dtype == "bf16" else 4
+    bytes_th = elt * (3 * K + V) + elt + elt * V
+    flops_th = 2 * (3 * K * V + (C / 2) * (3 * K + 2 * V)) + C * C / 3
+    return bytes_th, flops_th
+
+
+def stage_bytes(w, stage, NT, N):
+    """Algorithmic (unique) HBM bytes one launch of a stage moves: what it must
+    read and write at least, given the workspace format of the current kernels."""
+    B, T, H, K, V, C = w.B, w.T, w.H, w.K, w.V, w.chunk_size
+    ein = 2 if w.dtype == "bf16" else 4
+    ews = 4                      # chunk factors are stored in fp32 by the current kernels
+    tokh = B * T * H
+    per_chunk = C * (3 * K + V + C) * ews + K * 4   # W, Qt, Kb, U, Aqk, gL
+    if stage == 1:   # prologue: q,k,gate,beta in -> qn,kn,g,beta fp32 out
+        return tokh * ((3 * K + 1) * ein + (3 * K + 1) * 4)
+    if stage == 2:   # chunk factors: qn,kn,g,beta,v in -> factors out
+        return tokh * ((3 * K + 1) * 4 + V * ein) + NT * H * per_chunk
+    if stage == 3:   # state pass: factors in, o out, states
+        return NT * H * per_chunk + tokh * V * ein + N * H * K * V * 4
+    return 0
+
+
+def cpu_baseline(inp, w, budget_s=12.0):
+    """The oracle as it stands on a bounded sample: row 0, a few heads, the
+    first tokens of the row; scaled to Mtokens/s of the full H-head workload."""
+    import oracle
+    threads = oracle.default_threads()
+    heads = list(range(min(w.H, max(1, threads))))
+    # calibrate on a short prefix, then size the sample for ~budget_s
+    def run(T):
+        cut = lambda t: t[:1, :T][:, :, heads].float().cpu().numpy()
+        args = [cut(inp[x]) for x in ("q", "k", "v", "gate")]
+        beta = inp["beta"][:1, :T][:, :, heads].float().cpu().numpy()
+        a_log = inp["a_log"][heads].cpu().numpy()
+        dt_bias = inp["dt_bias"][heads].cpu().numpy()
+        t0 = time.perf_counter()
+        oracle.kda_fwd(*args, beta, a_log, dt_bias, scale=w.scale, lower_bound=w.lower_bound,
+                       threads=threads)
+        return time.perf_counter() - t0
+    t_probe = 256
+    dt = run(t_probe)
+    T = int(min(w.T, max(t_probe, t_probe * budget_s / max(dt, 1e-6))))
+    dt = run(T)
+    token_heads = T * len(heads)
+    mtok = token_heads / w.H / dt / 1e6
+    return {"value": mtok, "unit": "Mtokens/s", "cores": threads, "kind": "oracle",
+            "sample": "row 0, heads 0..%d, first %d tokens (%d token-heads, %.1f s), fp64 "
+                      "token recurrence, scaled to %d heads" % (len(heads) - 1, T, token_heads, dt, w.H)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(the forward shards by head or by sequence slice; see DESIGN.md).", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    kda.load_library()
+    w = synthetic.WORKLOADS[args.workload]
+    dev = torch.device("cuda", 0)
+    print("[bench] drawing %s on %s" % (w.name, dev), file=sys.stderr, flush=True)
+    inp = synthetic.make_inputs(w, dev)
+    cu = inp["cu_seqlens"]
+    cu_host = None if cu is None else cu.cpu()
+    N = w.B if cu is None else cu.numel() - 1
+    o = torch.empty(w.B, w.T, w.H, w.V, dtype=w.torch_dtype, device=dev)
+    need = kda.fwd_workspace_size((w.B, w.T, w.H, w.K), w.V, w.torch_dtype, w.chunk_size,
+                                  w.lower_bound, N=N, cu_seqlens_host=cu_host)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    ws = ws[(-ws.data_ptr()) % 256:][:need]
+    fin = None
+
+    def step(events=None):
+        nonlocal fin
+        _, fin = kda.kda_fwd(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"],
+                             inp["a_log"], inp["dt_bias"], scale=w.scale,
+                             lower_bound=w.lower_bound, chunk_size=w.chunk_size, cu_seqlens=cu,
+                             cu_seqlens_host=cu_host, initial_state=inp["initial_state"],
+                             output_final_state=w.output_final_state, out=o, workspace=ws,
+                             stage_events=events)
+
+    for i in range(args.warmup):
+        step()
+        torch.cuda.synchronize()
+        print("[bench] warmup %d/%d done" % (i + 1, args.warmup), file=sys.stderr, flush=True)
+    ev = StageEvents(args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(ev.arrays[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    stage_ms = ev.stage_ms()
+    ev.close()
+    print("[bench] timed %d steps: %.3f ms/step; stages (ms) %s" % (
+        args.steps, ms_per_step, dict(zip(kda.STAGE_NAMES, np.round(stage_ms, 4).tolist()))),
+        file=sys.stderr, flush=True)
+
+    tokens = w.B * w.T
+    value = tokens / (ms_per_step / 1e3) / 1e6
+    bytes_th, flops_th = algorithmic(w)
+    tokh = tokens * w.H
+    NT = w.B * math.ceil(w.T / w.chunk_size) if cu is None else int(
+        sum(math.ceil(int(b - a) / w.chunk_size) for a, b in zip(cu_host[:-1], cu_host[1:])))
+    dom = int(np.argmax(stage_ms))
+    dom_bytes = stage_bytes(w, dom, NT, N)
+    achieved = dom_bytes / (stage_ms[dom] / 1e3) / 1e9 if stage_ms[dom] > 0 else 0.0
+    roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None,
+                "kernel": kda.STAGE_NAMES[dom], "kernel_ms": round(float(stage_ms[dom]), 4),
+                "bytes_per_launch": dom_bytes}
+    path_gbs = tokh * bytes_th / (ms_per_step / 1e3) / 1e9
+    mfma_util = tokh * flops_th / (ms_per_step / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS * 100
+    out = {
+        "metric": METRIC, "value": round(value, 4), "unit": "Mtokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "dk": w.K, "dv": w.V,
+                   "chunk_size": w.chunk_size, "lower_bound": w.lower_bound,
+                   "documents": N, "initial_state": w.init_std is not None},
+        "stage_ms": dict(zip(kda.STAGE_NAMES, [round(float(x), 4) for x in stage_ms])),
+        "path_algorithmic_GBps": round(path_gbs, 2),
+        "path_hbm_frac": round(path_gbs / HBM_PEAK_GBS, 5),
+        "mfma_util_pct_useful_flops": round(mfma_util, 3),
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(inp, w)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,319 @@
+// Host side of libkda.so: argument validation, workspace layout, launch plan.
+// Every check runs before anything is enqueued; see include/kda.h for the
+// contract each entry point keeps.
+#include "../../include/kda.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "kda_internal.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kda_status fail(kda_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool head_dim_ok(int d) { return d == 64 || d == 128; }
+
+// Shape/flag validation shared by every entry point (no pointers checked here).
+kda_status validate_problem(const kda_problem* p, bool summary) {
+  if (!p) return fail(KDA_EINVAL, "problem is NULL");
+  if (p->B < 1 || p->T < 0 || p->H < 1 || p->K < 1 || p->V < 1)
+    return fail(KDA_EINVAL, "bad shape B=%d T=%d H=%d K=%d V=%d (need B,H,K,V >= 1, T >= 0)", p->B,
+                p->T, p->H, p->K, p->V);
+  if (p->dtype != KDA_F32 && p->dtype != KDA_BF16)
+    return fail(KDA_EINVAL, "dtype must be KDA_F32 or KDA_BF16, got %d", p->dtype);
+  if (p->chunk_size <= 0) return fail(KDA_EINVAL, "chunk_size must be positive, got %d", p->chunk_size);
+  if (p->chunk_size != 16 && p->chunk_size != 32 && p->chunk_size != 64)
+    return fail(KDA_EUNSUPPORTED, "chunk_size %d is not supported (16, 32 or 64)", p->chunk_size);
+  if (!std::isnan(p->lower_bound) && !(p->lower_bound < 0.f && std::isfinite(p->lower_bound)))
+    return fail(KDA_EINVAL, "lower_bound must be negative, got %g", (double)p->lower_bound);
+  if (!head_dim_ok(p->K) || !head_dim_ok(p->V))
+    return fail(KDA_EUNSUPPORTED, "head dims K=%d V=%d are not supported (64 or 128)", p->K, p->V);
+  const long long BT = (long long)p->B * p->T;
+  if (BT >= (1LL << 31) || BT * p->H >= (1LL << 31))
+    return fail(KDA_EUNSUPPORTED, "B*T*H = %lld tokens-heads exceeds 2^31", BT * p->H);
+  if (p->cu_seqlens == nullptr) {
+    if (p->cu_seqlens_host != nullptr)
+      return fail(KDA_EINVAL, "cu_seqlens_host given without cu_seqlens");
+    if (p->N != p->B)
+      return fail(KDA_EINVAL, "N must equal B (%d) without cu_seqlens, got %d", p->B, p->N);
+  } else {
+    if (summary) return fail(KDA_EINVAL, "a state summary takes no cu_seqlens (one slice per row)");
+    if (p->B != 1) return fail(KDA_EINVAL, "cu_seqlens requires B == 1 (one packed row), got B=%d", p->B);
+    if (p->N < 0 || (p->N == 0 && p->T != 0))
+      return fail(KDA_EINVAL, "cu_seqlens must describe at least one sequence (N=%d, T=%d)", p->N, p->T);
+    if (const int32_t* cu = p->cu_seqlens_host) {
+      if (cu[0] != 0) return fail(KDA_EINVAL, "cu_seqlens[0] must be 0, got %d", cu[0]);
+      for (int n = 0; n < p->N; ++n) {
+        if (cu[n + 1] < 0)
+          return fail(KDA_EINVAL, "cu_seqlens[%d] = %d is negative (padding sentinels are not accepted)",
+                      n + 1, cu[n + 1]);
+        if (cu[n + 1] < cu[n])
+          return fail(KDA_EINVAL, "cu_seqlens must be non-decreasing: cu[%d]=%d < cu[%d]=%d", n + 1,
+                      cu[n + 1], n, cu[n]);
+      }
+      if (cu[p->N] != p->T)
+        return fail(KDA_EINVAL, "cu_seqlens[N] must equal T=%d, got %d", p->T, cu[p->N]);
+    }
+  }
+  return KDA_OK;
+}
+
+struct Layout {
+  int NT = 0;
+  int exact = 1;
+  size_t off_tok = 0, off_len = 0, off_seq0 = 0, off_nt = 0;
+  size_t off_qn = 0, off_kn = 0, off_g = 0, off_bt = 0;
+  size_t off_W = 0, off_U = 0, off_Qt = 0, off_Kb = 0, off_Aqk = 0, off_gL = 0;
+  size_t total = 0;
+};
+
+int chunk_count(const kda_problem* p, int* exact) {
+  const int C = p->chunk_size;
+  if (!p->cu_seqlens) {
+    *exact = 1;
+    return p->B * ((p->T + C - 1) / C);
+  }
+  if (p->cu_seqlens_host) {
+    long long nt = 0;
+    for (int n = 0; n < p->N; ++n) nt += (p->cu_seqlens_host[n + 1] - p->cu_seqlens_host[n] + C - 1) / C;
+    *exact = 1;
+    return (int)nt;
+  }
+  *exact = 0;  // sum_n ceil(L_n / C) <= floor(T / C) + N
+  return p->T / C + p->N;
+}
+
+Layout layout(const kda_problem* p) {
+  Layout L;
+  L.NT = chunk_count(p, &L.exact);
+  const size_t NT = (size_t)L.NT, H = p->H, K = p->K, V = p->V, C = p->chunk_size, N = p->N;
+  const size_t tokh = (size_t)p->B * p->T * H;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  L.off_tok = take(NT * 4);
+  L.off_len = take(NT * 4);
+  L.off_seq0 = take((N + 1) * 4);
+  L.off_nt = take(4);
+  L.off_qn = take(tokh * K * 4);
+  L.off_kn = take(tokh * K * 4);
+  L.off_g = take(tokh * K * 4);
+  L.off_bt = take(tokh * 4);
+  const size_t elt = 4;
+  L.off_W = take(NT * H * C * K * elt);
+  L.off_U = take(NT * H * C * V * elt);
+  L.off_Qt = take(NT * H * C * K * elt);
+  L.off_Kb = take(NT * H * C * K * elt);
+  L.off_Aqk = take(NT * H * C * C * elt);
+  L.off_gL = take(NT * H * K * 4);
+  L.total = o;
+  return L;
+}
+
+kda::FwdArgs make_args(const kda_problem* p, const Layout& L, void* ws) {
+  kda::FwdArgs a{};
+  a.B = p->B; a.T = p->T; a.H = p->H; a.K = p->K; a.V = p->V; a.C = p->chunk_size; a.N = p->N;
+  a.NT = L.NT;
+  a.exact_nt = L.exact;
+  a.dtype = p->dtype;
+  a.scale = (p->scale > 0.f) ? p->scale : 1.0f / std::sqrt((float)p->K);
+  a.has_lb = std::isnan(p->lower_bound) ? 0 : 1;
+  a.lb = a.has_lb ? p->lower_bound : 0.f;
+  a.cu = p->cu_seqlens;
+  char* w = (char*)ws;
+  a.chunk_tok = (int32_t*)(w + L.off_tok);
+  a.chunk_len = (int32_t*)(w + L.off_len);
+  a.seq_chunk0 = (int32_t*)(w + L.off_seq0);
+  a.nt_dev = (int32_t*)(w + L.off_nt);
+  a.qn = (float*)(w + L.off_qn);
+  a.kn = (float*)(w + L.off_kn);
+  a.g = (float*)(w + L.off_g);
+  a.bt = (float*)(w + L.off_bt);
+  a.ws_bf16 = 0;
+  a.W = w + L.off_W;
+  a.U = w + L.off_U;
+  a.Qt = w + L.off_Qt;
+  a.Kb = w + L.off_Kb;
+  a.Aqk = w + L.off_Aqk;
+  a.gL = (float*)(w + L.off_gL);
+  return a;
+}
+
+bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
+
+kda_status check_inputs(const kda_problem* p, const void* q, const void* k, const void* v,
+                        const void* gate, const void* beta, const float* a_log,
+                        const float* dt_bias) {
+  const bool any_tokens = (long long)p->B * p->T > 0;
+  if (any_tokens && (!q || !k || !v || !gate || !beta))
+    return fail(KDA_EINVAL, "q, k, v, gate and beta must be non-NULL");
+  if (!a_log || !dt_bias) return fail(KDA_EINVAL, "a_log and dt_bias must be non-NULL (fp32 [H] and [H,K])");
+  const size_t elt = p->dtype == KDA_BF16 ? 2 : 4;
+  const void* ptrs[] = {q, k, v, gate, beta};
+  for (const void* ptr : ptrs)
+    if (ptr && !aligned(ptr, elt)) return fail(KDA_EINVAL, "input tensor is not %zu-byte aligned", elt);
+  if (!aligned(a_log, 4) || !aligned(dt_bias, 4)) return fail(KDA_EINVAL, "a_log/dt_bias misaligned");
+  return KDA_OK;
+}
+
+kda_status check_ws(size_t need, void* ws, size_t bytes) {
+  if (need == 0) return KDA_OK;
+  if (!ws) return fail(KDA_EWORKSPACE, "workspace is NULL but %zu bytes are needed", need);
+  if (bytes < need) return fail(KDA_EWORKSPACE, "workspace has %zu bytes, %zu needed", bytes, need);
+  if (!aligned(ws, kAlign)) return fail(KDA_EINVAL, "workspace must be 256-byte aligned");
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+kda_status kda_validate(const kda_problem* p) {
+  kda_status st = validate_problem(p, false);
+  if (st == KDA_OK) g_last_error.clear();
+  return st;
+}
+
+size_t kda_fwd_workspace_size(const kda_problem* p, kda_status* status) {
+  kda_status st = validate_problem(p, false);
+  if (status) *status = st;
+  return st == KDA_OK ? layout(p).total : 0;
+}
+
+size_t kda_state_summary_workspace_size(const kda_problem* p, kda_status* status) {
+  kda_status st = validate_problem(p, true);
+  if (status) *status = st;
+  return st == KDA_OK ? layout(p).total : 0;
+}
+
+kda_status kda_fwd_profiled(const kda_problem* p, const void* q, const void* k, const void* v,
+                            const void* gate, const void* beta, const float* a_log,
+                            const float* dt_bias, const float* initial_state, void* o,
+                            float* final_state, void* workspace, size_t workspace_bytes,
+                            void* stream, void* const* stage_events) {
+  kda_status st = validate_problem(p, false);
+  if (st != KDA_OK) return st;
+  st = check_inputs(p, q, k, v, gate, beta, a_log, dt_bias);
+  if (st != KDA_OK) return st;
+  if (!o && (long long)p->B * p->T > 0) return fail(KDA_EINVAL, "output o must be non-NULL");
+  if (initial_state && !aligned(initial_state, 4)) return fail(KDA_EINVAL, "initial_state misaligned");
+  if (final_state && !aligned(final_state, 4)) return fail(KDA_EINVAL, "final_state misaligned");
+  if (o && !aligned(o, p->dtype == KDA_BF16 ? 2 : 4)) return fail(KDA_EINVAL, "o misaligned");
+  const Layout L = layout(p);
+  st = check_ws(L.total, workspace, workspace_bytes);
+  if (st != KDA_OK) return st;
+
+  kda::FwdArgs a = make_args(p, L, workspace);
+  a.q = q; a.k = k; a.v = v; a.gate = gate; a.beta = beta;
+  a.a_log = a_log; a.dt_bias = dt_bias; a.init = initial_state;
+  a.o = o; a.fin = final_state; a.summary = 0;
+  a.events = stage_events;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = kda::launch_chunk_table(a, s);
+  if (e == hipSuccess) e = kda::launch_valu_path(a, s);
+  if (e != hipSuccess) return fail(KDA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_last_error.clear();
+  return KDA_OK;
+}
+
+kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const void* v,
+                   const void* gate, const void* beta, const float* a_log, const float* dt_bias,
+                   const float* initial_state, void* o, float* final_state, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return kda_fwd_profiled(p, q, k, v, gate, beta, a_log, dt_bias, initial_state, o, final_state,
+                          workspace, workspace_bytes, stream, nullptr);
+}
+
+kda_status kda_state_summary(const kda_problem* p, const void* q, const void* k, const void* v,
+                             const void* gate, const void* beta, const float* a_log,
+                             const float* dt_bias, float* state_ext, float* transition,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  kda_status st = validate_problem(p, true);
+  if (st != KDA_OK) return st;
+  st = check_inputs(p, q, k, v, gate, beta, a_log, dt_bias);
+  if (st != KDA_OK) return st;
+  if (!state_ext || !transition) return fail(KDA_EINVAL, "state_ext and transition must be non-NULL");
+  if (!aligned(state_ext, 4) || !aligned(transition, 4)) return fail(KDA_EINVAL, "summary outputs misaligned");
+  const Layout L = layout(p);
+  st = check_ws(L.total, workspace, workspace_bytes);
+  if (st != KDA_OK) return st;
+  kda::FwdArgs a = make_args(p, L, workspace);
+  a.q = q; a.k = k; a.v = v; a.gate = gate; a.beta = beta;
+  a.a_log = a_log; a.dt_bias = dt_bias; a.init = nullptr;
+  a.o = nullptr; a.fin = nullptr; a.summary = 1;
+  a.state_ext = state_ext; a.transition = transition;
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = kda::launch_chunk_table(a, s);
+  if (e == hipSuccess) e = kda::launch_valu_path(a, s);
+  if (e != hipSuccess) return fail(KDA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_last_error.clear();
+  return KDA_OK;
+}
+
+kda_status kda_apply_state_summary(int32_t B, int32_t H, int32_t K, int32_t V,
+                                   const float* state_ext, const float* transition,
+                                   const float* initial_state, float* final_state, void* stream) {
+  if (B < 1 || H < 1 || !head_dim_ok(K) || !head_dim_ok(V))
+    return fail(B < 1 || H < 1 ? KDA_EINVAL : KDA_EUNSUPPORTED,
+                "bad summary shape B=%d H=%d K=%d V=%d", B, H, K, V);
+  if (!state_ext || !final_state || (initial_state && !transition))
+    return fail(KDA_EINVAL, "state_ext, final_state (and transition when initial_state is given) must be non-NULL");
+  if (initial_state && (final_state == initial_state || (const float*)final_state == transition))
+    return fail(KDA_EINVAL, "final_state may not alias initial_state or transition");
+  hipError_t e = kda::launch_apply_summary(B, H, K, V, state_ext, transition, initial_state,
+                                           final_state, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(KDA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_last_error.clear();
+  return KDA_OK;
+}
+
+int32_t kda_chunk_capacity(const kda_problem* p, kda_status* status) {
+  kda_status st = validate_problem(p, false);
+  if (status) *status = st;
+  if (st != KDA_OK) return 0;
+  int exact = 0;
+  return chunk_count(p, &exact);
+}
+
+kda_status kda_chunk_table(const kda_problem* p, int32_t* tok, int32_t* len, int32_t* seq_chunk0,
+                           int32_t* count, int32_t cap, void* stream) {
+  kda_status st = validate_problem(p, false);
+  if (st != KDA_OK) return st;
+  int exact = 0;
+  const int need = chunk_count(p, &exact);
+  if (cap < need) return fail(KDA_EINVAL, "chunk table capacity %d < %d", cap, need);
+  if ((need > 0 && (!tok || !len)) || !seq_chunk0 || !count)
+    return fail(KDA_EINVAL, "chunk table buffers must be non-NULL");
+  kda::FwdArgs a{};
+  a.B = p->B; a.T = p->T; a.C = p->chunk_size; a.N = p->N; a.NT = need; a.cu = p->cu_seqlens;
+  a.chunk_tok = tok; a.chunk_len = len; a.seq_chunk0 = seq_chunk0; a.nt_dev = count;
+  hipError_t e = kda::launch_chunk_table(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(KDA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_last_error.clear();
+  return KDA_OK;
+}
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+int32_t kda_version(void) { return (0 << 16) | 1; }
+
+}  // extern "C"

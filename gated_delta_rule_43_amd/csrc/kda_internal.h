@@ -1,0 +1,85 @@
+// Internal declarations shared by the host orchestration (kda_api.cpp) and the
+// HIP kernels of libkda.so.  Not part of the public ABI (include/kda.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// ---------------------------------------------------------------------------
+// bf16 stored as raw 16-bit patterns; conversions round to nearest even.
+// ---------------------------------------------------------------------------
+typedef uint16_t bf16;
+
+__host__ __device__ inline float bf16_to_f32(bf16 x) {
+  union { uint32_t u; float f; } c;
+  c.u = ((uint32_t)x) << 16;
+  return c.f;
+}
+
+__host__ __device__ inline bf16 f32_to_bf16(float f) {
+  union { uint32_t u; float f; } c;
+  c.f = f;
+  if ((c.u & 0x7f800000u) == 0x7f800000u && (c.u & 0x007fffffu)) return (bf16)((c.u >> 16) | 0x40);
+  uint32_t r = c.u + 0x7fffu + ((c.u >> 16) & 1u);
+  return (bf16)(r >> 16);
+}
+
+__device__ inline float load_f32(const float* p) { return *p; }
+__device__ inline float load_f32(const bf16* p) { return bf16_to_f32(*p); }
+__device__ inline void store_as(float* p, float x) { *p = x; }
+__device__ inline void store_as(bf16* p, float x) { *p = f32_to_bf16(x); }
+
+// ---------------------------------------------------------------------------
+// Everything one forward / summary call needs, resolved on the host.
+// ---------------------------------------------------------------------------
+struct FwdArgs {
+  // shapes
+  int B, T, H, K, V, C, N;
+  int NT;          // chunk count: exact, or an upper bound when exact_nt == 0
+  int exact_nt;
+  int dtype;       // 0 fp32, 1 bf16
+  float scale;
+  int has_lb;
+  float lb;
+  // inputs
+  const int32_t* cu;  // device cu_seqlens or nullptr
+  const void *q, *k, *v, *gate, *beta;
+  const float *a_log, *dt_bias, *init;
+  // outputs
+  void* o;
+  float* fin;
+  float* state_ext;   // summary mode
+  float* transition;  // summary mode
+  int summary;
+  // workspace: chunk table
+  int32_t* chunk_tok;  // [NT] flat token index b*T + t of the chunk's first token
+  int32_t* chunk_len;  // [NT] tokens in the chunk (1..C)
+  int32_t* seq_chunk0; // [N+1] first chunk of each sequence
+  int32_t* nt_dev;     // [1] actual number of chunks
+  // workspace: per-token prologue results (VALU path)
+  float *qn, *kn, *g, *bt;
+  // workspace: per chunk-head factors, element type ws_dtype
+  int ws_bf16;
+  void *W, *U, *Qt, *Kb, *Aqk;
+  float* gL;
+  // optional stage timing: hipEvent_t handles, [2 * kNumStages], entries may be null
+  void* const* events;
+};
+
+// Stages of one forward, in launch order (timing hooks of kda_fwd_profiled).
+enum Stage { kStageTable = 0, kStagePrologue = 1, kStageChunk = 2, kStageState = 3, kNumStages = 4 };
+
+inline void mark(const FwdArgs& a, int stage, int end, hipStream_t s) {
+  if (a.events && a.events[2 * stage + end]) hipEventRecord((hipEvent_t)a.events[2 * stage + end], s);
+}
+
+// Kernel launchers (return the first HIP error, hipSuccess otherwise).
+hipError_t launch_chunk_table(const FwdArgs& a, hipStream_t s);
+hipError_t launch_valu_path(const FwdArgs& a, hipStream_t s);
+hipError_t launch_apply_summary(int B, int H, int K, int V, const float* E, const float* P,
+                                const float* S0, float* F, hipStream_t s);
+
+}  // namespace kda

@@ -1,0 +1,315 @@
+// Plain-VALU fp32 path of the KDA chunked forward.
+//
+// It serves fp32 inputs and every chunk size, and is the path the faster MFMA
+// kernels are measured against.  Three kernels, all fp32 arithmetic:
+//
+//   1. k_prologue_valu   one wave per token-head: q^, k^ (L2 norm), the
+//                        per-key-channel log-decay g from the raw gate logits,
+//                        a_log and dt_bias, and beta = sigmoid(logit);
+//   2. k_chunk_valu      one workgroup per chunk-head: the chunk-local factors
+//                        of the WY/UT form (below);
+//   3. k_state_valu      one workgroup per (sequence, head, column tile):
+//                        the sequential pass over the sequence's chunks that
+//                        carries the fp32 state and writes the output.
+//
+// Chunk algebra (derived from the token recurrence; the pages name the chunked
+// kernel, chunk_kda, but print no algorithm).  For a chunk of L tokens entering
+// with state S0, gamma = chunk-local inclusive cumulative sum of g:
+//   Akk[r,i] = sum_c k^_rc k^_ic exp(gamma_rc - gamma_ic)       (i < r)
+//   Aqk[r,i] = sum_c q^_rc k^_ic exp(gamma_rc - gamma_ic)       (i <= r)
+//   Tm = (I + Diag(beta) Akk)^-1                                 (forward substitution)
+//   W  = Tm Diag(beta) (K^ . exp(gamma)),   U = Tm Diag(beta) V
+//   Delta = U - W S0
+//   O     = scale (Q^ . exp(gamma)) S0 + scale Aqk Delta
+//   S_L   = Diag(exp(gamma_L)) S0 + (K^ . exp(gamma_L - gamma))^T Delta
+// All exponents above are <= 0 because g <= 0, so nothing overflows.
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxD = 128;  // largest head dimension
+
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+  return x;
+}
+
+__device__ inline float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
+__device__ inline float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
+
+// In-kernel gate: g = -exp(a_log) softplus(x + dt_bias), or with a lower bound
+// lb < 0: g = lb * sigmoid(exp(a_log) (x + dt_bias)).  g is floored at -110:
+// exp(-110) is already below the smallest fp32 denormal, so no decay factor
+// representable in fp32 changes, and the chunk-local cumulative sums stay
+// small enough for their differences to keep full precision.
+constexpr float kGateFloor = -110.f;
+__device__ inline float gate_value(float x, float A, int has_lb, float lb) {
+  return fmaxf(has_lb ? lb * sigmoid_f(A * x) : -A * softplus_f(x), kGateFloor);
+}
+
+template <typename Tin>
+__global__ __launch_bounds__(kThreads) void k_prologue_valu(
+    const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ gate,
+    const Tin* __restrict__ beta, const float* __restrict__ a_log,
+    const float* __restrict__ dt_bias, int64_t n_th, int H, int K, int has_lb, float lb,
+    float* __restrict__ qn, float* __restrict__ kn, float* __restrict__ g,
+    float* __restrict__ bt) {
+  const int lane = threadIdx.x & 63;
+  const int64_t th = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (th >= n_th) return;
+  const int h = (int)(th % H);
+  const int64_t base = th * K;
+  float ssq = 0.f, ssk = 0.f;
+  for (int c = lane; c < K; c += 64) {
+    float xq = load_f32(q + base + c), xk = load_f32(k + base + c);
+    ssq = fmaf(xq, xq, ssq);
+    ssk = fmaf(xk, xk, ssk);
+  }
+  ssq = wave_sum(ssq);
+  ssk = wave_sum(ssk);
+  const float rq = 1.f / sqrtf(ssq + 1e-6f), rk = 1.f / sqrtf(ssk + 1e-6f);
+  const float A = expf(a_log[h]);
+  for (int c = lane; c < K; c += 64) {
+    qn[base + c] = load_f32(q + base + c) * rq;
+    kn[base + c] = load_f32(k + base + c) * rk;
+    float x = load_f32(gate + base + c) + dt_bias[(int64_t)h * K + c];
+    g[base + c] = gate_value(x, A, has_lb, lb);
+  }
+  if (lane == 0) bt[th] = sigmoid_f(load_f32(beta + th));
+}
+
+// One workgroup per chunk-head (flattened j*H + h).
+template <typename Tin, int C>
+__global__ __launch_bounds__(kThreads) void k_chunk_valu(FwdArgs a) {
+  const int H = a.H, K = a.K, V = a.V;
+  const int64_t wid = blockIdx.x;
+  const int j = (int)(wid / H), h = (int)(wid % H);
+  if (j >= *a.nt_dev) return;
+  const int tid = threadIdx.x;
+  const int tok0 = a.chunk_tok[j], L = a.chunk_len[j];
+
+  __shared__ float sG[C][kMaxD];   // gamma, later X = beta k^ exp(gamma)
+  __shared__ float sA[C][C + 1];   // Akk, then Tm in place
+  __shared__ float sRow[C];
+  __shared__ float sB[C];
+
+  auto tok_off = [&](int r) { return ((int64_t)(tok0 + r) * H + h); };
+
+  // gamma: chunk-local inclusive cumsum; rows >= L repeat gamma_{L-1}
+  for (int c = tid; c < K; c += kThreads) {
+    float acc = 0.f;
+    for (int r = 0; r < C; ++r) {
+      if (r < L) acc += a.g[tok_off(r) * K + c];
+      sG[r][c] = acc;
+    }
+  }
+  for (int r = tid; r < C; r += kThreads) sB[r] = r < L ? a.bt[tok_off(r)] : 0.f;
+  __syncthreads();
+
+  const int64_t chb = (int64_t)j * H + h;  // chunk-head index
+  float* Aqk = (float*)a.Aqk + chb * C * C;
+  for (int p = tid; p < C * C; p += kThreads) {
+    const int r = p / C, i = p % C;
+    float akk = 0.f, aqk = 0.f;
+    if (r < L && i <= r) {
+      const float* kr = a.kn + tok_off(r) * K;
+      const float* qr = a.qn + tok_off(r) * K;
+      const float* ki = a.kn + tok_off(i) * K;
+      for (int c = 0; c < K; ++c) {
+        const float d = expf(sG[r][c] - sG[i][c]);
+        const float kd = ki[c] * d;
+        akk = fmaf(kr[c], kd, akk);
+        aqk = fmaf(qr[c], kd, aqk);
+      }
+    }
+    sA[r][i] = (i < r) ? akk : 0.f;
+    Aqk[p] = (i <= r && r < L) ? a.scale * aqk : 0.f;
+  }
+  __syncthreads();
+
+  // Tm = (I + Diag(beta) Akk)^-1, row by row: Tm_r = e_r - beta_r sum_{i<r} Akk_ri Tm_i
+  for (int r = 0; r < C; ++r) {
+    if (tid < r) sRow[tid] = sA[r][tid];
+    __syncthreads();
+    if (tid < r) {
+      float acc = 0.f;
+      for (int i = tid; i < r; ++i) acc = fmaf(sRow[i], sA[i][tid], acc);
+      sA[r][tid] = -sB[r] * acc;
+    } else if (tid == r) {
+      sA[r][r] = 1.f;
+    }
+    __syncthreads();
+  }
+
+  // Qt = scale q^ exp(gamma), Kb = k^ exp(gamma_L - gamma), gL = exp(gamma_L)
+  float* Qt = (float*)a.Qt + chb * C * K;
+  float* Kb = (float*)a.Kb + chb * C * K;
+  for (int p = tid; p < C * K; p += kThreads) {
+    const int r = p / K, c = p % K;
+    float qt = 0.f, kb = 0.f;
+    if (r < L) {
+      qt = a.scale * a.qn[tok_off(r) * K + c] * expf(sG[r][c]);
+      kb = a.kn[tok_off(r) * K + c] * expf(sG[C - 1][c] - sG[r][c]);
+    }
+    Qt[p] = qt;
+    Kb[p] = kb;
+  }
+  for (int c = tid; c < K; c += kThreads) a.gL[chb * K + c] = expf(sG[C - 1][c]);
+  __syncthreads();
+  // X = beta k^ exp(gamma), in place of gamma
+  for (int p = tid; p < C * K; p += kThreads) {
+    const int r = p / K, c = p % K;
+    sG[r][c] = r < L ? sB[r] * a.kn[tok_off(r) * K + c] * expf(sG[r][c]) : 0.f;
+  }
+  __syncthreads();
+  // W = Tm X, U = Tm Diag(beta) V   (Tm lower triangular with unit diagonal)
+  float* W = (float*)a.W + chb * C * K;
+  for (int p = tid; p < C * K; p += kThreads) {
+    const int r = p / K, c = p % K;
+    float acc = 0.f;
+    for (int i = 0; i <= r; ++i) acc = fmaf(sA[r][i], sG[i][c], acc);
+    W[p] = acc;
+  }
+  float* U = (float*)a.U + chb * C * V;
+  const Tin* v = (const Tin*)a.v;
+  for (int p = tid; p < C * V; p += kThreads) {
+    const int r = p / V, c = p % V;
+    float acc = 0.f;
+    const int iend = min(r, L - 1);
+    for (int i = 0; i <= iend; ++i)
+      acc = fmaf(sA[r][i] * sB[i], load_f32(v + tok_off(i) * V + c), acc);
+    U[p] = acc;
+  }
+}
+
+// One workgroup per (sequence n, head h, tile of VT state columns).  Columns
+// [0, V) are the value columns of the state; in summary mode columns
+// [V, V+K) carry the transition (its values are zero, it starts as I).
+template <typename Tin, int C, int VT>
+__global__ __launch_bounds__(kThreads) void k_state_valu(FwdArgs a) {
+  const int H = a.H, K = a.K, V = a.V;
+  const int ncols = a.summary ? V + K : V;
+  const int ntile = ncols / VT;
+  const int64_t wid = blockIdx.x;
+  const int tile = (int)(wid % ntile);
+  const int64_t nh = wid / ntile;
+  const int h = (int)(nh % H), n = (int)(nh / H);
+  const int col0 = tile * VT;
+  const int tid = threadIdx.x;
+
+  __shared__ float sS[kMaxD][VT];
+  __shared__ float sD[C][VT];
+
+  const int64_t sbase = ((int64_t)n * H + h) * K * V;
+  for (int e = tid; e < K * VT; e += kThreads) {
+    const int c = e / VT, jj = e % VT, col = col0 + jj;
+    float s;
+    if (col < V)
+      s = (a.init && !a.summary) ? a.init[sbase + (int64_t)c * V + col] : 0.f;
+    else
+      s = (c == col - V) ? 1.f : 0.f;
+    sS[c][jj] = s;
+  }
+  const int jc0 = a.seq_chunk0[n], jc1 = a.seq_chunk0[n + 1];
+  for (int j = jc0; j < jc1; ++j) {
+    const int64_t chb = (int64_t)j * H + h;
+    const float* W = (const float*)a.W + chb * C * K;
+    const float* U = (const float*)a.U + chb * C * V;
+    const float* Qt = (const float*)a.Qt + chb * C * K;
+    const float* Kb = (const float*)a.Kb + chb * C * K;
+    const float* Aqk = (const float*)a.Aqk + chb * C * C;
+    const float* gL = a.gL + chb * K;
+    const int tok0 = a.chunk_tok[j], L = a.chunk_len[j];
+    __syncthreads();
+    // Delta = U - W S
+    for (int e = tid; e < C * VT; e += kThreads) {
+      const int r = e / VT, jj = e % VT, col = col0 + jj;
+      float acc = col < V ? U[(int64_t)r * V + col] : 0.f;
+      for (int c = 0; c < K; ++c) acc = fmaf(-W[(int64_t)r * K + c], sS[c][jj], acc);
+      sD[r][jj] = acc;
+    }
+    __syncthreads();
+    // O = Qt S + Aqk Delta  (scale folded into Qt and Aqk)
+    if (!a.summary) {
+      Tin* o = (Tin*)a.o;
+      for (int e = tid; e < C * VT; e += kThreads) {
+        const int r = e / VT, jj = e % VT, col = col0 + jj;
+        if (r >= L) continue;
+        float acc = 0.f;
+        for (int c = 0; c < K; ++c) acc = fmaf(Qt[(int64_t)r * K + c], sS[c][jj], acc);
+        for (int i = 0; i <= r; ++i) acc = fmaf(Aqk[(int64_t)r * C + i], sD[i][jj], acc);
+        store_as(o + ((int64_t)(tok0 + r) * H + h) * V + col, acc);
+      }
+    }
+    __syncthreads();
+    // S = Diag(gL) S + Kb^T Delta
+    for (int e = tid; e < K * VT; e += kThreads) {
+      const int c = e / VT, jj = e % VT;
+      float acc = gL[c] * sS[c][jj];
+      for (int r = 0; r < L; ++r) acc = fmaf(Kb[(int64_t)r * K + c], sD[r][jj], acc);
+      sS[c][jj] = acc;
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < K * VT; e += kThreads) {
+    const int c = e / VT, jj = e % VT, col = col0 + jj;
+    if (!a.summary) {
+      if (a.fin) a.fin[sbase + (int64_t)c * V + col] = sS[c][jj];
+    } else if (col < V) {
+      a.state_ext[sbase + (int64_t)c * V + col] = sS[c][jj];
+    } else {
+      a.transition[((int64_t)n * H + h) * K * K + (int64_t)c * K + (col - V)] = sS[c][jj];
+    }
+  }
+}
+
+template <typename Tin, int C>
+hipError_t run(const FwdArgs& a, hipStream_t s) {
+  const int64_t n_th = (int64_t)a.B * a.T * a.H;
+  mark(a, kStagePrologue, 0, s);
+  if (n_th > 0) {
+    const int64_t blocks = (n_th + 3) / 4;
+    hipLaunchKernelGGL(k_prologue_valu<Tin>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                       (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.gate, (const Tin*)a.beta,
+                       a.a_log, a.dt_bias, n_th, a.H, a.K, a.has_lb, a.lb, a.qn, a.kn, a.g, a.bt);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
+  mark(a, kStagePrologue, 1, s);
+  mark(a, kStageChunk, 0, s);
+  if (a.NT > 0) {
+    hipLaunchKernelGGL((k_chunk_valu<Tin, C>), dim3((unsigned)((int64_t)a.NT * a.H)),
+                       dim3(kThreads), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
+  mark(a, kStageChunk, 1, s);
+  constexpr int VT = 32;
+  const int ncols = a.summary ? a.V + a.K : a.V;
+  const int64_t wgs = (int64_t)a.N * a.H * (ncols / VT);
+  mark(a, kStageState, 0, s);
+  if (wgs > 0 && (a.summary || a.fin || a.NT > 0)) {
+    hipLaunchKernelGGL((k_state_valu<Tin, C, VT>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
+  mark(a, kStageState, 1, s);
+  return hipSuccess;
+}
+
+template <typename Tin>
+hipError_t run_c(const FwdArgs& a, hipStream_t s) {
+  switch (a.C) {
+    case 16: return run<Tin, 16>(a, s);
+    case 32: return run<Tin, 32>(a, s);
+    default: return run<Tin, 64>(a, s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_valu_path(const FwdArgs& a, hipStream_t s) {
+  return a.dtype == 0 ? run_c<float>(a, s) : run_c<bf16>(a, s);
+}
+
+}  // namespace kda

@@ -1,0 +1,334 @@
+"""Python binding of libkda.so (C ABI in include/kda.h).
+
+Argument marshalling only: shapes, dtypes and devices are checked, outputs and
+the workspace are allocated with torch, and every step of the forward runs in
+the HIP kernels of libkda.so on the current HIP stream.  There is no other
+implementation behind these functions: if the library is missing they raise.
+
+Keywords mirror the chunk_kda call on the hyper_parallel coverage page for
+context_parallel/kimi_delta_attention.py (`_run_local_kda`): scale,
+lower_bound, chunk_size, initial_state, output_final_state; document boundaries
+come as cu_seqlens (NeMo AutoModel page "nemo_automodel.components.models.
+kimi_k3.cp").  Errors map as the pages raise them: malformed arguments ->
+ValueError, unsupported shapes -> NotImplementedError, launch failures ->
+RuntimeError.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
+NUM_STAGES = 4
+STAGE_NAMES = ("chunk_table", "prologue", "chunk_factors", "state_pass")
+EXPORTED = ("kda_validate", "kda_fwd_workspace_size", "kda_fwd", "kda_fwd_profiled",
+            "kda_state_summary_workspace_size", "kda_state_summary",
+            "kda_apply_state_summary", "kda_chunk_capacity", "kda_chunk_table",
+            "kda_last_error", "kda_version")
+
+
+class KdaProblem(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("dtype", ctypes.c_int32),
+                ("scale", ctypes.c_float), ("lower_bound", ctypes.c_float),
+                ("chunk_size", ctypes.c_int32), ("N", ctypes.c_int32),
+                ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def load_library(path: Optional[str] = None):
+    """Load libkda.so (once).  Raises ImportError when it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    path = path or LIB_PATH
+    if not os.path.exists(path):
+        raise ImportError("libkda.so is not built (expected at %s); run "
+                          "`python -c 'import __graft_entry__ as g; g.build()'`" % path)
+    lib = ctypes.CDLL(path)
+    P, S, I32 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int32
+    PP = ctypes.POINTER(KdaProblem)
+    PI = ctypes.POINTER(ctypes.c_int)
+    lib.kda_validate.argtypes = [PP]
+    lib.kda_validate.restype = ctypes.c_int
+    lib.kda_fwd_workspace_size.argtypes = [PP, PI]
+    lib.kda_fwd_workspace_size.restype = S
+    lib.kda_state_summary_workspace_size.argtypes = [PP, PI]
+    lib.kda_state_summary_workspace_size.restype = S
+    lib.kda_fwd.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib.kda_fwd.restype = ctypes.c_int
+    lib.kda_fwd_profiled.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, S, P, P]
+    lib.kda_fwd_profiled.restype = ctypes.c_int
+    lib.kda_state_summary.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib.kda_state_summary.restype = ctypes.c_int
+    lib.kda_apply_state_summary.argtypes = [I32, I32, I32, I32, P, P, P, P, P]
+    lib.kda_apply_state_summary.restype = ctypes.c_int
+    lib.kda_chunk_capacity.argtypes = [PP, PI]
+    lib.kda_chunk_capacity.restype = I32
+    lib.kda_chunk_table.argtypes = [PP, P, P, P, P, I32, P]
+    lib.kda_chunk_table.restype = ctypes.c_int
+    lib.kda_last_error.argtypes = []
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_version.argtypes = []
+    lib.kda_version.restype = I32
+    if path == LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _raise(st: int, what: str):
+    msg = "%s: %s" % (what, load_library().kda_last_error().decode())
+    if st == EUNSUPPORTED:
+        raise NotImplementedError(msg)
+    if st == EHIP:
+        raise RuntimeError(msg)
+    raise ValueError(msg)
+
+
+def _nan() -> float:
+    return float("nan")
+
+
+def make_problem(B, T, H, K, V, dtype, scale=None, lower_bound=None, chunk_size=64, N=None,
+                 cu_seqlens_ptr=None, cu_seqlens_host_ptr=None) -> KdaProblem:
+    p = KdaProblem()
+    p.B, p.T, p.H, p.K, p.V = B, T, H, K, V
+    p.dtype = dtype
+    p.scale = 0.0 if scale is None else float(scale)
+    p.lower_bound = _nan() if lower_bound is None else float(lower_bound)
+    p.chunk_size = chunk_size
+    p.N = B if N is None else N
+    p.cu_seqlens = cu_seqlens_ptr
+    p.cu_seqlens_host = cu_seqlens_host_ptr
+    return p
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return KDA_F32
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    raise NotImplementedError("KDA inputs must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _dev(t, name, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise ValueError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor, got device %s" % (name, t.device))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _stream_ptr(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _workspace(nbytes: int, device):
+    if nbytes == 0:
+        return None, 0
+    buf = torch.empty(nbytes + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + nbytes], nbytes
+
+
+def _check_inputs(q, k, v, gate, beta, a_log, dt_bias):
+    """The projected-tensor contract (`_validate_projected_inputs` on the hyper_parallel page)."""
+    for name, t, r in (("query", q, 4), ("key", k, 4), ("value", v, 4), ("gate", gate, 4)):
+        if not isinstance(t, torch.Tensor) or t.dim() != r:
+            raise ValueError("query, key, value, and gate must be rank-4 tensors.")
+    if not isinstance(beta, torch.Tensor) or beta.dim() != 3:
+        raise ValueError("beta must be a rank-3 tensor.")
+    if q.shape != k.shape:
+        raise ValueError("query and key must have identical shapes.")
+    B, T, H, K = q.shape
+    if tuple(v.shape[:2]) != (B, T):
+        raise ValueError("value batch and sequence dimensions must match query.")
+    HV, V = v.shape[2], v.shape[3]
+    if tuple(gate.shape) != (B, T, HV, K):
+        raise ValueError("gate must have shape [B, S_local, num_v_heads, k_head_dim].")
+    if tuple(beta.shape) != (B, T, HV):
+        raise ValueError("beta must have shape [B, S_local, num_v_heads].")
+    if HV % H != 0:
+        raise ValueError("num_v_heads must be divisible by num_k_heads.")
+    if HV != H:
+        raise NotImplementedError("num_v_heads != num_k_heads (grouped value heads) is not supported")
+    if a_log.numel() != HV:
+        raise ValueError("a_log must contain %d elements, got %d." % (HV, a_log.numel()))
+    if dt_bias.numel() != HV * K:
+        raise ValueError("dt_bias must contain %d elements, got %d." % (HV * K, dt_bias.numel()))
+    dt = q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("beta", beta)):
+        _dev(t, name, dtype=dt)
+    _dtype_code(q)
+    _dev(a_log, "a_log", dtype=torch.float32)
+    _dev(dt_bias, "dt_bias", dtype=torch.float32)
+    return B, T, H, K, V
+
+
+def _cu_args(cu_seqlens, cu_seqlens_host, T):
+    if cu_seqlens is None:
+        if cu_seqlens_host is not None:
+            raise ValueError("cu_seqlens_host given without cu_seqlens")
+        return None, None, None, None
+    _dev(cu_seqlens, "cu_seqlens", dtype=torch.int32)
+    if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
+        raise ValueError("cu_seqlens must be a 1-D int32 tensor of N+1 offsets")
+    N = cu_seqlens.numel() - 1
+    if cu_seqlens_host is False:   # caller vouches for the device offsets
+        return cu_seqlens, None, N, None
+    if cu_seqlens_host is None:
+        host = cu_seqlens.to("cpu")
+    else:
+        host = torch.as_tensor(cu_seqlens_host, dtype=torch.int32, device="cpu").contiguous()
+        if host.numel() != N + 1:
+            raise ValueError("cu_seqlens_host must hold the same N+1 offsets as cu_seqlens")
+    return cu_seqlens, host, N, host.data_ptr()
+
+
+def fwd_workspace_size(q_shape, V, dtype=torch.bfloat16, chunk_size=64, lower_bound=None,
+                       N=None, cu_seqlens_host=None) -> int:
+    B, T, H, K = q_shape
+    host = None if cu_seqlens_host is None else torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous()
+    p = make_problem(B, T, H, K, V, KDA_F32 if dtype == torch.float32 else KDA_BF16,
+                     lower_bound=lower_bound, chunk_size=chunk_size,
+                     N=(host.numel() - 1) if host is not None else N,
+                     cu_seqlens_ptr=1 if host is not None else None,
+                     cu_seqlens_host_ptr=host.data_ptr() if host is not None else None)
+    st = ctypes.c_int(0)
+    n = load_library().kda_fwd_workspace_size(ctypes.byref(p), ctypes.byref(st))
+    if st.value:
+        _raise(st.value, "kda_fwd_workspace_size")
+    return int(n)
+
+
+def kda_fwd(q, k, v, gate, beta, a_log, dt_bias, *, scale=None, lower_bound=None,
+            chunk_size=64, cu_seqlens=None, cu_seqlens_host=None, initial_state=None,
+            output_final_state=False, out=None, workspace=None, stage_events=None):
+    """Chunked KDA forward; returns (o, final_state or None).
+
+    q, k, gate [B,T,H,K]; v [B,T,H,V]; beta [B,T,H] (float32 or bfloat16, one
+    dtype); a_log [H] and dt_bias [H,K] float32; cu_seqlens int32 [N+1] on the
+    GPU with B == 1; initial_state float32 [N,H,K,V].  ``cu_seqlens_host`` may
+    carry a CPU copy of the offsets (otherwise one is made, which waits for the
+    GPU); pass ``False`` to skip the host-side check.  ``stage_events`` is an
+    optional ctypes array of 2*NUM_STAGES hipEvent_t handles recorded around
+    each stage (see kda_fwd_profiled in include/kda.h).
+    """
+    B, T, H, K, V = _check_inputs(q, k, v, gate, beta, a_log, dt_bias)
+    lib = load_library()
+    device = q.device
+    cu, host, N, host_ptr = _cu_args(cu_seqlens, cu_seqlens_host, T)
+    if N is None:
+        N = B
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", dtype=torch.float32, shape=(N, H, K, V))
+    if scale is not None and not scale > 0:
+        raise ValueError("scale must be positive, got %r" % (scale,))
+    p = make_problem(B, T, H, K, V, _dtype_code(q), scale, lower_bound, chunk_size, N,
+                     None if cu is None else cu.data_ptr(), host_ptr)
+    st = ctypes.c_int(0)
+    need = lib.kda_fwd_workspace_size(ctypes.byref(p), ctypes.byref(st))
+    if st.value:
+        _raise(st.value, "kda_fwd")
+    o = out if out is not None else torch.empty((B, T, H, V), dtype=q.dtype, device=device)
+    _dev(o, "out", dtype=q.dtype, shape=(B, T, H, V))
+    fin = torch.empty((N, H, K, V), dtype=torch.float32, device=device) if output_final_state else None
+    if workspace is None:
+        ws, nbytes = _workspace(need, device)
+    else:
+        _dev(workspace, "workspace", dtype=torch.uint8)
+        ws, nbytes = workspace, workspace.numel()
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib.kda_fwd_profiled(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ptr(gate), ptr(beta),
+                              ptr(a_log), ptr(dt_bias), ptr(initial_state), ptr(o), ptr(fin),
+                              ptr(ws), nbytes, _stream_ptr(device), stage_events)
+    if st:
+        _raise(st, "kda_fwd")
+    return o, fin
+
+
+def kda_state_summary(q, k, v, gate, beta, a_log, dt_bias, *, lower_bound=None, chunk_size=64,
+                      workspace=None):
+    """Affine summary of each row: (state_ext [B,H,K,V], transition [B,H,K,K]), float32."""
+    B, T, H, K, V = _check_inputs(q, k, v, gate, beta, a_log, dt_bias)
+    lib = load_library()
+    device = q.device
+    p = make_problem(B, T, H, K, V, _dtype_code(q), None, lower_bound, chunk_size, B)
+    st = ctypes.c_int(0)
+    need = lib.kda_state_summary_workspace_size(ctypes.byref(p), ctypes.byref(st))
+    if st.value:
+        _raise(st.value, "kda_state_summary")
+    E = torch.empty((B, H, K, V), dtype=torch.float32, device=device)
+    P = torch.empty((B, H, K, K), dtype=torch.float32, device=device)
+    if workspace is None:
+        ws, nbytes = _workspace(need, device)
+    else:
+        ws, nbytes = workspace, workspace.numel()
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib.kda_state_summary(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ptr(gate), ptr(beta),
+                               ptr(a_log), ptr(dt_bias), ptr(E), ptr(P), ptr(ws), nbytes,
+                               _stream_ptr(device))
+    if st:
+        _raise(st, "kda_state_summary")
+    return E, P
+
+
+def kda_apply_state_summary(state_ext, transition, initial_state=None, out=None):
+    """final = transition . initial_state + state_ext (state_ext when initial_state is None)."""
+    _dev(state_ext, "state_ext", dtype=torch.float32)
+    if state_ext.dim() != 4:
+        raise ValueError("state_ext must be [B,H,K,V]")
+    B, H, K, V = state_ext.shape
+    _dev(transition, "transition", dtype=torch.float32, shape=(B, H, K, K))
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", dtype=torch.float32, shape=(B, H, K, V))
+    out = torch.empty_like(state_ext) if out is None else out
+    _dev(out, "out", dtype=torch.float32, shape=(B, H, K, V))
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = load_library().kda_apply_state_summary(B, H, K, V, ptr(state_ext), ptr(transition),
+                                                ptr(initial_state), ptr(out),
+                                                _stream_ptr(state_ext.device))
+    if st:
+        _raise(st, "kda_apply_state_summary")
+    return out
+
+
+def chunk_table(T, chunk_size=64, cu_seqlens=None, B=1, cu_seqlens_host=None, device="cuda"):
+    """The device chunk table: (tok, len, seq_chunk0) as CPU int32 tensors."""
+    lib = load_library()
+    cu, host, N, host_ptr = _cu_args(cu_seqlens, cu_seqlens_host, T)
+    if N is None:
+        N = B
+    p = make_problem(B, T, 1, 64, 64, KDA_BF16, None, None, chunk_size, N,
+                     None if cu is None else cu.data_ptr(), host_ptr)
+    st = ctypes.c_int(0)
+    cap = lib.kda_chunk_capacity(ctypes.byref(p), ctypes.byref(st))
+    if st.value:
+        _raise(st.value, "kda_chunk_capacity")
+    dev = torch.device(device) if cu is None else cu.device
+    tok = torch.full((max(cap, 1),), -1, dtype=torch.int32, device=dev)
+    ln = torch.full((max(cap, 1),), -1, dtype=torch.int32, device=dev)
+    seq0 = torch.full((N + 1,), -1, dtype=torch.int32, device=dev)
+    cnt = torch.zeros((1,), dtype=torch.int32, device=dev)
+    st = lib.kda_chunk_table(ctypes.byref(p), tok.data_ptr(), ln.data_ptr(), seq0.data_ptr(),
+                             cnt.data_ptr(), cap, _stream_ptr(dev))
+    if st:
+        _raise(st, "kda_chunk_table")
+    n = int(cnt.item())
+    return tok[:n].cpu(), ln[:n].cpu(), seq0.cpu()

@@ -1,0 +1,206 @@
+/*
+ * kda.h -- C ABI of the KDA (Kimi Delta Attention) chunked forward for AMD
+ * MI355X (gfx950).  Library: libkda.so.
+ *
+ * KDA is a gated delta-rule linear attention with a per-key-channel decay.
+ * Per sequence n and head h the recurrent state S is a K x V fp32 matrix
+ * (row = key channel, column = value channel) and, token by token,
+ *
+ *     q^ = q / sqrt(sum q^2 + 1e-6),     k^ likewise            (in-kernel L2 norm)
+ *     x_c = gate_c + dt_bias[h,c],       A = exp(a_log[h])
+ *     g_c = -A * softplus(x_c)                 when lower_bound is unset
+ *     g_c = lower_bound * sigmoid(A * x_c)     when lower_bound < 0 (safe gate)
+ *     beta = sigmoid(beta_logit)                                  (in-kernel sigmoid)
+ *     S_t = (I - beta k^ k^T) Diag(exp g) S_{t-1} + beta k^ v^T
+ *     o_t = scale * S_t^T q^
+ *
+ * The entry points mirror the chunk_kda call and the affine state-summary pair
+ * on the hyper_parallel coverage page for
+ * context_parallel/kimi_delta_attention.py (`_run_local_kda`,
+ * `_eager_kda_state_p2p`, `_validate_projected_inputs`), and take document
+ * boundaries as cu_seqlens like the NeMo AutoModel page
+ * "nemo_automodel.components.models.kimi_k3.cp" (module introduction,
+ * `doc_ids_from_cu_seqlens`).  The gate formula is not printed on the pages;
+ * the two forms above are this library's reading of the in-kernel gate and of
+ * the lower-bounded gate parameterisation.
+ *
+ * Conventions for every entry point
+ *  - All tensors are dense, contiguous, token-major ("token-first"):
+ *      q, k, gate : [B, T, H, K]     v, o : [B, T, H, V]     beta : [B, T, H]
+ *      a_log      : [H]    fp32      dt_bias : [H, K] fp32
+ *      states     : [N, H, K, V] fp32      transitions : [B, H, K, K] fp32
+ *    q, k, v, gate, beta and o share one dtype (kda_dtype).
+ *  - Every tensor pointer is a device pointer unless its name ends in _host.
+ *  - The caller owns and allocates all memory, including the workspace.  The
+ *    library allocates nothing, keeps no state between calls, never frees and
+ *    never synchronises the stream.  Kernels are enqueued on `stream`
+ *    (a hipStream_t; NULL = the default stream) and may still be running when
+ *    the call returns.
+ *  - Arguments are validated on the host before anything is enqueued; on any
+ *    non-OK status nothing was launched and kda_last_error() describes why.
+ *  - One head layout: the number of value heads equals the number of key heads.
+ *  - Not thread-safe across concurrent calls that share a workspace.
+ */
+#ifndef KDA_H_
+#define KDA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_EINVAL = 1,        /* malformed argument (null pointer, bad shape, bad cu_seqlens, ...) */
+  KDA_EUNSUPPORTED = 2,  /* well-formed but outside what this build implements          */
+  KDA_EWORKSPACE = 3,    /* workspace missing or smaller than *_workspace_size()        */
+  KDA_EHIP = 4           /* a HIP launch failed                                          */
+} kda_status;
+
+/*
+ * One problem description, shared by kda_fwd and kda_state_summary.
+ *
+ *  B, T, H, K, V  shapes above.  T >= 0, B >= 1, H >= 1; K and V in {64, 128}.
+ *  dtype          element type of q, k, v, gate, beta and o.
+ *  scale          output scale; any value that is not > 0 (0, negative, NaN)
+ *                 selects the default 1/sqrt(K) ("scale=None" of chunk_kda).
+ *  lower_bound    NaN = unset (softplus gate); otherwise it must be < 0
+ *                 ("lower_bound must be negative", KimiDeltaAttentionUlyssesCP
+ *                 constructor on the hyper_parallel page).
+ *  chunk_size     tokens per chunk: 16, 32 or 64 (default of the pages: 64).
+ *                 <= 0 is KDA_EINVAL ("chunk_size must be positive"); other
+ *                 positive values are KDA_EUNSUPPORTED.  The result does not
+ *                 depend on it beyond rounding.
+ *  cu_seqlens     NULL: every row b is one sequence (N = B).  Otherwise B must
+ *                 be 1 and it holds N+1 int32 offsets into the row with
+ *                 cu[0] = 0, cu[N] = T, non-decreasing (empty documents are
+ *                 allowed); the state restarts at every document start.
+ *                 Device pointer.
+ *  cu_seqlens_host  optional host copy of the same N+1 offsets.  When given,
+ *                 the offsets are validated (KDA_EINVAL on a violation,
+ *                 including the negative padding sentinels some packers use)
+ *                 and the launch is sized exactly.  When NULL the caller
+ *                 guarantees validity; malformed device offsets are clamped
+ *                 into range on the device so that no access leaves the
+ *                 buffers, and the results are then unspecified.
+ *  N              number of sequences: B without cu_seqlens, else len-1.
+ */
+typedef struct kda_problem {
+  int32_t B, T, H, K, V;
+  int32_t dtype;
+  float scale;
+  float lower_bound;
+  int32_t chunk_size;
+  int32_t N;
+  const int32_t* cu_seqlens;
+  const int32_t* cu_seqlens_host;
+} kda_problem;
+
+/* Host-only validation of a problem; launches nothing, touches no device. */
+kda_status kda_validate(const kda_problem* p);
+
+/* Bytes of device workspace kda_fwd needs for this problem (0 on a bad problem,
+ * with the status in *status when status is not NULL).  The size depends only
+ * on the shapes, dtype, chunk_size and, without a host copy of cu_seqlens, on
+ * N through an upper bound of the chunk count. */
+size_t kda_fwd_workspace_size(const kda_problem* p, kda_status* status);
+
+/*
+ * Chunked KDA forward (the chunk_kda call of `_run_local_kda` /
+ * `_eager_kda_state_p2p` with use_qk_l2norm_in_kernel, use_gate_in_kernel and
+ * use_beta_sigmoid_in_kernel all on).
+ *
+ *  q, k, v, gate, beta   inputs, dtype p->dtype, layouts above.
+ *  a_log [H], dt_bias [H,K]   fp32 gate parameters.
+ *  initial_state         [N,H,K,V] fp32, or NULL for zeros.
+ *  o                     [B,T,H,V] output, dtype p->dtype (required).
+ *  final_state           [N,H,K,V] fp32 output, or NULL to not produce it
+ *                        (output_final_state=False).  With cu_seqlens, entry n
+ *                        is document n's state after its last token; an empty
+ *                        document returns its initial state.
+ *  workspace             device buffer of at least kda_fwd_workspace_size()
+ *                        bytes, 256-byte aligned; contents need not be cleared.
+ * Returns KDA_OK once every kernel is enqueued on `stream`.
+ */
+kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const void* v,
+                   const void* gate, const void* beta, const float* a_log,
+                   const float* dt_bias, const float* initial_state, void* o,
+                   float* final_state, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * kda_fwd with per-stage timing hooks, for measurement.  It does exactly the
+ * work of kda_fwd; in addition, when stage_events is not NULL it must hold
+ * 2 * KDA_NUM_STAGES hipEvent_t handles created by the caller (entries may be
+ * NULL), and the library records stage_events[2*i] on `stream` just before
+ * stage i is enqueued and stage_events[2*i+1] just after.  Stages, in order:
+ *   0 chunk table, 1 per-token prologue, 2 chunk-local factors,
+ *   3 state pass and output.
+ * A stage that the chosen kernels fold into another records both events back
+ * to back.
+ */
+#define KDA_NUM_STAGES 4
+kda_status kda_fwd_profiled(const kda_problem* p, const void* q, const void* k, const void* v,
+                            const void* gate, const void* beta, const float* a_log,
+                            const float* dt_bias, const float* initial_state, void* o,
+                            float* final_state, void* workspace, size_t workspace_bytes,
+                            void* stream, void* const* stage_events);
+
+/* Workspace bytes for kda_state_summary. */
+size_t kda_state_summary_workspace_size(const kda_problem* p, kda_status* status);
+
+/*
+ * Affine summary of each row as a contiguous slice (torch_kda_state_summary in
+ * `_eager_kda_state_p2p` on the hyper_parallel page): the row's effect on the
+ * state is  final = transition . initial + state_ext,  with
+ *  state_ext  [B,H,K,V] fp32 = the row's final state from a zero initial state,
+ *  transition [B,H,K,K] fp32 = the ordered product over the row's tokens of
+ *             (I - beta k^ k^T) Diag(exp g), later tokens on the left.
+ * p->cu_seqlens must be NULL (a slice summary has no document resets; the
+ * pages' state-CP adapters reject cu_seqlens as well).  No output o is made.
+ */
+kda_status kda_state_summary(const kda_problem* p, const void* q, const void* k, const void* v,
+                             const void* gate, const void* beta, const float* a_log,
+                             const float* dt_bias, float* state_ext, float* transition,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * final_state = transition . initial_state + state_ext for each of the B*H
+ * (row, head) pairs (torch_apply_kda_state_summary on the hyper_parallel
+ * page); initial_state may be NULL (rank 0 of a state-parallel chain), then
+ * final_state = state_ext.  All fp32, shapes [B,H,K,V] and [B,H,K,K].
+ * final_state may alias state_ext (in-place update); it may not alias
+ * transition or initial_state.
+ */
+kda_status kda_apply_state_summary(int32_t B, int32_t H, int32_t K, int32_t V,
+                                   const float* state_ext, const float* transition,
+                                   const float* initial_state, float* final_state, void* stream);
+
+/*
+ * The chunk table kda_fwd builds on the device, written into caller buffers so
+ * that it can be inspected.  Every sequence is cut into chunks of chunk_size
+ * tokens starting at the sequence's own first token (so the last chunk of a
+ * document may be partial and the next document starts a new chunk):
+ *  tok        [cap] flat token index (b*T + t) of each chunk's first token
+ *  len        [cap] tokens in each chunk (1..chunk_size)
+ *  seq_chunk0 [N+1] index of each sequence's first chunk; seq_chunk0[N] = count
+ *  count      [1]   number of chunks
+ * cap must be at least kda_chunk_capacity(p).  Device pointers.
+ */
+int32_t kda_chunk_capacity(const kda_problem* p, kda_status* status);
+kda_status kda_chunk_table(const kda_problem* p, int32_t* tok, int32_t* len, int32_t* seq_chunk0,
+                           int32_t* count, int32_t cap, void* stream);
+
+/* Message for the last non-OK status returned on the calling thread ("" if none). */
+const char* kda_last_error(void);
+
+/* Library version, (major << 16) | minor. */
+int32_t kda_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H_ */

@@ -1,0 +1,182 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads, exports
+every entry point include/kda.h declares, and rejects malformed problems with
+the documented status before anything is launched."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+import torch
+
+from gated_delta_rule_43_amd import kda
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+FAKE = 0x100000  # a non-NULL pointer that validation never dereferences
+
+
+def _declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return kda.load_library()
+
+
+def test_library_exports_every_declared_symbol(lib):
+    names = _declared_functions()
+    assert "kda_fwd" in names and "kda_state_summary" in names and "kda_apply_state_summary" in names
+    for n in names:
+        assert hasattr(lib, n), "libkda.so does not export %s" % n
+    assert set(kda.EXPORTED) == set(names)
+    assert lib.kda_version() >= 1
+
+
+def _p(**kw):
+    base = dict(B=1, T=256, H=2, K=64, V=64, dtype=kda.KDA_BF16, scale=None, lower_bound=None,
+                chunk_size=64, N=None)
+    base.update(kw)
+    return kda.make_problem(**base)
+
+
+def _status(lib, p):
+    return lib.kda_validate(ctypes.byref(p)), lib.kda_last_error().decode()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(chunk_size=0), kda.EINVAL, "chunk_size must be positive"),
+    (dict(chunk_size=-64), kda.EINVAL, "chunk_size must be positive"),
+    (dict(chunk_size=48), kda.EUNSUPPORTED, "chunk_size 48"),
+    (dict(chunk_size=128), kda.EUNSUPPORTED, "chunk_size 128"),
+    (dict(lower_bound=0.0), kda.EINVAL, "lower_bound must be negative"),
+    (dict(lower_bound=2.5), kda.EINVAL, "lower_bound must be negative"),
+    (dict(lower_bound=-math.inf), kda.EINVAL, "lower_bound must be negative"),
+    (dict(K=96), kda.EUNSUPPORTED, "head dims"),
+    (dict(V=32), kda.EUNSUPPORTED, "head dims"),
+    (dict(B=0), kda.EINVAL, "bad shape"),
+    (dict(T=-1), kda.EINVAL, "bad shape"),
+    (dict(H=0), kda.EINVAL, "bad shape"),
+    (dict(dtype=7), kda.EINVAL, "dtype"),
+    (dict(N=3), kda.EINVAL, "N must equal B"),
+])
+def test_validation_rejects(lib, kw, status, msg):
+    st, err = _status(lib, _p(**kw))
+    assert st == status and msg in err, (st, err)
+
+
+def test_validation_accepts(lib):
+    for kw in (dict(), dict(lower_bound=-5.0), dict(chunk_size=16), dict(chunk_size=32),
+               dict(K=128, V=64), dict(T=0), dict(dtype=kda.KDA_F32, scale=0.125)):
+        st, err = _status(lib, _p(**kw))
+        assert st == kda.OK, (kw, err)
+
+
+def _cu_problem(cu, T=None, B=1):
+    host = (ctypes.c_int32 * len(cu))(*cu)
+    p = _p(B=B, T=T if T is not None else cu[-1], N=len(cu) - 1, cu_seqlens_ptr=FAKE,
+           cu_seqlens_host_ptr=ctypes.addressof(host))
+    return p, host
+
+
+@pytest.mark.parametrize("cu,T,B,msg", [
+    ([0, 5, 3, 10], 10, 1, "non-decreasing"),
+    ([0, 5, -1, 10], 10, 1, "negative"),
+    ([1, 5, 10], 10, 1, "cu_seqlens[0] must be 0"),
+    ([0, 5, 9], 10, 1, "must equal T"),
+    ([0, 5, 10], 10, 2, "B == 1"),
+])
+def test_cu_seqlens_rejected(lib, cu, T, B, msg):
+    p, host = _cu_problem(cu, T, B)
+    st, err = _status(lib, p)
+    assert st == kda.EINVAL and msg in err, (st, err)
+
+
+def test_cu_seqlens_accepted_and_chunk_count_exact(lib):
+    cu = [0, 0, 1, 65, 65, 200]          # empty docs, a 1-token doc, a 64-token doc
+    p, host = _cu_problem(cu)
+    st = ctypes.c_int(0)
+    n = lib.kda_chunk_capacity(ctypes.byref(p), ctypes.byref(st))
+    assert st.value == kda.OK
+    assert n == sum(math.ceil((b - a) / 64) for a, b in zip(cu[:-1], cu[1:]))
+    # without the host copy the capacity is the bound floor(T/C) + N
+    p2 = _p(T=200, N=5, cu_seqlens_ptr=FAKE)
+    assert lib.kda_chunk_capacity(ctypes.byref(p2), ctypes.byref(st)) == 200 // 64 + 5
+
+
+def test_summary_rejects_cu_seqlens(lib):
+    p, host = _cu_problem([0, 5, 10])
+    st = ctypes.c_int(0)
+    assert lib.kda_state_summary_workspace_size(ctypes.byref(p), ctypes.byref(st)) == 0
+    assert st.value == kda.EINVAL
+
+
+def test_workspace_size_scales_with_problem(lib):
+    st = ctypes.c_int(0)
+    small = lib.kda_fwd_workspace_size(ctypes.byref(_p(T=64)), ctypes.byref(st))
+    big = lib.kda_fwd_workspace_size(ctypes.byref(_p(T=4096)), ctypes.byref(st))
+    assert st.value == kda.OK and 0 < small < big
+    bad = lib.kda_fwd_workspace_size(ctypes.byref(_p(chunk_size=0)), ctypes.byref(st))
+    assert bad == 0 and st.value == kda.EINVAL
+
+
+def test_fwd_rejects_before_launch(lib):
+    p = _p()
+    args = [FAKE] * 5 + [FAKE, FAKE, None, FAKE, None]
+    # no workspace
+    st = lib.kda_fwd(ctypes.byref(p), *args, None, 0, None)
+    assert st == kda.EWORKSPACE and "workspace" in lib.kda_last_error().decode()
+    # too small a workspace
+    st = lib.kda_fwd(ctypes.byref(p), *args, FAKE, 256, None)
+    assert st == kda.EWORKSPACE
+    # NULL input
+    bad = list(args)
+    bad[0] = None
+    st = lib.kda_fwd(ctypes.byref(p), *bad, FAKE, 1 << 40, None)
+    assert st == kda.EINVAL and "non-NULL" in lib.kda_last_error().decode()
+    # NULL output
+    bad = list(args)
+    bad[8] = None
+    st = lib.kda_fwd(ctypes.byref(p), *bad, FAKE, 1 << 40, None)
+    assert st == kda.EINVAL
+    # misaligned workspace
+    st = lib.kda_fwd(ctypes.byref(p), *args, FAKE + 8, 1 << 40, None)
+    assert st == kda.EINVAL and "aligned" in lib.kda_last_error().decode()
+    # misaligned bf16 input
+    bad = list(args)
+    bad[1] = FAKE + 1
+    st = lib.kda_fwd(ctypes.byref(p), *bad, FAKE, 1 << 40, None)
+    assert st == kda.EINVAL
+
+
+def test_apply_summary_rejects(lib):
+    st = lib.kda_apply_state_summary(1, 2, 64, 64, FAKE, FAKE, FAKE, FAKE, None)
+    assert st == kda.EINVAL and "alias" in lib.kda_last_error().decode()
+    st = lib.kda_apply_state_summary(1, 2, 96, 64, FAKE, FAKE, None, FAKE + 4096, None)
+    assert st == kda.EUNSUPPORTED
+    st = lib.kda_apply_state_summary(1, 2, 64, 64, None, FAKE, None, FAKE, None)
+    assert st == kda.EINVAL
+
+
+def test_python_binding_rejects_host_tensors():
+    """The binding refuses CPU tensors before anything reaches the library."""
+    B, T, H, K = 1, 8, 2, 64
+    q = torch.zeros(B, T, H, K, dtype=torch.bfloat16)
+    v = torch.zeros(B, T, H, K, dtype=torch.bfloat16)
+    beta = torch.zeros(B, T, H, dtype=torch.bfloat16)
+    a_log = torch.zeros(H)
+    dt = torch.zeros(H, K)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.kda_fwd(q, q, v, q, beta, a_log, dt)
+    with pytest.raises(ValueError, match="rank-4"):
+        kda.kda_fwd(q[0], q, v, q, beta, a_log, dt)
+    with pytest.raises(ValueError, match="beta must have shape"):
+        kda.kda_fwd(q, q, v, q, beta[:, :4], a_log, dt)
+    with pytest.raises(ValueError, match="a_log must contain"):
+        kda.kda_fwd(q, q, v, q, beta, torch.zeros(3), dt)
+    with pytest.raises(NotImplementedError):
+        kda.kda_fwd(q, q, torch.zeros(B, T, 4, K, dtype=torch.bfloat16), torch.zeros(B, T, 4, K),
+                    torch.zeros(B, T, 4), torch.zeros(4), torch.zeros(4, K))
