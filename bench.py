@@ -115,31 +115,42 @@ def stage_bytes(w, stage, NT, N):
 
 
 def cpu_baseline(inp, w, budget_s=12.0):
-    """The oracle as it stands on a bounded sample: row 0, a few heads, the
-    first tokens of the row; scaled to Mtokens/s of the full H-head workload."""
+    """The oracle as it stands on a bounded sample of the workload: whole rows
+    (all tokens) of a growing number of (row, head) pairs, sized from a short
+    probe to take about budget_s; scaled to Mtokens/s of the full H-head rows."""
     import oracle
     threads = oracle.default_threads()
-    heads = list(range(min(w.H, max(1, threads))))
-    # calibrate on a short prefix, then size the sample for ~budget_s
-    def run(T):
-        cut = lambda t: t[:1, :T][:, :, heads].float().cpu().numpy()
-        args = [cut(inp[x]) for x in ("q", "k", "v", "gate")]
-        beta = inp["beta"][:1, :T][:, :, heads].float().cpu().numpy()
-        a_log = inp["a_log"][heads].cpu().numpy()
-        dt_bias = inp["dt_bias"][heads].cpu().numpy()
-        t0 = time.perf_counter()
-        oracle.kda_fwd(*args, beta, a_log, dt_bias, scale=w.scale, lower_bound=w.lower_bound,
-                       threads=threads)
-        return time.perf_counter() - t0
-    t_probe = 256
-    dt = run(t_probe)
-    T = int(min(w.T, max(t_probe, t_probe * budget_s / max(dt, 1e-6))))
-    dt = run(T)
-    token_heads = T * len(heads)
-    mtok = token_heads / w.H / dt / 1e6
-    return {"value": mtok, "unit": "Mtokens/s", "cores": threads, "kind": "oracle",
-            "sample": "row 0, heads 0..%d, first %d tokens (%d token-heads, %.1f s), fp64 "
-                      "token recurrence, scaled to %d heads" % (len(heads) - 1, T, token_heads, dt, w.H)}
+    pairs_all = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def run(npairs, T):
+        rows = sorted(set(b for b, _ in pairs_all[:npairs]))
+        secs = 0.0
+        done = 0
+        for b in rows:
+            heads = [h for bb, h in pairs_all[:npairs] if bb == b]
+            cut = lambda t: t[b:b + 1, :T][:, :, heads].float().cpu().numpy()
+            args = [cut(inp[x]) for x in ("q", "k", "v", "gate", "beta")]
+            t0 = time.perf_counter()
+            oracle.kda_fwd(*args, inp["a_log"][heads].cpu().numpy(),
+                           inp["dt_bias"][heads].cpu().numpy(), scale=w.scale,
+                           lower_bound=w.lower_bound, threads=threads, output_final_state=False)
+            secs += time.perf_counter() - t0
+            done += T * len(heads)
+        return secs, done
+
+    probe_pairs = min(len(pairs_all), threads)
+    dt, _ = run(probe_pairs, 512)
+    per_th = dt / (probe_pairs * 512)              # seconds per token-head at this parallelism
+    npairs = probe_pairs
+    while npairs < len(pairs_all) and per_th * npairs * w.T < budget_s * 0.5:
+        npairs = min(len(pairs_all), npairs + threads)
+    T = int(min(w.T, max(512, budget_s / max(per_th * npairs, 1e-12))))
+    secs, token_heads = run(npairs, T)
+    mtok = token_heads / w.H / secs / 1e6
+    return {"value": round(mtok, 6), "unit": "Mtokens/s", "cores": threads, "kind": "oracle",
+            "sample": "%d (row, head) pairs x first %d tokens = %d token-heads in %.1f s; fp64 "
+                      "token recurrence, rate scaled to %d heads per token"
+                      % (npairs, T, token_heads, secs, w.H)}
 
 
 def main():
