@@ -97,20 +97,26 @@ def algorithmic(w):
     return bytes_th, flops_th
 
 
+def record_bytes(K, V):
+    """Bytes of one chunk record of the MFMA path (per chunk-head): Qt, W and
+    Kbar^T fragments (C*K bf16 each), Aqk fragments (C*C bf16), gL (K fp32) and
+    U tiles (C*V bf16)."""
+    C = 64
+    return 3 * C * K * 2 + C * C * 2 + K * 4 + C * V * 2
+
+
 def stage_bytes(w, stage, NT, N):
-    """Algorithmic (unique) HBM bytes one launch of a stage moves: what it must
-    read and write at least, given the workspace format of the current kernels."""
-    B, T, H, K, V, C = w.B, w.T, w.H, w.K, w.V, w.chunk_size
+    """Algorithmic (unique) HBM bytes one launch of a stage must move: every
+    input element read once, every output element written once."""
+    B, T, H, K, V = w.B, w.T, w.H, w.K, w.V
     ein = 2 if w.dtype == "bf16" else 4
-    ews = 4                      # chunk factors are stored in fp32 by the current kernels
     tokh = B * T * H
-    per_chunk = C * (3 * K + V + C) * ews + K * 4   # W, Qt, Kb, U, Aqk, gL
-    if stage == 1:   # prologue: q,k,gate,beta in -> qn,kn,g,beta fp32 out
-        return tokh * ((3 * K + 1) * ein + (3 * K + 1) * 4)
-    if stage == 2:   # chunk factors: qn,kn,g,beta,v in -> factors out
-        return tokh * ((3 * K + 1) * 4 + V * ein) + NT * H * per_chunk
-    if stage == 3:   # state pass: factors in, o out, states
-        return NT * H * per_chunk + tokh * V * ein + N * H * K * V * 4
+    rec = record_bytes(K, V)
+    states = N * H * K * V * 4 * ((1 if w.init_std is not None else 0) + (1 if w.output_final_state else 0))
+    if stage == 2:   # chunk factors: q, k, gate, v, beta in -> one record per chunk-head out
+        return tokh * (3 * K + V + 1) * ein + NT * H * rec
+    if stage == 3:   # state pass: records in, o out, initial/final states
+        return NT * H * rec + tokh * V * ein + states
     return 0
 
 

@@ -6,6 +6,8 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
+#include <cstring>
 #include <string>
 
 #include "kda_internal.h"
@@ -74,12 +76,22 @@ kda_status validate_problem(const kda_problem* p, bool summary) {
   return KDA_OK;
 }
 
+// Which kernels run: the MFMA path for bf16 with 64-token chunks, the fp32
+// VALU path otherwise.  KDA_PATH=valu forces the VALU path (for comparisons).
+bool use_mfma(const kda_problem* p) {
+  const char* env = std::getenv("KDA_PATH");
+  if (env && std::strcmp(env, "valu") == 0) return false;
+  return p->dtype == KDA_BF16 && p->chunk_size == 64;
+}
+
 struct Layout {
   int NT = 0;
   int exact = 1;
+  bool mfma = false;
   size_t off_tok = 0, off_len = 0, off_seq0 = 0, off_nt = 0;
   size_t off_qn = 0, off_kn = 0, off_g = 0, off_bt = 0;
   size_t off_W = 0, off_U = 0, off_Qt = 0, off_Kb = 0, off_Aqk = 0, off_gL = 0;
+  size_t off_rec = 0;
   size_t total = 0;
 };
 
@@ -102,6 +114,7 @@ int chunk_count(const kda_problem* p, int* exact) {
 Layout layout(const kda_problem* p) {
   Layout L;
   L.NT = chunk_count(p, &L.exact);
+  L.mfma = use_mfma(p);
   const size_t NT = (size_t)L.NT, H = p->H, K = p->K, V = p->V, C = p->chunk_size, N = p->N;
   const size_t tokh = (size_t)p->B * p->T * H;
   size_t o = 0;
@@ -114,17 +127,22 @@ Layout layout(const kda_problem* p) {
   L.off_len = take(NT * 4);
   L.off_seq0 = take((N + 1) * 4);
   L.off_nt = take(4);
-  L.off_qn = take(tokh * K * 4);
-  L.off_kn = take(tokh * K * 4);
-  L.off_g = take(tokh * K * 4);
-  L.off_bt = take(tokh * 4);
-  const size_t elt = 4;
-  L.off_W = take(NT * H * C * K * elt);
-  L.off_U = take(NT * H * C * V * elt);
-  L.off_Qt = take(NT * H * C * K * elt);
-  L.off_Kb = take(NT * H * C * K * elt);
-  L.off_Aqk = take(NT * H * C * C * elt);
-  L.off_gL = take(NT * H * K * 4);
+  if (L.mfma) {
+    // one record of MFMA-ready chunk factors per chunk-head
+    L.off_rec = take(NT * H * kda::mfma_record_bytes(p->K, p->V));
+  } else {
+    L.off_qn = take(tokh * K * 4);
+    L.off_kn = take(tokh * K * 4);
+    L.off_g = take(tokh * K * 4);
+    L.off_bt = take(tokh * 4);
+    const size_t elt = 4;
+    L.off_W = take(NT * H * C * K * elt);
+    L.off_U = take(NT * H * C * V * elt);
+    L.off_Qt = take(NT * H * C * K * elt);
+    L.off_Kb = take(NT * H * C * K * elt);
+    L.off_Aqk = take(NT * H * C * C * elt);
+    L.off_gL = take(NT * H * K * 4);
+  }
   L.total = o;
   return L;
 }
@@ -144,18 +162,27 @@ kda::FwdArgs make_args(const kda_problem* p, const Layout& L, void* ws) {
   a.chunk_len = (int32_t*)(w + L.off_len);
   a.seq_chunk0 = (int32_t*)(w + L.off_seq0);
   a.nt_dev = (int32_t*)(w + L.off_nt);
-  a.qn = (float*)(w + L.off_qn);
-  a.kn = (float*)(w + L.off_kn);
-  a.g = (float*)(w + L.off_g);
-  a.bt = (float*)(w + L.off_bt);
-  a.ws_bf16 = 0;
-  a.W = w + L.off_W;
-  a.U = w + L.off_U;
-  a.Qt = w + L.off_Qt;
-  a.Kb = w + L.off_Kb;
-  a.Aqk = w + L.off_Aqk;
-  a.gL = (float*)(w + L.off_gL);
+  if (L.mfma) {
+    a.rec = w + L.off_rec;
+  } else {
+    a.qn = (float*)(w + L.off_qn);
+    a.kn = (float*)(w + L.off_kn);
+    a.g = (float*)(w + L.off_g);
+    a.bt = (float*)(w + L.off_bt);
+    a.W = w + L.off_W;
+    a.U = w + L.off_U;
+    a.Qt = w + L.off_Qt;
+    a.Kb = w + L.off_Kb;
+    a.Aqk = w + L.off_Aqk;
+    a.gL = (float*)(w + L.off_gL);
+  }
   return a;
+}
+
+hipError_t launch(const kda::FwdArgs& a, const Layout& L, hipStream_t s) {
+  hipError_t e = kda::launch_chunk_table(a, s);
+  if (e != hipSuccess) return e;
+  return L.mfma ? kda::launch_mfma_path(a, s) : kda::launch_valu_path(a, s);
 }
 
 bool aligned(const void* ptr, size_t a) { return ((uintptr_t)ptr % a) == 0; }
@@ -221,6 +248,12 @@ kda_status kda_fwd_profiled(const kda_problem* p, const void* q, const void* k, 
   const Layout L = layout(p);
   st = check_ws(L.total, workspace, workspace_bytes);
   if (st != KDA_OK) return st;
+  if (L.mfma) {
+    const void* vec[] = {q, k, v, gate, o};
+    for (const void* ptr : vec)
+      if (ptr && !aligned(ptr, 16))
+        return fail(KDA_EINVAL, "bf16 q, k, v, gate and o must be 16-byte aligned");
+  }
 
   kda::FwdArgs a = make_args(p, L, workspace);
   a.q = q; a.k = k; a.v = v; a.gate = gate; a.beta = beta;
@@ -228,8 +261,7 @@ kda_status kda_fwd_profiled(const kda_problem* p, const void* q, const void* k, 
   a.o = o; a.fin = final_state; a.summary = 0;
   a.events = stage_events;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = kda::launch_chunk_table(a, s);
-  if (e == hipSuccess) e = kda::launch_valu_path(a, s);
+  hipError_t e = launch(a, L, s);
   if (e != hipSuccess) return fail(KDA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   g_last_error.clear();
   return KDA_OK;
@@ -256,14 +288,19 @@ kda_status kda_state_summary(const kda_problem* p, const void* q, const void* k,
   const Layout L = layout(p);
   st = check_ws(L.total, workspace, workspace_bytes);
   if (st != KDA_OK) return st;
+  if (L.mfma) {
+    const void* vec[] = {q, k, v, gate};
+    for (const void* ptr : vec)
+      if (ptr && !aligned(ptr, 16))
+        return fail(KDA_EINVAL, "bf16 q, k, v and gate must be 16-byte aligned");
+  }
   kda::FwdArgs a = make_args(p, L, workspace);
   a.q = q; a.k = k; a.v = v; a.gate = gate; a.beta = beta;
   a.a_log = a_log; a.dt_bias = dt_bias; a.init = nullptr;
   a.o = nullptr; a.fin = nullptr; a.summary = 1;
   a.state_ext = state_ext; a.transition = transition;
   hipStream_t s = (hipStream_t)stream;
-  hipError_t e = kda::launch_chunk_table(a, s);
-  if (e == hipSuccess) e = kda::launch_valu_path(a, s);
+  hipError_t e = launch(a, L, s);
   if (e != hipSuccess) return fail(KDA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   g_last_error.clear();
   return KDA_OK;

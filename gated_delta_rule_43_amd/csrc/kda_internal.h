@@ -65,6 +65,8 @@ struct FwdArgs {
   int ws_bf16;
   void *W, *U, *Qt, *Kb, *Aqk;
   float* gL;
+  // workspace: per chunk-head records of the MFMA path
+  void* rec;
   // optional stage timing: hipEvent_t handles, [2 * kNumStages], entries may be null
   void* const* events;
 };
@@ -79,6 +81,8 @@ inline void mark(const FwdArgs& a, int stage, int end, hipStream_t s) {
 // Kernel launchers (return the first HIP error, hipSuccess otherwise).
 hipError_t launch_chunk_table(const FwdArgs& a, hipStream_t s);
 hipError_t launch_valu_path(const FwdArgs& a, hipStream_t s);
+hipError_t launch_mfma_path(const FwdArgs& a, hipStream_t s);
+size_t mfma_record_bytes(int K, int V);
 hipError_t launch_apply_summary(int B, int H, int K, int V, const float* E, const float* P,
                                 const float* S0, float* F, hipStream_t s);
 

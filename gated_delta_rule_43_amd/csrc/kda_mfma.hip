@@ -1,0 +1,716 @@
+// MFMA path of the KDA chunked forward (bf16 inputs, chunk 64, K,V in {64,128}).
+//
+// Two kernels:
+//   k_chunk_mfma  one workgroup (4 waves) per chunk-head, all chunks in
+//                 parallel.  Fuses the prologue (q/k L2 norm, in-kernel gate,
+//                 beta sigmoid, chunk-local cumulative log-decay) with the
+//                 chunk-local WY/UT factors, and writes one "chunk record" per
+//                 chunk-head whose operands are already laid out as MFMA
+//                 fragments for the state pass.
+//   k_state_mfma  one workgroup per (sequence, head, column tile), sequential
+//                 over the sequence's chunks.  The fp32 state lives in MFMA
+//                 accumulators; per chunk
+//                     X = W S,  Y = Qt S,  Delta = U - X,
+//                     O = Y + Aqk Delta,  S <- Diag(gL) S + Kbar^T Delta.
+//
+// Chunk algebra (derived from the token recurrence, see kda_valu.hip):
+//   Akk[r,i] = sum_c k^_rc k^_ic e^{gamma_rc-gamma_ic} (i<r), Aqk likewise with
+//   q^ (i<=r), Tm = (I + Diag(beta) Akk)^-1, W = Tm Diag(beta)(K^ e^gamma),
+//   U = Tm Diag(beta) V, Qt = scale Q^ e^gamma, Kbar = K^ e^{gamma_L-gamma},
+//   gL = e^{gamma_L}, Aqk scaled by `scale` and masked to i <= r.
+//
+// Decay factors.  Rows of a chunk form four 16-row blocks b.  With lambda the
+// cumulative log-decay from the start of a row's own block, Lam_b the block
+// total and Gam_b the sum of the totals of the blocks before b:
+//   e^{gamma_r - gamma_i} = e^{lambda_r} * e^{Gam_R - Gam_{I+1}} * e^{Lam_I - lambda_i}
+// for rows r in block R and i in an earlier block I: three factors <= 1, so
+// nothing overflows.  Inside one block (I = R) the split is
+//   e^{lambda_r} * (e^{Lam_R - lambda_i} e^{-Lam_R}),
+// whose second factor is >= 1; it is used while the block's total decay stays
+// below 80 in every channel (e^80 fits bf16/fp32), and an exact per-pair path
+// takes over otherwise.
+//
+// MFMA: v_mfma_f32_16x16x32_bf16.  Lane l = 16 g + n (g = l/16, n = l%16):
+//   A operand  lane holds A[n][8g + e], e = 0..7      (m = n, k = 8g+e)
+//   B operand  lane holds B[8g + e][n]
+//   C/D        lane holds D[4g + e][n], e = 0..3
+// A k-step of 32 uses the k order sigma(g, e) = e<4 ? 4g+e : 16+4g+(e-4): two
+// accumulator tiles (rows 0-15 and 16-31) then give a B operand, and a matrix
+// product with a 0/1 selection matrix turns "one row, 8 columns per lane"
+// registers into accumulator layout (a transpose on the matrix cores).
+#include "kda_internal.h"
+
+namespace kda {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kC = 64;
+constexpr int kThreads = 256;
+constexpr float kDiagSafe = 80.f;  // largest in-block decay the factorised diagonal accepts
+constexpr float kGateFloor = -110.f;
+
+__device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+__device__ __forceinline__ int sig(int g, int e) { return e < 4 ? 4 * g + e : 16 + 4 * g + (e - 4); }
+
+__device__ __forceinline__ bf16x8 pack8(const float* x) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)x[e];
+  return r;
+}
+__device__ __forceinline__ bf16x8 pair_frag(f32x4 lo, f32x4 hi) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    r[e] = (__bf16)lo[e];
+    r[e + 4] = (__bf16)hi[e];
+  }
+  return r;
+}
+// four consecutive bf16 (8 bytes) -> float
+__device__ __forceinline__ void load4_bf16(const bf16* p, float* out) {
+  uint2 u = *(const uint2*)p;
+  out[0] = bf16_to_f32((bf16)(u.x & 0xffff));
+  out[1] = bf16_to_f32((bf16)(u.x >> 16));
+  out[2] = bf16_to_f32((bf16)(u.y & 0xffff));
+  out[3] = bf16_to_f32((bf16)(u.y >> 16));
+}
+__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
+__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
+__device__ __forceinline__ float gate_value(float x, float A, int has_lb, float lb) {
+  return fmaxf(has_lb ? lb * sigmoid_f(A * x) : -A * softplus_f(x), kGateFloor);
+}
+// 0/1 selection fragment: as a B operand it picks logical column 16*half + n
+// of a 32-wide k-step laid out in sigma order.
+__device__ __forceinline__ bf16x8 select_frag(int g, int n, int half) {
+  bf16x8 r;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r[e] = (__bf16)((sig(g, e) == 16 * half + n) ? 1.f : 0.f);
+  return r;
+}
+
+// ---------------------------------------------------------------------------
+// Chunk record layout (bytes, per chunk-head), shared by both kernels.
+// ---------------------------------------------------------------------------
+template <int K, int V>
+struct Rec {
+  static constexpr int NKJ = K / 32, NKT = K / 16, NVT = V / 16;
+  static constexpr int kFrag = 1024;                        // 64 lanes x 16 B
+  static constexpr int oQt = 0;                             // [4][NKJ] frags
+  static constexpr int oW = oQt + 4 * NKJ * kFrag;          // [4][NKJ] frags
+  static constexpr int oKbar = oW + 4 * NKJ * kFrag;        // [NKT][2] frags
+  static constexpr int oAqk = oKbar + NKT * 2 * kFrag;      // [4][2] frags
+  static constexpr int oGL = oAqk + 8 * kFrag;              // [K] fp32
+  static constexpr int kStage = oGL + K * 4;                // staged into LDS by the state pass
+  static constexpr int oU = kStage;                         // [4][NVT] tiles of 64 lanes x 8 B
+  static constexpr int kBytes = oU + 4 * NVT * 512;
+  // the state pass copies whole 4 KiB rounds (256 threads x 16 B); the rounded
+  // stage still ends inside the record
+  static constexpr int kStageRounds = (kStage + 4095) / 4096;
+  static_assert(kStage % 16 == 0 && kBytes % 256 == 0, "record alignment");
+  static_assert(kStageRounds * 4096 <= kBytes, "rounded stage must stay inside the record");
+};
+
+// ---------------------------------------------------------------------------
+// Kernel A: prologue + chunk-local factors.
+// ---------------------------------------------------------------------------
+template <int K, int V>
+__global__ __launch_bounds__(kThreads) void k_chunk_mfma(FwdArgs a) {
+  using R = Rec<K, V>;
+  constexpr int NKJ = K / 32, NVJ = V / 32, NVT = V / 16, KL = K / 4;
+  const int H = a.H;
+  const int64_t wid = blockIdx.x;
+  const int jchunk = (int)(wid / H), h = (int)(wid % H);
+  if (jchunk >= *a.nt_dev) return;
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int tok0 = a.chunk_tok[jchunk], L = a.chunk_len[jchunk];
+  const int row = 16 * w + n;
+  const bool valid = row < L;
+  const int64_t th = (int64_t)(tok0 + (valid ? row : 0)) * H + h;  // token-head index
+  char* rec = (char*)a.rec + ((int64_t)jchunk * H + h) * R::kBytes;
+
+  __shared__ __attribute__((aligned(16))) float sTot[4][K];
+  __shared__ float sBeta[kC];
+  __shared__ bf16x8 sX[4][NKJ][64];
+  __shared__ bf16x8 sKbar[4][NKJ][64];
+  __shared__ __attribute__((aligned(16))) float sA[kC][68];
+  __shared__ float sP[4][16][17];
+  // sKb (fragments) and later sT share storage
+  __shared__ __attribute__((aligned(16))) char sU1[(kC * 68 * 4 > 4 * NKJ * 64 * 16) ? kC * 68 * 4 : 4 * NKJ * 64 * 16];
+  bf16x8 (*sKb)[NKJ][64] = (bf16x8(*)[NKJ][64])sU1;
+  float (*sT)[68] = (float(*)[68])sU1;
+
+  // ---- 1. loads (own row, channels 32j + sig(g, e)) ----
+  float qv[KL], kv[KL], gv[KL];
+  {
+    const bf16* q = (const bf16*)a.q + th * K;
+    const bf16* k = (const bf16*)a.k + th * K;
+    const bf16* gt = (const bf16*)a.gate + th * K;
+    const float* db = a.dt_bias + (int64_t)h * K;
+#pragma unroll
+    for (int j = 0; j < NKJ; ++j) {
+      const int c0 = 32 * j + 4 * g, c1 = c0 + 16;
+      if (valid) {
+        load4_bf16(q + c0, qv + 8 * j);
+        load4_bf16(q + c1, qv + 8 * j + 4);
+        load4_bf16(k + c0, kv + 8 * j);
+        load4_bf16(k + c1, kv + 8 * j + 4);
+        load4_bf16(gt + c0, gv + 8 * j);
+        load4_bf16(gt + c1, gv + 8 * j + 4);
+        const float4 d0 = *(const float4*)(db + c0), d1 = *(const float4*)(db + c1);
+        gv[8 * j + 0] += d0.x; gv[8 * j + 1] += d0.y; gv[8 * j + 2] += d0.z; gv[8 * j + 3] += d0.w;
+        gv[8 * j + 4] += d1.x; gv[8 * j + 5] += d1.y; gv[8 * j + 6] += d1.z; gv[8 * j + 7] += d1.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[8 * j + e] = kv[8 * j + e] = gv[8 * j + e] = 0.f;
+      }
+    }
+  }
+  const float beta_r = valid ? sigmoid_f(bf16_to_f32(((const bf16*)a.beta)[th])) : 0.f;
+
+  // ---- 2. L2 norms (4 lanes share a row), gate ----
+  {
+    float ssq = 0.f, ssk = 0.f;
+#pragma unroll
+    for (int s = 0; s < KL; ++s) {
+      ssq = fmaf(qv[s], qv[s], ssq);
+      ssk = fmaf(kv[s], kv[s], ssk);
+    }
+    ssq += __shfl_xor(ssq, 16);
+    ssq += __shfl_xor(ssq, 32);
+    ssk += __shfl_xor(ssk, 16);
+    ssk += __shfl_xor(ssk, 32);
+    const float rq = 1.f / sqrtf(ssq + 1e-6f), rk = 1.f / sqrtf(ssk + 1e-6f);
+    const float A = expf(a.a_log[h]);
+#pragma unroll
+    for (int s = 0; s < KL; ++s) {
+      qv[s] *= rq;
+      kv[s] *= rk;
+      gv[s] = valid ? gate_value(gv[s], A, a.has_lb, a.lb) : 0.f;
+    }
+  }
+  // ---- 3. cumulative log-decay inside the 16-row block (lanes n of one g) ----
+#pragma unroll
+  for (int s = 0; s < KL; ++s) {
+    float x = gv[s];
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const float y = __shfl_up(x, d, 16);
+      if (n >= d) x += y;
+    }
+    gv[s] = x;  // lambda
+  }
+  if (n == 15) {
+#pragma unroll
+    for (int j = 0; j < NKJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sTot[w][32 * j + sig(g, e)] = gv[8 * j + e];
+  }
+  if (g == 0) sBeta[row] = beta_r;
+  __syncthreads();
+
+  // ---- 4. per-element factors; fragments to LDS and to the record ----
+  bf16x8 qrow[NKJ], krow[NKJ], kbown[NKJ];
+  float negmax = 0.f;
+  {
+    const float scale = a.scale;
+#pragma unroll
+    for (int j = 0; j < NKJ; ++j) {
+      float fq[8], fk[8], fx[8], fkb[8], fkbar[8], fqr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = 32 * j + sig(g, e);
+        float gam_w = 0.f, gam_all = 0.f;
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          const float t = sTot[b][c];
+          gam_all += t;
+          if (b < w) gam_w += t;
+        }
+        const float lam_tot = sTot[w][c];
+        const float lam = gv[8 * j + e];
+        const float ef = expf(lam);                 // e^{gamma_r - Gam_w}
+        const float F = expf(lam_tot - lam);        // e^{Gam_{w+1} - gamma_r}
+        const float EG = expf(gam_w);               // e^{Gam_w}
+        const float EL = expf(gam_all - gam_w - lam_tot);  // e^{gamma_L - Gam_{w+1}}
+        negmax = fmaxf(negmax, -lam_tot);
+        fqr[e] = qv[8 * j + e] * ef;
+        fk[e] = kv[8 * j + e] * ef;
+        fq[e] = scale * fqr[e] * EG;
+        fx[e] = beta_r * fk[e] * EG;
+        fkb[e] = kv[8 * j + e] * F;
+        fkbar[e] = fkb[e] * EL;
+      }
+      qrow[j] = pack8(fqr);
+      krow[j] = pack8(fk);
+      kbown[j] = pack8(fkb);
+      ((bf16x8*)(rec + R::oQt))[(w * NKJ + j) * 64 + lane] = pack8(fq);
+      sX[w][j][lane] = pack8(fx);
+      sKbar[w][j][lane] = pack8(fkbar);
+      sKb[w][j][lane] = kbown[j];
+    }
+  }
+  // gL = e^{gamma_L} in natural channel order
+  if (w == 0 && n == 0) {
+#pragma unroll
+    for (int j = 0; j < NKJ; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = 32 * j + sig(g, e);
+        ((float*)(rec + R::oGL))[c] = expf(sTot[0][c] + sTot[1][c] + sTot[2][c] + sTot[3][c]);
+      }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) negmax = fmaxf(negmax, __shfl_xor(negmax, off));
+  const bool exact_diag = negmax > kDiagSafe;  // wave-uniform
+  __syncthreads();
+
+  // ---- 5. decayed key/query products, blocks (I <= R = w), transposed tiles ----
+  f32x4 dq[4], dk[4];
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    dq[I] = zero4();
+    dk[I] = zero4();
+    if (I > w) continue;
+    if (I == w && exact_diag) continue;
+#pragma unroll
+    for (int j = 0; j < NKJ; ++j) {
+      float f[8];
+      bf16x8 src = (I == w) ? kbown[j] : sKb[I][j][lane];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int c = 32 * j + sig(g, e);
+        float m;
+        if (I == w) {
+          m = expf(-sTot[w][c]);
+        } else {
+          float acc = 0.f;
+#pragma unroll
+          for (int b = 0; b < 4; ++b)
+            if (b > I && b < w) acc += sTot[b][c];
+          m = expf(acc);
+        }
+        f[e] = (float)src[e] * m;
+      }
+      const bf16x8 kc = pack8(f);
+      dq[I] = mfma(kc, qrow[j], dq[I]);
+      dk[I] = mfma(kc, krow[j], dk[I]);
+    }
+  }
+  if (exact_diag) {
+    // exact per-pair path for the diagonal block: lane (g, n) builds row n against every i
+    float aq[16], ak[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      float pq = 0.f, pk = 0.f;
+#pragma unroll
+      for (int s = 0; s < KL; ++s) {
+        const float ki = __shfl(kv[s], 16 * g + i);
+        const float li = __shfl(gv[s], 16 * g + i);
+        const float d = (i <= n) ? expf(gv[s] - li) : 0.f;
+        pq = fmaf(qv[s] * ki, d, pq);
+        pk = fmaf(kv[s] * ki, d, pk);
+      }
+      pq += __shfl_xor(pq, 16);
+      pq += __shfl_xor(pq, 32);
+      pk += __shfl_xor(pk, 16);
+      pk += __shfl_xor(pk, 32);
+      aq[i] = pq;
+      ak[i] = pk;
+    }
+    // tile (I = w) holds A[r = 16w + n][i = 4g + e]
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      float vq = 0.f, vk = 0.f;
+#pragma unroll
+      for (int gg = 0; gg < 4; ++gg)
+        if (gg == g) {
+          vq = aq[4 * gg + e];
+          vk = ak[4 * gg + e];
+        }
+      dq[w][e] = vq;
+      dk[w][e] = vk;
+    }
+  }
+  // masks: Akk strictly lower -> LDS (fp32, row r = 16w+n), Aqk lower incl. diagonal -> record
+  {
+    const int r = 16 * w + n;
+#pragma unroll
+    for (int I = 0; I < 4; ++I) {
+      float4 v4;
+      float* vv = (float*)&v4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int i = 16 * I + 4 * g + e;
+        vv[e] = (i < r) ? dk[I][e] : 0.f;
+        dq[I][e] = (i <= r) ? a.scale * dq[I][e] : 0.f;
+      }
+      *(float4*)&sA[r][16 * I + 4 * g] = v4;
+    }
+    bf16x8* aq = (bf16x8*)(rec + R::oAqk);
+    aq[(w * 2 + 0) * 64 + lane] = pair_frag(dq[0], dq[1]);
+    aq[(w * 2 + 1) * 64 + lane] = pair_frag(dq[2], dq[3]);
+  }
+  __syncthreads();
+
+  // ---- 6. Tm = (I + Diag(beta) Akk)^-1 in fp32 ----
+  // zero Tm, then diagonal blocks by forward substitution (lane n = column)
+  for (int p = tid; p < kC * 68; p += kThreads) (&sT[0][0])[p] = 0.f;
+  __syncthreads();
+  if (g == 0) {
+    const int b0 = 16 * w;
+    float tc[16];
+#pragma unroll
+    for (int rr = 0; rr < 16; ++rr) {
+      float s = 0.f;
+#pragma unroll
+      for (int i = 0; i < rr; ++i) s = fmaf(sA[b0 + rr][b0 + i], tc[i], s);
+      tc[rr] = (n == rr) ? 1.f : ((n < rr) ? -sBeta[b0 + rr] * s : 0.f);
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) sT[b0 + i][b0 + n] = tc[i];
+  }
+  __syncthreads();
+  // off-diagonal blocks along diagonals d = R - I
+  {
+    const int rho = lane >> 2, k0 = 4 * (lane & 3);
+    for (int d = 1; d < 4; ++d) {
+      const int Rb = w, Ib = w - d;
+      if (Ib >= 0) {
+        float p[4] = {0.f, 0.f, 0.f, 0.f};
+        const float bt = sBeta[16 * Rb + rho];
+        for (int J = Ib; J < Rb; ++J) {
+#pragma unroll
+          for (int mu = 0; mu < 16; ++mu) {
+            const float av = sA[16 * Rb + rho][16 * J + mu];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) p[q] = fmaf(av, sT[16 * J + mu][16 * Ib + k0 + q], p[q]);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sP[w][rho][k0 + q] = bt * p[q];
+      }
+      __syncthreads();
+      if (Ib >= 0) {
+        float t[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int mu = 0; mu < 16; ++mu) {
+          const float tv = sT[16 * Rb + rho][16 * Rb + mu];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) t[q] = fmaf(tv, sP[w][mu][k0 + q], t[q]);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sT[16 * Rb + rho][16 * Ib + k0 + q] = -t[q];
+      }
+      __syncthreads();
+    }
+  }
+
+  // ---- 7. jobs: W (channel pairs), Kbar (channel pairs), U (value pairs) ----
+  const bf16x8 sel0 = select_frag(g, n, 0), sel1 = select_frag(g, n, 1);
+  bf16x8 tfrag[4][2];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float4 lo = *(const float4*)&sT[16 * t + n][32 * j + 4 * g];
+      const float4 hi = *(const float4*)&sT[16 * t + n][32 * j + 16 + 4 * g];
+      float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+      tfrag[t][j] = pack8(f);
+    }
+  constexpr int NJOBS = 2 * NKJ + NVJ;
+  for (int job = w; job < NJOBS; job += 4) {
+    if (job < 2 * NKJ) {
+      const bool isW = job < NKJ;
+      const int p = isW ? job : job - NKJ;
+      f32x4 did[4][2];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const bf16x8 src = isW ? sX[I][p][lane] : sKbar[I][p][lane];
+        did[I][0] = mfma(src, sel0, zero4());
+        did[I][1] = mfma(src, sel1, zero4());
+      }
+      if (isW) {
+        // W^T = X^T Tm^T; X^T fragments from the transposed tiles
+        bf16x8 xt[2][2];
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+          for (int j = 0; j < 2; ++j) xt[a2][j] = pair_frag(did[2 * j][a2], did[2 * j + 1][a2]);
+        bf16x8* wout = (bf16x8*)(rec + R::oW);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          f32x4 acc[2];
+#pragma unroll
+          for (int a2 = 0; a2 < 2; ++a2) {
+            acc[a2] = mfma(xt[a2][0], tfrag[t][0], zero4());
+            if (t >= 2) acc[a2] = mfma(xt[a2][1], tfrag[t][1], acc[a2]);
+          }
+          wout[(t * NKJ + p) * 64 + lane] = pair_frag(acc[0], acc[1]);
+        }
+      } else {
+        bf16x8* kout = (bf16x8*)(rec + R::oKbar);
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            kout[((2 * p + a2) * 2 + j) * 64 + lane] = pair_frag(did[2 * j][a2], did[2 * j + 1][a2]);
+      }
+    } else {
+      const int p = job - 2 * NKJ;
+      f32x4 did[4][2];
+#pragma unroll
+      for (int I = 0; I < 4; ++I) {
+        const int ri = 16 * I + n;
+        float f[8];
+        if (ri < L) {
+          const bf16* vp = (const bf16*)a.v + ((int64_t)(tok0 + ri) * H + h) * V + 32 * p + 4 * g;
+          load4_bf16(vp, f);
+          load4_bf16(vp + 16, f + 4);
+          const float bt = sBeta[ri];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] *= bt;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) f[e] = 0.f;
+        }
+        const bf16x8 src = pack8(f);
+        did[I][0] = mfma(src, sel0, zero4());
+        did[I][1] = mfma(src, sel1, zero4());
+      }
+      bf16x8 vb[2][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2) vb[j][a2] = pair_frag(did[2 * j][a2], did[2 * j + 1][a2]);
+      uint2* uout = (uint2*)(rec + R::oU);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2) {
+          f32x4 acc = mfma(tfrag[t][0], vb[0][a2], zero4());
+          if (t >= 2) acc = mfma(tfrag[t][1], vb[1][a2], acc);
+          uint2 u;
+          u.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
+          u.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
+          uout[(t * NVT + 2 * p + a2) * 64 + lane] = u;
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel B: state pass and output.
+// ---------------------------------------------------------------------------
+template <int K, int V, int NCT>
+__global__ __launch_bounds__(kThreads) void k_state_mfma(FwdArgs a) {
+  using R = Rec<K, V>;
+  constexpr int NKJ = K / 32, NKT = K / 16, NVT = V / 16;
+  constexpr int NPF = R::kStageRounds;
+  const int H = a.H;
+  const int ncols = a.summary ? V + K : V;
+  const int nct_total = ncols / 16;
+  const int tiles_wg = 4 * NCT;
+  const int ntile_wg = (nct_total + tiles_wg - 1) / tiles_wg;
+  const int64_t wid = blockIdx.x;
+  const int tileg = (int)(wid % ntile_wg);
+  const int64_t nh = wid / ntile_wg;
+  const int h = (int)(nh % H), seq = (int)(nh / H);
+  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
+
+  __shared__ __attribute__((aligned(16))) char sStage[R::kStageRounds * 4096];
+  const bf16x8* sQt = (const bf16x8*)(sStage + R::oQt);
+  const bf16x8* sW = (const bf16x8*)(sStage + R::oW);
+  const bf16x8* sKbar = (const bf16x8*)(sStage + R::oKbar);
+  const bf16x8* sAqk = (const bf16x8*)(sStage + R::oAqk);
+  const float* sGL = (const float*)(sStage + R::oGL);
+
+  int ctg[NCT];
+  bool act[NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    ctg[ct] = tileg * tiles_wg + w * NCT + ct;
+    act[ct] = ctg[ct] < nct_total;
+  }
+  const int64_t sbase = ((int64_t)seq * H + h) * K * V;
+
+  // state S: K/16 accumulator tiles per column tile
+  f32x4 S[NKT][NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int col = 16 * ctg[ct] + n;
+#pragma unroll
+    for (int at = 0; at < NKT; ++at)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 16 * at + 4 * g + e;
+        float s = 0.f;
+        if (act[ct]) {
+          if (col < V)
+            s = (a.init && !a.summary) ? a.init[sbase + (int64_t)c * V + col] : 0.f;
+          else
+            s = (c == col - V) ? 1.f : 0.f;
+        }
+        S[at][ct][e] = s;
+      }
+  }
+
+  const int jc0 = a.seq_chunk0[seq], jc1 = a.seq_chunk0[seq + 1];
+  const char* recbase = (const char*)a.rec;
+  u32x4 pf[NPF];
+  if (jc0 < jc1) {
+    const u32x4* src = (const u32x4*)(recbase + ((int64_t)jc0 * H + h) * R::kBytes);
+#pragma unroll
+    for (int i = 0; i < NPF; ++i) ((u32x4*)sStage)[tid + kThreads * i] = src[tid + kThreads * i];
+  }
+  __syncthreads();
+
+  for (int jc = jc0; jc < jc1; ++jc) {
+    const bool more = jc + 1 < jc1;
+    {
+      // prefetch the next record (the last iteration reloads its own, unused)
+      const u32x4* src = (const u32x4*)(recbase + ((int64_t)(more ? jc + 1 : jc) * H + h) * R::kBytes);
+#pragma unroll
+      for (int i = 0; i < NPF; ++i) pf[i] = src[tid + kThreads * i];
+    }
+    const int tok0 = a.chunk_tok[jc], L = a.chunk_len[jc];
+    const uint2* ug = (const uint2*)(recbase + ((int64_t)jc * H + h) * R::kBytes + R::oU);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      if (!act[ct]) continue;
+      const int col = 16 * ctg[ct] + n;
+      const bool vcol = col < V;
+      // U tiles for this column tile (zero for transition columns)
+      f32x4 Ut[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        if (vcol) {
+          const uint2 u = ug[(t * NVT + ctg[ct]) * 64 + lane];
+          Ut[t][0] = bf16_to_f32((bf16)(u.x & 0xffff));
+          Ut[t][1] = bf16_to_f32((bf16)(u.x >> 16));
+          Ut[t][2] = bf16_to_f32((bf16)(u.y & 0xffff));
+          Ut[t][3] = bf16_to_f32((bf16)(u.y >> 16));
+        } else {
+          Ut[t] = zero4();
+        }
+      }
+      // S as B operand (k = key channel in sigma order)
+      bf16x8 sb[NKJ];
+#pragma unroll
+      for (int j = 0; j < NKJ; ++j) sb[j] = pair_frag(S[2 * j][ct], S[2 * j + 1][ct]);
+      f32x4 X[4], Y[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        X[t] = zero4();
+        Y[t] = zero4();
+#pragma unroll
+        for (int j = 0; j < NKJ; ++j) {
+          X[t] = mfma(sW[(t * NKJ + j) * 64 + lane], sb[j], X[t]);
+          if (!a.summary) Y[t] = mfma(sQt[(t * NKJ + j) * 64 + lane], sb[j], Y[t]);
+        }
+      }
+      f32x4 D[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) D[t] = Ut[t] - X[t];
+      bf16x8 db[2];
+      db[0] = pair_frag(D[0], D[1]);
+      db[1] = pair_frag(D[2], D[3]);
+      if (!a.summary) {
+        bf16* o = (bf16*)a.o;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          Y[t] = mfma(sAqk[(t * 2 + 0) * 64 + lane], db[0], Y[t]);
+          if (t >= 2) Y[t] = mfma(sAqk[(t * 2 + 1) * 64 + lane], db[1], Y[t]);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * t + 4 * g + e;
+            if (r < L) o[((int64_t)(tok0 + r) * H + h) * V + col] = f32_to_bf16(Y[t][e]);
+          }
+        }
+      }
+#pragma unroll
+      for (int at = 0; at < NKT; ++at) {
+        f32x4 acc;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[e] = sGL[16 * at + 4 * g + e] * S[at][ct][e];
+        acc = mfma(sKbar[(at * 2 + 0) * 64 + lane], db[0], acc);
+        acc = mfma(sKbar[(at * 2 + 1) * 64 + lane], db[1], acc);
+        S[at][ct] = acc;
+      }
+    }
+    __syncthreads();
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < NPF; ++i) ((u32x4*)sStage)[tid + kThreads * i] = pf[i];
+    }
+    __syncthreads();
+  }
+
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    if (!act[ct]) continue;
+    const int col = 16 * ctg[ct] + n;
+#pragma unroll
+    for (int at = 0; at < NKT; ++at)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 16 * at + 4 * g + e;
+        const float s = S[at][ct][e];
+        if (!a.summary) {
+          if (a.fin) a.fin[sbase + (int64_t)c * V + col] = s;
+        } else if (col < V) {
+          a.state_ext[sbase + (int64_t)c * V + col] = s;
+        } else {
+          a.transition[((int64_t)seq * H + h) * K * K + (int64_t)c * K + (col - V)] = s;
+        }
+      }
+  }
+}
+
+template <int K, int V>
+hipError_t run(const FwdArgs& a, hipStream_t s) {
+  mark(a, kStagePrologue, 0, s);
+  mark(a, kStagePrologue, 1, s);
+  mark(a, kStageChunk, 0, s);
+  if (a.NT > 0) {
+    hipLaunchKernelGGL((k_chunk_mfma<K, V>), dim3((unsigned)((int64_t)a.NT * a.H)), dim3(kThreads),
+                       0, s, a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
+  mark(a, kStageChunk, 1, s);
+  mark(a, kStageState, 0, s);
+  constexpr int NCT = 1;
+  const int ncols = a.summary ? V + K : V;
+  const int ntile_wg = (ncols / 16 + 4 * NCT - 1) / (4 * NCT);
+  const int64_t wgs = (int64_t)a.N * a.H * ntile_wg;
+  if (wgs > 0 && (a.summary || a.fin || a.NT > 0)) {
+    hipLaunchKernelGGL((k_state_mfma<K, V, NCT>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
+  mark(a, kStageState, 1, s);
+  return hipSuccess;
+}
+
+}  // namespace
+
+size_t mfma_record_bytes(int K, int V) {
+  if (K == 128 && V == 128) return Rec<128, 128>::kBytes;
+  if (K == 128 && V == 64) return Rec<128, 64>::kBytes;
+  if (K == 64 && V == 128) return Rec<64, 128>::kBytes;
+  return Rec<64, 64>::kBytes;
+}
+
+hipError_t launch_mfma_path(const FwdArgs& a, hipStream_t s) {
+  if (a.K == 128 && a.V == 128) return run<128, 128>(a, s);
+  if (a.K == 128 && a.V == 64) return run<128, 64>(a, s);
+  if (a.K == 64 && a.V == 128) return run<64, 128>(a, s);
+  return run<64, 64>(a, s);
+}
+
+}  // namespace kda
