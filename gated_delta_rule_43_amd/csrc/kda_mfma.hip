@@ -49,6 +49,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kC = 64;
 constexpr int kThreads = 256;
+constexpr int kXcds = 8;  // accelerator complex dies of an MI355X, each with its own L2
 constexpr float kDiagSafe = 80.f;  // largest in-block decay the factorised diagonal accepts
 constexpr float kGateFloor = -110.f;
 
@@ -81,10 +82,15 @@ __device__ __forceinline__ void load4_bf16(const bf16* p, float* out) {
   out[2] = bf16_to_f32((bf16)(u.y & 0xffff));
   out[3] = bf16_to_f32((bf16)(u.y >> 16));
 }
-__device__ __forceinline__ float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
-__device__ __forceinline__ float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
-__device__ __forceinline__ float gate_value(float x, float A, int has_lb, float lb) {
-  return fmaxf(has_lb ? lb * sigmoid_f(A * x) : -A * softplus_f(x), kGateFloor);
+// Hardware transcendentals (v_exp_f32 / v_log_f32 are base 2, ~1 ulp): the
+// bf16 path's tolerance is far above their error.
+__device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float flog(float x) { return __builtin_amdgcn_logf(x) * 0.6931471805599453f; }
+__device__ __forceinline__ float fsigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + fexp(-x)); }
+__device__ __forceinline__ float fsoftplus(float x) { return fmaxf(x, 0.f) + flog(1.f + fexp(-fabsf(x))); }
+// In-kernel gate (see kda_valu.hip for the floor at -110).
+__device__ __forceinline__ float fgate(float x, float A, int has_lb, float lb) {
+  return fmaxf(has_lb ? lb * fsigmoid(A * x) : -A * fsoftplus(x), kGateFloor);
 }
 // 0/1 selection fragment: as a B operand it picks logical column 16*half + n
 // of a 32-wide k-step laid out in sigma order.
@@ -120,8 +126,22 @@ struct Rec {
 // ---------------------------------------------------------------------------
 // Kernel A: prologue + chunk-local factors.
 // ---------------------------------------------------------------------------
+// Per-channel factor table rows (fp32, [kNF][K]) built once per workgroup from
+// the block totals Lam_b (b = 0..3), with Gam_b = sum_{b'<b} Lam_b':
+enum {
+  kF_LAM = 0,    // 4 rows: Lam_b
+  kF_EG = 4,     // 4 rows: e^{Gam_b}
+  kF_EL = 8,     // 4 rows: e^{gamma_L - Gam_{b+1}}
+  kF_EML = 12,   // 4 rows: e^{-Lam_b} (diagonal blocks; used while Lam_b >= -80)
+  kF_M20 = 16,   // e^{Gam_2 - Gam_1} = e^{Lam_1}
+  kF_M30 = 17,   // e^{Gam_3 - Gam_1} = e^{Lam_1 + Lam_2}
+  kF_M31 = 18,   // e^{Gam_3 - Gam_2} = e^{Lam_2}
+  kF_GL = 19,    // e^{gamma_L}
+  kNF = 20
+};
+
 template <int K, int V>
-__global__ __launch_bounds__(kThreads) void k_chunk_mfma(FwdArgs a) {
+__global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
   using R = Rec<K, V>;
   constexpr int NKJ = K / 32, NVJ = V / 32, NVT = V / 16, KL = K / 4;
   const int H = a.H;
@@ -135,19 +155,22 @@ __global__ __launch_bounds__(kThreads) void k_chunk_mfma(FwdArgs a) {
   const int64_t th = (int64_t)(tok0 + (valid ? row : 0)) * H + h;  // token-head index
   char* rec = (char*)a.rec + ((int64_t)jchunk * H + h) * R::kBytes;
 
-  __shared__ __attribute__((aligned(16))) float sTot[4][K];
+  // the factor table (steps 3-5) and the solve's scratch sP (step 6) share storage
+  __shared__ __attribute__((aligned(16))) float sFacMem[kNF * K];
+  float (*sFac)[K] = (float(*)[K])sFacMem;
+  float (*sP)[16][17] = (float(*)[16][17])sFacMem;
+  static_assert(4 * 16 * 17 <= kNF * K, "sP must fit in the factor table");
   __shared__ float sBeta[kC];
   __shared__ bf16x8 sX[4][NKJ][64];
   __shared__ bf16x8 sKbar[4][NKJ][64];
   __shared__ __attribute__((aligned(16))) float sA[kC][68];
-  __shared__ float sP[4][16][17];
-  // sKb (fragments) and later sT share storage
+  // sKb (fragments, steps 4-5) and sT (triangular inverse, steps 6-7) share storage
   __shared__ __attribute__((aligned(16))) char sU1[(kC * 68 * 4 > 4 * NKJ * 64 * 16) ? kC * 68 * 4 : 4 * NKJ * 64 * 16];
   bf16x8 (*sKb)[NKJ][64] = (bf16x8(*)[NKJ][64])sU1;
   float (*sT)[68] = (float(*)[68])sU1;
 
   // ---- 1. loads (own row, channels 32j + sig(g, e)) ----
-  float qv[KL], kv[KL], gv[KL];
+  float qv[KL], kv[KL], lam[KL];
   {
     const bf16* q = (const bf16*)a.q + th * K;
     const bf16* k = (const bf16*)a.k + th * K;
@@ -161,20 +184,21 @@ __global__ __launch_bounds__(kThreads) void k_chunk_mfma(FwdArgs a) {
         load4_bf16(q + c1, qv + 8 * j + 4);
         load4_bf16(k + c0, kv + 8 * j);
         load4_bf16(k + c1, kv + 8 * j + 4);
-        load4_bf16(gt + c0, gv + 8 * j);
-        load4_bf16(gt + c1, gv + 8 * j + 4);
+        load4_bf16(gt + c0, lam + 8 * j);
+        load4_bf16(gt + c1, lam + 8 * j + 4);
         const float4 d0 = *(const float4*)(db + c0), d1 = *(const float4*)(db + c1);
-        gv[8 * j + 0] += d0.x; gv[8 * j + 1] += d0.y; gv[8 * j + 2] += d0.z; gv[8 * j + 3] += d0.w;
-        gv[8 * j + 4] += d1.x; gv[8 * j + 5] += d1.y; gv[8 * j + 6] += d1.z; gv[8 * j + 7] += d1.w;
+        lam[8 * j + 0] += d0.x; lam[8 * j + 1] += d0.y; lam[8 * j + 2] += d0.z; lam[8 * j + 3] += d0.w;
+        lam[8 * j + 4] += d1.x; lam[8 * j + 5] += d1.y; lam[8 * j + 6] += d1.z; lam[8 * j + 7] += d1.w;
       } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) qv[8 * j + e] = kv[8 * j + e] = gv[8 * j + e] = 0.f;
+        for (int e = 0; e < 8; ++e) qv[8 * j + e] = kv[8 * j + e] = lam[8 * j + e] = 0.f;
       }
     }
   }
-  const float beta_r = valid ? sigmoid_f(bf16_to_f32(((const bf16*)a.beta)[th])) : 0.f;
+  const float beta_r = valid ? fsigmoid(bf16_to_f32(((const bf16*)a.beta)[th])) : 0.f;
 
-  // ---- 2. L2 norms (4 lanes share a row), gate ----
+  // ---- 2. L2 norms (the 4 lanes of a row share it), gate ----
+  float rq, rk;
   {
     float ssq = 0.f, ssk = 0.f;
 #pragma unroll
@@ -186,34 +210,61 @@ __global__ __launch_bounds__(kThreads) void k_chunk_mfma(FwdArgs a) {
     ssq += __shfl_xor(ssq, 32);
     ssk += __shfl_xor(ssk, 16);
     ssk += __shfl_xor(ssk, 32);
-    const float rq = 1.f / sqrtf(ssq + 1e-6f), rk = 1.f / sqrtf(ssk + 1e-6f);
-    const float A = expf(a.a_log[h]);
+    rq = __builtin_amdgcn_rsqf(ssq + 1e-6f);
+    rk = __builtin_amdgcn_rsqf(ssk + 1e-6f);
+    const float A = fexp(a.a_log[h]);
 #pragma unroll
     for (int s = 0; s < KL; ++s) {
       qv[s] *= rq;
       kv[s] *= rk;
-      gv[s] = valid ? gate_value(gv[s], A, a.has_lb, a.lb) : 0.f;
+      lam[s] = valid ? fgate(lam[s], A, a.has_lb, a.lb) : 0.f;
     }
   }
   // ---- 3. cumulative log-decay inside the 16-row block (lanes n of one g) ----
 #pragma unroll
   for (int s = 0; s < KL; ++s) {
-    float x = gv[s];
+    float x = lam[s];
 #pragma unroll
     for (int d = 1; d < 16; d <<= 1) {
       const float y = __shfl_up(x, d, 16);
       if (n >= d) x += y;
     }
-    gv[s] = x;  // lambda
+    lam[s] = x;
   }
   if (n == 15) {
 #pragma unroll
     for (int j = 0; j < NKJ; ++j)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sTot[w][32 * j + sig(g, e)] = gv[8 * j + e];
+      for (int e = 0; e < 8; ++e) sFac[kF_LAM + w][32 * j + sig(g, e)] = lam[8 * j + e];
   }
   if (g == 0) sBeta[row] = beta_r;
   __syncthreads();
+  // per-channel factor table
+  for (int c = tid; c < K; c += kThreads) {
+    const float l0 = sFac[kF_LAM + 0][c], l1 = sFac[kF_LAM + 1][c];
+    const float l2 = sFac[kF_LAM + 2][c], l3 = sFac[kF_LAM + 3][c];
+    const float gam[5] = {0.f, l0, l0 + l1, l0 + l1 + l2, l0 + l1 + l2 + l3};
+    const float lamb[4] = {l0, l1, l2, l3};
+#pragma unroll
+    for (int b = 0; b < 4; ++b) {
+      sFac[kF_EG + b][c] = fexp(gam[b]);
+      sFac[kF_EL + b][c] = fexp(gam[4] - gam[b + 1]);
+      sFac[kF_EML + b][c] = fexp(-lamb[b]);
+    }
+    sFac[kF_M20][c] = fexp(l1);
+    sFac[kF_M30][c] = fexp(l1 + l2);
+    sFac[kF_M31][c] = fexp(l2);
+    sFac[kF_GL][c] = fexp(gam[4]);
+  }
+  __syncthreads();
+
+  // factor of table row `rowf` for the lane's 8 channels of k-step j
+  auto fac8 = [&](int rowf, int j, float* out) {
+    const float4 lo = *(const float4*)&sFac[rowf][32 * j + 4 * g];
+    const float4 hi = *(const float4*)&sFac[rowf][32 * j + 16 + 4 * g];
+    out[0] = lo.x; out[1] = lo.y; out[2] = lo.z; out[3] = lo.w;
+    out[4] = hi.x; out[5] = hi.y; out[6] = hi.z; out[7] = hi.w;
+  };
 
   // ---- 4. per-element factors; fragments to LDS and to the record ----
   bf16x8 qrow[NKJ], krow[NKJ], kbown[NKJ];
@@ -222,30 +273,23 @@ __global__ __launch_bounds__(kThreads) void k_chunk_mfma(FwdArgs a) {
     const float scale = a.scale;
 #pragma unroll
     for (int j = 0; j < NKJ; ++j) {
+      float lt[8], eg[8], el[8];
+      fac8(kF_LAM + w, j, lt);
+      fac8(kF_EG + w, j, eg);
+      fac8(kF_EL + w, j, el);
       float fq[8], fk[8], fx[8], fkb[8], fkbar[8], fqr[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const int c = 32 * j + sig(g, e);
-        float gam_w = 0.f, gam_all = 0.f;
-#pragma unroll
-        for (int b = 0; b < 4; ++b) {
-          const float t = sTot[b][c];
-          gam_all += t;
-          if (b < w) gam_w += t;
-        }
-        const float lam_tot = sTot[w][c];
-        const float lam = gv[8 * j + e];
-        const float ef = expf(lam);                 // e^{gamma_r - Gam_w}
-        const float F = expf(lam_tot - lam);        // e^{Gam_{w+1} - gamma_r}
-        const float EG = expf(gam_w);               // e^{Gam_w}
-        const float EL = expf(gam_all - gam_w - lam_tot);  // e^{gamma_L - Gam_{w+1}}
-        negmax = fmaxf(negmax, -lam_tot);
+        const float l = lam[8 * j + e];
+        const float ef = fexp(l);            // e^{gamma_r - Gam_w}
+        const float F = fexp(lt[e] - l);     // e^{Gam_{w+1} - gamma_r}
+        negmax = fmaxf(negmax, -lt[e]);
         fqr[e] = qv[8 * j + e] * ef;
         fk[e] = kv[8 * j + e] * ef;
-        fq[e] = scale * fqr[e] * EG;
-        fx[e] = beta_r * fk[e] * EG;
+        fq[e] = scale * fqr[e] * eg[e];
+        fx[e] = beta_r * fk[e] * eg[e];
         fkb[e] = kv[8 * j + e] * F;
-        fkbar[e] = fkb[e] * EL;
+        fkbar[e] = fkb[e] * el[e];
       }
       qrow[j] = pack8(fqr);
       krow[j] = pack8(fk);
@@ -256,16 +300,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_mfma(FwdArgs a) {
       sKb[w][j][lane] = kbown[j];
     }
   }
-  // gL = e^{gamma_L} in natural channel order
-  if (w == 0 && n == 0) {
-#pragma unroll
-    for (int j = 0; j < NKJ; ++j)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = 32 * j + sig(g, e);
-        ((float*)(rec + R::oGL))[c] = expf(sTot[0][c] + sTot[1][c] + sTot[2][c] + sTot[3][c]);
-      }
-  }
+  for (int c = tid; c < K; c += kThreads) ((float*)(rec + R::oGL))[c] = sFac[kF_GL][c];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) negmax = fmaxf(negmax, __shfl_xor(negmax, off));
   const bool exact_diag = negmax > kDiagSafe;  // wave-uniform
@@ -279,32 +314,52 @@ __global__ __launch_bounds__(kThreads) void k_chunk_mfma(FwdArgs a) {
     dk[I] = zero4();
     if (I > w) continue;
     if (I == w && exact_diag) continue;
+    // factor row: e^{-Lam_w} on the diagonal, e^{Gam_w - Gam_{I+1}} below it
+    int frow = -1;
+    if (I == w) frow = kF_EML + w;
+    else if (w == 2 && I == 0) frow = kF_M20;
+    else if (w == 3 && I == 0) frow = kF_M30;
+    else if (w == 3 && I == 1) frow = kF_M31;
 #pragma unroll
     for (int j = 0; j < NKJ; ++j) {
-      float f[8];
-      bf16x8 src = (I == w) ? kbown[j] : sKb[I][j][lane];
+      bf16x8 kc = (I == w) ? kbown[j] : sKb[I][j][lane];
+      if (frow >= 0) {
+        float m[8], f[8];
+        fac8(frow, j, m);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int c = 32 * j + sig(g, e);
-        float m;
-        if (I == w) {
-          m = expf(-sTot[w][c]);
-        } else {
-          float acc = 0.f;
-#pragma unroll
-          for (int b = 0; b < 4; ++b)
-            if (b > I && b < w) acc += sTot[b][c];
-          m = expf(acc);
-        }
-        f[e] = (float)src[e] * m;
+        for (int e = 0; e < 8; ++e) f[e] = (float)kc[e] * m[e];
+        kc = pack8(f);
       }
-      const bf16x8 kc = pack8(f);
       dq[I] = mfma(kc, qrow[j], dq[I]);
       dk[I] = mfma(kc, krow[j], dk[I]);
     }
   }
   if (exact_diag) {
-    // exact per-pair path for the diagonal block: lane (g, n) builds row n against every i
+    // exact per-pair path for the diagonal block (the block's decay exceeds the
+    // factorised range): lane (g, n) builds row n against every i of the block.
+    // q^ and k^ are reloaded so that they need not stay live until here.
+    {
+      const bf16* q = (const bf16*)a.q + th * K;
+      const bf16* k = (const bf16*)a.k + th * K;
+#pragma unroll
+      for (int j = 0; j < NKJ; ++j) {
+        const int c0 = 32 * j + 4 * g, c1 = c0 + 16;
+        if (valid) {
+          load4_bf16(q + c0, qv + 8 * j);
+          load4_bf16(q + c1, qv + 8 * j + 4);
+          load4_bf16(k + c0, kv + 8 * j);
+          load4_bf16(k + c1, kv + 8 * j + 4);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) qv[8 * j + e] = kv[8 * j + e] = 0.f;
+        }
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < KL; ++s2) {
+        qv[s2] *= rq;
+        kv[s2] *= rk;
+      }
+    }
     float aq[16], ak[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -312,8 +367,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_mfma(FwdArgs a) {
 #pragma unroll
       for (int s = 0; s < KL; ++s) {
         const float ki = __shfl(kv[s], 16 * g + i);
-        const float li = __shfl(gv[s], 16 * g + i);
-        const float d = (i <= n) ? expf(gv[s] - li) : 0.f;
+        const float li = __shfl(lam[s], 16 * g + i);
+        const float d = (i <= n) ? fexp(lam[s] - li) : 0.f;
         pq = fmaf(qv[s] * ki, d, pq);
         pk = fmaf(kv[s] * ki, d, pk);
       }
@@ -324,7 +379,6 @@ __global__ __launch_bounds__(kThreads) void k_chunk_mfma(FwdArgs a) {
       aq[i] = pq;
       ak[i] = pk;
     }
-    // tile (I = w) holds A[r = 16w + n][i = 4g + e]
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
       float vq = 0.f, vk = 0.f;
@@ -360,57 +414,67 @@ __global__ __launch_bounds__(kThreads) void k_chunk_mfma(FwdArgs a) {
   __syncthreads();
 
   // ---- 6. Tm = (I + Diag(beta) Akk)^-1 in fp32 ----
-  // zero Tm, then diagonal blocks by forward substitution (lane n = column)
-  for (int p = tid; p < kC * 68; p += kThreads) (&sT[0][0])[p] = 0.f;
-  __syncthreads();
-  if (g == 0) {
+  // (a) zero Tm's strictly-upper blocks and invert the diagonal blocks by
+  //     forward substitution: lane (g, n) carries column n of block w, the four
+  //     g-lanes split each row's sum and combine it with two shuffles.
+  {
     const int b0 = 16 * w;
+#pragma unroll
+    for (int I = 0; I < 4; ++I)
+      if (I > w) *(float4*)&sT[b0 + n][16 * I + 4 * g] = make_float4(0.f, 0.f, 0.f, 0.f);
     float tc[16];
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       float s = 0.f;
 #pragma unroll
-      for (int i = 0; i < rr; ++i) s = fmaf(sA[b0 + rr][b0 + i], tc[i], s);
+      for (int i = 0; i < rr; ++i)
+        if ((i & 3) == g) s = fmaf(sA[b0 + rr][b0 + i], tc[i], s);
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
       tc[rr] = (n == rr) ? 1.f : ((n < rr) ? -sBeta[b0 + rr] * s : 0.f);
     }
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sT[b0 + i][b0 + n] = tc[i];
+    for (int e = 0; e < 4; ++e) sT[b0 + 4 * g + e][b0 + n] = tc[4 * g + e];
   }
   __syncthreads();
-  // off-diagonal blocks along diagonals d = R - I
+  // (b) column block I = w, rows R = w+1..3 in order, inside one wave:
+  //     Tm_RI = -Tm_RR Diag(beta_R) sum_{J=I}^{R-1} Akk_RJ Tm_JI
   {
+    const int Ib = w;
     const int rho = lane >> 2, k0 = 4 * (lane & 3);
-    for (int d = 1; d < 4; ++d) {
-      const int Rb = w, Ib = w - d;
-      if (Ib >= 0) {
-        float p[4] = {0.f, 0.f, 0.f, 0.f};
-        const float bt = sBeta[16 * Rb + rho];
-        for (int J = Ib; J < Rb; ++J) {
-#pragma unroll
-          for (int mu = 0; mu < 16; ++mu) {
-            const float av = sA[16 * Rb + rho][16 * J + mu];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) p[q] = fmaf(av, sT[16 * J + mu][16 * Ib + k0 + q], p[q]);
-          }
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sP[w][rho][k0 + q] = bt * p[q];
-      }
-      __syncthreads();
-      if (Ib >= 0) {
-        float t[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int Rb = Ib + 1; Rb < 4; ++Rb) {
+      float p[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int J = Ib; J < Rb; ++J) {
 #pragma unroll
         for (int mu = 0; mu < 16; ++mu) {
-          const float tv = sT[16 * Rb + rho][16 * Rb + mu];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) t[q] = fmaf(tv, sP[w][mu][k0 + q], t[q]);
+          const float av = sA[16 * Rb + rho][16 * J + mu];
+          const float4 tv = *(const float4*)&sT[16 * J + mu][16 * Ib + k0];
+          p[0] = fmaf(av, tv.x, p[0]);
+          p[1] = fmaf(av, tv.y, p[1]);
+          p[2] = fmaf(av, tv.z, p[2]);
+          p[3] = fmaf(av, tv.w, p[3]);
         }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) sT[16 * Rb + rho][16 * Ib + k0 + q] = -t[q];
       }
-      __syncthreads();
+      const float bt = sBeta[16 * Rb + rho];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sP[w][rho][k0 + q] = bt * p[q];
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      float t[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mu = 0; mu < 16; ++mu) {
+        const float tv = sT[16 * Rb + rho][16 * Rb + mu];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) t[q] = fmaf(tv, sP[w][mu][k0 + q], t[q]);
+      }
+      *(float4*)&sT[16 * Rb + rho][16 * Ib + k0] = make_float4(-t[0], -t[1], -t[2], -t[3]);
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     }
   }
+  __syncthreads();
 
   // ---- 7. jobs: W (channel pairs), Kbar (channel pairs), U (value pairs) ----
   const bf16x8 sel0 = select_frag(g, n, 0), sel1 = select_frag(g, n, 1);
@@ -518,9 +582,14 @@ __global__ __launch_bounds__(kThreads) void k_state_mfma(FwdArgs a) {
   const int nct_total = ncols / 16;
   const int tiles_wg = 4 * NCT;
   const int ntile_wg = (nct_total + tiles_wg - 1) / tiles_wg;
-  const int64_t wid = blockIdx.x;
-  const int tileg = (int)(wid % ntile_wg);
-  const int64_t nh = wid / ntile_wg;
+  // Workgroups are dealt to the 8 XCDs round-robin; the column tiles of one
+  // (sequence, head) get consecutive slots of one XCD so that they share its L2.
+  const int64_t bid = blockIdx.x;
+  const int xcd = (int)(bid % kXcds);
+  const int64_t q8 = bid / kXcds;
+  const int tileg = (int)(q8 % ntile_wg);
+  const int64_t nh = (q8 / ntile_wg) * kXcds + xcd;
+  if (nh >= (int64_t)a.N * H) return;
   const int h = (int)(nh % H), seq = (int)(nh / H);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
 
@@ -688,7 +757,7 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
   constexpr int NCT = 1;
   const int ncols = a.summary ? V + K : V;
   const int ntile_wg = (ncols / 16 + 4 * NCT - 1) / (4 * NCT);
-  const int64_t wgs = (int64_t)a.N * a.H * ntile_wg;
+  const int64_t wgs = ((int64_t)a.N * a.H + kXcds - 1) / kXcds * kXcds * ntile_wg;
   if (wgs > 0 && (a.summary || a.fin || a.NT > 0)) {
     hipLaunchKernelGGL((k_state_mfma<K, V, NCT>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
