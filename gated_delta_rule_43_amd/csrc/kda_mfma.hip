@@ -74,6 +74,12 @@ __device__ __forceinline__ bf16x8 pair_frag(f32x4 lo, f32x4 hi) {
   }
   return r;
 }
+__device__ __forceinline__ void unpack4(uint2 u, float* out) {
+  out[0] = bf16_to_f32((bf16)(u.x & 0xffff));
+  out[1] = bf16_to_f32((bf16)(u.x >> 16));
+  out[2] = bf16_to_f32((bf16)(u.y & 0xffff));
+  out[3] = bf16_to_f32((bf16)(u.y >> 16));
+}
 // four consecutive bf16 (8 bytes) -> float
 __device__ __forceinline__ void load4_bf16(const bf16* p, float* out) {
   uint2 u = *(const uint2*)p;
@@ -92,6 +98,20 @@ __device__ __forceinline__ float fsoftplus(float x) { return fmaxf(x, 0.f) + flo
 __device__ __forceinline__ float fgate(float x, float A, int has_lb, float lb) {
   return fmaxf(has_lb ? lb * fsigmoid(A * x) : -A * fsoftplus(x), kGateFloor);
 }
+// Row shift right by N inside each 16-lane row (DPP row_shr), zero fill.
+template <int N>
+__device__ __forceinline__ float row_shr(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xF, 0xF, true));
+}
+// Inclusive prefix sum over the 16 lanes of each row.
+__device__ __forceinline__ float row_scan16(float x) {
+  x += row_shr<1>(x);
+  x += row_shr<2>(x);
+  x += row_shr<4>(x);
+  x += row_shr<8>(x);
+  return x;
+}
+
 // 0/1 selection fragment: as a B operand it picks logical column 16*half + n
 // of a 32-wide k-step laid out in sigma order.
 __device__ __forceinline__ bf16x8 select_frag(int g, int n, int half) {
@@ -170,6 +190,23 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
   float (*sT)[68] = (float(*)[68])sU1;
 
   // ---- 1. loads (own row, channels 32j + sig(g, e)) ----
+  // this wave's value-pair job (at most one), its V rows prefetched now
+  constexpr int NJOBS = 2 * NKJ + NVJ;
+  int upair = -1;
+  for (int job = w; job < NJOBS; job += 4)
+    if (job >= 2 * NKJ) upair = job - 2 * NKJ;
+  uint2 vraw[4][2];
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    const int ri = 16 * I + n;
+    vraw[I][0] = make_uint2(0u, 0u);
+    vraw[I][1] = make_uint2(0u, 0u);
+    if (upair >= 0 && ri < L) {
+      const bf16* vp = (const bf16*)a.v + ((int64_t)(tok0 + ri) * H + h) * V + 32 * upair + 4 * g;
+      vraw[I][0] = *(const uint2*)vp;
+      vraw[I][1] = *(const uint2*)(vp + 16);
+    }
+  }
   float qv[KL], kv[KL], lam[KL];
   {
     const bf16* q = (const bf16*)a.q + th * K;
@@ -222,15 +259,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
   }
   // ---- 3. cumulative log-decay inside the 16-row block (lanes n of one g) ----
 #pragma unroll
-  for (int s = 0; s < KL; ++s) {
-    float x = lam[s];
-#pragma unroll
-    for (int d = 1; d < 16; d <<= 1) {
-      const float y = __shfl_up(x, d, 16);
-      if (n >= d) x += y;
-    }
-    lam[s] = x;
-  }
+  for (int s = 0; s < KL; ++s) lam[s] = row_scan16(lam[s]);
   if (n == 15) {
 #pragma unroll
     for (int j = 0; j < NKJ; ++j)
@@ -415,8 +444,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
 
   // ---- 6. Tm = (I + Diag(beta) Akk)^-1 in fp32 ----
   // (a) zero Tm's strictly-upper blocks and invert the diagonal blocks by
-  //     forward substitution: lane (g, n) carries column n of block w, the four
-  //     g-lanes split each row's sum and combine it with two shuffles.
+  //     forward substitution.  Every lane (g, n) builds column n of block w in
+  //     full (the 4 g-lanes redundantly), reading each row of Akk as float4
+  //     broadcasts; the g = 0 lanes write the column.
   {
     const int b0 = 16 * w;
 #pragma unroll
@@ -425,16 +455,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
     float tc[16];
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
-      float s = 0.f;
+      float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < rr; ++i)
-        if ((i & 3) == g) s = fmaf(sA[b0 + rr][b0 + i], tc[i], s);
-      s += __shfl_xor(s, 16);
-      s += __shfl_xor(s, 32);
-      tc[rr] = (n == rr) ? 1.f : ((n < rr) ? -sBeta[b0 + rr] * s : 0.f);
+      for (int i4 = 0; i4 < rr; i4 += 4) {
+        const float4 av = *(const float4*)&sA[b0 + rr][b0 + i4];
+        const float ar[4] = {av.x, av.y, av.z, av.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          if (i4 + e < rr) acc[e] = fmaf(ar[e], tc[i4 + e], acc[e]);
+      }
+      const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+      tc[rr] = (n == rr) ? 1.f : ((n < rr) ? -sBeta[b0 + rr] * sum : 0.f);
     }
+    if (g == 0) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) sT[b0 + 4 * g + e][b0 + n] = tc[4 * g + e];
+      for (int i = 0; i < 16; ++i) sT[b0 + i][b0 + n] = tc[i];
+    }
   }
   __syncthreads();
   // (b) column block I = w, rows R = w+1..3 in order, inside one wave:
@@ -488,7 +524,6 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
       float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       tfrag[t][j] = pack8(f);
     }
-  constexpr int NJOBS = 2 * NKJ + NVJ;
   for (int job = w; job < NJOBS; job += 4) {
     if (job < 2 * NKJ) {
       const bool isW = job < NKJ;
@@ -531,19 +566,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
       f32x4 did[4][2];
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
-        const int ri = 16 * I + n;
+        const float bt = sBeta[16 * I + n];  // 0 on rows past the chunk end
         float f[8];
-        if (ri < L) {
-          const bf16* vp = (const bf16*)a.v + ((int64_t)(tok0 + ri) * H + h) * V + 32 * p + 4 * g;
-          load4_bf16(vp, f);
-          load4_bf16(vp + 16, f + 4);
-          const float bt = sBeta[ri];
+        unpack4(vraw[I][0], f);
+        unpack4(vraw[I][1], f + 4);
 #pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] *= bt;
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) f[e] = 0.f;
-        }
+        for (int e = 0; e < 8; ++e) f[e] *= bt;
         const bf16x8 src = pack8(f);
         did[I][0] = mfma(src, sel0, zero4());
         did[I][1] = mfma(src, sel1, zero4());
