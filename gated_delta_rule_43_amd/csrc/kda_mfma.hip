@@ -38,6 +38,8 @@
 // accumulator tiles (rows 0-15 and 16-31) then give a B operand, and a matrix
 // product with a 0/1 selection matrix turns "one row, 8 columns per lane"
 // registers into accumulator layout (a transpose on the matrix cores).
+#include <type_traits>
+
 #include "kda_internal.h"
 
 namespace kda {
@@ -46,6 +48,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
 
 constexpr int kC = 64;
 constexpr int kThreads = 256;
@@ -598,18 +601,19 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Kernel B: state pass and output.
+// Kernel B: state pass and output.  SUM = summary mode (state columns only,
+// with the transition columns [V, V+K) that start as I and carry no values).
 // ---------------------------------------------------------------------------
-template <int K, int V, int NCT>
-__global__ __launch_bounds__(kThreads) void k_state_mfma(FwdArgs a) {
+template <int K, int V, int NCT, bool SUM>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_state_mfma(FwdArgs a) {
   using R = Rec<K, V>;
   constexpr int NKJ = K / 32, NKT = K / 16, NVT = V / 16;
-  constexpr int NPF = R::kStageRounds;
+  constexpr int ncols = SUM ? V + K : V;
+  constexpr int nct_total = ncols / 16;
+  constexpr int tiles_wg = 4 * NCT;
+  static_assert(nct_total % tiles_wg == 0, "every wave owns whole column tiles");
+  constexpr int ntile_wg = nct_total / tiles_wg;
   const int H = a.H;
-  const int ncols = a.summary ? V + K : V;
-  const int nct_total = ncols / 16;
-  const int tiles_wg = 4 * NCT;
-  const int ntile_wg = (nct_total + tiles_wg - 1) / tiles_wg;
   // Workgroups are dealt to the 8 XCDs round-robin; the column tiles of one
   // (sequence, head) get consecutive slots of one XCD so that they share its L2.
   const int64_t bid = blockIdx.x;
@@ -621,20 +625,15 @@ __global__ __launch_bounds__(kThreads) void k_state_mfma(FwdArgs a) {
   const int h = (int)(nh % H), seq = (int)(nh / H);
   const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
 
-  __shared__ __attribute__((aligned(16))) char sStage[R::kStageRounds * 4096];
-  const bf16x8* sQt = (const bf16x8*)(sStage + R::oQt);
-  const bf16x8* sW = (const bf16x8*)(sStage + R::oW);
-  const bf16x8* sKbar = (const bf16x8*)(sStage + R::oKbar);
-  const bf16x8* sAqk = (const bf16x8*)(sStage + R::oAqk);
-  const float* sGL = (const float*)(sStage + R::oGL);
+  // two stage buffers: the next chunk's record streams in (global -> LDS,
+  // no registers) while the current one is consumed
+  constexpr int kStageBytes = R::kStageRounds * 4096;
+  __shared__ __attribute__((aligned(16))) char sStage0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) char sStage1[kStageBytes];
 
   int ctg[NCT];
-  bool act[NCT];
 #pragma unroll
-  for (int ct = 0; ct < NCT; ++ct) {
-    ctg[ct] = tileg * tiles_wg + w * NCT + ct;
-    act[ct] = ctg[ct] < nct_total;
-  }
+  for (int ct = 0; ct < NCT; ++ct) ctg[ct] = tileg * tiles_wg + w * NCT + ct;
   const int64_t sbase = ((int64_t)seq * H + h) * K * V;
 
   // state S: K/16 accumulator tiles per column tile
@@ -642,60 +641,137 @@ __global__ __launch_bounds__(kThreads) void k_state_mfma(FwdArgs a) {
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
     const int col = 16 * ctg[ct] + n;
+    const bool vcol = col < V;
+    const float* init = (!SUM && a.init && vcol) ? a.init + sbase + col : nullptr;
 #pragma unroll
     for (int at = 0; at < NKT; ++at)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int c = 16 * at + 4 * g + e;
-        float s = 0.f;
-        if (act[ct]) {
-          if (col < V)
-            s = (a.init && !a.summary) ? a.init[sbase + (int64_t)c * V + col] : 0.f;
-          else
-            s = (c == col - V) ? 1.f : 0.f;
-        }
-        S[at][ct][e] = s;
+        float sv = 0.f;
+        if (init) sv = init[(int64_t)c * V];
+        if (SUM && !vcol) sv = (c == col - V) ? 1.f : 0.f;
+        S[at][ct][e] = sv;
       }
   }
 
   const int jc0 = a.seq_chunk0[seq], jc1 = a.seq_chunk0[seq + 1];
   const char* recbase = (const char*)a.rec;
-  u32x4 pf[NPF];
-  if (jc0 < jc1) {
-    const u32x4* src = (const u32x4*)(recbase + ((int64_t)jc0 * H + h) * R::kBytes);
+  // U tiles of this wave's column tiles for one chunk (zero for transition columns)
+  uint2 ucur[NCT][4], unext[NCT][4];
 #pragma unroll
-    for (int i = 0; i < NPF; ++i) ((u32x4*)sStage)[tid + kThreads * i] = src[tid + kThreads * i];
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ucur[ct][t] = unext[ct][t] = make_uint2(0u, 0u);
+  int tok_cur = 0, len_cur = 0, tok_nxt = 0, len_nxt = 0;
+  if (jc0 < jc1) {
+    const char* rec = recbase + ((int64_t)jc0 * H + h) * R::kBytes;
+#pragma unroll
+    for (int i = 0; i < R::kStageRounds; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(rec + (tid + kThreads * i) * 16),
+                                       (lds_void*)(&sStage0[(w * 64 + kThreads * i) * 16]), 16, 0, 0);
+    const uint2* ug = (const uint2*)(rec + R::oU);
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct)
+      if (16 * ctg[ct] < V)
+#pragma unroll
+        for (int t = 0; t < 4; ++t) ucur[ct][t] = ug[(t * NVT + ctg[ct]) * 64 + lane];
+    tok_cur = a.chunk_tok[jc0];
+    len_cur = a.chunk_len[jc0];
   }
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
 
-  for (int jc = jc0; jc < jc1; ++jc) {
-    const bool more = jc + 1 < jc1;
-    {
-      // prefetch the next record (the last iteration reloads its own, unused)
-      const u32x4* src = (const u32x4*)(recbase + ((int64_t)(more ? jc + 1 : jc) * H + h) * R::kBytes);
-#pragma unroll
-      for (int i = 0; i < NPF; ++i) pf[i] = src[tid + kThreads * i];
-    }
-    const int tok0 = a.chunk_tok[jc], L = a.chunk_len[jc];
-    const uint2* ug = (const uint2*)(recbase + ((int64_t)jc * H + h) * R::kBytes + R::oU);
+  // output of the previous chunk, stored one iteration late so that the
+  // stores never hold up the wait for the next record
+  uint2 opend[NCT][4];
+  int otok = 0, olen = 0;
+  bool have_out = false;
+  bf16* const o = (bf16*)a.o;
+  auto store_out = [&]() {
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
-      if (!act[ct]) continue;
       const int col = 16 * ctg[ct] + n;
-      const bool vcol = col < V;
-      // U tiles for this column tile (zero for transition columns)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const uint32_t xs[2] = {opend[ct][t].x, opend[ct][t].y};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * t + 4 * g + e;
+          if (r < olen)
+            o[((int64_t)(otok + r) * H + h) * V + col] = (bf16)((xs[e >> 1] >> (16 * (e & 1))) & 0xffff);
+        }
+      }
+    }
+  };
+
+  // one chunk; BUF (compile-time) is the stage buffer holding it, the next
+  // record streams into the other one.  Two distinct buffers let the compiler
+  // see that the async copy never aliases the reads.
+  auto chunk_step = [&](int jc, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    char* const cur = BUF ? sStage1 : sStage0;
+    char* const nxt = BUF ? sStage0 : sStage1;
+    const bool more = jc + 1 < jc1;
+    if (!SUM && have_out) store_out();
+    if (more) {
+      const char* rec = recbase + ((int64_t)(jc + 1) * H + h) * R::kBytes;
+#pragma unroll
+      for (int i = 0; i < R::kStageRounds; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(rec + (tid + kThreads * i) * 16),
+                                         (lds_void*)(&nxt[(w * 64 + kThreads * i) * 16]),
+                                         16, 0, 0);
+      const uint2* ug = (const uint2*)(rec + R::oU);
+#pragma unroll
+      for (int ct = 0; ct < NCT; ++ct)
+        if (16 * ctg[ct] < V)
+#pragma unroll
+          for (int t = 0; t < 4; ++t) unext[ct][t] = ug[(t * NVT + ctg[ct]) * 64 + lane];
+      tok_nxt = a.chunk_tok[jc + 1];
+      len_nxt = a.chunk_len[jc + 1];
+    }
+    const bf16x8* sQt = (const bf16x8*)(cur + R::oQt);
+    const bf16x8* sW = (const bf16x8*)(cur + R::oW);
+    const bf16x8* sKbar = (const bf16x8*)(cur + R::oKbar);
+    const bf16x8* sAqk = (const bf16x8*)(cur + R::oAqk);
+    const float* sGL = (const float*)(cur + R::oGL);
+    // every A-operand fragment of this chunk, read up front
+    bf16x8 fW[4][NKJ], fQ[4][NKJ], fA[4][2], fK[NKT][2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int j = 0; j < NKJ; ++j) {
+        fW[t][j] = sW[(t * NKJ + j) * 64 + lane];
+        if (!SUM) fQ[t][j] = sQt[(t * NKJ + j) * 64 + lane];
+      }
+    if (!SUM) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        fA[t][0] = sAqk[(t * 2 + 0) * 64 + lane];
+        if (t >= 2) fA[t][1] = sAqk[(t * 2 + 1) * 64 + lane];
+      }
+    }
+#pragma unroll
+    for (int at = 0; at < NKT; ++at) {
+      fK[at][0] = sKbar[(at * 2 + 0) * 64 + lane];
+      fK[at][1] = sKbar[(at * 2 + 1) * 64 + lane];
+    }
+    float gl[NKT][4];
+#pragma unroll
+    for (int at = 0; at < NKT; ++at) {
+      const float4 v4 = *(const float4*)&sGL[16 * at + 4 * g];
+      gl[at][0] = v4.x; gl[at][1] = v4.y; gl[at][2] = v4.z; gl[at][3] = v4.w;
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
       f32x4 Ut[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        if (vcol) {
-          const uint2 u = ug[(t * NVT + ctg[ct]) * 64 + lane];
-          Ut[t][0] = bf16_to_f32((bf16)(u.x & 0xffff));
-          Ut[t][1] = bf16_to_f32((bf16)(u.x >> 16));
-          Ut[t][2] = bf16_to_f32((bf16)(u.y & 0xffff));
-          Ut[t][3] = bf16_to_f32((bf16)(u.y >> 16));
-        } else {
-          Ut[t] = zero4();
-        }
+        const uint2 u = ucur[ct][t];
+        Ut[t][0] = bf16_to_f32((bf16)(u.x & 0xffff));
+        Ut[t][1] = bf16_to_f32((bf16)(u.x >> 16));
+        Ut[t][2] = bf16_to_f32((bf16)(u.y & 0xffff));
+        Ut[t][3] = bf16_to_f32((bf16)(u.y >> 16));
       }
       // S as B operand (k = key channel in sigma order)
       bf16x8 sb[NKJ];
@@ -708,8 +784,8 @@ __global__ __launch_bounds__(kThreads) void k_state_mfma(FwdArgs a) {
         Y[t] = zero4();
 #pragma unroll
         for (int j = 0; j < NKJ; ++j) {
-          X[t] = mfma(sW[(t * NKJ + j) * 64 + lane], sb[j], X[t]);
-          if (!a.summary) Y[t] = mfma(sQt[(t * NKJ + j) * 64 + lane], sb[j], Y[t]);
+          X[t] = mfma(fW[t][j], sb[j], X[t]);
+          if (!SUM) Y[t] = mfma(fQ[t][j], sb[j], Y[t]);
         }
       }
       f32x4 D[4];
@@ -718,53 +794,60 @@ __global__ __launch_bounds__(kThreads) void k_state_mfma(FwdArgs a) {
       bf16x8 db[2];
       db[0] = pair_frag(D[0], D[1]);
       db[1] = pair_frag(D[2], D[3]);
-      if (!a.summary) {
-        bf16* o = (bf16*)a.o;
+      if (!SUM) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          Y[t] = mfma(sAqk[(t * 2 + 0) * 64 + lane], db[0], Y[t]);
-          if (t >= 2) Y[t] = mfma(sAqk[(t * 2 + 1) * 64 + lane], db[1], Y[t]);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * t + 4 * g + e;
-            if (r < L) o[((int64_t)(tok0 + r) * H + h) * V + col] = f32_to_bf16(Y[t][e]);
-          }
+          Y[t] = mfma(fA[t][0], db[0], Y[t]);
+          if (t >= 2) Y[t] = mfma(fA[t][1], db[1], Y[t]);
+          opend[ct][t].x = (uint32_t)f32_to_bf16(Y[t][0]) | ((uint32_t)f32_to_bf16(Y[t][1]) << 16);
+          opend[ct][t].y = (uint32_t)f32_to_bf16(Y[t][2]) | ((uint32_t)f32_to_bf16(Y[t][3]) << 16);
         }
       }
 #pragma unroll
       for (int at = 0; at < NKT; ++at) {
         f32x4 acc;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = sGL[16 * at + 4 * g + e] * S[at][ct][e];
-        acc = mfma(sKbar[(at * 2 + 0) * 64 + lane], db[0], acc);
-        acc = mfma(sKbar[(at * 2 + 1) * 64 + lane], db[1], acc);
+        for (int e = 0; e < 4; ++e) acc[e] = gl[at][e] * S[at][ct][e];
+        acc = mfma(fK[at][0], db[0], acc);
+        acc = mfma(fK[at][1], db[1], acc);
         S[at][ct] = acc;
       }
     }
+    otok = tok_cur;
+    olen = len_cur;
+    have_out = true;
+    // the next record has landed (own copies), and every wave is done with this buffer
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
-    if (more) {
 #pragma unroll
-      for (int i = 0; i < NPF; ++i) ((u32x4*)sStage)[tid + kThreads * i] = pf[i];
-    }
-    __syncthreads();
+    for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) ucur[ct][t] = unext[ct][t];
+    tok_cur = tok_nxt;
+    len_cur = len_nxt;
+  };
+  for (int jc = jc0; jc < jc1; jc += 2) {
+    chunk_step(jc, std::integral_constant<int, 0>{});
+    if (jc + 1 < jc1) chunk_step(jc + 1, std::integral_constant<int, 1>{});
   }
+
+  if (!SUM && have_out) store_out();
 
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
-    if (!act[ct]) continue;
     const int col = 16 * ctg[ct] + n;
 #pragma unroll
     for (int at = 0; at < NKT; ++at)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int c = 16 * at + 4 * g + e;
-        const float s = S[at][ct][e];
-        if (!a.summary) {
-          if (a.fin) a.fin[sbase + (int64_t)c * V + col] = s;
+        const float sv = S[at][ct][e];
+        if (!SUM) {
+          if (a.fin) a.fin[sbase + (int64_t)c * V + col] = sv;
         } else if (col < V) {
-          a.state_ext[sbase + (int64_t)c * V + col] = s;
+          a.state_ext[sbase + (int64_t)c * V + col] = sv;
         } else {
-          a.transition[((int64_t)seq * H + h) * K * K + (int64_t)c * K + (col - V)] = s;
+          a.transition[((int64_t)seq * H + h) * K * K + (int64_t)c * K + (col - V)] = sv;
         }
       }
   }
@@ -787,7 +870,10 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
   const int ntile_wg = (ncols / 16 + 4 * NCT - 1) / (4 * NCT);
   const int64_t wgs = ((int64_t)a.N * a.H + kXcds - 1) / kXcds * kXcds * ntile_wg;
   if (wgs > 0 && (a.summary || a.fin || a.NT > 0)) {
-    hipLaunchKernelGGL((k_state_mfma<K, V, NCT>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
+    if (a.summary)
+      hipLaunchKernelGGL((k_state_mfma<K, V, NCT, true>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
+    else
+      hipLaunchKernelGGL((k_state_mfma<K, V, NCT, false>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   mark(a, kStageState, 1, s);
