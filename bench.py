@@ -97,6 +97,22 @@ def algorithmic(w):
     return bytes_th, flops_th
 
 
+def measured_traffic(stage_name):
+    """HBM bytes per launch of a stage from the committed rocprofv3 FETCH_SIZE /
+    WRITE_SIZE summary, or None when the kernel source changed since then."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "traffic_throughput_bf16_B4_T16384_H32_d128.json")
+    try:
+        info = json.load(open(path))
+        src = open(os.path.join(ROOT, info["source"]), "rb").read()
+    except (OSError, ValueError, KeyError):
+        return None
+    if hashlib.sha256(src).hexdigest() != info.get("source_sha256"):
+        return None
+    k = info.get("kernels", {}).get(stage_name)
+    return None if k is None else int(k["traffic_bytes"])
+
+
 def record_bytes(K, V):
     """Bytes of one chunk record of the MFMA path (per chunk-head): Qt, W and
     Kbar^T fragments (C*K bf16 each), Aqk fragments (C*C bf16), gL (K fp32) and
@@ -237,8 +253,9 @@ def main():
     dom = int(np.argmax(stage_ms))
     dom_bytes = stage_bytes(w, dom, NT, N)
     achieved = dom_bytes / (stage_ms[dom] / 1e3) / 1e9 if stage_ms[dom] > 0 else 0.0
+    traffic = measured_traffic(kda.STAGE_NAMES[dom]) if args.workload == 3 else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": None,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": traffic,
                 "kernel": kda.STAGE_NAMES[dom], "kernel_ms": round(float(stage_ms[dom]), 4),
                 "bytes_per_launch": dom_bytes}
     path_gbs = tokh * bytes_th / (ms_per_step / 1e3) / 1e9
