@@ -27,6 +27,7 @@ kda_status fail(kda_status st, const char* fmt, ...) {
 }
 
 constexpr size_t kAlign = 256;
+constexpr size_t kSinkBytes = 16384;  // 256 threads x 2 column tiles x 8 B, with room
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
@@ -91,7 +92,7 @@ struct Layout {
   size_t off_tok = 0, off_len = 0, off_seq0 = 0, off_nt = 0;
   size_t off_qn = 0, off_kn = 0, off_g = 0, off_bt = 0;
   size_t off_W = 0, off_U = 0, off_Qt = 0, off_Kb = 0, off_Aqk = 0, off_gL = 0;
-  size_t off_rec = 0;
+  size_t off_rec = 0, off_sink = 0;
   size_t total = 0;
 };
 
@@ -130,6 +131,7 @@ Layout layout(const kda_problem* p) {
   if (L.mfma) {
     // one record of MFMA-ready chunk factors per chunk-head
     L.off_rec = take(NT * H * kda::mfma_record_bytes(p->K, p->V));
+    L.off_sink = take(kSinkBytes);
   } else {
     L.off_qn = take(tokh * K * 4);
     L.off_kn = take(tokh * K * 4);
@@ -164,6 +166,7 @@ kda::FwdArgs make_args(const kda_problem* p, const Layout& L, void* ws) {
   a.nt_dev = (int32_t*)(w + L.off_nt);
   if (L.mfma) {
     a.rec = w + L.off_rec;
+    a.sink = w + L.off_sink;
   } else {
     a.qn = (float*)(w + L.off_qn);
     a.kn = (float*)(w + L.off_kn);

@@ -65,8 +65,10 @@ struct FwdArgs {
   int ws_bf16;
   void *W, *U, *Qt, *Kb, *Aqk;
   float* gL;
-  // workspace: per chunk-head records of the MFMA path
+  // workspace: per chunk-head records of the MFMA path, and a small sink for
+  // the state pass's masked-off output stores
   void* rec;
+  void* sink;
   // optional stage timing: hipEvent_t handles, [2 * kNumStages], entries may be null
   void* const* events;
 };

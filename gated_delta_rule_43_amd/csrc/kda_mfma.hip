@@ -38,6 +38,7 @@
 // accumulator tiles (rows 0-15 and 16-31) then give a B operand, and a matrix
 // product with a 0/1 selection matrix turns "one row, 8 columns per lane"
 // registers into accumulator layout (a transpose on the matrix cores).
+#include <cstdlib>
 #include <type_traits>
 
 #include "kda_internal.h"
@@ -623,7 +624,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   const int64_t nh = (q8 / ntile_wg) * kXcds + xcd;
   if (nh >= (int64_t)a.N * H) return;
   const int h = (int)(nh % H), seq = (int)(nh / H);
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
 
   // two stage buffers: the next chunk's record streams in (global -> LDS,
   // no registers) while the current one is consumed
@@ -672,10 +674,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                                        (lds_void*)(&sStage0[(w * 64 + kThreads * i) * 16]), 16, 0, 0);
     const uint2* ug = (const uint2*)(rec + R::oU);
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct)
-      if (16 * ctg[ct] < V)
+    for (int ct = 0; ct < NCT; ++ct) {
+      const bool vt = !SUM || 16 * ctg[ct] < V;  // transition columns carry no values
+      const int ut = vt ? ctg[ct] : 0;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) ucur[ct][t] = ug[(t * NVT + ctg[ct]) * 64 + lane];
+      for (int t = 0; t < 4; ++t) {
+        const uint2 u = ug[(t * NVT + ut) * 64 + lane];
+        ucur[ct][t] = vt ? u : make_uint2(0u, 0u);
+      }
+    }
     tok_cur = a.chunk_tok[jc0];
     len_cur = a.chunk_len[jc0];
   }
@@ -685,22 +692,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   // output of the previous chunk, stored one iteration late so that the
   // stores never hold up the wait for the next record
   uint2 opend[NCT][4];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct)
+#pragma unroll
+    for (int t = 0; t < 4; ++t) opend[ct][t] = make_uint2(0u, 0u);
   int otok = 0, olen = 0;
-  bool have_out = false;
   bf16* const o = (bf16*)a.o;
+  // opend[ct][t]: row 16t+n, columns 16*ctg+4g..+3 (the transposed output tile).
+  // Rows past the chunk end (and the pass before the first chunk) are written
+  // to a small sink in the workspace instead, which keeps the loop branch-free.
+  uint2* const sink = (uint2*)a.sink + tid * NCT;
   auto store_out = [&]() {
 #pragma unroll
-    for (int ct = 0; ct < NCT; ++ct) {
-      const int col = 16 * ctg[ct] + n;
+    for (int t = 0; t < 4; ++t) {
+      const int r = 16 * t + n;
+      const bool ok = r < olen;
+      bf16* orow = o + ((int64_t)(otok + (ok ? r : 0)) * H + h) * V + 4 * g;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const uint32_t xs[2] = {opend[ct][t].x, opend[ct][t].y};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 16 * t + 4 * g + e;
-          if (r < olen)
-            o[((int64_t)(otok + r) * H + h) * V + col] = (bf16)((xs[e >> 1] >> (16 * (e & 1))) & 0xffff);
-        }
+      for (int ct = 0; ct < NCT; ++ct) {
+        uint2* dst = ok ? (uint2*)(orow + 16 * ctg[ct]) : sink + ct;
+        *dst = opend[ct][t];
       }
     }
   };
@@ -712,10 +723,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     constexpr int BUF = decltype(bufc)::value;
     char* const cur = BUF ? sStage1 : sStage0;
     char* const nxt = BUF ? sStage0 : sStage1;
-    const bool more = jc + 1 < jc1;
-    if (!SUM && have_out) store_out();
-    if (more) {
-      const char* rec = recbase + ((int64_t)(jc + 1) * H + h) * R::kBytes;
+    // the next record (the current one again on the last chunk: harmless, and
+    // it keeps the body free of branches)
+    const int jn = (jc + 1 < jc1) ? jc + 1 : jc;
+    if (!SUM) store_out();
+    {
+      const char* rec = recbase + ((int64_t)jn * H + h) * R::kBytes;
 #pragma unroll
       for (int i = 0; i < R::kStageRounds; ++i)
         __builtin_amdgcn_global_load_lds((const void*)(rec + (tid + kThreads * i) * 16),
@@ -723,12 +736,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
                                          16, 0, 0);
       const uint2* ug = (const uint2*)(rec + R::oU);
 #pragma unroll
-      for (int ct = 0; ct < NCT; ++ct)
-        if (16 * ctg[ct] < V)
+      for (int ct = 0; ct < NCT; ++ct) {
+        const bool vt = !SUM || 16 * ctg[ct] < V;
+        const int ut = vt ? ctg[ct] : 0;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) unext[ct][t] = ug[(t * NVT + ctg[ct]) * 64 + lane];
-      tok_nxt = a.chunk_tok[jc + 1];
-      len_nxt = a.chunk_len[jc + 1];
+        for (int t = 0; t < 4; ++t) {
+          const uint2 u = ug[(t * NVT + ut) * 64 + lane];
+          unext[ct][t] = vt ? u : make_uint2(0u, 0u);
+        }
+      }
+      tok_nxt = a.chunk_tok[jn];
+      len_nxt = a.chunk_len[jn];
     }
     const bf16x8* sQt = (const bf16x8*)(cur + R::oQt);
     const bf16x8* sW = (const bf16x8*)(cur + R::oW);
@@ -777,6 +795,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       bf16x8 sb[NKJ];
 #pragma unroll
       for (int j = 0; j < NKJ; ++j) sb[j] = pair_frag(S[2 * j][ct], S[2 * j + 1][ct]);
+      // X = W S (rows r, column n); Yt = (Qt S)^T = S^T Qt^T: the same fragments
+      // with the operands swapped, giving lane (g, n) row 16t+n, columns 4g..4g+3
       f32x4 X[4], Y[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -785,7 +805,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
 #pragma unroll
         for (int j = 0; j < NKJ; ++j) {
           X[t] = mfma(fW[t][j], sb[j], X[t]);
-          if (!SUM) Y[t] = mfma(fQ[t][j], sb[j], Y[t]);
+          if (!SUM) Y[t] = mfma(sb[j], fQ[t][j], Y[t]);
         }
       }
       f32x4 D[4];
@@ -797,8 +817,8 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       if (!SUM) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
-          Y[t] = mfma(fA[t][0], db[0], Y[t]);
-          if (t >= 2) Y[t] = mfma(fA[t][1], db[1], Y[t]);
+          Y[t] = mfma(db[0], fA[t][0], Y[t]);
+          if (t >= 2) Y[t] = mfma(db[1], fA[t][1], Y[t]);
           opend[ct][t].x = (uint32_t)f32_to_bf16(Y[t][0]) | ((uint32_t)f32_to_bf16(Y[t][1]) << 16);
           opend[ct][t].y = (uint32_t)f32_to_bf16(Y[t][2]) | ((uint32_t)f32_to_bf16(Y[t][3]) << 16);
         }
@@ -813,9 +833,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         S[at][ct] = acc;
       }
     }
+    // spread the memory instructions over the matrix-core stream
+#pragma unroll
+    for (int i = 0; i < 14; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
+      __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);  // global memory
+    }
     otok = tok_cur;
     olen = len_cur;
-    have_out = true;
     // the next record has landed (own copies), and every wave is done with this buffer
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
@@ -831,7 +857,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     if (jc + 1 < jc1) chunk_step(jc + 1, std::integral_constant<int, 1>{});
   }
 
-  if (!SUM && have_out) store_out();
+  if (!SUM) store_out();
 
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct) {
@@ -853,6 +879,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
 }
 
+// Column tiles per wave in the state pass: one (a workgroup covers 64 state
+// columns), which measures faster than two on MI355X; KDA_STATE_NCT=2 selects
+// two where the column count allows it.
+inline int state_nct(const FwdArgs& a, int V) {
+  const char* env = std::getenv("KDA_STATE_NCT");
+  const int ncols = a.summary ? V + a.K : V;
+  return (env && env[0] == '2' && ncols % 128 == 0) ? 2 : 1;
+}
+
 template <int K, int V>
 hipError_t run(const FwdArgs& a, hipStream_t s) {
   mark(a, kStagePrologue, 0, s);
@@ -865,15 +900,21 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
   }
   mark(a, kStageChunk, 1, s);
   mark(a, kStageState, 0, s);
-  constexpr int NCT = 1;
   const int ncols = a.summary ? V + K : V;
-  const int ntile_wg = (ncols / 16 + 4 * NCT - 1) / (4 * NCT);
+  const int nct = state_nct(a, V);
+  const int ntile_wg = ncols / 16 / (4 * nct);
   const int64_t wgs = ((int64_t)a.N * a.H + kXcds - 1) / kXcds * kXcds * ntile_wg;
   if (wgs > 0 && (a.summary || a.fin || a.NT > 0)) {
-    if (a.summary)
-      hipLaunchKernelGGL((k_state_mfma<K, V, NCT, true>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
-    else
-      hipLaunchKernelGGL((k_state_mfma<K, V, NCT, false>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
+    const dim3 grid((unsigned)wgs), block(kThreads);
+    if (a.summary) {
+      if constexpr (((V + K) / 16) % 8 == 0)
+        if (nct == 2) hipLaunchKernelGGL((k_state_mfma<K, V, 2, true>), grid, block, 0, s, a);
+      if (nct == 1) hipLaunchKernelGGL((k_state_mfma<K, V, 1, true>), grid, block, 0, s, a);
+    } else {
+      if constexpr ((V / 16) % 8 == 0)
+        if (nct == 2) hipLaunchKernelGGL((k_state_mfma<K, V, 2, false>), grid, block, 0, s, a);
+      if (nct == 1) hipLaunchKernelGGL((k_state_mfma<K, V, 1, false>), grid, block, 0, s, a);
+    }
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   mark(a, kStageState, 1, s);
