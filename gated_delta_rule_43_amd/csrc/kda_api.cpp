@@ -92,7 +92,7 @@ struct Layout {
   size_t off_tok = 0, off_len = 0, off_seq0 = 0, off_nt = 0;
   size_t off_qn = 0, off_kn = 0, off_g = 0, off_bt = 0;
   size_t off_W = 0, off_U = 0, off_Qt = 0, off_Kb = 0, off_Aqk = 0, off_gL = 0;
-  size_t off_rec = 0, off_sink = 0;
+  size_t off_rec = 0, off_sink = 0, off_xcount = 0, off_xlist = 0;
   size_t total = 0;
 };
 
@@ -132,6 +132,8 @@ Layout layout(const kda_problem* p) {
     // one record of MFMA-ready chunk factors per chunk-head
     L.off_rec = take(NT * H * kda::mfma_record_bytes(p->K, p->V));
     L.off_sink = take(kSinkBytes);
+    L.off_xcount = take(4);
+    L.off_xlist = take(NT * H * 4);
   } else {
     L.off_qn = take(tokh * K * 4);
     L.off_kn = take(tokh * K * 4);
@@ -167,6 +169,8 @@ kda::FwdArgs make_args(const kda_problem* p, const Layout& L, void* ws) {
   if (L.mfma) {
     a.rec = w + L.off_rec;
     a.sink = w + L.off_sink;
+    a.exact_count = (int32_t*)(w + L.off_xcount);
+    a.exact_list = (int32_t*)(w + L.off_xlist);
   } else {
     a.qn = (float*)(w + L.off_qn);
     a.kn = (float*)(w + L.off_kn);

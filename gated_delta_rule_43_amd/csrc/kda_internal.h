@@ -69,6 +69,8 @@ struct FwdArgs {
   // the state pass's masked-off output stores
   void* rec;
   void* sink;
+  int32_t* exact_count;  // [1] chunk-heads listed for the exact fix-up pass
+  int32_t* exact_list;   // [NT*H]
   // optional stage timing: hipEvent_t handles, [2 * kNumStages], entries may be null
   void* const* events;
 };

@@ -38,6 +38,7 @@
 // accumulator tiles (rows 0-15 and 16-31) then give a B operand, and a matrix
 // product with a 0/1 selection matrix turns "one row, 8 columns per lane"
 // registers into accumulator layout (a transpose on the matrix cores).
+#include <algorithm>
 #include <cstdlib>
 #include <type_traits>
 
@@ -164,15 +165,17 @@ enum {
   kNF = 20
 };
 
-template <int K, int V>
-__global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
+// One chunk-head.  EXACT = false: the common kernel; a 16-row block whose
+// decay exceeds the factorised range makes the workgroup append the chunk-head
+// to a fix-up list instead.  EXACT = true: the fix-up, with the exact per-pair
+// path on such blocks.
+template <int K, int V, bool EXACT>
+__device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, const int h) {
   using R = Rec<K, V>;
   constexpr int NKJ = K / 32, NVJ = V / 32, NVT = V / 16, KL = K / 4;
   const int H = a.H;
-  const int64_t wid = blockIdx.x;
-  const int jchunk = (int)(wid / H), h = (int)(wid % H);
-  if (jchunk >= *a.nt_dev) return;
-  const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int tok0 = a.chunk_tok[jchunk], L = a.chunk_len[jchunk];
   const int row = 16 * w + n;
   const bool valid = row < L;
@@ -186,33 +189,21 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
   static_assert(4 * 16 * 17 <= kNF * K, "sP must fit in the factor table");
   __shared__ float sBeta[kC];
   __shared__ bf16x8 sX[4][NKJ][64];
-  __shared__ bf16x8 sKbar[4][NKJ][64];
-  __shared__ __attribute__((aligned(16))) float sA[kC][68];
+  __shared__ __attribute__((aligned(16))) bf16 sA[kC][72];  // Akk (bf16), rows padded
   // sKb (fragments, steps 4-5) and sT (triangular inverse, steps 6-7) share storage
   __shared__ __attribute__((aligned(16))) char sU1[(kC * 68 * 4 > 4 * NKJ * 64 * 16) ? kC * 68 * 4 : 4 * NKJ * 64 * 16];
   bf16x8 (*sKb)[NKJ][64] = (bf16x8(*)[NKJ][64])sU1;
   float (*sT)[68] = (float(*)[68])sU1;
 
-  // ---- 1. loads (own row, channels 32j + sig(g, e)) ----
-  // this wave's value-pair job (at most one), its V rows prefetched now
-  constexpr int NJOBS = 2 * NKJ + NVJ;
+  // ---- 1-3. own row: q^, k^ (L2 norm), gate, cumulative log-decay in the block ----
+  constexpr int NJOBS = NKJ + NVJ;  // W channel pairs, then U value pairs
   int upair = -1;
   for (int job = w; job < NJOBS; job += 4)
-    if (job >= 2 * NKJ) upair = job - 2 * NKJ;
-  uint2 vraw[4][2];
-#pragma unroll
-  for (int I = 0; I < 4; ++I) {
-    const int ri = 16 * I + n;
-    vraw[I][0] = make_uint2(0u, 0u);
-    vraw[I][1] = make_uint2(0u, 0u);
-    if (upair >= 0 && ri < L) {
-      const bf16* vp = (const bf16*)a.v + ((int64_t)(tok0 + ri) * H + h) * V + 32 * upair + 4 * g;
-      vraw[I][0] = *(const uint2*)vp;
-      vraw[I][1] = *(const uint2*)(vp + 16);
-    }
-  }
-  float qv[KL], kv[KL], lam[KL];
-  {
+    if (job >= NKJ) upair = job - NKJ;
+  // Loads q, k, gate of the lane's row at channels 32j + sig(g, e), normalises
+  // q and k, applies the gate and scans it over the 16 rows of the block.
+  // Used once up front and again by the exact diagonal path.
+  auto row_prologue = [&](float* qv, float* kv, float* lam) {
     const bf16* q = (const bf16*)a.q + th * K;
     const bf16* k = (const bf16*)a.k + th * K;
     const bf16* gt = (const bf16*)a.gate + th * K;
@@ -235,35 +226,28 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
         for (int e = 0; e < 8; ++e) qv[8 * j + e] = kv[8 * j + e] = lam[8 * j + e] = 0.f;
       }
     }
-  }
-  const float beta_r = valid ? fsigmoid(bf16_to_f32(((const bf16*)a.beta)[th])) : 0.f;
-
-  // ---- 2. L2 norms (the 4 lanes of a row share it), gate ----
-  float rq, rk;
-  {
     float ssq = 0.f, ssk = 0.f;
 #pragma unroll
-    for (int s = 0; s < KL; ++s) {
-      ssq = fmaf(qv[s], qv[s], ssq);
-      ssk = fmaf(kv[s], kv[s], ssk);
+    for (int s2 = 0; s2 < KL; ++s2) {
+      ssq = fmaf(qv[s2], qv[s2], ssq);
+      ssk = fmaf(kv[s2], kv[s2], ssk);
     }
     ssq += __shfl_xor(ssq, 16);
     ssq += __shfl_xor(ssq, 32);
     ssk += __shfl_xor(ssk, 16);
     ssk += __shfl_xor(ssk, 32);
-    rq = __builtin_amdgcn_rsqf(ssq + 1e-6f);
-    rk = __builtin_amdgcn_rsqf(ssk + 1e-6f);
+    const float rq = __builtin_amdgcn_rsqf(ssq + 1e-6f), rk = __builtin_amdgcn_rsqf(ssk + 1e-6f);
     const float A = fexp(a.a_log[h]);
 #pragma unroll
-    for (int s = 0; s < KL; ++s) {
-      qv[s] *= rq;
-      kv[s] *= rk;
-      lam[s] = valid ? fgate(lam[s], A, a.has_lb, a.lb) : 0.f;
+    for (int s2 = 0; s2 < KL; ++s2) {
+      qv[s2] *= rq;
+      kv[s2] *= rk;
+      lam[s2] = row_scan16(valid ? fgate(lam[s2], A, a.has_lb, a.lb) : 0.f);
     }
-  }
-  // ---- 3. cumulative log-decay inside the 16-row block (lanes n of one g) ----
-#pragma unroll
-  for (int s = 0; s < KL; ++s) lam[s] = row_scan16(lam[s]);
+  };
+  float qv[KL], kv[KL], lam[KL];
+  row_prologue(qv, kv, lam);
+  const float beta_r = valid ? fsigmoid(bf16_to_f32(((const bf16*)a.beta)[th])) : 0.f;
   if (n == 15) {
 #pragma unroll
     for (int j = 0; j < NKJ; ++j)
@@ -300,6 +284,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
   };
 
   // ---- 4. per-element factors; fragments to LDS and to the record ----
+  const bf16x8 sel0 = select_frag(g, n, 0), sel1 = select_frag(g, n, 1);
   bf16x8 qrow[NKJ], krow[NKJ], kbown[NKJ];
   float negmax = 0.f;
   {
@@ -329,15 +314,40 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
       kbown[j] = pack8(fkb);
       ((bf16x8*)(rec + R::oQt))[(w * NKJ + j) * 64 + lane] = pack8(fq);
       sX[w][j][lane] = pack8(fx);
-      sKbar[w][j][lane] = pack8(fkbar);
       sKb[w][j][lane] = kbown[j];
+      // Kbar^T fragments (a, w/2): this block's rows transposed on the matrix
+      // cores, written as the (w%2) half of each lane's 16 bytes
+      {
+        const bf16x8 kb8 = pack8(fkbar);
+#pragma unroll
+        for (int a2 = 0; a2 < 2; ++a2) {
+          const f32x4 d = mfma(kb8, a2 ? sel1 : sel0, zero4());
+          uint2 u;
+          u.x = (uint32_t)f32_to_bf16(d[0]) | ((uint32_t)f32_to_bf16(d[1]) << 16);
+          u.y = (uint32_t)f32_to_bf16(d[2]) | ((uint32_t)f32_to_bf16(d[3]) << 16);
+          const int at = 2 * j + a2;
+          *(uint2*)(rec + R::oKbar + ((at * 2 + (w >> 1)) * 64 + lane) * 16 + 8 * (w & 1)) = u;
+        }
+      }
     }
   }
   for (int c = tid; c < K; c += kThreads) ((float*)(rec + R::oGL))[c] = sFac[kF_GL][c];
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) negmax = fmaxf(negmax, __shfl_xor(negmax, off));
-  const bool exact_diag = negmax > kDiagSafe;  // wave-uniform
-  __syncthreads();
+  const bool exact_diag = EXACT && negmax > kDiagSafe;  // wave-uniform
+  if (!EXACT) {
+    __shared__ int sNeedExact;
+    if (tid == 0) sNeedExact = 0;
+    __syncthreads();
+    if (negmax > kDiagSafe && lane == 0) sNeedExact = 1;
+    __syncthreads();
+    if (tid == 0 && sNeedExact) {
+      const int slot = atomicAdd(a.exact_count, 1);
+      a.exact_list[slot] = jchunk * H + h;  // slot < NT*H: each chunk-head appends once
+    }
+  } else {
+    __syncthreads();
+  }
 
   // ---- 5. decayed key/query products, blocks (I <= R = w), transposed tiles ----
   f32x4 dq[4], dk[4];
@@ -346,7 +356,7 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
     dq[I] = zero4();
     dk[I] = zero4();
     if (I > w) continue;
-    if (I == w && exact_diag) continue;
+    if (I == w && exact_diag) continue;  // filled by the exact path below
     // factor row: e^{-Lam_w} on the diagonal, e^{Gam_w - Gam_{I+1}} below it
     int frow = -1;
     if (I == w) frow = kF_EML + w;
@@ -367,84 +377,77 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
       dk[I] = mfma(kc, krow[j], dk[I]);
     }
   }
-  if (exact_diag) {
+  if (EXACT && exact_diag) {
     // exact per-pair path for the diagonal block (the block's decay exceeds the
-    // factorised range): lane (g, n) builds row n against every i of the block.
-    // q^ and k^ are reloaded so that they need not stay live until here.
-    {
-      const bf16* q = (const bf16*)a.q + th * K;
-      const bf16* k = (const bf16*)a.k + th * K;
-#pragma unroll
-      for (int j = 0; j < NKJ; ++j) {
-        const int c0 = 32 * j + 4 * g, c1 = c0 + 16;
-        if (valid) {
-          load4_bf16(q + c0, qv + 8 * j);
-          load4_bf16(q + c1, qv + 8 * j + 4);
-          load4_bf16(k + c0, kv + 8 * j);
-          load4_bf16(k + c1, kv + 8 * j + 4);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) qv[8 * j + e] = kv[8 * j + e] = 0.f;
-        }
-      }
-#pragma unroll
-      for (int s2 = 0; s2 < KL; ++s2) {
-        qv[s2] *= rq;
-        kv[s2] *= rk;
-      }
-    }
-    float aq[16], ak[16];
-#pragma unroll
+    // factorised range).  Lane (g, n) is row n; for every row i of the block the
+    // four g-lanes sum their channels and lane g keeps the sums for i = 4g..4g+3,
+    // which are its entries of the transposed tile.  q^, k^ and lambda are
+    // recomputed so that they need not stay live until here.
+    row_prologue(qv, kv, lam);
+    f32x4 eq = zero4(), ek = zero4();
+#pragma unroll 1
     for (int i = 0; i < 16; ++i) {
       float pq = 0.f, pk = 0.f;
 #pragma unroll
-      for (int s = 0; s < KL; ++s) {
-        const float ki = __shfl(kv[s], 16 * g + i);
-        const float li = __shfl(lam[s], 16 * g + i);
-        const float d = (i <= n) ? fexp(lam[s] - li) : 0.f;
-        pq = fmaf(qv[s] * ki, d, pq);
-        pk = fmaf(kv[s] * ki, d, pk);
+      for (int s2 = 0; s2 < KL; ++s2) {
+        const float ki = __shfl(kv[s2], 16 * g + i);
+        const float li = __shfl(lam[s2], 16 * g + i);
+        const float d = (i <= n) ? fexp(lam[s2] - li) : 0.f;
+        pq = fmaf(qv[s2] * ki, d, pq);
+        pk = fmaf(kv[s2] * ki, d, pk);
       }
       pq += __shfl_xor(pq, 16);
       pq += __shfl_xor(pq, 32);
       pk += __shfl_xor(pk, 16);
       pk += __shfl_xor(pk, 32);
-      aq[i] = pq;
-      ak[i] = pk;
-    }
+      const bool mine = (i >> 2) == g;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      float vq = 0.f, vk = 0.f;
-#pragma unroll
-      for (int gg = 0; gg < 4; ++gg)
-        if (gg == g) {
-          vq = aq[4 * gg + e];
-          vk = ak[4 * gg + e];
-        }
-      dq[w][e] = vq;
-      dk[w][e] = vk;
+      for (int e = 0; e < 4; ++e) {
+        const bool sel = mine && ((i & 3) == e);
+        eq[e] = sel ? pq : eq[e];
+        ek[e] = sel ? pk : ek[e];
+      }
     }
+    dq[w] = eq;
+    dk[w] = ek;
   }
   // masks: Akk strictly lower -> LDS (fp32, row r = 16w+n), Aqk lower incl. diagonal -> record
   {
     const int r = 16 * w + n;
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
-      float4 v4;
-      float* vv = (float*)&v4;
+      float vv[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * I + 4 * g + e;
         vv[e] = (i < r) ? dk[I][e] : 0.f;
         dq[I][e] = (i <= r) ? a.scale * dq[I][e] : 0.f;
       }
-      *(float4*)&sA[r][16 * I + 4 * g] = v4;
+      uint2 u;
+      u.x = (uint32_t)f32_to_bf16(vv[0]) | ((uint32_t)f32_to_bf16(vv[1]) << 16);
+      u.y = (uint32_t)f32_to_bf16(vv[2]) | ((uint32_t)f32_to_bf16(vv[3]) << 16);
+      *(uint2*)&sA[r][16 * I + 4 * g] = u;
     }
     bf16x8* aq = (bf16x8*)(rec + R::oAqk);
     aq[(w * 2 + 0) * 64 + lane] = pair_frag(dq[0], dq[1]);
     aq[(w * 2 + 1) * 64 + lane] = pair_frag(dq[2], dq[3]);
   }
   __syncthreads();
+
+  // this wave's value-pair job (at most one): its V rows are fetched now, so
+  // that the triangular solve hides their latency
+  uint2 vraw[4][2];
+#pragma unroll
+  for (int I = 0; I < 4; ++I) {
+    const int ri = 16 * I + n;
+    vraw[I][0] = make_uint2(0u, 0u);
+    vraw[I][1] = make_uint2(0u, 0u);
+    if (upair >= 0 && ri < L) {
+      const bf16* vp = (const bf16*)a.v + ((int64_t)(tok0 + ri) * H + h) * V + 32 * upair + 4 * g;
+      vraw[I][0] = *(const uint2*)vp;
+      vraw[I][1] = *(const uint2*)(vp + 16);
+    }
+  }
 
   // ---- 6. Tm = (I + Diag(beta) Akk)^-1 in fp32 ----
   // (a) zero Tm's strictly-upper blocks and invert the diagonal blocks by
@@ -462,8 +465,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i4 = 0; i4 < rr; i4 += 4) {
-        const float4 av = *(const float4*)&sA[b0 + rr][b0 + i4];
-        const float ar[4] = {av.x, av.y, av.z, av.w};
+        float ar[4];
+        unpack4(*(const uint2*)&sA[b0 + rr][b0 + i4], ar);
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (i4 + e < rr) acc[e] = fmaf(ar[e], tc[i4 + e], acc[e]);
@@ -480,44 +483,54 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
   // (b) column block I = w, rows R = w+1..3 in order, inside one wave:
   //     Tm_RI = -Tm_RR Diag(beta_R) sum_{J=I}^{R-1} Akk_RJ Tm_JI
   {
-    const int Ib = w;
     const int rho = lane >> 2, k0 = 4 * (lane & 3);
-    for (int Rb = Ib + 1; Rb < 4; ++Rb) {
-      float p[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int J = Ib; J < Rb; ++J) {
+    auto colblock = [&](auto ibc) {
+      constexpr int Ib = decltype(ibc)::value;
+#pragma unroll
+      for (int Rb = Ib + 1; Rb < 4; ++Rb) {
+        float p[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int J = Ib; J < Rb; ++J) {
+#pragma unroll
+          for (int m4 = 0; m4 < 16; m4 += 4) {
+            float ar[4];
+            unpack4(*(const uint2*)&sA[16 * Rb + rho][16 * J + m4], ar);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const float4 tv = *(const float4*)&sT[16 * J + m4 + e][16 * Ib + k0];
+              p[0] = fmaf(ar[e], tv.x, p[0]);
+              p[1] = fmaf(ar[e], tv.y, p[1]);
+              p[2] = fmaf(ar[e], tv.z, p[2]);
+              p[3] = fmaf(ar[e], tv.w, p[3]);
+            }
+          }
+        }
+        const float bt = sBeta[16 * Rb + rho];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sP[Ib][rho][k0 + q] = bt * p[q];
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        float t[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int mu = 0; mu < 16; ++mu) {
-          const float av = sA[16 * Rb + rho][16 * J + mu];
-          const float4 tv = *(const float4*)&sT[16 * J + mu][16 * Ib + k0];
-          p[0] = fmaf(av, tv.x, p[0]);
-          p[1] = fmaf(av, tv.y, p[1]);
-          p[2] = fmaf(av, tv.z, p[2]);
-          p[3] = fmaf(av, tv.w, p[3]);
+          const float tv = sT[16 * Rb + rho][16 * Rb + mu];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) t[q] = fmaf(tv, sP[Ib][mu][k0 + q], t[q]);
         }
+        *(float4*)&sT[16 * Rb + rho][16 * Ib + k0] = make_float4(-t[0], -t[1], -t[2], -t[3]);
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
-      const float bt = sBeta[16 * Rb + rho];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) sP[w][rho][k0 + q] = bt * p[q];
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      float t[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int mu = 0; mu < 16; ++mu) {
-        const float tv = sT[16 * Rb + rho][16 * Rb + mu];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) t[q] = fmaf(tv, sP[w][mu][k0 + q], t[q]);
-      }
-      *(float4*)&sT[16 * Rb + rho][16 * Ib + k0] = make_float4(-t[0], -t[1], -t[2], -t[3]);
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-      __builtin_amdgcn_wave_barrier();
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    }
+    };
+    if (w == 0) colblock(std::integral_constant<int, 0>{});
+    else if (w == 1) colblock(std::integral_constant<int, 1>{});
+    else if (w == 2) colblock(std::integral_constant<int, 2>{});
   }
   __syncthreads();
 
-  // ---- 7. jobs: W (channel pairs), Kbar (channel pairs), U (value pairs) ----
-  const bf16x8 sel0 = select_frag(g, n, 0), sel1 = select_frag(g, n, 1);
+  // ---- 7. jobs: W (channel pairs), U (value pairs) ----
   bf16x8 tfrag[4][2];
 #pragma unroll
   for (int t = 0; t < 4; ++t)
@@ -529,17 +542,16 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
       tfrag[t][j] = pack8(f);
     }
   for (int job = w; job < NJOBS; job += 4) {
-    if (job < 2 * NKJ) {
-      const bool isW = job < NKJ;
-      const int p = isW ? job : job - NKJ;
+    if (job < NKJ) {
+      const int p = job;
       f32x4 did[4][2];
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
-        const bf16x8 src = isW ? sX[I][p][lane] : sKbar[I][p][lane];
+        const bf16x8 src = sX[I][p][lane];
         did[I][0] = mfma(src, sel0, zero4());
         did[I][1] = mfma(src, sel1, zero4());
       }
-      if (isW) {
+      {
         // W^T = X^T Tm^T; X^T fragments from the transposed tiles
         bf16x8 xt[2][2];
 #pragma unroll
@@ -557,16 +569,9 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
           }
           wout[(t * NKJ + p) * 64 + lane] = pair_frag(acc[0], acc[1]);
         }
-      } else {
-        bf16x8* kout = (bf16x8*)(rec + R::oKbar);
-#pragma unroll
-        for (int a2 = 0; a2 < 2; ++a2)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            kout[((2 * p + a2) * 2 + j) * 64 + lane] = pair_frag(did[2 * j][a2], did[2 * j + 1][a2]);
       }
     } else {
-      const int p = job - 2 * NKJ;
+      const int p = job - NKJ;
       f32x4 did[4][2];
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
@@ -598,6 +603,25 @@ __global__ __launch_bounds__(kThreads, 2) void k_chunk_mfma(FwdArgs a) {
           uout[(t * NVT + 2 * p + a2) * 64 + lane] = u;
         }
     }
+  }
+}
+
+template <int K, int V>
+__global__ __launch_bounds__(kThreads, 3) void k_chunk_mfma(FwdArgs a) {
+  const int64_t wid = blockIdx.x;
+  const int jchunk = (int)(wid / a.H), h = (int)(wid % a.H);
+  if (jchunk >= *a.nt_dev) return;
+  chunk_body<K, V, false>(a, jchunk, h);
+}
+
+// Fix-up pass: recomputes the listed chunk-heads with the exact diagonal path.
+template <int K, int V>
+__global__ __launch_bounds__(kThreads) void k_chunk_mfma_exact(FwdArgs a) {
+  const int count = *a.exact_count;
+  for (int i = blockIdx.x; i < count; i += gridDim.x) {
+    const int ch = a.exact_list[i];
+    chunk_body<K, V, true>(a, ch / a.H, ch % a.H);
+    __syncthreads();
   }
 }
 
@@ -896,6 +920,11 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
   if (a.NT > 0) {
     hipLaunchKernelGGL((k_chunk_mfma<K, V>), dim3((unsigned)((int64_t)a.NT * a.H)), dim3(kThreads),
                        0, s, a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    // chunk-heads whose in-block decay left the factorised range (rare; the
+    // grid is fixed and exits at once when the list is empty)
+    const int64_t fix_wgs = std::min<int64_t>((int64_t)a.NT * a.H, 256);
+    hipLaunchKernelGGL((k_chunk_mfma_exact<K, V>), dim3((unsigned)fix_wgs), dim3(kThreads), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   mark(a, kStageChunk, 1, s);

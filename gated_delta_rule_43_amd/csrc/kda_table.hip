@@ -35,9 +35,11 @@ __global__ __launch_bounds__(kTableThreads) void k_chunk_table(const int32_t* __
                                                                int32_t* __restrict__ tok,
                                                                int32_t* __restrict__ len,
                                                                int32_t* __restrict__ seq0,
-                                                               int32_t* __restrict__ nt_out) {
+                                                               int32_t* __restrict__ nt_out,
+                                                               int32_t* __restrict__ zero_out) {
   __shared__ int sh[kTableThreads];
   const int tid = threadIdx.x;
+  if (zero_out && tid == 0) *zero_out = 0;  // counter the later kernels append to
   if (cu == nullptr) {
     const int nc = (T + C - 1) / C;
     for (int n = tid; n <= B; n += kTableThreads) seq0[n] = n * nc;
@@ -123,7 +125,7 @@ __global__ __launch_bounds__(256) void k_apply_summary(int64_t total, int K, int
 hipError_t launch_chunk_table(const FwdArgs& a, hipStream_t s) {
   mark(a, kStageTable, 0, s);
   hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(kTableThreads), 0, s, a.cu, a.N, a.B, a.T, a.C,
-                     a.NT, a.chunk_tok, a.chunk_len, a.seq_chunk0, a.nt_dev);
+                     a.NT, a.chunk_tok, a.chunk_len, a.seq_chunk0, a.nt_dev, a.exact_count);
   hipError_t e = hipGetLastError();
   mark(a, kStageTable, 1, s);
   return e;

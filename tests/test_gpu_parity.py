@@ -256,3 +256,26 @@ def test_apply_without_initial_state_is_state_ext():
     F = kda.kda_apply_state_summary(E, P, S0)
     ref = (P.double() @ S0.double() + E.double()).cpu().numpy()
     assert errors(to_np(F), ref)[0] <= 1e-4
+
+
+# --------------------------------------------------------------------------
+# extreme decays: 16-row blocks whose decay leaves the factorised range
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 64)])
+def test_extreme_gates_exact_diagonal(K, V):
+    """Gate logits of +30 on ~10% of (token, channel) entries make single steps
+    decay by ~50 nats: such blocks must take the exact in-block path."""
+    inp = synthetic.random_problem(41, 1, 300, 2, K, V, dtype=torch.bfloat16, device=DEV,
+                                   init_std=0.5, lengths=[170, 130])
+    gen = torch.Generator(device="cpu").manual_seed(7)
+    spikes = torch.rand(inp["gate"].shape, generator=gen) < 0.1
+    gate = inp["gate"].float().cpu()
+    gate[spikes] = 30.0
+    inp["gate"] = gate.to(torch.bfloat16).to(DEV)
+    inp["a_log"] = torch.full_like(inp["a_log"], 0.5)
+    inp.update(scale=None, lower_bound=None, chunk_size=64)
+    o, fin = gpu_fwd(inp)
+    assert torch.isfinite(o.float()).all() and torch.isfinite(fin).all()
+    o_ref, f_ref = oracle_fwd(inp)
+    assert_close(to_np(o), o_ref, torch.bfloat16, "o")
+    assert_close(to_np(fin), f_ref, torch.bfloat16, "final_state")
