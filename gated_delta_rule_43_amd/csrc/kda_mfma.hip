@@ -79,6 +79,24 @@ __device__ __forceinline__ bf16x8 pair_frag(f32x4 lo, f32x4 hi) {
   }
   return r;
 }
+// four fp32 -> four bf16 in 8 bytes, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint2 pk4(float a, float b, float c, float d) {
+  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  const bf16x4 r = {(__bf16)a, (__bf16)b, (__bf16)c, (__bf16)d};
+  const u32x2 u = __builtin_bit_cast(u32x2, r);
+  return make_uint2(u.x, u.y);
+}
+__device__ __forceinline__ uint2 pk4(f32x4 v) { return pk4(v[0], v[1], v[2], v[3]); }
+// x = hi + lo with hi = bf16(x) and lo = x - hi (exact in fp32), both returned
+// as fp32 values that are exactly representable in bf16 (hi) or rounded once (lo)
+__device__ __forceinline__ void split4(f32x4 x, f32x4& hi, f32x4& lo) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    hi[e] = (float)(__bf16)x[e];
+    lo[e] = x[e] - hi[e];
+  }
+}
 __device__ __forceinline__ void unpack4(uint2 u, float* out) {
   out[0] = bf16_to_f32((bf16)(u.x & 0xffff));
   out[1] = bf16_to_f32((bf16)(u.x >> 16));
@@ -168,8 +186,8 @@ enum {
 // One chunk-head.  EXACT = false: the common kernel; a 16-row block whose
 // decay exceeds the factorised range makes the workgroup append the chunk-head
 // to a fix-up list instead.  EXACT = true: the fix-up, with the exact per-pair
-// path on such blocks.
-template <int K, int V, bool EXACT>
+// path on such blocks.  LB: the gate has a lower bound (sigmoid form).
+template <int K, int V, bool EXACT, bool LB>
 __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, const int h) {
   using R = Rec<K, V>;
   constexpr int NKJ = K / 32, NVJ = V / 32, NVT = V / 16, KL = K / 4;
@@ -182,12 +200,12 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
   const int64_t th = (int64_t)(tok0 + (valid ? row : 0)) * H + h;  // token-head index
   char* rec = (char*)a.rec + ((int64_t)jchunk * H + h) * R::kBytes;
 
-  // the factor table (steps 3-5) and the solve's scratch sP (step 6) share storage
+  // the factor table (steps 3-5) and the diagonal Akk blocks (step 6) share storage
   __shared__ __attribute__((aligned(16))) float sFacMem[kNF * K];
   float (*sFac)[K] = (float(*)[K])sFacMem;
-  float (*sP)[16][17] = (float(*)[16][17])sFacMem;
-  static_assert(4 * 16 * 17 <= kNF * K, "sP must fit in the factor table");
-  __shared__ float sBeta[kC];
+  float (*sDg)[16][16] = (float(*)[16][16])sFacMem;  // fp32 diagonal Akk blocks (step 6)
+  static_assert(4 * 16 * 16 <= kNF * K, "sDg must fit in the factor table");
+  __shared__ __attribute__((aligned(16))) float sBeta[kC];
   __shared__ bf16x8 sX[4][NKJ][64];
   __shared__ __attribute__((aligned(16))) bf16 sA[kC][72];  // Akk (bf16), rows padded
   // sKb (fragments, steps 4-5) and sT (triangular inverse, steps 6-7) share storage
@@ -208,23 +226,20 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
     const bf16* k = (const bf16*)a.k + th * K;
     const bf16* gt = (const bf16*)a.gate + th * K;
     const float* db = a.dt_bias + (int64_t)h * K;
+    // rows past the chunk end read the chunk's first row (th is clamped) and
+    // are zeroed below through the norm scale and the gate select
 #pragma unroll
     for (int j = 0; j < NKJ; ++j) {
       const int c0 = 32 * j + 4 * g, c1 = c0 + 16;
-      if (valid) {
-        load4_bf16(q + c0, qv + 8 * j);
-        load4_bf16(q + c1, qv + 8 * j + 4);
-        load4_bf16(k + c0, kv + 8 * j);
-        load4_bf16(k + c1, kv + 8 * j + 4);
-        load4_bf16(gt + c0, lam + 8 * j);
-        load4_bf16(gt + c1, lam + 8 * j + 4);
-        const float4 d0 = *(const float4*)(db + c0), d1 = *(const float4*)(db + c1);
-        lam[8 * j + 0] += d0.x; lam[8 * j + 1] += d0.y; lam[8 * j + 2] += d0.z; lam[8 * j + 3] += d0.w;
-        lam[8 * j + 4] += d1.x; lam[8 * j + 5] += d1.y; lam[8 * j + 6] += d1.z; lam[8 * j + 7] += d1.w;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qv[8 * j + e] = kv[8 * j + e] = lam[8 * j + e] = 0.f;
-      }
+      load4_bf16(q + c0, qv + 8 * j);
+      load4_bf16(q + c1, qv + 8 * j + 4);
+      load4_bf16(k + c0, kv + 8 * j);
+      load4_bf16(k + c1, kv + 8 * j + 4);
+      load4_bf16(gt + c0, lam + 8 * j);
+      load4_bf16(gt + c1, lam + 8 * j + 4);
+      const float4 d0 = *(const float4*)(db + c0), d1 = *(const float4*)(db + c1);
+      lam[8 * j + 0] += d0.x; lam[8 * j + 1] += d0.y; lam[8 * j + 2] += d0.z; lam[8 * j + 3] += d0.w;
+      lam[8 * j + 4] += d1.x; lam[8 * j + 5] += d1.y; lam[8 * j + 6] += d1.z; lam[8 * j + 7] += d1.w;
     }
     float ssq = 0.f, ssk = 0.f;
 #pragma unroll
@@ -236,14 +251,17 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
     ssq += __shfl_xor(ssq, 32);
     ssk += __shfl_xor(ssk, 16);
     ssk += __shfl_xor(ssk, 32);
-    const float rq = __builtin_amdgcn_rsqf(ssq + 1e-6f), rk = __builtin_amdgcn_rsqf(ssk + 1e-6f);
+    const float rq = valid ? __builtin_amdgcn_rsqf(ssq + 1e-6f) : 0.f;
+    const float rk = valid ? __builtin_amdgcn_rsqf(ssk + 1e-6f) : 0.f;
     const float A = fexp(a.a_log[h]);
+    const float vmask = valid ? 1.f : 0.f;  // the gate is finite (floored), so masking multiplies
 #pragma unroll
     for (int s2 = 0; s2 < KL; ++s2) {
       qv[s2] *= rq;
       kv[s2] *= rk;
-      lam[s2] = row_scan16(valid ? fgate(lam[s2], A, a.has_lb, a.lb) : 0.f);
     }
+#pragma unroll
+    for (int s2 = 0; s2 < KL; ++s2) lam[s2] = row_scan16(vmask * fgate(lam[s2], A, LB, a.lb));
   };
   float qv[KL], kv[KL], lam[KL];
   row_prologue(qv, kv, lam);
@@ -285,17 +303,18 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
 
   // ---- 4. per-element factors; fragments to LDS and to the record ----
   const bf16x8 sel0 = select_frag(g, n, 0), sel1 = select_frag(g, n, 1);
-  bf16x8 qrow[NKJ], krow[NKJ], kbown[NKJ];
+  bf16x8 qrow[NKJ], krow[NKJ], kdiag[NKJ];
   float negmax = 0.f;
   {
     const float scale = a.scale;
 #pragma unroll
     for (int j = 0; j < NKJ; ++j) {
-      float lt[8], eg[8], el[8];
+      float lt[8], eg[8], el[8], eml[8];
       fac8(kF_LAM + w, j, lt);
       fac8(kF_EG + w, j, eg);
       fac8(kF_EL + w, j, el);
-      float fq[8], fk[8], fx[8], fkb[8], fkbar[8], fqr[8];
+      fac8(kF_EML + w, j, eml);
+      float fq[8], fk[8], fx[8], fkb[8], fkbar[8], fqr[8], fkd[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float l = lam[8 * j + e];
@@ -308,13 +327,16 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
         fx[e] = beta_r * fk[e] * eg[e];
         fkb[e] = kv[8 * j + e] * F;
         fkbar[e] = fkb[e] * el[e];
+        fkd[e] = fkb[e] * eml[e];            // e^{-gamma_r + Gam_w}: diagonal block
       }
       qrow[j] = pack8(fqr);
       krow[j] = pack8(fk);
-      kbown[j] = pack8(fkb);
+      kdiag[j] = pack8(fkd);
+      // keep the packed fragments (not their fp32 sources) live into step 5
+      asm volatile("" : "+v"(qrow[j]), "+v"(krow[j]), "+v"(kdiag[j]));
       ((bf16x8*)(rec + R::oQt))[(w * NKJ + j) * 64 + lane] = pack8(fq);
       sX[w][j][lane] = pack8(fx);
-      sKb[w][j][lane] = kbown[j];
+      sKb[w][j][lane] = pack8(fkb);
       // Kbar^T fragments (a, w/2): this block's rows transposed on the matrix
       // cores, written as the (w%2) half of each lane's 16 bytes
       {
@@ -322,9 +344,7 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
 #pragma unroll
         for (int a2 = 0; a2 < 2; ++a2) {
           const f32x4 d = mfma(kb8, a2 ? sel1 : sel0, zero4());
-          uint2 u;
-          u.x = (uint32_t)f32_to_bf16(d[0]) | ((uint32_t)f32_to_bf16(d[1]) << 16);
-          u.y = (uint32_t)f32_to_bf16(d[2]) | ((uint32_t)f32_to_bf16(d[3]) << 16);
+          const uint2 u = pk4(d);
           const int at = 2 * j + a2;
           *(uint2*)(rec + R::oKbar + ((at * 2 + (w >> 1)) * 64 + lane) * 16 + 8 * (w & 1)) = u;
         }
@@ -357,15 +377,15 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
     dk[I] = zero4();
     if (I > w) continue;
     if (I == w && exact_diag) continue;  // filled by the exact path below
-    // factor row: e^{-Lam_w} on the diagonal, e^{Gam_w - Gam_{I+1}} below it
+    // factor row e^{Gam_w - Gam_{I+1}} below the diagonal (the diagonal
+    // operand already carries e^{-Lam_w})
     int frow = -1;
-    if (I == w) frow = kF_EML + w;
-    else if (w == 2 && I == 0) frow = kF_M20;
+    if (w == 2 && I == 0) frow = kF_M20;
     else if (w == 3 && I == 0) frow = kF_M30;
     else if (w == 3 && I == 1) frow = kF_M31;
 #pragma unroll
     for (int j = 0; j < NKJ; ++j) {
-      bf16x8 kc = (I == w) ? kbown[j] : sKb[I][j][lane];
+      bf16x8 kc = (I == w) ? kdiag[j] : sKb[I][j][lane];
       if (frow >= 0) {
         float m[8], f[8];
         fac8(frow, j, m);
@@ -411,7 +431,9 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
     dq[w] = eq;
     dk[w] = ek;
   }
-  // masks: Akk strictly lower -> LDS (fp32, row r = 16w+n), Aqk lower incl. diagonal -> record
+  // masks: Akk strictly lower -> LDS (bf16, row r = 16w+n; the diagonal block
+  // also in fp32 after the barrier), Aqk lower incl. diagonal -> record
+  float4 dgv;
   {
     const int r = 16 * w + n;
 #pragma unroll
@@ -423,10 +445,8 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
         vv[e] = (i < r) ? dk[I][e] : 0.f;
         dq[I][e] = (i <= r) ? a.scale * dq[I][e] : 0.f;
       }
-      uint2 u;
-      u.x = (uint32_t)f32_to_bf16(vv[0]) | ((uint32_t)f32_to_bf16(vv[1]) << 16);
-      u.y = (uint32_t)f32_to_bf16(vv[2]) | ((uint32_t)f32_to_bf16(vv[3]) << 16);
-      *(uint2*)&sA[r][16 * I + 4 * g] = u;
+      *(uint2*)&sA[r][16 * I + 4 * g] = pk4(vv[0], vv[1], vv[2], vv[3]);
+      if (I == w) dgv = make_float4(vv[0], vv[1], vv[2], vv[3]);
     }
     bf16x8* aq = (bf16x8*)(rec + R::oAqk);
     aq[(w * 2 + 0) * 64 + lane] = pair_frag(dq[0], dq[1]);
@@ -436,43 +456,53 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
 
   // this wave's value-pair job (at most one): its V rows are fetched now, so
   // that the triangular solve hides their latency
+  // (rows past the chunk end read row 0 and are zeroed by their beta = 0)
   uint2 vraw[4][2];
+  if (upair >= 0) {
 #pragma unroll
-  for (int I = 0; I < 4; ++I) {
-    const int ri = 16 * I + n;
-    vraw[I][0] = make_uint2(0u, 0u);
-    vraw[I][1] = make_uint2(0u, 0u);
-    if (upair >= 0 && ri < L) {
+    for (int I = 0; I < 4; ++I) {
+      const int ri = 16 * I + n < L ? 16 * I + n : 0;
       const bf16* vp = (const bf16*)a.v + ((int64_t)(tok0 + ri) * H + h) * V + 32 * upair + 4 * g;
       vraw[I][0] = *(const uint2*)vp;
       vraw[I][1] = *(const uint2*)(vp + 16);
     }
   }
 
-  // ---- 6. Tm = (I + Diag(beta) Akk)^-1 in fp32 ----
-  // (a) zero Tm's strictly-upper blocks and invert the diagonal blocks by
-  //     forward substitution.  Every lane (g, n) builds column n of block w in
-  //     full (the 4 g-lanes redundantly), reading each row of Akk as float4
-  //     broadcasts; the g = 0 lanes write the column.
+  // ---- 6. Tm = (I + Diag(beta) Akk)^-1 ----
+  // (a) zero Tm's strictly-upper blocks and invert the diagonal blocks in fp32
+  //     by forward substitution.  Every lane (g, n) builds column n of block w
+  //     in full (the 4 g-lanes redundantly), reading each row of the fp32
+  //     diagonal block as float4 broadcasts; the g = 0 lanes write the column.
+  *(float4*)&sDg[w][n][4 * g] = dgv;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   {
     const int b0 = 16 * w;
 #pragma unroll
     for (int I = 0; I < 4; ++I)
       if (I > w) *(float4*)&sT[b0 + n][16 * I + 4 * g] = make_float4(0.f, 0.f, 0.f, 0.f);
+    float bw[16];
+#pragma unroll
+    for (int i4 = 0; i4 < 16; i4 += 4) {
+      const float4 b4 = *(const float4*)&sBeta[b0 + i4];
+      bw[i4] = b4.x; bw[i4 + 1] = b4.y; bw[i4 + 2] = b4.z; bw[i4 + 3] = b4.w;
+    }
     float tc[16];
 #pragma unroll
     for (int rr = 0; rr < 16; ++rr) {
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i4 = 0; i4 < rr; i4 += 4) {
-        float ar[4];
-        unpack4(*(const uint2*)&sA[b0 + rr][b0 + i4], ar);
+        const float4 a4 = *(const float4*)&sDg[w][rr][i4];
+        const float ar[4] = {a4.x, a4.y, a4.z, a4.w};
 #pragma unroll
         for (int e = 0; e < 4; ++e)
           if (i4 + e < rr) acc[e] = fmaf(ar[e], tc[i4 + e], acc[e]);
       }
       const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-      tc[rr] = (n == rr) ? 1.f : ((n < rr) ? -sBeta[b0 + rr] * sum : 0.f);
+      // 1 on the diagonal, -beta * sum below it, 0 above (sum is finite)
+      tc[rr] = fmaf((n < rr) ? -bw[rr] : 0.f, sum, (n == rr) ? 1.f : 0.f);
     }
     if (g == 0) {
 #pragma unroll
@@ -480,48 +510,51 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
     }
   }
   __syncthreads();
-  // (b) column block I = w, rows R = w+1..3 in order, inside one wave:
-  //     Tm_RI = -Tm_RR Diag(beta_R) sum_{J=I}^{R-1} Akk_RJ Tm_JI
+  // (b) column block Ib = w, block rows R = w+1..3 in order, inside one wave,
+  //     on the matrix cores: Tm_{R,Ib} = -Tm_RR Diag(beta_R) sum_{J=Ib}^{R-1}
+  //     Akk_RJ Tm_{J,Ib}.  Tm enters the products as bf16 hi + lo parts (about
+  //     16 significant bits); Akk is bf16 already.  Tiles are kept in the
+  //     accumulator layout (lane (g, n): rows 4g..4g+3, column n), two of which
+  //     form one B operand in sigma order.
   {
-    const int rho = lane >> 2, k0 = 4 * (lane & 3);
     auto colblock = [&](auto ibc) {
       constexpr int Ib = decltype(ibc)::value;
+      f32x4 tcol[4];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) tcol[Ib][e] = sT[16 * Ib + 4 * g + e][16 * Ib + n];
 #pragma unroll
       for (int Rb = Ib + 1; Rb < 4; ++Rb) {
-        float p[4] = {0.f, 0.f, 0.f, 0.f};
+        f32x4 p = zero4();
 #pragma unroll
-        for (int J = Ib; J < Rb; ++J) {
-#pragma unroll
-          for (int m4 = 0; m4 < 16; m4 += 4) {
-            float ar[4];
-            unpack4(*(const uint2*)&sA[16 * Rb + rho][16 * J + m4], ar);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const float4 tv = *(const float4*)&sT[16 * J + m4 + e][16 * Ib + k0];
-              p[0] = fmaf(ar[e], tv.x, p[0]);
-              p[1] = fmaf(ar[e], tv.y, p[1]);
-              p[2] = fmaf(ar[e], tv.z, p[2]);
-              p[3] = fmaf(ar[e], tv.w, p[3]);
-            }
-          }
+        for (int J0 = Ib; J0 < Rb; J0 += 2) {
+          const bool two = J0 + 1 < Rb;
+          float av[8];
+          unpack4(*(const uint2*)&sA[16 * Rb + n][16 * J0 + 4 * g], av);
+          if (two) unpack4(*(const uint2*)&sA[16 * Rb + n][16 * J0 + 16 + 4 * g], av + 4);
+          else av[4] = av[5] = av[6] = av[7] = 0.f;
+          const bf16x8 af = pack8(av);
+          const f32x4 t1 = two ? tcol[J0 + 1] : zero4();
+          f32x4 h0, h1, l0, l1;
+          split4(tcol[J0], h0, l0);
+          split4(t1, h1, l1);
+          p = mfma(af, pair_frag(h0, h1), p);
+          p = mfma(af, pair_frag(l0, l1), p);
         }
-        const float bt = sBeta[16 * Rb + rho];
+        const float4 bt = *(const float4*)&sBeta[16 * Rb + 4 * g];
+        const f32x4 y = {bt.x * p[0], bt.y * p[1], bt.z * p[2], bt.w * p[3]};
+        f32x4 yh, yl;
+        split4(y, yh, yl);
+        const float4 td = *(const float4*)&sT[16 * Rb + n][16 * Rb + 4 * g];
+        f32x4 th, tl;
+        split4(f32x4{td.x, td.y, td.z, td.w}, th, tl);
+        const bf16x8 tf = pair_frag(th, tl);  // [Tm_RR hi | Tm_RR lo] along k
+        f32x4 d = mfma(tf, pair_frag(yh, yh), zero4());
+        d = mfma(tf, pair_frag(yl, yl), d);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sP[Ib][rho][k0 + q] = bt * p[q];
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-        float t[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int mu = 0; mu < 16; ++mu) {
-          const float tv = sT[16 * Rb + rho][16 * Rb + mu];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) t[q] = fmaf(tv, sP[Ib][mu][k0 + q], t[q]);
+        for (int e = 0; e < 4; ++e) {
+          tcol[Rb][e] = -d[e];
+          sT[16 * Rb + 4 * g + e][16 * Ib + n] = -d[e];
         }
-        *(float4*)&sT[16 * Rb + rho][16 * Ib + k0] = make_float4(-t[0], -t[1], -t[2], -t[3]);
-        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-        __builtin_amdgcn_wave_barrier();
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
       }
     };
     if (w == 0) colblock(std::integral_constant<int, 0>{});
@@ -597,30 +630,27 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
         for (int a2 = 0; a2 < 2; ++a2) {
           f32x4 acc = mfma(tfrag[t][0], vb[0][a2], zero4());
           if (t >= 2) acc = mfma(tfrag[t][1], vb[1][a2], acc);
-          uint2 u;
-          u.x = (uint32_t)f32_to_bf16(acc[0]) | ((uint32_t)f32_to_bf16(acc[1]) << 16);
-          u.y = (uint32_t)f32_to_bf16(acc[2]) | ((uint32_t)f32_to_bf16(acc[3]) << 16);
-          uout[(t * NVT + 2 * p + a2) * 64 + lane] = u;
+          uout[(t * NVT + 2 * p + a2) * 64 + lane] = pk4(acc);
         }
     }
   }
 }
 
-template <int K, int V>
+template <int K, int V, bool LB>
 __global__ __launch_bounds__(kThreads, 3) void k_chunk_mfma(FwdArgs a) {
   const int64_t wid = blockIdx.x;
   const int jchunk = (int)(wid / a.H), h = (int)(wid % a.H);
   if (jchunk >= *a.nt_dev) return;
-  chunk_body<K, V, false>(a, jchunk, h);
+  chunk_body<K, V, false, LB>(a, jchunk, h);
 }
 
 // Fix-up pass: recomputes the listed chunk-heads with the exact diagonal path.
-template <int K, int V>
+template <int K, int V, bool LB>
 __global__ __launch_bounds__(kThreads) void k_chunk_mfma_exact(FwdArgs a) {
   const int count = *a.exact_count;
   for (int i = blockIdx.x; i < count; i += gridDim.x) {
     const int ch = a.exact_list[i];
-    chunk_body<K, V, true>(a, ch / a.H, ch % a.H);
+    chunk_body<K, V, true, LB>(a, ch / a.H, ch % a.H);
     __syncthreads();
   }
 }
@@ -843,8 +873,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         for (int t = 0; t < 4; ++t) {
           Y[t] = mfma(db[0], fA[t][0], Y[t]);
           if (t >= 2) Y[t] = mfma(db[1], fA[t][1], Y[t]);
-          opend[ct][t].x = (uint32_t)f32_to_bf16(Y[t][0]) | ((uint32_t)f32_to_bf16(Y[t][1]) << 16);
-          opend[ct][t].y = (uint32_t)f32_to_bf16(Y[t][2]) | ((uint32_t)f32_to_bf16(Y[t][3]) << 16);
+          opend[ct][t] = pk4(Y[t]);
         }
       }
 #pragma unroll
@@ -918,13 +947,15 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
   mark(a, kStagePrologue, 1, s);
   mark(a, kStageChunk, 0, s);
   if (a.NT > 0) {
-    hipLaunchKernelGGL((k_chunk_mfma<K, V>), dim3((unsigned)((int64_t)a.NT * a.H)), dim3(kThreads),
-                       0, s, a);
+    const dim3 grid((unsigned)((int64_t)a.NT * a.H)), block(kThreads);
+    if (a.has_lb) hipLaunchKernelGGL((k_chunk_mfma<K, V, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_chunk_mfma<K, V, false>), grid, block, 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     // chunk-heads whose in-block decay left the factorised range (rare; the
     // grid is fixed and exits at once when the list is empty)
-    const int64_t fix_wgs = std::min<int64_t>((int64_t)a.NT * a.H, 256);
-    hipLaunchKernelGGL((k_chunk_mfma_exact<K, V>), dim3((unsigned)fix_wgs), dim3(kThreads), 0, s, a);
+    const dim3 fix_grid((unsigned)std::min<int64_t>((int64_t)a.NT * a.H, 256));
+    if (a.has_lb) hipLaunchKernelGGL((k_chunk_mfma_exact<K, V, true>), fix_grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_chunk_mfma_exact<K, V, false>), fix_grid, block, 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   mark(a, kStageChunk, 1, s);
