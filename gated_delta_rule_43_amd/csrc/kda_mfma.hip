@@ -188,17 +188,21 @@ enum {
 // to a fix-up list instead.  EXACT = true: the fix-up, with the exact per-pair
 // path on such blocks.  LB: the gate has a lower bound (sigmoid form).
 template <int K, int V, bool EXACT, bool LB>
-__device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, const int h) {
+__device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, const int h,
+                                           const int tok0, const int L) {
   using R = Rec<K, V>;
   constexpr int NKJ = K / 32, NVJ = V / 32, NVT = V / 16, KL = K / 4;
   const int H = a.H;
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tok0 = a.chunk_tok[jchunk], L = a.chunk_len[jchunk];
   const int row = 16 * w + n;
   const bool valid = row < L;
   const int64_t th = (int64_t)(tok0 + (valid ? row : 0)) * H + h;  // token-head index
   char* rec = (char*)a.rec + ((int64_t)jchunk * H + h) * R::kBytes;
+  // beta and a_log are issued with the row loads so that their latency is not
+  // paid again after them
+  const bf16 braw = ((const bf16*)a.beta)[th];
+  const float alog = a.a_log[h];
 
   // the factor table (steps 3-5) and the diagonal Akk blocks (step 6) share storage
   __shared__ __attribute__((aligned(16))) float sFacMem[kNF * K];
@@ -253,7 +257,7 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
     ssk += __shfl_xor(ssk, 32);
     const float rq = valid ? __builtin_amdgcn_rsqf(ssq + 1e-6f) : 0.f;
     const float rk = valid ? __builtin_amdgcn_rsqf(ssk + 1e-6f) : 0.f;
-    const float A = fexp(a.a_log[h]);
+    const float A = fexp(alog);
     const float vmask = valid ? 1.f : 0.f;  // the gate is finite (floored), so masking multiplies
 #pragma unroll
     for (int s2 = 0; s2 < KL; ++s2) {
@@ -265,7 +269,7 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
   };
   float qv[KL], kv[KL], lam[KL];
   row_prologue(qv, kv, lam);
-  const float beta_r = valid ? fsigmoid(bf16_to_f32(((const bf16*)a.beta)[th])) : 0.f;
+  const float beta_r = valid ? fsigmoid(bf16_to_f32(braw)) : 0.f;
   if (n == 15) {
 #pragma unroll
     for (int j = 0; j < NKJ; ++j)
@@ -638,10 +642,15 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
 
 template <int K, int V, bool LB>
 __global__ __launch_bounds__(kThreads, 3) void k_chunk_mfma(FwdArgs a) {
-  const int64_t wid = blockIdx.x;
-  const int jchunk = (int)(wid / a.H), h = (int)(wid % a.H);
-  if (jchunk >= *a.nt_dev) return;
-  chunk_body<K, V, false, LB>(a, jchunk, h);
+  const unsigned wid = blockIdx.x, H = (unsigned)a.H;
+  const int jchunk = (int)(wid / H), h = (int)(wid % H);
+  // the table holds at least gridDim.x / H entries, so the reads below stay in
+  // bounds; they are issued together with the count, ahead of its test
+  const int nt = *a.nt_dev;
+  const int tok0 = a.chunk_tok[jchunk], L = a.chunk_len[jchunk];
+  asm volatile("" ::"s"(tok0), "s"(L));
+  if (jchunk >= nt) return;
+  chunk_body<K, V, false, LB>(a, jchunk, h, tok0, L);
 }
 
 // Fix-up pass: recomputes the listed chunk-heads with the exact diagonal path.
@@ -650,7 +659,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_mfma_exact(FwdArgs a) {
   const int count = *a.exact_count;
   for (int i = blockIdx.x; i < count; i += gridDim.x) {
     const int ch = a.exact_list[i];
-    chunk_body<K, V, true, LB>(a, ch / a.H, ch % a.H);
+    const int jchunk = ch / a.H;
+    chunk_body<K, V, true, LB>(a, jchunk, ch % a.H, a.chunk_tok[jchunk], a.chunk_len[jchunk]);
     __syncthreads();
   }
 }
