@@ -669,8 +669,13 @@ __global__ __launch_bounds__(kThreads) void k_chunk_mfma_exact(FwdArgs a) {
 // Kernel B: state pass and output.  SUM = summary mode (state columns only,
 // with the transition columns [V, V+K) that start as I and carry no values).
 // ---------------------------------------------------------------------------
+// Four compute waves own the column tiles; a fifth wave only streams the next
+// chunk's record into LDS, so that the compute waves never stall on those loads.
+constexpr int kStateComputeWaves = 4;
+constexpr int kStateThreads = 64 * (kStateComputeWaves + 1);
+
 template <int K, int V, int NCT, bool SUM>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_state_mfma(FwdArgs a) {
+__global__ __launch_bounds__(kStateThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_state_mfma(FwdArgs a) {
   using R = Rec<K, V>;
   constexpr int NKJ = K / 32, NKT = K / 16, NVT = V / 16;
   constexpr int ncols = SUM ? V + K : V;
@@ -696,6 +701,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   constexpr int kStageBytes = R::kStageRounds * 4096;
   __shared__ __attribute__((aligned(16))) char sStage0[kStageBytes];
   __shared__ __attribute__((aligned(16))) char sStage1[kStageBytes];
+  const int jc0 = a.seq_chunk0[seq], jc1 = a.seq_chunk0[seq + 1];
+  const char* recbase = (const char*)a.rec;
+
+  if (w == kStateComputeWaves) {
+    // the loader wave: copies chunk c+1's record into LDS while chunk c is
+    // consumed; one barrier per chunk, as the compute waves
+    // (the LDS side of the copy is a compile-time buffer: its address goes to M0)
+    auto stage = [&](int jc, auto bufc) {
+      char* const dst = decltype(bufc)::value ? sStage1 : sStage0;
+      const char* rec = recbase + ((int64_t)jc * H + h) * R::kBytes;
+#pragma unroll
+      for (int i = 0; i < 4 * R::kStageRounds; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(rec + (lane + 64 * i) * 16),
+                                         (lds_void*)(&dst[(64 * i) * 16]), 16, 0, 0);
+    };
+    if (jc0 < jc1) stage(jc0, std::integral_constant<int, 0>{});
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    for (int jc = jc0; jc < jc1; jc += 2) {
+      if (jc + 1 < jc1) stage(jc + 1, std::integral_constant<int, 1>{});
+      __builtin_amdgcn_s_waitcnt(0);
+      __syncthreads();
+      if (jc + 1 < jc1) {
+        if (jc + 2 < jc1) stage(jc + 2, std::integral_constant<int, 0>{});
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+      }
+    }
+    return;
+  }
 
   int ctg[NCT];
 #pragma unroll
@@ -721,8 +756,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
       }
   }
 
-  const int jc0 = a.seq_chunk0[seq], jc1 = a.seq_chunk0[seq + 1];
-  const char* recbase = (const char*)a.rec;
   // U tiles of this wave's column tiles for one chunk (zero for transition columns)
   uint2 ucur[NCT][4], unext[NCT][4];
 #pragma unroll
@@ -732,10 +765,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   int tok_cur = 0, len_cur = 0, tok_nxt = 0, len_nxt = 0;
   if (jc0 < jc1) {
     const char* rec = recbase + ((int64_t)jc0 * H + h) * R::kBytes;
-#pragma unroll
-    for (int i = 0; i < R::kStageRounds; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(rec + (tid + kThreads * i) * 16),
-                                       (lds_void*)(&sStage0[(w * 64 + kThreads * i) * 16]), 16, 0, 0);
     const uint2* ug = (const uint2*)(rec + R::oU);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -780,24 +809,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
     }
   };
 
-  // one chunk; BUF (compile-time) is the stage buffer holding it, the next
-  // record streams into the other one.  Two distinct buffers let the compiler
-  // see that the async copy never aliases the reads.
+  // one chunk; BUF (compile-time) is the stage buffer holding it while the
+  // loader wave fills the other one.
   auto chunk_step = [&](int jc, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
     char* const cur = BUF ? sStage1 : sStage0;
-    char* const nxt = BUF ? sStage0 : sStage1;
-    // the next record (the current one again on the last chunk: harmless, and
-    // it keeps the body free of branches)
+    // the next chunk's U tiles and table entries (the current chunk's again on
+    // the last chunk: harmless, and it keeps the body free of branches)
     const int jn = (jc + 1 < jc1) ? jc + 1 : jc;
     if (!SUM) store_out();
     {
       const char* rec = recbase + ((int64_t)jn * H + h) * R::kBytes;
-#pragma unroll
-      for (int i = 0; i < R::kStageRounds; ++i)
-        __builtin_amdgcn_global_load_lds((const void*)(rec + (tid + kThreads * i) * 16),
-                                         (lds_void*)(&nxt[(w * 64 + kThreads * i) * 16]),
-                                         16, 0, 0);
       const uint2* ug = (const uint2*)(rec + R::oU);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
@@ -896,16 +918,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
         S[at][ct] = acc;
       }
     }
-    // spread the memory instructions over the matrix-core stream
+    // spread the LDS reads and memory instructions over the matrix-core stream
 #pragma unroll
     for (int i = 0; i < 14; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 3, 0);  // LDS reads
+      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS reads
       __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x010, 2, 0);  // global memory
+      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // global memory
     }
     otok = tok_cur;
     olen = len_cur;
-    // the next record has landed (own copies), and every wave is done with this buffer
+    // the next record has landed (the loader waited for it), and every wave is
+    // done with this buffer
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 #pragma unroll
@@ -942,15 +965,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1))
   }
 }
 
-// Column tiles per wave in the state pass: one (a workgroup covers 64 state
-// columns), which measures faster than two on MI355X; KDA_STATE_NCT=2 selects
-// two where the column count allows it.
-inline int state_nct(const FwdArgs& a, int V) {
-  const char* env = std::getenv("KDA_STATE_NCT");
-  const int ncols = a.summary ? V + a.K : V;
-  return (env && env[0] == '2' && ncols % 128 == 0) ? 2 : 1;
-}
-
 template <int K, int V>
 hipError_t run(const FwdArgs& a, hipStream_t s) {
   mark(a, kStagePrologue, 0, s);
@@ -970,21 +984,14 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
   }
   mark(a, kStageChunk, 1, s);
   mark(a, kStageState, 0, s);
+  // one 16-column tile per compute wave: a workgroup covers 64 state columns
   const int ncols = a.summary ? V + K : V;
-  const int nct = state_nct(a, V);
-  const int ntile_wg = ncols / 16 / (4 * nct);
+  const int ntile_wg = ncols / 16 / kStateComputeWaves;
   const int64_t wgs = ((int64_t)a.N * a.H + kXcds - 1) / kXcds * kXcds * ntile_wg;
   if (wgs > 0 && (a.summary || a.fin || a.NT > 0)) {
-    const dim3 grid((unsigned)wgs), block(kThreads);
-    if (a.summary) {
-      if constexpr (((V + K) / 16) % 8 == 0)
-        if (nct == 2) hipLaunchKernelGGL((k_state_mfma<K, V, 2, true>), grid, block, 0, s, a);
-      if (nct == 1) hipLaunchKernelGGL((k_state_mfma<K, V, 1, true>), grid, block, 0, s, a);
-    } else {
-      if constexpr ((V / 16) % 8 == 0)
-        if (nct == 2) hipLaunchKernelGGL((k_state_mfma<K, V, 2, false>), grid, block, 0, s, a);
-      if (nct == 1) hipLaunchKernelGGL((k_state_mfma<K, V, 1, false>), grid, block, 0, s, a);
-    }
+    const dim3 grid((unsigned)wgs), block(kStateThreads);
+    if (a.summary) hipLaunchKernelGGL((k_state_mfma<K, V, 1, true>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_state_mfma<K, V, 1, false>), grid, block, 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   mark(a, kStageState, 1, s);
