@@ -154,13 +154,13 @@ struct Rec {
   static constexpr int oQt = 0;                             // [4][NKJ] frags
   static constexpr int oW = oQt + 4 * NKJ * kFrag;          // [4][NKJ] frags
   static constexpr int oKbar = oW + 4 * NKJ * kFrag;        // [NKT][2] frags
-  static constexpr int oAqk = oKbar + NKT * 2 * kFrag;      // [4][2] frags
-  static constexpr int oGL = oAqk + 8 * kFrag;              // [K] fp32
+  static constexpr int oGL = oKbar + NKT * 2 * kFrag;       // [K] fp32
   static constexpr int kStage = oGL + K * 4;                // staged into LDS by the state pass
-  static constexpr int oU = kStage;                         // [4][NVT] tiles of 64 lanes x 8 B
+  static constexpr int oAqk = kStage;                       // [4][2] frags (read straight to registers)
+  static constexpr int oU = oAqk + 8 * kFrag;               // [4][NVT] tiles of 64 lanes x 8 B
   static constexpr int kBytes = oU + 4 * NVT * 512;
-  // the state pass copies whole 4 KiB rounds (256 threads x 16 B); the rounded
-  // stage still ends inside the record
+  // the state pass copies whole 4 KiB rounds (64 lanes x 16 B x 4); the
+  // rounded stage still ends inside the record
   static constexpr int kStageRounds = (kStage + 4095) / 4096;
   static_assert(kStage % 16 == 0 && kBytes % 256 == 0, "record alignment");
   static_assert(kStageRounds * 4096 <= kBytes, "rounded stage must stay inside the record");
@@ -696,39 +696,62 @@ __global__ __launch_bounds__(kStateThreads) __attribute__((amdgpu_waves_per_eu(2
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index, uniform
 
-  // two stage buffers: the next chunk's record streams in (global -> LDS,
-  // no registers) while the current one is consumed
+  // three stage buffers: chunk c is consumed while c+1 has landed or is landing
+  // and c+2 streams in (global -> LDS, no registers), which gives each copy two
+  // chunks' time to arrive from HBM
   constexpr int kStageBytes = R::kStageRounds * 4096;
   __shared__ __attribute__((aligned(16))) char sStage0[kStageBytes];
   __shared__ __attribute__((aligned(16))) char sStage1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) char sStage2[kStageBytes];
   const int jc0 = a.seq_chunk0[seq], jc1 = a.seq_chunk0[seq + 1];
   const char* recbase = (const char*)a.rec;
 
   if (w == kStateComputeWaves) {
-    // the loader wave: copies chunk c+1's record into LDS while chunk c is
-    // consumed; one barrier per chunk, as the compute waves
-    // (the LDS side of the copy is a compile-time buffer: its address goes to M0)
+    // The loader wave: at the start of chunk c it issues the copy of chunk c+2
+    // and then waits only for chunk c+1's copy (vector-memory loads complete
+    // in issue order) before the barrier that ends chunk c.  The barrier is
+    // written out because a workgroup fence would also wait for the newer
+    // copy; this wave reads nothing, and the memory clobber keeps each copy
+    // below the barrier that frees its buffer.
+    constexpr int kCopies = 4 * R::kStageRounds;  // copy instructions per record
+    static_assert(kCopies < 64, "wait count field");
+    // (the LDS side of a copy is a compile-time buffer: its address goes to M0)
     auto stage = [&](int jc, auto bufc) {
-      char* const dst = decltype(bufc)::value ? sStage1 : sStage0;
+      constexpr int B = decltype(bufc)::value;
+      char* const dst = B == 0 ? sStage0 : (B == 1 ? sStage1 : sStage2);
       const char* rec = recbase + ((int64_t)jc * H + h) * R::kBytes;
 #pragma unroll
-      for (int i = 0; i < 4 * R::kStageRounds; ++i)
+      for (int i = 0; i < kCopies; ++i)
         __builtin_amdgcn_global_load_lds((const void*)(rec + (lane + 64 * i) * 16),
                                          (lds_void*)(&dst[(64 * i) * 16]), 16, 0, 0);
     };
-    if (jc0 < jc1) stage(jc0, std::integral_constant<int, 0>{});
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    for (int jc = jc0; jc < jc1; jc += 2) {
-      if (jc + 1 < jc1) stage(jc + 1, std::integral_constant<int, 1>{});
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (jc + 1 < jc1) {
-        if (jc + 2 < jc1) stage(jc + 2, std::integral_constant<int, 0>{});
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+    auto barrier_one_pending = [&]() { asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kCopies) : "memory"); };
+    auto barrier_none_pending = [&]() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); };
+    // chunk c+2 goes into buffer (c+2) % 3, freed by the barrier ending chunk c-1
+    auto step = [&](int jc, auto nbufc) {
+      if (jc + 2 < jc1) {
+        // let the compute waves' own loads for the next chunk enter the memory
+        // queue ahead of this copy
+        __builtin_amdgcn_s_sleep(2);
+        stage(jc + 2, nbufc);
+        barrier_one_pending();
+      } else {
+        barrier_none_pending();
       }
+    };
+    if (jc0 < jc1) stage(jc0, std::integral_constant<int, 0>{});
+    if (jc0 + 1 < jc1) {
+      stage(jc0 + 1, std::integral_constant<int, 1>{});
+      barrier_one_pending();
+    } else {
+      barrier_none_pending();
     }
+    for (int jc = jc0; jc < jc1; jc += 3) {
+      step(jc, std::integral_constant<int, 2>{});
+      if (jc + 1 < jc1) step(jc + 1, std::integral_constant<int, 0>{});
+      if (jc + 2 < jc1) step(jc + 2, std::integral_constant<int, 1>{});
+    }
+    __builtin_amdgcn_s_waitcnt(0);
     return;
   }
 
@@ -756,15 +779,26 @@ __global__ __launch_bounds__(kStateThreads) __attribute__((amdgpu_waves_per_eu(2
       }
   }
 
-  // U tiles of this wave's column tiles for one chunk (zero for transition columns)
+  // U tiles of this wave's column tiles for one chunk (zero for transition
+  // columns) and the Aqk fragments: read straight to registers, one chunk ahead
   uint2 ucur[NCT][4], unext[NCT][4];
+  bf16x8 fA[4][2], fAn[4][2];
 #pragma unroll
   for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
     for (int t = 0; t < 4; ++t) ucur[ct][t] = unext[ct][t] = make_uint2(0u, 0u);
+  auto load_aqk = [&](const char* rec, bf16x8 (&dst)[4][2]) {
+    const bf16x8* ga = (const bf16x8*)(rec + R::oAqk);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      dst[t][0] = ga[(t * 2 + 0) * 64 + lane];
+      if (t >= 2) dst[t][1] = ga[(t * 2 + 1) * 64 + lane];
+    }
+  };
   int tok_cur = 0, len_cur = 0, tok_nxt = 0, len_nxt = 0;
   if (jc0 < jc1) {
     const char* rec = recbase + ((int64_t)jc0 * H + h) * R::kBytes;
+    if (!SUM) load_aqk(rec, fA);
     const uint2* ug = (const uint2*)(rec + R::oU);
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
@@ -813,13 +847,14 @@ __global__ __launch_bounds__(kStateThreads) __attribute__((amdgpu_waves_per_eu(2
   // loader wave fills the other one.
   auto chunk_step = [&](int jc, auto bufc) {
     constexpr int BUF = decltype(bufc)::value;
-    char* const cur = BUF ? sStage1 : sStage0;
-    // the next chunk's U tiles and table entries (the current chunk's again on
-    // the last chunk: harmless, and it keeps the body free of branches)
+    char* const cur = BUF == 0 ? sStage0 : (BUF == 1 ? sStage1 : sStage2);
+    // the next chunk's U tiles, Aqk fragments and table entries (the current
+    // chunk's again on the last chunk: harmless, and it keeps the body free of
+    // branches)
     const int jn = (jc + 1 < jc1) ? jc + 1 : jc;
-    if (!SUM) store_out();
     {
       const char* rec = recbase + ((int64_t)jn * H + h) * R::kBytes;
+      if (!SUM) load_aqk(rec, fAn);
       const uint2* ug = (const uint2*)(rec + R::oU);
 #pragma unroll
       for (int ct = 0; ct < NCT; ++ct) {
@@ -834,13 +869,13 @@ __global__ __launch_bounds__(kStateThreads) __attribute__((amdgpu_waves_per_eu(2
       tok_nxt = a.chunk_tok[jn];
       len_nxt = a.chunk_len[jn];
     }
+    if (!SUM) store_out();
     const bf16x8* sQt = (const bf16x8*)(cur + R::oQt);
     const bf16x8* sW = (const bf16x8*)(cur + R::oW);
     const bf16x8* sKbar = (const bf16x8*)(cur + R::oKbar);
-    const bf16x8* sAqk = (const bf16x8*)(cur + R::oAqk);
     const float* sGL = (const float*)(cur + R::oGL);
-    // every A-operand fragment of this chunk, read up front
-    bf16x8 fW[4][NKJ], fQ[4][NKJ], fA[4][2], fK[NKT][2];
+    // every staged A-operand fragment of this chunk, read up front
+    bf16x8 fW[4][NKJ], fQ[4][NKJ], fK[NKT][2];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -848,13 +883,6 @@ __global__ __launch_bounds__(kStateThreads) __attribute__((amdgpu_waves_per_eu(2
         fW[t][j] = sW[(t * NKJ + j) * 64 + lane];
         if (!SUM) fQ[t][j] = sQt[(t * NKJ + j) * 64 + lane];
       }
-    if (!SUM) {
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        fA[t][0] = sAqk[(t * 2 + 0) * 64 + lane];
-        if (t >= 2) fA[t][1] = sAqk[(t * 2 + 1) * 64 + lane];
-      }
-    }
 #pragma unroll
     for (int at = 0; at < NKT; ++at) {
       fK[at][0] = sKbar[(at * 2 + 0) * 64 + lane];
@@ -928,19 +956,28 @@ __global__ __launch_bounds__(kStateThreads) __attribute__((amdgpu_waves_per_eu(2
     otok = tok_cur;
     olen = len_cur;
     // the next record has landed (the loader waited for it), and every wave is
-    // done with this buffer
-    __builtin_amdgcn_s_waitcnt(0);
+    // done with this buffer.  The U and Aqk loads for the next chunk are not
+    // waited for here: they share the memory queue with the loader's copies and
+    // are waited for where they are first used.
     __syncthreads();
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct)
 #pragma unroll
       for (int t = 0; t < 4; ++t) ucur[ct][t] = unext[ct][t];
+    if (!SUM) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        fA[t][0] = fAn[t][0];
+        if (t >= 2) fA[t][1] = fAn[t][1];
+      }
+    }
     tok_cur = tok_nxt;
     len_cur = len_nxt;
   };
-  for (int jc = jc0; jc < jc1; jc += 2) {
+  for (int jc = jc0; jc < jc1; jc += 3) {
     chunk_step(jc, std::integral_constant<int, 0>{});
     if (jc + 1 < jc1) chunk_step(jc + 1, std::integral_constant<int, 1>{});
+    if (jc + 2 < jc1) chunk_step(jc + 2, std::integral_constant<int, 2>{});
   }
 
   if (!SUM) store_out();
