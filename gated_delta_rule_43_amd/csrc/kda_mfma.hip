@@ -669,18 +669,18 @@ __global__ __launch_bounds__(kThreads) void k_chunk_mfma_exact(FwdArgs a) {
 // Kernel B: state pass and output.  SUM = summary mode (state columns only,
 // with the transition columns [V, V+K) that start as I and carry no values).
 // ---------------------------------------------------------------------------
-// Four compute waves own the column tiles; a fifth wave only streams the next
-// chunk's record into LDS, so that the compute waves never stall on those loads.
-constexpr int kStateComputeWaves = 4;
-constexpr int kStateThreads = 64 * (kStateComputeWaves + 1);
-
-template <int K, int V, int NCT, bool SUM>
-__global__ __launch_bounds__(kStateThreads) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_state_mfma(FwdArgs a) {
+// CW compute waves (1, 2 or 4) each own one 16-column tile of the state; one
+// more wave only streams the records into LDS, so that the compute waves never
+// stall on those loads.  Fewer compute waves per workgroup spread a problem
+// with few (sequence, head) pairs over more CUs.
+template <int K, int V, int CW, bool SUM>
+__global__ __launch_bounds__(64 * (CW + 1)) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_state_mfma(FwdArgs a) {
   using R = Rec<K, V>;
+  constexpr int NCT = 1;  // column tiles per compute wave
   constexpr int NKJ = K / 32, NKT = K / 16, NVT = V / 16;
   constexpr int ncols = SUM ? V + K : V;
   constexpr int nct_total = ncols / 16;
-  constexpr int tiles_wg = 4 * NCT;
+  constexpr int tiles_wg = CW * NCT;
   static_assert(nct_total % tiles_wg == 0, "every wave owns whole column tiles");
   constexpr int ntile_wg = nct_total / tiles_wg;
   const int H = a.H;
@@ -706,7 +706,7 @@ __global__ __launch_bounds__(kStateThreads) __attribute__((amdgpu_waves_per_eu(2
   const int jc0 = a.seq_chunk0[seq], jc1 = a.seq_chunk0[seq + 1];
   const char* recbase = (const char*)a.rec;
 
-  if (w == kStateComputeWaves) {
+  if (w == CW) {
     // The loader wave: at the start of chunk c it issues the copy of chunk c+2
     // and then waits only for chunk c+1's copy (vector-memory loads complete
     // in issue order) before the barrier that ends chunk c.  The barrier is
@@ -1002,6 +1002,19 @@ __global__ __launch_bounds__(kStateThreads) __attribute__((amdgpu_waves_per_eu(2
   }
 }
 
+// compute units of the current device (cached per device)
+inline int device_cus() {
+  static int cache[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cache[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cache[dev] = n;
+  }
+  return cache[dev];
+}
+
 template <int K, int V>
 hipError_t run(const FwdArgs& a, hipStream_t s) {
   mark(a, kStagePrologue, 0, s);
@@ -1021,14 +1034,24 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
   }
   mark(a, kStageChunk, 1, s);
   mark(a, kStageState, 0, s);
-  // one 16-column tile per compute wave: a workgroup covers 64 state columns
+  // one 16-column tile per compute wave; the widest workgroup (most compute
+  // waves) that still gives every CU a workgroup
   const int ncols = a.summary ? V + K : V;
-  const int ntile_wg = ncols / 16 / kStateComputeWaves;
-  const int64_t wgs = ((int64_t)a.N * a.H + kXcds - 1) / kXcds * kXcds * ntile_wg;
+  const int64_t heads = ((int64_t)a.N * a.H + kXcds - 1) / kXcds * kXcds;
+  const int cus = device_cus();
+  int cw = 4;
+  while (cw > 1 && heads * (ncols / 16 / cw) < cus) cw /= 2;
+  const int64_t wgs = heads * (ncols / 16 / cw);
   if (wgs > 0 && (a.summary || a.fin || a.NT > 0)) {
-    const dim3 grid((unsigned)wgs), block(kStateThreads);
-    if (a.summary) hipLaunchKernelGGL((k_state_mfma<K, V, 1, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_state_mfma<K, V, 1, false>), grid, block, 0, s, a);
+    const dim3 grid((unsigned)wgs), block(64 * (cw + 1));
+    auto launch_cw = [&](auto cwc) {
+      constexpr int CW = decltype(cwc)::value;
+      if (a.summary) hipLaunchKernelGGL((k_state_mfma<K, V, CW, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((k_state_mfma<K, V, CW, false>), grid, block, 0, s, a);
+    };
+    if (cw == 4) launch_cw(std::integral_constant<int, 4>{});
+    else if (cw == 2) launch_cw(std::integral_constant<int, 2>{});
+    else launch_cw(std::integral_constant<int, 1>{});
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   mark(a, kStageState, 1, s);
