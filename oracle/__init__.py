@@ -55,9 +55,9 @@ def _load():
         I = ctypes.c_int
         D = ctypes.c_double
         lib.oracle_prologue.argtypes = [I, I, I, I, P, P, P, P, P, P, I, D, P, P, P, P]
-        lib.oracle_kda_fwd.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, D, I, D, I, P, P, P, P, I]
+        lib.oracle_kda_fwd.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, D, I, D, I, P, P, P, P, I]
         lib.oracle_recurrence.argtypes = [I, I, I, I, I, P, P, P, P, P, D, I, P, P, P, P, I]
-        lib.oracle_state_summary.argtypes = [I, I, I, I, I, P, P, P, P, P, P, P, I, D, P, P, I]
+        lib.oracle_state_summary.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, I, D, P, P, I]
         lib.oracle_apply_state_summary.argtypes = [I, I, I, I, P, P, P, P]
         for f in (lib.oracle_prologue, lib.oracle_kda_fwd, lib.oracle_recurrence,
                   lib.oracle_state_summary, lib.oracle_apply_state_summary):
@@ -121,10 +121,16 @@ def _cu(cu_seqlens, B, T):
 def kda_fwd(q, k, v, gate, beta, a_log, dt_bias, scale=None, lower_bound=None,
             cu_seqlens=None, initial_state=None, output_final_state=True,
             gate_mode=None, threads=None, want_output=True):
-    """Full KDA forward.  Returns (o [B,T,H,V] fp64 or None, final [N,H,K,V] fp64 or None)."""
+    """Full KDA forward.  Returns (o [B,T,H,V] fp64 or None, final [N,H,K,V] fp64 or None).
+
+    H is the number of value heads (v, gate, beta, a_log, dt_bias, o, states);
+    q and k may have fewer key heads HK dividing H, value head h then reading
+    key head h // (H // HK) (grouped value heads)."""
     q, k, v, gate, beta, a_log, dt_bias = map(_f32, (q, k, v, gate, beta, a_log, dt_bias))
-    B, T, H, K = q.shape
-    V = v.shape[-1]
+    B, T, HK, K = q.shape
+    H, V = v.shape[2], v.shape[-1]
+    if H % HK:
+        raise ValueError("value heads %d must be a multiple of key heads %d" % (H, HK))
     if scale is None:
         scale = 1.0 / math.sqrt(K)
     mode, lb = _gate(lower_bound, gate_mode)
@@ -132,7 +138,7 @@ def kda_fwd(q, k, v, gate, beta, a_log, dt_bias, scale=None, lower_bound=None,
     init = None if initial_state is None else _f32(initial_state)
     o = np.zeros((B, T, H, V), np.float64) if want_output else None
     fin = np.zeros((N, H, K, V), np.float64) if output_final_state else None
-    rc = _load().oracle_kda_fwd(B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
+    rc = _load().oracle_kda_fwd(B, T, H, HK, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
                                 _ptr(a_log), _ptr(dt_bias), float(scale), mode, lb, N, _ptr(cu),
                                 _ptr(init), _ptr(o), _ptr(fin), threads or default_threads())
     if rc:
@@ -160,14 +166,17 @@ def recurrence(qn, kn, v, g, b, scale, cu_seqlens=None, initial_state=None, thre
 
 def state_summary(q, k, v, gate, beta, a_log, dt_bias, lower_bound=None, gate_mode=None,
                   threads=None):
-    """Affine summary of each row: (state_ext [B,H,K,V], transition [B,H,K,K]), fp64."""
+    """Affine summary of each row: (state_ext [B,H,K,V], transition [B,H,K,K]), fp64.
+    Heads as in kda_fwd (q, k may carry fewer key heads)."""
     q, k, v, gate, beta, a_log, dt_bias = map(_f32, (q, k, v, gate, beta, a_log, dt_bias))
-    B, T, H, K = q.shape
-    V = v.shape[-1]
+    B, T, HK, K = q.shape
+    H, V = v.shape[2], v.shape[-1]
+    if H % HK:
+        raise ValueError("value heads %d must be a multiple of key heads %d" % (H, HK))
     mode, lb = _gate(lower_bound, gate_mode)
     E = np.zeros((B, H, K, V), np.float64)
     P = np.zeros((B, H, K, K), np.float64)
-    rc = _load().oracle_state_summary(B, T, H, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
+    rc = _load().oracle_state_summary(B, T, H, HK, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(gate),
                                       _ptr(beta), _ptr(a_log), _ptr(dt_bias), mode, lb,
                                       _ptr(E), _ptr(P), threads or default_threads())
     if rc:

@@ -135,6 +135,7 @@ static void recur_step(double* S, int K, int V, const double* qn, const double* 
 /* ------------------------------------------------------------------------ */
 typedef struct {
   int B, T, H, K, V;
+  int HK; /* key heads of q and k (raw entries); value head h reads key head h / (H / HK) */
   const float *q, *k, *v, *gate, *beta, *a_log, *dt_bias;
   /* pre-normalised inputs (recurrence-only entry); NULL when raw is used */
   const double *qn, *kn, *g, *bb;
@@ -202,8 +203,10 @@ static void* worker(void* arg) {
         pg = J->g + th * K;
         bt = J->bb[th];
       } else {
-        l2norm(J->q + th * K, K, qn);
-        l2norm(J->k + th * K, K, kn);
+        /* grouped value heads: G = H / HK value heads share one key head */
+        long thk = ((row * J->T) + t) * J->HK + h / (H / J->HK);
+        l2norm(J->q + thk * K, K, qn);
+        l2norm(J->k + thk * K, K, kn);
         gate_row(J->gate + th * K, J->dt_bias + (long)h * K, (double)J->a_log[h], K, J->gate_mode,
                  J->lb, g);
         bt = sigmoid((double)J->beta[th]);
@@ -258,18 +261,21 @@ static int check_cu(int B, int T, int N, const int32_t* cu) {
 
 /* ------------------------------------------------------------------------ */
 /* Public: full forward from raw inputs.                                     */
-/*   o [B,T,H,V] (may be NULL), final_state [N,H,K,V] (may be NULL).         */
+/*   H value heads, HK key heads (H % HK == 0; HK == H without grouping):   */
+/*   q, k [B,T,HK,K]; v [B,T,H,V]; gate [B,T,H,K]; beta [B,T,H];             */
+/*   a_log [H], dt_bias [H,K]; o [B,T,H,V] (may be NULL), final_state        */
+/*   [N,H,K,V] (may be NULL).                                                */
 /* ------------------------------------------------------------------------ */
-int oracle_kda_fwd(int B, int T, int H, int K, int V, const float* q, const float* k,
+int oracle_kda_fwd(int B, int T, int H, int HK, int K, int V, const float* q, const float* k,
                    const float* v, const float* gate, const float* beta, const float* a_log,
                    const float* dt_bias, double scale, int gate_mode, double lower_bound, int N,
                    const int32_t* cu_seqlens, const float* initial_state, double* o,
                    double* final_state, int threads) {
-  if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return 1;
+  if (B < 0 || T < 0 || H <= 0 || HK <= 0 || H % HK || K <= 0 || V <= 0) return 1;
   if (check_cu(B, T, N, cu_seqlens)) return 2;
   job_t J;
   memset(&J, 0, sizeof(J));
-  J.B = B; J.T = T; J.H = H; J.K = K; J.V = V;
+  J.B = B; J.T = T; J.H = H; J.HK = HK; J.K = K; J.V = V;
   J.q = q; J.k = k; J.v = v; J.gate = gate; J.beta = beta; J.a_log = a_log; J.dt_bias = dt_bias;
   J.gate_mode = gate_mode; J.lb = lower_bound; J.scale = scale;
   J.N = N; J.cu = cu_seqlens; J.init = initial_state; J.o = o; J.fin = final_state;
@@ -301,14 +307,14 @@ int oracle_recurrence(int B, int T, int H, int K, int V, const double* qn, const
 /*                          (I - beta k^ k^T) Diag(exp g), later on the left */
 /* so that final_state = transition . initial_state + state_ext.            */
 /* ------------------------------------------------------------------------ */
-int oracle_state_summary(int B, int T, int H, int K, int V, const float* q, const float* k,
-                         const float* v, const float* gate, const float* beta, const float* a_log,
-                         const float* dt_bias, int gate_mode, double lower_bound,
-                         double* state_ext, double* transition, int threads) {
-  if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return 1;
+int oracle_state_summary(int B, int T, int H, int HK, int K, int V, const float* q,
+                         const float* k, const float* v, const float* gate, const float* beta,
+                         const float* a_log, const float* dt_bias, int gate_mode,
+                         double lower_bound, double* state_ext, double* transition, int threads) {
+  if (B < 0 || T < 0 || H <= 0 || HK <= 0 || H % HK || K <= 0 || V <= 0) return 1;
   job_t J;
   memset(&J, 0, sizeof(J));
-  J.B = B; J.T = T; J.H = H; J.K = K; J.V = V;
+  J.B = B; J.T = T; J.H = H; J.HK = HK; J.K = K; J.V = V;
   J.q = q; J.k = k; J.v = v; J.gate = gate; J.beta = beta; J.a_log = a_log; J.dt_bias = dt_bias;
   J.gate_mode = gate_mode; J.lb = lower_bound; J.scale = 1.0;
   J.N = B; J.fin = state_ext; J.trans = transition; J.summary = 1;

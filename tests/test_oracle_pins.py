@@ -351,3 +351,38 @@ def test_chunked_form_matches_recurrence(C, lb):
                                            initial_state=init)
     np.testing.assert_allclose(o_chk, o_ref, atol=1e-10)
     np.testing.assert_allclose(f_chk, f_ref, atol=1e-10)
+
+
+def test_grouped_value_heads_equal_repeated_key_heads():
+    """Grouped value heads (hyper_parallel page, `_validate_projected_inputs`:
+    v/gate/beta carry HV heads, a multiple of the H heads of q and k).  Under the
+    reading that value head j uses key head j // (HV/H), a grouped run must equal
+    the ungrouped run on q and k repeated along the head axis, bit for bit (the
+    same fp64 operations), for the forward and for the state summary.  A modulo
+    mapping (j % H) or a swapped group order fails this for G, H > 1."""
+    rng = np.random.default_rng(7)
+    B, T, HK, G, K, V = 2, 29, 2, 3, 8, 5
+    H = HK * G
+    f = lambda *s: rng.standard_normal(s).astype(np.float32)
+    q, k = f(B, T, HK, K), f(B, T, HK, K)
+    v, gate, beta = f(B, T, H, V), f(B, T, H, K), f(B, T, H)
+    a_log = rng.uniform(-1, 1, H).astype(np.float32)
+    dt_bias = (0.1 * f(H, K)).astype(np.float32)
+    init = f(B, H, K, V)
+    qr, kr = np.repeat(q, G, axis=2), np.repeat(k, G, axis=2)
+    for lb, mode in ((None, None), (-3.0, "sigmoid"), (-3.0, "clamp")):
+        o1, f1 = oracle.kda_fwd(q, k, v, gate, beta, a_log, dt_bias, lower_bound=lb, gate_mode=mode,
+                                initial_state=init, threads=2)
+        o2, f2 = oracle.kda_fwd(qr, kr, v, gate, beta, a_log, dt_bias, lower_bound=lb, gate_mode=mode,
+                                initial_state=init, threads=2)
+        assert np.array_equal(o1, o2) and np.array_equal(f1, f2)
+        E1, P1 = oracle.state_summary(q, k, v, gate, beta, a_log, dt_bias, lower_bound=lb, gate_mode=mode)
+        E2, P2 = oracle.state_summary(qr, kr, v, gate, beta, a_log, dt_bias, lower_bound=lb, gate_mode=mode)
+        assert np.array_equal(E1, E2) and np.array_equal(P1, P2)
+    # the key heads matter: changing key head 1 changes exactly value heads G..2G-1
+    q2 = q.copy()
+    q2[:, :, 1] += 1.0
+    o3, _ = oracle.kda_fwd(q2, k, v, gate, beta, a_log, dt_bias, threads=2)
+    o1, _ = oracle.kda_fwd(q, k, v, gate, beta, a_log, dt_bias, threads=2)
+    changed = [j for j in range(H) if not np.array_equal(o1[:, :, j], o3[:, :, j])]
+    assert changed == list(range(G, 2 * G))
