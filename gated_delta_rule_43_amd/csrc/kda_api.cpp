@@ -32,6 +32,9 @@ size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 bool head_dim_ok(int d) { return d == 64 || d == 128; }
 
+// value heads (HV, 0 meaning H)
+int value_heads(const kda_problem* p) { return p->HV > 0 ? p->HV : p->H; }
+
 // Shape/flag validation shared by every entry point (no pointers checked here).
 kda_status validate_problem(const kda_problem* p, bool summary) {
   if (!p) return fail(KDA_EINVAL, "problem is NULL");
@@ -45,11 +48,19 @@ kda_status validate_problem(const kda_problem* p, bool summary) {
     return fail(KDA_EUNSUPPORTED, "chunk_size %d is not supported (16, 32 or 64)", p->chunk_size);
   if (!std::isnan(p->lower_bound) && !(p->lower_bound < 0.f && std::isfinite(p->lower_bound)))
     return fail(KDA_EINVAL, "lower_bound must be negative, got %g", (double)p->lower_bound);
+  if (p->lower_bound_form != KDA_LB_SIGMOID && p->lower_bound_form != KDA_LB_CLAMP)
+    return fail(KDA_EINVAL, "lower_bound_form must be KDA_LB_SIGMOID or KDA_LB_CLAMP, got %d",
+                p->lower_bound_form);
+  if (p->lower_bound_form == KDA_LB_CLAMP && std::isnan(p->lower_bound))
+    return fail(KDA_EINVAL, "the clamped gate needs a lower_bound");
+  if (p->HV < 0 || (p->HV > 0 && p->HV % p->H != 0))
+    return fail(KDA_EINVAL, "value heads HV=%d must be a positive multiple of the key heads H=%d (or 0)",
+                p->HV, p->H);
   if (!head_dim_ok(p->K) || !head_dim_ok(p->V))
     return fail(KDA_EUNSUPPORTED, "head dims K=%d V=%d are not supported (64 or 128)", p->K, p->V);
   const long long BT = (long long)p->B * p->T;
-  if (BT >= (1LL << 31) || BT * p->H >= (1LL << 31))
-    return fail(KDA_EUNSUPPORTED, "B*T*H = %lld tokens-heads exceeds 2^31", BT * p->H);
+  if (BT >= (1LL << 31) || BT * value_heads(p) >= (1LL << 31))
+    return fail(KDA_EUNSUPPORTED, "B*T*HV = %lld token-heads exceeds 2^31", BT * value_heads(p));
   if (p->cu_seqlens == nullptr) {
     if (p->cu_seqlens_host != nullptr)
       return fail(KDA_EINVAL, "cu_seqlens_host given without cu_seqlens");
@@ -116,7 +127,7 @@ Layout layout(const kda_problem* p) {
   Layout L;
   L.NT = chunk_count(p, &L.exact);
   L.mfma = use_mfma(p);
-  const size_t NT = (size_t)L.NT, H = p->H, K = p->K, V = p->V, C = p->chunk_size, N = p->N;
+  const size_t NT = (size_t)L.NT, H = value_heads(p), K = p->K, V = p->V, C = p->chunk_size, N = p->N;
   const size_t tokh = (size_t)p->B * p->T * H;
   size_t o = 0;
   auto take = [&](size_t bytes) {
@@ -153,13 +164,14 @@ Layout layout(const kda_problem* p) {
 
 kda::FwdArgs make_args(const kda_problem* p, const Layout& L, void* ws) {
   kda::FwdArgs a{};
-  a.B = p->B; a.T = p->T; a.H = p->H; a.K = p->K; a.V = p->V; a.C = p->chunk_size; a.N = p->N;
+  a.B = p->B; a.T = p->T; a.H = value_heads(p); a.HK = p->H; a.K = p->K; a.V = p->V;
+  a.C = p->chunk_size; a.N = p->N;
   a.NT = L.NT;
   a.exact_nt = L.exact;
   a.dtype = p->dtype;
   a.scale = (p->scale > 0.f) ? p->scale : 1.0f / std::sqrt((float)p->K);
-  a.has_lb = std::isnan(p->lower_bound) ? 0 : 1;
-  a.lb = a.has_lb ? p->lower_bound : 0.f;
+  a.gate_form = std::isnan(p->lower_bound) ? 0 : (p->lower_bound_form == KDA_LB_CLAMP ? 2 : 1);
+  a.lb = a.gate_form ? p->lower_bound : 0.f;
   a.cu = p->cu_seqlens;
   char* w = (char*)ws;
   a.chunk_tok = (int32_t*)(w + L.off_tok);

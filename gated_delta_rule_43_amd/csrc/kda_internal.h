@@ -36,13 +36,15 @@ __device__ inline void store_as(bf16* p, float x) { *p = f32_to_bf16(x); }
 // Everything one forward / summary call needs, resolved on the host.
 // ---------------------------------------------------------------------------
 struct FwdArgs {
-  // shapes
+  // shapes: H value heads (every per-head tensor but q, k), HK key heads of
+  // q and k; value head h reads key head h / (H / HK)
   int B, T, H, K, V, C, N;
+  int HK;
   int NT;          // chunk count: exact, or an upper bound when exact_nt == 0
   int exact_nt;
   int dtype;       // 0 fp32, 1 bf16
   float scale;
-  int has_lb;
+  int gate_form;   // 0: -A softplus(x); 1: lb sigmoid(A x); 2: max(lb, -A softplus(x))
   float lb;
   // inputs
   const int32_t* cu;  // device cu_seqlens or nullptr

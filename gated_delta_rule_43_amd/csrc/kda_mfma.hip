@@ -117,9 +117,11 @@ __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x
 __device__ __forceinline__ float flog(float x) { return __builtin_amdgcn_logf(x) * 0.6931471805599453f; }
 __device__ __forceinline__ float fsigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + fexp(-x)); }
 __device__ __forceinline__ float fsoftplus(float x) { return fmaxf(x, 0.f) + flog(1.f + fexp(-fabsf(x))); }
-// In-kernel gate (see kda_valu.hip for the floor at -110).
-__device__ __forceinline__ float fgate(float x, float A, int has_lb, float lb) {
-  return fmaxf(has_lb ? lb * fsigmoid(A * x) : -A * fsoftplus(x), kGateFloor);
+// In-kernel gate, GATE as in FwdArgs::gate_form (see kda_valu.hip for the floor at -110).
+template <int GATE>
+__device__ __forceinline__ float fgate(float x, float A, float lb) {
+  const float g = GATE == 1 ? lb * fsigmoid(A * x) : -A * fsoftplus(x);
+  return fmaxf(GATE == 2 ? fmaxf(g, lb) : g, kGateFloor);
 }
 // Row shift right by N inside each 16-lane row (DPP row_shr), zero fill.
 template <int N>
@@ -186,8 +188,8 @@ enum {
 // One chunk-head.  EXACT = false: the common kernel; a 16-row block whose
 // decay exceeds the factorised range makes the workgroup append the chunk-head
 // to a fix-up list instead.  EXACT = true: the fix-up, with the exact per-pair
-// path on such blocks.  LB: the gate has a lower bound (sigmoid form).
-template <int K, int V, bool EXACT, bool LB>
+// path on such blocks.  GATE: the gate form (FwdArgs::gate_form).
+template <int K, int V, bool EXACT, int GATE>
 __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, const int h,
                                            const int tok0, const int L) {
   using R = Rec<K, V>;
@@ -198,6 +200,8 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
   const int row = 16 * w + n;
   const bool valid = row < L;
   const int64_t th = (int64_t)(tok0 + (valid ? row : 0)) * H + h;  // token-head index
+  // the same token at the key head this value head reads (grouped value heads)
+  const int64_t thk = (int64_t)(tok0 + (valid ? row : 0)) * a.HK + h / (H / a.HK);
   char* rec = (char*)a.rec + ((int64_t)jchunk * H + h) * R::kBytes;
   // beta and a_log are issued with the row loads so that their latency is not
   // paid again after them
@@ -226,8 +230,8 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
   // q and k, applies the gate and scans it over the 16 rows of the block.
   // Used once up front and again by the exact diagonal path.
   auto row_prologue = [&](float* qv, float* kv, float* lam) {
-    const bf16* q = (const bf16*)a.q + th * K;
-    const bf16* k = (const bf16*)a.k + th * K;
+    const bf16* q = (const bf16*)a.q + thk * K;
+    const bf16* k = (const bf16*)a.k + thk * K;
     const bf16* gt = (const bf16*)a.gate + th * K;
     const float* db = a.dt_bias + (int64_t)h * K;
     // rows past the chunk end read the chunk's first row (th is clamped) and
@@ -265,7 +269,7 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
       kv[s2] *= rk;
     }
 #pragma unroll
-    for (int s2 = 0; s2 < KL; ++s2) lam[s2] = row_scan16(vmask * fgate(lam[s2], A, LB, a.lb));
+    for (int s2 = 0; s2 < KL; ++s2) lam[s2] = row_scan16(vmask * fgate<GATE>(lam[s2], A, a.lb));
   };
   float qv[KL], kv[KL], lam[KL];
   row_prologue(qv, kv, lam);
@@ -640,7 +644,7 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
   }
 }
 
-template <int K, int V, bool LB>
+template <int K, int V, int GATE>
 __global__ __launch_bounds__(kThreads, 3) void k_chunk_mfma(FwdArgs a) {
   const unsigned wid = blockIdx.x, H = (unsigned)a.H;
   const int jchunk = (int)(wid / H), h = (int)(wid % H);
@@ -650,17 +654,17 @@ __global__ __launch_bounds__(kThreads, 3) void k_chunk_mfma(FwdArgs a) {
   const int tok0 = a.chunk_tok[jchunk], L = a.chunk_len[jchunk];
   asm volatile("" ::"s"(tok0), "s"(L));
   if (jchunk >= nt) return;
-  chunk_body<K, V, false, LB>(a, jchunk, h, tok0, L);
+  chunk_body<K, V, false, GATE>(a, jchunk, h, tok0, L);
 }
 
 // Fix-up pass: recomputes the listed chunk-heads with the exact diagonal path.
-template <int K, int V, bool LB>
+template <int K, int V, int GATE>
 __global__ __launch_bounds__(kThreads) void k_chunk_mfma_exact(FwdArgs a) {
   const int count = *a.exact_count;
   for (int i = blockIdx.x; i < count; i += gridDim.x) {
     const int ch = a.exact_list[i];
     const int jchunk = ch / a.H;
-    chunk_body<K, V, true, LB>(a, jchunk, ch % a.H, a.chunk_tok[jchunk], a.chunk_len[jchunk]);
+    chunk_body<K, V, true, GATE>(a, jchunk, ch % a.H, a.chunk_tok[jchunk], a.chunk_len[jchunk]);
     __syncthreads();
   }
 }
@@ -1022,14 +1026,17 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
   mark(a, kStageChunk, 0, s);
   if (a.NT > 0) {
     const dim3 grid((unsigned)((int64_t)a.NT * a.H)), block(kThreads);
-    if (a.has_lb) hipLaunchKernelGGL((k_chunk_mfma<K, V, true>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_chunk_mfma<K, V, false>), grid, block, 0, s, a);
-    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    // chunk-heads whose in-block decay left the factorised range (rare; the
-    // grid is fixed and exits at once when the list is empty)
+    // chunk-heads whose in-block decay left the factorised range go to a fix-up
+    // pass (rare; its grid is fixed and exits at once when the list is empty)
     const dim3 fix_grid((unsigned)std::min<int64_t>((int64_t)a.NT * a.H, 256));
-    if (a.has_lb) hipLaunchKernelGGL((k_chunk_mfma_exact<K, V, true>), fix_grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_chunk_mfma_exact<K, V, false>), fix_grid, block, 0, s, a);
+    auto launch_gate = [&](auto gc) {
+      constexpr int GATE = decltype(gc)::value;
+      hipLaunchKernelGGL((k_chunk_mfma<K, V, GATE>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((k_chunk_mfma_exact<K, V, GATE>), fix_grid, block, 0, s, a);
+    };
+    if (a.gate_form == 1) launch_gate(std::integral_constant<int, 1>{});
+    else if (a.gate_form == 2) launch_gate(std::integral_constant<int, 2>{});
+    else launch_gate(std::integral_constant<int, 0>{});
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   mark(a, kStageChunk, 1, s);

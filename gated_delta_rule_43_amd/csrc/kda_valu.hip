@@ -41,30 +41,34 @@ __device__ inline float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf
 __device__ inline float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
 
 // In-kernel gate: g = -exp(a_log) softplus(x + dt_bias), or with a lower bound
-// lb < 0: g = lb * sigmoid(exp(a_log) (x + dt_bias)).  g is floored at -110:
+// lb < 0: g = lb * sigmoid(exp(a_log) (x + dt_bias)) (gate 1) or the clamp
+// g = max(lb, -exp(a_log) softplus(x + dt_bias)) (gate 2).  g is floored at -110:
 // exp(-110) is already below the smallest fp32 denormal, so no decay factor
 // representable in fp32 changes, and the chunk-local cumulative sums stay
 // small enough for their differences to keep full precision.
 constexpr float kGateFloor = -110.f;
-__device__ inline float gate_value(float x, float A, int has_lb, float lb) {
-  return fmaxf(has_lb ? lb * sigmoid_f(A * x) : -A * softplus_f(x), kGateFloor);
+__device__ inline float gate_value(float x, float A, int gate, float lb) {
+  const float g = gate == 1 ? lb * sigmoid_f(A * x) : -A * softplus_f(x);
+  return fmaxf(gate == 2 ? fmaxf(g, lb) : g, kGateFloor);
 }
 
 template <typename Tin>
 __global__ __launch_bounds__(kThreads) void k_prologue_valu(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ gate,
     const Tin* __restrict__ beta, const float* __restrict__ a_log,
-    const float* __restrict__ dt_bias, int64_t n_th, int H, int K, int has_lb, float lb,
+    const float* __restrict__ dt_bias, int64_t n_th, int H, int HK, int K, int gate_form, float lb,
     float* __restrict__ qn, float* __restrict__ kn, float* __restrict__ g,
     float* __restrict__ bt) {
   const int lane = threadIdx.x & 63;
   const int64_t th = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
   if (th >= n_th) return;
   const int h = (int)(th % H);
-  const int64_t base = th * K;
+  const int64_t base = th * K;  // value-head token-head (outputs, gate)
+  // q and k of the key head this value head reads
+  const int64_t kbase = ((th / H) * HK + h / (H / HK)) * K;
   float ssq = 0.f, ssk = 0.f;
   for (int c = lane; c < K; c += 64) {
-    float xq = load_f32(q + base + c), xk = load_f32(k + base + c);
+    float xq = load_f32(q + kbase + c), xk = load_f32(k + kbase + c);
     ssq = fmaf(xq, xq, ssq);
     ssk = fmaf(xk, xk, ssk);
   }
@@ -73,10 +77,10 @@ __global__ __launch_bounds__(kThreads) void k_prologue_valu(
   const float rq = 1.f / sqrtf(ssq + 1e-6f), rk = 1.f / sqrtf(ssk + 1e-6f);
   const float A = expf(a_log[h]);
   for (int c = lane; c < K; c += 64) {
-    qn[base + c] = load_f32(q + base + c) * rq;
-    kn[base + c] = load_f32(k + base + c) * rk;
+    qn[base + c] = load_f32(q + kbase + c) * rq;
+    kn[base + c] = load_f32(k + kbase + c) * rk;
     float x = load_f32(gate + base + c) + dt_bias[(int64_t)h * K + c];
-    g[base + c] = gate_value(x, A, has_lb, lb);
+    g[base + c] = gate_value(x, A, gate_form, lb);
   }
   if (lane == 0) bt[th] = sigmoid_f(load_f32(beta + th));
 }
@@ -274,7 +278,7 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
     const int64_t blocks = (n_th + 3) / 4;
     hipLaunchKernelGGL(k_prologue_valu<Tin>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.gate, (const Tin*)a.beta,
-                       a.a_log, a.dt_bias, n_th, a.H, a.K, a.has_lb, a.lb, a.qn, a.kn, a.g, a.bt);
+                       a.a_log, a.dt_bias, n_th, a.H, a.HK, a.K, a.gate_form, a.lb, a.qn, a.kn, a.g, a.bt);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   mark(a, kStagePrologue, 1, s);

@@ -40,7 +40,11 @@ class KdaProblem(ctypes.Structure):
                 ("K", ctypes.c_int32), ("V", ctypes.c_int32), ("dtype", ctypes.c_int32),
                 ("scale", ctypes.c_float), ("lower_bound", ctypes.c_float),
                 ("chunk_size", ctypes.c_int32), ("N", ctypes.c_int32),
-                ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p)]
+                ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
+                ("lower_bound_form", ctypes.c_int32), ("HV", ctypes.c_int32)]
+
+# form of the lower-bounded gate (kda_lower_bound_form)
+LOWER_BOUND_FORMS = {"sigmoid": 0, "clamp": 1}
 
 
 _lib = None
@@ -100,7 +104,11 @@ def _nan() -> float:
 
 
 def make_problem(B, T, H, K, V, dtype, scale=None, lower_bound=None, chunk_size=64, N=None,
-                 cu_seqlens_ptr=None, cu_seqlens_host_ptr=None) -> KdaProblem:
+                 cu_seqlens_ptr=None, cu_seqlens_host_ptr=None, lower_bound_form="sigmoid",
+                 HV=0) -> KdaProblem:
+    if lower_bound_form not in LOWER_BOUND_FORMS:
+        raise ValueError("lower_bound_form must be one of %s, got %r"
+                         % (sorted(LOWER_BOUND_FORMS), lower_bound_form))
     p = KdaProblem()
     p.B, p.T, p.H, p.K, p.V = B, T, H, K, V
     p.dtype = dtype
@@ -110,6 +118,8 @@ def make_problem(B, T, H, K, V, dtype, scale=None, lower_bound=None, chunk_size=
     p.N = B if N is None else N
     p.cu_seqlens = cu_seqlens_ptr
     p.cu_seqlens_host = cu_seqlens_host_ptr
+    p.lower_bound_form = LOWER_BOUND_FORMS[lower_bound_form]
+    p.HV = HV
     return p
 
 
@@ -166,8 +176,6 @@ def _check_inputs(q, k, v, gate, beta, a_log, dt_bias):
         raise ValueError("beta must have shape [B, S_local, num_v_heads].")
     if HV % H != 0:
         raise ValueError("num_v_heads must be divisible by num_k_heads.")
-    if HV != H:
-        raise NotImplementedError("num_v_heads != num_k_heads (grouped value heads) is not supported")
     if a_log.numel() != HV:
         raise ValueError("a_log must contain %d elements, got %d." % (HV, a_log.numel()))
     if dt_bias.numel() != HV * K:
@@ -178,7 +186,7 @@ def _check_inputs(q, k, v, gate, beta, a_log, dt_bias):
     _dtype_code(q)
     _dev(a_log, "a_log", dtype=torch.float32)
     _dev(dt_bias, "dt_bias", dtype=torch.float32)
-    return B, T, H, K, V
+    return B, T, H, K, V, HV
 
 
 def _cu_args(cu_seqlens, cu_seqlens_host, T):
@@ -202,14 +210,14 @@ def _cu_args(cu_seqlens, cu_seqlens_host, T):
 
 
 def fwd_workspace_size(q_shape, V, dtype=torch.bfloat16, chunk_size=64, lower_bound=None,
-                       N=None, cu_seqlens_host=None) -> int:
+                       N=None, cu_seqlens_host=None, HV=0) -> int:
     B, T, H, K = q_shape
     host = None if cu_seqlens_host is None else torch.as_tensor(cu_seqlens_host, dtype=torch.int32).contiguous()
     p = make_problem(B, T, H, K, V, KDA_F32 if dtype == torch.float32 else KDA_BF16,
                      lower_bound=lower_bound, chunk_size=chunk_size,
                      N=(host.numel() - 1) if host is not None else N,
                      cu_seqlens_ptr=1 if host is not None else None,
-                     cu_seqlens_host_ptr=host.data_ptr() if host is not None else None)
+                     cu_seqlens_host_ptr=host.data_ptr() if host is not None else None, HV=HV)
     st = ctypes.c_int(0)
     n = load_library().kda_fwd_workspace_size(ctypes.byref(p), ctypes.byref(st))
     if st.value:
@@ -219,36 +227,40 @@ def fwd_workspace_size(q_shape, V, dtype=torch.bfloat16, chunk_size=64, lower_bo
 
 def kda_fwd(q, k, v, gate, beta, a_log, dt_bias, *, scale=None, lower_bound=None,
             chunk_size=64, cu_seqlens=None, cu_seqlens_host=None, initial_state=None,
-            output_final_state=False, out=None, workspace=None, stage_events=None):
+            output_final_state=False, out=None, workspace=None, stage_events=None,
+            lower_bound_form="sigmoid"):
     """Chunked KDA forward; returns (o, final_state or None).
 
-    q, k, gate [B,T,H,K]; v [B,T,H,V]; beta [B,T,H] (float32 or bfloat16, one
-    dtype); a_log [H] and dt_bias [H,K] float32; cu_seqlens int32 [N+1] on the
-    GPU with B == 1; initial_state float32 [N,H,K,V].  ``cu_seqlens_host`` may
+    q, k [B,T,H,K]; gate [B,T,HV,K]; v [B,T,HV,V]; beta [B,T,HV] (float32 or
+    bfloat16, one dtype; HV a multiple of H, value head j reading key head
+    j // (HV/H)); a_log [HV] and dt_bias [HV,K] float32; cu_seqlens int32 [N+1]
+    on the GPU with B == 1; initial_state float32 [N,HV,K,V].
+    ``lower_bound_form`` ("sigmoid" or "clamp") picks the form of the
+    lower-bounded gate when lower_bound is given.  ``cu_seqlens_host`` may
     carry a CPU copy of the offsets (otherwise one is made, which waits for the
     GPU); pass ``False`` to skip the host-side check.  ``stage_events`` is an
     optional ctypes array of 2*NUM_STAGES hipEvent_t handles recorded around
     each stage (see kda_fwd_profiled in include/kda.h).
     """
-    B, T, H, K, V = _check_inputs(q, k, v, gate, beta, a_log, dt_bias)
+    B, T, H, K, V, HV = _check_inputs(q, k, v, gate, beta, a_log, dt_bias)
     lib = load_library()
     device = q.device
     cu, host, N, host_ptr = _cu_args(cu_seqlens, cu_seqlens_host, T)
     if N is None:
         N = B
     if initial_state is not None:
-        _dev(initial_state, "initial_state", dtype=torch.float32, shape=(N, H, K, V))
+        _dev(initial_state, "initial_state", dtype=torch.float32, shape=(N, HV, K, V))
     if scale is not None and not scale > 0:
         raise ValueError("scale must be positive, got %r" % (scale,))
     p = make_problem(B, T, H, K, V, _dtype_code(q), scale, lower_bound, chunk_size, N,
-                     None if cu is None else cu.data_ptr(), host_ptr)
+                     None if cu is None else cu.data_ptr(), host_ptr, lower_bound_form, HV)
     st = ctypes.c_int(0)
     need = lib.kda_fwd_workspace_size(ctypes.byref(p), ctypes.byref(st))
     if st.value:
         _raise(st.value, "kda_fwd")
-    o = out if out is not None else torch.empty((B, T, H, V), dtype=q.dtype, device=device)
-    _dev(o, "out", dtype=q.dtype, shape=(B, T, H, V))
-    fin = torch.empty((N, H, K, V), dtype=torch.float32, device=device) if output_final_state else None
+    o = out if out is not None else torch.empty((B, T, HV, V), dtype=q.dtype, device=device)
+    _dev(o, "out", dtype=q.dtype, shape=(B, T, HV, V))
+    fin = torch.empty((N, HV, K, V), dtype=torch.float32, device=device) if output_final_state else None
     if workspace is None:
         ws, nbytes = _workspace(need, device)
     else:
@@ -264,18 +276,19 @@ def kda_fwd(q, k, v, gate, beta, a_log, dt_bias, *, scale=None, lower_bound=None
 
 
 def kda_state_summary(q, k, v, gate, beta, a_log, dt_bias, *, lower_bound=None, chunk_size=64,
-                      workspace=None):
-    """Affine summary of each row: (state_ext [B,H,K,V], transition [B,H,K,K]), float32."""
-    B, T, H, K, V = _check_inputs(q, k, v, gate, beta, a_log, dt_bias)
+                      workspace=None, lower_bound_form="sigmoid"):
+    """Affine summary of each row: (state_ext [B,HV,K,V], transition [B,HV,K,K]), float32."""
+    B, T, H, K, V, HV = _check_inputs(q, k, v, gate, beta, a_log, dt_bias)
     lib = load_library()
     device = q.device
-    p = make_problem(B, T, H, K, V, _dtype_code(q), None, lower_bound, chunk_size, B)
+    p = make_problem(B, T, H, K, V, _dtype_code(q), None, lower_bound, chunk_size, B,
+                     lower_bound_form=lower_bound_form, HV=HV)
     st = ctypes.c_int(0)
     need = lib.kda_state_summary_workspace_size(ctypes.byref(p), ctypes.byref(st))
     if st.value:
         _raise(st.value, "kda_state_summary")
-    E = torch.empty((B, H, K, V), dtype=torch.float32, device=device)
-    P = torch.empty((B, H, K, K), dtype=torch.float32, device=device)
+    E = torch.empty((B, HV, K, V), dtype=torch.float32, device=device)
+    P = torch.empty((B, HV, K, K), dtype=torch.float32, device=device)
     if workspace is None:
         ws, nbytes = _workspace(need, device)
     else:

@@ -141,8 +141,11 @@ def make_inputs(w: Workload, device="cpu", T: Optional[int] = None, H: Optional[
 
 
 def random_problem(seed, B, T, H, K, V, dtype=torch.float32, device="cpu", gate_std=1.0,
-                   beta_std=1.0, init_std=None, lengths=None, a_log_range=1.0):
-    """Free-form draw with the same recipe, for edge-case tests."""
+                   beta_std=1.0, init_std=None, lengths=None, a_log_range=1.0, HV=None):
+    """Free-form draw with the same recipe, for edge-case tests.  HV (a multiple
+    of H) gives v, gate, beta, a_log, dt_bias and the states HV value heads while
+    q and k keep H key heads; None means HV = H."""
+    HV = H if HV is None else HV
     dev = torch.device(device)
     gen = torch.Generator(device=dev)
     gen.manual_seed(seed)
@@ -152,17 +155,17 @@ def random_problem(seed, B, T, H, K, V, dtype=torch.float32, device="cpu", gate_
 
     q = randn(B, T, H, K)
     k = randn(B, T, H, K)
-    v = randn(B, T, H, V)
-    gate = randn(B, T, H, K, std=gate_std)
-    beta = randn(B, T, H, std=beta_std)
-    a_log = (torch.rand(H, generator=gen, device=dev) * 2.0 - 1.0) * a_log_range
-    dt_bias = randn(H, K, std=0.1)
+    v = randn(B, T, HV, V)
+    gate = randn(B, T, HV, K, std=gate_std)
+    beta = randn(B, T, HV, std=beta_std)
+    a_log = (torch.rand(HV, generator=gen, device=dev) * 2.0 - 1.0) * a_log_range
+    dt_bias = randn(HV, K, std=0.1)
     cu = None
     N = B
     if lengths is not None:
         cu = torch.from_numpy(cu_from_lengths(lengths)).to(dev)
         N = len(lengths)
-    init = randn(N, H, K, V, std=init_std) if init_std is not None else None
+    init = randn(N, HV, K, V, std=init_std) if init_std is not None else None
     return dict(q=q.to(dtype), k=k.to(dtype), v=v.to(dtype), gate=gate.to(dtype),
                 beta=beta.to(dtype), a_log=a_log, dt_bias=dt_bias, initial_state=init,
                 cu_seqlens=cu)

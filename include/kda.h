@@ -3,13 +3,15 @@
  * MI355X (gfx950).  Library: libkda.so.
  *
  * KDA is a gated delta-rule linear attention with a per-key-channel decay.
- * Per sequence n and head h the recurrent state S is a K x V fp32 matrix
+ * Per sequence n and value head h the recurrent state S is a K x V fp32 matrix
  * (row = key channel, column = value channel) and, token by token,
  *
  *     q^ = q / sqrt(sum q^2 + 1e-6),     k^ likewise            (in-kernel L2 norm)
  *     x_c = gate_c + dt_bias[h,c],       A = exp(a_log[h])
  *     g_c = -A * softplus(x_c)                 when lower_bound is unset
  *     g_c = lower_bound * sigmoid(A * x_c)     when lower_bound < 0 (safe gate)
+ *     g_c = max(lower_bound, -A * softplus(x_c))   the same, with lower_bound_form
+ *                                                  = KDA_LB_CLAMP
  *     beta = sigmoid(beta_logit)                                  (in-kernel sigmoid)
  *     S_t = (I - beta k^ k^T) Diag(exp g) S_{t-1} + beta k^ v^T
  *     o_t = scale * S_t^T q^
@@ -21,15 +23,19 @@
  * boundaries as cu_seqlens like the NeMo AutoModel page
  * "nemo_automodel.components.models.kimi_k3.cp" (module introduction,
  * `doc_ids_from_cu_seqlens`).  The gate formula is not printed on the pages;
- * the two forms above are this library's reading of the in-kernel gate and of
- * the lower-bounded gate parameterisation.
+ * the forms above are this library's reading of the in-kernel gate and of the
+ * lower-bounded gate parameterisation (sigmoid by default; the hard clamp is
+ * the alternative reading, selected per call).
  *
  * Conventions for every entry point
- *  - All tensors are dense, contiguous, token-major ("token-first"):
- *      q, k, gate : [B, T, H, K]     v, o : [B, T, H, V]     beta : [B, T, H]
- *      a_log      : [H]    fp32      dt_bias : [H, K] fp32
- *      states     : [N, H, K, V] fp32      transitions : [B, H, K, K] fp32
- *    q, k, v, gate, beta and o share one dtype (kda_dtype).
+ *  - All tensors are dense, contiguous, token-major ("token-first"), with H key
+ *    heads and HV value heads (HV a multiple of H; HV = H without grouping):
+ *      q, k   : [B, T, H, K]       gate : [B, T, HV, K]     beta : [B, T, HV]
+ *      v, o   : [B, T, HV, V]      a_log : [HV] fp32        dt_bias : [HV, K] fp32
+ *      states : [N, HV, K, V] fp32      transitions : [B, HV, K, K] fp32
+ *    Value head h reads key head h / (HV / H) (grouped value heads, the shape
+ *    contract of `_validate_projected_inputs`).  q, k, v, gate, beta and o
+ *    share one dtype (kda_dtype).
  *  - Every tensor pointer is a device pointer unless its name ends in _host.
  *  - The caller owns and allocates all memory, including the workspace.  The
  *    library allocates nothing, keeps no state between calls, never frees and
@@ -38,7 +44,6 @@
  *    the call returns.
  *  - Arguments are validated on the host before anything is enqueued; on any
  *    non-OK status nothing was launched and kda_last_error() describes why.
- *  - One head layout: the number of value heads equals the number of key heads.
  *  - Not thread-safe across concurrent calls that share a workspace.
  */
 #ifndef KDA_H_
@@ -52,6 +57,9 @@ extern "C" {
 #endif
 
 typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+
+/* Form of the lower-bounded gate (used only when lower_bound is set). */
+typedef enum { KDA_LB_SIGMOID = 0, KDA_LB_CLAMP = 1 } kda_lower_bound_form;
 
 typedef enum {
   KDA_OK = 0,
@@ -88,6 +96,13 @@ typedef enum {
  *                 into range on the device so that no access leaves the
  *                 buffers, and the results are then unspecified.
  *  N              number of sequences: B without cu_seqlens, else len-1.
+ *  lower_bound_form  KDA_LB_SIGMOID (0, default) or KDA_LB_CLAMP (1); with
+ *                 KDA_LB_CLAMP lower_bound must be set.  Other values and a
+ *                 clamp without a bound are KDA_EINVAL.
+ *  HV             value heads; 0 means HV = H.  Otherwise a positive multiple
+ *                 of H (KDA_EINVAL if not).
+ * Fields are appended at the end only: a zero-initialised problem with the
+ * first ten fields set describes the ungrouped, sigmoid-form problem.
  */
 typedef struct kda_problem {
   int32_t B, T, H, K, V;
@@ -98,6 +113,8 @@ typedef struct kda_problem {
   int32_t N;
   const int32_t* cu_seqlens;
   const int32_t* cu_seqlens_host;
+  int32_t lower_bound_form;
+  int32_t HV;
 } kda_problem;
 
 /* Host-only validation of a problem; launches nothing, touches no device. */
@@ -115,10 +132,10 @@ size_t kda_fwd_workspace_size(const kda_problem* p, kda_status* status);
  * use_beta_sigmoid_in_kernel all on).
  *
  *  q, k, v, gate, beta   inputs, dtype p->dtype, layouts above.
- *  a_log [H], dt_bias [H,K]   fp32 gate parameters.
- *  initial_state         [N,H,K,V] fp32, or NULL for zeros.
- *  o                     [B,T,H,V] output, dtype p->dtype (required).
- *  final_state           [N,H,K,V] fp32 output, or NULL to not produce it
+ *  a_log [HV], dt_bias [HV,K]   fp32 gate parameters.
+ *  initial_state         [N,HV,K,V] fp32, or NULL for zeros.
+ *  o                     [B,T,HV,V] output, dtype p->dtype (required).
+ *  final_state           [N,HV,K,V] fp32 output, or NULL to not produce it
  *                        (output_final_state=False).  With cu_seqlens, entry n
  *                        is document n's state after its last token; an empty
  *                        document returns its initial state.
@@ -156,8 +173,8 @@ size_t kda_state_summary_workspace_size(const kda_problem* p, kda_status* status
  * Affine summary of each row as a contiguous slice (torch_kda_state_summary in
  * `_eager_kda_state_p2p` on the hyper_parallel page): the row's effect on the
  * state is  final = transition . initial + state_ext,  with
- *  state_ext  [B,H,K,V] fp32 = the row's final state from a zero initial state,
- *  transition [B,H,K,K] fp32 = the ordered product over the row's tokens of
+ *  state_ext  [B,HV,K,V] fp32 = the row's final state from a zero initial state,
+ *  transition [B,HV,K,K] fp32 = the ordered product over the row's tokens of
  *             (I - beta k^ k^T) Diag(exp g), later tokens on the left.
  * p->cu_seqlens must be NULL (a slice summary has no document resets; the
  * pages' state-CP adapters reject cu_seqlens as well).  No output o is made.
@@ -169,7 +186,7 @@ kda_status kda_state_summary(const kda_problem* p, const void* q, const void* k,
 
 /*
  * final_state = transition . initial_state + state_ext for each of the B*H
- * (row, head) pairs (torch_apply_kda_state_summary on the hyper_parallel
+ * (row, head) pairs (H = the value heads of the summary) (torch_apply_kda_state_summary on the hyper_parallel
  * page); initial_state may be NULL (rank 0 of a state-parallel chain), then
  * final_state = state_ext.  All fp32, shapes [B,H,K,V] and [B,H,K,K].
  * final_state may alias state_ext (in-place update); it may not alias

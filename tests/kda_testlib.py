@@ -23,7 +23,8 @@ def to_np(t):
 def gpu_fwd(inp, output_final_state=True, **kw):
     args = dict(scale=inp.get("scale"), lower_bound=inp.get("lower_bound"),
                 chunk_size=inp.get("chunk_size", 64), cu_seqlens=inp.get("cu_seqlens"),
-                initial_state=inp.get("initial_state"), output_final_state=output_final_state)
+                initial_state=inp.get("initial_state"), output_final_state=output_final_state,
+                lower_bound_form=inp.get("lower_bound_form", "sigmoid"))
     args.update(kw)
     o, fin = kda.kda_fwd(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"], inp["a_log"],
                          inp["dt_bias"], **args)
@@ -32,7 +33,8 @@ def gpu_fwd(inp, output_final_state=True, **kw):
 
 
 def oracle_fwd(inp, heads=None, rows=None, threads=None):
-    """Oracle on (a head/row subset of) the same inputs; returns fp64 numpy arrays."""
+    """Oracle on (a head/row subset of) the same inputs; returns fp64 numpy arrays.
+    A head subset needs q and k with as many heads as v (no grouping)."""
     sel_h = slice(None) if heads is None else list(heads)
     sel_b = slice(None) if rows is None else list(rows)
 
@@ -54,6 +56,7 @@ def oracle_fwd(inp, heads=None, rows=None, threads=None):
     return oracle.kda_fwd(cut("q", "bthx"), cut("k", "bthx"), cut("v", "bthx"), cut("gate", "bthx"),
                           cut("beta", "bth"), cut("a_log", "h"), cut("dt_bias", "h"),
                           scale=inp.get("scale"), lower_bound=inp.get("lower_bound"),
+                          gate_mode="clamp" if inp.get("lower_bound_form") == "clamp" else None,
                           cu_seqlens=None if cu is None else cu.cpu().numpy(),
                           initial_state=cut("initial_state", "nh"), threads=threads)
 

@@ -62,6 +62,9 @@ def _status(lib, p):
     (dict(H=0), kda.EINVAL, "bad shape"),
     (dict(dtype=7), kda.EINVAL, "dtype"),
     (dict(N=3), kda.EINVAL, "N must equal B"),
+    (dict(lower_bound_form="clamp"), kda.EINVAL, "clamped gate needs a lower_bound"),
+    (dict(H=2, HV=3), kda.EINVAL, "positive multiple of the key heads"),
+    (dict(H=2, HV=-2), kda.EINVAL, "positive multiple of the key heads"),
 ])
 def test_validation_rejects(lib, kw, status, msg):
     st, err = _status(lib, _p(**kw))
@@ -70,9 +73,26 @@ def test_validation_rejects(lib, kw, status, msg):
 
 def test_validation_accepts(lib):
     for kw in (dict(), dict(lower_bound=-5.0), dict(chunk_size=16), dict(chunk_size=32),
-               dict(K=128, V=64), dict(T=0), dict(dtype=kda.KDA_F32, scale=0.125)):
+               dict(K=128, V=64), dict(T=0), dict(dtype=kda.KDA_F32, scale=0.125),
+               dict(lower_bound=-5.0, lower_bound_form="clamp"), dict(H=2, HV=6), dict(H=2, HV=2)):
         st, err = _status(lib, _p(**kw))
         assert st == kda.OK, (kw, err)
+
+
+def test_validation_rejects_unknown_lower_bound_form(lib):
+    p = _p(lower_bound=-5.0)
+    p.lower_bound_form = 7
+    st, err = _status(lib, p)
+    assert st == kda.EINVAL and "lower_bound_form" in err, (st, err)
+    with pytest.raises(ValueError, match="lower_bound_form"):
+        _p(lower_bound_form="hard")
+
+
+def test_workspace_grows_with_value_heads(lib):
+    st = ctypes.c_int(0)
+    one = lib.kda_fwd_workspace_size(ctypes.byref(_p(H=2)), ctypes.byref(st))
+    three = lib.kda_fwd_workspace_size(ctypes.byref(_p(H=2, HV=6)), ctypes.byref(st))
+    assert st.value == kda.OK and three > 2 * one
 
 
 def _cu_problem(cu, T=None, B=1):
@@ -177,6 +197,13 @@ def test_python_binding_rejects_host_tensors():
         kda.kda_fwd(q, q, v, q, beta[:, :4], a_log, dt)
     with pytest.raises(ValueError, match="a_log must contain"):
         kda.kda_fwd(q, q, v, q, beta, torch.zeros(3), dt)
-    with pytest.raises(NotImplementedError):
-        kda.kda_fwd(q, q, torch.zeros(B, T, 4, K, dtype=torch.bfloat16), torch.zeros(B, T, 4, K),
-                    torch.zeros(B, T, 4), torch.zeros(4), torch.zeros(4, K))
+    # grouped value heads: 3 value heads do not divide over 2 key heads
+    with pytest.raises(ValueError, match="divisible"):
+        kda.kda_fwd(q, q, torch.zeros(B, T, 3, K, dtype=torch.bfloat16),
+                    torch.zeros(B, T, 3, K, dtype=torch.bfloat16),
+                    torch.zeros(B, T, 3, dtype=torch.bfloat16), torch.zeros(3), torch.zeros(3, K))
+    # 4 value heads over 2 key heads pass the shape checks and stop at the device check
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.kda_fwd(q, q, torch.zeros(B, T, 4, K, dtype=torch.bfloat16),
+                    torch.zeros(B, T, 4, K, dtype=torch.bfloat16),
+                    torch.zeros(B, T, 4, dtype=torch.bfloat16), torch.zeros(4), torch.zeros(4, K))

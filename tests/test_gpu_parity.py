@@ -7,6 +7,7 @@ import numpy as np
 import pytest
 import torch
 
+import oracle
 from gated_delta_rule_43_amd import kda, synthetic
 from kda_testlib import assert_close, errors, gpu_fwd, oracle_fwd, to_device, to_np
 
@@ -279,3 +280,68 @@ def test_extreme_gates_exact_diagonal(K, V):
     o_ref, f_ref = oracle_fwd(inp)
     assert_close(to_np(o), o_ref, torch.bfloat16, "o")
     assert_close(to_np(fin), f_ref, torch.bfloat16, "final_state")
+
+
+# ---------------------------------------------------------------------------
+# Grouped value heads: q, k with H key heads, v/gate/beta/states with HV value
+# heads, value head j reading key head j // (HV/H) (the shape contract of
+# `_validate_projected_inputs` on the hyper_parallel page).
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,K,V,chunk", [(torch.bfloat16, 128, 128, 64), (torch.bfloat16, 64, 64, 64),
+                                             (torch.float32, 64, 64, 32)])
+def test_grouped_value_heads_packed_documents(dtype, K, V, chunk):
+    print("[gpu-test] grouped value heads %s K=%d V=%d chunk=%d" % (dtype, K, V, chunk), flush=True)
+    lengths = [100, 37, 0, 170]
+    inp = synthetic.random_problem(2101, 1, sum(lengths), 2, K, V, dtype=dtype, device=DEV,
+                                   init_std=0.05, lengths=lengths, HV=6)
+    inp["chunk_size"] = chunk
+    o, fin = gpu_fwd(inp)
+    assert o.shape == (1, sum(lengths), 6, V) and fin.shape == (4, 6, K, V)
+    o_ref, f_ref = oracle_fwd(inp)
+    assert_close(to_np(o), o_ref, dtype, "o")
+    assert_close(to_np(fin), f_ref, dtype, "final_state")
+
+
+def test_grouped_value_heads_rows_and_summary():
+    print("[gpu-test] grouped value heads, rows + summary", flush=True)
+    inp = synthetic.random_problem(2102, 2, 150, 2, 128, 128, dtype=torch.bfloat16, device=DEV, HV=4)
+    o, fin = gpu_fwd(inp)
+    o_ref, f_ref = oracle_fwd(inp)
+    assert_close(to_np(o), o_ref, torch.bfloat16, "o")
+    assert_close(to_np(fin), f_ref, torch.bfloat16, "final_state")
+    E, P = kda.kda_state_summary(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"],
+                                 inp["a_log"], inp["dt_bias"])
+    torch.cuda.synchronize()
+    E_ref, P_ref = oracle.state_summary(*(to_np(inp[x]) for x in ("q", "k", "v", "gate", "beta", "a_log", "dt_bias")))
+    assert E.shape == (2, 4, 128, 128) and P.shape == (2, 4, 128, 128)
+    assert_close(to_np(E), E_ref, torch.bfloat16, "state_ext")
+    assert_close(to_np(P), P_ref, torch.bfloat16, "transition")
+
+
+# ---------------------------------------------------------------------------
+# The clamped lower-bounded gate, g = max(lb, -exp(a_log) softplus(x + b)), the
+# alternative reading of the bounded gate.  Heavy-tailed gate logits and a
+# tight bound make the clamp bind on a large share of the channels.
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,chunk", [(torch.bfloat16, 64), (torch.float32, 64), (torch.float32, 16)])
+def test_clamped_gate(dtype, chunk):
+    print("[gpu-test] clamped gate %s chunk=%d" % (dtype, chunk), flush=True)
+    lengths = [90, 1, 64, 129]
+    inp = synthetic.random_problem(2103, 1, sum(lengths), 3, 64, 64, dtype=dtype, device=DEV,
+                                   gate_std=3.0, beta_std=2.0, init_std=0.05, lengths=lengths)
+    inp.update(lower_bound=-0.5, lower_bound_form="clamp", chunk_size=chunk)
+    x = inp["gate"].float() + inp["dt_bias"][None, None]
+    A = torch.exp(inp["a_log"])[None, None, :, None]
+    g_free = -A * torch.nn.functional.softplus(x)
+    frac = float((g_free < -0.5).float().mean())
+    assert 0.2 < frac < 0.9, frac  # the clamp binds on a real share of the channels
+    o, fin = gpu_fwd(inp)
+    o_ref, f_ref = oracle_fwd(inp)
+    assert_close(to_np(o), o_ref, dtype, "o")
+    assert_close(to_np(fin), f_ref, dtype, "final_state")
+    # and it is the clamp, not the sigmoid form: the result is several times
+    # closer to the clamp oracle than to the sigmoid one
+    o_sig, _ = oracle_fwd(dict(inp, lower_bound_form="sigmoid"))
+    d_ref, _ = errors(to_np(o), o_ref)
+    d_sig, _ = errors(to_np(o), o_sig)
+    assert d_sig > 5e-3 and d_sig > 5 * d_ref, (d_sig, d_ref)
