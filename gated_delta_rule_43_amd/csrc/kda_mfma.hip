@@ -161,11 +161,11 @@ struct Rec {
   static constexpr int oAqk = kStage;                       // [4][2] frags (read straight to registers)
   static constexpr int oU = oAqk + 8 * kFrag;               // [4][NVT] tiles of 64 lanes x 8 B
   static constexpr int kBytes = oU + 4 * NVT * 512;
-  // the state pass copies whole 4 KiB rounds (64 lanes x 16 B x 4); the
-  // rounded stage still ends inside the record
-  static constexpr int kStageRounds = (kStage + 4095) / 4096;
+  // the state pass copies the stage in whole 1 KiB copies (64 lanes x 16 B);
+  // the rounded stage still ends inside the record
+  static constexpr int kStageCopies = (kStage + 1023) / 1024;
   static_assert(kStage % 16 == 0 && kBytes % 256 == 0, "record alignment");
-  static_assert(kStageRounds * 4096 <= kBytes, "rounded stage must stay inside the record");
+  static_assert(kStageCopies * 1024 <= kBytes, "rounded stage must stay inside the record");
 };
 
 // ---------------------------------------------------------------------------
@@ -703,7 +703,7 @@ __global__ __launch_bounds__(64 * (CW + 1)) __attribute__((amdgpu_waves_per_eu(2
   // three stage buffers: chunk c is consumed while c+1 has landed or is landing
   // and c+2 streams in (global -> LDS, no registers), which gives each copy two
   // chunks' time to arrive from HBM
-  constexpr int kStageBytes = R::kStageRounds * 4096;
+  constexpr int kStageBytes = R::kStageCopies * 1024;
   __shared__ __attribute__((aligned(16))) char sStage0[kStageBytes];
   __shared__ __attribute__((aligned(16))) char sStage1[kStageBytes];
   __shared__ __attribute__((aligned(16))) char sStage2[kStageBytes];
@@ -717,7 +717,7 @@ __global__ __launch_bounds__(64 * (CW + 1)) __attribute__((amdgpu_waves_per_eu(2
     // written out because a workgroup fence would also wait for the newer
     // copy; this wave reads nothing, and the memory clobber keeps each copy
     // below the barrier that frees its buffer.
-    constexpr int kCopies = 4 * R::kStageRounds;  // copy instructions per record
+    constexpr int kCopies = R::kStageCopies;  // copy instructions per record
     static_assert(kCopies < 64, "wait count field");
     // (the LDS side of a copy is a compile-time buffer: its address goes to M0)
     auto stage = [&](int jc, auto bufc) {
