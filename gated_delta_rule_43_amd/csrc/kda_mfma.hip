@@ -677,8 +677,11 @@ __global__ __launch_bounds__(kThreads) void k_chunk_mfma_exact(FwdArgs a) {
 // more wave only streams the records into LDS, so that the compute waves never
 // stall on those loads.  Fewer compute waves per workgroup spread a problem
 // with few (sequence, head) pairs over more CUs.
+// (the bound is the five-wave workgroup for every CW: it keeps the register
+// allocation of all variants within 256 without accumulator-register copies)
 template <int K, int V, int CW, bool SUM>
-__global__ __launch_bounds__(64 * (CW + 1)) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_state_mfma(FwdArgs a) {
+__global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(2, 2))) void k_state_mfma(FwdArgs a) {
+  static_assert(64 * (CW + 1) <= 320, "workgroup size");
   using R = Rec<K, V>;
   constexpr int NCT = 1;  // column tiles per compute wave
   constexpr int NKJ = K / 32, NKT = K / 16, NVT = V / 16;
