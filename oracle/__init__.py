@@ -6,15 +6,19 @@ HIP library and its Python binding) never imports this package, and this
 package imports nothing from the product.
 
 The arithmetic lives in ``kda_oracle.c`` (compiled with gcc, loaded through
-ctypes).  Inputs are taken as float32 arrays (bf16 and fp32 values upcast
-exactly), outputs are float64.  See ``kda_oracle.c`` for the definition and the
+ctypes).  q, k and v are taken as float64 arrays (bf16 and fp32 values upcast
+exactly; the short convolution's fp64 output passes through unrounded), the
+gate inputs as float32 arrays; outputs are float64.  See ``kda_oracle.c`` for the definition and the
 passages of the pages each part follows.  ``chunked.py`` holds a second,
 chunk-parallel fp64 form used only to cross-check the chunk algebra.
 
 Pins: every public function here is checked by ``tests/test_oracle_*.py``
 against brute-force matrix products, closed forms and invariants; the
 alternative gate reading (``gate_mode="clamp"``) is pinned by closed forms of
-its own gate values only.
+its own gate values only.  ``short_conv_silu`` (the layer's causal depthwise
+convolution and SiLU before the forward) is pinned by
+``tests/test_oracle_short_conv.py`` against the library conv1d called the way
+the pages call it, closed-form taps and SiLU special values.
 """
 from __future__ import annotations
 
@@ -59,8 +63,10 @@ def _load():
         lib.oracle_recurrence.argtypes = [I, I, I, I, I, P, P, P, P, P, D, I, P, P, P, P, I]
         lib.oracle_state_summary.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, I, D, P, P, I]
         lib.oracle_apply_state_summary.argtypes = [I, I, I, I, P, P, P, P]
+        lib.oracle_short_conv_silu.argtypes = [I, I, I, I, P, P, P, I, P, P]
         for f in (lib.oracle_prologue, lib.oracle_kda_fwd, lib.oracle_recurrence,
-                  lib.oracle_state_summary, lib.oracle_apply_state_summary):
+                  lib.oracle_state_summary, lib.oracle_apply_state_summary,
+                  lib.oracle_short_conv_silu):
             f.restype = I
         _lib = lib
     return _lib
@@ -96,7 +102,8 @@ def default_threads() -> int:
 
 def prologue(q, k, gate, beta, a_log, dt_bias, lower_bound=None, gate_mode=None):
     """q^, k^ (L2-normalised), log-decay g and beta = sigmoid(logit), all fp64."""
-    q, k, gate, beta, a_log, dt_bias = map(_f32, (q, k, gate, beta, a_log, dt_bias))
+    q, k = _f64(q), _f64(k)
+    gate, beta, a_log, dt_bias = map(_f32, (gate, beta, a_log, dt_bias))
     B, T, H, K = q.shape
     mode, lb = _gate(lower_bound, gate_mode)
     qn = np.empty(q.shape, np.float64)
@@ -126,7 +133,8 @@ def kda_fwd(q, k, v, gate, beta, a_log, dt_bias, scale=None, lower_bound=None,
     H is the number of value heads (v, gate, beta, a_log, dt_bias, o, states);
     q and k may have fewer key heads HK dividing H, value head h then reading
     key head h // (H // HK) (grouped value heads)."""
-    q, k, v, gate, beta, a_log, dt_bias = map(_f32, (q, k, v, gate, beta, a_log, dt_bias))
+    q, k, v = map(_f64, (q, k, v))
+    gate, beta, a_log, dt_bias = map(_f32, (gate, beta, a_log, dt_bias))
     B, T, HK, K = q.shape
     H, V = v.shape[2], v.shape[-1]
     if H % HK:
@@ -148,8 +156,7 @@ def kda_fwd(q, k, v, gate, beta, a_log, dt_bias, scale=None, lower_bound=None,
 
 def recurrence(qn, kn, v, g, b, scale, cu_seqlens=None, initial_state=None, threads=None):
     """Token recurrence from already normalised inputs.  Returns (o, final_state)."""
-    qn, kn, g, b = map(_f64, (qn, kn, g, b))
-    v = _f32(v)
+    qn, kn, g, b, v = map(_f64, (qn, kn, g, b, v))
     B, T, H, K = qn.shape
     V = v.shape[-1]
     cu, N = _cu(cu_seqlens, B, T)
@@ -168,7 +175,8 @@ def state_summary(q, k, v, gate, beta, a_log, dt_bias, lower_bound=None, gate_mo
                   threads=None):
     """Affine summary of each row: (state_ext [B,H,K,V], transition [B,H,K,K]), fp64.
     Heads as in kda_fwd (q, k may carry fewer key heads)."""
-    q, k, v, gate, beta, a_log, dt_bias = map(_f32, (q, k, v, gate, beta, a_log, dt_bias))
+    q, k, v = map(_f64, (q, k, v))
+    gate, beta, a_log, dt_bias = map(_f32, (gate, beta, a_log, dt_bias))
     B, T, HK, K = q.shape
     H, V = v.shape[2], v.shape[-1]
     if H % HK:
@@ -193,3 +201,43 @@ def apply_state_summary(state_ext, transition, initial_state=None):
     out = np.zeros_like(E)
     _load().oracle_apply_state_summary(B, H, K, V, _ptr(E), _ptr(P), _ptr(init), _ptr(out))
     return out
+
+
+def short_conv_silu(x, weight=None, bias=None, cu_seqlens=None):
+    """SiLU of the causal depthwise convolution of x over time, fp64.
+
+    x [B,T,C] or [B,T,H,D] (channels h*D + d); weight [C,W] (or [C,1,W], the
+    depthwise Conv1d weight) with tap W-1 on the current token; bias [C] or
+    None.  weight None: SiLU alone.  Tokens before a sequence's first token
+    (row start, or document start with cu_seqlens) count as zero."""
+    x = _f64(x)
+    shape = x.shape
+    B, T = shape[0], shape[1]
+    C = int(np.prod(shape[2:]))
+    if weight is None:
+        W, w = 0, None
+    else:
+        w = _f64(weight).reshape(C, -1)
+        W = w.shape[1]
+    b = None if bias is None else _f64(bias).reshape(C)
+    cu, N = _cu(cu_seqlens, B, T)
+    y = np.empty(shape, np.float64)
+    rc = _load().oracle_short_conv_silu(B, T, C, W, _ptr(x), _ptr(w), _ptr(b), N, _ptr(cu), _ptr(y))
+    if rc:
+        raise ValueError("oracle_short_conv_silu rejected its arguments (%d)" % rc)
+    return y
+
+
+def kda_fwd_short_conv(q, k, v, gate, beta, a_log, dt_bias, conv_weights=None, conv_biases=None,
+                       cu_seqlens=None, **kwargs):
+    """kda_fwd after the layer's short convolution and SiLU on q, k and v.
+
+    conv_weights: None (SiLU alone) or (w_q, w_k, w_v), each [channels, W];
+    conv_biases: None or (b_q, b_k, b_v), entries may be None.  The remaining
+    keyword arguments are those of kda_fwd."""
+    wq, wk, wv = conv_weights if conv_weights is not None else (None, None, None)
+    bq, bk, bv = conv_biases if conv_biases is not None else (None, None, None)
+    q2 = short_conv_silu(q, wq, bq, cu_seqlens)
+    k2 = short_conv_silu(k, wk, bk, cu_seqlens)
+    v2 = short_conv_silu(v, wv, bv, cu_seqlens)
+    return kda_fwd(q2, k2, v2, gate, beta, a_log, dt_bias, cu_seqlens=cu_seqlens, **kwargs)

@@ -5,8 +5,10 @@
  * call this file; only the tests, the smoke check and the benchmark's CPU
  * baseline use it.  It shares no code with the HIP library.
  *
- * Everything is computed token by token, in fp64, after an exact upcast of the
- * fp32 (or bf16-valued) inputs.  No chunking, no blocking, no fusion.
+ * Everything is computed token by token, in fp64.  q, k and v are taken as
+ * fp64 (an exact upcast of fp32 or bf16 values, or the fp64 output of the
+ * short convolution below); the gate inputs are fp32.  No chunking, no
+ * blocking, no fusion.
  *
  * Sources (the pages give the interface; the recurrence is the KDA definition):
  *  - call contract of chunk_kda (q, k, v, gate, beta, a_log, dt_bias, scale,
@@ -55,11 +57,11 @@ static double softplus(double x) { return fmax(x, 0.0) + log1p(exp(-fabs(x))); }
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
 /* L2 normalisation of one head vector (in-kernel q/k norm). */
-static void l2norm(const float* x, int n, double* out) {
+static void l2norm(const double* x, int n, double* out) {
   double ss = 0.0;
-  for (int i = 0; i < n; ++i) ss += (double)x[i] * (double)x[i];
+  for (int i = 0; i < n; ++i) ss += x[i] * x[i];
   double r = 1.0 / sqrt(ss + ORACLE_EPS);
-  for (int i = 0; i < n; ++i) out[i] = (double)x[i] * r;
+  for (int i = 0; i < n; ++i) out[i] = x[i] * r;
 }
 
 /* Per-key-channel log-decay built from the raw gate logits (in-kernel gate). */
@@ -81,7 +83,7 @@ static void gate_row(const float* gate, const float* dt_bias_h, double a_log_h, 
 /* ------------------------------------------------------------------------ */
 /* Public: prologue only (q^, k^, g, beta) for every token and head.         */
 /* ------------------------------------------------------------------------ */
-int oracle_prologue(int B, int T, int H, int K, const float* q, const float* k, const float* gate,
+int oracle_prologue(int B, int T, int H, int K, const double* q, const double* k, const float* gate,
                     const float* beta, const float* a_log, const float* dt_bias, int gate_mode,
                     double lower_bound, double* qn, double* kn, double* g, double* b) {
   if (B < 0 || T < 0 || H <= 0 || K <= 0) return 1;
@@ -100,7 +102,7 @@ int oracle_prologue(int B, int T, int H, int K, const float* q, const float* k, 
 
 /* One token of the recurrence on state S (K x V, row-major). */
 static void recur_step(double* S, int K, int V, const double* qn, const double* kn, const double* g,
-                       double bt, const float* v, double scale, double* u, double* o_out) {
+                       double bt, const double* v, double scale, double* u, double* o_out) {
   /* S <- Diag(exp g) S */
   for (int c = 0; c < K; ++c) {
     double d = exp(g[c]);
@@ -117,7 +119,7 @@ static void recur_step(double* S, int K, int V, const double* qn, const double* 
   for (int c = 0; c < K; ++c) {
     double* row = S + (long)c * V;
     double bk = bt * kn[c];
-    for (int j = 0; j < V; ++j) row[j] += bk * ((double)v[j] - u[j]);
+    for (int j = 0; j < V; ++j) row[j] += bk * (v[j] - u[j]);
   }
   /* o = scale * S^T q^ */
   if (o_out) {
@@ -136,7 +138,8 @@ static void recur_step(double* S, int K, int V, const double* qn, const double* 
 typedef struct {
   int B, T, H, K, V;
   int HK; /* key heads of q and k (raw entries); value head h reads key head h / (H / HK) */
-  const float *q, *k, *v, *gate, *beta, *a_log, *dt_bias;
+  const double *q, *k, *v;
+  const float *gate, *beta, *a_log, *dt_bias;
   /* pre-normalised inputs (recurrence-only entry); NULL when raw is used */
   const double *qn, *kn, *g, *bb;
   int gate_mode;
@@ -180,7 +183,7 @@ static void* worker(void* arg) {
   double* qn = (double*)malloc(sizeof(double) * K);
   double* kn = (double*)malloc(sizeof(double) * K);
   double* g = (double*)malloc(sizeof(double) * K);
-  float* zeros = (float*)calloc((size_t)(K > V ? K : V), sizeof(float));
+  double* zeros = (double*)calloc((size_t)(K > V ? K : V), sizeof(double));
   for (;;) {
     int w = take(J);
     if (w >= J->N * H) break;
@@ -266,8 +269,8 @@ static int check_cu(int B, int T, int N, const int32_t* cu) {
 /*   a_log [H], dt_bias [H,K]; o [B,T,H,V] (may be NULL), final_state        */
 /*   [N,H,K,V] (may be NULL).                                                */
 /* ------------------------------------------------------------------------ */
-int oracle_kda_fwd(int B, int T, int H, int HK, int K, int V, const float* q, const float* k,
-                   const float* v, const float* gate, const float* beta, const float* a_log,
+int oracle_kda_fwd(int B, int T, int H, int HK, int K, int V, const double* q, const double* k,
+                   const double* v, const float* gate, const float* beta, const float* a_log,
                    const float* dt_bias, double scale, int gate_mode, double lower_bound, int N,
                    const int32_t* cu_seqlens, const float* initial_state, double* o,
                    double* final_state, int threads) {
@@ -284,10 +287,10 @@ int oracle_kda_fwd(int B, int T, int H, int HK, int K, int V, const float* q, co
 
 /* ------------------------------------------------------------------------ */
 /* Public: recurrence only, from already normalised q^, k^, log-decay g and  */
-/* beta (all [B,T,H,*] fp64).  v and initial_state are fp32 as above.        */
+/* beta (all [B,T,H,*] fp64).  v is fp64, initial_state fp32 as above.      */
 /* ------------------------------------------------------------------------ */
 int oracle_recurrence(int B, int T, int H, int K, int V, const double* qn, const double* kn,
-                      const float* v, const double* g, const double* b, double scale, int N,
+                      const double* v, const double* g, const double* b, double scale, int N,
                       const int32_t* cu_seqlens, const float* initial_state, double* o,
                       double* final_state, int threads) {
   if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return 1;
@@ -307,8 +310,8 @@ int oracle_recurrence(int B, int T, int H, int K, int V, const double* qn, const
 /*                          (I - beta k^ k^T) Diag(exp g), later on the left */
 /* so that final_state = transition . initial_state + state_ext.            */
 /* ------------------------------------------------------------------------ */
-int oracle_state_summary(int B, int T, int H, int HK, int K, int V, const float* q,
-                         const float* k, const float* v, const float* gate, const float* beta,
+int oracle_state_summary(int B, int T, int H, int HK, int K, int V, const double* q,
+                         const double* k, const double* v, const float* gate, const float* beta,
                          const float* a_log, const float* dt_bias, int gate_mode,
                          double lower_bound, double* state_ext, double* transition, int threads) {
   if (B < 0 || T < 0 || H <= 0 || HK <= 0 || H % HK || K <= 0 || V <= 0) return 1;
@@ -319,6 +322,49 @@ int oracle_state_summary(int B, int T, int H, int HK, int K, int V, const float*
   J.gate_mode = gate_mode; J.lb = lower_bound; J.scale = 1.0;
   J.N = B; J.fin = state_ext; J.trans = transition; J.summary = 1;
   return run_job(&J, threads);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Public: the causal depthwise short convolution and SiLU applied to q, k  */
+/* and v before the recurrence (the ShortConv of the Kimi layer: depthwise   */
+/* conv1d, stride 1, dilation 1, zero padding of W-1 tokens on the left,     */
+/* output cut to the sequence length, then SiLU; without the convolution the */
+/* layer applies SiLU alone).  Source: hyper_parallel coverage page,         */
+/* `_run_causal_short_conv`, `_validate_layer_short_conv` and the forward of */
+/* KimiDeltaAttentionUlyssesCP.                                             */
+/*   x, y [B,T,C] fp64 (C channels, e.g. H*K), w [C,W] (tap W-1 weights the */
+/*   current token, tap 0 the token W-1 steps back), bias [C] or NULL.      */
+/*   y[t,c] = silu(bias[c] + sum_j w[c,j] * x[t-(W-1)+j, c]),               */
+/*   silu(z) = z * sigmoid(z).                                              */
+/* Tokens before the first token of t's sequence count as zero: with        */
+/* cu_seqlens every document is padded on its own (the pages pad each row;  */
+/* a packed row holds independent documents, so the padding is taken per     */
+/* document).  W = 0: y = silu(x).                                          */
+/* ------------------------------------------------------------------------ */
+int oracle_short_conv_silu(int B, int T, int C, int W, const double* x, const double* w,
+                           const double* bias, int N, const int32_t* cu_seqlens, double* y) {
+  if (B < 0 || T < 0 || C <= 0 || W < 0 || (W > 0 && !w)) return 1;
+  if (check_cu(B, T, N, cu_seqlens)) return 2;
+  for (int n = 0; n < N; ++n) {
+    const long row = cu_seqlens ? 0 : n;
+    const long t0 = cu_seqlens ? cu_seqlens[n] : 0;
+    const long t1 = cu_seqlens ? cu_seqlens[n + 1] : T;
+    for (long t = t0; t < t1; ++t)
+      for (int c = 0; c < C; ++c) {
+        double z;
+        if (W == 0) {
+          z = x[(row * T + t) * C + c];
+        } else {
+          z = bias ? bias[c] : 0.0;
+          for (int j = 0; j < W; ++j) {
+            const long s = t - (W - 1) + j; /* input token of tap j */
+            if (s >= t0) z += w[(long)c * W + j] * x[(row * T + s) * C + c];
+          }
+        }
+        y[(row * T + t) * C + c] = z * sigmoid(z);
+      }
+  }
+  return 0;
 }
 
 /* Public: final = transition . initial + state_ext (initial may be NULL). */
