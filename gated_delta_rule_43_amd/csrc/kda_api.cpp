@@ -35,6 +35,41 @@ bool head_dim_ok(int d) { return d == 64 || d == 128; }
 // value heads (HV, 0 meaning H)
 int value_heads(const kda_problem* p) { return p->HV > 0 ? p->HV : p->H; }
 
+// Rows, dtype and document layout (B, T, dtype, N, cu_seqlens, cu_seqlens_host).
+kda_status validate_rows(const kda_problem* p, bool summary) {
+  if (!p) return fail(KDA_EINVAL, "problem is NULL");
+  if (p->B < 1 || p->T < 0) return fail(KDA_EINVAL, "bad shape B=%d T=%d (need B >= 1, T >= 0)", p->B, p->T);
+  if (p->dtype != KDA_F32 && p->dtype != KDA_BF16)
+    return fail(KDA_EINVAL, "dtype must be KDA_F32 or KDA_BF16, got %d", p->dtype);
+  if ((long long)p->B * p->T >= (1LL << 31))
+    return fail(KDA_EUNSUPPORTED, "B*T = %lld tokens exceeds 2^31", (long long)p->B * p->T);
+  if (p->cu_seqlens == nullptr) {
+    if (p->cu_seqlens_host != nullptr)
+      return fail(KDA_EINVAL, "cu_seqlens_host given without cu_seqlens");
+    if (p->N != p->B)
+      return fail(KDA_EINVAL, "N must equal B (%d) without cu_seqlens, got %d", p->B, p->N);
+  } else {
+    if (summary) return fail(KDA_EINVAL, "a state summary takes no cu_seqlens (one slice per row)");
+    if (p->B != 1) return fail(KDA_EINVAL, "cu_seqlens requires B == 1 (one packed row), got B=%d", p->B);
+    if (p->N < 0 || (p->N == 0 && p->T != 0))
+      return fail(KDA_EINVAL, "cu_seqlens must describe at least one sequence (N=%d, T=%d)", p->N, p->T);
+    if (const int32_t* cu = p->cu_seqlens_host) {
+      if (cu[0] != 0) return fail(KDA_EINVAL, "cu_seqlens[0] must be 0, got %d", cu[0]);
+      for (int n = 0; n < p->N; ++n) {
+        if (cu[n + 1] < 0)
+          return fail(KDA_EINVAL, "cu_seqlens[%d] = %d is negative (padding sentinels are not accepted)",
+                      n + 1, cu[n + 1]);
+        if (cu[n + 1] < cu[n])
+          return fail(KDA_EINVAL, "cu_seqlens must be non-decreasing: cu[%d]=%d < cu[%d]=%d", n + 1,
+                      cu[n + 1], n, cu[n]);
+      }
+      if (cu[p->N] != p->T)
+        return fail(KDA_EINVAL, "cu_seqlens[N] must equal T=%d, got %d", p->T, cu[p->N]);
+    }
+  }
+  return KDA_OK;
+}
+
 // Shape/flag validation shared by every entry point (no pointers checked here).
 kda_status validate_problem(const kda_problem* p, bool summary) {
   if (!p) return fail(KDA_EINVAL, "problem is NULL");
@@ -61,31 +96,7 @@ kda_status validate_problem(const kda_problem* p, bool summary) {
   const long long BT = (long long)p->B * p->T;
   if (BT >= (1LL << 31) || BT * value_heads(p) >= (1LL << 31))
     return fail(KDA_EUNSUPPORTED, "B*T*HV = %lld token-heads exceeds 2^31", BT * value_heads(p));
-  if (p->cu_seqlens == nullptr) {
-    if (p->cu_seqlens_host != nullptr)
-      return fail(KDA_EINVAL, "cu_seqlens_host given without cu_seqlens");
-    if (p->N != p->B)
-      return fail(KDA_EINVAL, "N must equal B (%d) without cu_seqlens, got %d", p->B, p->N);
-  } else {
-    if (summary) return fail(KDA_EINVAL, "a state summary takes no cu_seqlens (one slice per row)");
-    if (p->B != 1) return fail(KDA_EINVAL, "cu_seqlens requires B == 1 (one packed row), got B=%d", p->B);
-    if (p->N < 0 || (p->N == 0 && p->T != 0))
-      return fail(KDA_EINVAL, "cu_seqlens must describe at least one sequence (N=%d, T=%d)", p->N, p->T);
-    if (const int32_t* cu = p->cu_seqlens_host) {
-      if (cu[0] != 0) return fail(KDA_EINVAL, "cu_seqlens[0] must be 0, got %d", cu[0]);
-      for (int n = 0; n < p->N; ++n) {
-        if (cu[n + 1] < 0)
-          return fail(KDA_EINVAL, "cu_seqlens[%d] = %d is negative (padding sentinels are not accepted)",
-                      n + 1, cu[n + 1]);
-        if (cu[n + 1] < cu[n])
-          return fail(KDA_EINVAL, "cu_seqlens must be non-decreasing: cu[%d]=%d < cu[%d]=%d", n + 1,
-                      cu[n + 1], n, cu[n]);
-      }
-      if (cu[p->N] != p->T)
-        return fail(KDA_EINVAL, "cu_seqlens[N] must equal T=%d, got %d", p->T, cu[p->N]);
-    }
-  }
-  return KDA_OK;
+  return validate_rows(p, summary);
 }
 
 // Which kernels run: the MFMA path for bf16 with 64-token chunks, the fp32
@@ -229,6 +240,104 @@ kda_status check_ws(size_t need, void* ws, size_t bytes) {
   return KDA_OK;
 }
 
+// Widths of the short convolution this build instantiates.
+kda_status check_width(int width) {
+  if (width < 0) return fail(KDA_EINVAL, "short convolution width must be >= 0, got %d", width);
+  if (width > 4) return fail(KDA_EUNSUPPORTED, "short convolution width %d is not supported (0..4)", width);
+  return KDA_OK;
+}
+
+// The convolved q, k, v of kda_fwd_short_conv, placed after the forward's own
+// workspace (which starts at offset 0 and is laid out as for kda_fwd).
+struct ConvBuffers {
+  size_t off_q = 0, off_k = 0, off_v = 0, total = 0;
+};
+
+ConvBuffers conv_buffers(const kda_problem* p, size_t base) {
+  ConvBuffers c;
+  const size_t elt = p->dtype == KDA_BF16 ? 2 : 4;
+  const size_t tokens = (size_t)p->B * p->T;
+  c.off_q = align_up(base);
+  c.off_k = align_up(c.off_q + tokens * p->H * p->K * elt);
+  c.off_v = align_up(c.off_k + tokens * p->H * p->K * elt);
+  c.total = align_up(c.off_v + tokens * value_heads(p) * p->V * elt);
+  return c;
+}
+
+kda_status check_conv(const kda_problem* p, const kda_short_conv* conv, const void* q,
+                      const void* k, const void* v) {
+  kda_status st = check_width(conv->width);
+  if (st != KDA_OK) return st;
+  if (conv->width > 0 && (!conv->q_weight || !conv->k_weight || !conv->v_weight))
+    return fail(KDA_EINVAL, "a convolution of width %d needs q, k and v weights", conv->width);
+  const float* fp[] = {conv->q_weight, conv->k_weight, conv->v_weight,
+                       conv->q_bias, conv->k_bias, conv->v_bias};
+  for (const float* f : fp)
+    if (f && !aligned(f, 4)) return fail(KDA_EINVAL, "short convolution weights and biases must be 4-byte aligned");
+  const void* in[] = {q, k, v};
+  for (const void* ptr : in)
+    if (ptr && !aligned(ptr, 16))
+      return fail(KDA_EINVAL, "q, k and v must be 16-byte aligned for the short convolution");
+  return KDA_OK;
+}
+
+// kda_fwd, optionally after the short convolution of q, k and v.
+kda_status fwd_impl(const kda_problem* p, const kda_short_conv* conv, const void* q, const void* k,
+                    const void* v, const void* gate, const void* beta, const float* a_log,
+                    const float* dt_bias, const float* initial_state, void* o,
+                    float* final_state, void* workspace, size_t workspace_bytes, void* stream,
+                    void* const* stage_events) {
+  kda_status st = validate_problem(p, false);
+  if (st != KDA_OK) return st;
+  st = check_inputs(p, q, k, v, gate, beta, a_log, dt_bias);
+  if (st != KDA_OK) return st;
+  if (!o && (long long)p->B * p->T > 0) return fail(KDA_EINVAL, "output o must be non-NULL");
+  if (initial_state && !aligned(initial_state, 4)) return fail(KDA_EINVAL, "initial_state misaligned");
+  if (final_state && !aligned(final_state, 4)) return fail(KDA_EINVAL, "final_state misaligned");
+  if (o && !aligned(o, p->dtype == KDA_BF16 ? 2 : 4)) return fail(KDA_EINVAL, "o misaligned");
+  const Layout L = layout(p);
+  ConvBuffers cb;
+  if (conv) {
+    st = check_conv(p, conv, q, k, v);
+    if (st != KDA_OK) return st;
+    cb = conv_buffers(p, L.total);
+  }
+  st = check_ws(conv ? cb.total : L.total, workspace, workspace_bytes);
+  if (st != KDA_OK) return st;
+  if (L.mfma) {
+    const void* vec[] = {q, k, v, gate, o};
+    for (const void* ptr : vec)
+      if (ptr && !aligned(ptr, 16))
+        return fail(KDA_EINVAL, "bf16 q, k, v, gate and o must be 16-byte aligned");
+  }
+  hipStream_t s = (hipStream_t)stream;
+  if (conv && (long long)p->B * p->T > 0) {
+    char* w = (char*)workspace;
+    kda::ConvArgs c{};
+    c.B = p->B; c.T = p->T; c.N = p->N; c.dtype = p->dtype; c.width = conv->width;
+    c.cu = p->cu_seqlens;
+    c.count = 3;
+    c.t[0] = kda::ConvTensor{q, conv->q_weight, conv->q_bias, w + cb.off_q, p->H * p->K};
+    c.t[1] = kda::ConvTensor{k, conv->k_weight, conv->k_bias, w + cb.off_k, p->H * p->K};
+    c.t[2] = kda::ConvTensor{v, conv->v_weight, conv->v_bias, w + cb.off_v, value_heads(p) * p->V};
+    hipError_t e = kda::launch_short_conv(c, s);
+    if (e != hipSuccess) return fail(KDA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+    q = w + cb.off_q;
+    k = w + cb.off_k;
+    v = w + cb.off_v;
+  }
+
+  kda::FwdArgs a = make_args(p, L, workspace);
+  a.q = q; a.k = k; a.v = v; a.gate = gate; a.beta = beta;
+  a.a_log = a_log; a.dt_bias = dt_bias; a.init = initial_state;
+  a.o = o; a.fin = final_state; a.summary = 0;
+  a.events = stage_events;
+  hipError_t e = launch(a, L, s);
+  if (e != hipSuccess) return fail(KDA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_last_error.clear();
+  return KDA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -256,42 +365,65 @@ kda_status kda_fwd_profiled(const kda_problem* p, const void* q, const void* k, 
                             const float* dt_bias, const float* initial_state, void* o,
                             float* final_state, void* workspace, size_t workspace_bytes,
                             void* stream, void* const* stage_events) {
-  kda_status st = validate_problem(p, false);
-  if (st != KDA_OK) return st;
-  st = check_inputs(p, q, k, v, gate, beta, a_log, dt_bias);
-  if (st != KDA_OK) return st;
-  if (!o && (long long)p->B * p->T > 0) return fail(KDA_EINVAL, "output o must be non-NULL");
-  if (initial_state && !aligned(initial_state, 4)) return fail(KDA_EINVAL, "initial_state misaligned");
-  if (final_state && !aligned(final_state, 4)) return fail(KDA_EINVAL, "final_state misaligned");
-  if (o && !aligned(o, p->dtype == KDA_BF16 ? 2 : 4)) return fail(KDA_EINVAL, "o misaligned");
-  const Layout L = layout(p);
-  st = check_ws(L.total, workspace, workspace_bytes);
-  if (st != KDA_OK) return st;
-  if (L.mfma) {
-    const void* vec[] = {q, k, v, gate, o};
-    for (const void* ptr : vec)
-      if (ptr && !aligned(ptr, 16))
-        return fail(KDA_EINVAL, "bf16 q, k, v, gate and o must be 16-byte aligned");
-  }
-
-  kda::FwdArgs a = make_args(p, L, workspace);
-  a.q = q; a.k = k; a.v = v; a.gate = gate; a.beta = beta;
-  a.a_log = a_log; a.dt_bias = dt_bias; a.init = initial_state;
-  a.o = o; a.fin = final_state; a.summary = 0;
-  a.events = stage_events;
-  hipStream_t s = (hipStream_t)stream;
-  hipError_t e = launch(a, L, s);
-  if (e != hipSuccess) return fail(KDA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
-  g_last_error.clear();
-  return KDA_OK;
+  return fwd_impl(p, nullptr, q, k, v, gate, beta, a_log, dt_bias, initial_state, o, final_state,
+                  workspace, workspace_bytes, stream, stage_events);
 }
 
 kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const void* v,
                    const void* gate, const void* beta, const float* a_log, const float* dt_bias,
                    const float* initial_state, void* o, float* final_state, void* workspace,
                    size_t workspace_bytes, void* stream) {
-  return kda_fwd_profiled(p, q, k, v, gate, beta, a_log, dt_bias, initial_state, o, final_state,
-                          workspace, workspace_bytes, stream, nullptr);
+  return fwd_impl(p, nullptr, q, k, v, gate, beta, a_log, dt_bias, initial_state, o, final_state,
+                  workspace, workspace_bytes, stream, nullptr);
+}
+
+size_t kda_fwd_short_conv_workspace_size(const kda_problem* p, kda_status* status) {
+  kda_status st = validate_problem(p, false);
+  if (status) *status = st;
+  return st == KDA_OK ? conv_buffers(p, layout(p).total).total : 0;
+}
+
+kda_status kda_fwd_short_conv(const kda_problem* p, const kda_short_conv* conv, const void* q,
+                              const void* k, const void* v, const void* gate, const void* beta,
+                              const float* a_log, const float* dt_bias,
+                              const float* initial_state, void* o, float* final_state,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!conv) return fail(KDA_EINVAL, "short convolution description is NULL");
+  return fwd_impl(p, conv, q, k, v, gate, beta, a_log, dt_bias, initial_state, o, final_state,
+                  workspace, workspace_bytes, stream, nullptr);
+}
+
+kda_status kda_short_conv_silu(const kda_problem* p, int32_t channels, int32_t width,
+                               const void* x, const float* weight, const float* bias, void* y,
+                               void* stream) {
+  kda_status st = validate_rows(p, false);
+  if (st != KDA_OK) return st;
+  st = check_width(width);
+  if (st != KDA_OK) return st;
+  const int nv = p->dtype == KDA_BF16 ? 8 : 4;
+  if (channels < 1 || channels % nv)
+    return fail(KDA_EINVAL, "channels must be a positive multiple of %d, got %d", nv, channels);
+  const long long tokens = (long long)p->B * p->T;
+  if (tokens == 0) {
+    g_last_error.clear();
+    return KDA_OK;
+  }
+  if (!x || !y) return fail(KDA_EINVAL, "x and y must be non-NULL");
+  if (!aligned(x, 16) || !aligned(y, 16)) return fail(KDA_EINVAL, "x and y must be 16-byte aligned");
+  if (width > 0 && !weight) return fail(KDA_EINVAL, "a convolution of width %d needs its weight", width);
+  if ((weight && !aligned(weight, 4)) || (bias && !aligned(bias, 4)))
+    return fail(KDA_EINVAL, "weight and bias must be 4-byte aligned");
+  const size_t bytes = (size_t)tokens * channels * (p->dtype == KDA_BF16 ? 2 : 4);
+  const uintptr_t xb = (uintptr_t)x, yb = (uintptr_t)y;
+  if (xb < yb + bytes && yb < xb + bytes) return fail(KDA_EINVAL, "y may not overlap x");
+  kda::ConvArgs c{};
+  c.B = p->B; c.T = p->T; c.N = p->N; c.dtype = p->dtype; c.width = width; c.cu = p->cu_seqlens;
+  c.count = 1;
+  c.t[0] = kda::ConvTensor{x, weight, bias, y, channels};
+  hipError_t e = kda::launch_short_conv(c, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(KDA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_last_error.clear();
+  return KDA_OK;
 }
 
 kda_status kda_state_summary(const kda_problem* p, const void* q, const void* k, const void* v,

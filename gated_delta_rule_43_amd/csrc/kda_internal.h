@@ -77,6 +77,24 @@ struct FwdArgs {
   void* const* events;
 };
 
+// One short-convolution launch over up to three tensors x -> y ([B*T, C],
+// dtype as FwdArgs::dtype); weights [C, width] fp32, bias [C] fp32 or null.
+struct ConvTensor {
+  const void* x;
+  const float* w;
+  const float* bias;
+  void* y;
+  int C;
+};
+struct ConvArgs {
+  int B, T, N;
+  int dtype;   // 0 fp32, 1 bf16
+  int width;   // taps, 0..4 (0: SiLU alone)
+  int count;   // tensors in t[]
+  const int32_t* cu;  // device cu_seqlens or nullptr
+  ConvTensor t[3];
+};
+
 // Stages of one forward, in launch order (timing hooks of kda_fwd_profiled).
 enum Stage { kStageTable = 0, kStagePrologue = 1, kStageChunk = 2, kStageState = 3, kNumStages = 4 };
 
@@ -88,6 +106,7 @@ inline void mark(const FwdArgs& a, int stage, int end, hipStream_t s) {
 hipError_t launch_chunk_table(const FwdArgs& a, hipStream_t s);
 hipError_t launch_valu_path(const FwdArgs& a, hipStream_t s);
 hipError_t launch_mfma_path(const FwdArgs& a, hipStream_t s);
+hipError_t launch_short_conv(const ConvArgs& a, hipStream_t s);
 size_t mfma_record_bytes(int K, int V);
 hipError_t launch_apply_summary(int B, int H, int K, int V, const float* E, const float* P,
                                 const float* S0, float* F, hipStream_t s);

@@ -32,7 +32,9 @@ STAGE_NAMES = ("chunk_table", "prologue", "chunk_factors", "state_pass")
 EXPORTED = ("kda_validate", "kda_fwd_workspace_size", "kda_fwd", "kda_fwd_profiled",
             "kda_state_summary_workspace_size", "kda_state_summary",
             "kda_apply_state_summary", "kda_chunk_capacity", "kda_chunk_table",
+            "kda_short_conv_silu", "kda_fwd_short_conv_workspace_size", "kda_fwd_short_conv",
             "kda_last_error", "kda_version")
+MAX_CONV_WIDTH = 4
 
 
 class KdaProblem(ctypes.Structure):
@@ -42,6 +44,13 @@ class KdaProblem(ctypes.Structure):
                 ("chunk_size", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("cu_seqlens", ctypes.c_void_p), ("cu_seqlens_host", ctypes.c_void_p),
                 ("lower_bound_form", ctypes.c_int32), ("HV", ctypes.c_int32)]
+
+class KdaShortConv(ctypes.Structure):
+    _fields_ = [("width", ctypes.c_int32),
+                ("q_weight", ctypes.c_void_p), ("k_weight", ctypes.c_void_p),
+                ("v_weight", ctypes.c_void_p), ("q_bias", ctypes.c_void_p),
+                ("k_bias", ctypes.c_void_p), ("v_bias", ctypes.c_void_p)]
+
 
 # form of the lower-bounded gate (kda_lower_bound_form)
 LOWER_BOUND_FORMS = {"sigmoid": 0, "clamp": 1}
@@ -81,6 +90,12 @@ def load_library(path: Optional[str] = None):
     lib.kda_chunk_capacity.restype = I32
     lib.kda_chunk_table.argtypes = [PP, P, P, P, P, I32, P]
     lib.kda_chunk_table.restype = ctypes.c_int
+    lib.kda_short_conv_silu.argtypes = [PP, I32, I32, P, P, P, P, P]
+    lib.kda_short_conv_silu.restype = ctypes.c_int
+    lib.kda_fwd_short_conv_workspace_size.argtypes = [PP, PI]
+    lib.kda_fwd_short_conv_workspace_size.restype = S
+    lib.kda_fwd_short_conv.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
+    lib.kda_fwd_short_conv.restype = ctypes.c_int
     lib.kda_last_error.argtypes = []
     lib.kda_last_error.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -242,6 +257,111 @@ def kda_fwd(q, k, v, gate, beta, a_log, dt_bias, *, scale=None, lower_bound=None
     optional ctypes array of 2*NUM_STAGES hipEvent_t handles recorded around
     each stage (see kda_fwd_profiled in include/kda.h).
     """
+    return _fwd(q, k, v, gate, beta, a_log, dt_bias, None, scale, lower_bound, chunk_size,
+                cu_seqlens, cu_seqlens_host, initial_state, output_final_state, out, workspace,
+                stage_events, lower_bound_form)
+
+
+def kda_fwd_short_conv(q, k, v, gate, beta, a_log, dt_bias, conv_weights=None, conv_biases=None,
+                       *, scale=None, lower_bound=None, chunk_size=64, cu_seqlens=None,
+                       cu_seqlens_host=None, initial_state=None, output_final_state=False,
+                       out=None, workspace=None, lower_bound_form="sigmoid"):
+    """kda_fwd after the layer's short convolution and SiLU on q, k and v.
+
+    q, k, v are the raw projections.  conv_weights: None (SiLU alone) or
+    (w_q, w_k, w_v), float32 GPU tensors [channels, W] or [channels, 1, W]
+    (channels H*K for q and k, HV*V for v; 1 <= W <= MAX_CONV_WIDTH);
+    conv_biases: None or (b_q, b_k, b_v), each [channels] or None.  The other
+    arguments are those of kda_fwd."""
+    B, T, H, K, V, HV = _check_inputs(q, k, v, gate, beta, a_log, dt_bias)
+    conv = _conv_spec(conv_weights, conv_biases, (H * K, H * K, HV * V))
+    return _fwd(q, k, v, gate, beta, a_log, dt_bias, conv, scale, lower_bound, chunk_size,
+                cu_seqlens, cu_seqlens_host, initial_state, output_final_state, out, workspace,
+                None, lower_bound_form)
+
+
+def _conv_weight(w, C, name):
+    _dev(w, name, dtype=torch.float32)
+    if w.dim() == 3 and w.shape[1] == 1:
+        w = w.reshape(w.shape[0], w.shape[2])
+    if w.dim() != 2 or w.shape[0] != C:
+        raise ValueError("%s must be [%d, W] or [%d, 1, W], got %s" % (name, C, C, tuple(w.shape)))
+    return w
+
+
+def _conv_spec(conv_weights, conv_biases, channels):
+    """A KdaShortConv (plus the tensors it points to, kept alive with it)."""
+    spec = KdaShortConv()
+    keep = []
+    if conv_weights is None:
+        if conv_biases is not None:
+            raise ValueError("conv_biases given without conv_weights")
+        spec.width = 0
+        return spec, keep
+    if len(conv_weights) != 3:
+        raise ValueError("conv_weights must be (w_q, w_k, w_v)")
+    ws = [_conv_weight(w, C, n) for w, C, n in zip(conv_weights, channels, ("w_q", "w_k", "w_v"))]
+    widths = {w.shape[1] for w in ws}
+    if len(widths) != 1:
+        raise ValueError("q, k and v convolutions must have one width, got %s" % sorted(widths))
+    spec.width = widths.pop()
+    spec.q_weight, spec.k_weight, spec.v_weight = (w.data_ptr() for w in ws)
+    keep += ws
+    if conv_biases is not None:
+        if len(conv_biases) != 3:
+            raise ValueError("conv_biases must be (b_q, b_k, b_v)")
+        ptrs = []
+        for b, C, n in zip(conv_biases, channels, ("b_q", "b_k", "b_v")):
+            if b is None:
+                ptrs.append(None)
+                continue
+            _dev(b, n, dtype=torch.float32, shape=(C,))
+            keep.append(b)
+            ptrs.append(b.data_ptr())
+        spec.q_bias, spec.k_bias, spec.v_bias = ptrs
+    return spec, keep
+
+
+def short_conv_silu(x, weight=None, bias=None, *, cu_seqlens=None, cu_seqlens_host=None, out=None):
+    """SiLU of the causal depthwise convolution of x over time (one tensor).
+
+    x [B,T,C] or [B,T,H,D] (channel h*D + d), float32 or bfloat16 on the GPU;
+    weight float32 [C, W] or [C, 1, W] (None: SiLU alone); bias float32 [C] or
+    None.  With cu_seqlens (B == 1) every document is padded on its own."""
+    if not isinstance(x, torch.Tensor) or x.dim() < 3:
+        raise ValueError("x must be a [B, T, ...] tensor")
+    _dev(x, "x")
+    B, T = x.shape[0], x.shape[1]
+    C = 1
+    for d in x.shape[2:]:
+        C *= d
+    width = 0
+    if weight is not None:
+        weight = _conv_weight(weight, C, "weight")
+        width = weight.shape[1]
+    elif bias is not None:
+        raise ValueError("bias given without weight")
+    if bias is not None:
+        _dev(bias, "bias", dtype=torch.float32, shape=(C,))
+    cu, host, N, host_ptr = _cu_args(cu_seqlens, cu_seqlens_host, T)
+    if N is None:
+        N = B
+    p = make_problem(B, T, 0, 0, 0, _dtype_code(x), N=N,
+                     cu_seqlens_ptr=None if cu is None else cu.data_ptr(),
+                     cu_seqlens_host_ptr=host_ptr)
+    y = torch.empty_like(x) if out is None else out
+    _dev(y, "out", dtype=x.dtype, shape=tuple(x.shape))
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = load_library().kda_short_conv_silu(ctypes.byref(p), C, width, ptr(x), ptr(weight),
+                                            ptr(bias), ptr(y), _stream_ptr(x.device))
+    if st:
+        _raise(st, "kda_short_conv_silu")
+    return y
+
+
+def _fwd(q, k, v, gate, beta, a_log, dt_bias, conv, scale, lower_bound, chunk_size, cu_seqlens,
+         cu_seqlens_host, initial_state, output_final_state, out, workspace, stage_events,
+         lower_bound_form):
     B, T, H, K, V, HV = _check_inputs(q, k, v, gate, beta, a_log, dt_bias)
     lib = load_library()
     device = q.device
@@ -255,7 +375,8 @@ def kda_fwd(q, k, v, gate, beta, a_log, dt_bias, *, scale=None, lower_bound=None
     p = make_problem(B, T, H, K, V, _dtype_code(q), scale, lower_bound, chunk_size, N,
                      None if cu is None else cu.data_ptr(), host_ptr, lower_bound_form, HV)
     st = ctypes.c_int(0)
-    need = lib.kda_fwd_workspace_size(ctypes.byref(p), ctypes.byref(st))
+    size_fn = lib.kda_fwd_workspace_size if conv is None else lib.kda_fwd_short_conv_workspace_size
+    need = size_fn(ctypes.byref(p), ctypes.byref(st))
     if st.value:
         _raise(st.value, "kda_fwd")
     o = out if out is not None else torch.empty((B, T, HV, V), dtype=q.dtype, device=device)
@@ -267,11 +388,18 @@ def kda_fwd(q, k, v, gate, beta, a_log, dt_bias, *, scale=None, lower_bound=None
         _dev(workspace, "workspace", dtype=torch.uint8)
         ws, nbytes = workspace, workspace.numel()
     ptr = lambda t: None if t is None else t.data_ptr()
-    st = lib.kda_fwd_profiled(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ptr(gate), ptr(beta),
-                              ptr(a_log), ptr(dt_bias), ptr(initial_state), ptr(o), ptr(fin),
-                              ptr(ws), nbytes, _stream_ptr(device), stage_events)
+    if conv is None:
+        st = lib.kda_fwd_profiled(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ptr(gate), ptr(beta),
+                                  ptr(a_log), ptr(dt_bias), ptr(initial_state), ptr(o), ptr(fin),
+                                  ptr(ws), nbytes, _stream_ptr(device), stage_events)
+    else:
+        spec, _keep = conv
+        st = lib.kda_fwd_short_conv(ctypes.byref(p), ctypes.byref(spec), ptr(q), ptr(k), ptr(v),
+                                    ptr(gate), ptr(beta), ptr(a_log), ptr(dt_bias),
+                                    ptr(initial_state), ptr(o), ptr(fin), ptr(ws), nbytes,
+                                    _stream_ptr(device))
     if st:
-        _raise(st, "kda_fwd")
+        _raise(st, "kda_fwd_short_conv" if conv is not None else "kda_fwd")
     return o, fin
 
 

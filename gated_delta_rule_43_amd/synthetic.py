@@ -169,3 +169,24 @@ def random_problem(seed, B, T, H, K, V, dtype=torch.float32, device="cpu", gate_
     return dict(q=q.to(dtype), k=k.to(dtype), v=v.to(dtype), gate=gate.to(dtype),
                 beta=beta.to(dtype), a_log=a_log, dt_bias=dt_bias, initial_state=init,
                 cu_seqlens=cu)
+
+
+def short_conv_params(seed, channels, width, bias=True, device="cpu"):
+    """Seeded weights of the three short convolutions (q, k, v).
+
+    ``channels`` = (C_q, C_k, C_v).  The draw follows the default
+    initialisation of a depthwise torch Conv1d (fan-in = width): weights and
+    biases uniform in [-1/sqrt(width), 1/sqrt(width)], float32, drawn in the
+    order w_q, w_k, w_v, b_q, b_k, b_v from ``torch.Generator(device)``.
+    Returns (weights [C, width] each, biases [C] each or None)."""
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    bound = 1.0 / float(np.sqrt(width))
+
+    def uni(n, shape):
+        return (torch.rand(shape, generator=gen, device=dev) * 2.0 - 1.0) * bound
+
+    ws = tuple(uni(C, (C, width)) for C in channels)
+    bs = tuple(uni(C, (C,)) for C in channels) if bias else None
+    return ws, bs

@@ -211,6 +211,72 @@ int32_t kda_chunk_capacity(const kda_problem* p, kda_status* status);
 kda_status kda_chunk_table(const kda_problem* p, int32_t* tok, int32_t* len, int32_t* seq_chunk0,
                            int32_t* count, int32_t cap, void* stream);
 
+/*
+ * The layer's short convolution before the forward: SiLU of a causal
+ * depthwise convolution over time, applied per channel to q, k and v
+ * (hyper_parallel coverage page: `_run_causal_short_conv`,
+ * `_local_short_conv` and the channel constraints of
+ * `_validate_layer_short_conv` -- depthwise, stride 1, dilation 1, zero
+ * padding of width-1 tokens on the left, output cut to the sequence length,
+ * SiLU activation; without the convolution the layer applies SiLU alone, as
+ * in the forward of KimiDeltaAttentionUlyssesCP).  For channel c of a tensor
+ * x [B,T,C] (C = H*K for q and k, HV*V for v; channel h*D + d of head h):
+ *
+ *     y[t,c] = silu(bias[c] + sum_{j<W} weight[c,j] * x[t-(W-1)+j, c]),
+ *     silu(z) = z * sigmoid(z)
+ *
+ * where x of a token before the first token of t's sequence counts as zero:
+ * every row is padded on its own, and with cu_seqlens every document of the
+ * packed row is (the NeMo AutoModel page "nemo_automodel.components.models.
+ * kimi_k3.cp" hands the conv kernel size to the per-row context that carries
+ * the document layout, `build_fla_cp_context`).
+ *
+ *  width      W, taps per channel: 0 = no convolution (y = silu(x), weights
+ *             and biases ignored), 1..4.  Larger widths are KDA_EUNSUPPORTED,
+ *             negative ones KDA_EINVAL.
+ *  *_weight   fp32 [C, W] (the depthwise Conv1d weight [C, 1, W]); tap W-1
+ *             weights the current token.  Required when width > 0.
+ *  *_bias     fp32 [C], or NULL for no bias.
+ * Device pointers, 4-byte aligned.
+ */
+typedef struct kda_short_conv {
+  int32_t width;
+  const float* q_weight;
+  const float* k_weight;
+  const float* v_weight;
+  const float* q_bias;
+  const float* k_bias;
+  const float* v_bias;
+} kda_short_conv;
+
+/*
+ * One tensor through the short convolution: y = SiLU(conv(x)) as above.
+ * x, y [B,T,channels] with p->dtype elements, 16-byte aligned, channels a
+ * multiple of 8 (bf16) or 4 (fp32); y may not overlap x.  Only B, T, dtype
+ * and the document layout (N, cu_seqlens, cu_seqlens_host, validated as for
+ * kda_fwd) are read from p.  Computes in fp32, rounds once to p->dtype.
+ */
+kda_status kda_short_conv_silu(const kda_problem* p, int32_t channels, int32_t width,
+                               const void* x, const float* weight, const float* bias, void* y,
+                               void* stream);
+
+/* Workspace bytes for kda_fwd_short_conv: kda_fwd's plus the convolved q, k, v. */
+size_t kda_fwd_short_conv_workspace_size(const kda_problem* p, kda_status* status);
+
+/*
+ * kda_fwd after the short convolution and SiLU of `conv` on q, k and v (the
+ * layer order of the pages: projections, ShortConv + SiLU, then chunk_kda).
+ * q, k, v are the raw projections; the convolved tensors live in the
+ * workspace (p->dtype, rounded once), and the forward then runs on them
+ * exactly as kda_fwd.  All other arguments are those of kda_fwd; q, k and v
+ * must be 16-byte aligned.
+ */
+kda_status kda_fwd_short_conv(const kda_problem* p, const kda_short_conv* conv, const void* q,
+                              const void* k, const void* v, const void* gate, const void* beta,
+                              const float* a_log, const float* dt_bias,
+                              const float* initial_state, void* o, float* final_state,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* kda_last_error(void);
 

@@ -207,3 +207,88 @@ def test_python_binding_rejects_host_tensors():
         kda.kda_fwd(q, q, torch.zeros(B, T, 4, K, dtype=torch.bfloat16),
                     torch.zeros(B, T, 4, K, dtype=torch.bfloat16),
                     torch.zeros(B, T, 4, dtype=torch.bfloat16), torch.zeros(4), torch.zeros(4, K))
+
+
+def _conv(width=4, weights=True):
+    c = kda.KdaShortConv()
+    c.width = width
+    if weights:
+        c.q_weight = c.k_weight = c.v_weight = FAKE
+    return c
+
+
+def test_short_conv_workspace_adds_the_convolved_inputs(lib):
+    st = ctypes.c_int(0)
+    for dtype, elt in ((kda.KDA_BF16, 2), (kda.KDA_F32, 4)):
+        p = _p(B=2, T=100, H=2, K=64, V=128, dtype=dtype, HV=4)
+        base = lib.kda_fwd_workspace_size(ctypes.byref(p), ctypes.byref(st))
+        conv = lib.kda_fwd_short_conv_workspace_size(ctypes.byref(p), ctypes.byref(st))
+        assert st.value == kda.OK
+        tokens = 2 * 100
+        need = tokens * 2 * 64 * elt * 2 + tokens * 4 * 128 * elt
+        assert need <= conv - base <= need + 3 * 256
+
+
+def test_fwd_short_conv_rejects_before_launch(lib):
+    p = _p()
+    args = [FAKE] * 5 + [FAKE, FAKE, None, FAKE, None]
+    big = 1 << 40
+    st = lib.kda_fwd_short_conv(ctypes.byref(p), None, *args, FAKE, big, None)
+    assert st == kda.EINVAL and "NULL" in lib.kda_last_error().decode()
+    st = lib.kda_fwd_short_conv(ctypes.byref(p), ctypes.byref(_conv(width=5)), *args, FAKE, big, None)
+    assert st == kda.EUNSUPPORTED and "width" in lib.kda_last_error().decode()
+    st = lib.kda_fwd_short_conv(ctypes.byref(p), ctypes.byref(_conv(width=-1)), *args, FAKE, big, None)
+    assert st == kda.EINVAL
+    st = lib.kda_fwd_short_conv(ctypes.byref(p), ctypes.byref(_conv(weights=False)), *args, FAKE, big,
+                                None)
+    assert st == kda.EINVAL and "weights" in lib.kda_last_error().decode()
+    c = _conv()
+    c.k_bias = FAKE + 2
+    st = lib.kda_fwd_short_conv(ctypes.byref(p), ctypes.byref(c), *args, FAKE, big, None)
+    assert st == kda.EINVAL and "aligned" in lib.kda_last_error().decode()
+    # the convolution reads q, k and v 16 bytes at a time, also for fp32
+    pf = _p(dtype=kda.KDA_F32)
+    bad = list(args)
+    bad[2] = FAKE + 4
+    st = lib.kda_fwd_short_conv(ctypes.byref(pf), ctypes.byref(_conv()), *bad, FAKE, big, None)
+    assert st == kda.EINVAL and "16-byte" in lib.kda_last_error().decode()
+    # the workspace must hold the convolved inputs too
+    st = ctypes.c_int(0)
+    base = lib.kda_fwd_workspace_size(ctypes.byref(p), ctypes.byref(st))
+    st = lib.kda_fwd_short_conv(ctypes.byref(p), ctypes.byref(_conv()), *args, FAKE, base, None)
+    assert st == kda.EWORKSPACE
+
+
+def test_short_conv_silu_rejects_before_launch(lib):
+    p = _p(B=1, T=50)
+    st = lib.kda_short_conv_silu(ctypes.byref(p), 12, 4, FAKE, FAKE, None, FAKE + 4096, None)
+    assert st == kda.EINVAL and "multiple of 8" in lib.kda_last_error().decode()
+    st = lib.kda_short_conv_silu(ctypes.byref(p), 64, 4, FAKE, None, None, FAKE + (1 << 20), None)
+    assert st == kda.EINVAL and "weight" in lib.kda_last_error().decode()
+    st = lib.kda_short_conv_silu(ctypes.byref(p), 64, 7, FAKE, FAKE, None, FAKE + (1 << 20), None)
+    assert st == kda.EUNSUPPORTED
+    # y overlapping x
+    st = lib.kda_short_conv_silu(ctypes.byref(p), 64, 4, FAKE, FAKE, None, FAKE + 64, None)
+    assert st == kda.EINVAL and "overlap" in lib.kda_last_error().decode()
+    st = lib.kda_short_conv_silu(ctypes.byref(p), 64, 4, FAKE + 8, FAKE, None, FAKE + (1 << 20), None)
+    assert st == kda.EINVAL and "16-byte" in lib.kda_last_error().decode()
+    # only the rows and the document layout of the problem are read: head
+    # shapes the forward would refuse do not matter here (the call gets past
+    # them to the alignment check, so nothing is launched)
+    q = _p(B=1, T=50, K=96)
+    st = lib.kda_short_conv_silu(ctypes.byref(q), 64, 4, FAKE, FAKE, None, FAKE + (1 << 20) + 8, None)
+    assert st == kda.EINVAL and "16-byte" in lib.kda_last_error().decode()
+    cu = (ctypes.c_int32 * 3)(0, 30, 40)  # does not end at T = 50
+    r = _p(B=1, T=50, N=2, cu_seqlens_ptr=FAKE, cu_seqlens_host_ptr=ctypes.addressof(cu))
+    st = lib.kda_short_conv_silu(ctypes.byref(r), 64, 4, FAKE, FAKE, None, FAKE + (1 << 20), None)
+    assert st == kda.EINVAL and "cu_seqlens" in lib.kda_last_error().decode()
+
+
+def test_python_short_conv_binding_checks_shapes():
+    B, T, H, K = 1, 8, 2, 64
+    x = torch.zeros(B, T, H, K, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.short_conv_silu(x)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.kda_fwd_short_conv(x, x, x, x, torch.zeros(B, T, H, dtype=torch.bfloat16),
+                               torch.zeros(H), torch.zeros(H, K))
