@@ -10,6 +10,8 @@ resident in HBM.  W untimed steps, then exactly K timed steps between two
 device synchronisations; rank 0 prints one JSON line.
 
 Besides the throughput it reports
+  * "short_conv": the same step after the layer's short convolution + SiLU of
+    q, k, v (kda_fwd_short_conv), and that convolution kernel's own HBM rate;
   * "roofline": the dominant kernel's algorithmic bytes per launch divided by
     its average duration, timed live with HIP events recorded by the library
     around each stage on the kernel's own stream (kda_fwd_profiled);
@@ -125,6 +127,14 @@ def measured_mfma_util(workload):
     return None if not k else {n: v["mfma_util_pct"] for n, v in k.items()}
 
 
+def measured_conv_traffic():
+    """HBM bytes per launch of the short-convolution kernel on q alone, from the
+    committed FETCH_SIZE / WRITE_SIZE summary, or None when stale/absent."""
+    info = _current_profile("short_conv_throughput_bf16_B4_T16384_H32_d128.json")
+    k = None if info is None else info.get("q_only")
+    return None if k is None else int(k["traffic_bytes"])
+
+
 def record_bytes(K, V):
     """Bytes of one chunk record of the MFMA path (per chunk-head): Qt, W and
     Kbar^T fragments (C*K bf16 each), Aqk fragments (C*C bf16), gL (K fp32) and
@@ -195,6 +205,63 @@ def cpu_baseline(inp, w, budget_s=12.0):
                       % (npairs, T, passes, token_heads, secs, w.H)}
 
 
+def bench_short_conv(inp, w, o, steps, warmup, width=4):
+    """The forward after the layer's short convolution + SiLU (kda_fwd_short_conv,
+    width-4 convolutions with bias on q, k, v) on the same resident inputs, and
+    the convolution kernel alone (kda_short_conv_silu on q), timed with events
+    on the stream both are launched on."""
+    dev = inp["q"].device
+    chans = (w.H * w.K, w.H * w.K, w.H * w.V)
+    ws_, bs_ = synthetic.short_conv_params(123, chans, width, True, device=dev)
+    cu = inp["cu_seqlens"]
+    cu_host = None if cu is None else cu.cpu()
+
+    def fwd():
+        kda.kda_fwd_short_conv(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"],
+                               inp["a_log"], inp["dt_bias"], ws_, bs_, scale=w.scale,
+                               lower_bound=w.lower_bound, chunk_size=w.chunk_size,
+                               cu_seqlens=cu, cu_seqlens_host=cu_host,
+                               initial_state=inp["initial_state"],
+                               output_final_state=w.output_final_state, out=o)
+
+    for _ in range(warmup):
+        fwd()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fwd()
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    # the convolution kernel alone, on q (events on the current stream, which
+    # is the stream the binding launches on)
+    y = torch.empty_like(inp["q"])
+    for _ in range(2):
+        kda.short_conv_silu(inp["q"], ws_[0], bs_[0], cu_seqlens=cu, cu_seqlens_host=cu_host, out=y)
+    stream = torch.cuda.current_stream(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        kda.short_conv_silu(inp["q"], ws_[0], bs_[0], cu_seqlens=cu, cu_seqlens_host=cu_host, out=y)
+        b.record(stream)
+    torch.cuda.synchronize()
+    conv_ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    elt = 2 if w.dtype == "bf16" else 4
+    conv_bytes = 2 * w.B * w.T * chans[0] * elt      # x read once, y written once
+    achieved = conv_bytes / (conv_ms / 1e3) / 1e9
+    tokens = w.B * w.T
+    return {"workload": w.name + " after a width-%d short convolution + SiLU (with bias) on q, k, v"
+                        % width,
+            "value": round(tokens / (ms / 1e3) / 1e6, 4), "unit": "Mtokens/s",
+            "ms_per_step": round(ms, 4),
+            "conv_kernel": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                            "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
+                            "kernel_ms": round(conv_ms, 4), "bytes_per_launch": conv_bytes,
+                            "traffic": measured_conv_traffic() if w.name.startswith("throughput")
+                            else None,
+                            "tensor": "q [B,T,H*K]"}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -202,6 +269,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-short-conv", action="store_true",
+                    help="skip the forward-after-short-convolution measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (to scale the "
                          "FETCH_SIZE/WRITE_SIZE counters) and exit")
@@ -295,6 +364,9 @@ def main():
         "mfma_util_pct_counters": measured_mfma_util(args.workload),
         "roofline": roofline,
     }
+    if not args.no_short_conv:
+        print("[bench] timing the forward after the short convolution", file=sys.stderr, flush=True)
+        out["short_conv"] = bench_short_conv(inp, w, o, args.steps, args.warmup)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, w)
