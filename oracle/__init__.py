@@ -6,9 +6,9 @@ HIP library and its Python binding) never imports this package, and this
 package imports nothing from the product.
 
 The arithmetic lives in ``kda_oracle.c`` (compiled with gcc, loaded through
-ctypes).  q, k and v are taken as float64 arrays (bf16 and fp32 values upcast
-exactly; the short convolution's fp64 output passes through unrounded), the
-gate inputs as float32 arrays; outputs are float64.  See ``kda_oracle.c`` for the definition and the
+ctypes).  Every input is taken as a float64 array (bf16 and fp32 values upcast
+exactly; the short convolution's fp64 output passes through unrounded, and
+finite differences can perturb any input); outputs are float64.  See ``kda_oracle.c`` for the definition and the
 passages of the pages each part follows.  ``chunked.py`` holds a second,
 chunk-parallel fp64 form used only to cross-check the chunk algebra.
 
@@ -18,7 +18,10 @@ alternative gate reading (``gate_mode="clamp"``) is pinned by closed forms of
 its own gate values only.  ``short_conv_silu`` (the layer's causal depthwise
 convolution and SiLU before the forward) is pinned by
 ``tests/test_oracle_short_conv.py`` against the library conv1d called the way
-the pages call it, closed-form taps and SiLU special values.
+the pages call it, closed-form taps and SiLU special values.  ``kda_bwd`` (the
+reverse mode of the token recurrence) is pinned by
+``tests/test_oracle_bwd.py`` against central finite differences of the forward,
+entry by entry, for every input, plus closed forms.
 """
 from __future__ import annotations
 
@@ -64,9 +67,11 @@ def _load():
         lib.oracle_state_summary.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, I, D, P, P, I]
         lib.oracle_apply_state_summary.argtypes = [I, I, I, I, P, P, P, P]
         lib.oracle_short_conv_silu.argtypes = [I, I, I, I, P, P, P, I, P, P]
+        lib.oracle_kda_bwd.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, D, I, D, I, P, P, P, P,
+                                       P, P, P, P, P, P, P, P, I]
         for f in (lib.oracle_prologue, lib.oracle_kda_fwd, lib.oracle_recurrence,
                   lib.oracle_state_summary, lib.oracle_apply_state_summary,
-                  lib.oracle_short_conv_silu):
+                  lib.oracle_short_conv_silu, lib.oracle_kda_bwd):
             f.restype = I
         _lib = lib
     return _lib
@@ -102,8 +107,7 @@ def default_threads() -> int:
 
 def prologue(q, k, gate, beta, a_log, dt_bias, lower_bound=None, gate_mode=None):
     """q^, k^ (L2-normalised), log-decay g and beta = sigmoid(logit), all fp64."""
-    q, k = _f64(q), _f64(k)
-    gate, beta, a_log, dt_bias = map(_f32, (gate, beta, a_log, dt_bias))
+    q, k, gate, beta, a_log, dt_bias = map(_f64, (q, k, gate, beta, a_log, dt_bias))
     B, T, H, K = q.shape
     mode, lb = _gate(lower_bound, gate_mode)
     qn = np.empty(q.shape, np.float64)
@@ -133,8 +137,7 @@ def kda_fwd(q, k, v, gate, beta, a_log, dt_bias, scale=None, lower_bound=None,
     H is the number of value heads (v, gate, beta, a_log, dt_bias, o, states);
     q and k may have fewer key heads HK dividing H, value head h then reading
     key head h // (H // HK) (grouped value heads)."""
-    q, k, v = map(_f64, (q, k, v))
-    gate, beta, a_log, dt_bias = map(_f32, (gate, beta, a_log, dt_bias))
+    q, k, v, gate, beta, a_log, dt_bias = map(_f64, (q, k, v, gate, beta, a_log, dt_bias))
     B, T, HK, K = q.shape
     H, V = v.shape[2], v.shape[-1]
     if H % HK:
@@ -143,7 +146,7 @@ def kda_fwd(q, k, v, gate, beta, a_log, dt_bias, scale=None, lower_bound=None,
         scale = 1.0 / math.sqrt(K)
     mode, lb = _gate(lower_bound, gate_mode)
     cu, N = _cu(cu_seqlens, B, T)
-    init = None if initial_state is None else _f32(initial_state)
+    init = None if initial_state is None else _f64(initial_state)
     o = np.zeros((B, T, H, V), np.float64) if want_output else None
     fin = np.zeros((N, H, K, V), np.float64) if output_final_state else None
     rc = _load().oracle_kda_fwd(B, T, H, HK, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
@@ -160,7 +163,7 @@ def recurrence(qn, kn, v, g, b, scale, cu_seqlens=None, initial_state=None, thre
     B, T, H, K = qn.shape
     V = v.shape[-1]
     cu, N = _cu(cu_seqlens, B, T)
-    init = None if initial_state is None else _f32(initial_state)
+    init = None if initial_state is None else _f64(initial_state)
     o = np.zeros((B, T, H, V), np.float64)
     fin = np.zeros((N, H, K, V), np.float64)
     rc = _load().oracle_recurrence(B, T, H, K, V, _ptr(qn), _ptr(kn), _ptr(v), _ptr(g), _ptr(b),
@@ -175,8 +178,7 @@ def state_summary(q, k, v, gate, beta, a_log, dt_bias, lower_bound=None, gate_mo
                   threads=None):
     """Affine summary of each row: (state_ext [B,H,K,V], transition [B,H,K,K]), fp64.
     Heads as in kda_fwd (q, k may carry fewer key heads)."""
-    q, k, v = map(_f64, (q, k, v))
-    gate, beta, a_log, dt_bias = map(_f32, (gate, beta, a_log, dt_bias))
+    q, k, v, gate, beta, a_log, dt_bias = map(_f64, (q, k, v, gate, beta, a_log, dt_bias))
     B, T, HK, K = q.shape
     H, V = v.shape[2], v.shape[-1]
     if H % HK:
@@ -241,3 +243,35 @@ def kda_fwd_short_conv(q, k, v, gate, beta, a_log, dt_bias, conv_weights=None, c
     k2 = short_conv_silu(k, wk, bk, cu_seqlens)
     v2 = short_conv_silu(v, wv, bv, cu_seqlens)
     return kda_fwd(q2, k2, v2, gate, beta, a_log, dt_bias, cu_seqlens=cu_seqlens, **kwargs)
+
+
+def kda_bwd(q, k, v, gate, beta, a_log, dt_bias, d_o, d_final=None, scale=None, lower_bound=None,
+            cu_seqlens=None, initial_state=None, gate_mode=None, threads=None):
+    """Gradients of L = sum(d_o * o) + sum(d_final * final_state) for kda_fwd's
+    inputs (reverse mode of the token recurrence, fp64).  Returns a dict with
+    dq, dk ([B,T,HK,K], summed over the value heads that share a key head), dv,
+    dgate, dbeta (of the logit), da_log, ddt_bias and dinit (the initial state's
+    gradient, [N,H,K,V]; returned also when no initial state is given)."""
+    q, k, v, gate, beta, a_log, dt_bias, d_o = map(_f64, (q, k, v, gate, beta, a_log, dt_bias, d_o))
+    B, T, HK, K = q.shape
+    H, V = v.shape[2], v.shape[-1]
+    if H % HK:
+        raise ValueError("value heads %d must be a multiple of key heads %d" % (H, HK))
+    if scale is None:
+        scale = 1.0 / math.sqrt(K)
+    mode, lb = _gate(lower_bound, gate_mode)
+    cu, N = _cu(cu_seqlens, B, T)
+    init = None if initial_state is None else _f64(initial_state)
+    dfin = None if d_final is None else _f64(d_final)
+    out = dict(dq=np.zeros(q.shape), dk=np.zeros(q.shape), dv=np.zeros(v.shape),
+               dgate=np.zeros(gate.shape), dbeta=np.zeros(beta.shape), da_log=np.zeros(H),
+               ddt_bias=np.zeros((H, K)), dinit=np.zeros((N, H, K, V)))
+    rc = _load().oracle_kda_bwd(B, T, H, HK, K, V, _ptr(q), _ptr(k), _ptr(v), _ptr(gate), _ptr(beta),
+                                _ptr(a_log), _ptr(dt_bias), float(scale), mode, lb, N, _ptr(cu),
+                                _ptr(init), _ptr(d_o), _ptr(dfin), _ptr(out["dq"]), _ptr(out["dk"]),
+                                _ptr(out["dv"]), _ptr(out["dgate"]), _ptr(out["dbeta"]),
+                                _ptr(out["da_log"]), _ptr(out["ddt_bias"]), _ptr(out["dinit"]),
+                                threads or default_threads())
+    if rc:
+        raise ValueError("oracle_kda_bwd rejected its arguments (%d)" % rc)
+    return out

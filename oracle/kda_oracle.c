@@ -65,7 +65,7 @@ static void l2norm(const double* x, int n, double* out) {
 }
 
 /* Per-key-channel log-decay built from the raw gate logits (in-kernel gate). */
-static void gate_row(const float* gate, const float* dt_bias_h, double a_log_h, int K, int mode,
+static void gate_row(const double* gate, const double* dt_bias_h, double a_log_h, int K, int mode,
                      double lb, double* g) {
   double A = exp(a_log_h);
   for (int c = 0; c < K; ++c) {
@@ -83,8 +83,8 @@ static void gate_row(const float* gate, const float* dt_bias_h, double a_log_h, 
 /* ------------------------------------------------------------------------ */
 /* Public: prologue only (q^, k^, g, beta) for every token and head.         */
 /* ------------------------------------------------------------------------ */
-int oracle_prologue(int B, int T, int H, int K, const double* q, const double* k, const float* gate,
-                    const float* beta, const float* a_log, const float* dt_bias, int gate_mode,
+int oracle_prologue(int B, int T, int H, int K, const double* q, const double* k, const double* gate,
+                    const double* beta, const double* a_log, const double* dt_bias, int gate_mode,
                     double lower_bound, double* qn, double* kn, double* g, double* b) {
   if (B < 0 || T < 0 || H <= 0 || K <= 0) return 1;
   for (long bt = 0; bt < (long)B * T; ++bt) {
@@ -139,14 +139,14 @@ typedef struct {
   int B, T, H, K, V;
   int HK; /* key heads of q and k (raw entries); value head h reads key head h / (H / HK) */
   const double *q, *k, *v;
-  const float *gate, *beta, *a_log, *dt_bias;
+  const double *gate, *beta, *a_log, *dt_bias;
   /* pre-normalised inputs (recurrence-only entry); NULL when raw is used */
   const double *qn, *kn, *g, *bb;
   int gate_mode;
   double lb, scale;
   int N;
   const int32_t* cu;
-  const float* init;
+  const double* init;
   double* o;
   double* fin;
   double* trans; /* summary mode: transition [N,H,K,K] */
@@ -270,9 +270,9 @@ static int check_cu(int B, int T, int N, const int32_t* cu) {
 /*   [N,H,K,V] (may be NULL).                                                */
 /* ------------------------------------------------------------------------ */
 int oracle_kda_fwd(int B, int T, int H, int HK, int K, int V, const double* q, const double* k,
-                   const double* v, const float* gate, const float* beta, const float* a_log,
-                   const float* dt_bias, double scale, int gate_mode, double lower_bound, int N,
-                   const int32_t* cu_seqlens, const float* initial_state, double* o,
+                   const double* v, const double* gate, const double* beta, const double* a_log,
+                   const double* dt_bias, double scale, int gate_mode, double lower_bound, int N,
+                   const int32_t* cu_seqlens, const double* initial_state, double* o,
                    double* final_state, int threads) {
   if (B < 0 || T < 0 || H <= 0 || HK <= 0 || H % HK || K <= 0 || V <= 0) return 1;
   if (check_cu(B, T, N, cu_seqlens)) return 2;
@@ -291,7 +291,7 @@ int oracle_kda_fwd(int B, int T, int H, int HK, int K, int V, const double* q, c
 /* ------------------------------------------------------------------------ */
 int oracle_recurrence(int B, int T, int H, int K, int V, const double* qn, const double* kn,
                       const double* v, const double* g, const double* b, double scale, int N,
-                      const int32_t* cu_seqlens, const float* initial_state, double* o,
+                      const int32_t* cu_seqlens, const double* initial_state, double* o,
                       double* final_state, int threads) {
   if (B < 0 || T < 0 || H <= 0 || K <= 0 || V <= 0) return 1;
   if (check_cu(B, T, N, cu_seqlens)) return 2;
@@ -311,8 +311,8 @@ int oracle_recurrence(int B, int T, int H, int K, int V, const double* qn, const
 /* so that final_state = transition . initial_state + state_ext.            */
 /* ------------------------------------------------------------------------ */
 int oracle_state_summary(int B, int T, int H, int HK, int K, int V, const double* q,
-                         const double* k, const double* v, const float* gate, const float* beta,
-                         const float* a_log, const float* dt_bias, int gate_mode,
+                         const double* k, const double* v, const double* gate, const double* beta,
+                         const double* a_log, const double* dt_bias, int gate_mode,
                          double lower_bound, double* state_ext, double* transition, int threads) {
   if (B < 0 || T < 0 || H <= 0 || HK <= 0 || H % HK || K <= 0 || V <= 0) return 1;
   job_t J;
@@ -365,6 +365,270 @@ int oracle_short_conv_silu(int B, int T, int C, int W, const double* x, const do
       }
   }
   return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Public: gradients of the forward (reverse mode, token by token).         */
+/*   The forward is the definition above; the loss is                       */
+/*     L = sum(d_o * o) + sum(d_final * final_state)                         */
+/*   and every input's gradient is dL/d(input), through the in-kernel L2     */
+/*   norm, gate and beta sigmoid.  Source for what is differentiated: the    */
+/*   pages test chunk_kda forward and backward together (torchtitan PR      */
+/*   #4025 commit note) and route state gradients between slices            */
+/*   (hyper_parallel page, the backward of _RecvKDAInitialState); the        */
+/*   derivative itself is the chain rule applied to the definition.          */
+/* Per (sequence, value head): a forward pass that keeps every state, then   */
+/* a reverse pass.  With S' = Diag(e^g) S_prev, u = S'^T k^, e = v - u,     */
+/* S = S' + beta k^ e^T and o = scale S^T q^, for the incoming dS:           */
+/*   dS += scale q^ do^T;  dq^ = scale S do;  dbeta = k^T dS e;             */
+/*   de = beta dS^T k^ (= dv);  dk^ = beta dS e - S' de;                    */
+/*   dS' = dS - k^ de^T;  dg_c = sum_j dS'_cj S'_cj;  dS_prev = Diag(e^g) dS' */
+/* Outputs: dq, dk [B,T,HK,K] (summed over the value heads of a group); dv   */
+/* [B,T,H,V]; dgate [B,T,H,K]; dbeta [B,T,H] (of the logit); da_log [H],     */
+/* ddt_bias [H,K] (summed over tokens); dinit [N,H,K,V] (may be NULL).       */
+/* d_final may be NULL (zero).                                               */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+  job_t f;               /* forward description (raw inputs) */
+  const double* d_o;
+  const double* d_fin;
+  double *dqh, *dkh;     /* [B,T,H,K] per value head, reduced over groups after */
+  double *dv, *dgate, *dbeta;
+  double *da_part, *ddt_part; /* [N,H], [N,H,K] */
+  double* dinit;
+  int oom;
+} bwd_job_t;
+
+/* gradient of one L2-normalised row: x^ = x / sqrt(sum x^2 + eps) */
+static void l2norm_bwd(const double* x, const double* dxh, int n, double* dx) {
+  double ss = 0.0, dot = 0.0;
+  for (int i = 0; i < n; ++i) {
+    ss += x[i] * x[i];
+    dot += x[i] * dxh[i];
+  }
+  const double nr = sqrt(ss + ORACLE_EPS);
+  for (int i = 0; i < n; ++i) dx[i] = dxh[i] / nr - x[i] * dot / (nr * nr * nr);
+}
+
+/* dg/dx and dg/da_log of one gate entry (x = gate + dt_bias) */
+static void gate_grad(double x, double a_log_h, int mode, double lb, double* dgdx, double* dgda) {
+  const double A = exp(a_log_h);
+  if (mode == GATE_SIGMOID_BOUND) {
+    const double s = sigmoid(A * x);
+    *dgdx = lb * s * (1.0 - s) * A;
+    *dgda = lb * s * (1.0 - s) * A * x;
+    return;
+  }
+  const double g = -A * softplus(x);
+  if (mode == GATE_CLAMP_BOUND && !(g > lb)) {
+    *dgdx = 0.0;
+    *dgda = 0.0;
+    return;
+  }
+  *dgdx = -A * sigmoid(x);
+  *dgda = g;
+}
+
+static void* bwd_worker(void* arg) {
+  bwd_job_t* BJ = (bwd_job_t*)arg;
+  job_t* J = &BJ->f;
+  const int K = J->K, V = J->V, H = J->H;
+  for (;;) {
+    int w = take(J);
+    if (w >= J->N * H) break;
+    const int n = w / H, h = w % H;
+    long row, t0, t1;
+    seq_range(J, n, &row, &t0, &t1);
+    const long L = t1 - t0;
+    const long KV = (long)K * V;
+    double* S = (double*)malloc(sizeof(double) * (size_t)(L + 1) * KV);  /* S[0] = entering state */
+    double* qn = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1) * K);
+    double* kn = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1) * K);
+    double* g = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1) * K);
+    double* bt = (double*)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1));
+    double* dS = (double*)malloc(sizeof(double) * KV);
+    double* Sd = (double*)malloc(sizeof(double) * KV);
+    double* u = (double*)malloc(sizeof(double) * (K > V ? K : V));
+    double* e = (double*)malloc(sizeof(double) * V);
+    double* de = (double*)malloc(sizeof(double) * V);
+    double* dqh = (double*)malloc(sizeof(double) * K);
+    double* dkh = (double*)malloc(sizeof(double) * K);
+    double* dg = (double*)malloc(sizeof(double) * K);
+    if (!S || !qn || !kn || !g || !bt || !dS || !Sd || !u || !e || !de || !dqh || !dkh || !dg) {
+      BJ->oom = 1;
+      free(S); free(qn); free(kn); free(g); free(bt); free(dS); free(Sd); free(u); free(e);
+      free(de); free(dqh); free(dkh); free(dg);
+      continue;
+    }
+    const long sidx = ((long)n * H + h) * KV;
+    for (long i = 0; i < KV; ++i) S[i] = J->init ? J->init[sidx + i] : 0.0;
+    const int G = H / J->HK;
+    /* forward, keeping every state */
+    for (long t = t0; t < t1; ++t) {
+      const long l = t - t0;
+      const long th = ((row * J->T) + t) * H + h;
+      const long thk = ((row * J->T) + t) * J->HK + h / G;
+      l2norm(J->q + thk * K, K, qn + l * K);
+      l2norm(J->k + thk * K, K, kn + l * K);
+      gate_row(J->gate + th * K, J->dt_bias + (long)h * K, J->a_log[h], K, J->gate_mode, J->lb,
+               g + l * K);
+      bt[l] = sigmoid(J->beta[th]);
+      memcpy(S + (l + 1) * KV, S + l * KV, sizeof(double) * KV);
+      recur_step(S + (l + 1) * KV, K, V, qn + l * K, kn + l * K, g + l * K, bt[l], J->v + th * V,
+                 J->scale, u, NULL);
+    }
+    /* reverse */
+    for (long i = 0; i < KV; ++i) dS[i] = BJ->d_fin ? BJ->d_fin[sidx + i] : 0.0;
+    double da = 0.0;
+    double* ddt = BJ->ddt_part + ((long)n * H + h) * K;
+    for (int c = 0; c < K; ++c) ddt[c] = 0.0;
+    for (long t = t1 - 1; t >= t0; --t) {
+      const long l = t - t0;
+      const long th = ((row * J->T) + t) * H + h;
+      const double* St = S + (l + 1) * KV;
+      const double* Sp = S + l * KV;
+      const double* q_ = qn + l * K;
+      const double* k_ = kn + l * K;
+      const double* g_ = g + l * K;
+      const double b_ = bt[l];
+      const double* do_ = BJ->d_o + th * V;
+      const double* v_ = J->v + th * V;
+      /* recompute S' = Diag(e^g) S_prev, u = S'^T k^, e = v - u */
+      for (int c = 0; c < K; ++c) {
+        const double d = exp(g_[c]);
+        for (int j = 0; j < V; ++j) Sd[(long)c * V + j] = d * Sp[(long)c * V + j];
+      }
+      for (int j = 0; j < V; ++j) {
+        double acc = 0.0;
+        for (int c = 0; c < K; ++c) acc += Sd[(long)c * V + j] * k_[c];
+        u[j] = acc;
+        e[j] = v_[j] - acc;
+      }
+      /* output */
+      for (int c = 0; c < K; ++c) {
+        double acc = 0.0;
+        for (int j = 0; j < V; ++j) {
+          dS[(long)c * V + j] += J->scale * q_[c] * do_[j];
+          acc += St[(long)c * V + j] * do_[j];
+        }
+        dqh[c] = J->scale * acc;
+      }
+      /* update S = S' + beta k^ e^T */
+      double dbeta = 0.0;
+      for (int j = 0; j < V; ++j) {
+        double acc = 0.0;
+        for (int c = 0; c < K; ++c) acc += dS[(long)c * V + j] * k_[c];
+        de[j] = b_ * acc;
+        dbeta += acc * e[j];
+      }
+      for (int c = 0; c < K; ++c) {
+        double acc = 0.0, acc2 = 0.0;
+        for (int j = 0; j < V; ++j) {
+          acc += dS[(long)c * V + j] * e[j];
+          acc2 += Sd[(long)c * V + j] * de[j];
+        }
+        dkh[c] = b_ * acc - acc2;  /* through e (directly) and through u = S'^T k^ */
+      }
+      /* dS' = dS - k^ de^T, the decay's gradient, and dS_prev */
+      for (int c = 0; c < K; ++c) {
+        const double d = exp(g_[c]);
+        double acc = 0.0;
+        for (int j = 0; j < V; ++j) {
+          const double dsd = dS[(long)c * V + j] - k_[c] * de[j];
+          acc += dsd * Sd[(long)c * V + j];
+          dS[(long)c * V + j] = d * dsd;
+        }
+        dg[c] = acc;
+      }
+      for (int j = 0; j < V; ++j) BJ->dv[th * V + j] = de[j];
+      BJ->dbeta[th] = dbeta * b_ * (1.0 - b_);
+      /* raw q, k through the L2 norm (per value head; groups are summed later) */
+      const long thk = ((row * J->T) + t) * J->HK + h / G;
+      l2norm_bwd(J->q + thk * K, dqh, K, BJ->dqh + th * K);
+      l2norm_bwd(J->k + thk * K, dkh, K, BJ->dkh + th * K);
+      /* gate */
+      for (int c = 0; c < K; ++c) {
+        double dgdx, dgda;
+        gate_grad(J->gate[th * K + c] + J->dt_bias[(long)h * K + c], J->a_log[h], J->gate_mode,
+                  J->lb, &dgdx, &dgda);
+        BJ->dgate[th * K + c] = dg[c] * dgdx;
+        ddt[c] += dg[c] * dgdx;
+        da += dg[c] * dgda;
+      }
+    }
+    BJ->da_part[(long)n * H + h] = da;
+    if (BJ->dinit)
+      for (long i = 0; i < KV; ++i) BJ->dinit[sidx + i] = dS[i];
+    free(S); free(qn); free(kn); free(g); free(bt); free(dS); free(Sd); free(u); free(e);
+    free(de); free(dqh); free(dkh); free(dg);
+  }
+  return NULL;
+}
+
+int oracle_kda_bwd(int B, int T, int H, int HK, int K, int V, const double* q, const double* k,
+                   const double* v, const double* gate, const double* beta, const double* a_log,
+                   const double* dt_bias, double scale, int gate_mode, double lower_bound, int N,
+                   const int32_t* cu_seqlens, const double* initial_state, const double* d_o,
+                   const double* d_final, double* dq, double* dk, double* dv, double* dgate,
+                   double* dbeta, double* da_log, double* ddt_bias, double* dinit, int threads) {
+  if (B < 0 || T < 0 || H <= 0 || HK <= 0 || H % HK || K <= 0 || V <= 0) return 1;
+  if (check_cu(B, T, N, cu_seqlens)) return 2;
+  bwd_job_t BJ;
+  memset(&BJ, 0, sizeof(BJ));
+  job_t* J = &BJ.f;
+  J->B = B; J->T = T; J->H = H; J->HK = HK; J->K = K; J->V = V;
+  J->q = q; J->k = k; J->v = v; J->gate = gate; J->beta = beta; J->a_log = a_log;
+  J->dt_bias = dt_bias; J->gate_mode = gate_mode; J->lb = lower_bound; J->scale = scale;
+  J->N = N; J->cu = cu_seqlens; J->init = initial_state;
+  BJ.d_o = d_o; BJ.d_fin = d_final; BJ.dv = dv; BJ.dgate = dgate; BJ.dbeta = dbeta;
+  BJ.dinit = dinit;
+  const size_t tokh = (size_t)B * T * H;
+  BJ.dqh = (double*)calloc(tokh * K + 1, sizeof(double));
+  BJ.dkh = (double*)calloc(tokh * K + 1, sizeof(double));
+  BJ.da_part = (double*)calloc((size_t)N * H + 1, sizeof(double));
+  BJ.ddt_part = (double*)calloc((size_t)N * H * K + 1, sizeof(double));
+  if (!BJ.dqh || !BJ.dkh || !BJ.da_part || !BJ.ddt_part) {
+    free(BJ.dqh); free(BJ.dkh); free(BJ.da_part); free(BJ.ddt_part);
+    return 3;
+  }
+  if (threads < 1) threads = 1;
+  if (threads > 256) threads = 256;
+  pthread_mutex_init(&J->mu, NULL);
+  J->next = 0;
+  pthread_t tid[256];
+  int started = 0;
+  for (int i = 1; i < threads; ++i)
+    if (pthread_create(&tid[started], NULL, bwd_worker, &BJ) == 0) ++started;
+  bwd_worker(&BJ);
+  for (int i = 0; i < started; ++i) pthread_join(tid[i], NULL);
+  pthread_mutex_destroy(&J->mu);
+  /* group sums for the key heads, sums over sequences for the gate parameters */
+  const int G = H / HK;
+  for (long bt = 0; bt < (long)B * T; ++bt)
+    for (int hk = 0; hk < HK; ++hk)
+      for (int c = 0; c < K; ++c) {
+        double sq = 0.0, sk = 0.0;
+        for (int gi = 0; gi < G; ++gi) {
+          const long th = bt * H + (long)hk * G + gi;
+          sq += BJ.dqh[th * K + c];
+          sk += BJ.dkh[th * K + c];
+        }
+        dq[(bt * HK + hk) * K + c] = sq;
+        dk[(bt * HK + hk) * K + c] = sk;
+      }
+  for (int h = 0; h < H; ++h) {
+    double a = 0.0;
+    for (int n = 0; n < N; ++n) a += BJ.da_part[(long)n * H + h];
+    da_log[h] = a;
+    for (int c = 0; c < K; ++c) {
+      double d = 0.0;
+      for (int n = 0; n < N; ++n) d += BJ.ddt_part[((long)n * H + h) * K + c];
+      ddt_bias[(long)h * K + c] = d;
+    }
+  }
+  const int oom = BJ.oom;
+  free(BJ.dqh); free(BJ.dkh); free(BJ.da_part); free(BJ.ddt_part);
+  return oom ? 3 : 0;
 }
 
 /* Public: final = transition . initial + state_ext (initial may be NULL). */
