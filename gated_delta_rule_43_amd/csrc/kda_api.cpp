@@ -134,10 +134,10 @@ int chunk_count(const kda_problem* p, int* exact) {
   return p->T / C + p->N;
 }
 
-Layout layout(const kda_problem* p) {
+Layout layout_for(const kda_problem* p, bool mfma) {
   Layout L;
   L.NT = chunk_count(p, &L.exact);
-  L.mfma = use_mfma(p);
+  L.mfma = mfma;
   const size_t NT = (size_t)L.NT, H = value_heads(p), K = p->K, V = p->V, C = p->chunk_size, N = p->N;
   const size_t tokh = (size_t)p->B * p->T * H;
   size_t o = 0;
@@ -171,6 +171,45 @@ Layout layout(const kda_problem* p) {
   }
   L.total = o;
   return L;
+}
+
+Layout layout(const kda_problem* p) { return layout_for(p, use_mfma(p)); }
+
+// The backward's workspace: the VALU forward's (recomputed factors) followed by
+// Akk and Tm, per-chunk states and their gradients, per-token-head gradient
+// staging and per-chunk partial sums of the gate-parameter gradients.
+struct BwdLayout {
+  Layout f;
+  size_t off_akk = 0, off_tm = 0, off_hc = 0, off_dhc = 0, off_dc = 0, off_ddc = 0;
+  size_t off_dqh = 0, off_dkh = 0, off_dgam = 0, off_tkb = 0, off_da = 0, off_ddt = 0;
+  size_t total = 0;
+};
+
+BwdLayout bwd_layout(const kda_problem* p) {
+  BwdLayout B;
+  B.f = layout_for(p, false);
+  const size_t NT = (size_t)B.f.NT, H = value_heads(p), K = p->K, V = p->V, C = p->chunk_size;
+  const size_t tokh = (size_t)p->B * p->T * H;
+  size_t o = B.f.total;
+  auto take = [&](size_t bytes) {
+    size_t at = o;
+    o = align_up(o + bytes);
+    return at;
+  };
+  B.off_akk = take(NT * H * C * C * 4);
+  B.off_tm = take(NT * H * C * C * 4);
+  B.off_hc = take(NT * H * K * V * 4);
+  B.off_dhc = take(NT * H * K * V * 4);
+  B.off_dc = take(NT * H * C * V * 4);
+  B.off_ddc = take(NT * H * C * V * 4);
+  B.off_dqh = take(tokh * K * 4);
+  B.off_dkh = take(tokh * K * 4);
+  B.off_dgam = take(tokh * K * 4);
+  B.off_tkb = take(tokh * K * 4);
+  B.off_da = take(NT * H * 4);
+  B.off_ddt = take(NT * H * K * 4);
+  B.total = o;
+  return B;
 }
 
 kda::FwdArgs make_args(const kda_problem* p, const Layout& L, void* ws) {
@@ -495,6 +534,57 @@ kda_status kda_chunk_table(const kda_problem* p, int32_t* tok, int32_t* len, int
   a.B = p->B; a.T = p->T; a.C = p->chunk_size; a.N = p->N; a.NT = need; a.cu = p->cu_seqlens;
   a.chunk_tok = tok; a.chunk_len = len; a.seq_chunk0 = seq_chunk0; a.nt_dev = count;
   hipError_t e = kda::launch_chunk_table(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(KDA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_last_error.clear();
+  return KDA_OK;
+}
+
+size_t kda_bwd_workspace_size(const kda_problem* p, kda_status* status) {
+  kda_status st = validate_problem(p, false);
+  if (status) *status = st;
+  return st == KDA_OK ? bwd_layout(p).total : 0;
+}
+
+kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const void* v,
+                   const void* gate, const void* beta, const float* a_log, const float* dt_bias,
+                   const float* initial_state, const void* d_o, const float* d_final_state,
+                   void* dq, void* dk, void* dv, void* dgate, void* dbeta, float* da_log,
+                   float* ddt_bias, float* d_initial_state, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  kda_status st = validate_problem(p, false);
+  if (st != KDA_OK) return st;
+  st = check_inputs(p, q, k, v, gate, beta, a_log, dt_bias);
+  if (st != KDA_OK) return st;
+  const bool any_tokens = (long long)p->B * p->T > 0;
+  if (any_tokens && (!d_o || !dq || !dk || !dv || !dgate || !dbeta))
+    return fail(KDA_EINVAL, "d_o, dq, dk, dv, dgate and dbeta must be non-NULL");
+  if (!da_log || !ddt_bias) return fail(KDA_EINVAL, "da_log and ddt_bias must be non-NULL");
+  const size_t elt = p->dtype == KDA_BF16 ? 2 : 4;
+  const void* typed[] = {d_o, dq, dk, dv, dgate, dbeta};
+  for (const void* ptr : typed)
+    if (ptr && !aligned(ptr, elt)) return fail(KDA_EINVAL, "gradient tensor is not %zu-byte aligned", elt);
+  const void* f32[] = {initial_state, d_final_state, da_log, ddt_bias, d_initial_state};
+  for (const void* ptr : f32)
+    if (ptr && !aligned(ptr, 4)) return fail(KDA_EINVAL, "fp32 state or parameter gradient misaligned");
+  const BwdLayout L = bwd_layout(p);
+  st = check_ws(L.total, workspace, workspace_bytes);
+  if (st != KDA_OK) return st;
+  char* w = (char*)workspace;
+  kda::BwdArgs b{};
+  b.f = make_args(p, L.f, workspace);
+  b.f.q = q; b.f.k = k; b.f.v = v; b.f.gate = gate; b.f.beta = beta;
+  b.f.a_log = a_log; b.f.dt_bias = dt_bias; b.f.init = initial_state;
+  b.f.Akk_out = (float*)(w + L.off_akk);
+  b.f.Tm_out = (float*)(w + L.off_tm);
+  b.d_o = d_o; b.d_fin = d_final_state;
+  b.hc = (float*)(w + L.off_hc); b.dhc = (float*)(w + L.off_dhc);
+  b.Dc = (float*)(w + L.off_dc); b.dDc = (float*)(w + L.off_ddc);
+  b.dqh = (float*)(w + L.off_dqh); b.dkh = (float*)(w + L.off_dkh);
+  b.dgam = (float*)(w + L.off_dgam); b.tkb = (float*)(w + L.off_tkb);
+  b.da_part = (float*)(w + L.off_da); b.ddt_part = (float*)(w + L.off_ddt);
+  b.dq = dq; b.dk = dk; b.dv = dv; b.dgate = dgate; b.dbeta = dbeta;
+  b.da_log = da_log; b.ddt_bias = ddt_bias; b.dinit = d_initial_state;
+  hipError_t e = kda::launch_bwd(b, (hipStream_t)stream);
   if (e != hipSuccess) return fail(KDA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   g_last_error.clear();
   return KDA_OK;

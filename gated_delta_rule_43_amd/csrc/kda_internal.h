@@ -67,6 +67,9 @@ struct FwdArgs {
   int ws_bf16;
   void *W, *U, *Qt, *Kb, *Aqk;
   float* gL;
+  // backward only: Akk (strictly lower) and Tm per chunk-head, [C*C] each
+  float* Akk_out;
+  float* Tm_out;
   // workspace: per chunk-head records of the MFMA path, and a small sink for
   // the state pass's masked-off output stores
   void* rec;
@@ -95,6 +98,25 @@ struct ConvArgs {
   ConvTensor t[3];
 };
 
+// The backward: the forward's VALU workspace (FwdArgs, with Akk_out/Tm_out
+// set) plus per-chunk states and their gradients, and the gradient outputs.
+struct BwdArgs {
+  FwdArgs f;
+  // inputs
+  const void* d_o;       // [B,T,H,V], dtype as f.dtype
+  const float* d_fin;    // [N,H,K,V] or nullptr
+  // workspace
+  float *hc, *dhc;       // [NT*H][K*V] state entering each chunk, gradient of the state leaving it
+  float *Dc, *dDc;       // [NT*H][C*V] Delta and its gradient
+  float *dqh, *dkh;      // [B*T*H][K] gradient of q^, k^ per value head
+  float *dgam, *tkb;     // [B*T*H][K] gradient of gamma; the Kbar term summed into gamma_L
+  float *da_part;        // [NT*H]
+  float *ddt_part;       // [NT*H][K]
+  // outputs
+  void *dq, *dk, *dv, *dgate, *dbeta;  // dtype as f.dtype
+  float *da_log, *ddt_bias, *dinit;    // fp32; dinit may be nullptr
+};
+
 // Stages of one forward, in launch order (timing hooks of kda_fwd_profiled).
 enum Stage { kStageTable = 0, kStagePrologue = 1, kStageChunk = 2, kStageState = 3, kNumStages = 4 };
 
@@ -105,6 +127,8 @@ inline void mark(const FwdArgs& a, int stage, int end, hipStream_t s) {
 // Kernel launchers (return the first HIP error, hipSuccess otherwise).
 hipError_t launch_chunk_table(const FwdArgs& a, hipStream_t s);
 hipError_t launch_valu_path(const FwdArgs& a, hipStream_t s);
+hipError_t launch_valu_prep(const FwdArgs& a, hipStream_t s);
+hipError_t launch_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_mfma_path(const FwdArgs& a, hipStream_t s);
 hipError_t launch_short_conv(const ConvArgs& a, hipStream_t s);
 size_t mfma_record_bytes(int K, int V);

@@ -131,6 +131,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_valu(FwdArgs a) {
     }
     sA[r][i] = (i < r) ? akk : 0.f;
     Aqk[p] = (i <= r && r < L) ? a.scale * aqk : 0.f;
+    if (a.Akk_out) a.Akk_out[chb * C * C + p] = (i < r) ? akk : 0.f;
   }
   __syncthreads();
 
@@ -147,6 +148,8 @@ __global__ __launch_bounds__(kThreads) void k_chunk_valu(FwdArgs a) {
     }
     __syncthreads();
   }
+  if (a.Tm_out)
+    for (int p = tid; p < C * C; p += kThreads) a.Tm_out[chb * C * C + p] = sA[p / C][p % C];
 
   // Qt = scale q^ exp(gamma), Kb = k^ exp(gamma_L - gamma), gL = exp(gamma_L)
   float* Qt = (float*)a.Qt + chb * C * K;
@@ -271,6 +274,24 @@ __global__ __launch_bounds__(kThreads) void k_state_valu(FwdArgs a) {
 }
 
 template <typename Tin, int C>
+hipError_t run_prep(const FwdArgs& a, hipStream_t s) {
+  const int64_t n_th = (int64_t)a.B * a.T * a.H;
+  if (n_th > 0) {
+    const int64_t blocks = (n_th + 3) / 4;
+    hipLaunchKernelGGL(k_prologue_valu<Tin>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+                       (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.gate, (const Tin*)a.beta,
+                       a.a_log, a.dt_bias, n_th, a.H, a.HK, a.K, a.gate_form, a.lb, a.qn, a.kn, a.g, a.bt);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
+  if (a.NT > 0) {
+    hipLaunchKernelGGL((k_chunk_valu<Tin, C>), dim3((unsigned)((int64_t)a.NT * a.H)),
+                       dim3(kThreads), 0, s, a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
+  return hipSuccess;
+}
+
+template <typename Tin, int C>
 hipError_t run(const FwdArgs& a, hipStream_t s) {
   const int64_t n_th = (int64_t)a.B * a.T * a.H;
   mark(a, kStagePrologue, 0, s);
@@ -314,6 +335,23 @@ hipError_t run_c(const FwdArgs& a, hipStream_t s) {
 
 hipError_t launch_valu_path(const FwdArgs& a, hipStream_t s) {
   return a.dtype == 0 ? run_c<float>(a, s) : run_c<bf16>(a, s);
+}
+
+// The prologue and chunk-factor kernels alone (no state pass): the
+// recomputation the backward starts from.
+hipError_t launch_valu_prep(const FwdArgs& a, hipStream_t s) {
+  if (a.dtype == 0) {
+    switch (a.C) {
+      case 16: return run_prep<float, 16>(a, s);
+      case 32: return run_prep<float, 32>(a, s);
+      default: return run_prep<float, 64>(a, s);
+    }
+  }
+  switch (a.C) {
+    case 16: return run_prep<bf16, 16>(a, s);
+    case 32: return run_prep<bf16, 32>(a, s);
+    default: return run_prep<bf16, 64>(a, s);
+  }
 }
 
 }  // namespace kda

@@ -33,6 +33,7 @@ EXPORTED = ("kda_validate", "kda_fwd_workspace_size", "kda_fwd", "kda_fwd_profil
             "kda_state_summary_workspace_size", "kda_state_summary",
             "kda_apply_state_summary", "kda_chunk_capacity", "kda_chunk_table",
             "kda_short_conv_silu", "kda_fwd_short_conv_workspace_size", "kda_fwd_short_conv",
+            "kda_bwd_workspace_size", "kda_bwd",
             "kda_last_error", "kda_version")
 MAX_CONV_WIDTH = 4
 
@@ -96,6 +97,10 @@ def load_library(path: Optional[str] = None):
     lib.kda_fwd_short_conv_workspace_size.restype = S
     lib.kda_fwd_short_conv.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P, P, S, P]
     lib.kda_fwd_short_conv.restype = ctypes.c_int
+    lib.kda_bwd_workspace_size.argtypes = [PP, PI]
+    lib.kda_bwd_workspace_size.restype = S
+    lib.kda_bwd.argtypes = [PP] + [P] * 18 + [P, S, P]
+    lib.kda_bwd.restype = ctypes.c_int
     lib.kda_last_error.argtypes = []
     lib.kda_last_error.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -401,6 +406,53 @@ def _fwd(q, k, v, gate, beta, a_log, dt_bias, conv, scale, lower_bound, chunk_si
     if st:
         _raise(st, "kda_fwd_short_conv" if conv is not None else "kda_fwd")
     return o, fin
+
+
+def kda_bwd(q, k, v, gate, beta, a_log, dt_bias, d_o, d_final_state=None, *, scale=None,
+            lower_bound=None, chunk_size=64, cu_seqlens=None, cu_seqlens_host=None,
+            initial_state=None, lower_bound_form="sigmoid", workspace=None):
+    """Gradients of L = sum(d_o * o) + sum(d_final_state * final_state) of kda_fwd
+    with the same arguments.  Returns a dict: dq, dk [B,T,H,K], dv [B,T,HV,V],
+    dgate [B,T,HV,K], dbeta [B,T,HV] (of the logits; q's dtype), da_log [HV],
+    ddt_bias [HV,K] and dinit [N,HV,K,V] (float32)."""
+    B, T, H, K, V, HV = _check_inputs(q, k, v, gate, beta, a_log, dt_bias)
+    lib = load_library()
+    device = q.device
+    _dev(d_o, "d_o", dtype=q.dtype, shape=(B, T, HV, V))
+    cu, host, N, host_ptr = _cu_args(cu_seqlens, cu_seqlens_host, T)
+    if N is None:
+        N = B
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", dtype=torch.float32, shape=(N, HV, K, V))
+    if d_final_state is not None:
+        _dev(d_final_state, "d_final_state", dtype=torch.float32, shape=(N, HV, K, V))
+    if scale is not None and not scale > 0:
+        raise ValueError("scale must be positive, got %r" % (scale,))
+    p = make_problem(B, T, H, K, V, _dtype_code(q), scale, lower_bound, chunk_size, N,
+                     None if cu is None else cu.data_ptr(), host_ptr, lower_bound_form, HV)
+    st = ctypes.c_int(0)
+    need = lib.kda_bwd_workspace_size(ctypes.byref(p), ctypes.byref(st))
+    if st.value:
+        _raise(st.value, "kda_bwd")
+    out = dict(dq=torch.empty_like(q), dk=torch.empty_like(k), dv=torch.empty_like(v),
+               dgate=torch.empty_like(gate), dbeta=torch.empty_like(beta),
+               da_log=torch.empty(HV, dtype=torch.float32, device=device),
+               ddt_bias=torch.empty(HV, K, dtype=torch.float32, device=device),
+               dinit=torch.empty(N, HV, K, V, dtype=torch.float32, device=device))
+    if workspace is None:
+        ws, nbytes = _workspace(need, device)
+    else:
+        _dev(workspace, "workspace", dtype=torch.uint8)
+        ws, nbytes = workspace, workspace.numel()
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib.kda_bwd(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ptr(gate), ptr(beta), ptr(a_log),
+                     ptr(dt_bias), ptr(initial_state), ptr(d_o), ptr(d_final_state),
+                     ptr(out["dq"]), ptr(out["dk"]), ptr(out["dv"]), ptr(out["dgate"]),
+                     ptr(out["dbeta"]), ptr(out["da_log"]), ptr(out["ddt_bias"]), ptr(out["dinit"]),
+                     ptr(ws), nbytes, _stream_ptr(device))
+    if st:
+        _raise(st, "kda_bwd")
+    return out
 
 
 def kda_state_summary(q, k, v, gate, beta, a_log, dt_bias, *, lower_bound=None, chunk_size=64,

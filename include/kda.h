@@ -212,6 +212,39 @@ kda_status kda_chunk_table(const kda_problem* p, int32_t* tok, int32_t* len, int
                            int32_t* count, int32_t cap, void* stream);
 
 /*
+ * Gradients of the forward: for L = sum(d_o * o) + sum(d_final_state *
+ * final_state), with o and final_state what kda_fwd returns for the same
+ * problem and inputs, the gradient of L with respect to every input, through
+ * the in-kernel L2 norm, gate and beta sigmoid (the chunk_kda call that the
+ * torchtitan PR #4025 commit note tests forward and backward together; the
+ * hyper_parallel page routes the state gradient between slices in the
+ * backward of `_RecvKDAInitialState`).
+ *
+ *  q .. dt_bias, initial_state   the forward's inputs (initial_state NULL = zeros).
+ *  d_o              [B,T,HV,V], p->dtype: gradient of o (required).
+ *  d_final_state    [N,HV,K,V] fp32, or NULL for zeros.
+ *  dq, dk           [B,T,H,K], p->dtype: with grouped value heads, summed over
+ *                   the value heads that read the key head.
+ *  dv [B,T,HV,V], dgate [B,T,HV,K], dbeta [B,T,HV]   p->dtype (dbeta is the
+ *                   gradient of the beta logits).
+ *  da_log [HV], ddt_bias [HV,K]   fp32, summed over all tokens (required).
+ *  d_initial_state  [N,HV,K,V] fp32, or NULL to not produce it; for an empty
+ *                   document it equals that document's d_final_state.
+ *  workspace        at least kda_bwd_workspace_size() bytes, 256-byte aligned.
+ * Where the forward floors the log-decay at -110 or clamps it at the bound,
+ * the gate's gradient is zero.  Computed in fp32 for both dtypes; the forward's
+ * factors are recomputed, not read from a forward call.  Results are
+ * deterministic (fixed summation orders, no atomics).
+ */
+size_t kda_bwd_workspace_size(const kda_problem* p, kda_status* status);
+kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const void* v,
+                   const void* gate, const void* beta, const float* a_log, const float* dt_bias,
+                   const float* initial_state, const void* d_o, const float* d_final_state,
+                   void* dq, void* dk, void* dv, void* dgate, void* dbeta, float* da_log,
+                   float* ddt_bias, float* d_initial_state, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/*
  * The layer's short convolution before the forward: SiLU of a causal
  * depthwise convolution over time, applied per channel to q, k and v
  * (hyper_parallel coverage page: `_run_causal_short_conv`,
