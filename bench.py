@@ -12,6 +12,7 @@ device synchronisations; rank 0 prints one JSON line.
 Besides the throughput it reports
   * "short_conv": the same step after the layer's short convolution + SiLU of
     q, k, v (kda_fwd_short_conv), and that convolution kernel's own HBM rate;
+  * "backward": the gradients of the same forward (kda_bwd);
   * "roofline": the dominant kernel's algorithmic bytes per launch divided by
     its average duration, timed live with HIP events recorded by the library
     around each stage on the kernel's own stream (kda_fwd_profiled);
@@ -262,6 +263,43 @@ def bench_short_conv(inp, w, o, steps, warmup, width=4):
                             "tensor": "q [B,T,H*K]"}}
 
 
+def bench_backward(inp, w, steps, warmup):
+    """The backward (kda_bwd) of the same forward on the same resident inputs,
+    with a seeded output gradient; events on the launch stream around each call."""
+    dev = inp["q"].device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    d_o = torch.randn(w.B, w.T, w.H, w.V, generator=gen, device=dev).to(w.torch_dtype)
+    cu = inp["cu_seqlens"]
+    cu_host = None if cu is None else cu.cpu()
+
+    def bwd():
+        return kda.kda_bwd(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"], inp["a_log"],
+                           inp["dt_bias"], d_o, None, scale=w.scale, lower_bound=w.lower_bound,
+                           chunk_size=w.chunk_size, cu_seqlens=cu, cu_seqlens_host=cu_host,
+                           initial_state=inp["initial_state"])
+
+    for _ in range(max(1, warmup)):
+        bwd()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    t0 = time.perf_counter()
+    for a, b in evs:
+        a.record(stream)
+        bwd()
+        b.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    tokens = w.B * w.T
+    return {"workload": w.name + " backward (gradients of q, k, v, gate, beta, a_log, dt_bias)",
+            "value": round(tokens / (ms / 1e3) / 1e6, 4), "unit": "Mtokens/s",
+            "ms_per_step": round(ms, 3), "wall_ms_per_step": round(wall, 3),
+            "arith": "fp32 VALU (both dtypes)"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -271,6 +309,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-short-conv", action="store_true",
                     help="skip the forward-after-short-convolution measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (to scale the "
                          "FETCH_SIZE/WRITE_SIZE counters) and exit")
@@ -367,6 +406,9 @@ def main():
     if not args.no_short_conv:
         print("[bench] timing the forward after the short convolution", file=sys.stderr, flush=True)
         out["short_conv"] = bench_short_conv(inp, w, o, args.steps, args.warmup)
+    if not args.no_backward:
+        print("[bench] timing the backward", file=sys.stderr, flush=True)
+        out["backward"] = bench_backward(inp, w, min(args.steps, 5), 1)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, w)

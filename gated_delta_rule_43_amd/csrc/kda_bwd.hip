@@ -33,6 +33,10 @@ namespace kda {
 namespace {
 
 constexpr int kThreads = 256;
+// Workgroup size of the chunk-gradient kernel per (C, K): its LDS (up to 151 KB)
+// allows one workgroup per CU, so the widest size that compiles without
+// register spills gives the most waves to hide LDS latency.
+constexpr int chunk_threads(int C, int K) { return C == 64 ? (K == 128 ? 1024 : 512) : C == 32 ? 256 : 512; }
 constexpr int kMaxD = 128;
 constexpr float kGateFloor = -110.f;
 
@@ -66,135 +70,209 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
+// Copy n floats (n a multiple of 4, 16-byte aligned) from global memory to LDS.
+__device__ inline void stage(float* dst, const float* src, int n) {
+  for (int e = threadIdx.x; e < n / 4; e += kThreads) ((float4*)dst)[e] = ((const float4*)src)[e];
+}
+
 // Forward state pass keeping S0 and Delta of every chunk.  One workgroup per
-// (sequence, head, tile of VT columns).
-template <int C, int VT>
+// (sequence, head, tile of 64 columns): lane = column, wave w owns the state
+// rows [w K/4, (w+1) K/4) in registers; W and Kbar of each chunk are staged in
+// LDS and read as float4 broadcasts.
+template <int C, int K>
 __global__ __launch_bounds__(kThreads) void k_bwd_fstate(BwdArgs b) {
+  constexpr int VT = 64, RS = K / 4, RD = C / 4;
   const FwdArgs& a = b.f;
-  const int H = a.H, K = a.K, V = a.V;
+  const int H = a.H, V = a.V;
   const int ntile = V / VT;
   const int64_t wid = blockIdx.x;
   const int tile = (int)(wid % ntile);
   const int64_t nh = wid / ntile;
   const int h = (int)(nh % H), n = (int)(nh / H);
-  const int col0 = tile * VT;
-  const int tid = threadIdx.x;
-  __shared__ float sS[kMaxD][VT];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = tile * VT + lane;
+  __shared__ float sS[K][VT];
   __shared__ float sD[C][VT];
+  __shared__ __attribute__((aligned(16))) float sW[C][K];
+  __shared__ __attribute__((aligned(16))) float sKb[C][K];
   const int64_t sbase = ((int64_t)n * H + h) * K * V;
-  for (int e = tid; e < K * VT; e += kThreads) {
-    const int c = e / VT, jj = e % VT;
-    sS[c][jj] = a.init ? a.init[sbase + (int64_t)c * V + col0 + jj] : 0.f;
+  float st[RS];
+#pragma unroll
+  for (int m = 0; m < RS; ++m) {
+    st[m] = a.init ? a.init[sbase + (int64_t)(w * RS + m) * V + col] : 0.f;
+    sS[w * RS + m][lane] = st[m];
   }
   const int jc0 = a.seq_chunk0[n], jc1 = a.seq_chunk0[n + 1];
   for (int j = jc0; j < jc1; ++j) {
     const int64_t chb = (int64_t)j * H + h;
-    const float* W = (const float*)a.W + chb * C * K;
     const float* U = (const float*)a.U + chb * C * V;
-    const float* Kb = (const float*)a.Kb + chb * C * K;
     const float* gL = a.gL + chb * K;
     float* hc = b.hc + chb * K * V;
     float* Dc = b.Dc + chb * C * V;
     const int L = a.chunk_len[j];
+    __syncthreads();  // the previous chunk is done with sW, sKb; sS holds the state
+    stage(&sW[0][0], (const float*)a.W + chb * C * K, C * K);
+    stage(&sKb[0][0], (const float*)a.Kb + chb * C * K, C * K);
+#pragma unroll
+    for (int m = 0; m < RS; ++m) hc[(int64_t)(w * RS + m) * V + col] = st[m];
     __syncthreads();
-    for (int e = tid; e < K * VT; e += kThreads) {
-      const int c = e / VT, jj = e % VT;
-      hc[(int64_t)c * V + col0 + jj] = sS[c][jj];
+    // Delta = U - W S for rows [w C/4, (w+1) C/4)
+    float d[RD];
+#pragma unroll
+    for (int m = 0; m < RD; ++m) d[m] = U[(int64_t)(w * RD + m) * V + col];
+    for (int c = 0; c < K; c += 4) {
+      const float s0 = sS[c][lane], s1 = sS[c + 1][lane], s2 = sS[c + 2][lane], s3 = sS[c + 3][lane];
+#pragma unroll
+      for (int m = 0; m < RD; ++m) {
+        const float4 wv = *(const float4*)&sW[w * RD + m][c];
+        d[m] -= wv.x * s0 + wv.y * s1 + wv.z * s2 + wv.w * s3;
+      }
     }
-    for (int e = tid; e < C * VT; e += kThreads) {
-      const int r = e / VT, jj = e % VT, col = col0 + jj;
-      float acc = U[(int64_t)r * V + col];
-      for (int c = 0; c < K; ++c) acc = fmaf(-W[(int64_t)r * K + c], sS[c][jj], acc);
-      sD[r][jj] = acc;
-      Dc[(int64_t)r * V + col] = acc;
+#pragma unroll
+    for (int m = 0; m < RD; ++m) {
+      sD[w * RD + m][lane] = d[m];
+      Dc[(int64_t)(w * RD + m) * V + col] = d[m];
     }
     __syncthreads();
-    for (int e = tid; e < K * VT; e += kThreads) {
-      const int c = e / VT, jj = e % VT;
-      float acc = gL[c] * sS[c][jj];
-      for (int r = 0; r < L; ++r) acc = fmaf(Kb[(int64_t)r * K + c], sD[r][jj], acc);
-      sS[c][jj] = acc;
+    // S = Diag(gL) S + Kbar^T Delta for the wave's rows
+#pragma unroll
+    for (int m = 0; m < RS; ++m) st[m] *= gL[w * RS + m];
+    for (int r = 0; r < L; ++r) {
+      const float dv = sD[r][lane];
+#pragma unroll
+      for (int m = 0; m < RS; m += 4) {
+        const float4 kb = *(const float4*)&sKb[r][w * RS + m];
+        st[m] = fmaf(kb.x, dv, st[m]);
+        st[m + 1] = fmaf(kb.y, dv, st[m + 1]);
+        st[m + 2] = fmaf(kb.z, dv, st[m + 2]);
+        st[m + 3] = fmaf(kb.w, dv, st[m + 3]);
+      }
     }
+#pragma unroll
+    for (int m = 0; m < RS; ++m) sS[w * RS + m][lane] = st[m];
   }
 }
 
 // Reverse state pass: dS_L and dDelta of every chunk, and the initial state's
-// gradient.  One workgroup per (sequence, head, tile of VT columns).
-template <typename Tin, int C, int VT>
+// gradient.  Same layout as the forward pass; Aqk and Kbar, then Qt and W,
+// take turns in one LDS region.
+template <typename Tin, int C, int K>
 __global__ __launch_bounds__(kThreads) void k_bwd_dstate(BwdArgs b) {
+  constexpr int VT = 64, RS = K / 4, RD = C / 4;
   const FwdArgs& a = b.f;
-  const int H = a.H, K = a.K, V = a.V;
+  const int H = a.H, V = a.V;
   const int ntile = V / VT;
   const int64_t wid = blockIdx.x;
   const int tile = (int)(wid % ntile);
   const int64_t nh = wid / ntile;
   const int h = (int)(nh % H), n = (int)(nh / H);
-  const int col0 = tile * VT;
-  const int tid = threadIdx.x;
-  __shared__ float sS[kMaxD][VT];  // dS
-  __shared__ float sD[C][VT];      // dDelta
-  __shared__ float sO[C][VT];      // dO
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int col = tile * VT + lane;
+  __shared__ float sS[K][VT];   // dS
+  __shared__ float sO[C][VT];   // dO
+  __shared__ float sD[C][VT];   // dDelta
+  __shared__ __attribute__((aligned(16))) float sR[2 * C * K];  // Aqk | Kbar, then Qt | W
+  float (*sA)[C] = (float(*)[C])sR;
+  float (*sKb)[K] = (float(*)[K])(sR + C * C);
+  float (*sQt)[K] = (float(*)[K])sR;
+  float (*sW)[K] = (float(*)[K])(sR + C * K);
   const int64_t sbase = ((int64_t)n * H + h) * K * V;
-  for (int e = tid; e < K * VT; e += kThreads) {
-    const int c = e / VT, jj = e % VT;
-    sS[c][jj] = b.d_fin ? b.d_fin[sbase + (int64_t)c * V + col0 + jj] : 0.f;
-  }
+  float ds[RS];
+#pragma unroll
+  for (int m = 0; m < RS; ++m) ds[m] = b.d_fin ? b.d_fin[sbase + (int64_t)(w * RS + m) * V + col] : 0.f;
   const Tin* dO = (const Tin*)b.d_o;
   const int jc0 = a.seq_chunk0[n], jc1 = a.seq_chunk0[n + 1];
   for (int j = jc1 - 1; j >= jc0; --j) {
     const int64_t chb = (int64_t)j * H + h;
-    const float* W = (const float*)a.W + chb * C * K;
-    const float* Qt = (const float*)a.Qt + chb * C * K;
-    const float* Kb = (const float*)a.Kb + chb * C * K;
-    const float* Aqk = (const float*)a.Aqk + chb * C * C;
     const float* gL = a.gL + chb * K;
     float* dhc = b.dhc + chb * K * V;
     float* dDc = b.dDc + chb * C * V;
     const int tok0 = a.chunk_tok[j], L = a.chunk_len[j];
-    __syncthreads();
-    for (int e = tid; e < K * VT; e += kThreads) {
-      const int c = e / VT, jj = e % VT;
-      dhc[(int64_t)c * V + col0 + jj] = sS[c][jj];
+    __syncthreads();  // the previous chunk is done with sR, sO, sD, sS
+#pragma unroll
+    for (int m = 0; m < RS; ++m) {
+      dhc[(int64_t)(w * RS + m) * V + col] = ds[m];
+      sS[w * RS + m][lane] = ds[m];
     }
-    for (int e = tid; e < C * VT; e += kThreads) {
-      const int r = e / VT, jj = e % VT;
-      sO[r][jj] = r < L ? load_f32(dO + ((int64_t)(tok0 + r) * H + h) * V + col0 + jj) : 0.f;
+#pragma unroll
+    for (int m = 0; m < RD; ++m) {
+      const int r = w * RD + m;
+      sO[r][lane] = r < L ? load_f32(dO + ((int64_t)(tok0 + r) * H + h) * V + col) : 0.f;
     }
+    stage(sR, (const float*)a.Aqk + chb * C * C, C * C);
+    stage(sR + C * C, (const float*)a.Kb + chb * C * K, C * K);
     __syncthreads();
-    // dDelta = Aqk_s^T dO + Kbar dS_L
-    for (int e = tid; e < C * VT; e += kThreads) {
-      const int r = e / VT, jj = e % VT;
-      float acc = 0.f;
-      for (int rr = r; rr < L; ++rr) acc = fmaf(Aqk[(int64_t)rr * C + r], sO[rr][jj], acc);
-      for (int c = 0; c < K; ++c) acc = fmaf(Kb[(int64_t)r * K + c], sS[c][jj], acc);
-      sD[r][jj] = acc;
-      dDc[(int64_t)r * V + col0 + jj] = acc;
-    }
-    __syncthreads();
-    // dS0 = Qt_s^T dO + e^gamma_L dS_L - W^T dDelta (each element reads only its own dS)
-    for (int e = tid; e < K * VT; e += kThreads) {
-      const int c = e / VT, jj = e % VT;
-      float acc = gL[c] * sS[c][jj];
-      for (int r = 0; r < L; ++r) {
-        acc = fmaf(Qt[(int64_t)r * K + c], sO[r][jj], acc);
-        acc = fmaf(-W[(int64_t)r * K + c], sD[r][jj], acc);
+    // dDelta = Aqk_s^T dO + Kbar dS_L (Aqk_s is zero above the diagonal)
+    float d[RD];
+#pragma unroll
+    for (int m = 0; m < RD; ++m) d[m] = 0.f;
+    for (int rr = 0; rr < L; ++rr) {
+      const float o = sO[rr][lane];
+#pragma unroll
+      for (int m = 0; m < RD; m += 4) {
+        const float4 av = *(const float4*)&sA[rr][w * RD + m];
+        d[m] = fmaf(av.x, o, d[m]);
+        d[m + 1] = fmaf(av.y, o, d[m + 1]);
+        d[m + 2] = fmaf(av.z, o, d[m + 2]);
+        d[m + 3] = fmaf(av.w, o, d[m + 3]);
       }
-      sS[c][jj] = acc;
+    }
+    for (int c = 0; c < K; c += 4) {
+      const float s0 = sS[c][lane], s1 = sS[c + 1][lane], s2 = sS[c + 2][lane], s3 = sS[c + 3][lane];
+#pragma unroll
+      for (int m = 0; m < RD; ++m) {
+        const float4 kv = *(const float4*)&sKb[w * RD + m][c];
+        d[m] += kv.x * s0 + kv.y * s1 + kv.z * s2 + kv.w * s3;
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < RD; ++m) {
+      sD[w * RD + m][lane] = d[m];
+      dDc[(int64_t)(w * RD + m) * V + col] = d[m];
+    }
+    __syncthreads();  // dDelta complete; Aqk and Kbar are no longer read
+    stage(sR, (const float*)a.Qt + chb * C * K, C * K);
+    stage(sR + C * K, (const float*)a.W + chb * C * K, C * K);
+    __syncthreads();
+    // dS0 = Diag(gL) dS_L + Qt_s^T dO - W^T dDelta
+#pragma unroll
+    for (int m = 0; m < RS; ++m) ds[m] *= gL[w * RS + m];
+    for (int r = 0; r < L; ++r) {
+      const float o = sO[r][lane], dd = sD[r][lane];
+#pragma unroll
+      for (int m = 0; m < RS; m += 4) {
+        const float4 qv = *(const float4*)&sQt[r][w * RS + m];
+        const float4 wv = *(const float4*)&sW[r][w * RS + m];
+        ds[m] = fmaf(qv.x, o, fmaf(-wv.x, dd, ds[m]));
+        ds[m + 1] = fmaf(qv.y, o, fmaf(-wv.y, dd, ds[m + 1]));
+        ds[m + 2] = fmaf(qv.z, o, fmaf(-wv.z, dd, ds[m + 2]));
+        ds[m + 3] = fmaf(qv.w, o, fmaf(-wv.w, dd, ds[m + 3]));
+      }
     }
   }
-  __syncthreads();
   if (b.dinit)
-    for (int e = tid; e < K * VT; e += kThreads) {
-      const int c = e / VT, jj = e % VT;
-      b.dinit[sbase + (int64_t)c * V + col0 + jj] = sS[c][jj];
-    }
+#pragma unroll
+    for (int m = 0; m < RS; ++m) b.dinit[sbase + (int64_t)(w * RS + m) * V + col] = ds[m];
 }
 
 // Chunk-local gradients.  One workgroup per chunk-head.
-template <typename Tin, int C>
-__global__ __launch_bounds__(kThreads) void k_bwd_chunk(BwdArgs b) {
+//
+// Thread layouts: C x K elements (r, c) are owned as c = tid % K, r = tid / K +
+// (256 / K) m, so a wave shares its rows (broadcast LDS reads) and its lanes
+// hold consecutive channels (coalesced global access); C x C elements (r, i)
+// likewise with i = tid % C (a row's C lanes sit in one wave).  The products
+// over the value dimension (dW, dQ~, dKbar, P, the V half of Y, and dV) run
+// in one pass over 32-column tiles of S0, dS_L, dDelta, dO, Delta and V staged
+// in LDS; everything after that reads LDS only, apart from per-element
+// staging in the gradient outputs' own slots (read back by the same thread).
+template <typename Tin, int C, int K, int NT>
+__global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
+  constexpr int VTL = 32, TS = VTL + 4;  // value tile and its padded row stride
+  constexpr int NE1 = C * K / NT, NE2 = (C * C + NT - 1) / NT;
+  constexpr int RSTEP1 = NT / K, RSTEP2 = NT / C;
+  constexpr int NEV = (C * VTL + NT - 1) / NT;  // dV elements per thread and tile
   const FwdArgs& a = b.f;
-  const int H = a.H, K = a.K, V = a.V;
+  const int H = a.H, V = a.V;
   const int64_t wid = blockIdx.x;
   const int j = (int)(wid / H), h = (int)(wid % H);
   if (j >= *a.nt_dev) return;
@@ -202,7 +280,6 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk(BwdArgs b) {
   const int tok0 = a.chunk_tok[j], L = a.chunk_len[j];
   const int64_t chb = (int64_t)j * H + h;
   auto th = [&](int r) { return (int64_t)(tok0 + r) * H + h; };
-  const float* Tm = a.Tm_out + chb * C * C;
   const float* Akk = a.Akk_out + chb * C * C;
   const float* S0 = b.hc + chb * K * V;
   const float* dSL = b.dhc + chb * K * V;
@@ -212,133 +289,288 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk(BwdArgs b) {
   const Tin* v = (const Tin*)a.v;
   const float scale = a.scale;
 
-  __shared__ float sGam[C][kMaxD];  // gamma (rows >= L repeat gamma_{L-1})
-  __shared__ float sDW[C][kMaxD];   // dW = -dDelta S0^T
-  __shared__ float sT[C][C + 1];    // Tm
-  __shared__ float sP[C][C + 1];    // gradient of the unscaled Aqk (i <= r)
-  __shared__ float sY[C][C + 1];    // Y = dW K~^T + dDelta V^T (i <= r), later dAkk (i < r)
-  __shared__ float sZ[C][C + 1];    // Z = Tm^T dT (b < r)
-  __shared__ float sB[C], sDb[C];   // beta, d(beta)
-  __shared__ float sRed[kMaxD];
+  // LDS: gamma and Tm for the whole kernel; one region reused by phase
+  constexpr int kTiles = C * K + 2 * K * (VTL + 1) + 4 * C * TS;
+  constexpr int kAfter = C * K + 2 * C * (C + 1) + K * (C + 1);
+  constexpr int kRegion = kTiles > kAfter ? kTiles : kAfter;
+  __shared__ float sGam[C][K];
+  __shared__ float sT[C][C + 1];
+  __shared__ __attribute__((aligned(16))) float sReg[kRegion];
+  __shared__ float sB[C], sDb[C], sSd[K], sRed[K];
+  // phase B, first sweep's tiles
+  float (*tS0)[VTL + 1] = (float(*)[VTL + 1])sReg;
+  float (*tdD)[TS] = (float(*)[TS])(sReg + K * (VTL + 1));
+  float (*tdO)[TS] = (float(*)[TS])(sReg + K * (VTL + 1) + C * TS);
+  // after phase B: dW | P | Y (then dAkk) | K~ transposed (then Z); from phase F on,
+  // q^ takes dW's place and k^ K~'s; from phase G on, dgamma and the Kbar term
+  float (*sDW)[K] = (float(*)[K])sReg;
+  float (*sP)[C + 1] = (float(*)[C + 1])(sReg + C * K);
+  float (*sY)[C + 1] = (float(*)[C + 1])(sReg + C * K + C * (C + 1));
+  float* sR4 = sReg + C * K + 2 * C * (C + 1);
+  float (*sKtT)[C + 1] = (float(*)[C + 1])sR4;
+  float (*sZ)[C + 1] = (float(*)[C + 1])sR4;
+  float (*sQn)[K] = (float(*)[K])sReg;
+  float (*sKn)[K] = (float(*)[K])sR4;
+  float (*sDg)[K] = (float(*)[K])sReg;
+  float (*sTk)[K] = (float(*)[K])sR4;
 
-  for (int c = tid; c < K; c += kThreads) {
+  // ---- phase A: gamma, beta, Tm ----
+  for (int c = tid; c < K; c += NT) {
     float acc = 0.f;
-    for (int r = 0; r < C; ++r) {
-      if (r < L) acc += a.g[th(r) * K + c];
-      sGam[r][c] = acc;
+    for (int r0 = 0; r0 < C; r0 += 16) {
+      float gv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) gv[u] = r0 + u < L ? a.g[th(r0 + u) * K + c] : 0.f;
+#pragma unroll
+      for (int u = 0; u < 16; ++u) {
+        acc += gv[u];
+        sGam[r0 + u][c] = acc;
+      }
     }
   }
-  for (int r = tid; r < C; r += kThreads) {
+  for (int r = tid; r < C; r += NT) {
     sB[r] = r < L ? a.bt[th(r)] : 0.f;
     sDb[r] = 0.f;
   }
-  for (int p = tid; p < C * C; p += kThreads) sT[p / C][p % C] = Tm[p];
-  __syncthreads();
+  for (int p = tid; p < C * C; p += NT) sT[p / C][p % C] = a.Tm_out[chb * C * C + p];
 
-  // dW and P
-  for (int p = tid; p < C * K; p += kThreads) {
-    const int r = p / K, c = p % K;
-    float acc = 0.f;
-    if (r < L)
-      for (int jv = 0; jv < V; ++jv) acc = fmaf(dDl[(int64_t)r * V + jv], S0[(int64_t)c * V + jv], acc);
-    sDW[r][c] = -acc;
-  }
-  for (int p = tid; p < C * C; p += kThreads) {
-    const int r = p / C, i = p % C;
-    float acc = 0.f;
-    if (i <= r && r < L)
-      for (int jv = 0; jv < V; ++jv)
-        acc = fmaf(load_f32(dO + th(r) * V + jv), Dl[(int64_t)i * V + jv], acc);
-    sP[r][i] = scale * acc;
-  }
-  __syncthreads();
-
-  // Y[a][i] = sum_c dW[a][c] K~[i][c] + sum_j dDelta[a][j] v[i][j]   (i <= a < L)
-  for (int p = tid; p < C * C; p += kThreads) {
-    const int r = p / C, i = p % C;
-    float acc = 0.f;
-    if (i <= r && r < L) {
-      const float* ki = a.kn + th(i) * K;
-      for (int c = 0; c < K; ++c) acc = fmaf(sDW[r][c], ki[c] * expf(sGam[i][c]), acc);
-      for (int jv = 0; jv < V; ++jv)
-        acc = fmaf(dDl[(int64_t)r * V + jv], load_f32(v + th(i) * V + jv), acc);
+  // ---- phase B: products over the value dimension, and dV, in two sweeps over
+  //      the value tiles (dW and dQ~; then dKbar, P, the V half of Y and dV) so
+  //      that each keeps about 64 accumulators live ----
+  const int c1 = tid % K, rb1 = tid / K;       // C x K layout
+  const int i2 = tid % C, rb2 = tid / C;       // C x C layout
+  Tin* dv = (Tin*)b.dv;
+  {
+    float dw[NE1], dqt[NE1];
+#pragma unroll
+    for (int m = 0; m < NE1; ++m) dw[m] = dqt[m] = 0.f;
+    for (int j0 = 0; j0 < V; j0 += VTL) {
+      __syncthreads();
+      for (int e = tid; e < K * VTL; e += NT) {
+        const int c = e / VTL, jj = e % VTL;
+        tS0[c][jj] = S0[(int64_t)c * V + j0 + jj];
+      }
+      for (int e = tid; e < C * VTL; e += NT) {
+        const int r = e / VTL, jj = e % VTL;
+        tdD[r][jj] = dDl[(int64_t)r * V + j0 + jj];
+        tdO[r][jj] = r < L ? load_f32(dO + th(r) * V + j0 + jj) : 0.f;
+      }
+      __syncthreads();
+      for (int jj = 0; jj < VTL; jj += 4) {
+        const float s0[4] = {tS0[c1][jj], tS0[c1][jj + 1], tS0[c1][jj + 2], tS0[c1][jj + 3]};
+#pragma unroll
+        for (int m = 0; m < NE1; ++m) {
+          const int r = rb1 + RSTEP1 * m;
+          const float4 x = *(const float4*)&tdD[r][jj];
+          const float4 y = *(const float4*)&tdO[r][jj];
+          dw[m] += x.x * s0[0] + x.y * s0[1] + x.z * s0[2] + x.w * s0[3];
+          dqt[m] += y.x * s0[0] + y.y * s0[1] + y.z * s0[2] + y.w * s0[3];
+        }
+      }
     }
-    sY[r][i] = acc;
+    __syncthreads();  // the tiles are dead; dW goes where they were
+#pragma unroll
+    for (int m = 0; m < NE1; ++m) {
+      const int r = rb1 + RSTEP1 * m;
+      sDW[r][c1] = -dw[m];
+      if (r < L) b.dqh[th(r) * K + c1] = scale * dqt[m];  // staged in the element's own slot
+    }
+  }
+  // second sweep: its tiles live in the part of the region above dW
+  float* sReg2 = sReg + C * K;
+  float (*tdSL2)[VTL + 1] = (float(*)[VTL + 1])sReg2;
+  float (*tD2)[TS] = (float(*)[TS])(sReg2 + K * (VTL + 1));
+  float (*tdO2)[TS] = (float(*)[TS])(sReg2 + K * (VTL + 1) + C * TS);
+  float (*tdD2)[TS] = (float(*)[TS])(sReg2 + K * (VTL + 1) + 2 * C * TS);
+  float (*tv2)[TS] = (float(*)[TS])(sReg2 + K * (VTL + 1) + 3 * C * TS);
+  float (*tS02)[VTL + 1] = (float(*)[VTL + 1])(sReg2 + K * (VTL + 1) + 4 * C * TS);
+  float dkb[NE1], pp[NE2], yv[NE2], sd = 0.f;
+#pragma unroll
+  for (int m = 0; m < NE1; ++m) dkb[m] = 0.f;
+#pragma unroll
+  for (int m = 0; m < NE2; ++m) pp[m] = yv[m] = 0.f;
+  for (int j0 = 0; j0 < V; j0 += VTL) {
+    __syncthreads();
+    for (int e = tid; e < K * VTL; e += NT) {
+      const int c = e / VTL, jj = e % VTL;
+      tdSL2[c][jj] = dSL[(int64_t)c * V + j0 + jj];
+      tS02[c][jj] = S0[(int64_t)c * V + j0 + jj];
+    }
+    for (int e = tid; e < C * VTL; e += NT) {
+      const int r = e / VTL, jj = e % VTL;
+      const bool in = r < L;
+      tdD2[r][jj] = dDl[(int64_t)r * V + j0 + jj];
+      tD2[r][jj] = Dl[(int64_t)r * V + j0 + jj];
+      tdO2[r][jj] = in ? load_f32(dO + th(r) * V + j0 + jj) : 0.f;
+      tv2[r][jj] = in ? load_f32(v + th(r) * V + j0 + jj) : 0.f;
+    }
+    __syncthreads();
+    for (int jj = 0; jj < VTL; jj += 4) {
+      const float l0[4] = {tdSL2[c1][jj], tdSL2[c1][jj + 1], tdSL2[c1][jj + 2], tdSL2[c1][jj + 3]};
+      sd += tS02[c1][jj] * l0[0] + tS02[c1][jj + 1] * l0[1] + tS02[c1][jj + 2] * l0[2] +
+            tS02[c1][jj + 3] * l0[3];
+#pragma unroll
+      for (int m = 0; m < NE1; ++m) {
+        const int r = rb1 + RSTEP1 * m;
+        const float4 z = *(const float4*)&tD2[r][jj];
+        dkb[m] += z.x * l0[0] + z.y * l0[1] + z.z * l0[2] + z.w * l0[3];
+      }
+      const float4 di = *(const float4*)&tD2[i2][jj];
+      const float4 vi = *(const float4*)&tv2[i2][jj];
+#pragma unroll
+      for (int m = 0; m < NE2; ++m) {
+        const int r = rb2 + RSTEP2 * m;
+        if (r < C) {
+          const float4 o = *(const float4*)&tdO2[r][jj];
+          const float4 x = *(const float4*)&tdD2[r][jj];
+          pp[m] += o.x * di.x + o.y * di.y + o.z * di.z + o.w * di.w;
+          yv[m] += x.x * vi.x + x.y * vi.y + x.z * vi.z + x.w * vi.w;
+        }
+      }
+    }
+    // dV = Diag(beta) Tm^T dDelta for this tile's columns
+#pragma unroll
+    for (int m = 0; m < NEV; ++m) {
+      const int e = tid + NT * m, r = e / VTL, jj = e % VTL;
+      if (e < C * VTL && r < L) {
+        float acc = 0.f;
+        for (int aa = r; aa < L; ++aa) acc = fmaf(sT[aa][r], tdD2[aa][jj], acc);
+        store_as(dv + th(r) * V + j0 + jj, sB[r] * acc);
+      }
+    }
+  }
+  __syncthreads();  // the tiles are dead
+#pragma unroll
+  for (int m = 0; m < NE1; ++m) {
+    const int r = rb1 + RSTEP1 * m;
+    sKtT[c1][r] = r < L ? a.kn[th(r) * K + c1] * expf(sGam[r][c1]) : 0.f;
+    if (r < L) b.tkb[th(r) * K + c1] = dkb[m];
+  }
+#pragma unroll
+  for (int m = 0; m < NE2; ++m) {
+    const int r = rb2 + RSTEP2 * m;
+    if (r < C) {
+      const bool low = i2 <= r && r < L;
+      sP[r][i2] = low ? scale * pp[m] : 0.f;
+      sY[r][i2] = low ? yv[m] : 0.f;
+    }
+  }
+  if (tid < K) sSd[tid] = sd;
+  __syncthreads();
+
+  // ---- phase C: Y += dW K~^T (i <= r) ----
+#pragma unroll
+  for (int m = 0; m < NE2; ++m) {
+    const int r = rb2 + RSTEP2 * m;
+    if (r < L && i2 <= r) {
+      float acc = 0.f;
+      for (int c = 0; c < K; c += 4) {
+        const float4 dwv = *(const float4*)&sDW[r][c];
+        acc += dwv.x * sKtT[c][i2] + dwv.y * sKtT[c + 1][i2] + dwv.z * sKtT[c + 2][i2] +
+               dwv.w * sKtT[c + 3][i2];
+      }
+      sY[r][i2] += acc;
+    }
   }
   __syncthreads();
 
-  // dbeta, first part: diag(Tm^T Y); Z[r][bb] = beta_bb sum_{a >= r} Tm[a][r] Y[a][bb] (bb < r)
-  for (int r = tid; r < L; r += kThreads) {
+  // ---- phase D: dbeta (first part), Z = Tm^T dT (bb < r), and through dW the
+  //      K~ term of k^ and gamma (staged in the element's own output slots) ----
+  for (int r = tid; r < L; r += NT) {
     float acc = 0.f;
     for (int aa = r; aa < L; ++aa) acc = fmaf(sT[aa][r], sY[aa][r], acc);
     sDb[r] = acc;
   }
-  for (int p = tid; p < C * C; p += kThreads) {
-    const int r = p / C, bb = p % C;
+  float zv[NE2];
+#pragma unroll
+  for (int m = 0; m < NE2; ++m) {
+    const int r = rb2 + RSTEP2 * m;
     float acc = 0.f;
-    if (bb < r && r < L)
-      for (int aa = r; aa < L; ++aa) acc = fmaf(sT[aa][r], sY[aa][bb], acc);
-    sZ[r][bb] = sB[bb] * acc;
+    if (r < L && i2 < r)
+      for (int aa = r; aa < L; ++aa) acc = fmaf(sT[aa][r], sY[aa][i2], acc);
+    zv[m] = sB[i2] * acc;
   }
-  __syncthreads();
-
-  // dN[r][i] = -sum_{bb <= i} Z[r][bb] Tm[i][bb] (i < r); dAkk = beta_r dN -> sY;
-  // dbeta, second part: sum_i dN[r][i] Akk[r][i]
-  for (int r = tid; r < C; r += kThreads) {
-    float db = 0.f;
-    for (int i = 0; i < C; ++i) {
-      float dAkk = 0.f;
-      if (i < r && r < L) {
-        float dn = 0.f;
-        for (int bb = 0; bb <= i; ++bb) dn = fmaf(-sZ[r][bb], sT[i][bb], dn);
-        db = fmaf(dn, Akk[(int64_t)r * C + i], db);
-        dAkk = sB[r] * dn;
-      }
-      sY[r][i] = dAkk;
+#pragma unroll
+  for (int m = 0; m < NE1; ++m) {
+    const int r = rb1 + RSTEP1 * m;
+    if (r < L) {
+      float dxk = 0.f;
+      for (int aa = r; aa < L; ++aa) dxk = fmaf(sT[aa][r], sDW[aa][c1], dxk);
+      const float e = expf(sGam[r][c1]) * sB[r] * dxk;
+      b.dkh[th(r) * K + c1] = e;
+      b.dgam[th(r) * K + c1] = a.kn[th(r) * K + c1] * e;
     }
-    sDb[r] += db;
+  }
+  __syncthreads();  // K~ and dW are dead: Z and q^ take their places
+#pragma unroll
+  for (int m = 0; m < NE2; ++m) {
+    const int r = rb2 + RSTEP2 * m;
+    if (r < C) sZ[r][i2] = zv[m];
+  }
+  for (int e = tid; e < C * K / 4; e += NT) {
+    const int r = e / (K / 4), c4 = e % (K / 4);
+    ((float4*)&sQn[r][0])[c4] = r < L ? ((const float4*)(a.qn + th(r) * K))[c4]
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __syncthreads();
 
-  // per element (r, c): the gradients of q^, k^ and gamma
-  for (int p = tid; p < L * K; p += kThreads) {
-    const int r = p / K, c = p % K;
-    const float q = a.qn[th(r) * K + c], kk = a.kn[th(r) * K + c];
+  // ---- phase E: dN = -Z Tm^T (i < r), dAkk = beta_r dN -> sY; dbeta (second part) ----
+  float dak[NE2];
+#pragma unroll
+  for (int m = 0; m < NE2; ++m) {
+    const int r = rb2 + RSTEP2 * m;
+    float dn = 0.f;
+    if (r < L && i2 < r)
+      for (int bb = 0; bb <= i2; ++bb) dn = fmaf(-sZ[r][bb], sT[i2][bb], dn);
+    float part = (r < L && i2 < r) ? dn * Akk[(int64_t)r * C + i2] : 0.f;
+#pragma unroll
+    for (int off = C / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+    if (r < C && i2 == 0) sDb[r] += part;
+    dak[m] = (r < C) ? sB[r < C ? r : 0] * dn : 0.f;
+  }
+  __syncthreads();  // Z is dead: k^ takes its place; dAkk replaces Y
+#pragma unroll
+  for (int m = 0; m < NE2; ++m) {
+    const int r = rb2 + RSTEP2 * m;
+    if (r < C) sY[r][i2] = dak[m];
+  }
+  for (int e = tid; e < C * K / 4; e += NT) {
+    const int r = e / (K / 4), c4 = e % (K / 4);
+    ((float4*)&sKn[r][0])[c4] = r < L ? ((const float4*)(a.kn + th(r) * K))[c4]
+                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  __syncthreads();
+
+  // ---- phase F: per element (r, c), the gradients of q^, k^ and gamma ----
+  for (int m = 0; m < NE1; ++m) {
+    const int r = rb1 + RSTEP1 * m, c = c1;
+    if (r >= L) continue;
+    const float q = sQn[r][c], kk = sKn[r][c];
     const float gm = sGam[r][c], egm = expf(gm), ekb = expf(sGam[L - 1][c] - gm);
-    float dqt = 0.f, dkb = 0.f;
-    for (int jv = 0; jv < V; ++jv) {
-      const float s0 = S0[(int64_t)c * V + jv];
-      dqt = fmaf(load_f32(dO + th(r) * V + jv), s0, dqt);
-      dkb = fmaf(Dl[(int64_t)r * V + jv], dSL[(int64_t)c * V + jv], dkb);
-    }
-    dqt *= scale;
-    float dxk = 0.f;
-    for (int aa = r; aa < L; ++aa) dxk = fmaf(sT[aa][r], sDW[aa][c], dxk);
-    const float dkt = sB[r] * dxk;
+    const float dq_t = b.dqh[th(r) * K + c], dk_b = b.tkb[th(r) * K + c];
+    const float dk0 = b.dkh[th(r) * K + c], dg0 = b.dgam[th(r) * K + c];
     float r1 = 0.f, r2 = 0.f;
     for (int i = 0; i <= r; ++i) {
-      const float ke = a.kn[th(i) * K + c] * expf(gm - sGam[i][c]);
+      const float ke = sKn[i][c] * expf(gm - sGam[i][c]);
       r1 = fmaf(sP[r][i], ke, r1);
-      r2 = fmaf(sY[r][i], ke, r2);  // zero on the diagonal
+      r2 = fmaf(sY[r][i], ke, r2);
     }
     float c12 = 0.f;
     for (int rr = r; rr < L; ++rr) {
       const float e = expf(sGam[rr][c] - gm);
-      c12 = fmaf(sP[rr][r] * a.qn[th(rr) * K + c] + sY[rr][r] * a.kn[th(rr) * K + c], e, c12);
+      c12 = fmaf(sP[rr][r] * sQn[rr][c] + sY[rr][r] * sKn[rr][c], e, c12);
     }
-    const float tkb = kk * ekb * dkb;
-    b.dqh[th(r) * K + c] = egm * dqt + r1;
-    b.dkh[th(r) * K + c] = egm * dkt + ekb * dkb + r2 + c12;
-    b.dgam[th(r) * K + c] = q * egm * dqt + kk * egm * dkt - tkb + q * r1 + kk * r2 - kk * c12;
+    const float tkb = kk * ekb * dk_b;
+    b.dqh[th(r) * K + c] = egm * dq_t + r1;
+    b.dkh[th(r) * K + c] = dk0 + ekb * dk_b + r2 + c12;
+    b.dgam[th(r) * K + c] = dg0 + q * egm * dq_t - tkb + q * r1 + kk * r2 - kk * c12;
     b.tkb[th(r) * K + c] = tkb;
   }
-  // dV = Diag(beta) Tm^T dDelta
-  Tin* dv = (Tin*)b.dv;
-  for (int p = tid; p < L * V; p += kThreads) {
-    const int r = p / V, jv = p % V;
-    float acc = 0.f;
-    for (int aa = r; aa < L; ++aa) acc = fmaf(sT[aa][r], dDl[(int64_t)aa * V + jv], acc);
-    store_as(dv + th(r) * V + jv, sB[r] * acc);
+  __syncthreads();  // q^, k^ are dead
+  for (int m = 0; m < NE1; ++m) {
+    const int r = rb1 + RSTEP1 * m;
+    sDg[r][c1] = r < L ? b.dgam[th(r) * K + c1] : 0.f;
+    sTk[r][c1] = r < L ? b.tkb[th(r) * K + c1] : 0.f;
   }
   __syncthreads();
 
@@ -346,34 +578,41 @@ __global__ __launch_bounds__(kThreads) void k_bwd_chunk(BwdArgs b) {
   // the state decay), then through the gate
   Tin* dgate = (Tin*)b.dgate;
   const Tin* gate = (const Tin*)a.gate;
-  for (int c = tid; c < K; c += kThreads) {
+  for (int c = tid; c < K; c += NT) {
     float cst = 0.f;
-    for (int r = 0; r < L; ++r) cst += b.tkb[th(r) * K + c];
-    float sd = 0.f;
-    for (int jv = 0; jv < V; ++jv) sd = fmaf(dSL[(int64_t)c * V + jv], S0[(int64_t)c * V + jv], sd);
-    cst = fmaf(expf(sGam[L - 1][c]), sd, cst);
+    for (int r = 0; r < L; ++r) cst += sTk[r][c];
+    cst = fmaf(expf(sGam[L - 1][c]), sSd[c], cst);
     float run = cst, ddt = 0.f, da = 0.f;
     const float alog = a.a_log[h], db = a.dt_bias[(int64_t)h * K + c];
-    for (int r = L - 1; r >= 0; --r) {
-      run += b.dgam[th(r) * K + c];
-      float gx, ga;
-      gate_grad(load_f32(gate + th(r) * K + c) + db, alog, a.gate_form, a.lb, &gx, &ga);
-      const float dg = run * gx;
-      store_as(dgate + th(r) * K + c, dg);
-      ddt += dg;
-      da = fmaf(run, ga, da);
+    for (int r1 = C - 16; r1 >= 0; r1 -= 16) {
+      if (r1 >= L) continue;
+      float gv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) gv[u] = r1 + u < L ? load_f32(gate + th(r1 + u) * K + c) : 0.f;
+#pragma unroll
+      for (int u = 15; u >= 0; --u) {
+        const int r = r1 + u;
+        if (r >= L) continue;
+        run += sDg[r][c];
+        float gx, ga;
+        gate_grad(gv[u] + db, alog, a.gate_form, a.lb, &gx, &ga);
+        const float dg = run * gx;
+        store_as(dgate + th(r) * K + c, dg);
+        ddt += dg;
+        da = fmaf(run, ga, da);
+      }
     }
     b.ddt_part[chb * K + c] = ddt;
     sRed[c] = da;
   }
   // beta logit
   Tin* dbeta = (Tin*)b.dbeta;
-  for (int r = tid; r < L; r += kThreads) store_as(dbeta + th(r), sDb[r] * sB[r] * (1.f - sB[r]));
+  for (int r = tid; r < L; r += NT) store_as(dbeta + th(r), sDb[r] * sB[r] * (1.f - sB[r]));
   __syncthreads();
   if (tid == 0) {
-    float s = 0.f;
-    for (int c = 0; c < K; ++c) s += sRed[c];
-    b.da_part[chb] = s;
+    float acc = 0.f;
+    for (int c = 0; c < K; ++c) acc += sRed[c];
+    b.da_part[chb] = acc;
   }
 }
 
@@ -438,18 +677,22 @@ hipError_t run(const BwdArgs& b, hipStream_t s) {
   const FwdArgs& a = b.f;
   hipError_t e = launch_valu_prep(a, s);
   if (e != hipSuccess) return e;
-  constexpr int VT = 32;
-  const int64_t wgs = (int64_t)a.N * a.H * (a.V / VT);
+  const int64_t wgs = (int64_t)a.N * a.H * (a.V / 64);
   if (wgs > 0) {
     if (a.NT > 0) {
-      hipLaunchKernelGGL((k_bwd_fstate<C, VT>), dim3((unsigned)wgs), dim3(kThreads), 0, s, b);
+      if (a.K == 64) hipLaunchKernelGGL((k_bwd_fstate<C, 64>), dim3((unsigned)wgs), dim3(kThreads), 0, s, b);
+      else hipLaunchKernelGGL((k_bwd_fstate<C, 128>), dim3((unsigned)wgs), dim3(kThreads), 0, s, b);
       if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
-    hipLaunchKernelGGL((k_bwd_dstate<Tin, C, VT>), dim3((unsigned)wgs), dim3(kThreads), 0, s, b);
+    if (a.K == 64) hipLaunchKernelGGL((k_bwd_dstate<Tin, C, 64>), dim3((unsigned)wgs), dim3(kThreads), 0, s, b);
+    else hipLaunchKernelGGL((k_bwd_dstate<Tin, C, 128>), dim3((unsigned)wgs), dim3(kThreads), 0, s, b);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   if (a.NT > 0) {
-    hipLaunchKernelGGL((k_bwd_chunk<Tin, C>), dim3((unsigned)((int64_t)a.NT * a.H)), dim3(kThreads), 0, s, b);
+    const dim3 grid((unsigned)((int64_t)a.NT * a.H));
+    constexpr int T64 = chunk_threads(C, 64), T128 = chunk_threads(C, 128);
+    if (a.K == 64) hipLaunchKernelGGL((k_bwd_chunk<Tin, C, 64, T64>), grid, dim3(T64), 0, s, b);
+    else hipLaunchKernelGGL((k_bwd_chunk<Tin, C, 128, T128>), grid, dim3(T128), 0, s, b);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   const int64_t tk = (int64_t)a.B * a.T * a.HK;
