@@ -70,18 +70,24 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
-// Copy n floats (n a multiple of 4, 16-byte aligned) from global memory to LDS.
-__device__ inline void stage(float* dst, const float* src, int n) {
-  for (int e = threadIdx.x; e < n / 4; e += kThreads) ((float4*)dst)[e] = ((const float4*)src)[e];
+// Copy n floats (n a multiple of 4, 16-byte aligned) from global memory to LDS
+// with a workgroup of nt threads.
+__device__ inline void stage(float* dst, const float* src, int n, int nt) {
+  for (int e = threadIdx.x; e < n / 4; e += nt) ((float4*)dst)[e] = ((const float4*)src)[e];
 }
+
+// Waves per workgroup of the state passes: two per SIMD where the row groups
+// (C/NW rows of Delta per wave) stay multiples of four.
+constexpr int state_waves(int C) { return C >= 32 ? 8 : 4; }
 
 // Forward state pass keeping S0 and Delta of every chunk.  One workgroup per
 // (sequence, head, tile of 64 columns): lane = column, wave w owns the state
 // rows [w K/4, (w+1) K/4) in registers; W and Kbar of each chunk are staged in
 // LDS and read as float4 broadcasts.
 template <int C, int K>
-__global__ __launch_bounds__(kThreads) void k_bwd_fstate(BwdArgs b) {
-  constexpr int VT = 64, RS = K / 4, RD = C / 4;
+__global__ __launch_bounds__(64 * state_waves(C)) void k_bwd_fstate(BwdArgs b) {
+  constexpr int NW = state_waves(C), NT = 64 * NW;
+  constexpr int VT = 64, RS = K / NW, RD = C / NW;
   const FwdArgs& a = b.f;
   const int H = a.H, V = a.V;
   const int ntile = V / VT;
@@ -111,8 +117,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_fstate(BwdArgs b) {
     float* Dc = b.Dc + chb * C * V;
     const int L = a.chunk_len[j];
     __syncthreads();  // the previous chunk is done with sW, sKb; sS holds the state
-    stage(&sW[0][0], (const float*)a.W + chb * C * K, C * K);
-    stage(&sKb[0][0], (const float*)a.Kb + chb * C * K, C * K);
+    stage(&sW[0][0], (const float*)a.W + chb * C * K, C * K, NT);
+    stage(&sKb[0][0], (const float*)a.Kb + chb * C * K, C * K, NT);
 #pragma unroll
     for (int m = 0; m < RS; ++m) hc[(int64_t)(w * RS + m) * V + col] = st[m];
     __syncthreads();
@@ -157,8 +163,9 @@ __global__ __launch_bounds__(kThreads) void k_bwd_fstate(BwdArgs b) {
 // gradient.  Same layout as the forward pass; Aqk and Kbar, then Qt and W,
 // take turns in one LDS region.
 template <typename Tin, int C, int K>
-__global__ __launch_bounds__(kThreads) void k_bwd_dstate(BwdArgs b) {
-  constexpr int VT = 64, RS = K / 4, RD = C / 4;
+__global__ __launch_bounds__(64 * state_waves(C)) void k_bwd_dstate(BwdArgs b) {
+  constexpr int NW = state_waves(C), NT = 64 * NW;
+  constexpr int VT = 64, RS = K / NW, RD = C / NW;
   const FwdArgs& a = b.f;
   const int H = a.H, V = a.V;
   const int ntile = V / VT;
@@ -199,8 +206,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dstate(BwdArgs b) {
       const int r = w * RD + m;
       sO[r][lane] = r < L ? load_f32(dO + ((int64_t)(tok0 + r) * H + h) * V + col) : 0.f;
     }
-    stage(sR, (const float*)a.Aqk + chb * C * C, C * C);
-    stage(sR + C * C, (const float*)a.Kb + chb * C * K, C * K);
+    stage(sR, (const float*)a.Aqk + chb * C * C, C * C, NT);
+    stage(sR + C * C, (const float*)a.Kb + chb * C * K, C * K, NT);
     __syncthreads();
     // dDelta = Aqk_s^T dO + Kbar dS_L (Aqk_s is zero above the diagonal)
     float d[RD];
@@ -231,8 +238,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_dstate(BwdArgs b) {
       dDc[(int64_t)(w * RD + m) * V + col] = d[m];
     }
     __syncthreads();  // dDelta complete; Aqk and Kbar are no longer read
-    stage(sR, (const float*)a.Qt + chb * C * K, C * K);
-    stage(sR + C * K, (const float*)a.W + chb * C * K, C * K);
+    stage(sR, (const float*)a.Qt + chb * C * K, C * K, NT);
+    stage(sR + C * K, (const float*)a.W + chb * C * K, C * K, NT);
     __syncthreads();
     // dS0 = Diag(gL) dS_L + Qt_s^T dO - W^T dDelta
 #pragma unroll
@@ -680,12 +687,14 @@ hipError_t run(const BwdArgs& b, hipStream_t s) {
   const int64_t wgs = (int64_t)a.N * a.H * (a.V / 64);
   if (wgs > 0) {
     if (a.NT > 0) {
-      if (a.K == 64) hipLaunchKernelGGL((k_bwd_fstate<C, 64>), dim3((unsigned)wgs), dim3(kThreads), 0, s, b);
-      else hipLaunchKernelGGL((k_bwd_fstate<C, 128>), dim3((unsigned)wgs), dim3(kThreads), 0, s, b);
+      constexpr int NTS = 64 * state_waves(C);
+      if (a.K == 64) hipLaunchKernelGGL((k_bwd_fstate<C, 64>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
+      else hipLaunchKernelGGL((k_bwd_fstate<C, 128>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
       if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
     }
-    if (a.K == 64) hipLaunchKernelGGL((k_bwd_dstate<Tin, C, 64>), dim3((unsigned)wgs), dim3(kThreads), 0, s, b);
-    else hipLaunchKernelGGL((k_bwd_dstate<Tin, C, 128>), dim3((unsigned)wgs), dim3(kThreads), 0, s, b);
+    constexpr int NTS = 64 * state_waves(C);
+    if (a.K == 64) hipLaunchKernelGGL((k_bwd_dstate<Tin, C, 64>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
+    else hipLaunchKernelGGL((k_bwd_dstate<Tin, C, 128>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   if (a.NT > 0) {

@@ -85,7 +85,8 @@ __global__ __launch_bounds__(kThreads) void k_prologue_valu(
   if (lane == 0) bt[th] = sigmoid_f(load_f32(beta + th));
 }
 
-// One workgroup per chunk-head (flattened j*H + h).
+// One workgroup per chunk-head (flattened j*H + h).  gamma's rows are padded
+// to K+1 floats: the pairwise products read gamma of row i with lanes over i.
 template <typename Tin, int C>
 __global__ __launch_bounds__(kThreads) void k_chunk_valu(FwdArgs a) {
   const int H = a.H, K = a.K, V = a.V;
@@ -95,7 +96,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_valu(FwdArgs a) {
   const int tid = threadIdx.x;
   const int tok0 = a.chunk_tok[j], L = a.chunk_len[j];
 
-  __shared__ float sG[C][kMaxD];   // gamma, later X = beta k^ exp(gamma)
+  __shared__ float sG[C][kMaxD + 1];  // gamma, later X = beta k^ exp(gamma)
   __shared__ float sA[C][C + 1];   // Akk, then Tm in place
   __shared__ float sRow[C];
   __shared__ float sB[C];
