@@ -83,3 +83,76 @@ def test_workload3_repeatable_bitwise():
     a = gpu_fwd(inp)
     b = gpu_fwd(inp)
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+
+
+def test_workload3_short_conv_sampled():
+    """The forward after the width-4 short convolution with bias (the benchmark's
+    short_conv configuration) at full size; sampled (row, head) pairs against
+    the oracle's convolution + forward over their full length.  The convolution
+    is per channel, so cutting the sampled heads' channels is exact."""
+    import oracle
+    w = synthetic.WORKLOADS[3]
+    _banner("workload 3 after the short convolution")
+    inp = synthetic.make_inputs(w, DEV)
+    chans = (w.H * w.K, w.H * w.K, w.H * w.V)
+    ws_, bs_ = synthetic.short_conv_params(123, chans, 4, True, device=DEV)
+    o, fin = kda.kda_fwd_short_conv(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"],
+                                    inp["a_log"], inp["dt_bias"], ws_, bs_, scale=w.scale,
+                                    output_final_state=True)
+    torch.cuda.synchronize()
+    rows, heads = [0, 3], [0, 17, 31]
+
+    def cut(t, D):
+        x = to_np(t[rows][:, :, heads])
+        return x
+
+    def wcut(wt, D):
+        wt = to_np(wt)
+        return np.concatenate([wt[h * D:(h + 1) * D] for h in heads])
+
+    qc = oracle.short_conv_silu(cut(inp["q"], w.K), wcut(ws_[0], w.K), wcut(bs_[0], w.K))
+    kc = oracle.short_conv_silu(cut(inp["k"], w.K), wcut(ws_[1], w.K), wcut(bs_[1], w.K))
+    vc = oracle.short_conv_silu(cut(inp["v"], w.V), wcut(ws_[2], w.V), wcut(bs_[2], w.V))
+    o_ref, f_ref = oracle.kda_fwd(qc, kc, vc, cut(inp["gate"], w.K), to_np(inp["beta"][rows][:, :, heads]),
+                                  to_np(inp["a_log"][heads]), to_np(inp["dt_bias"][heads]),
+                                  scale=w.scale)
+    got_o = to_np(o[rows][:, :, heads])
+    print("workload 3 + short conv o errors (max-abs, rel-F):", errors(got_o, o_ref), flush=True)
+    assert_close(got_o, o_ref, torch.bfloat16, "o")
+    assert_close(to_np(fin[rows][:, heads]), f_ref, torch.bfloat16, "final_state")
+
+
+def test_workload3_backward_sampled():
+    """The backward at full size (the benchmark's backward configuration); every
+    row of two heads against the oracle's reverse mode over the full length, so
+    the gate-parameter gradients (sums over rows) are compared too.  Tolerance
+    as for the backward's other bf16 tests: per tensor, max-abs within 2e-2 of
+    its largest magnitude and relative Frobenius 1e-2."""
+    import oracle
+    w = synthetic.WORKLOADS[3]
+    _banner("workload 3 backward")
+    inp = synthetic.make_inputs(w, DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7)
+    d_o = torch.randn(w.B, w.T, w.H, w.V, generator=gen, device=DEV).to(w.torch_dtype)
+    got = kda.kda_bwd(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"], inp["a_log"],
+                      inp["dt_bias"], d_o, None, scale=w.scale)
+    torch.cuda.synchronize()
+    heads = [0, 31]
+    cut = lambda t: to_np(t[:, :, heads])
+    ref = oracle.kda_bwd(cut(inp["q"]), cut(inp["k"]), cut(inp["v"]), cut(inp["gate"]),
+                         cut(inp["beta"]), to_np(inp["a_log"][heads]),
+                         to_np(inp["dt_bias"][heads]), cut(d_o), None, scale=w.scale,
+                         threads=8)
+    sel = {"dq": cut(got["dq"]), "dk": cut(got["dk"]), "dv": cut(got["dv"]),
+           "dgate": cut(got["dgate"]), "dbeta": to_np(got["dbeta"][:, :, heads]),
+           "da_log": to_np(got["da_log"][heads]), "ddt_bias": to_np(got["ddt_bias"][heads]),
+           "dinit": to_np(got["dinit"][:, heads])}
+    for n, g in sel.items():
+        r = ref[n]
+        scale_ = max(1.0, float(np.abs(r).max()))
+        err = float(np.abs(g - r).max())
+        rf = float(np.linalg.norm(g - r) / max(1e-30, np.linalg.norm(r)))
+        print("workload 3 backward %s: max-abs %.3g (scale %.3g) rel-F %.3g" % (n, err, scale_, rf),
+              flush=True)
+        assert err <= 2e-2 * scale_ and rf <= 1e-2, n
