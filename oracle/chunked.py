@@ -18,6 +18,15 @@ chunk-local inclusive cumulative sum of the log-decay g (a K-vector per row):
 It uses numpy's matmul and solve as steps and nothing else; it takes its
 q^/k^/g/beta from the oracle's prologue.  It is not used as a parity
 reference for the GPU path.
+
+``kda_bwd_chunked`` is the reverse mode of the same chunk algebra (the
+decomposition the GPU backward follows): a forward pass keeping each chunk's
+entering state S0 and Delta, a reverse pass over chunks carrying the state
+gradient (dDelta = scale Aqk^T dO + Kbar dS_L, dS0 = scale Q~^T dO +
+e^gamma_L dS_L - W^T dDelta), and per chunk the gradients through Tinv, the WY
+factors and the pairwise decayed products.  It returns the gradients of
+q^, k^, v, g, beta and the initial state and is pinned against finite
+differences of the token recurrence.
 """
 from __future__ import annotations
 
@@ -66,3 +75,98 @@ def kda_fwd_chunked(qn, kn, v, g, b, scale, chunk_size, cu_seqlens=None, initial
                 o[row, c0:c1, h] = O
             fin[n, h] = S
     return o, fin
+
+
+def kda_bwd_chunked(qn, kn, v, g, b, d_o, d_final, scale, chunk_size, cu_seqlens=None,
+                    initial_state=None):
+    """Gradients of sum(d_o * O) + sum(d_final * S_final) for the chunked
+    forward with respect to qn, kn, v, g, b ([B,T,H,*]) and the initial state
+    ([N,H,K,V]).  Returns a dict dqn, dkn, dv, dg, db, dinit."""
+    B, T, H, K = qn.shape
+    V = v.shape[-1]
+    C = chunk_size
+    seqs = [(bb, 0, T) for bb in range(B)] if cu_seqlens is None else \
+        [(0, int(cu_seqlens[n]), int(cu_seqlens[n + 1])) for n in range(len(cu_seqlens) - 1)]
+    N = len(seqs)
+    out = dict(dqn=np.zeros(qn.shape), dkn=np.zeros(kn.shape), dv=np.zeros(v.shape),
+               dg=np.zeros(g.shape), db=np.zeros(b.shape), dinit=np.zeros((N, H, K, V)))
+    for n, (bb, t0, t1) in enumerate(seqs):
+        for h in range(H):
+            chunks = []
+            for s0 in range(t0, t1, C):
+                e0 = min(s0 + C, t1)
+                L = e0 - s0
+                q_, k_, v_ = qn[bb, s0:e0, h], kn[bb, s0:e0, h], v[bb, s0:e0, h]
+                gam = np.cumsum(g[bb, s0:e0, h], axis=0)
+                b_ = b[bb, s0:e0, h]
+                lower = np.tril(np.ones((L, L), bool), 0)
+                strict = np.tril(np.ones((L, L), bool), -1)
+                diff = gam[:, None, :] - gam[None, :, :]
+                E = np.where(lower[:, :, None], np.exp(np.where(lower[:, :, None], diff, 0.0)), 0.0)
+                Akk = np.einsum("rc,ic,ric->ri", k_, k_, E) * strict
+                Aqk = np.einsum("rc,ic,ric->ri", q_, k_, E) * lower
+                Tm = np.linalg.inv(np.eye(L) + b_[:, None] * Akk)
+                Kt, Qt = k_ * np.exp(gam), q_ * np.exp(gam)
+                gL = gam[-1]
+                Kb = k_ * np.exp(gL[None] - gam)
+                W, U = Tm @ (b_[:, None] * Kt), Tm @ (b_[:, None] * v_)
+                chunks.append(dict(s=s0, e=e0, L=L, q=q_, k=k_, v=v_, gam=gam, b=b_, E=E, Akk=Akk,
+                                   Aqk=Aqk, Tm=Tm, Kt=Kt, Qt=Qt, gL=gL, Kb=Kb, W=W, U=U,
+                                   lower=lower, strict=strict))
+            S = initial_state[n, h].copy() if initial_state is not None else np.zeros((K, V))
+            for P in chunks:
+                P["S0"] = S.copy()
+                P["D"] = P["U"] - P["W"] @ S
+                S = np.exp(P["gL"])[:, None] * S + P["Kb"].T @ P["D"]
+            dS = d_final[n, h].copy() if d_final is not None else np.zeros((K, V))
+            for P in reversed(chunks):
+                dO = d_o[bb, P["s"]:P["e"], h]
+                P["dSL"] = dS.copy()
+                P["dD"] = scale * P["Aqk"].T @ dO + P["Kb"] @ dS
+                dS = scale * P["Qt"].T @ dO + np.exp(P["gL"])[:, None] * dS - P["W"].T @ P["dD"]
+            out["dinit"][n, h] = dS
+            for P in chunks:
+                dO = d_o[bb, P["s"]:P["e"], h]
+                q_, k_, E, S0, dSL, D, dD = P["q"], P["k"], P["E"], P["S0"], P["dSL"], P["D"], P["dD"]
+                dq = np.zeros_like(q_)
+                dk = np.zeros_like(k_)
+                dgam = np.zeros_like(q_)
+                # Aqk (incl. diagonal) and the Q~ S0 term of O
+                dAqk = np.where(P["lower"], scale * dO @ D.T, 0.0)
+                Em = np.where(P["lower"][:, :, None], E, 0.0)
+                dq += np.einsum("ri,ic,ric->rc", dAqk, k_, Em)
+                dk += np.einsum("ri,rc,ric->ic", dAqk, q_, Em)
+                t = np.einsum("ri,rc,ic,ric->ric", dAqk, q_, k_, Em)
+                dgam += t.sum(1) - t.sum(0)
+                dQt = scale * dO @ S0.T
+                dq += dQt * np.exp(P["gam"])
+                dgam += dQt * P["Qt"]
+                # S_L = e^gamma_L S0 + Kbar^T Delta
+                dKb = D @ dSL.T
+                dk += dKb * np.exp(P["gL"][None] - P["gam"])
+                tt = dKb * P["Kb"]
+                dgam -= tt
+                dgam[-1] += tt.sum(0) + np.exp(P["gL"]) * (dSL * S0).sum(1)
+                # W, U through Tinv
+                dW, dU = -dD @ S0.T, dD
+                Xk, Xv = P["b"][:, None] * P["Kt"], P["b"][:, None] * P["v"]
+                dT = dW @ Xk.T + dU @ Xv.T
+                dXk, dXv = P["Tm"].T @ dW, P["Tm"].T @ dU
+                out["dv"][bb, P["s"]:P["e"], h] = P["b"][:, None] * dXv
+                db = (dXk * P["Kt"]).sum(1) + (dXv * P["v"]).sum(1)
+                dKt = P["b"][:, None] * dXk
+                dk += dKt * np.exp(P["gam"])
+                dgam += dKt * P["Kt"]
+                dN = -P["Tm"].T @ dT @ P["Tm"].T
+                dAkk = np.where(P["strict"], P["b"][:, None] * dN, 0.0)
+                db += np.where(P["strict"], dN * P["Akk"], 0.0).sum(1)
+                Es = np.where(P["strict"][:, :, None], E, 0.0)
+                dk += np.einsum("ri,ic,ric->rc", dAkk, k_, Es)
+                dk += np.einsum("ri,rc,ric->ic", dAkk, k_, Es)
+                t = np.einsum("ri,rc,ic,ric->ric", dAkk, k_, k_, Es)
+                dgam += t.sum(1) - t.sum(0)
+                out["dqn"][bb, P["s"]:P["e"], h] = dq
+                out["dkn"][bb, P["s"]:P["e"], h] = dk
+                out["dg"][bb, P["s"]:P["e"], h] = np.cumsum(dgam[::-1], 0)[::-1]
+                out["db"][bb, P["s"]:P["e"], h] = db
+    return out

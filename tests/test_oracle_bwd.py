@@ -125,3 +125,45 @@ def test_no_update_no_decay_closed_form():
         jac = np.eye(K) / nr - np.outer(x, x) / nr ** 3
         dqn = scale * S0[0, 0] @ d_o[0, t, 0]
         np.testing.assert_allclose(g["dq"][0, t, 0], jac @ dqn, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("C,lengths", [(4, None), (3, [5, 0, 1, 6])])
+def test_chunked_backward_matches_finite_differences_of_the_recurrence(C, lengths):
+    """The chunked reverse mode (the decomposition of the GPU backward) against
+    central differences of the token recurrence, for the normalised inputs,
+    the log-decay, beta and the initial state."""
+    from oracle import chunked
+    rng = np.random.default_rng(8)
+    B, H, K, V = (2, 2, 3, 2) if lengths is None else (1, 1, 3, 2)
+    T = 9 if lengths is None else sum(lengths)
+    cu = None if lengths is None else np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    N = B if cu is None else len(lengths)
+    x = dict(qn=rng.standard_normal((B, T, H, K)), kn=rng.standard_normal((B, T, H, K)) * 0.6,
+             v=rng.standard_normal((B, T, H, V)), g=-np.log1p(np.exp(rng.standard_normal((B, T, H, K)))),
+             b=1 / (1 + np.exp(-rng.standard_normal((B, T, H)))),
+             init=rng.standard_normal((N, H, K, V)))
+    d_o = rng.standard_normal((B, T, H, V))
+    d_fin = rng.standard_normal((N, H, K, V))
+    scale = 0.8
+
+    def loss():
+        o, fin = oracle.recurrence(x["qn"], x["kn"], x["v"], x["g"], x["b"], scale, cu_seqlens=cu,
+                                   initial_state=x["init"], threads=1)
+        return float(np.sum(o * d_o) + np.sum(fin * d_fin))
+
+    got = chunked.kda_bwd_chunked(x["qn"], x["kn"], x["v"], x["g"], x["b"], d_o, d_fin, scale, C,
+                                  cu_seqlens=cu, initial_state=x["init"])
+    names = {"qn": "dqn", "kn": "dkn", "v": "dv", "g": "dg", "b": "db", "init": "dinit"}
+    h = 1e-6
+    for name, key in names.items():
+        arr = x[name]
+        fd = np.zeros_like(arr)
+        for idx in np.ndindex(arr.shape):
+            keep = arr[idx]
+            arr[idx] = keep + h
+            lp = loss()
+            arr[idx] = keep - h
+            lm = loss()
+            arr[idx] = keep
+            fd[idx] = (lp - lm) / (2 * h)
+        np.testing.assert_allclose(got[key], fd, rtol=1e-6, atol=1e-7, err_msg=name)
