@@ -98,7 +98,6 @@ __global__ __launch_bounds__(kThreads) void k_chunk_valu(FwdArgs a) {
 
   __shared__ float sG[C][kMaxD + 1];  // gamma, later X = beta k^ exp(gamma)
   __shared__ float sA[C][C + 1];   // Akk, then Tm in place
-  __shared__ float sRow[C];
   __shared__ float sB[C];
 
   auto tok_off = [&](int r) { return ((int64_t)(tok0 + r) * H + h); };
@@ -136,16 +135,55 @@ __global__ __launch_bounds__(kThreads) void k_chunk_valu(FwdArgs a) {
   }
   __syncthreads();
 
-  // Tm = (I + Diag(beta) Akk)^-1, row by row: Tm_r = e_r - beta_r sum_{i<r} Akk_ri Tm_i
-  for (int r = 0; r < C; ++r) {
-    if (tid < r) sRow[tid] = sA[r][tid];
+  // Tm = (I + Diag(beta) Akk)^-1 in 16 x 16 blocks.  Diagonal blocks: lane s of
+  // wave b solves column s of block b by forward substitution (independent
+  // lanes, no barriers).  Off-diagonal blocks, block row by block row:
+  // Tm_RI = -Tm_RR Diag(beta_R) sum_{I <= J < R} Akk_RJ Tm_JI.
+  {
+    constexpr int NB = C / 16;
+    __shared__ float sM[NB > 1 ? NB - 1 : 1][16][17];
+    const int wv = tid >> 6, ln = tid & 63;
+    float col[16];
+    if (wv < NB && ln < 16) {
+      const int o = 16 * wv;
+#pragma unroll
+      for (int t = 0; t < 16; ++t) {
+        float x = t == ln ? 1.f : 0.f;
+        if (t > ln) {
+          float acc = 0.f;
+          for (int u = ln; u < t; ++u) acc = fmaf(sA[o + t][o + u], col[u], acc);
+          x = -sB[o + t] * acc;
+        }
+        col[t] = x;
+      }
+    }
     __syncthreads();
-    if (tid < r) {
-      float acc = 0.f;
-      for (int i = tid; i < r; ++i) acc = fmaf(sRow[i], sA[i][tid], acc);
-      sA[r][tid] = -sB[r] * acc;
-    } else if (tid == r) {
-      sA[r][r] = 1.f;
+    if (wv < NB && ln < 16)
+#pragma unroll
+      for (int t = 0; t < 16; ++t) sA[16 * wv + t][16 * wv + ln] = col[t];
+    __syncthreads();
+    for (int R = 1; R < NB; ++R) {
+      // M_I = sum_{I <= J < R} Akk_RJ Tm_JI for every I < R
+      for (int e = tid; e < R * 256; e += kThreads) {
+        const int I = e >> 8, t = (e >> 4) & 15, sc = e & 15;
+        float acc = 0.f;
+        for (int u = 16 * I; u < 16 * R; ++u) acc = fmaf(sA[16 * R + t][u], sA[u][16 * I + sc], acc);
+        sM[I][t][sc] = acc;
+      }
+      __syncthreads();
+      for (int e = tid; e < R * 256; e += kThreads) {
+        const int I = e >> 8, t = (e >> 4) & 15, sc = e & 15;
+        float acc = 0.f;
+        for (int u = 0; u <= t; ++u)
+          acc = fmaf(sA[16 * R + t][16 * R + u] * sB[16 * R + u], sM[I][u][sc], acc);
+        sA[16 * R + t][16 * I + sc] = -acc;
+      }
+      __syncthreads();
+    }
+    // strictly upper blocks of Tm are zero
+    for (int e = tid; e < C * C; e += kThreads) {
+      const int r = e / C, i = e % C;
+      if ((i >> 4) > (r >> 4)) sA[r][i] = 0.f;
     }
     __syncthreads();
   }
@@ -173,23 +211,35 @@ __global__ __launch_bounds__(kThreads) void k_chunk_valu(FwdArgs a) {
     sG[r][c] = r < L ? sB[r] * a.kn[tok_off(r) * K + c] * expf(sG[r][c]) : 0.f;
   }
   __syncthreads();
-  // W = Tm X, U = Tm Diag(beta) V   (Tm lower triangular with unit diagonal)
+  // W = Tm X, U = Tm Diag(beta) V   (Tm lower triangular with unit diagonal).
+  // A thread's elements share one column (c = tid % D, rows tid / D + (256/D) m):
+  // that column of X and of Diag(beta) V is read into registers once.
   float* W = (float*)a.W + chb * C * K;
-  for (int p = tid; p < C * K; p += kThreads) {
-    const int r = p / K, c = p % K;
-    float acc = 0.f;
-    for (int i = 0; i <= r; ++i) acc = fmaf(sA[r][i], sG[i][c], acc);
-    W[p] = acc;
+  {
+    const int c = tid % K, r0 = tid / K, rs = kThreads / K;
+    float xc[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) xc[i] = sG[i][c];
+    for (int r = r0; r < C; r += rs) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < C; ++i) acc = (i <= r) ? fmaf(sA[r][i], xc[i], acc) : acc;
+      W[(int64_t)r * K + c] = acc;
+    }
   }
   float* U = (float*)a.U + chb * C * V;
   const Tin* v = (const Tin*)a.v;
-  for (int p = tid; p < C * V; p += kThreads) {
-    const int r = p / V, c = p % V;
-    float acc = 0.f;
-    const int iend = min(r, L - 1);
-    for (int i = 0; i <= iend; ++i)
-      acc = fmaf(sA[r][i] * sB[i], load_f32(v + tok_off(i) * V + c), acc);
-    U[p] = acc;
+  {
+    const int c = tid % V, r0 = tid / V, rs = kThreads / V;
+    float vc[C];
+#pragma unroll
+    for (int i = 0; i < C; ++i) vc[i] = i < L ? sB[i] * load_f32(v + tok_off(i) * V + c) : 0.f;
+    for (int r = r0; r < C; r += rs) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < C; ++i) acc = (i <= r) ? fmaf(sA[r][i], vc[i], acc) : acc;
+      U[(int64_t)r * V + c] = acc;
+    }
   }
 }
 
