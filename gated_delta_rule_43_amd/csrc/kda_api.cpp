@@ -176,12 +176,13 @@ Layout layout_for(const kda_problem* p, bool mfma) {
 Layout layout(const kda_problem* p) { return layout_for(p, use_mfma(p)); }
 
 // The backward's workspace: the VALU forward's (recomputed factors) followed by
-// Akk and Tm, per-chunk states and their gradients, per-token-head gradient
-// staging and per-chunk partial sums of the gate-parameter gradients.
+// Akk and Tm, per-chunk states and their gradients, the per-value-head
+// gradients of q^ and k^, and per-chunk partial sums of the gate-parameter
+// gradients.
 struct BwdLayout {
   Layout f;
   size_t off_akk = 0, off_tm = 0, off_hc = 0, off_dhc = 0, off_dc = 0, off_ddc = 0;
-  size_t off_dqh = 0, off_dkh = 0, off_dgam = 0, off_tkb = 0, off_da = 0, off_ddt = 0;
+  size_t off_dqh = 0, off_dkh = 0, off_da = 0, off_ddt = 0;
   size_t total = 0;
 };
 
@@ -204,8 +205,6 @@ BwdLayout bwd_layout(const kda_problem* p) {
   B.off_ddc = take(NT * H * C * V * 4);
   B.off_dqh = take(tokh * K * 4);
   B.off_dkh = take(tokh * K * 4);
-  B.off_dgam = take(tokh * K * 4);
-  B.off_tkb = take(tokh * K * 4);
   B.off_da = take(NT * H * 4);
   B.off_ddt = take(NT * H * K * 4);
   B.total = o;
@@ -580,7 +579,6 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
   b.hc = (float*)(w + L.off_hc); b.dhc = (float*)(w + L.off_dhc);
   b.Dc = (float*)(w + L.off_dc); b.dDc = (float*)(w + L.off_ddc);
   b.dqh = (float*)(w + L.off_dqh); b.dkh = (float*)(w + L.off_dkh);
-  b.dgam = (float*)(w + L.off_dgam); b.tkb = (float*)(w + L.off_tkb);
   b.da_part = (float*)(w + L.off_da); b.ddt_part = (float*)(w + L.off_ddt);
   b.dq = dq; b.dk = dk; b.dv = dv; b.dgate = dgate; b.dbeta = dbeta;
   b.da_log = da_log; b.ddt_bias = ddt_bias; b.dinit = d_initial_state;

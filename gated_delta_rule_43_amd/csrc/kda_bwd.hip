@@ -6,7 +6,9 @@
 // tests forward and backward together, whose state gradient the hyper_parallel
 // coverage page routes between slices (the backward of _RecvKDAInitialState).
 //
-// Plain VALU fp32 arithmetic for both input dtypes.  The forward's chunk
+// Plain VALU fp32 arithmetic for both input dtypes; the decay factors use the
+// hardware exponential (__expf: one v_exp_f32 after a scaling, about one ulp
+// on the result), the gate's derivative the full-accuracy functions.  The forward's chunk
 // factors are recomputed first (the VALU prologue and chunk kernels, which
 // here also keep Akk and Tm); then, per chunk of L rows entering with state
 // S0 and with Q~ = q^ e^gamma, K~ = k^ e^gamma, Kbar = k^ e^(gamma_L - gamma),
@@ -347,6 +349,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   const int c1 = tid % K, rb1 = tid / K;       // C x K layout
   const int i2 = tid % C, rb2 = tid / C;       // C x C layout
   Tin* dv = (Tin*)b.dv;
+  float dqs[NE1];  // scale dO S0^T, kept until phase F
   {
     float dw[NE1], dqt[NE1];
 #pragma unroll
@@ -380,7 +383,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     for (int m = 0; m < NE1; ++m) {
       const int r = rb1 + RSTEP1 * m;
       sDW[r][c1] = -dw[m];
-      if (r < L) b.dqh[th(r) * K + c1] = scale * dqt[m];  // staged in the element's own slot
+      dqs[m] = scale * dqt[m];
     }
   }
   // second sweep: its tiles live in the part of the region above dW
@@ -450,8 +453,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
 #pragma unroll
   for (int m = 0; m < NE1; ++m) {
     const int r = rb1 + RSTEP1 * m;
-    sKtT[c1][r] = r < L ? a.kn[th(r) * K + c1] * expf(sGam[r][c1]) : 0.f;
-    if (r < L) b.tkb[th(r) * K + c1] = dkb[m];
+    sKtT[c1][r] = r < L ? a.kn[th(r) * K + c1] * __expf(sGam[r][c1]) : 0.f;
   }
 #pragma unroll
   for (int m = 0; m < NE2; ++m) {
@@ -497,16 +499,14 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
       for (int aa = r; aa < L; ++aa) acc = fmaf(sT[aa][r], sY[aa][i2], acc);
     zv[m] = sB[i2] * acc;
   }
+  float ekt[NE1];  // e^gamma beta (Tm^T dW): the K~ term of dk^ (and, times k^, of dgamma)
 #pragma unroll
   for (int m = 0; m < NE1; ++m) {
     const int r = rb1 + RSTEP1 * m;
-    if (r < L) {
-      float dxk = 0.f;
+    float dxk = 0.f;
+    if (r < L)
       for (int aa = r; aa < L; ++aa) dxk = fmaf(sT[aa][r], sDW[aa][c1], dxk);
-      const float e = expf(sGam[r][c1]) * sB[r] * dxk;
-      b.dkh[th(r) * K + c1] = e;
-      b.dgam[th(r) * K + c1] = a.kn[th(r) * K + c1] * e;
-    }
+    ekt[m] = r < L ? __expf(sGam[r][c1]) * sB[r] * dxk : 0.f;
   }
   __syncthreads();  // K~ and dW are dead: Z and q^ take their places
 #pragma unroll
@@ -549,35 +549,37 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   __syncthreads();
 
   // ---- phase F: per element (r, c), the gradients of q^, k^ and gamma ----
+  float dgm[NE1], tkm[NE1];
+#pragma unroll
   for (int m = 0; m < NE1; ++m) {
     const int r = rb1 + RSTEP1 * m, c = c1;
+    dgm[m] = tkm[m] = 0.f;
     if (r >= L) continue;
     const float q = sQn[r][c], kk = sKn[r][c];
-    const float gm = sGam[r][c], egm = expf(gm), ekb = expf(sGam[L - 1][c] - gm);
-    const float dq_t = b.dqh[th(r) * K + c], dk_b = b.tkb[th(r) * K + c];
-    const float dk0 = b.dkh[th(r) * K + c], dg0 = b.dgam[th(r) * K + c];
+    const float gm = sGam[r][c], egm = __expf(gm), ekb = __expf(sGam[L - 1][c] - gm);
     float r1 = 0.f, r2 = 0.f;
     for (int i = 0; i <= r; ++i) {
-      const float ke = sKn[i][c] * expf(gm - sGam[i][c]);
+      const float ke = sKn[i][c] * __expf(gm - sGam[i][c]);
       r1 = fmaf(sP[r][i], ke, r1);
       r2 = fmaf(sY[r][i], ke, r2);
     }
     float c12 = 0.f;
     for (int rr = r; rr < L; ++rr) {
-      const float e = expf(sGam[rr][c] - gm);
+      const float e = __expf(sGam[rr][c] - gm);
       c12 = fmaf(sP[rr][r] * sQn[rr][c] + sY[rr][r] * sKn[rr][c], e, c12);
     }
-    const float tkb = kk * ekb * dk_b;
-    b.dqh[th(r) * K + c] = egm * dq_t + r1;
-    b.dkh[th(r) * K + c] = dk0 + ekb * dk_b + r2 + c12;
-    b.dgam[th(r) * K + c] = dg0 + q * egm * dq_t - tkb + q * r1 + kk * r2 - kk * c12;
-    b.tkb[th(r) * K + c] = tkb;
+    const float tkb = kk * ekb * dkb[m];
+    b.dqh[th(r) * K + c] = egm * dqs[m] + r1;
+    b.dkh[th(r) * K + c] = ekt[m] + ekb * dkb[m] + r2 + c12;
+    dgm[m] = kk * ekt[m] + q * egm * dqs[m] - tkb + q * r1 + kk * r2 - kk * c12;
+    tkm[m] = tkb;
   }
   __syncthreads();  // q^, k^ are dead
+#pragma unroll
   for (int m = 0; m < NE1; ++m) {
     const int r = rb1 + RSTEP1 * m;
-    sDg[r][c1] = r < L ? b.dgam[th(r) * K + c1] : 0.f;
-    sTk[r][c1] = r < L ? b.tkb[th(r) * K + c1] : 0.f;
+    sDg[r][c1] = dgm[m];
+    sTk[r][c1] = tkm[m];
   }
   __syncthreads();
 
@@ -588,7 +590,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   for (int c = tid; c < K; c += NT) {
     float cst = 0.f;
     for (int r = 0; r < L; ++r) cst += sTk[r][c];
-    cst = fmaf(expf(sGam[L - 1][c]), sSd[c], cst);
+    cst = fmaf(__expf(sGam[L - 1][c]), sSd[c], cst);
     float run = cst, ddt = 0.f, da = 0.f;
     const float alog = a.a_log[h], db = a.dt_bias[(int64_t)h * K + c];
     for (int r1 = C - 16; r1 >= 0; r1 -= 16) {

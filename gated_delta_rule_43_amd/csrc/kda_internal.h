@@ -109,7 +109,6 @@ struct BwdArgs {
   float *hc, *dhc;       // [NT*H][K*V] state entering each chunk, gradient of the state leaving it
   float *Dc, *dDc;       // [NT*H][C*V] Delta and its gradient
   float *dqh, *dkh;      // [B*T*H][K] gradient of q^, k^ per value head
-  float *dgam, *tkb;     // [B*T*H][K] gradient of gamma; the Kbar term summed into gamma_L
   float *da_part;        // [NT*H]
   float *ddt_part;       // [NT*H][K]
   // outputs

@@ -85,7 +85,8 @@ __global__ __launch_bounds__(kThreads) void k_prologue_valu(
   if (lane == 0) bt[th] = sigmoid_f(load_f32(beta + th));
 }
 
-// One workgroup per chunk-head (flattened j*H + h).  gamma's rows are padded
+// One workgroup per chunk-head (flattened j*H + h).  The decay factors use the
+// hardware exponential (__expf, about one ulp; all arguments are <= 0).  gamma's rows are padded
 // to K+1 floats: the pairwise products read gamma of row i with lanes over i.
 template <typename Tin, int C>
 __global__ __launch_bounds__(kThreads) void k_chunk_valu(FwdArgs a) {
@@ -123,7 +124,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_valu(FwdArgs a) {
       const float* qr = a.qn + tok_off(r) * K;
       const float* ki = a.kn + tok_off(i) * K;
       for (int c = 0; c < K; ++c) {
-        const float d = expf(sG[r][c] - sG[i][c]);
+        const float d = __expf(sG[r][c] - sG[i][c]);
         const float kd = ki[c] * d;
         akk = fmaf(kr[c], kd, akk);
         aqk = fmaf(qr[c], kd, aqk);
@@ -197,18 +198,18 @@ __global__ __launch_bounds__(kThreads) void k_chunk_valu(FwdArgs a) {
     const int r = p / K, c = p % K;
     float qt = 0.f, kb = 0.f;
     if (r < L) {
-      qt = a.scale * a.qn[tok_off(r) * K + c] * expf(sG[r][c]);
-      kb = a.kn[tok_off(r) * K + c] * expf(sG[C - 1][c] - sG[r][c]);
+      qt = a.scale * a.qn[tok_off(r) * K + c] * __expf(sG[r][c]);
+      kb = a.kn[tok_off(r) * K + c] * __expf(sG[C - 1][c] - sG[r][c]);
     }
     Qt[p] = qt;
     Kb[p] = kb;
   }
-  for (int c = tid; c < K; c += kThreads) a.gL[chb * K + c] = expf(sG[C - 1][c]);
+  for (int c = tid; c < K; c += kThreads) a.gL[chb * K + c] = __expf(sG[C - 1][c]);
   __syncthreads();
   // X = beta k^ exp(gamma), in place of gamma
   for (int p = tid; p < C * K; p += kThreads) {
     const int r = p / K, c = p % K;
-    sG[r][c] = r < L ? sB[r] * a.kn[tok_off(r) * K + c] * expf(sG[r][c]) : 0.f;
+    sG[r][c] = r < L ? sB[r] * a.kn[tok_off(r) * K + c] * __expf(sG[r][c]) : 0.f;
   }
   __syncthreads();
   // W = Tm X, U = Tm Diag(beta) V   (Tm lower triangular with unit diagonal).
