@@ -583,36 +583,63 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   }
   __syncthreads();
 
-  // gamma -> g (reverse cumulative sum; gamma_L also collects the Kbar terms and
+  // gamma -> g (a reverse cumulative sum over rows, segmented: thread (c, s)
+  // takes rows [s RSEG, (s+1) RSEG); gamma_L also collects the Kbar terms and
   // the state decay), then through the gate
+  constexpr int NSEG = NT / K, RSEG = C / NSEG > 0 ? C / NSEG : 1;
+  __shared__ float sSeg[NSEG][K], sSeg2[NSEG][K];
+  const int cS = tid % K, sS_ = tid / K;
   Tin* dgate = (Tin*)b.dgate;
   const Tin* gate = (const Tin*)a.gate;
-  for (int c = tid; c < K; c += NT) {
-    float cst = 0.f;
-    for (int r = 0; r < L; ++r) cst += sTk[r][c];
-    cst = fmaf(__expf(sGam[L - 1][c]), sSd[c], cst);
-    float run = cst, ddt = 0.f, da = 0.f;
-    const float alog = a.a_log[h], db = a.dt_bias[(int64_t)h * K + c];
-    for (int r1 = C - 16; r1 >= 0; r1 -= 16) {
-      if (r1 >= L) continue;
-      float gv[16];
+  const bool segok = sS_ * RSEG < C;
+  if (segok) {
+    float sdg = 0.f, stk = 0.f;
 #pragma unroll
-      for (int u = 0; u < 16; ++u) gv[u] = r1 + u < L ? load_f32(gate + th(r1 + u) * K + c) : 0.f;
-#pragma unroll
-      for (int u = 15; u >= 0; --u) {
-        const int r = r1 + u;
-        if (r >= L) continue;
-        run += sDg[r][c];
-        float gx, ga;
-        gate_grad(gv[u] + db, alog, a.gate_form, a.lb, &gx, &ga);
-        const float dg = run * gx;
-        store_as(dgate + th(r) * K + c, dg);
-        ddt += dg;
-        da = fmaf(run, ga, da);
-      }
+    for (int u = 0; u < RSEG; ++u) {
+      const int r = sS_ * RSEG + u;
+      sdg += sDg[r][cS];
+      stk += sTk[r][cS];
     }
-    b.ddt_part[chb * K + c] = ddt;
-    sRed[c] = da;
+    sSeg[sS_][cS] = sdg;
+    sSeg2[sS_][cS] = stk;
+  }
+  __syncthreads();
+  float ddt = 0.f, da = 0.f;
+  if (segok) {
+    float run = __expf(sGam[L - 1][cS]) * sSd[cS];
+    for (int s2 = 0; s2 < NSEG; ++s2) {
+      if (s2 * RSEG >= C) break;
+      run += sSeg2[s2][cS];
+      if (s2 > sS_) run += sSeg[s2][cS];
+    }
+    const float alog = a.a_log[h], db = a.dt_bias[(int64_t)h * K + cS];
+#pragma unroll 1
+    for (int u = RSEG - 1; u >= 0; --u) {
+      const int r = sS_ * RSEG + u;
+      if (r >= L) continue;
+      run += sDg[r][cS];
+      float gx, ga;
+      gate_grad(load_f32(gate + th(r) * K + cS) + db, alog, a.gate_form, a.lb, &gx, &ga);
+      const float dg = run * gx;
+      store_as(dgate + th(r) * K + cS, dg);
+      ddt += dg;
+      da = fmaf(run, ga, da);
+    }
+  }
+  __syncthreads();  // segment sums are read; reuse them for the partials
+  if (segok) {
+    sSeg[sS_][cS] = ddt;
+    sSeg2[sS_][cS] = da;
+  }
+  __syncthreads();
+  for (int c = tid; c < K; c += NT) {
+    float sddt = 0.f, sda = 0.f;
+    for (int s2 = 0; s2 < NSEG && s2 * RSEG < C; ++s2) {
+      sddt += sSeg[s2][c];
+      sda += sSeg2[s2][c];
+    }
+    b.ddt_part[chb * K + c] = sddt;
+    sRed[c] = sda;
   }
   // beta logit
   Tin* dbeta = (Tin*)b.dbeta;
