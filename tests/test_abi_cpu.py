@@ -292,3 +292,37 @@ def test_python_short_conv_binding_checks_shapes():
     with pytest.raises(ValueError, match="GPU tensor"):
         kda.kda_fwd_short_conv(x, x, x, x, torch.zeros(B, T, H, dtype=torch.bfloat16),
                                torch.zeros(H), torch.zeros(H, K))
+
+
+def test_bwd_rejects_before_launch(lib):
+    p = _p()
+    st = ctypes.c_int(0)
+    need = lib.kda_bwd_workspace_size(ctypes.byref(p), ctypes.byref(st))
+    assert st.value == kda.OK and need > lib.kda_fwd_workspace_size(ctypes.byref(p), ctypes.byref(st))
+    ins = [FAKE] * 5 + [FAKE, FAKE]            # q k v gate beta a_log dt_bias
+    grads = [FAKE] * 5 + [FAKE, FAKE, None]    # dq dk dv dgate dbeta da_log ddt_bias dinit
+    big = 1 << 40
+
+    def call(p_, ins_=ins, d_o=FAKE, dfin=None, grads_=grads, ws=FAKE, nbytes=big):
+        return lib.kda_bwd(ctypes.byref(p_), *ins_, None, d_o, dfin, *grads_, ws, nbytes, None)
+
+    assert call(p, d_o=None) == kda.EINVAL and "non-NULL" in lib.kda_last_error().decode()
+    bad = list(grads)
+    bad[5] = None  # da_log
+    assert call(p, grads_=bad) == kda.EINVAL and "da_log" in lib.kda_last_error().decode()
+    bad = list(grads)
+    bad[2] = FAKE + 1  # dv misaligned for bf16
+    assert call(p, grads_=bad) == kda.EINVAL and "aligned" in lib.kda_last_error().decode()
+    assert call(p, dfin=FAKE + 2) == kda.EINVAL and "misaligned" in lib.kda_last_error().decode()
+    assert call(p, nbytes=need - 1) == kda.EWORKSPACE
+    assert call(p, ws=None, nbytes=0) == kda.EWORKSPACE
+    assert call(_p(chunk_size=48)) == kda.EUNSUPPORTED
+    assert call(_p(HV=3)) == kda.EINVAL
+
+
+def test_python_bwd_binding_checks_shapes():
+    B, T, H, K = 1, 8, 2, 64
+    x = torch.zeros(B, T, H, K, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.kda_bwd(x, x, x, x, torch.zeros(B, T, H, dtype=torch.bfloat16), torch.zeros(H),
+                    torch.zeros(H, K), x)

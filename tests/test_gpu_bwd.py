@@ -149,3 +149,20 @@ def test_bwd_empty_and_zero_upstream():
     torch.cuda.synchronize()
     for n in NAMES:
         assert torch.all(got[n] == 0), n
+
+
+def test_bwd_device_only_offsets_match_host_checked():
+    """cu_seqlens without a host copy (sized from the upper bound of the chunk
+    count) gives the same bits as with the host-checked exact sizing."""
+    _banner("bwd device-only offsets")
+    inp = to_device(synthetic.random_problem(39, 1, 300, 2, 64, 64, dtype=torch.bfloat16,
+                                             lengths=[1, 63, 64, 65, 0, 107], init_std=0.5))
+    d_o, d_fin = _upstream(inp, 9)
+    args = (inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"], inp["a_log"], inp["dt_bias"],
+            d_o, d_fin)
+    a = kda.kda_bwd(*args, cu_seqlens=inp["cu_seqlens"], initial_state=inp["initial_state"])
+    b = kda.kda_bwd(*args, cu_seqlens=inp["cu_seqlens"], cu_seqlens_host=False,
+                    initial_state=inp["initial_state"])
+    torch.cuda.synchronize()
+    for n in NAMES:
+        assert torch.equal(a[n], b[n]), n
