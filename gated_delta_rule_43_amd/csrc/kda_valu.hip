@@ -29,6 +29,9 @@ namespace kda {
 namespace {
 
 constexpr int kThreads = 256;
+// The chunk-factor kernel's workgroup: its LDS (about 50 KB for C = 64) leaves
+// room for three workgroups per CU, so 512 threads give each SIMD six waves.
+constexpr int kChunkThreads = 512;
 constexpr int kMaxD = 128;  // largest head dimension
 
 __device__ inline float wave_sum(float x) {
@@ -89,7 +92,8 @@ __global__ __launch_bounds__(kThreads) void k_prologue_valu(
 // hardware exponential (__expf, about one ulp; all arguments are <= 0).  gamma's rows are padded
 // to K+1 floats: the pairwise products read gamma of row i with lanes over i.
 template <typename Tin, int C>
-__global__ __launch_bounds__(kThreads) void k_chunk_valu(FwdArgs a) {
+__global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
+  constexpr int kThreads = kChunkThreads;  // the loops below stride by the workgroup
   const int H = a.H, K = a.K, V = a.V;
   const int64_t wid = blockIdx.x;
   const int j = (int)(wid / H), h = (int)(wid % H);
@@ -337,7 +341,7 @@ hipError_t run_prep(const FwdArgs& a, hipStream_t s) {
   }
   if (a.NT > 0) {
     hipLaunchKernelGGL((k_chunk_valu<Tin, C>), dim3((unsigned)((int64_t)a.NT * a.H)),
-                       dim3(kThreads), 0, s, a);
+                       dim3(kChunkThreads), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   return hipSuccess;
@@ -358,7 +362,7 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
   mark(a, kStageChunk, 0, s);
   if (a.NT > 0) {
     hipLaunchKernelGGL((k_chunk_valu<Tin, C>), dim3((unsigned)((int64_t)a.NT * a.H)),
-                       dim3(kThreads), 0, s, a);
+                       dim3(kChunkThreads), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   mark(a, kStageChunk, 1, s);
