@@ -78,9 +78,9 @@ __device__ inline void stage(float* dst, const float* src, int n, int nt) {
   for (int e = threadIdx.x; e < n / 4; e += nt) ((float4*)dst)[e] = ((const float4*)src)[e];
 }
 
-// Waves per workgroup of the state passes: two per SIMD where the row groups
-// (C/NW rows of Delta per wave) stay multiples of four.
-constexpr int state_waves(int C) { return C >= 32 ? 8 : 4; }
+// Waves per workgroup of the state passes: as many as keep the row groups
+// (C/NW rows of Delta per wave) multiples of four.
+constexpr int state_waves(int C) { return C >= 64 ? 16 : C >= 32 ? 8 : 4; }
 
 // Forward state pass keeping S0 and Delta of every chunk.  One workgroup per
 // (sequence, head, tile of 64 columns): lane = column, wave w owns the state
