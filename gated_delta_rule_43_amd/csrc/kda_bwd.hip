@@ -8,9 +8,9 @@
 //
 // Plain VALU fp32 arithmetic for both input dtypes; the decay factors use the
 // hardware exponential (__expf: one v_exp_f32 after a scaling, about one ulp
-// on the result), the gate's derivative the full-accuracy functions.  The forward's chunk
-// factors are recomputed first (the VALU prologue and chunk kernels, which
-// here also keep Akk and Tm); then, per chunk of L rows entering with state
+// on the result), the gate's derivative the full-accuracy functions.  The
+// forward's chunk factors are recomputed first (the VALU prologue and chunk
+// kernels, which here also keep Akk and Tm); then, per chunk of L rows entering with state
 // S0 and with Q~ = q^ e^gamma, K~ = k^ e^gamma, Kbar = k^ e^(gamma_L - gamma),
 // Aqk_s = scale Aqk, Qt_s = scale Q~ (the forward's stored operands):
 //
@@ -35,7 +35,7 @@ namespace kda {
 namespace {
 
 constexpr int kThreads = 256;
-// Workgroup size of the chunk-gradient kernel per (C, K): its LDS (up to 151 KB)
+// Workgroup size of the chunk-gradient kernel per (C, K): its LDS (up to 159 KB)
 // allows one workgroup per CU, so the widest size that compiles without
 // register spills gives the most waves to hide LDS latency.
 constexpr int chunk_threads(int C, int K) { return C == 64 ? (K == 128 ? 1024 : 512) : C == 32 ? 256 : 512; }
@@ -266,14 +266,14 @@ __global__ __launch_bounds__(64 * state_waves(C)) void k_bwd_dstate(BwdArgs b) {
 
 // Chunk-local gradients.  One workgroup per chunk-head.
 //
-// Thread layouts: C x K elements (r, c) are owned as c = tid % K, r = tid / K +
-// (256 / K) m, so a wave shares its rows (broadcast LDS reads) and its lanes
-// hold consecutive channels (coalesced global access); C x C elements (r, i)
-// likewise with i = tid % C (a row's C lanes sit in one wave).  The products
-// over the value dimension (dW, dQ~, dKbar, P, the V half of Y, and dV) run
-// in one pass over 32-column tiles of S0, dS_L, dDelta, dO, Delta and V staged
-// in LDS; everything after that reads LDS only, apart from per-element
-// staging in the gradient outputs' own slots (read back by the same thread).
+// Thread layouts (NT threads): C x K elements (r, c) are owned as c = tid % K,
+// r = tid / K + (NT / K) m, so a wave shares its rows (broadcast LDS reads) and
+// its lanes hold consecutive channels (coalesced global access); C x C
+// elements (r, i) likewise with i = tid % C (a row's C lanes sit in one wave).
+// The products over the value dimension (dW, dQ~, dKbar, P, the V half of Y,
+// and dV) run in two sweeps over 32-column tiles of S0, dS_L, dDelta, dO,
+// Delta and V staged in LDS; everything after that reads LDS, and each
+// element's partial terms stay in its owner's registers between phases.
 template <typename Tin, int C, int K, int NT>
 __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   constexpr int VTL = 32, TS = VTL + 4;  // value tile and its padded row stride
@@ -310,8 +310,9 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   float (*tS0)[VTL + 1] = (float(*)[VTL + 1])sReg;
   float (*tdD)[TS] = (float(*)[TS])(sReg + K * (VTL + 1));
   float (*tdO)[TS] = (float(*)[TS])(sReg + K * (VTL + 1) + C * TS);
-  // after phase B: dW | P | Y (then dAkk) | K~ transposed (then Z); from phase F on,
-  // q^ takes dW's place and k^ K~'s; from phase G on, dgamma and the Kbar term
+  // after phase B: dW | P | Y (then dAkk) | K~ transposed (then Z); after phase
+  // D, q^ takes dW's place; after phase E, k^ takes Z's; after phase F, dgamma
+  // and the Kbar term take those two places
   float (*sDW)[K] = (float(*)[K])sReg;
   float (*sP)[C + 1] = (float(*)[C + 1])(sReg + C * K);
   float (*sY)[C + 1] = (float(*)[C + 1])(sReg + C * K + C * (C + 1));
@@ -484,7 +485,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   __syncthreads();
 
   // ---- phase D: dbeta (first part), Z = Tm^T dT (bb < r), and through dW the
-  //      K~ term of k^ and gamma (staged in the element's own output slots) ----
+  //      K~ term of k^ and gamma (kept in the element owner's registers) ----
   for (int r = tid; r < L; r += NT) {
     float acc = 0.f;
     for (int aa = r; aa < L; ++aa) acc = fmaf(sT[aa][r], sY[aa][r], acc);
