@@ -69,9 +69,10 @@ def _load():
         lib.oracle_short_conv_silu.argtypes = [I, I, I, I, P, P, P, I, P, P]
         lib.oracle_kda_bwd.argtypes = [I, I, I, I, I, I, P, P, P, P, P, P, P, D, I, D, I, P, P, P, P,
                                        P, P, P, P, P, P, P, P, I]
+        lib.oracle_gated_rms_norm.argtypes = [ctypes.c_long, I, P, P, P, D, I, P]
         for f in (lib.oracle_prologue, lib.oracle_kda_fwd, lib.oracle_recurrence,
                   lib.oracle_state_summary, lib.oracle_apply_state_summary,
-                  lib.oracle_short_conv_silu, lib.oracle_kda_bwd):
+                  lib.oracle_short_conv_silu, lib.oracle_kda_bwd, lib.oracle_gated_rms_norm):
             f.restype = I
         _lib = lib
     return _lib
@@ -275,3 +276,23 @@ def kda_bwd(q, k, v, gate, beta, a_log, dt_bias, d_o, d_final=None, scale=None, 
     if rc:
         raise ValueError("oracle_kda_bwd rejected its arguments (%d)" % rc)
     return out
+
+
+NORM_ACTIVATIONS = {"sigmoid": 0, "silu": 1}
+
+
+def gated_rms_norm(o, gate, weight=None, eps=1e-5, activation="sigmoid"):
+    """The gated output norm (fp64): per row of the last dimension V,
+    o / sqrt(mean(o^2) + eps) * weight * act(gate), act = sigmoid or SiLU."""
+    o, gate = _f64(o), _f64(gate)
+    if o.shape != gate.shape:
+        raise ValueError("o and gate must have one shape")
+    V = o.shape[-1]
+    R = o.size // V if V else 0
+    w = None if weight is None else _f64(weight).reshape(V)
+    y = np.empty(o.shape, np.float64)
+    rc = _load().oracle_gated_rms_norm(R, V, _ptr(o), _ptr(gate), _ptr(w), float(eps),
+                                       NORM_ACTIVATIONS[activation], _ptr(y))
+    if rc:
+        raise ValueError("oracle_gated_rms_norm rejected its arguments (%d)" % rc)
+    return y

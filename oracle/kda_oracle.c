@@ -631,6 +631,35 @@ int oracle_kda_bwd(int B, int T, int H, int HK, int K, int V, const double* q, c
   return oom ? 3 : 0;
 }
 
+/* ------------------------------------------------------------------------ */
+/* Public: the gated output norm after the forward, o_norm(o, output_gate)  */
+/* of the layer (hyper_parallel coverage page, the forward of               */
+/* KimiDeltaAttentionUlyssesCP: the output gate projection reshaped to      */
+/* [B, T, HV, V], then o_norm(output, output_gate) per value head; the       */
+/* torchtitan PR #4025 review names the model's RMSNorm with its reduction   */
+/* in fp32).  The pages do not print the norm; the reading taken here is a   */
+/* gated RMSNorm over the head's V values:                                  */
+/*   y[v] = o[v] / sqrt(mean_v(o^2) + eps) * weight[v] * act(gate[v])        */
+/* with act = sigmoid (act_mode 0) or SiLU x*sigmoid(x) (act_mode 1).        */
+/*   o, gate, y [R, V] fp64 (R = rows = tokens x heads); weight [V] or NULL. */
+/* ------------------------------------------------------------------------ */
+int oracle_gated_rms_norm(long R, int V, const double* o, const double* gate,
+                          const double* weight, double eps, int act_mode, double* y) {
+  if (R < 0 || V <= 0 || (act_mode != 0 && act_mode != 1)) return 1;
+  for (long r = 0; r < R; ++r) {
+    const double* x = o + r * V;
+    double ss = 0.0;
+    for (int v = 0; v < V; ++v) ss += x[v] * x[v];
+    const double inv = 1.0 / sqrt(ss / V + eps);
+    for (int v = 0; v < V; ++v) {
+      const double g = gate[r * V + v];
+      const double a = act_mode == 0 ? sigmoid(g) : g * sigmoid(g);
+      y[r * V + v] = x[v] * inv * (weight ? weight[v] : 1.0) * a;
+    }
+  }
+  return 0;
+}
+
 /* Public: final = transition . initial + state_ext (initial may be NULL). */
 int oracle_apply_state_summary(int B, int H, int K, int V, const double* state_ext,
                                const double* transition, const double* initial_state,
