@@ -12,6 +12,7 @@ device synchronisations; rank 0 prints one JSON line.
 Besides the throughput it reports
   * "short_conv": the same step after the layer's short convolution + SiLU of
     q, k, v (kda_fwd_short_conv), and that convolution kernel's own HBM rate;
+  * "output_norm": the gated output norm after the forward (its kernel's HBM rate);
   * "backward": the gradients of the same forward (kda_bwd);
   * "roofline": the dominant kernel's algorithmic bytes per launch divided by
     its average duration, timed live with HIP events recorded by the library
@@ -263,6 +264,33 @@ def bench_short_conv(inp, w, o, steps, warmup, width=4):
                             "tensor": "q [B,T,H*K]"}}
 
 
+def bench_output_norm(o, w, steps):
+    """The gated output norm after the forward (kda_gated_rms_norm, sigmoid gate)
+    on the forward's output shape, with a seeded gate; events on its stream."""
+    dev = o.device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(11)
+    gate = torch.randn(o.shape, generator=gen, device=dev).to(o.dtype)
+    weight = torch.rand(o.shape[-1], generator=gen, device=dev) + 0.5
+    y = torch.empty_like(o)
+    for _ in range(2):
+        kda.gated_rms_norm(o, gate, weight, out=y)
+    stream = torch.cuda.current_stream(dev)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(steps)]
+    for a, b in evs:
+        a.record(stream)
+        kda.gated_rms_norm(o, gate, weight, out=y)
+        b.record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    nbytes = 3 * o.numel() * o.element_size() + weight.numel() * 4   # o, gate in; y out
+    achieved = nbytes / (ms / 1e3) / 1e9
+    return {"kernel": "k_gated_rms_norm", "shape": list(o.shape), "kernel_ms": round(ms, 4),
+            "bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 5), "bytes_per_launch": nbytes}
+
+
 def bench_backward(inp, w, steps, warmup):
     """The backward (kda_bwd) of the same forward on the same resident inputs,
     with a seeded output gradient; events on the launch stream around each call."""
@@ -406,6 +434,8 @@ def main():
     if not args.no_short_conv:
         print("[bench] timing the forward after the short convolution", file=sys.stderr, flush=True)
         out["short_conv"] = bench_short_conv(inp, w, o, args.steps, args.warmup)
+    if not args.no_short_conv:
+        out["output_norm"] = bench_output_norm(o, w, args.steps)
     if not args.no_backward:
         print("[bench] timing the backward", file=sys.stderr, flush=True)
         out["backward"] = bench_backward(inp, w, min(args.steps, 5), 1)

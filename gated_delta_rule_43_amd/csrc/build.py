@@ -19,7 +19,7 @@ PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 OUT = os.path.join(PKG, "libkda.so")
 BUILD = os.path.join(ROOT, "_build", "kda")
-SOURCES = ["kda_api.cpp", "kda_table.hip", "kda_valu.hip", "kda_mfma.hip", "kda_conv.hip", "kda_bwd.hip"]
+SOURCES = ["kda_api.cpp", "kda_table.hip", "kda_valu.hip", "kda_mfma.hip", "kda_conv.hip", "kda_bwd.hip", "kda_norm.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -588,6 +588,35 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
   return KDA_OK;
 }
 
+kda_status kda_gated_rms_norm(const kda_problem* p, const void* o, const void* gate,
+                              const float* weight, float eps, int32_t activation, void* y,
+                              void* stream) {
+  kda_status st = validate_rows(p, false);
+  if (st != KDA_OK) return st;
+  if (p->H < 1 || p->HV < 0 || (p->HV > 0 && p->HV % p->H != 0))
+    return fail(KDA_EINVAL, "bad heads H=%d HV=%d", p->H, p->HV);
+  if (!head_dim_ok(p->V)) return fail(KDA_EUNSUPPORTED, "value head dim V=%d is not supported (64 or 128)", p->V);
+  if (activation != KDA_NORM_SIGMOID && activation != KDA_NORM_SILU)
+    return fail(KDA_EINVAL, "activation must be KDA_NORM_SIGMOID or KDA_NORM_SILU, got %d", activation);
+  if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(KDA_EINVAL, "eps must be finite and >= 0, got %g", (double)eps);
+  const long long rows = (long long)p->B * p->T * value_heads(p);
+  if (rows == 0) {
+    g_last_error.clear();
+    return KDA_OK;
+  }
+  if (!o || !gate || !y) return fail(KDA_EINVAL, "o, gate and y must be non-NULL");
+  if (!aligned(o, 16) || !aligned(gate, 16) || !aligned(y, 16))
+    return fail(KDA_EINVAL, "o, gate and y must be 16-byte aligned");
+  if (weight && !aligned(weight, 4)) return fail(KDA_EINVAL, "weight must be 4-byte aligned");
+  kda::NormArgs a{};
+  a.rows = rows; a.V = p->V; a.dtype = p->dtype; a.act = activation; a.eps = eps;
+  a.o = o; a.gate = gate; a.w = weight; a.y = y;
+  hipError_t e = kda::launch_gated_rms_norm(a, (hipStream_t)stream);
+  if (e != hipSuccess) return fail(KDA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
+  g_last_error.clear();
+  return KDA_OK;
+}
+
 const char* kda_last_error(void) { return g_last_error.c_str(); }
 
 int32_t kda_version(void) { return (0 << 16) | 1; }

@@ -116,6 +116,19 @@ struct BwdArgs {
   float *da_log, *ddt_bias, *dinit;    // fp32; dinit may be nullptr
 };
 
+// The gated output norm over rows of V values (o, gate, y: dtype; w: fp32 [V] or null).
+struct NormArgs {
+  int64_t rows;
+  int V;
+  int dtype;   // 0 fp32, 1 bf16
+  int act;     // 0 sigmoid, 1 SiLU
+  float eps;
+  const void* o;
+  const void* gate;
+  const float* w;
+  void* y;
+};
+
 // Stages of one forward, in launch order (timing hooks of kda_fwd_profiled).
 enum Stage { kStageTable = 0, kStagePrologue = 1, kStageChunk = 2, kStageState = 3, kNumStages = 4 };
 
@@ -130,6 +143,7 @@ hipError_t launch_valu_prep(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_mfma_path(const FwdArgs& a, hipStream_t s);
 hipError_t launch_short_conv(const ConvArgs& a, hipStream_t s);
+hipError_t launch_gated_rms_norm(const NormArgs& a, hipStream_t s);
 size_t mfma_record_bytes(int K, int V);
 hipError_t launch_apply_summary(int B, int H, int K, int V, const float* E, const float* P,
                                 const float* S0, float* F, hipStream_t s);

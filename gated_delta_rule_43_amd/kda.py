@@ -33,7 +33,7 @@ EXPORTED = ("kda_validate", "kda_fwd_workspace_size", "kda_fwd", "kda_fwd_profil
             "kda_state_summary_workspace_size", "kda_state_summary",
             "kda_apply_state_summary", "kda_chunk_capacity", "kda_chunk_table",
             "kda_short_conv_silu", "kda_fwd_short_conv_workspace_size", "kda_fwd_short_conv",
-            "kda_bwd_workspace_size", "kda_bwd",
+            "kda_bwd_workspace_size", "kda_bwd", "kda_gated_rms_norm",
             "kda_last_error", "kda_version")
 MAX_CONV_WIDTH = 4
 
@@ -101,6 +101,8 @@ def load_library(path: Optional[str] = None):
     lib.kda_bwd_workspace_size.restype = S
     lib.kda_bwd.argtypes = [PP] + [P] * 18 + [P, S, P]
     lib.kda_bwd.restype = ctypes.c_int
+    lib.kda_gated_rms_norm.argtypes = [PP, P, P, P, ctypes.c_float, I32, P, P]
+    lib.kda_gated_rms_norm.restype = ctypes.c_int
     lib.kda_last_error.argtypes = []
     lib.kda_last_error.restype = ctypes.c_char_p
     lib.kda_version.argtypes = []
@@ -453,6 +455,34 @@ def kda_bwd(q, k, v, gate, beta, a_log, dt_bias, d_o, d_final_state=None, *, sca
     if st:
         _raise(st, "kda_bwd")
     return out
+
+
+NORM_ACTIVATIONS = {"sigmoid": 0, "silu": 1}
+
+
+def gated_rms_norm(o, gate, weight=None, *, eps=1e-5, activation="sigmoid", out=None):
+    """The gated output norm after the forward: per [..., V] row,
+    o / sqrt(mean(o^2) + eps) * weight * act(gate), act = sigmoid or SiLU.
+    o, gate [B, T, HV, V] (float32 or bfloat16, GPU); weight float32 [V] or None."""
+    if activation not in NORM_ACTIVATIONS:
+        raise ValueError("activation must be one of %s, got %r" % (sorted(NORM_ACTIVATIONS), activation))
+    if not isinstance(o, torch.Tensor) or o.dim() != 4:
+        raise ValueError("o must be a [B, T, HV, V] tensor")
+    _dev(o, "o")
+    _dev(gate, "gate", dtype=o.dtype, shape=tuple(o.shape))
+    B, T, HV, V = o.shape
+    if weight is not None:
+        _dev(weight, "weight", dtype=torch.float32, shape=(V,))
+    p = make_problem(B, T, HV, 0, V, _dtype_code(o))
+    y = torch.empty_like(o) if out is None else out
+    _dev(y, "out", dtype=o.dtype, shape=tuple(o.shape))
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = load_library().kda_gated_rms_norm(ctypes.byref(p), ptr(o), ptr(gate), ptr(weight),
+                                           float(eps), NORM_ACTIVATIONS[activation], ptr(y),
+                                           _stream_ptr(o.device))
+    if st:
+        _raise(st, "kda_gated_rms_norm")
+    return y
 
 
 def kda_state_summary(q, k, v, gate, beta, a_log, dt_bias, *, lower_bound=None, chunk_size=64,

@@ -310,6 +310,30 @@ kda_status kda_fwd_short_conv(const kda_problem* p, const kda_short_conv* conv, 
                               const float* initial_state, void* o, float* final_state,
                               void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * The gated output norm after the forward: o_norm(o, output_gate) of the
+ * layer (hyper_parallel coverage page, the forward of
+ * KimiDeltaAttentionUlyssesCP: the output gate projection reshaped to
+ * [B, T, HV, V] and o_norm(output, output_gate) applied per value head; the
+ * torchtitan PR #4025 review names the model's RMSNorm with an fp32
+ * reduction).  The pages print neither the norm nor the gate's activation;
+ * this library's reading, per (token, value head) row of V values:
+ *
+ *     y[v] = o[v] / sqrt(mean_v(o^2) + eps) * weight[v] * act(gate[v])
+ *
+ *  o, gate, y   [B, T, HV, V], p->dtype, 16-byte aligned; y may equal o.
+ *  weight       fp32 [V] shared by all heads, or NULL for ones.
+ *  eps          finite, >= 0.
+ *  activation   KDA_NORM_SIGMOID (0) or KDA_NORM_SILU (1, x * sigmoid(x)).
+ * Only B, T, H, HV, V, dtype and the row layout are read from p.  Computes in
+ * fp32 (the mean over V in fp32), rounds once to p->dtype.
+ */
+#define KDA_NORM_SIGMOID 0
+#define KDA_NORM_SILU 1
+kda_status kda_gated_rms_norm(const kda_problem* p, const void* o, const void* gate,
+                              const float* weight, float eps, int32_t activation, void* y,
+                              void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* kda_last_error(void);
 

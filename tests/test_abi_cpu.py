@@ -326,3 +326,25 @@ def test_python_bwd_binding_checks_shapes():
     with pytest.raises(ValueError, match="GPU tensor"):
         kda.kda_bwd(x, x, x, x, torch.zeros(B, T, H, dtype=torch.bfloat16), torch.zeros(H),
                     torch.zeros(H, K), x)
+
+
+def test_gated_rms_norm_rejects_before_launch(lib):
+    p = _p(B=1, T=10)
+    big = FAKE + (1 << 20)
+    assert lib.kda_gated_rms_norm(ctypes.byref(p), FAKE, big, None, 1e-5, 7, FAKE, None) == kda.EINVAL
+    assert "activation" in lib.kda_last_error().decode()
+    assert lib.kda_gated_rms_norm(ctypes.byref(p), FAKE, big, None, -1.0, 0, FAKE, None) == kda.EINVAL
+    assert lib.kda_gated_rms_norm(ctypes.byref(p), FAKE, big, None, float("nan"), 0, FAKE, None) == kda.EINVAL
+    assert lib.kda_gated_rms_norm(ctypes.byref(p), None, big, None, 1e-5, 0, FAKE, None) == kda.EINVAL
+    assert lib.kda_gated_rms_norm(ctypes.byref(p), FAKE + 8, big, None, 1e-5, 0, FAKE, None) == kda.EINVAL
+    assert "16-byte" in lib.kda_last_error().decode()
+    q = _p(B=1, T=10, V=96)
+    assert lib.kda_gated_rms_norm(ctypes.byref(q), FAKE, big, None, 1e-5, 0, FAKE, None) == kda.EUNSUPPORTED
+
+
+def test_python_norm_binding_checks_shapes():
+    o = torch.zeros(1, 4, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        kda.gated_rms_norm(o, o)
+    with pytest.raises(ValueError, match="activation"):
+        kda.gated_rms_norm(o, o, activation="tanh")

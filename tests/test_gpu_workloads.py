@@ -156,3 +156,23 @@ def test_workload3_backward_sampled():
         print("workload 3 backward %s: max-abs %.3g (scale %.3g) rel-F %.3g" % (n, err, scale_, rf),
               flush=True)
         assert err <= 2e-2 * scale_ and rf <= 1e-2, n
+
+
+def test_workload3_output_norm_sampled():
+    """The gated output norm on the forward output's full shape (the benchmark's
+    output_norm configuration); sampled rows against the oracle, each within one
+    bf16 rounding."""
+    import oracle
+    w = synthetic.WORKLOADS[3]
+    _banner("workload 3 output norm")
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(11)
+    o = (torch.randn(w.B, w.T, w.H, w.V, generator=gen, device=DEV) * 0.05).to(torch.bfloat16)
+    gate = torch.randn(w.B, w.T, w.H, w.V, generator=gen, device=DEV).to(torch.bfloat16)
+    weight = torch.rand(w.V, generator=gen, device=DEV) + 0.5
+    y = kda.gated_rms_norm(o, gate, weight)
+    torch.cuda.synchronize()
+    idx = (slice(None), slice(0, w.T, 997), slice(None))
+    ref = oracle.gated_rms_norm(to_np(o[idx]), to_np(gate[idx]), to_np(weight), 1e-5, "sigmoid")
+    got = to_np(y[idx]).astype(np.float64)
+    assert np.all(np.abs(got - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-6)
