@@ -11,14 +11,17 @@
 // review (the model's RMSNorm reduces in fp32).  The pages print neither the
 // norm nor the gate's activation; this is the gated RMSNorm reading.
 //
-// HBM-bound: every lane holds 16 bytes of one row (8 bf16 or 4 fp32 values);
-// the V / 8 (or V / 4) lanes of a row sum their squares with xor shuffles.
+// HBM-bound: every lane holds 16 bytes of one row (8 bf16 or 4 fp32 values)
+// for kNormRows rows; the V / 8 (or V / 4) lanes of a row sum their squares
+// with xor shuffles; the gate's sigmoid uses the hardware exponential and
+// reciprocal (about one ulp each).
 #include "kda_internal.h"
 
 namespace kda {
 namespace {
 
 constexpr int kNormThreads = 256;
+constexpr int kNormRows = 4;  // rows per thread
 
 template <typename T> __device__ __forceinline__ void ld16(const T* p, float* out);
 template <> __device__ __forceinline__ void ld16<float>(const float* p, float* out) {
@@ -47,32 +50,41 @@ __device__ __forceinline__ void st16(bf16* p, const float* v) {
 template <typename T, int V, int ACT>
 __global__ __launch_bounds__(kNormThreads) void k_gated_rms_norm(NormArgs a) {
   constexpr int NV = 16 / (int)sizeof(T), LPR = V / NV;  // values per lane, lanes per row
+  constexpr int RPB = kNormThreads / LPR;                 // rows per block and round
   static_assert(LPR >= 1 && LPR <= 64 && (LPR & (LPR - 1)) == 0, "a row's lanes sit in one wave");
-  const int64_t gid = (int64_t)blockIdx.x * kNormThreads + threadIdx.x;
-  const int64_t row = gid / LPR;
-  const int part = (int)(gid % LPR);
-  // rows past the end take row 0 and store nothing (whole row groups stay
-  // together for the shuffles)
-  const bool live = row < a.rows;
-  const int64_t off = (live ? row : 0) * V + part * NV;
-  float x[NV], g[NV];
-  ld16((const T*)a.o + off, x);
-  ld16((const T*)a.gate + off, g);
-  float ss = 0.f;
+  const int part = threadIdx.x % LPR;
+  const int64_t row0 = (int64_t)blockIdx.x * RPB * kNormRows + threadIdx.x / LPR;
+  // all of a thread's rows are loaded before any arithmetic; rows past the end
+  // read row 0 and store nothing (whole row groups stay together for the shuffles)
+  float x[kNormRows][NV], g[kNormRows][NV];
 #pragma unroll
-  for (int e = 0; e < NV; ++e) ss = fmaf(x[e], x[e], ss);
-#pragma unroll
-  for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
-  const float inv = 1.f / sqrtf(ss / V + a.eps);
-  float y[NV];
-#pragma unroll
-  for (int e = 0; e < NV; ++e) {
-    const float s = 1.f / (1.f + __expf(-g[e]));
-    const float act = ACT == 0 ? s : g[e] * s;
-    const float w = a.w ? a.w[part * NV + e] : 1.f;
-    y[e] = x[e] * inv * w * act;
+  for (int k = 0; k < kNormRows; ++k) {
+    const int64_t row = row0 + (int64_t)k * RPB;
+    const int64_t off = (row < a.rows ? row : 0) * V + part * NV;
+    ld16((const T*)a.o + off, x[k]);
+    ld16((const T*)a.gate + off, g[k]);
   }
-  if (live) st16((T*)a.y + off, y);
+  float w[NV];
+#pragma unroll
+  for (int e = 0; e < NV; ++e) w[e] = a.w ? a.w[part * NV + e] : 1.f;
+#pragma unroll
+  for (int k = 0; k < kNormRows; ++k) {
+    const int64_t row = row0 + (int64_t)k * RPB;
+    float ss = 0.f;
+#pragma unroll
+    for (int e = 0; e < NV; ++e) ss = fmaf(x[k][e], x[k][e], ss);
+#pragma unroll
+    for (int m = LPR / 2; m >= 1; m >>= 1) ss += __shfl_xor(ss, m, 64);
+    const float inv = 1.f / sqrtf(ss / V + a.eps);
+    float y[NV];
+#pragma unroll
+    for (int e = 0; e < NV; ++e) {
+      const float s = __builtin_amdgcn_rcpf(1.f + __expf(-g[k][e]));  // sigmoid
+      const float act = ACT == 0 ? s : g[k][e] * s;
+      y[e] = x[k][e] * inv * w[e] * act;
+    }
+    if (row < a.rows) st16((T*)a.y + row * V + part * NV, y);
+  }
 }
 
 template <typename T, int V>
@@ -87,8 +99,8 @@ hipError_t launch_v(const NormArgs& a, dim3 grid, hipStream_t s) {
 hipError_t launch_gated_rms_norm(const NormArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   const int nv = a.dtype == 1 ? 8 : 4;
-  const int64_t threads = a.rows * (a.V / nv);
-  const dim3 grid((unsigned)((threads + kNormThreads - 1) / kNormThreads));
+  const int64_t rows_per_block = (int64_t)(kNormThreads / (a.V / nv)) * kNormRows;
+  const dim3 grid((unsigned)((a.rows + rows_per_block - 1) / rows_per_block));
   if (a.dtype == 1) return a.V == 64 ? launch_v<bf16, 64>(a, grid, s) : launch_v<bf16, 128>(a, grid, s);
   return a.V == 64 ? launch_v<float, 64>(a, grid, s) : launch_v<float, 128>(a, grid, s);
 }
