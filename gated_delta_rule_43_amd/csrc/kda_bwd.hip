@@ -690,7 +690,8 @@ __global__ __launch_bounds__(kThreads) void k_bwd_qk(BwdArgs b) {
   }
 }
 
-// da_log, ddt_bias: sums over chunks in chunk order.
+// da_log, ddt_bias: sums over chunks in chunk order (the additions stay in that
+// order; the loads are issued 16 at a time).
 __global__ __launch_bounds__(kThreads) void k_bwd_params(BwdArgs b) {
   const FwdArgs& a = b.f;
   const int H = a.H, K = a.K;
@@ -699,12 +700,28 @@ __global__ __launch_bounds__(kThreads) void k_bwd_params(BwdArgs b) {
   if (t < (int64_t)H * K) {
     const int h = (int)(t / K), c = (int)(t % K);
     float s = 0.f;
-    for (int j = 0; j < nt; ++j) s += b.ddt_part[((int64_t)j * H + h) * K + c];
+    int j = 0;
+    for (; j + 16 <= nt; j += 16) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = b.ddt_part[((int64_t)(j + u) * H + h) * K + c];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) s += v[u];
+    }
+    for (; j < nt; ++j) s += b.ddt_part[((int64_t)j * H + h) * K + c];
     b.ddt_bias[t] = s;
   }
   if (t < H) {
     float s = 0.f;
-    for (int j = 0; j < nt; ++j) s += b.da_part[(int64_t)j * H + t];
+    int j = 0;
+    for (; j + 16 <= nt; j += 16) {
+      float v[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) v[u] = b.da_part[(int64_t)(j + u) * H + t];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) s += v[u];
+    }
+    for (; j < nt; ++j) s += b.da_part[(int64_t)j * H + t];
     b.da_log[t] = s;
   }
 }
