@@ -345,3 +345,25 @@ def test_clamped_gate(dtype, chunk):
     d_ref, _ = errors(to_np(o), o_ref)
     d_sig, _ = errors(to_np(o), o_sig)
     assert d_sig > 5e-3 and d_sig > 5 * d_ref, (d_sig, d_ref)
+
+
+# --------------------------------------------------------------------------
+# long rows with few (row, head) chains: every chain carries its state over
+# 64 to 131 chunks (several record-staging rounds of the state pass, a ragged
+# last chunk, grouped value heads)
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("B,T,H,HV,K,V,init", [
+    (2, 64 * 130 + 29, 2, 2, 128, 128, True),   # 131 chunks, ragged tail
+    (1, 64 * 64, 1, 2, 64, 64, False),          # 64 chunks, grouped value heads
+])
+def test_long_rows_few_chains(B, T, H, HV, K, V, init):
+    _banner("long rows B=%d T=%d HV=%d K=%d" % (B, T, HV, K))
+    inp = to_device(synthetic.random_problem(61, B, T, H, K, V, dtype=torch.bfloat16, HV=HV,
+                                             init_std=0.5 if init else None))
+    o, fin = gpu_fwd(inp)
+    o_ref, f_ref = oracle_fwd(inp)
+    assert_close(to_np(o), o_ref, torch.bfloat16, "o")
+    assert_close(to_np(fin), f_ref, torch.bfloat16, "final_state")
+    # the output alone (no final state) is the same bits
+    o2, _ = gpu_fwd(inp, output_final_state=False)
+    assert torch.equal(o, o2)
