@@ -14,6 +14,13 @@ Besides the throughput it reports
     q, k, v (kda_fwd_short_conv), and that convolution kernel's own HBM rate;
   * "output_norm": the gated output norm after the forward (its kernel's HBM rate);
   * "backward": the gradients of the same forward (kda_bwd);
+  * "workloads": the forward on the other four workloads (tiny fp32, packed
+    varlen, long slice with carried state, short documents with a lower
+    bound), each on its own seeded inputs, timed the same way;
+  * "state_summary": the long row cut into 8 contiguous slices, the affine
+    summary of every slice (kda_state_summary, one call) and their composition
+    from the initial state (kda_apply_state_summary, slice by slice), compared
+    with the forward's final state;
   * "roofline": the dominant kernel's algorithmic bytes per launch divided by
     its average duration, timed live with HIP events recorded by the library
     around each stage on the kernel's own stream (kda_fwd_profiled);
@@ -158,6 +165,124 @@ def stage_bytes(w, stage, NT, N):
     if stage == 3:   # state pass: records in, o out, initial/final states
         return NT * H * rec + tokh * V * ein + states
     return 0
+
+
+def fwd_runner(w, inp, dev):
+    """A closure running kda_fwd once on resident inputs (its own output and
+    workspace), with optional per-stage events; and the sequence count N."""
+    cu = inp["cu_seqlens"]
+    cu_host = None if cu is None else cu.cpu()
+    N = w.B if cu is None else cu.numel() - 1
+    o = torch.empty(w.B, w.T, w.H, w.V, dtype=w.torch_dtype, device=dev)
+    need = kda.fwd_workspace_size((w.B, w.T, w.H, w.K), w.V, w.torch_dtype, w.chunk_size,
+                                  w.lower_bound, N=N, cu_seqlens_host=cu_host)
+    ws = torch.empty(need + 256, dtype=torch.uint8, device=dev)
+    ws = ws[(-ws.data_ptr()) % 256:][:need]
+    res = {"o": o, "fin": None}
+
+    def step(events=None):
+        _, res["fin"] = kda.kda_fwd(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"],
+                                    inp["a_log"], inp["dt_bias"], scale=w.scale,
+                                    lower_bound=w.lower_bound, chunk_size=w.chunk_size,
+                                    cu_seqlens=cu, cu_seqlens_host=cu_host,
+                                    initial_state=inp["initial_state"],
+                                    output_final_state=w.output_final_state, out=o, workspace=ws,
+                                    stage_events=events)
+    return step, res, N, cu_host
+
+
+def time_fwd(step, steps, warmup):
+    """W untimed runs, then `steps` timed runs between two synchronisations:
+    (wall ms per step, mean ms of each stage from the library's events)."""
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = StageEvents(steps)
+    t0 = time.perf_counter()
+    for i in range(steps):
+        step(ev.arrays[i])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / steps
+    stage_ms = ev.stage_ms()
+    ev.close()
+    return ms, stage_ms
+
+
+def bench_state_summary(w, inp, fin_fwd, steps, warmup, slices=8):
+    """The long row as `slices` contiguous slices: the affine summary of every
+    slice in one kda_state_summary call (the slices are rows of one batch, a
+    view of the same memory), then the summaries composed from the initial
+    state with kda_apply_state_summary, one slice after another.  Events on the
+    launch stream around both parts; the composed state is compared with the
+    forward's final state of the same row."""
+    dev = inp["q"].device
+    S = w.T // slices
+    cut = lambda t: t.reshape(slices, S, *t.shape[2:])
+    args = [cut(inp[x]) for x in ("q", "k", "v", "gate", "beta")]
+    bufs = [torch.empty_like(inp["initial_state"]) for _ in range(2)]
+
+    def summary():
+        return kda.kda_state_summary(*args, inp["a_log"], inp["dt_bias"],
+                                     lower_bound=w.lower_bound, chunk_size=w.chunk_size)
+
+    def compose(E, P):
+        st = inp["initial_state"]
+        for r in range(slices):
+            st = kda.kda_apply_state_summary(E[r:r + 1], P[r:r + 1], st, out=bufs[r % 2])
+        return st
+
+    for _ in range(max(1, warmup)):
+        compose(*summary())
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream(dev)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    for e0, e1, e2 in evs:
+        e0.record(stream)
+        E, P = summary()
+        e1.record(stream)
+        st = compose(E, P)
+        e2.record(stream)
+    torch.cuda.synchronize()
+    sum_ms = float(np.mean([a.elapsed_time(b) for a, b, _ in evs]))
+    app_ms = float(np.mean([b.elapsed_time(c) for _, b, c in evs]))
+    err = float((st - fin_fwd).abs().max())
+    ref = float(fin_fwd.abs().max())
+    elt = 2 if w.dtype == "bf16" else 4
+    # algorithmic bytes of the summary call: every input read once, the slice
+    # summaries (E [slices,H,K,V], P [slices,H,K,K], fp32) written once
+    nbytes = w.T * w.H * (3 * w.K + w.V + 1) * elt + slices * w.H * (w.K * w.V + w.K * w.K) * 4
+    achieved = nbytes / (sum_ms / 1e3) / 1e9
+    return {"workload": "%s as %d contiguous slices of %d tokens" % (w.name, slices, S),
+            "value": round(w.T / ((sum_ms + app_ms) / 1e3) / 1e6, 4), "unit": "Mtokens/s",
+            "summary_ms": round(sum_ms, 4), "compose_ms": round(app_ms, 4),
+            "summary_path_algorithmic_GBps": round(achieved, 2),
+            "summary_path_hbm_frac": round(achieved / HBM_PEAK_GBS, 5),
+            "composed_vs_forward_final_state_max_abs": err,
+            "forward_final_state_max_abs": ref}
+
+
+def bench_other_workloads(skip, steps, warmup, dev):
+    """The forward on each other workload, on its own seeded inputs, timed like
+    the headline; the long-slice workload also times its slice summaries."""
+    out = {}
+    for wid in sorted(synthetic.WORKLOADS):
+        if wid == skip:
+            continue
+        w = synthetic.WORKLOADS[wid]
+        print("[bench] workload %s" % w.name, file=sys.stderr, flush=True)
+        inp = synthetic.make_inputs(w, dev)
+        step, res, N, _ = fwd_runner(w, inp, dev)
+        ms, stage_ms = time_fwd(step, steps, warmup)
+        out[w.name] = {"value": round(w.B * w.T / (ms / 1e3) / 1e6, 4), "unit": "Mtokens/s",
+                       "ms_per_step": round(ms, 4), "dtype": w.dtype, "sequences": N,
+                       "stage_ms": dict(zip(kda.STAGE_NAMES, [round(float(x), 4)
+                                                             for x in stage_ms]))}
+        if w.init_std is not None and N == 1:
+            print("[bench] slice summaries of %s" % w.name, file=sys.stderr, flush=True)
+            out["state_summary"] = bench_state_summary(w, inp, res["fin"], steps, warmup)
+        del inp, step, res
+        torch.cuda.empty_cache()
+    return out
 
 
 def cpu_baseline(inp, w, budget_s=12.0):
@@ -338,6 +463,8 @@ def main():
     ap.add_argument("--no-short-conv", action="store_true",
                     help="skip the forward-after-short-convolution measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the backward measurement")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the forward on the other workloads and the slice summaries")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (to scale the "
                          "FETCH_SIZE/WRITE_SIZE counters) and exit")
@@ -364,38 +491,13 @@ def main():
     print("[bench] drawing %s on %s" % (w.name, dev), file=sys.stderr, flush=True)
     inp = synthetic.make_inputs(w, dev)
     cu = inp["cu_seqlens"]
-    cu_host = None if cu is None else cu.cpu()
-    N = w.B if cu is None else cu.numel() - 1
-    o = torch.empty(w.B, w.T, w.H, w.V, dtype=w.torch_dtype, device=dev)
-    need = kda.fwd_workspace_size((w.B, w.T, w.H, w.K), w.V, w.torch_dtype, w.chunk_size,
-                                  w.lower_bound, N=N, cu_seqlens_host=cu_host)
-    ws = torch.empty(need + 256, dtype=torch.uint8, device=dev)
-    ws = ws[(-ws.data_ptr()) % 256:][:need]
-    fin = None
-
-    def step(events=None):
-        nonlocal fin
-        _, fin = kda.kda_fwd(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"],
-                             inp["a_log"], inp["dt_bias"], scale=w.scale,
-                             lower_bound=w.lower_bound, chunk_size=w.chunk_size, cu_seqlens=cu,
-                             cu_seqlens_host=cu_host, initial_state=inp["initial_state"],
-                             output_final_state=w.output_final_state, out=o, workspace=ws,
-                             stage_events=events)
-
+    step, res, N, cu_host = fwd_runner(w, inp, dev)
+    o = res["o"]
     for i in range(args.warmup):
         step()
         torch.cuda.synchronize()
         print("[bench] warmup %d/%d done" % (i + 1, args.warmup), file=sys.stderr, flush=True)
-    ev = StageEvents(args.steps)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        step(ev.arrays[i])
-    torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
-    ms_per_step = elapsed * 1e3 / args.steps
-    stage_ms = ev.stage_ms()
-    ev.close()
+    ms_per_step, stage_ms = time_fwd(step, args.steps, 0)
     print("[bench] timed %d steps: %.3f ms/step; stages (ms) %s" % (
         args.steps, ms_per_step, dict(zip(kda.STAGE_NAMES, np.round(stage_ms, 4).tolist()))),
         file=sys.stderr, flush=True)
@@ -439,6 +541,9 @@ def main():
     if not args.no_backward:
         print("[bench] timing the backward", file=sys.stderr, flush=True)
         out["backward"] = bench_backward(inp, w, min(args.steps, 5), 1)
+    if not args.no_other_workloads:
+        out["workloads"] = bench_other_workloads(args.workload, min(args.steps, 10),
+                                                 max(1, args.warmup), dev)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(inp, w)

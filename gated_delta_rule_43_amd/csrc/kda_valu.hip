@@ -251,10 +251,18 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
 // One workgroup per (sequence n, head h, tile of VT state columns).  Columns
 // [0, V) are the value columns of the state; in summary mode columns
 // [V, V+K) carry the transition (its values are zero, it starts as I).
-template <typename Tin, int C, int VT>
+// Each chunk's operands (W, Qt, Kbar, Aqk, the tile's U columns, gL) are first
+// copied into LDS with coalesced 16-byte loads; the products then read LDS
+// only, 4 channels (or rows) per step.
+template <typename Tin, int C, int KD, int VT, bool SUM>
 __global__ __launch_bounds__(kThreads) void k_state_valu(FwdArgs a) {
-  const int H = a.H, K = a.K, V = a.V;
-  const int ncols = a.summary ? V + K : V;
+  static_assert(VT == 32 && kThreads == 256, "thread layouts below");
+  constexpr int NR = C / 8;            // rows per thread in the row phases
+  constexpr int TPC = kThreads / KD;   // threads per channel in the state update
+  constexpr int JPT = VT / TPC;        // columns per thread in the state update
+  constexpr int KP = KD + 4, CP = C + 4;  // padded rows: the two half-waves hit other banks
+  const int H = a.H, V = a.V;
+  const int ncols = SUM ? V + KD : V;
   const int ntile = ncols / VT;
   const int64_t wid = blockIdx.x;
   const int tile = (int)(wid % ntile);
@@ -262,69 +270,162 @@ __global__ __launch_bounds__(kThreads) void k_state_valu(FwdArgs a) {
   const int h = (int)(nh % H), n = (int)(nh / H);
   const int col0 = tile * VT;
   const int tid = threadIdx.x;
+  constexpr bool out = !SUM;  // summary mode writes no output
 
-  __shared__ float sS[kMaxD][VT];
-  __shared__ float sD[C][VT];
+  __shared__ __attribute__((aligned(16))) float sS[KD][VT];
+  __shared__ __attribute__((aligned(16))) float sD[C][VT];
+  __shared__ __attribute__((aligned(16))) float sW[C][KP];
+  __shared__ __attribute__((aligned(16))) float sQ[C][KP];
+  __shared__ __attribute__((aligned(16))) float sKb[C][KD];
+  __shared__ __attribute__((aligned(16))) float sA[C][CP];
+  __shared__ __attribute__((aligned(16))) float sU[C][VT];
+  __shared__ float sG[KD];
 
-  const int64_t sbase = ((int64_t)n * H + h) * K * V;
-  for (int e = tid; e < K * VT; e += kThreads) {
+  const int64_t sbase = ((int64_t)n * H + h) * KD * V;
+  for (int e = tid; e < KD * VT; e += kThreads) {
     const int c = e / VT, jj = e % VT, col = col0 + jj;
     float s;
     if (col < V)
-      s = (a.init && !a.summary) ? a.init[sbase + (int64_t)c * V + col] : 0.f;
+      s = (a.init && out) ? a.init[sbase + (int64_t)c * V + col] : 0.f;
     else
       s = (c == col - V) ? 1.f : 0.f;
     sS[c][jj] = s;
   }
+  const int jj = tid % VT, rg = tid / VT;           // row phases: column jj, rows rg + 8m
+  const int cs = tid / TPC, j0 = (tid % TPC) * JPT;  // state update: channel cs, columns j0..
   const int jc0 = a.seq_chunk0[n], jc1 = a.seq_chunk0[n + 1];
   for (int j = jc0; j < jc1; ++j) {
     const int64_t chb = (int64_t)j * H + h;
-    const float* W = (const float*)a.W + chb * C * K;
+    const float4* W = (const float4*)((const float*)a.W + chb * C * KD);
+    const float4* Qt = (const float4*)((const float*)a.Qt + chb * C * KD);
+    const float4* Kb = (const float4*)((const float*)a.Kb + chb * C * KD);
+    const float4* Aqk = (const float4*)((const float*)a.Aqk + chb * C * C);
     const float* U = (const float*)a.U + chb * C * V;
-    const float* Qt = (const float*)a.Qt + chb * C * K;
-    const float* Kb = (const float*)a.Kb + chb * C * K;
-    const float* Aqk = (const float*)a.Aqk + chb * C * C;
-    const float* gL = a.gL + chb * K;
     const int tok0 = a.chunk_tok[j], L = a.chunk_len[j];
-    __syncthreads();
-    // Delta = U - W S
-    for (int e = tid; e < C * VT; e += kThreads) {
-      const int r = e / VT, jj = e % VT, col = col0 + jj;
-      float acc = col < V ? U[(int64_t)r * V + col] : 0.f;
-      for (int c = 0; c < K; ++c) acc = fmaf(-W[(int64_t)r * K + c], sS[c][jj], acc);
-      sD[r][jj] = acc;
+    __syncthreads();  // the previous chunk is done with every LDS operand
+    {
+      constexpr int N4 = C * KD / 4 / kThreads;
+      float4 wv[N4], qv[N4];
+#pragma unroll
+      for (int u = 0; u < N4; ++u) {
+        wv[u] = W[tid + kThreads * u];
+        if constexpr (out) qv[u] = Qt[tid + kThreads * u];
+      }
+#pragma unroll
+      for (int u = 0; u < N4; ++u) {
+        const int idx = tid + kThreads * u, r = idx / (KD / 4), c = 4 * (idx % (KD / 4));
+        *(float4*)&sW[r][c] = wv[u];
+        if constexpr (out) *(float4*)&sQ[r][c] = qv[u];
+      }
+      constexpr int NA = (C * C / 4 + kThreads - 1) / kThreads;
+      constexpr int NU = (C * VT / 4 + kThreads - 1) / kThreads;
+      float4 kv[N4], av[NA], uv[NU];
+#pragma unroll
+      for (int u = 0; u < N4; ++u) kv[u] = Kb[tid + kThreads * u];
+#pragma unroll
+      for (int u = 0; u < NA; ++u) {
+        const int idx = tid + kThreads * u;
+        av[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if constexpr (out)
+          if (idx < C * C / 4) av[u] = Aqk[idx];
+      }
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int idx = tid + kThreads * u, r = idx / (VT / 4), c = col0 + 4 * (idx % (VT / 4));
+        uv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (idx < C * VT / 4 && c < V) uv[u] = *(const float4*)(U + (int64_t)r * V + c);
+      }
+      const float gl = tid < KD ? a.gL[chb * KD + tid] : 0.f;
+#pragma unroll
+      for (int u = 0; u < N4; ++u) {
+        const int idx = tid + kThreads * u, r = idx / (KD / 4), c = 4 * (idx % (KD / 4));
+        *(float4*)&sKb[r][c] = kv[u];
+      }
+#pragma unroll
+      for (int u = 0; u < NA; ++u) {
+        const int idx = tid + kThreads * u, r = idx / (C / 4), c = 4 * (idx % (C / 4));
+        if constexpr (out)
+          if (idx < C * C / 4) *(float4*)&sA[r][c] = av[u];
+      }
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const int idx = tid + kThreads * u, r = idx / (VT / 4), c = 4 * (idx % (VT / 4));
+        if (idx < C * VT / 4) *(float4*)&sU[r][c] = uv[u];
+      }
+      if (tid < KD) sG[tid] = gl;
     }
     __syncthreads();
-    // O = Qt S + Aqk Delta  (scale folded into Qt and Aqk)
-    if (!a.summary) {
+    // X = W S and Y = Qt S for rows rg + 8m, column jj; Delta = U - X
+    float xs[NR], ys[NR];
+#pragma unroll
+    for (int m = 0; m < NR; ++m) xs[m] = ys[m] = 0.f;
+    for (int c = 0; c < KD; c += 4) {
+      const float s0 = sS[c][jj], s1 = sS[c + 1][jj], s2 = sS[c + 2][jj], s3 = sS[c + 3][jj];
+#pragma unroll
+      for (int m = 0; m < NR; ++m) {
+        const int r = rg + 8 * m;
+        const float4 w4 = *(const float4*)&sW[r][c];
+        xs[m] = fmaf(w4.x, s0, fmaf(w4.y, s1, fmaf(w4.z, s2, fmaf(w4.w, s3, xs[m]))));
+        if constexpr (out) {
+          const float4 q4 = *(const float4*)&sQ[r][c];
+          ys[m] = fmaf(q4.x, s0, fmaf(q4.y, s1, fmaf(q4.z, s2, fmaf(q4.w, s3, ys[m]))));
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NR; ++m) sD[rg + 8 * m][jj] = sU[rg + 8 * m][jj] - xs[m];
+    __syncthreads();
+    // O = Qt S + Aqk Delta  (scale folded into Qt and Aqk; Aqk is zero above the diagonal)
+    if constexpr (out) {
       Tin* o = (Tin*)a.o;
-      for (int e = tid; e < C * VT; e += kThreads) {
-        const int r = e / VT, jj = e % VT, col = col0 + jj;
+#pragma unroll
+      for (int m = 0; m < NR; ++m) {
+        const int r = rg + 8 * m;
         if (r >= L) continue;
-        float acc = 0.f;
-        for (int c = 0; c < K; ++c) acc = fmaf(Qt[(int64_t)r * K + c], sS[c][jj], acc);
-        for (int i = 0; i <= r; ++i) acc = fmaf(Aqk[(int64_t)r * C + i], sD[i][jj], acc);
-        store_as(o + ((int64_t)(tok0 + r) * H + h) * V + col, acc);
+        float acc = ys[m];
+        for (int i = 0; i <= r; i += 4) {
+          const float4 a4 = *(const float4*)&sA[r][i];
+          acc = fmaf(a4.x, sD[i][jj], fmaf(a4.y, sD[i + 1][jj],
+                fmaf(a4.z, sD[i + 2][jj], fmaf(a4.w, sD[i + 3][jj], acc))));
+        }
+        store_as(o + ((int64_t)(tok0 + r) * H + h) * V + col0 + jj, acc);
       }
     }
     __syncthreads();
-    // S = Diag(gL) S + Kb^T Delta
-    for (int e = tid; e < K * VT; e += kThreads) {
-      const int c = e / VT, jj = e % VT;
-      float acc = gL[c] * sS[c][jj];
-      for (int r = 0; r < L; ++r) acc = fmaf(Kb[(int64_t)r * K + c], sD[r][jj], acc);
-      sS[c][jj] = acc;
+    // S = Diag(gL) S + Kb^T Delta for channel cs, columns j0 .. j0 + JPT - 1
+    {
+      float acc[JPT];
+      const float gc = sG[cs];
+#pragma unroll
+      for (int t = 0; t < JPT; t += 4) {
+        const float4 s4 = *(const float4*)&sS[cs][j0 + t];
+        acc[t] = gc * s4.x; acc[t + 1] = gc * s4.y; acc[t + 2] = gc * s4.z; acc[t + 3] = gc * s4.w;
+      }
+      for (int r = 0; r < L; ++r) {
+        const float kb = sKb[r][cs];
+#pragma unroll
+        for (int t = 0; t < JPT; t += 4) {
+          const float4 d4 = *(const float4*)&sD[r][j0 + t];
+          acc[t] = fmaf(kb, d4.x, acc[t]);
+          acc[t + 1] = fmaf(kb, d4.y, acc[t + 1]);
+          acc[t + 2] = fmaf(kb, d4.z, acc[t + 2]);
+          acc[t + 3] = fmaf(kb, d4.w, acc[t + 3]);
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < JPT; t += 4)
+        *(float4*)&sS[cs][j0 + t] = make_float4(acc[t], acc[t + 1], acc[t + 2], acc[t + 3]);
     }
   }
   __syncthreads();
-  for (int e = tid; e < K * VT; e += kThreads) {
-    const int c = e / VT, jj = e % VT, col = col0 + jj;
-    if (!a.summary) {
-      if (a.fin) a.fin[sbase + (int64_t)c * V + col] = sS[c][jj];
+  for (int e = tid; e < KD * VT; e += kThreads) {
+    const int c = e / VT, jj2 = e % VT, col = col0 + jj2;
+    if constexpr (out) {
+      if (a.fin) a.fin[sbase + (int64_t)c * V + col] = sS[c][jj2];
     } else if (col < V) {
-      a.state_ext[sbase + (int64_t)c * V + col] = sS[c][jj];
+      a.state_ext[sbase + (int64_t)c * V + col] = sS[c][jj2];
     } else {
-      a.transition[((int64_t)n * H + h) * K * K + (int64_t)c * K + (col - V)] = sS[c][jj];
+      a.transition[((int64_t)n * H + h) * KD * KD + (int64_t)c * KD + (col - V)] = sS[c][jj2];
     }
   }
 }
@@ -371,7 +472,16 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
   const int64_t wgs = (int64_t)a.N * a.H * (ncols / VT);
   mark(a, kStageState, 0, s);
   if (wgs > 0 && (a.summary || a.fin || a.NT > 0)) {
-    hipLaunchKernelGGL((k_state_valu<Tin, C, VT>), dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
+    auto launch = [&](auto kd, auto sum) {
+      hipLaunchKernelGGL((k_state_valu<Tin, C, decltype(kd)::value, VT, decltype(sum)::value>),
+                         dim3((unsigned)wgs), dim3(kThreads), 0, s, a);
+    };
+    using K64 = std::integral_constant<int, 64>;
+    using K128 = std::integral_constant<int, 128>;
+    using S0 = std::false_type;
+    using S1 = std::true_type;
+    if (a.K == 64) a.summary ? launch(K64{}, S1{}) : launch(K64{}, S0{});
+    else a.summary ? launch(K128{}, S1{}) : launch(K128{}, S0{});
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   mark(a, kStageState, 1, s);
