@@ -49,6 +49,7 @@ from gated_delta_rule_43_amd import kda, synthetic  # noqa: E402
 METRIC = "KDA chunked fwd Mtokens/s at H=32,dk=dv=128 bf16; MFMA util % of peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector ALU, TFLOP/s
 
 
 def _hip():
@@ -60,15 +61,16 @@ def _hip():
 
 
 class StageEvents:
-    """2*NUM_STAGES hipEvents per timed step, read back after the timed region."""
+    """2*nstages hipEvents per timed step, read back after the timed region."""
 
-    def __init__(self, steps):
+    def __init__(self, steps, nstages=None):
+        self.nstages = kda.NUM_STAGES if nstages is None else nstages
         self.hip = _hip()
         self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                                  ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        n = 2 * kda.NUM_STAGES
+        n = 2 * self.nstages
         self.arrays = []
         for _ in range(steps):
             arr = (ctypes.c_void_p * n)()
@@ -82,9 +84,9 @@ class StageEvents:
 
     def stage_ms(self):
         """Average duration (ms) of each stage over the recorded steps."""
-        out = np.zeros(kda.NUM_STAGES)
+        out = np.zeros(self.nstages)
         for arr in self.arrays:
-            for s in range(kda.NUM_STAGES):
+            for s in range(self.nstages):
                 ms = ctypes.c_float(0.0)
                 rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), arr[2 * s], arr[2 * s + 1])
                 if rc != 0:
@@ -416,6 +418,18 @@ def bench_output_norm(o, w, steps):
             "frac": round(achieved / HBM_PEAK_GBS, 5), "bytes_per_launch": nbytes}
 
 
+def bwd_chunk_flops(C, K, V):
+    """FLOPs one chunk-head of the chunk-gradient kernel must do (full chunk,
+    2 per multiply-add, triangles counted once, exponentials not counted):
+    dW, dQ~ and dKbar (C x K over V each), the S0 . dS_L row sums, P and the V
+    half of Y (lower triangles over V), dV (triangular Tm^T over V), the K half
+    of Y (lower triangle over K), the two triangular products of Tm (C^3/3),
+    and the pairwise q^, k^, gamma terms (4 multiply-adds per pair and channel)."""
+    tri = C * (C + 1) // 2
+    macs = 3 * C * K * V + K * V + 3 * tri * V + tri * K + C ** 3 // 3 + 4 * tri * K
+    return 2 * macs
+
+
 def bench_backward(inp, w, steps, warmup):
     """The backward (kda_bwd) of the same forward on the same resident inputs,
     with a seeded output gradient; events on the launch stream around each call."""
@@ -446,11 +460,33 @@ def bench_backward(inp, w, steps, warmup):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     ms = float(np.mean([a.elapsed_time(b) for a, b in evs]))
+    # the same call with the library's per-stage events (kda_bwd_profiled)
+    sev = StageEvents(steps, kda.BWD_NUM_STAGES)
+    for i in range(steps):
+        kda.kda_bwd(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"], inp["a_log"],
+                    inp["dt_bias"], d_o, None, scale=w.scale, lower_bound=w.lower_bound,
+                    chunk_size=w.chunk_size, cu_seqlens=cu, cu_seqlens_host=cu_host,
+                    initial_state=inp["initial_state"], stage_events=sev.arrays[i])
+    torch.cuda.synchronize()
+    stage_ms = sev.stage_ms()
+    sev.close()
     tokens = w.B * w.T
+    NT = w.B * math.ceil(w.T / w.chunk_size) if cu is None else int(
+        sum(math.ceil(int(b - a) / w.chunk_size) for a, b in zip(cu_host[:-1], cu_host[1:])))
+    kidx = kda.BWD_STAGE_NAMES.index("chunk_gradients")
+    kms = float(stage_ms[kidx])
+    flops = NT * w.H * bwd_chunk_flops(w.chunk_size, w.K, w.V)
+    tflops = flops / (kms / 1e3) / 1e12 if kms > 0 else 0.0
     return {"workload": w.name + " backward (gradients of q, k, v, gate, beta, a_log, dt_bias)",
             "value": round(tokens / (ms / 1e3) / 1e6, 4), "unit": "Mtokens/s",
             "ms_per_step": round(ms, 3), "wall_ms_per_step": round(wall, 3),
-            "arith": "fp32 VALU (both dtypes)"}
+            "arith": "fp32 VALU (both dtypes)",
+            "stage_ms": dict(zip(kda.BWD_STAGE_NAMES, [round(float(x), 4) for x in stage_ms])),
+            "roofline": {"bound": "alu", "achieved": round(tflops, 3),
+                         "peak": FP32_VECTOR_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / FP32_VECTOR_PEAK_TFLOPS, 5), "traffic": None,
+                         "kernel": "chunk_gradients (k_bwd_chunk)", "kernel_ms": round(kms, 4),
+                         "flops_per_launch": flops}}
 
 
 def main():

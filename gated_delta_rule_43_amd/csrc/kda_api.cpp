@@ -550,6 +550,18 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
                    void* dq, void* dk, void* dv, void* dgate, void* dbeta, float* da_log,
                    float* ddt_bias, float* d_initial_state, void* workspace,
                    size_t workspace_bytes, void* stream) {
+  return kda_bwd_profiled(p, q, k, v, gate, beta, a_log, dt_bias, initial_state, d_o,
+                          d_final_state, dq, dk, dv, dgate, dbeta, da_log, ddt_bias,
+                          d_initial_state, workspace, workspace_bytes, stream, nullptr);
+}
+
+kda_status kda_bwd_profiled(const kda_problem* p, const void* q, const void* k, const void* v,
+                            const void* gate, const void* beta, const float* a_log,
+                            const float* dt_bias, const float* initial_state, const void* d_o,
+                            const float* d_final_state, void* dq, void* dk, void* dv,
+                            void* dgate, void* dbeta, float* da_log, float* ddt_bias,
+                            float* d_initial_state, void* workspace, size_t workspace_bytes,
+                            void* stream, void* const* stage_events) {
   kda_status st = validate_problem(p, false);
   if (st != KDA_OK) return st;
   st = check_inputs(p, q, k, v, gate, beta, a_log, dt_bias);
@@ -582,6 +594,7 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
   b.da_part = (float*)(w + L.off_da); b.ddt_part = (float*)(w + L.off_ddt);
   b.dq = dq; b.dk = dk; b.dv = dv; b.dgate = dgate; b.dbeta = dbeta;
   b.da_log = da_log; b.ddt_bias = ddt_bias; b.dinit = d_initial_state;
+  b.events = stage_events;
   hipError_t e = kda::launch_bwd(b, (hipStream_t)stream);
   if (e != hipSuccess) return fail(KDA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   g_last_error.clear();

@@ -729,21 +729,28 @@ __global__ __launch_bounds__(kThreads) void k_bwd_params(BwdArgs b) {
 template <typename Tin, int C>
 hipError_t run(const BwdArgs& b, hipStream_t s) {
   const FwdArgs& a = b.f;
+  bmark(b, kBwdRecompute, 0, s);
   hipError_t e = launch_valu_prep(a, s);
   if (e != hipSuccess) return e;
+  bmark(b, kBwdRecompute, 1, s);
   const int64_t wgs = (int64_t)a.N * a.H * (a.V / 64);
+  bmark(b, kBwdFState, 0, s);
+  if (wgs > 0 && a.NT > 0) {
+    constexpr int NTS = 64 * state_waves(C);
+    if (a.K == 64) hipLaunchKernelGGL((k_bwd_fstate<C, 64>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
+    else hipLaunchKernelGGL((k_bwd_fstate<C, 128>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
+  bmark(b, kBwdFState, 1, s);
+  bmark(b, kBwdDState, 0, s);
   if (wgs > 0) {
-    if (a.NT > 0) {
-      constexpr int NTS = 64 * state_waves(C);
-      if (a.K == 64) hipLaunchKernelGGL((k_bwd_fstate<C, 64>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
-      else hipLaunchKernelGGL((k_bwd_fstate<C, 128>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
-      if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
-    }
     constexpr int NTS = 64 * state_waves(C);
     if (a.K == 64) hipLaunchKernelGGL((k_bwd_dstate<Tin, C, 64>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
     else hipLaunchKernelGGL((k_bwd_dstate<Tin, C, 128>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
+  bmark(b, kBwdDState, 1, s);
+  bmark(b, kBwdChunk, 0, s);
   if (a.NT > 0) {
     const dim3 grid((unsigned)((int64_t)a.NT * a.H));
     constexpr int T64 = chunk_threads(C, 64), T128 = chunk_threads(C, 128);
@@ -751,14 +758,19 @@ hipError_t run(const BwdArgs& b, hipStream_t s) {
     else hipLaunchKernelGGL((k_bwd_chunk<Tin, C, 128, T128>), grid, dim3(T128), 0, s, b);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
+  bmark(b, kBwdChunk, 1, s);
   const int64_t tk = (int64_t)a.B * a.T * a.HK;
+  bmark(b, kBwdQK, 0, s);
   if (tk > 0) {
     hipLaunchKernelGGL((k_bwd_qk<Tin>), dim3((unsigned)((tk + 3) / 4)), dim3(kThreads), 0, s, b);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
+  bmark(b, kBwdQK, 1, s);
   const int64_t hk = (int64_t)a.H * a.K;
+  bmark(b, kBwdParams, 0, s);
   hipLaunchKernelGGL(k_bwd_params, dim3((unsigned)((hk + kThreads - 1) / kThreads)), dim3(kThreads), 0, s, b);
   if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  bmark(b, kBwdParams, 1, s);
   return hipSuccess;
 }
 
@@ -774,8 +786,10 @@ hipError_t run_c(const BwdArgs& b, hipStream_t s) {
 }  // namespace
 
 hipError_t launch_bwd(const BwdArgs& b, hipStream_t s) {
+  bmark(b, kBwdTable, 0, s);
   hipError_t e = launch_chunk_table(b.f, s);
   if (e != hipSuccess) return e;
+  bmark(b, kBwdTable, 1, s);
   return b.f.dtype == 0 ? run_c<float>(b, s) : run_c<bf16>(b, s);
 }
 

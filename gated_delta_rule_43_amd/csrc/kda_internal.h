@@ -114,6 +114,7 @@ struct BwdArgs {
   // outputs
   void *dq, *dk, *dv, *dgate, *dbeta;  // dtype as f.dtype
   float *da_log, *ddt_bias, *dinit;    // fp32; dinit may be nullptr
+  void* const* events;  // 2 * kNumBwdStages hipEvent_t or nullptr (kda_bwd_profiled)
 };
 
 // The gated output norm over rows of V values (o, gate, y: dtype; w: fp32 [V] or null).
@@ -134,6 +135,16 @@ enum Stage { kStageTable = 0, kStagePrologue = 1, kStageChunk = 2, kStageState =
 
 inline void mark(const FwdArgs& a, int stage, int end, hipStream_t s) {
   if (a.events && a.events[2 * stage + end]) hipEventRecord((hipEvent_t)a.events[2 * stage + end], s);
+}
+
+// Stages of one backward, in launch order (timing hooks of kda_bwd_profiled).
+enum BwdStage {
+  kBwdTable = 0, kBwdRecompute = 1, kBwdFState = 2, kBwdDState = 3, kBwdChunk = 4,
+  kBwdQK = 5, kBwdParams = 6, kNumBwdStages = 7
+};
+
+inline void bmark(const BwdArgs& b, int stage, int end, hipStream_t s) {
+  if (b.events && b.events[2 * stage + end]) hipEventRecord((hipEvent_t)b.events[2 * stage + end], s);
 }
 
 // Kernel launchers (return the first HIP error, hipSuccess otherwise).

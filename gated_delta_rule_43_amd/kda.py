@@ -29,11 +29,15 @@ KDA_F32, KDA_BF16 = 0, 1
 OK, EINVAL, EUNSUPPORTED, EWORKSPACE, EHIP = 0, 1, 2, 3, 4
 NUM_STAGES = 4
 STAGE_NAMES = ("chunk_table", "prologue", "chunk_factors", "state_pass")
+# stages of kda_bwd_profiled, in launch order (KDA_BWD_NUM_STAGES)
+BWD_NUM_STAGES = 7
+BWD_STAGE_NAMES = ("chunk_table", "recompute", "forward_states", "reverse_states",
+                   "chunk_gradients", "dq_dk", "param_sums")
 EXPORTED = ("kda_validate", "kda_fwd_workspace_size", "kda_fwd", "kda_fwd_profiled",
             "kda_state_summary_workspace_size", "kda_state_summary",
             "kda_apply_state_summary", "kda_chunk_capacity", "kda_chunk_table",
             "kda_short_conv_silu", "kda_fwd_short_conv_workspace_size", "kda_fwd_short_conv",
-            "kda_bwd_workspace_size", "kda_bwd", "kda_gated_rms_norm",
+            "kda_bwd_workspace_size", "kda_bwd", "kda_bwd_profiled", "kda_gated_rms_norm",
             "kda_last_error", "kda_version")
 MAX_CONV_WIDTH = 4
 
@@ -101,6 +105,8 @@ def load_library(path: Optional[str] = None):
     lib.kda_bwd_workspace_size.restype = S
     lib.kda_bwd.argtypes = [PP] + [P] * 18 + [P, S, P]
     lib.kda_bwd.restype = ctypes.c_int
+    lib.kda_bwd_profiled.argtypes = [PP] + [P] * 18 + [P, S, P, P]
+    lib.kda_bwd_profiled.restype = ctypes.c_int
     lib.kda_gated_rms_norm.argtypes = [PP, P, P, P, ctypes.c_float, I32, P, P]
     lib.kda_gated_rms_norm.restype = ctypes.c_int
     lib.kda_last_error.argtypes = []
@@ -412,11 +418,13 @@ def _fwd(q, k, v, gate, beta, a_log, dt_bias, conv, scale, lower_bound, chunk_si
 
 def kda_bwd(q, k, v, gate, beta, a_log, dt_bias, d_o, d_final_state=None, *, scale=None,
             lower_bound=None, chunk_size=64, cu_seqlens=None, cu_seqlens_host=None,
-            initial_state=None, lower_bound_form="sigmoid", workspace=None):
+            initial_state=None, lower_bound_form="sigmoid", workspace=None, stage_events=None):
     """Gradients of L = sum(d_o * o) + sum(d_final_state * final_state) of kda_fwd
     with the same arguments.  Returns a dict: dq, dk [B,T,H,K], dv [B,T,HV,V],
     dgate [B,T,HV,K], dbeta [B,T,HV] (of the logits; q's dtype), da_log [HV],
-    ddt_bias [HV,K] and dinit [N,HV,K,V] (float32)."""
+    ddt_bias [HV,K] and dinit [N,HV,K,V] (float32).  `stage_events`: optional
+    ctypes array of 2*BWD_NUM_STAGES hipEvent_t handles recorded around each
+    stage (kda_bwd_profiled)."""
     B, T, H, K, V, HV = _check_inputs(q, k, v, gate, beta, a_log, dt_bias)
     lib = load_library()
     device = q.device
@@ -447,11 +455,15 @@ def kda_bwd(q, k, v, gate, beta, a_log, dt_bias, d_o, d_final_state=None, *, sca
         _dev(workspace, "workspace", dtype=torch.uint8)
         ws, nbytes = workspace, workspace.numel()
     ptr = lambda t: None if t is None else t.data_ptr()
-    st = lib.kda_bwd(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ptr(gate), ptr(beta), ptr(a_log),
-                     ptr(dt_bias), ptr(initial_state), ptr(d_o), ptr(d_final_state),
-                     ptr(out["dq"]), ptr(out["dk"]), ptr(out["dv"]), ptr(out["dgate"]),
-                     ptr(out["dbeta"]), ptr(out["da_log"]), ptr(out["ddt_bias"]), ptr(out["dinit"]),
-                     ptr(ws), nbytes, _stream_ptr(device))
+    args = (ctypes.byref(p), ptr(q), ptr(k), ptr(v), ptr(gate), ptr(beta), ptr(a_log),
+            ptr(dt_bias), ptr(initial_state), ptr(d_o), ptr(d_final_state),
+            ptr(out["dq"]), ptr(out["dk"]), ptr(out["dv"]), ptr(out["dgate"]),
+            ptr(out["dbeta"]), ptr(out["da_log"]), ptr(out["ddt_bias"]), ptr(out["dinit"]),
+            ptr(ws), nbytes, _stream_ptr(device))
+    if stage_events is None:
+        st = lib.kda_bwd(*args)
+    else:
+        st = lib.kda_bwd_profiled(*args, stage_events)
     if st:
         _raise(st, "kda_bwd")
     return out

@@ -245,6 +245,27 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
                    size_t workspace_bytes, void* stream);
 
 /*
+ * kda_bwd with per-stage timing hooks, for measurement.  It does exactly the
+ * work of kda_bwd; in addition, when stage_events is not NULL it must hold
+ * 2 * KDA_BWD_NUM_STAGES hipEvent_t handles created by the caller (entries may
+ * be NULL), and the library records stage_events[2*i] on `stream` just before
+ * stage i is enqueued and stage_events[2*i+1] just after.  Stages, in order:
+ *   0 chunk table, 1 recomputation of the forward's chunk factors,
+ *   2 forward state pass (state entering each chunk), 3 reverse state pass,
+ *   4 chunk-local gradients, 5 dq/dk (group sums and the L2 norm's Jacobian),
+ *   6 da_log and ddt_bias sums.
+ * A stage with nothing to launch records both events back to back.
+ */
+#define KDA_BWD_NUM_STAGES 7
+kda_status kda_bwd_profiled(const kda_problem* p, const void* q, const void* k, const void* v,
+                            const void* gate, const void* beta, const float* a_log,
+                            const float* dt_bias, const float* initial_state, const void* d_o,
+                            const float* d_final_state, void* dq, void* dk, void* dv,
+                            void* dgate, void* dbeta, float* da_log, float* ddt_bias,
+                            float* d_initial_state, void* workspace, size_t workspace_bytes,
+                            void* stream, void* const* stage_events);
+
+/*
  * The layer's short convolution before the forward: SiLU of a causal
  * depthwise convolution over time, applied per channel to q, k and v
  * (hyper_parallel coverage page: `_run_causal_short_conv`,

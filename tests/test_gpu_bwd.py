@@ -166,3 +166,26 @@ def test_bwd_device_only_offsets_match_host_checked():
     torch.cuda.synchronize()
     for n in NAMES:
         assert torch.equal(a[n], b[n]), n
+
+
+def test_bwd_profiled_same_bits_and_stage_times():
+    """kda_bwd_profiled does exactly kda_bwd's work: identical bits, and every
+    stage's pair of events is recorded in order on the launch stream."""
+    import bench
+    _banner("bwd profiled")
+    inp = to_device(synthetic.random_problem(40, 1, 300, 2, 128, 128, dtype=torch.bfloat16,
+                                             lengths=[100, 200], init_std=0.5))
+    d_o, d_fin = _upstream(inp, 10)
+    args = (inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"], inp["a_log"], inp["dt_bias"],
+            d_o, d_fin)
+    kw = dict(cu_seqlens=inp["cu_seqlens"], initial_state=inp["initial_state"])
+    a = kda.kda_bwd(*args, **kw)
+    ev = bench.StageEvents(1, kda.BWD_NUM_STAGES)
+    b = kda.kda_bwd(*args, stage_events=ev.arrays[0], **kw)
+    torch.cuda.synchronize()
+    ms = ev.stage_ms()
+    ev.close()
+    for n in NAMES:
+        assert torch.equal(a[n], b[n]), n
+    assert ms.shape == (kda.BWD_NUM_STAGES,) and np.all(ms >= 0), ms
+    assert ms[kda.BWD_STAGE_NAMES.index("chunk_gradients")] > 0, ms
