@@ -66,6 +66,12 @@ __device__ inline void gate_grad(float x, float alog, int form, float lb, float*
   *dgda = ga;
 }
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+// fp32 matrix-core product of one 16 x 4 by 4 x 16 step into a 16 x 16 tile
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
 __device__ inline float wave_sum(float x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
@@ -345,12 +351,173 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   for (int p = tid; p < C * C; p += NT) sT[p / C][p % C] = a.Tm_out[chb * C * C + p];
 
   // ---- phase B: products over the value dimension, and dV, in two sweeps over
-  //      the value tiles (dW and dQ~; then dKbar, P, the V half of Y and dV) so
-  //      that each keeps about 64 accumulators live ----
+  //      32-column value tiles staged in LDS (dW and dQ~; then dKbar, P, the V
+  //      half of Y and dV).  For C = 64 the products run on the matrix cores in
+  //      fp32 (v_mfma_f32_16x16x4f32, one 16 x 16 output tile per accumulator;
+  //      lane l holds A[l%16][l/16], B[l/16][l%16] and D[4(l/16)+e][l%16]),
+  //      each wave owning fixed output tiles; results reach the thread layouts
+  //      below through LDS.  Smaller chunks keep per-thread VALU accumulators.
   const int c1 = tid % K, rb1 = tid / K;       // C x K layout
   const int i2 = tid % C, rb2 = tid / C;       // C x C layout
   Tin* dv = (Tin*)b.dv;
   float dqs[NE1];  // scale dO S0^T, kept until phase F
+  float dkb[NE1], sd = 0.f;
+  if constexpr (C == 64) {
+    constexpr int NW = NT / 64;
+    const int lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
+    // dW, dQ~ and dKbar tiles: row tile rt, column tiles 2 (w / 4) + {0, 1}
+    static_assert(2 * NW * 16 * 16 == C * K, "two output tiles per wave and product");
+    const int rt = w & 3, ct0 = 2 * (w >> 2);
+    // sweep 1: M1 = dDelta S0^T (-> -dW), M2 = dO S0^T (-> dQ~)
+    f32x4 m1[2], m2[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) m1[t] = m2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < V; j0 += VTL) {
+      __syncthreads();
+      for (int e = tid; e < K * VTL; e += NT) {
+        const int c = e / VTL, jj = e % VTL;
+        tS0[c][jj] = S0[(int64_t)c * V + j0 + jj];
+      }
+      for (int e = tid; e < C * VTL; e += NT) {
+        const int r = e / VTL, jj = e % VTL;
+        tdD[r][jj] = dDl[(int64_t)r * V + j0 + jj];
+        tdO[r][jj] = r < L ? load_f32(dO + th(r) * V + j0 + jj) : 0.f;
+      }
+      __syncthreads();
+#pragma unroll
+      for (int jj = 0; jj < VTL; jj += 4) {
+        const float ad = tdD[16 * rt + ln][jj + lg], ao = tdO[16 * rt + ln][jj + lg];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const float bs = tS0[16 * (ct0 + t) + ln][jj + lg];
+          m1[t] = mfma_f32(ad, bs, m1[t]);
+          m2[t] = mfma_f32(ao, bs, m2[t]);
+        }
+      }
+    }
+    __syncthreads();  // the tiles are dead: dW, and dQ~ on its way to registers
+    float (*sX)[K] = (float(*)[K])(sReg + C * K);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * lg + e, c = 16 * (ct0 + t) + ln;
+        sDW[r][c] = -m1[t][e];
+        sX[r][c] = scale * m2[t][e];
+      }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NE1; ++m) dqs[m] = sX[rb1 + RSTEP1 * m][c1];
+    // sweep 2: M3 = Delta dS_L^T (-> dKbar), P = dO Delta^T and Yv = dDelta V^T
+    // (lower tiles only), dV = Diag(beta) Tm^T dDelta per value tile
+    float* sReg2 = sReg + C * K;
+    float (*tdSL2)[VTL + 1] = (float(*)[VTL + 1])sReg2;
+    float (*tD2)[TS] = (float(*)[TS])(sReg2 + K * (VTL + 1));
+    float (*tdO2)[TS] = (float(*)[TS])(sReg2 + K * (VTL + 1) + C * TS);
+    float (*tdD2)[TS] = (float(*)[TS])(sReg2 + K * (VTL + 1) + 2 * C * TS);
+    float (*tv2)[TS] = (float(*)[TS])(sReg2 + K * (VTL + 1) + 3 * C * TS);
+    float (*tS02)[VTL + 1] = (float(*)[VTL + 1])(sReg2 + K * (VTL + 1) + 4 * C * TS);
+    constexpr int NTRI = 10;                  // lower 16 x 16 tiles (rt >= it) of a 64 x 64 matrix
+    constexpr int NPY = (NTRI + NW - 1) / NW;  // P and Yv tile pairs per wave
+    f32x4 m3[2], pt[NPY], yt[NPY];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) m3[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < NPY; ++u) pt[u] = yt[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    auto tri_tile = [](int t, int& r, int& i) {  // t = R (R + 1) / 2 + I, I <= R
+      r = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+      i = t - r * (r + 1) / 2;
+    };
+    // dV tile of this wave (waves 0..7): row tile w / 2, column tile w % 2 of the value tile
+    const bool has_dv = w < 8;
+    const int vrt = (w >> 1) & 3, vct = w & 1;
+    for (int j0 = 0; j0 < V; j0 += VTL) {
+      __syncthreads();
+      for (int e = tid; e < K * VTL; e += NT) {
+        const int c = e / VTL, jj = e % VTL;
+        tdSL2[c][jj] = dSL[(int64_t)c * V + j0 + jj];
+        tS02[c][jj] = S0[(int64_t)c * V + j0 + jj];
+      }
+      for (int e = tid; e < C * VTL; e += NT) {
+        const int r = e / VTL, jj = e % VTL;
+        const bool in = r < L;
+        tdD2[r][jj] = dDl[(int64_t)r * V + j0 + jj];
+        tD2[r][jj] = Dl[(int64_t)r * V + j0 + jj];
+        tdO2[r][jj] = in ? load_f32(dO + th(r) * V + j0 + jj) : 0.f;
+        tv2[r][jj] = in ? load_f32(v + th(r) * V + j0 + jj) : 0.f;
+      }
+      __syncthreads();
+      if (tid < K) {
+        const int c = tid;
+#pragma unroll 8
+        for (int jj = 0; jj < VTL; ++jj) sd = fmaf(tS02[c][jj], tdSL2[c][jj], sd);
+      }
+#pragma unroll
+      for (int jj = 0; jj < VTL; jj += 4) {
+        const float ad = tD2[16 * rt + ln][jj + lg];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) m3[t] = mfma_f32(ad, tdSL2[16 * (ct0 + t) + ln][jj + lg], m3[t]);
+#pragma unroll
+        for (int u = 0; u < NPY; ++u) {
+          const int t = w + NW * u;
+          if (t < NTRI) {
+            int R, I;
+            tri_tile(t, R, I);
+            pt[u] = mfma_f32(tdO2[16 * R + ln][jj + lg], tD2[16 * I + ln][jj + lg], pt[u]);
+            yt[u] = mfma_f32(tdD2[16 * R + ln][jj + lg], tv2[16 * I + ln][jj + lg], yt[u]);
+          }
+        }
+      }
+      if (has_dv) {
+        // dV rows 16 vrt .. + 15, value columns j0 + 16 vct .. + 15: the sum over
+        // a >= r of Tm[a][r] dDelta[a][j] (Tm is lower triangular)
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int a0 = 16 * vrt; a0 < C; a0 += 4)
+          acc = mfma_f32(sT[a0 + lg][16 * vrt + ln], tdD2[a0 + lg][16 * vct + ln], acc);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * vrt + 4 * lg + e;
+          if (r < L) store_as(dv + th(r) * V + j0 + 16 * vct + ln, sB[r] * acc[e]);
+        }
+      }
+    }
+    __syncthreads();  // the tiles are dead: dKbar on its way to registers
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sX[16 * rt + 4 * lg + e][16 * (ct0 + t) + ln] = m3[t][e];
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NE1; ++m) dkb[m] = sX[rb1 + RSTEP1 * m][c1];
+    __syncthreads();  // sX is dead: P, Y and K~^T take its place
+#pragma unroll
+  for (int m = 0; m < NE1; ++m) {
+    const int r = rb1 + RSTEP1 * m;
+    sKtT[c1][r] = r < L ? a.kn[th(r) * K + c1] * __expf(sGam[r][c1]) : 0.f;
+  }
+    // P (scaled) and the V half of Y, lower triangle i <= r < L; zero elsewhere
+    for (int e = tid; e < C * C; e += NT) {
+      const int r = e / C, i = e % C;
+      if ((i >> 4) > (r >> 4)) sP[r][i] = sY[r][i] = 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < NPY; ++u) {
+      const int t = w + NW * u;
+      if (t < NTRI) {
+        int R, I;
+        tri_tile(t, R, I);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * R + 4 * lg + e, i = 16 * I + ln;
+          const bool low = i <= r && r < L;
+          sP[r][i] = low ? scale * pt[u][e] : 0.f;
+          sY[r][i] = low ? yt[u][e] : 0.f;
+        }
+      }
+    }
+    if (tid < K) sSd[tid] = sd;
+    __syncthreads();
+  } else {
   {
     float dw[NE1], dqt[NE1];
 #pragma unroll
@@ -395,7 +562,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   float (*tdD2)[TS] = (float(*)[TS])(sReg2 + K * (VTL + 1) + 2 * C * TS);
   float (*tv2)[TS] = (float(*)[TS])(sReg2 + K * (VTL + 1) + 3 * C * TS);
   float (*tS02)[VTL + 1] = (float(*)[VTL + 1])(sReg2 + K * (VTL + 1) + 4 * C * TS);
-  float dkb[NE1], pp[NE2], yv[NE2], sd = 0.f;
+  float pp[NE2], yv[NE2];
 #pragma unroll
   for (int m = 0; m < NE1; ++m) dkb[m] = 0.f;
 #pragma unroll
@@ -467,6 +634,8 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   }
   if (tid < K) sSd[tid] = sd;
   __syncthreads();
+
+  }
 
   // ---- phase C: Y += dW K~^T (i <= r) ----
 #pragma unroll
