@@ -107,15 +107,32 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
 
   auto tok_off = [&](int r) { return ((int64_t)(tok0 + r) * H + h); };
 
-  // gamma: chunk-local inclusive cumsum; rows >= L repeat gamma_{L-1}
-  for (int c = tid; c < K; c += kThreads) {
-    float acc = 0.f;
-    for (int r = 0; r < C; ++r) {
-      if (r < L) acc += a.g[tok_off(r) * K + c];
-      sG[r][c] = acc;
+  // gamma: chunk-local inclusive cumsum; rows >= L repeat gamma_{L-1}.  The
+  // chunk's g values reach LDS first, read by all threads four at a time (one
+  // memory latency instead of one per row), then each channel's thread adds
+  // down its column in LDS.
+  for (int p0 = 0; p0 < C * K; p0 += 4 * kThreads) {
+    float gv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = p0 + tid + u * kThreads, r = p / K, c = p % K;
+      gv[u] = (p < C * K && r < L) ? a.g[tok_off(r) * K + c] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = p0 + tid + u * kThreads;
+      if (p < C * K) sG[p / K][p % K] = gv[u];
     }
   }
   for (int r = tid; r < C; r += kThreads) sB[r] = r < L ? a.bt[tok_off(r)] : 0.f;
+  __syncthreads();
+  for (int c = tid; c < K; c += kThreads) {
+    float acc = 0.f;
+    for (int r = 0; r < C; ++r) {
+      acc += sG[r][c];
+      sG[r][c] = acc;
+    }
+  }
   __syncthreads();
 
   const int64_t chb = (int64_t)j * H + h;  // chunk-head index
@@ -234,15 +251,28 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
   }
   float* U = (float*)a.U + chb * C * V;
   const Tin* v = (const Tin*)a.v;
+  // Diag(beta) V goes to LDS in X's place (read once, coalesced, four loads in
+  // flight per thread), then U's rows read it from there
+  __syncthreads();  // X is no longer read
+  for (int p0 = 0; p0 < C * V; p0 += 4 * kThreads) {
+    float vv[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = p0 + tid + u * kThreads, i = p / V, c = p % V;
+      vv[u] = (p < C * V && i < L) ? load_f32(v + tok_off(i) * V + c) : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int p = p0 + tid + u * kThreads, i = p / V;
+      if (p < C * V) sG[i][p % V] = i < L ? sB[i] * vv[u] : 0.f;
+    }
+  }
+  __syncthreads();
   {
     const int c = tid % V, r0 = tid / V, rs = kThreads / V;
-    float vc[C];
-#pragma unroll
-    for (int i = 0; i < C; ++i) vc[i] = i < L ? sB[i] * load_f32(v + tok_off(i) * V + c) : 0.f;
     for (int r = r0; r < C; r += rs) {
       float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < C; ++i) acc = (i <= r) ? fmaf(sA[r][i], vc[i], acc) : acc;
+      for (int i = 0; i <= r; ++i) acc = fmaf(sA[r][i], sG[i][c], acc);
       U[(int64_t)r * V + c] = acc;
     }
   }
