@@ -270,6 +270,133 @@ __global__ __launch_bounds__(64 * state_waves(C)) void k_bwd_dstate(BwdArgs b) {
     for (int m = 0; m < RS; ++m) b.dinit[sbase + (int64_t)(w * RS + m) * V + col] = ds[m];
 }
 
+// The reverse state pass for 64-token chunks on fp32 matrix cores
+// (v_mfma_f32_16x16x4f32), same arithmetic as k_bwd_dstate up to the order of
+// additions.  One workgroup of 16 waves per (sequence, head, 64 columns); the
+// state gradient dS (K x 64) lives in accumulator tiles, K/64 per wave (state
+// row tile (w*TPW+t)/4, column tile (w*TPW+t)%4); per chunk, wave w computes
+// one 16 x 16 tile of dDelta (row tile w/4, column tile w%4).  Operands come
+// from LDS rows padded so that the 16 lanes of a fragment column hit
+// different banks.
+template <typename Tin, int K>
+__global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
+  constexpr int C = 64, NT = 1024, VT = 64;
+  constexpr int TPW = K / 64;                     // state tiles per wave
+  constexpr int SP = VT + 16, AP = C + 4, KP = K + 4;
+  const FwdArgs& a = b.f;
+  const int H = a.H, V = a.V;
+  const int ntile = V / VT;
+  const int64_t wid = blockIdx.x;
+  const int tile = (int)(wid % ntile);
+  const int64_t nh = wid / ntile;
+  const int h = (int)(nh % H), n = (int)(nh / H);
+  const int col0 = tile * VT;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
+  __shared__ __attribute__((aligned(16))) float sS[K][SP];   // dS
+  __shared__ __attribute__((aligned(16))) float sO[C][SP];   // dO
+  __shared__ __attribute__((aligned(16))) float sD[C][SP];   // dDelta
+  __shared__ __attribute__((aligned(16))) float sR[2 * C * KP];  // Aqk | Kbar, then Qt | W
+  float (*sA)[AP] = (float(*)[AP])sR;
+  float (*sKb)[KP] = (float(*)[KP])(sR + C * AP);
+  float (*sQt)[KP] = (float(*)[KP])sR;
+  float (*sW)[KP] = (float(*)[KP])(sR + C * KP);
+  static_assert(C * AP + C * KP <= 2 * C * KP, "Aqk and Kbar fit the operand region");
+  // copy a [C][D] fp32 matrix into LDS rows of stride P (D, P multiples of 4)
+  auto stage_pad = [&](float* dst, const float* src, int D, int P) {
+    for (int e = tid; e < C * D / 4; e += NT) {
+      const int r = e / (D / 4), c4 = e % (D / 4);
+      *(float4*)(dst + r * P + 4 * c4) = ((const float4*)src)[e];
+    }
+  };
+  const int64_t sbase = ((int64_t)n * H + h) * K * V;
+  f32x4 st[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int s = w * TPW + t, srt = s >> 2, sct = s & 3;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = 16 * srt + 4 * lg + e, col = col0 + 16 * sct + ln;
+      st[t][e] = b.d_fin ? b.d_fin[sbase + (int64_t)c * V + col] : 0.f;
+    }
+  }
+  const int drt = w >> 2, dct = w & 3;  // this wave's dDelta tile
+  const Tin* dO = (const Tin*)b.d_o;
+  const int jc0 = a.seq_chunk0[n], jc1 = a.seq_chunk0[n + 1];
+  for (int j = jc1 - 1; j >= jc0; --j) {
+    const int64_t chb = (int64_t)j * H + h;
+    const float* gL = a.gL + chb * K;
+    float* dhc = b.dhc + chb * K * V;
+    float* dDc = b.dDc + chb * C * V;
+    const int tok0 = a.chunk_tok[j], L = a.chunk_len[j];
+    __syncthreads();  // the previous chunk is done with sR, sO, sD, sS
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int s = w * TPW + t, srt = s >> 2, sct = s & 3;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 16 * srt + 4 * lg + e, cc = 16 * sct + ln;
+        dhc[(int64_t)c * V + col0 + cc] = st[t][e];
+        sS[c][cc] = st[t][e];
+      }
+    }
+    for (int e = tid; e < C * VT; e += NT) {
+      const int r = e / VT, cc = e % VT;
+      sO[r][cc] = r < L ? load_f32(dO + ((int64_t)(tok0 + r) * H + h) * V + col0 + cc) : 0.f;
+    }
+    stage_pad(&sA[0][0], (const float*)a.Aqk + chb * C * C, C, AP);
+    stage_pad(&sKb[0][0], (const float*)a.Kb + chb * C * K, K, KP);
+    __syncthreads();
+    // dDelta = Aqk_s^T dO + Kbar dS_L (Aqk_s is zero above the diagonal, so
+    // rows rr below the tile's first row contribute nothing)
+    {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int rr = 16 * drt; rr < C; rr += 4)
+        acc = mfma_f32(sA[rr + lg][16 * drt + ln], sO[rr + lg][16 * dct + ln], acc);
+#pragma unroll 8
+      for (int c = 0; c < K; c += 4)
+        acc = mfma_f32(sKb[16 * drt + ln][c + lg], sS[c + lg][16 * dct + ln], acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * drt + 4 * lg + e, cc = 16 * dct + ln;
+        sD[r][cc] = acc[e];
+        dDc[(int64_t)r * V + col0 + cc] = acc[e];
+      }
+    }
+    __syncthreads();  // dDelta complete; Aqk and Kbar are no longer read
+    stage_pad(&sQt[0][0], (const float*)a.Qt + chb * C * K, K, KP);
+    stage_pad(&sW[0][0], (const float*)a.W + chb * C * K, K, KP);
+    float gl[TPW][4];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gl[t][e] = gL[16 * ((w * TPW + t) >> 2) + 4 * lg + e];
+    __syncthreads();
+    // dS0 = Diag(gL) dS_L + Qt_s^T dO - W^T dDelta (rows past the chunk end are zero)
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st[t][e] *= gl[t][e];
+#pragma unroll 4
+    for (int r = 0; r < C; r += 4) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int s = w * TPW + t, srt = s >> 2, sct = s & 3;
+        st[t] = mfma_f32(sQt[r + lg][16 * srt + ln], sO[r + lg][16 * sct + ln], st[t]);
+        st[t] = mfma_f32(-sW[r + lg][16 * srt + ln], sD[r + lg][16 * sct + ln], st[t]);
+      }
+    }
+  }
+  if (b.dinit) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int s = w * TPW + t, srt = s >> 2, sct = s & 3;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        b.dinit[sbase + (int64_t)(16 * srt + 4 * lg + e) * V + col0 + 16 * sct + ln] = st[t][e];
+    }
+  }
+}
+
 // Chunk-local gradients.  One workgroup per chunk-head.
 //
 // Thread layouts (NT threads): C x K elements (r, c) are owned as c = tid % K,
@@ -914,8 +1041,13 @@ hipError_t run(const BwdArgs& b, hipStream_t s) {
   bmark(b, kBwdDState, 0, s);
   if (wgs > 0) {
     constexpr int NTS = 64 * state_waves(C);
-    if (a.K == 64) hipLaunchKernelGGL((k_bwd_dstate<Tin, C, 64>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
-    else hipLaunchKernelGGL((k_bwd_dstate<Tin, C, 128>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
+    if constexpr (C == 64) {
+      if (a.K == 64) hipLaunchKernelGGL((k_bwd_dstate_mfma<Tin, 64>), dim3((unsigned)wgs), dim3(1024), 0, s, b);
+      else hipLaunchKernelGGL((k_bwd_dstate_mfma<Tin, 128>), dim3((unsigned)wgs), dim3(1024), 0, s, b);
+    } else {
+      if (a.K == 64) hipLaunchKernelGGL((k_bwd_dstate<Tin, C, 64>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
+      else hipLaunchKernelGGL((k_bwd_dstate<Tin, C, 128>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
+    }
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   bmark(b, kBwdDState, 1, s);
