@@ -167,6 +167,102 @@ __global__ __launch_bounds__(64 * state_waves(C)) void k_bwd_fstate(BwdArgs b) {
   }
 }
 
+// The forward state pass for 64-token chunks on fp32 matrix cores, same
+// arithmetic as k_bwd_fstate up to the order of additions: the state (K x 64
+// columns) lives in accumulator tiles, K/64 per wave; per chunk, wave w
+// computes one 16 x 16 tile of Delta (row tile w/4, column tile w%4).
+template <int K>
+__global__ __launch_bounds__(1024) void k_bwd_fstate_mfma(BwdArgs b) {
+  constexpr int C = 64, NT = 1024, VT = 64;
+  constexpr int TPW = K / 64;
+  constexpr int SP = VT + 16, KP = K + 4;
+  const FwdArgs& a = b.f;
+  const int H = a.H, V = a.V;
+  const int ntile = V / VT;
+  const int64_t wid = blockIdx.x;
+  const int tile = (int)(wid % ntile);
+  const int64_t nh = wid / ntile;
+  const int h = (int)(nh % H), n = (int)(nh / H);
+  const int col0 = tile * VT;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
+  __shared__ __attribute__((aligned(16))) float sS[K][SP];
+  __shared__ __attribute__((aligned(16))) float sD[C][SP];
+  __shared__ __attribute__((aligned(16))) float sW[C][KP];
+  __shared__ __attribute__((aligned(16))) float sKb[C][KP];
+  auto stage_pad = [&](float* dst, const float* src) {
+    for (int e = tid; e < C * K / 4; e += NT) {
+      const int r = e / (K / 4), c4 = e % (K / 4);
+      *(float4*)(dst + r * KP + 4 * c4) = ((const float4*)src)[e];
+    }
+  };
+  const int64_t sbase = ((int64_t)n * H + h) * K * V;
+  f32x4 st[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int s = w * TPW + t, srt = s >> 2, sct = s & 3;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = 16 * srt + 4 * lg + e, col = col0 + 16 * sct + ln;
+      st[t][e] = a.init ? a.init[sbase + (int64_t)c * V + col] : 0.f;
+    }
+  }
+  const int drt = w >> 2, dct = w & 3;  // this wave's Delta tile
+  const int jc0 = a.seq_chunk0[n], jc1 = a.seq_chunk0[n + 1];
+  for (int j = jc0; j < jc1; ++j) {
+    const int64_t chb = (int64_t)j * H + h;
+    const float* U = (const float*)a.U + chb * C * V;
+    const float* gL = a.gL + chb * K;
+    float* hc = b.hc + chb * K * V;
+    float* Dc = b.Dc + chb * C * V;
+    __syncthreads();  // the previous chunk is done with sW, sKb, sS, sD
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int s = w * TPW + t, srt = s >> 2, sct = s & 3;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int c = 16 * srt + 4 * lg + e, cc = 16 * sct + ln;
+        hc[(int64_t)c * V + col0 + cc] = st[t][e];
+        sS[c][cc] = st[t][e];
+      }
+    }
+    stage_pad(&sW[0][0], (const float*)a.W + chb * C * K);
+    stage_pad(&sKb[0][0], (const float*)a.Kb + chb * C * K);
+    f32x4 acc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = U[(int64_t)(16 * drt + 4 * lg + e) * V + col0 + 16 * dct + ln];
+    float gl[TPW][4];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gl[t][e] = gL[16 * ((w * TPW + t) >> 2) + 4 * lg + e];
+    __syncthreads();
+    // Delta = U - W S
+#pragma unroll 8
+    for (int c = 0; c < K; c += 4)
+      acc = mfma_f32(-sW[16 * drt + ln][c + lg], sS[c + lg][16 * dct + ln], acc);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int r = 16 * drt + 4 * lg + e, cc = 16 * dct + ln;
+      sD[r][cc] = acc[e];
+      Dc[(int64_t)r * V + col0 + cc] = acc[e];
+    }
+    __syncthreads();
+    // S = Diag(gL) S + Kbar^T Delta (rows past the chunk end are zero)
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st[t][e] *= gl[t][e];
+#pragma unroll 4
+    for (int r = 0; r < C; r += 4) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int s = w * TPW + t, srt = s >> 2, sct = s & 3;
+        st[t] = mfma_f32(sKb[r + lg][16 * srt + ln], sD[r + lg][16 * sct + ln], st[t]);
+      }
+    }
+  }
+}
+
 // Reverse state pass: dS_L and dDelta of every chunk, and the initial state's
 // gradient.  Same layout as the forward pass; Aqk and Kbar, then Qt and W,
 // take turns in one LDS region.
@@ -1033,8 +1129,13 @@ hipError_t run(const BwdArgs& b, hipStream_t s) {
   bmark(b, kBwdFState, 0, s);
   if (wgs > 0 && a.NT > 0) {
     constexpr int NTS = 64 * state_waves(C);
-    if (a.K == 64) hipLaunchKernelGGL((k_bwd_fstate<C, 64>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
-    else hipLaunchKernelGGL((k_bwd_fstate<C, 128>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
+    if constexpr (C == 64) {
+      if (a.K == 64) hipLaunchKernelGGL((k_bwd_fstate_mfma<64>), dim3((unsigned)wgs), dim3(1024), 0, s, b);
+      else hipLaunchKernelGGL((k_bwd_fstate_mfma<128>), dim3((unsigned)wgs), dim3(1024), 0, s, b);
+    } else {
+      if (a.K == 64) hipLaunchKernelGGL((k_bwd_fstate<C, 64>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
+      else hipLaunchKernelGGL((k_bwd_fstate<C, 128>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
+    }
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   bmark(b, kBwdFState, 1, s);
