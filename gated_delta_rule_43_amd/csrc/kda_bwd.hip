@@ -595,17 +595,39 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     f32x4 m1[2], m2[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) m1[t] = m2[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // each value tile is read into registers one tile ahead, so its loads are
+    // in flight while the previous tile's products run
+    constexpr int NS = K * VTL / NT, NR = C * VTL / NT;
+    static_assert(NS * NT == K * VTL && NR * NT == C * VTL, "whole tiles per thread");
+    float ps[NS], pd[NR], po[NR];
+    auto fetch1 = [&](int j0) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        const int e = tid + NT * u, c = e / VTL, jj = e % VTL;
+        ps[u] = S0[(int64_t)c * V + j0 + jj];
+      }
+#pragma unroll
+      for (int u = 0; u < NR; ++u) {
+        const int e = tid + NT * u, r = e / VTL, jj = e % VTL;
+        pd[u] = dDl[(int64_t)r * V + j0 + jj];
+        po[u] = r < L ? load_f32(dO + th(r) * V + j0 + jj) : 0.f;
+      }
+    };
+    fetch1(0);
     for (int j0 = 0; j0 < V; j0 += VTL) {
       __syncthreads();
-      for (int e = tid; e < K * VTL; e += NT) {
-        const int c = e / VTL, jj = e % VTL;
-        tS0[c][jj] = S0[(int64_t)c * V + j0 + jj];
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        const int e = tid + NT * u;
+        tS0[e / VTL][e % VTL] = ps[u];
       }
-      for (int e = tid; e < C * VTL; e += NT) {
-        const int r = e / VTL, jj = e % VTL;
-        tdD[r][jj] = dDl[(int64_t)r * V + j0 + jj];
-        tdO[r][jj] = r < L ? load_f32(dO + th(r) * V + j0 + jj) : 0.f;
+#pragma unroll
+      for (int u = 0; u < NR; ++u) {
+        const int e = tid + NT * u;
+        tdD[e / VTL][e % VTL] = pd[u];
+        tdO[e / VTL][e % VTL] = po[u];
       }
+      if (j0 + VTL < V) fetch1(j0 + VTL);
       __syncthreads();
 #pragma unroll
       for (int jj = 0; jj < VTL; jj += 4) {
@@ -654,21 +676,42 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     // dV tile of this wave (waves 0..7): row tile w / 2, column tile w % 2 of the value tile
     const bool has_dv = w < 8;
     const int vrt = (w >> 1) & 3, vct = w & 1;
+    float qs[NS], ql[NS], qd[NR], qD[NR], qo[NR], qv[NR];
+    auto fetch2 = [&](int j0) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        const int e = tid + NT * u, c = e / VTL, jj = e % VTL;
+        ql[u] = dSL[(int64_t)c * V + j0 + jj];
+        qs[u] = S0[(int64_t)c * V + j0 + jj];
+      }
+#pragma unroll
+      for (int u = 0; u < NR; ++u) {
+        const int e = tid + NT * u, r = e / VTL, jj = e % VTL;
+        const bool in = r < L;
+        qd[u] = dDl[(int64_t)r * V + j0 + jj];
+        qD[u] = Dl[(int64_t)r * V + j0 + jj];
+        qo[u] = in ? load_f32(dO + th(r) * V + j0 + jj) : 0.f;
+        qv[u] = in ? load_f32(v + th(r) * V + j0 + jj) : 0.f;
+      }
+    };
+    fetch2(0);
     for (int j0 = 0; j0 < V; j0 += VTL) {
       __syncthreads();
-      for (int e = tid; e < K * VTL; e += NT) {
-        const int c = e / VTL, jj = e % VTL;
-        tdSL2[c][jj] = dSL[(int64_t)c * V + j0 + jj];
-        tS02[c][jj] = S0[(int64_t)c * V + j0 + jj];
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        const int e = tid + NT * u;
+        tdSL2[e / VTL][e % VTL] = ql[u];
+        tS02[e / VTL][e % VTL] = qs[u];
       }
-      for (int e = tid; e < C * VTL; e += NT) {
-        const int r = e / VTL, jj = e % VTL;
-        const bool in = r < L;
-        tdD2[r][jj] = dDl[(int64_t)r * V + j0 + jj];
-        tD2[r][jj] = Dl[(int64_t)r * V + j0 + jj];
-        tdO2[r][jj] = in ? load_f32(dO + th(r) * V + j0 + jj) : 0.f;
-        tv2[r][jj] = in ? load_f32(v + th(r) * V + j0 + jj) : 0.f;
+#pragma unroll
+      for (int u = 0; u < NR; ++u) {
+        const int e = tid + NT * u;
+        tdD2[e / VTL][e % VTL] = qd[u];
+        tD2[e / VTL][e % VTL] = qD[u];
+        tdO2[e / VTL][e % VTL] = qo[u];
+        tv2[e / VTL][e % VTL] = qv[u];
       }
+      if (j0 + VTL < V) fetch2(j0 + VTL);
       __syncthreads();
       if (tid < K) {
         const int c = tid;
