@@ -1099,29 +1099,49 @@ __global__ __launch_bounds__(kThreads) void k_bwd_qk(BwdArgs b) {
   if (tk >= (int64_t)a.B * a.T * HK) return;
   const int64_t tok = tk / HK;
   const int hk = (int)(tk % HK);
-  for (int which = 0; which < 2; ++which) {
-    const Tin* x = (const Tin*)(which ? a.k : a.q) + tk * K;
-    const float* dxh = which ? b.dkh : b.dqh;
-    Tin* out = (Tin*)(which ? b.dk : b.dq) + tk * K;
-    float ss = 0.f, dot = 0.f;
-    float dn[kMaxD / 64];
-    for (int m = 0; m < K / 64; ++m) {
-      const int c = lane + 64 * m;
-      float s = 0.f;
-      for (int gi = 0; gi < G; ++gi) s += dxh[(tok * H + (int64_t)hk * G + gi) * K + c];
-      dn[m] = s;
-      const float xv = load_f32(x + c);
-      ss = fmaf(xv, xv, ss);
-      dot = fmaf(xv, s, dot);
+  // q and k together: every load is issued before the first reduction
+  constexpr int M = kMaxD / 64;
+  const Tin* xq = (const Tin*)a.q + tk * K;
+  const Tin* xk = (const Tin*)a.k + tk * K;
+  float dq[M], dk[M], vq[M], vk[M];
+  float ssq = 0.f, dotq = 0.f, ssk = 0.f, dotk = 0.f;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int c = lane + 64 * m;
+    if (c >= K) break;
+    float sq = 0.f, sk = 0.f;
+    for (int gi = 0; gi < G; ++gi) {
+      const int64_t row = (tok * H + (int64_t)hk * G + gi) * K + c;
+      sq += b.dqh[row];
+      sk += b.dkh[row];
     }
-    ss = wave_sum(ss);
-    dot = wave_sum(dot);
-    const float rn = 1.f / sqrtf(ss + 1e-6f);
-    const float r3 = rn * rn * rn;
-    for (int m = 0; m < K / 64; ++m) {
-      const int c = lane + 64 * m;
-      store_as(out + c, dn[m] * rn - load_f32(x + c) * dot * r3);
-    }
+    dq[m] = sq;
+    dk[m] = sk;
+    vq[m] = load_f32(xq + c);
+    vk[m] = load_f32(xk + c);
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    if (lane + 64 * m >= K) break;
+    ssq = fmaf(vq[m], vq[m], ssq);
+    dotq = fmaf(vq[m], dq[m], dotq);
+    ssk = fmaf(vk[m], vk[m], ssk);
+    dotk = fmaf(vk[m], dk[m], dotk);
+  }
+  ssq = wave_sum(ssq);
+  dotq = wave_sum(dotq);
+  ssk = wave_sum(ssk);
+  dotk = wave_sum(dotk);
+  const float rq = 1.f / sqrtf(ssq + 1e-6f), rk = 1.f / sqrtf(ssk + 1e-6f);
+  const float r3q = rq * rq * rq, r3k = rk * rk * rk;
+  Tin* oq = (Tin*)b.dq + tk * K;
+  Tin* ok = (Tin*)b.dk + tk * K;
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int c = lane + 64 * m;
+    if (c >= K) break;
+    store_as(oq + c, dq[m] * rq - vq[m] * dotq * r3q);
+    store_as(ok + c, dk[m] * rk - vk[m] * dotk * r3k);
   }
 }
 

@@ -69,23 +69,38 @@ __global__ __launch_bounds__(kThreads) void k_prologue_valu(
   const int64_t base = th * K;  // value-head token-head (outputs, gate)
   // q and k of the key head this value head reads
   const int64_t kbase = ((th / H) * HK + h / (H / HK)) * K;
+  // every load of the token-head is issued up front; q and k stay in registers
+  constexpr int M = kMaxD / 64;
+  float vq[M], vk[M], vx[M];
   float ssq = 0.f, ssk = 0.f;
-  for (int c = lane; c < K; c += 64) {
-    float xq = load_f32(q + kbase + c), xk = load_f32(k + kbase + c);
-    ssq = fmaf(xq, xq, ssq);
-    ssk = fmaf(xk, xk, ssk);
+  const float bl = load_f32(beta + th);
+  const float A = expf(a_log[h]);
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int c = lane + 64 * m;
+    if (c >= K) break;
+    vq[m] = load_f32(q + kbase + c);
+    vk[m] = load_f32(k + kbase + c);
+    vx[m] = load_f32(gate + base + c) + dt_bias[(int64_t)h * K + c];
+  }
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    if (lane + 64 * m >= K) break;
+    ssq = fmaf(vq[m], vq[m], ssq);
+    ssk = fmaf(vk[m], vk[m], ssk);
   }
   ssq = wave_sum(ssq);
   ssk = wave_sum(ssk);
   const float rq = 1.f / sqrtf(ssq + 1e-6f), rk = 1.f / sqrtf(ssk + 1e-6f);
-  const float A = expf(a_log[h]);
-  for (int c = lane; c < K; c += 64) {
-    qn[base + c] = load_f32(q + kbase + c) * rq;
-    kn[base + c] = load_f32(k + kbase + c) * rk;
-    float x = load_f32(gate + base + c) + dt_bias[(int64_t)h * K + c];
-    g[base + c] = gate_value(x, A, gate_form, lb);
+#pragma unroll
+  for (int m = 0; m < M; ++m) {
+    const int c = lane + 64 * m;
+    if (c >= K) break;
+    qn[base + c] = vq[m] * rq;
+    kn[base + c] = vk[m] * rk;
+    g[base + c] = gate_value(vx[m], A, gate_form, lb);
   }
-  if (lane == 0) bt[th] = sigmoid_f(load_f32(beta + th));
+  if (lane == 0) bt[th] = sigmoid_f(bl);
 }
 
 // One workgroup per chunk-head (flattened j*H + h).  The decay factors use the
