@@ -79,6 +79,16 @@ def test_bwd_fp32_rows(C):
     _run(inp, d_o, d_fin, torch.float32, "fp32 rows C=%d" % C, chunk_size=C, scale=0.3)
 
 
+def test_bwd_fp32_k128_v64_rows():
+    """K=128 with V=64: the chunk-64 matrix-core paths with two state tiles per
+    wave and a single 64-column state tile."""
+    _banner("bwd fp32 rows K=128 V=64")
+    inp = to_device(synthetic.random_problem(41, 2, 200, 2, 128, 64, dtype=torch.float32,
+                                             init_std=0.5))
+    d_o, d_fin = _upstream(inp, 11)
+    _run(inp, d_o, d_fin, torch.float32, "fp32 rows K=128 V=64")
+
+
 def test_bwd_fp32_packed_grouped_sigmoid_gate():
     _banner("bwd fp32 packed GVA sigmoid gate")
     inp = to_device(synthetic.random_problem(32, 1, 265, 1, 64, 64, dtype=torch.float32,
