@@ -28,6 +28,7 @@
 namespace kda {
 namespace {
 
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kThreads = 256;
 // The chunk-factor kernel's workgroup: its LDS (about 50 KB for C = 64) leaves
 // room for three workgroups per CU, so 512 threads give each SIMD six waves.
@@ -152,6 +153,78 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
 
   const int64_t chb = (int64_t)j * H + h;  // chunk-head index
   float* Aqk = (float*)a.Aqk + chb * C * C;
+  if constexpr (C == 64) {
+    // Off-diagonal 16 x 16 blocks (R > I) on fp32 matrix cores: with the
+    // per-channel reference gamma_ref = gamma_{16R-1} (the last row before block
+    // R), e^{gamma_r - gamma_i} = e^{gamma_r - gamma_ref} e^{gamma_ref - gamma_i},
+    // both factors <= 1 for r >= 16R > i, so the decayed products become
+    //   Akk_RI = (K^_R . e^{gamma_R - gamma_ref}) (K^_I . e^{gamma_ref - gamma_I})^T
+    // (and Aqk with Q^_R), one wave per block, lane l holding A[l%16][l/16],
+    // B[l/16][l%16] and D[4(l/16)+e][l%16] (v_mfma_f32_16x16x4f32).  The four
+    // diagonal blocks keep the per-pair sums; rows past the chunk end are zero.
+    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    if (w < 6) {
+      const int R = w < 1 ? 1 : w < 3 ? 2 : 3, I = w - R * (R - 1) / 2;
+      const int r = 16 * R + ln, i = 16 * I + ln;   // this lane's A row and B column
+      const bool rin = r < L, iin = i < L;
+      const float* kr = a.kn + tok_off(rin ? r : 0) * K;
+      const float* qr = a.qn + tok_off(rin ? r : 0) * K;
+      const float* ki = a.kn + tok_off(iin ? i : 0) * K;
+      f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
+      for (int c0 = 0; c0 < K; c0 += 4) {
+        const int c = c0 + lg;
+        const float gref = sG[16 * R - 1][c];
+        const float er = __expf(sG[r][c] - gref), ei = __expf(gref - sG[i][c]);
+        const float xk = rin ? kr[c] * er : 0.f, xq = rin ? qr[c] * er : 0.f;
+        const float yk = iin ? ki[c] * ei : 0.f;
+        ak = __builtin_amdgcn_mfma_f32_16x16x4f32(xk, yk, ak, 0, 0, 0);
+        aq = __builtin_amdgcn_mfma_f32_16x16x4f32(xq, yk, aq, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ro = 16 * R + 4 * lg + e, io = 16 * I + ln, pp = ro * C + io;
+        const bool in = ro < L;
+        sA[ro][io] = in ? ak[e] : 0.f;
+        Aqk[pp] = in ? a.scale * aq[e] : 0.f;
+        if (a.Akk_out) a.Akk_out[chb * C * C + pp] = in ? ak[e] : 0.f;
+      }
+    }
+    // diagonal blocks: 4 x 136 pairs (i <= r inside a block), spread over all threads
+    for (int gp = tid; gp < 4 * 136; gp += kThreads) {
+      const int bk = gp / 136, q = gp % 136;
+      int rl = (int)((sqrtf(8.f * q + 1.f) - 1.f) * 0.5f);
+      while (rl * (rl + 1) / 2 > q) --rl;
+      while ((rl + 1) * (rl + 2) / 2 <= q) ++rl;
+      const int il = q - rl * (rl + 1) / 2;
+      const int r = 16 * bk + rl, i = 16 * bk + il, pp = r * C + i;
+      float akk = 0.f, aqk = 0.f;
+      if (r < L) {
+        const float* kr = a.kn + tok_off(r) * K;
+        const float* qr = a.qn + tok_off(r) * K;
+        const float* ki = a.kn + tok_off(i) * K;
+        for (int c = 0; c < K; ++c) {
+          const float d = __expf(sG[r][c] - sG[i][c]);
+          const float kd = ki[c] * d;
+          akk = fmaf(kr[c], kd, akk);
+          aqk = fmaf(qr[c], kd, aqk);
+        }
+      }
+      sA[r][i] = (i < r) ? akk : 0.f;
+      Aqk[pp] = (r < L) ? a.scale * aqk : 0.f;
+      if (a.Akk_out) a.Akk_out[chb * C * C + pp] = (i < r) ? akk : 0.f;
+    }
+    // above the diagonal: zero
+    for (int pp = tid; pp < C * C; pp += kThreads) {
+      const int r = pp / C, i = pp % C;
+      if (i > r) {
+        sA[r][i] = 0.f;
+        Aqk[pp] = 0.f;
+        if (a.Akk_out) a.Akk_out[chb * C * C + pp] = 0.f;
+      }
+    }
+    __syncthreads();
+  } else {
+  float* Aqk = (float*)a.Aqk + chb * C * C;
   for (int p = tid; p < C * C; p += kThreads) {
     const int r = p / C, i = p % C;
     float akk = 0.f, aqk = 0.f;
@@ -172,6 +245,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
   }
   __syncthreads();
 
+  }
   // Tm = (I + Diag(beta) Akk)^-1 in 16 x 16 blocks.  Diagonal blocks: lane s of
   // wave b solves column s of block b by forward substitution (independent
   // lanes, no barriers).  Off-diagonal blocks, block row by block row:
