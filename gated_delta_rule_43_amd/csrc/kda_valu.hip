@@ -326,7 +326,25 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
   // A thread's elements share one column (c = tid % D, rows tid / D + (256/D) m):
   // that column of X and of Diag(beta) V is read into registers once.
   float* W = (float*)a.W + chb * C * K;
-  {
+  // Tm (lower triangular, in sA) times the C x D matrix in sG, written to out
+  // [C][D]: for 64-token chunks on fp32 matrix cores, one 16 x 16 output tile
+  // per accumulator, k-steps up to the tile's diagonal block.
+  auto tm_product = [&](float* out, int D) {
+    const int w = tid >> 6, lane = tid & 63, ln = lane & 15, lg = lane >> 4;
+    const int nct = D / 16;
+    for (int t = w; t < (C / 16) * nct; t += kThreads / 64) {
+      const int rt = t / nct, ct = t % nct;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int i0 = 0; i0 < 16 * (rt + 1); i0 += 4)
+        acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[16 * rt + ln][i0 + lg], sG[i0 + lg][16 * ct + ln],
+                                                   acc, 0, 0, 0);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[(int64_t)(16 * rt + 4 * lg + e) * D + 16 * ct + ln] = acc[e];
+    }
+  };
+  if constexpr (C == 64) {
+    tm_product(W, K);
+  } else {
     const int c = tid % K, r0 = tid / K, rs = kThreads / K;
     float xc[C];
 #pragma unroll
@@ -357,7 +375,9 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
     }
   }
   __syncthreads();
-  {
+  if constexpr (C == 64) {
+    tm_product(U, V);
+  } else {
     const int c = tid % V, r0 = tid / V, rs = kThreads / V;
     for (int r = r0; r < C; r += rs) {
       float acc = 0.f;
