@@ -904,17 +904,34 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   }
 
   // ---- phase C: Y += dW K~^T (i <= r) ----
+  if constexpr (C == 64) {
+    // the ten lower 16 x 16 tiles on fp32 matrix cores, each wave owning whole tiles
+    const int lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
+    for (int t = w; t < 10; t += NT / 64) {
+      const int R = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0, I = t - R * (R + 1) / 2;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+      for (int c = 0; c < K; c += 4)
+        acc = mfma_f32(sDW[16 * R + ln][c + lg], sKtT[c + lg][16 * I + ln], acc);
 #pragma unroll
-  for (int m = 0; m < NE2; ++m) {
-    const int r = rb2 + RSTEP2 * m;
-    if (r < L && i2 <= r) {
-      float acc = 0.f;
-      for (int c = 0; c < K; c += 4) {
-        const float4 dwv = *(const float4*)&sDW[r][c];
-        acc += dwv.x * sKtT[c][i2] + dwv.y * sKtT[c + 1][i2] + dwv.z * sKtT[c + 2][i2] +
-               dwv.w * sKtT[c + 3][i2];
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * R + 4 * lg + e, i = 16 * I + ln;
+        if (r < L && i <= r) sY[r][i] += acc[e];
       }
-      sY[r][i2] += acc;
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < NE2; ++m) {
+      const int r = rb2 + RSTEP2 * m;
+      if (r < L && i2 <= r) {
+        float acc = 0.f;
+        for (int c = 0; c < K; c += 4) {
+          const float4 dwv = *(const float4*)&sDW[r][c];
+          acc += dwv.x * sKtT[c][i2] + dwv.y * sKtT[c + 1][i2] + dwv.z * sKtT[c + 2][i2] +
+                 dwv.w * sKtT[c + 3][i2];
+        }
+        sY[r][i2] += acc;
+      }
     }
   }
   __syncthreads();
@@ -936,13 +953,35 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     zv[m] = sB[i2] * acc;
   }
   float ekt[NE1];  // e^gamma beta (Tm^T dW): the K~ term of dk^ (and, times k^, of dgamma)
+  if constexpr (C == 64) {
+    // Tm^T dW on fp32 matrix cores (Tm[aa][r] is zero for aa < r, so a row tile's
+    // k-steps start at its own block), scaled and passed to the element owners
+    // through the K~ region, which phase C has finished reading
+    float (*sE)[K] = (float(*)[K])sR4;
+    const int lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
+    for (int t = w; t < (C / 16) * (K / 16); t += NT / 64) {
+      const int rt = t / (K / 16), ct = t % (K / 16);
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int aa = 16 * rt; aa < C; aa += 4)
+        acc = mfma_f32(sT[aa + lg][16 * rt + ln], sDW[aa + lg][16 * ct + ln], acc);
 #pragma unroll
-  for (int m = 0; m < NE1; ++m) {
-    const int r = rb1 + RSTEP1 * m;
-    float dxk = 0.f;
-    if (r < L)
-      for (int aa = r; aa < L; ++aa) dxk = fmaf(sT[aa][r], sDW[aa][c1], dxk);
-    ekt[m] = r < L ? __expf(sGam[r][c1]) * sB[r] * dxk : 0.f;
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * lg + e, c = 16 * ct + ln;
+        sE[r][c] = r < L ? __expf(sGam[r][c]) * sB[r] * acc[e] : 0.f;
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NE1; ++m) ekt[m] = sE[rb1 + RSTEP1 * m][c1];
+  } else {
+#pragma unroll
+    for (int m = 0; m < NE1; ++m) {
+      const int r = rb1 + RSTEP1 * m;
+      float dxk = 0.f;
+      if (r < L)
+        for (int aa = r; aa < L; ++aa) dxk = fmaf(sT[aa][r], sDW[aa][c1], dxk);
+      ekt[m] = r < L ? __expf(sGam[r][c1]) * sB[r] * dxk : 0.f;
+    }
   }
   __syncthreads();  // K~ and dW are dead: Z and q^ take their places
 #pragma unroll
