@@ -189,10 +189,19 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_mfma(BwdArgs b) {
   __shared__ __attribute__((aligned(16))) float sD[C][SP];
   __shared__ __attribute__((aligned(16))) float sW[C][KP];
   __shared__ __attribute__((aligned(16))) float sKb[C][KP];
-  auto stage_pad = [&](float* dst, const float* src) {
-    for (int e = tid; e < C * K / 4; e += NT) {
-      const int r = e / (K / 4), c4 = e % (K / 4);
-      *(float4*)(dst + r * KP + 4 * c4) = ((const float4*)src)[e];
+  // W and Kbar of each chunk reach registers one chunk ahead (their loads are
+  // in flight while the previous chunk's products run)
+  constexpr int NF4 = C * K / 4 / NT;
+  static_assert(NF4 * NT * 4 == C * K && NF4 <= 2, "one or two float4 pieces per thread");
+  float4 pw0, pw1, pk0, pk1;  // named, so that they stay in registers
+  auto fetch_wk = [&](int64_t chb) __attribute__((always_inline)) {
+    const float4* W4 = (const float4*)((const float*)a.W + chb * C * K);
+    const float4* K4 = (const float4*)((const float*)a.Kb + chb * C * K);
+    pw0 = W4[tid];
+    pk0 = K4[tid];
+    if constexpr (NF4 == 2) {
+      pw1 = W4[tid + NT];
+      pk1 = K4[tid + NT];
     }
   };
   const int64_t sbase = ((int64_t)n * H + h) * K * V;
@@ -208,6 +217,7 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_mfma(BwdArgs b) {
   }
   const int drt = w >> 2, dct = w & 3;  // this wave's Delta tile
   const int jc0 = a.seq_chunk0[n], jc1 = a.seq_chunk0[n + 1];
+  if (jc0 < jc1) fetch_wk((int64_t)jc0 * H + h);
   for (int j = jc0; j < jc1; ++j) {
     const int64_t chb = (int64_t)j * H + h;
     const float* U = (const float*)a.U + chb * C * V;
@@ -225,8 +235,17 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_mfma(BwdArgs b) {
         sS[c][cc] = st[t][e];
       }
     }
-    stage_pad(&sW[0][0], (const float*)a.W + chb * C * K);
-    stage_pad(&sKb[0][0], (const float*)a.Kb + chb * C * K);
+    {
+      const int r0 = tid / (K / 4), c0 = 4 * (tid % (K / 4));
+      *(float4*)&sW[r0][c0] = pw0;
+      *(float4*)&sKb[r0][c0] = pk0;
+      if constexpr (NF4 == 2) {
+        const int r1 = (tid + NT) / (K / 4), c1 = 4 * ((tid + NT) % (K / 4));
+        *(float4*)&sW[r1][c1] = pw1;
+        *(float4*)&sKb[r1][c1] = pk1;
+      }
+    }
+    if (j + 1 < jc1) fetch_wk(chb + H);  // the next chunk of this sequence
     f32x4 acc;
 #pragma unroll
     for (int e = 0; e < 4; ++e) acc[e] = U[(int64_t)(16 * drt + 4 * lg + e) * V + col0 + 16 * dct + ln];
