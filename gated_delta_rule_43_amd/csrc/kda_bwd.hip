@@ -416,12 +416,31 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
   float (*sQt)[KP] = (float(*)[KP])sR;
   float (*sW)[KP] = (float(*)[KP])(sR + C * KP);
   static_assert(C * AP + C * KP <= 2 * C * KP, "Aqk and Kbar fit the operand region");
-  // copy a [C][D] fp32 matrix into LDS rows of stride P (D, P multiples of 4)
-  auto stage_pad = [&](float* dst, const float* src, int D, int P) {
-    for (int e = tid; e < C * D / 4; e += NT) {
-      const int r = e / (D / 4), c4 = e % (D / 4);
-      *(float4*)(dst + r * P + 4 * c4) = ((const float4*)src)[e];
+  // Aqk, Kbar, Qt and W of each chunk reach registers one chunk ahead (named,
+  // so that they stay in registers): their loads are in flight while the
+  // previous chunk's products run
+  static_assert(C * C / 4 == NT && C * K / 4 <= 2 * NT, "one Aqk piece, one or two of the others");
+  constexpr bool TWO = C * K / 4 == 2 * NT;
+  float4 pa, pk0, pk1, pq0, pq1, pw0, pw1;
+  auto fetch = [&](int64_t chb) __attribute__((always_inline)) {
+    const float4* A4 = (const float4*)((const float*)a.Aqk + chb * C * C);
+    const float4* K4 = (const float4*)((const float*)a.Kb + chb * C * K);
+    const float4* Q4 = (const float4*)((const float*)a.Qt + chb * C * K);
+    const float4* W4 = (const float4*)((const float*)a.W + chb * C * K);
+    pa = A4[tid];
+    pk0 = K4[tid];
+    pq0 = Q4[tid];
+    pw0 = W4[tid];
+    if constexpr (TWO) {
+      pk1 = K4[tid + NT];
+      pq1 = Q4[tid + NT];
+      pw1 = W4[tid + NT];
     }
+  };
+  // a [C][K] matrix held as pieces tid (and tid + NT) into LDS rows of stride KP
+  auto put_k = [&](float (*dst)[KP], const float4& v0, const float4& v1) __attribute__((always_inline)) {
+    *(float4*)&dst[tid / (K / 4)][4 * (tid % (K / 4))] = v0;
+    if constexpr (TWO) *(float4*)&dst[(tid + NT) / (K / 4)][4 * ((tid + NT) % (K / 4))] = v1;
   };
   const int64_t sbase = ((int64_t)n * H + h) * K * V;
   f32x4 st[TPW];
@@ -437,6 +456,7 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
   const int drt = w >> 2, dct = w & 3;  // this wave's dDelta tile
   const Tin* dO = (const Tin*)b.d_o;
   const int jc0 = a.seq_chunk0[n], jc1 = a.seq_chunk0[n + 1];
+  if (jc0 < jc1) fetch((int64_t)(jc1 - 1) * H + h);
   for (int j = jc1 - 1; j >= jc0; --j) {
     const int64_t chb = (int64_t)j * H + h;
     const float* gL = a.gL + chb * K;
@@ -458,8 +478,8 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
       const int r = e / VT, cc = e % VT;
       sO[r][cc] = r < L ? load_f32(dO + ((int64_t)(tok0 + r) * H + h) * V + col0 + cc) : 0.f;
     }
-    stage_pad(&sA[0][0], (const float*)a.Aqk + chb * C * C, C, AP);
-    stage_pad(&sKb[0][0], (const float*)a.Kb + chb * C * K, K, KP);
+    *(float4*)&sA[tid / (C / 4)][4 * (tid % (C / 4))] = pa;
+    put_k(sKb, pk0, pk1);
     __syncthreads();
     // dDelta = Aqk_s^T dO + Kbar dS_L (Aqk_s is zero above the diagonal, so
     // rows rr below the tile's first row contribute nothing)
@@ -478,8 +498,9 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
       }
     }
     __syncthreads();  // dDelta complete; Aqk and Kbar are no longer read
-    stage_pad(&sQt[0][0], (const float*)a.Qt + chb * C * K, K, KP);
-    stage_pad(&sW[0][0], (const float*)a.W + chb * C * K, K, KP);
+    put_k(sQt, pq0, pq1);
+    put_k(sW, pw0, pw1);
+    if (j - 1 >= jc0) fetch(chb - H);  // the previous chunk of this sequence
     float gl[TPW][4];
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
