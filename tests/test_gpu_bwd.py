@@ -199,3 +199,20 @@ def test_bwd_profiled_same_bits_and_stage_times():
         assert torch.equal(a[n], b[n]), n
     assert ms.shape == (kda.BWD_NUM_STAGES,) and np.all(ms >= 0), ms
     assert ms[kda.BWD_STAGE_NAMES.index("chunk_gradients")] > 0, ms
+
+
+def test_bwd_fp32_extreme_gates():
+    """Single steps that decay by ~50 nats on ~10% of (token, channel) entries:
+    the recomputation's block-split decay factors and the state passes stay
+    finite and match the oracle's gradients."""
+    _banner("bwd fp32 extreme gates")
+    inp = to_device(synthetic.random_problem(42, 1, 260, 2, 128, 128, dtype=torch.float32,
+                                             init_std=0.5, lengths=[150, 110]))
+    gen = torch.Generator(device="cpu").manual_seed(8)
+    spikes = torch.rand(inp["gate"].shape, generator=gen) < 0.1
+    gate = inp["gate"].cpu()
+    gate[spikes] = 30.0
+    inp["gate"] = gate.to(DEV)
+    inp["a_log"] = torch.full_like(inp["a_log"], 0.5)
+    d_o, d_fin = _upstream(inp, 12)
+    _run(inp, d_o, d_fin, torch.float32, "fp32 extreme gates")

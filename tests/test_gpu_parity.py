@@ -297,24 +297,28 @@ def test_apply_without_initial_state_is_state_ext():
 # --------------------------------------------------------------------------
 # extreme decays: 16-row blocks whose decay leaves the factorised range
 # --------------------------------------------------------------------------
-@pytest.mark.parametrize("K,V", [(128, 128), (64, 64)])
-def test_extreme_gates_exact_diagonal(K, V):
+@pytest.mark.parametrize("dt,K,V", [(torch.bfloat16, 128, 128), (torch.bfloat16, 64, 64),
+                                    (torch.float32, 128, 128), (torch.float32, 64, 64)],
+                         ids=["bf16-128", "bf16-64", "f32-128", "f32-64"])
+def test_extreme_gates_exact_diagonal(dt, K, V):
     """Gate logits of +30 on ~10% of (token, channel) entries make single steps
-    decay by ~50 nats: such blocks must take the exact in-block path."""
-    inp = synthetic.random_problem(41, 1, 300, 2, K, V, dtype=torch.bfloat16, device=DEV,
+    decay by ~50 nats: in bf16 such blocks must take the exact in-block path;
+    in fp32 the block-split decay factors of the off-diagonal products
+    underflow to zero exactly where the true decay does."""
+    inp = synthetic.random_problem(41, 1, 300, 2, K, V, dtype=dt, device=DEV,
                                    init_std=0.5, lengths=[170, 130])
     gen = torch.Generator(device="cpu").manual_seed(7)
     spikes = torch.rand(inp["gate"].shape, generator=gen) < 0.1
     gate = inp["gate"].float().cpu()
     gate[spikes] = 30.0
-    inp["gate"] = gate.to(torch.bfloat16).to(DEV)
+    inp["gate"] = gate.to(dt).to(DEV)
     inp["a_log"] = torch.full_like(inp["a_log"], 0.5)
     inp.update(scale=None, lower_bound=None, chunk_size=64)
     o, fin = gpu_fwd(inp)
     assert torch.isfinite(o.float()).all() and torch.isfinite(fin).all()
     o_ref, f_ref = oracle_fwd(inp)
-    assert_close(to_np(o), o_ref, torch.bfloat16, "o")
-    assert_close(to_np(fin), f_ref, torch.bfloat16, "final_state")
+    assert_close(to_np(o), o_ref, dt, "o")
+    assert_close(to_np(fin), f_ref, dt, "final_state")
 
 
 # ---------------------------------------------------------------------------
