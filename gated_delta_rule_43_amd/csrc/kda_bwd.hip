@@ -1067,18 +1067,22 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   float dgm[NE1], tkm[NE1];
 #pragma unroll
   for (int m = 0; m < NE1; ++m) {
-    const int r = rb1 + RSTEP1 * m, c = c1;
+    // rb1 = tid / K is the same for every lane of a wave, so the row and the
+    // loop bounds below are wave-uniform (scalar loop control)
+    const int r = __builtin_amdgcn_readfirstlane(rb1 + RSTEP1 * m), c = c1;
     dgm[m] = tkm[m] = 0.f;
     if (r >= L) continue;
     const float q = sQn[r][c], kk = sKn[r][c];
     const float gm = sGam[r][c], egm = __expf(gm), ekb = __expf(sGam[L - 1][c] - gm);
     float r1 = 0.f, r2 = 0.f;
+#pragma unroll 4
     for (int i = 0; i <= r; ++i) {
       const float ke = sKn[i][c] * __expf(gm - sGam[i][c]);
       r1 = fmaf(sP[r][i], ke, r1);
       r2 = fmaf(sY[r][i], ke, r2);
     }
     float c12 = 0.f;
+#pragma unroll 4
     for (int rr = r; rr < L; ++rr) {
       const float e = __expf(sGam[rr][c] - gm);
       c12 = fmaf(sP[rr][r] * sQn[rr][c] + sY[rr][r] * sKn[rr][c], e, c12);
