@@ -6,11 +6,16 @@
 // tests forward and backward together, whose state gradient the hyper_parallel
 // coverage page routes between slices (the backward of _RecvKDAInitialState).
 //
-// Plain VALU fp32 arithmetic for both input dtypes; the decay factors use the
-// hardware exponential (__expf: one v_exp_f32 after a scaling, about one ulp
-// on the result), the gate's derivative the full-accuracy functions.  The
-// forward's chunk factors are recomputed first (the VALU prologue and chunk
-// kernels, which here also keep Akk and Tm); then, per chunk of L rows entering with state
+// fp32 arithmetic for both input dtypes.  For 64-token chunks the dense
+// per-chunk products (the two state passes, and the value-dimension, Y and
+// Tm^T dW products of the chunk kernel) run on fp32 matrix cores
+// (v_mfma_f32_16x16x4f32: fp32 operands, fp32 accumulation); the pairwise,
+// triangular and per-element work, and chunks of 16 or 32, stay on VALU.  The
+// decay factors use the hardware exponential (__expf: one v_exp_f32 after a
+// scaling, about one ulp on the result), the gate's derivative the
+// full-accuracy functions.  The forward's chunk factors are recomputed first
+// (the fp32 prologue and chunk kernels, which here also keep Akk and Tm); then,
+// per chunk of L rows entering with state
 // S0 and with Q~ = q^ e^gamma, K~ = k^ e^gamma, Kbar = k^ e^(gamma_L - gamma),
 // Aqk_s = scale Aqk, Qt_s = scale Q~ (the forward's stored operands):
 //

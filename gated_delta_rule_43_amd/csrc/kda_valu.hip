@@ -1,7 +1,9 @@
-// Plain-VALU fp32 path of the KDA chunked forward.
+// fp32 path of the KDA chunked forward.
 //
-// It serves fp32 inputs and every chunk size, and is the path the faster MFMA
-// kernels are measured against.  Three kernels, all fp32 arithmetic:
+// It serves fp32 inputs and every chunk size, and recomputes the chunk factors
+// for the backward.  Three kernels, all fp32 arithmetic (for 64-token chunks
+// the chunk kernel's off-diagonal Akk/Aqk blocks and its W, U products run on
+// fp32 matrix cores, v_mfma_f32_16x16x4f32; everything else on VALU):
 //
 //   1. k_prologue_valu   one wave per token-head: q^, k^ (L2 norm), the
 //                        per-key-channel log-decay g from the raw gate logits,
