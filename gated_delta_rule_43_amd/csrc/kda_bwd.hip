@@ -11,9 +11,8 @@
 // Tm^T dW products of the chunk kernel) run on fp32 matrix cores
 // (v_mfma_f32_16x16x4f32: fp32 operands, fp32 accumulation); the pairwise,
 // triangular and per-element work, and chunks of 16 or 32, stay on VALU.  The
-// decay factors use the hardware exponential (__expf: one v_exp_f32 after a
-// scaling, about one ulp on the result), the gate's derivative the
-// full-accuracy functions.  The forward's chunk factors are recomputed first
+// decay factors and the gate's derivative use the hardware exponential,
+// logarithm and reciprocal (about one ulp on the result).  The forward's chunk factors are recomputed first
 // (the fp32 prologue and chunk kernels, which here also keep Akk and Tm); then,
 // per chunk of L rows entering with state
 // S0 and with Q~ = q^ e^gamma, K~ = k^ e^gamma, Kbar = k^ e^(gamma_L - gamma),
@@ -47,22 +46,33 @@ constexpr int chunk_threads(int C, int K) { return C == 64 ? (K == 128 ? 1024 : 
 constexpr int kMaxD = 128;
 constexpr float kGateFloor = -110.f;
 
-__device__ inline float softplus_f(float x) { return fmaxf(x, 0.f) + log1pf(expf(-fabsf(x))); }
-__device__ inline float sigmoid_f(float x) { return 1.f / (1.f + expf(-x)); }
+// Hardware exponential and logarithm (v_exp_f32 / v_log_f32 after a scaling,
+// about one ulp) and reciprocal: the gate's derivatives enter sums whose fp32
+// tolerance is far above their error.  softplus(x) = max(x, 0) + log(1 + e),
+// sigmoid(x) = 1 / (1 + e) for x >= 0 and e / (1 + e) otherwise, e = e^{-|x|}
+// (log(1 + e) loses e below half an ulp of 1, an absolute error under 6e-8).
+__device__ inline void softplus_sigmoid(float x, float* sp, float* sg) {
+  const float e = __expf(-fabsf(x));
+  const float r = __builtin_amdgcn_rcpf(1.f + e);
+  *sp = fmaxf(x, 0.f) + __logf(1.f + e);
+  *sg = x >= 0.f ? r : e * r;
+}
 
-// dg/dx and dg/da_log of the in-kernel gate at x = gate + dt_bias; zero where
-// the forward clamped g at the bound or floored it at -110.
-__device__ inline void gate_grad(float x, float alog, int form, float lb, float* dgdx, float* dgda) {
-  const float A = expf(alog);
+// dg/dx and dg/da_log of the in-kernel gate at x = gate + dt_bias (A = e^a_log);
+// zero where the forward clamped g at the bound or floored it at -110.
+__device__ inline void gate_grad(float x, float A, int form, float lb, float* dgdx, float* dgda) {
   float g, gx, ga;
   if (form == 1) {
-    const float s = sigmoid_f(A * x);
+    float sp, s;
+    softplus_sigmoid(A * x, &sp, &s);
     g = lb * s;
     gx = lb * s * (1.f - s) * A;
     ga = gx * x;
   } else {
-    g = -A * softplus_f(x);
-    gx = -A * sigmoid_f(x);
+    float sp, s;
+    softplus_sigmoid(x, &sp, &s);
+    g = -A * sp;
+    gx = -A * s;
     ga = g;
     if (form == 2 && !(g > lb)) gx = ga = 0.f;
   }
@@ -1136,14 +1146,14 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
       run += sSeg2[s2][cS];
       if (s2 > sS_) run += sSeg[s2][cS];
     }
-    const float alog = a.a_log[h], db = a.dt_bias[(int64_t)h * K + cS];
+    const float Aexp = expf(a.a_log[h]), db = a.dt_bias[(int64_t)h * K + cS];
 #pragma unroll 1
     for (int u = RSEG - 1; u >= 0; --u) {
       const int r = sS_ * RSEG + u;
       if (r >= L) continue;
       run += sDg[r][cS];
       float gx, ga;
-      gate_grad(load_f32(gate + th(r) * K + cS) + db, alog, a.gate_form, a.lb, &gx, &ga);
+      gate_grad(load_f32(gate + th(r) * K + cS) + db, Aexp, a.gate_form, a.lb, &gx, &ga);
       const float dg = run * gx;
       store_as(dgate + th(r) * K + cS, dg);
       ddt += dg;
