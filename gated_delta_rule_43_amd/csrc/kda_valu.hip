@@ -122,24 +122,34 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
   __shared__ float sG[C][kMaxD + 1];  // gamma, later X = beta k^ exp(gamma)
   __shared__ float sA[C][C + 1];   // Akk, then Tm in place
   __shared__ float sB[C];
+  __shared__ float sGL[kMaxD];     // gamma_L, the chunk's last row of gamma
+  __shared__ float sDg[2][C == 64 ? C : 1];  // halves of the diagonal Aqk sums
+  const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
   auto tok_off = [&](int r) { return ((int64_t)(tok0 + r) * H + h); };
+  const int64_t chb = (int64_t)j * H + h;  // chunk-head index
 
   // gamma: chunk-local inclusive cumsum; rows >= L repeat gamma_{L-1}.  The
-  // chunk's g values reach LDS first, read by all threads four at a time (one
-  // memory latency instead of one per row), then each channel's thread adds
-  // down its column in LDS.
-  for (int p0 = 0; p0 < C * K; p0 += 4 * kThreads) {
-    float gv[4];
+  // chunk's g values reach LDS first, every thread issuing all of its 16-byte
+  // loads before the first store (one memory latency), then each channel's
+  // thread adds down its column in LDS.  Loads here and below read a clamped,
+  // valid address and select zero afterwards, so none sits in a branch of its
+  // own waiting for its data.
+  for (int p0 = 0; p0 < C * K; p0 += 16 * kThreads) {
+    f32x4 gv[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int p = p0 + tid + u * kThreads, r = p / K, c = p % K;
-      gv[u] = (p < C * K && r < L) ? a.g[tok_off(r) * K + c] : 0.f;
+      const int p = p0 + 4 * (tid + u * kThreads), r = p / K, c = p % K;
+      const bool in = p < C * K && r < L;
+      const f32x4 x = *(const f32x4*)(a.g + (in ? tok_off(r) * K + c : tok_off(0) * K));
+      gv[u] = in ? x : zero4;
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int p = p0 + tid + u * kThreads;
-      if (p < C * K) sG[p / K][p % K] = gv[u];
+      const int p = p0 + 4 * (tid + u * kThreads);
+      if (p < C * K)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sG[p / K][p % K + e] = gv[u][e];
     }
   }
   for (int r = tid; r < C; r += kThreads) sB[r] = r < L ? a.bt[tok_off(r)] : 0.f;
@@ -150,10 +160,11 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
       acc += sG[r][c];
       sG[r][c] = acc;
     }
+    sGL[c] = acc;
+    a.gL[chb * K + c] = __expf(acc);
   }
   __syncthreads();
 
-  const int64_t chb = (int64_t)j * H + h;  // chunk-head index
   float* Aqk = (float*)a.Aqk + chb * C * C;
   if constexpr (C == 64) {
     // Off-diagonal 16 x 16 blocks (R > I) on fp32 matrix cores: with the
@@ -169,18 +180,31 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
       const int R = w < 1 ? 1 : w < 3 ? 2 : 3, I = w - R * (R - 1) / 2;
       const int r = 16 * R + ln, i = 16 * I + ln;   // this lane's A row and B column
       const bool rin = r < L, iin = i < L;
-      const float* kr = a.kn + tok_off(rin ? r : 0) * K;
-      const float* qr = a.qn + tok_off(rin ? r : 0) * K;
-      const float* ki = a.kn + tok_off(iin ? i : 0) * K;
-      f32x4 ak = {0.f, 0.f, 0.f, 0.f}, aq = {0.f, 0.f, 0.f, 0.f};
-      for (int c0 = 0; c0 < K; c0 += 4) {
-        const int c = c0 + lg;
-        const float gref = sG[16 * R - 1][c];
-        const float er = __expf(sG[r][c] - gref), ei = __expf(gref - sG[i][c]);
-        const float xk = rin ? kr[c] * er : 0.f, xq = rin ? qr[c] * er : 0.f;
-        const float yk = iin ? ki[c] * ei : 0.f;
-        ak = __builtin_amdgcn_mfma_f32_16x16x4f32(xk, yk, ak, 0, 0, 0);
-        aq = __builtin_amdgcn_mfma_f32_16x16x4f32(xq, yk, aq, 0, 0, 0);
+      // Lane group lg takes the channels [lg K/4, (lg + 1) K/4): its k-step s
+      // is channel lg K/4 + s, so each lane reads 16-byte pieces of its rows,
+      // the next piece in flight while the current one is multiplied.
+      const int KQ = K / 4, c0 = KQ * lg;
+      const float* kr = a.kn + tok_off(rin ? r : 0) * K + c0;
+      const float* qr = a.qn + tok_off(rin ? r : 0) * K + c0;
+      const float* ki = a.kn + tok_off(iin ? i : 0) * K + c0;
+      f32x4 ak = zero4, aq = zero4;
+      f32x4 nk = *(const f32x4*)kr, nq = *(const f32x4*)qr, ni = *(const f32x4*)ki;
+      for (int s0 = 0; s0 < KQ; s0 += 4) {
+        const f32x4 k4 = nk, q4 = nq, i4 = ni;
+        const int sn = s0 + 4 < KQ ? s0 + 4 : s0;
+        nk = *(const f32x4*)(kr + sn);
+        nq = *(const f32x4*)(qr + sn);
+        ni = *(const f32x4*)(ki + sn);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int c = c0 + s0 + e;
+          const float gref = sG[16 * R - 1][c];
+          const float er = __expf(sG[r][c] - gref), ei = __expf(gref - sG[i][c]);
+          const float xk = rin ? k4[e] * er : 0.f, xq = rin ? q4[e] * er : 0.f;
+          const float yk = iin ? i4[e] * ei : 0.f;
+          ak = __builtin_amdgcn_mfma_f32_16x16x4f32(xk, yk, ak, 0, 0, 0);
+          aq = __builtin_amdgcn_mfma_f32_16x16x4f32(xq, yk, aq, 0, 0, 0);
+        }
       }
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -190,30 +214,63 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
         Aqk[pp] = in ? a.scale * aq[e] : 0.f;
         if (a.Akk_out) a.Akk_out[chb * C * C + pp] = in ? ak[e] : 0.f;
       }
+    } else {
+      // The 64 diagonal Aqk elements (decay 1): lane r takes row r, wave 6 the
+      // first half of the channels and wave 7 the second; the two partial sums
+      // wait in sDg until the solve below adds them.
+      const int r = lane, c0 = (w - 6) * (K / 2);
+      const float* kr = a.kn + tok_off(r < L ? r : 0) * K + c0;
+      const float* qr = a.qn + tok_off(r < L ? r : 0) * K + c0;
+      float aqk = 0.f;
+      f32x4 nk = *(const f32x4*)kr, nq = *(const f32x4*)qr;
+      for (int c = 0; c < K / 2; c += 4) {
+        const f32x4 k4 = nk, q4 = nq;
+        const int cn = c + 4 < K / 2 ? c + 4 : c;
+        nk = *(const f32x4*)(kr + cn);
+        nq = *(const f32x4*)(qr + cn);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) aqk = fmaf(q4[e], k4[e], aqk);
+      }
+      sDg[w - 6][r] = aqk;
+      if (w == 6) {
+        sA[r][r] = 0.f;
+        if (a.Akk_out) a.Akk_out[chb * C * C + r * C + r] = 0.f;
+      }
     }
-    // diagonal blocks: 4 x 136 pairs (i <= r inside a block), spread over all threads
-    for (int gp = tid; gp < 4 * 136; gp += kThreads) {
-      const int bk = gp / 136, q = gp % 136;
-      int rl = (int)((sqrtf(8.f * q + 1.f) - 1.f) * 0.5f);
-      while (rl * (rl + 1) / 2 > q) --rl;
-      while ((rl + 1) * (rl + 2) / 2 <= q) ++rl;
-      const int il = q - rl * (rl + 1) / 2;
+    // Diagonal blocks: the 4 x 120 strictly lower pairs, one per thread, rows
+    // read in 16-byte pieces, the next piece in flight.
+    static_assert(kThreads >= 4 * 120, "one thread per diagonal-block pair");
+    if (tid < 4 * 120) {
+      const int bk = tid / 120, q = tid % 120;   // q = rl (rl - 1) / 2 + il, il < rl
+      int rl = (int)((sqrtf(8.f * q + 1.f) + 1.f) * 0.5f);
+      while (rl * (rl - 1) / 2 > q) --rl;
+      while ((rl + 1) * rl / 2 <= q) ++rl;
+      const int il = q - rl * (rl - 1) / 2;
       const int r = 16 * bk + rl, i = 16 * bk + il, pp = r * C + i;
       float akk = 0.f, aqk = 0.f;
       if (r < L) {
         const float* kr = a.kn + tok_off(r) * K;
         const float* qr = a.qn + tok_off(r) * K;
         const float* ki = a.kn + tok_off(i) * K;
-        for (int c = 0; c < K; ++c) {
-          const float d = __expf(sG[r][c] - sG[i][c]);
-          const float kd = ki[c] * d;
-          akk = fmaf(kr[c], kd, akk);
-          aqk = fmaf(qr[c], kd, aqk);
+        f32x4 nk = *(const f32x4*)kr, nq = *(const f32x4*)qr, ni = *(const f32x4*)ki;
+        for (int c = 0; c < K; c += 4) {
+          const f32x4 k4 = nk, q4 = nq, i4 = ni;
+          const int cn = c + 4 < K ? c + 4 : c;
+          nk = *(const f32x4*)(kr + cn);
+          nq = *(const f32x4*)(qr + cn);
+          ni = *(const f32x4*)(ki + cn);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float d = __expf(sG[r][c + e] - sG[i][c + e]);
+            const float kd = i4[e] * d;
+            akk = fmaf(k4[e], kd, akk);
+            aqk = fmaf(q4[e], kd, aqk);
+          }
         }
       }
-      sA[r][i] = (i < r) ? akk : 0.f;
+      sA[r][i] = akk;
       Aqk[pp] = (r < L) ? a.scale * aqk : 0.f;
-      if (a.Akk_out) a.Akk_out[chb * C * C + pp] = (i < r) ? akk : 0.f;
+      if (a.Akk_out) a.Akk_out[chb * C * C + pp] = akk;
     }
     // above the diagonal: zero
     for (int pp = tid; pp < C * C; pp += kThreads) {
@@ -256,18 +313,20 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
     constexpr int NB = C / 16;
     __shared__ float sM[NB > 1 ? NB - 1 : 1][16][17];
     const int wv = tid >> 6, ln = tid & 63;
+    if constexpr (C == 64) {
+      if (wv == 4) Aqk[ln * C + ln] = (ln < L) ? a.scale * (sDg[0][ln] + sDg[1][ln]) : 0.f;
+    }
     float col[16];
     if (wv < NB && ln < 16) {
       const int o = 16 * wv;
+      // col[u] is 0 for u < s, so every lane may sum from u = 0 (fixed
+      // register indices, the same sums)
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        float x = t == ln ? 1.f : 0.f;
-        if (t > ln) {
-          float acc = 0.f;
-          for (int u = ln; u < t; ++u) acc = fmaf(sA[o + t][o + u], col[u], acc);
-          x = -sB[o + t] * acc;
-        }
-        col[t] = x;
+        float acc = 0.f;
+#pragma unroll
+        for (int u = 0; u < t; ++u) acc = fmaf(sA[o + t][o + u], col[u], acc);
+        col[t] = t == ln ? 1.f : (t > ln ? -sB[o + t] * acc : 0.f);
       }
     }
     __syncthreads();
@@ -303,25 +362,38 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
   if (a.Tm_out)
     for (int p = tid; p < C * C; p += kThreads) a.Tm_out[chb * C * C + p] = sA[p / C][p % C];
 
-  // Qt = scale q^ exp(gamma), Kb = k^ exp(gamma_L - gamma), gL = exp(gamma_L)
+  // Qt = scale q^ exp(gamma), Kb = k^ exp(gamma_L - gamma) and, in gamma's
+  // place, X = beta k^ exp(gamma).  Each thread owns 16-byte pieces of rows
+  // (no other thread reads gamma there; gamma_L comes from sGL) and issues
+  // every load before its first store.
   float* Qt = (float*)a.Qt + chb * C * K;
   float* Kb = (float*)a.Kb + chb * C * K;
-  for (int p = tid; p < C * K; p += kThreads) {
-    const int r = p / K, c = p % K;
-    float qt = 0.f, kb = 0.f;
-    if (r < L) {
-      qt = a.scale * a.qn[tok_off(r) * K + c] * __expf(sG[r][c]);
-      kb = a.kn[tok_off(r) * K + c] * __expf(sG[C - 1][c] - sG[r][c]);
+  {
+    constexpr int NP = (C * kMaxD / 4 + kThreads - 1) / kThreads;
+    f32x4 q4[NP], k4[NP];
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int p = 4 * (tid + u * kThreads), r = p / K, c = p % K;
+      const int64_t off = (p < C * K && r < L) ? tok_off(r) * K + c : tok_off(0) * K;
+      q4[u] = *(const f32x4*)(a.qn + off);
+      k4[u] = *(const f32x4*)(a.kn + off);
     }
-    Qt[p] = qt;
-    Kb[p] = kb;
-  }
-  for (int c = tid; c < K; c += kThreads) a.gL[chb * K + c] = __expf(sG[C - 1][c]);
-  __syncthreads();
-  // X = beta k^ exp(gamma), in place of gamma
-  for (int p = tid; p < C * K; p += kThreads) {
-    const int r = p / K, c = p % K;
-    sG[r][c] = r < L ? sB[r] * a.kn[tok_off(r) * K + c] * __expf(sG[r][c]) : 0.f;
+#pragma unroll
+    for (int u = 0; u < NP; ++u) {
+      const int p = 4 * (tid + u * kThreads), r = p / K, c = p % K;
+      if (p >= C * K) break;
+      const bool in = r < L;
+      f32x4 qt, kb;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float gm = sG[r][c + e], eg = __expf(gm);
+        qt[e] = in ? a.scale * q4[u][e] * eg : 0.f;
+        kb[e] = in ? k4[u][e] * __expf(sGL[c + e] - gm) : 0.f;
+        sG[r][c + e] = in ? sB[r] * k4[u][e] * eg : 0.f;
+      }
+      *(f32x4*)(Qt + p) = qt;
+      *(f32x4*)(Kb + p) = kb;
+    }
   }
   __syncthreads();
   // W = Tm X, U = Tm Diag(beta) V   (Tm lower triangular with unit diagonal).
@@ -344,6 +416,17 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
       for (int e = 0; e < 4; ++e) out[(int64_t)(16 * rt + 4 * lg + e) * D + 16 * ct + ln] = acc[e];
     }
   };
+  // V's loads are issued before the W product and staged in X's place after it
+  const Tin* v = (const Tin*)a.v;
+  constexpr int NV = (C * kMaxD + kThreads - 1) / kThreads;
+  float vv[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int p = tid + u * kThreads, i = p / V;
+    const bool in = p < C * V && i < L;
+    const float x = load_f32(v + (in ? tok_off(i) * V + p % V : tok_off(0) * V));
+    vv[u] = in ? x : 0.f;
+  }
   if constexpr (C == 64) {
     tm_product(W, K);
   } else {
@@ -359,22 +442,12 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
     }
   }
   float* U = (float*)a.U + chb * C * V;
-  const Tin* v = (const Tin*)a.v;
-  // Diag(beta) V goes to LDS in X's place (read once, coalesced, four loads in
-  // flight per thread), then U's rows read it from there
+  // Diag(beta) V to LDS in X's place, then U's rows read it from there
   __syncthreads();  // X is no longer read
-  for (int p0 = 0; p0 < C * V; p0 += 4 * kThreads) {
-    float vv[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int p = p0 + tid + u * kThreads, i = p / V, c = p % V;
-      vv[u] = (p < C * V && i < L) ? load_f32(v + tok_off(i) * V + c) : 0.f;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int p = p0 + tid + u * kThreads, i = p / V;
-      if (p < C * V) sG[i][p % V] = i < L ? sB[i] * vv[u] : 0.f;
-    }
+  for (int u = 0; u < NV; ++u) {
+    const int p = tid + u * kThreads, i = p / V;
+    if (p < C * V) sG[i][p % V] = i < L ? sB[i] * vv[u] : 0.f;
   }
   __syncthreads();
   if constexpr (C == 64) {
