@@ -58,6 +58,11 @@ __device__ inline float gate_value(float x, float A, int gate, float lb) {
   return fmaxf(gate == 2 ? fmaxf(g, lb) : g, kGateFloor);
 }
 
+// Token-heads per wave in the prologue: a wave issues the loads of all of them
+// before it uses any, so each wave keeps several rows in flight (the kernel is
+// bound by the bytes in flight per CU, not by its arithmetic).
+constexpr int kProTPW = 4;
+
 template <typename Tin>
 __global__ __launch_bounds__(kThreads) void k_prologue_valu(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ gate,
@@ -66,44 +71,55 @@ __global__ __launch_bounds__(kThreads) void k_prologue_valu(
     float* __restrict__ qn, float* __restrict__ kn, float* __restrict__ g,
     float* __restrict__ bt) {
   const int lane = threadIdx.x & 63;
-  const int64_t th = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (th >= n_th) return;
-  const int h = (int)(th % H);
-  const int64_t base = th * K;  // value-head token-head (outputs, gate)
-  // q and k of the key head this value head reads
-  const int64_t kbase = ((th / H) * HK + h / (H / HK)) * K;
-  // every load of the token-head is issued up front; q and k stay in registers
+  const int64_t th0 = ((int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * kProTPW;
+  if (th0 >= n_th) return;
   constexpr int M = kMaxD / 64;
-  float vq[M], vk[M], vx[M];
-  float ssq = 0.f, ssk = 0.f;
-  const float bl = load_f32(beta + th);
-  const float A = expf(a_log[h]);
+  float vq[kProTPW][M], vk[kProTPW][M], vx[kProTPW][M], bl[kProTPW];
+  // every load of the wave's token-heads is issued up front (past the end,
+  // the last token-head is read again and nothing is stored)
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int c = lane + 64 * m;
-    if (c >= K) break;
-    vq[m] = load_f32(q + kbase + c);
-    vk[m] = load_f32(k + kbase + c);
-    vx[m] = load_f32(gate + base + c) + dt_bias[(int64_t)h * K + c];
+  for (int t = 0; t < kProTPW; ++t) {
+    const int64_t th = th0 + t < n_th ? th0 + t : n_th - 1;
+    const int h = (int)(th % H);
+    const int64_t base = th * K;  // value-head token-head (outputs, gate)
+    // q and k of the key head this value head reads
+    const int64_t kbase = ((th / H) * HK + h / (H / HK)) * K;
+    bl[t] = load_f32(beta + th);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int c = lane + 64 * m < K ? lane + 64 * m : 0;
+      vq[t][m] = load_f32(q + kbase + c);
+      vk[t][m] = load_f32(k + kbase + c);
+      vx[t][m] = load_f32(gate + base + c) + dt_bias[(int64_t)h * K + c];
+    }
   }
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    if (lane + 64 * m >= K) break;
-    ssq = fmaf(vq[m], vq[m], ssq);
-    ssk = fmaf(vk[m], vk[m], ssk);
-  }
-  ssq = wave_sum(ssq);
-  ssk = wave_sum(ssk);
-  const float rq = 1.f / sqrtf(ssq + 1e-6f), rk = 1.f / sqrtf(ssk + 1e-6f);
+  for (int t = 0; t < kProTPW; ++t) {
+    const int64_t th = th0 + t;
+    if (th >= n_th) break;
+    const int h = (int)(th % H);
+    const int64_t base = th * K;
+    float ssq = 0.f, ssk = 0.f;
+    const float A = expf(a_log[h]);
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int c = lane + 64 * m;
-    if (c >= K) break;
-    qn[base + c] = vq[m] * rq;
-    kn[base + c] = vk[m] * rk;
-    g[base + c] = gate_value(vx[m], A, gate_form, lb);
+    for (int m = 0; m < M; ++m) {
+      if (lane + 64 * m >= K) break;
+      ssq = fmaf(vq[t][m], vq[t][m], ssq);
+      ssk = fmaf(vk[t][m], vk[t][m], ssk);
+    }
+    ssq = wave_sum(ssq);
+    ssk = wave_sum(ssk);
+    const float rq = 1.f / sqrtf(ssq + 1e-6f), rk = 1.f / sqrtf(ssk + 1e-6f);
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      const int c = lane + 64 * m;
+      if (c >= K) break;
+      qn[base + c] = vq[t][m] * rq;
+      kn[base + c] = vk[t][m] * rk;
+      g[base + c] = gate_value(vx[t][m], A, gate_form, lb);
+    }
+    if (lane == 0) bt[th] = sigmoid_f(bl[t]);
   }
-  if (lane == 0) bt[th] = sigmoid_f(bl);
 }
 
 // One workgroup per chunk-head (flattened j*H + h).  The decay factors use the
@@ -648,7 +664,8 @@ template <typename Tin, int C>
 hipError_t run_prep(const FwdArgs& a, hipStream_t s) {
   const int64_t n_th = (int64_t)a.B * a.T * a.H;
   if (n_th > 0) {
-    const int64_t blocks = (n_th + 3) / 4;
+    const int64_t per_block = (kThreads / 64) * kProTPW;
+    const int64_t blocks = (n_th + per_block - 1) / per_block;
     hipLaunchKernelGGL(k_prologue_valu<Tin>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.gate, (const Tin*)a.beta,
                        a.a_log, a.dt_bias, n_th, a.H, a.HK, a.K, a.gate_form, a.lb, a.qn, a.kn, a.g, a.bt);
@@ -667,7 +684,8 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
   const int64_t n_th = (int64_t)a.B * a.T * a.H;
   mark(a, kStagePrologue, 0, s);
   if (n_th > 0) {
-    const int64_t blocks = (n_th + 3) / 4;
+    const int64_t per_block = (kThreads / 64) * kProTPW;
+    const int64_t blocks = (n_th + per_block - 1) / per_block;
     hipLaunchKernelGGL(k_prologue_valu<Tin>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.gate, (const Tin*)a.beta,
                        a.a_log, a.dt_bias, n_th, a.H, a.HK, a.K, a.gate_form, a.lb, a.qn, a.kn, a.g, a.bt);
