@@ -2,8 +2,9 @@
 //
 // It serves fp32 inputs and every chunk size, and recomputes the chunk factors
 // for the backward.  Three kernels, all fp32 arithmetic (for 64-token chunks
-// the chunk kernel's off-diagonal Akk/Aqk blocks and its W, U products run on
-// fp32 matrix cores, v_mfma_f32_16x16x4f32; everything else on VALU):
+// the chunk kernel's off-diagonal Akk/Aqk blocks, the off-diagonal blocks of
+// Tm and its W, U products run on fp32 matrix cores, v_mfma_f32_16x16x4f32;
+// everything else on VALU):
 //
 //   1. k_prologue_valu   one wave per token-head: q^, k^ (L2 norm), the
 //                        per-key-channel log-decay g from the raw gate logits,
@@ -351,6 +352,32 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
       for (int t = 0; t < 16; ++t) sA[16 * wv + t][16 * wv + ln] = col[t];
     __syncthreads();
     for (int R = 1; R < NB; ++R) {
+      if constexpr (C == 64) {
+        // On fp32 matrix cores, wave I < R taking block I (lane l holds
+        // A[l%16][l/16], B[l/16][l%16] and D[4(l/16)+e][l%16] of each
+        // 16 x 16 x 4 step): first M_I, then Tm_RI = -(Tm_RR Diag(beta_R)) M_I,
+        // summed over all 16 columns of Tm_RR (zero above its diagonal).
+        const int lq = ln & 15, lg = ln >> 4;
+        if (wv < R) {
+          f32x4 acc = zero4;
+          for (int u0 = 16 * wv; u0 < 16 * R; u0 += 4)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[16 * R + lq][u0 + lg], sA[u0 + lg][16 * wv + lq],
+                                                       acc, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sM[wv][4 * lg + e][lq] = acc[e];
+        }
+        __syncthreads();
+        if (wv < R) {
+          f32x4 acc = zero4;
+#pragma unroll
+          for (int u0 = 0; u0 < 16; u0 += 4)
+            acc = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                sA[16 * R + lq][16 * R + u0 + lg] * sB[16 * R + u0 + lg], sM[wv][u0 + lg][lq], acc, 0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sA[16 * R + 4 * lg + e][16 * wv + lq] = -acc[e];
+        }
+        __syncthreads();
+      } else {
       // M_I = sum_{I <= J < R} Akk_RJ Tm_JI for every I < R
       for (int e = tid; e < R * 256; e += kThreads) {
         const int I = e >> 8, t = (e >> 4) & 15, sc = e & 15;
@@ -367,6 +394,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
         sA[16 * R + t][16 * I + sc] = -acc;
       }
       __syncthreads();
+      }
     }
     // strictly upper blocks of Tm are zero
     for (int e = tid; e < C * C; e += kThreads) {
