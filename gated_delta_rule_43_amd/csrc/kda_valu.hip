@@ -460,17 +460,6 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
       for (int e = 0; e < 4; ++e) out[(int64_t)(16 * rt + 4 * lg + e) * D + 16 * ct + ln] = acc[e];
     }
   };
-  // V's loads are issued before the W product and staged in X's place after it
-  const Tin* v = (const Tin*)a.v;
-  constexpr int NV = (C * kMaxD + kThreads - 1) / kThreads;
-  float vv[NV];
-#pragma unroll
-  for (int u = 0; u < NV; ++u) {
-    const int p = tid + u * kThreads, i = p / V;
-    const bool in = p < C * V && i < L;
-    const float x = load_f32(v + (in ? tok_off(i) * V + p % V : tok_off(0) * V));
-    vv[u] = in ? x : 0.f;
-  }
   if constexpr (C == 64) {
     tm_product(W, K);
   } else {
@@ -486,7 +475,18 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
     }
   }
   float* U = (float*)a.U + chb * C * V;
-  // Diag(beta) V to LDS in X's place, then U's rows read it from there
+  // Diag(beta) V to LDS in X's place (every load issued before the first
+  // store), then U's rows read it from there
+  const Tin* v = (const Tin*)a.v;
+  constexpr int NV = (C * kMaxD + kThreads - 1) / kThreads;
+  float vv[NV];
+#pragma unroll
+  for (int u = 0; u < NV; ++u) {
+    const int p = tid + u * kThreads, i = p / V;
+    const bool in = p < C * V && i < L;
+    const float x = load_f32(v + (in ? tok_off(i) * V + p % V : tok_off(0) * V));
+    vv[u] = in ? x : 0.f;
+  }
   __syncthreads();  // X is no longer read
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
