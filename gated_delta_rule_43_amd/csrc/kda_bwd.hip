@@ -614,7 +614,12 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     for (int r0 = 0; r0 < C; r0 += 16) {
       float gv[16];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) gv[u] = r0 + u < L ? a.g[th(r0 + u) * K + c] : 0.f;
+      for (int u = 0; u < 16; ++u) {
+        // a clamped, valid row and the select after the load: a load under a
+        // condition of its own is waited for on the spot
+        const float x = a.g[th(r0 + u < L ? r0 + u : 0) * K + c];
+        gv[u] = r0 + u < L ? x : 0.f;
+      }
 #pragma unroll
       for (int u = 0; u < 16; ++u) {
         acc += gv[u];
@@ -623,7 +628,8 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     }
   }
   for (int r = tid; r < C; r += NT) {
-    sB[r] = r < L ? a.bt[th(r)] : 0.f;
+    const float x = a.bt[th(r < L ? r : 0)];
+    sB[r] = r < L ? x : 0.f;
     sDb[r] = 0.f;
   }
   for (int p = tid; p < C * C; p += NT) sT[p / C][p % C] = a.Tm_out[chb * C * C + p];
@@ -665,7 +671,8 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
       for (int u = 0; u < NR; ++u) {
         const int e = tid + NT * u, r = e / VTL, jj = e % VTL;
         pd[u] = dDl[(int64_t)r * V + j0 + jj];
-        po[u] = r < L ? load_f32(dO + th(r) * V + j0 + jj) : 0.f;
+        const float x = load_f32(dO + th(r < L ? r : 0) * V + j0 + jj);
+        po[u] = r < L ? x : 0.f;
       }
     };
     fetch1(0);
@@ -745,8 +752,10 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
         const bool in = r < L;
         qd[u] = dDl[(int64_t)r * V + j0 + jj];
         qD[u] = Dl[(int64_t)r * V + j0 + jj];
-        qo[u] = in ? load_f32(dO + th(r) * V + j0 + jj) : 0.f;
-        qv[u] = in ? load_f32(v + th(r) * V + j0 + jj) : 0.f;
+        const int64_t rv = th(in ? r : 0) * V + j0 + jj;
+        const float xo = load_f32(dO + rv), xv = load_f32(v + rv);
+        qo[u] = in ? xo : 0.f;
+        qv[u] = in ? xv : 0.f;
       }
     };
     fetch2(0);
@@ -814,7 +823,8 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
 #pragma unroll
   for (int m = 0; m < NE1; ++m) {
     const int r = rb1 + RSTEP1 * m;
-    sKtT[c1][r] = r < L ? a.kn[th(r) * K + c1] * __expf(sGam[r][c1]) : 0.f;
+    const float x = a.kn[th(r < L ? r : 0) * K + c1];
+    sKtT[c1][r] = r < L ? x * __expf(sGam[r][c1]) : 0.f;
   }
     // P (scaled) and the V half of Y, lower triangle i <= r < L; zero elsewhere
     for (int e = tid; e < C * C; e += NT) {
@@ -852,7 +862,8 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
       for (int e = tid; e < C * VTL; e += NT) {
         const int r = e / VTL, jj = e % VTL;
         tdD[r][jj] = dDl[(int64_t)r * V + j0 + jj];
-        tdO[r][jj] = r < L ? load_f32(dO + th(r) * V + j0 + jj) : 0.f;
+        const float x = load_f32(dO + th(r < L ? r : 0) * V + j0 + jj);
+        tdO[r][jj] = r < L ? x : 0.f;
       }
       __syncthreads();
       for (int jj = 0; jj < VTL; jj += 4) {
@@ -900,8 +911,10 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
       const bool in = r < L;
       tdD2[r][jj] = dDl[(int64_t)r * V + j0 + jj];
       tD2[r][jj] = Dl[(int64_t)r * V + j0 + jj];
-      tdO2[r][jj] = in ? load_f32(dO + th(r) * V + j0 + jj) : 0.f;
-      tv2[r][jj] = in ? load_f32(v + th(r) * V + j0 + jj) : 0.f;
+      const int64_t rv = th(in ? r : 0) * V + j0 + jj;
+      const float xo = load_f32(dO + rv), xv = load_f32(v + rv);
+      tdO2[r][jj] = in ? xo : 0.f;
+      tv2[r][jj] = in ? xv : 0.f;
     }
     __syncthreads();
     for (int jj = 0; jj < VTL; jj += 4) {
@@ -942,7 +955,8 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
 #pragma unroll
   for (int m = 0; m < NE1; ++m) {
     const int r = rb1 + RSTEP1 * m;
-    sKtT[c1][r] = r < L ? a.kn[th(r) * K + c1] * __expf(sGam[r][c1]) : 0.f;
+    const float x = a.kn[th(r < L ? r : 0) * K + c1];
+    sKtT[c1][r] = r < L ? x * __expf(sGam[r][c1]) : 0.f;
   }
 #pragma unroll
   for (int m = 0; m < NE2; ++m) {
