@@ -489,9 +489,13 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
         sS[c][cc] = st[t][e];
       }
     }
+    // (a clamped, valid row and the select after the load: a load under a
+    // condition of its own is waited for on the spot)
+#pragma unroll
     for (int e = tid; e < C * VT; e += NT) {
       const int r = e / VT, cc = e % VT;
-      sO[r][cc] = r < L ? load_f32(dO + ((int64_t)(tok0 + r) * H + h) * V + col0 + cc) : 0.f;
+      const float x = load_f32(dO + ((int64_t)(tok0 + (r < L ? r : 0)) * H + h) * V + col0 + cc);
+      sO[r][cc] = r < L ? x : 0.f;
     }
     *(float4*)&sA[tid / (C / 4)][4 * (tid % (C / 4))] = pa;
     put_k(sKb, pk0, pk1);
@@ -515,12 +519,17 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
     __syncthreads();  // dDelta complete; Aqk and Kbar are no longer read
     put_k(sQt, pq0, pq1);
     put_k(sW, pw0, pw1);
-    if (j - 1 >= jc0) fetch(chb - H);  // the previous chunk of this sequence
     float gl[TPW][4];
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) gl[t][e] = gL[16 * ((w * TPW + t) >> 2) + 4 * lg + e];
+    // The previous chunk of this sequence, issued after gL's loads (held there
+    // by the scheduling barrier) so that waiting for gL leaves it in flight;
+    // unconditional (the first chunk reads itself again, unused) so that the
+    // wait can count it.
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(j - 1 >= jc0 ? chb - H : chb);
     __syncthreads();
     // dS0 = Diag(gL) dS_L + Qt_s^T dO - W^T dDelta (rows past the chunk end are zero)
 #pragma unroll
