@@ -239,6 +239,18 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_mfma(BwdArgs b) {
     const float* gL = a.gL + chb * K;
     float* hc = b.hc + chb * K * V;
     float* Dc = b.Dc + chb * C * V;
+    // This chunk's U tile and gL are loaded before the next chunk's W and
+    // Kbar (the scheduling barriers hold that order), so that waiting for
+    // them leaves the prefetch in flight.
+    f32x4 acc;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = U[(int64_t)(16 * drt + 4 * lg + e) * V + col0 + 16 * dct + ln];
+    float gl[TPW][4];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gl[t][e] = gL[16 * ((w * TPW + t) >> 2) + 4 * lg + e];
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();  // the previous chunk is done with sW, sKb, sS, sD
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
@@ -260,15 +272,10 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_mfma(BwdArgs b) {
         *(float4*)&sKb[r1][c1] = pk1;
       }
     }
-    if (j + 1 < jc1) fetch_wk(chb + H);  // the next chunk of this sequence
-    f32x4 acc;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = U[(int64_t)(16 * drt + 4 * lg + e) * V + col0 + 16 * dct + ln];
-    float gl[TPW][4];
-#pragma unroll
-    for (int t = 0; t < TPW; ++t)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) gl[t][e] = gL[16 * ((w * TPW + t) >> 2) + 4 * lg + e];
+    __builtin_amdgcn_sched_barrier(0);
+    // the next chunk of this sequence; unconditional (the last chunk reads
+    // itself again, unused) so that the waits can count it
+    fetch_wk(j + 1 < jc1 ? chb + H : chb);
     __syncthreads();
     // Delta = U - W S
 #pragma unroll 8
