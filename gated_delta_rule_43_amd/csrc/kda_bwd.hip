@@ -625,30 +625,46 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   float (*sTk)[K] = (float(*)[K])sR4;
 
   // ---- phase A: gamma, beta, Tm ----
-  for (int c = tid; c < K; c += NT) {
-    float acc = 0.f;
-    for (int r0 = 0; r0 < C; r0 += 16) {
-      float gv[16];
+  // The chunk's g reaches LDS first, every thread loading its 16-byte pieces
+  // (rows past the chunk end are zero); then each channel's thread adds down
+  // its column.  Loads under a row condition read a clamped, valid row and
+  // select afterwards: a load under a condition of its own is waited for on
+  // the spot.
+  {
+    constexpr int NP = (C * K / 4 + NT - 1) / NT;
+    float4 gq[NP];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        // a clamped, valid row and the select after the load: a load under a
-        // condition of its own is waited for on the spot
-        const float x = a.g[th(r0 + u < L ? r0 + u : 0) * K + c];
-        gv[u] = r0 + u < L ? x : 0.f;
-      }
+    for (int u = 0; u < NP; ++u) {
+      const int p = 4 * (tid + u * NT), r = p / K, c = p % K;
+      const bool in = p < C * K && r < L;
+      const float4 x = *(const float4*)(a.g + th(in ? r : 0) * K + (in ? c : 0));
+      gq[u] = in ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+    for (int r = tid; r < C; r += NT) {
+      const float x = a.bt[th(r < L ? r : 0)];
+      sB[r] = r < L ? x : 0.f;
+      sDb[r] = 0.f;
+    }
+    for (int p = tid; p < C * C; p += NT) sT[p / C][p % C] = a.Tm_out[chb * C * C + p];
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        acc += gv[u];
-        sGam[r0 + u][c] = acc;
+    for (int u = 0; u < NP; ++u) {
+      const int p = 4 * (tid + u * NT), r = p / K, c = p % K;
+      if (p < C * K) {
+        sGam[r][c] = gq[u].x;
+        sGam[r][c + 1] = gq[u].y;
+        sGam[r][c + 2] = gq[u].z;
+        sGam[r][c + 3] = gq[u].w;
       }
     }
   }
-  for (int r = tid; r < C; r += NT) {
-    const float x = a.bt[th(r < L ? r : 0)];
-    sB[r] = r < L ? x : 0.f;
-    sDb[r] = 0.f;
+  __syncthreads();
+  for (int c = tid; c < K; c += NT) {
+    float acc = 0.f;
+    for (int r = 0; r < C; ++r) {
+      acc += sGam[r][c];
+      sGam[r][c] = acc;
+    }
   }
-  for (int p = tid; p < C * C; p += NT) sT[p / C][p % C] = a.Tm_out[chb * C * C + p];
 
   // ---- phase B: products over the value dimension, and dV, in two sweeps over
   //      32-column value tiles staged in LDS (dW and dQ~; then dKbar, P, the V
