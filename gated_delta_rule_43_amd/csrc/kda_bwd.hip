@@ -349,7 +349,8 @@ __global__ __launch_bounds__(64 * state_waves(C)) void k_bwd_dstate(BwdArgs b) {
 #pragma unroll
     for (int m = 0; m < RD; ++m) {
       const int r = w * RD + m;
-      sO[r][lane] = r < L ? load_f32(dO + ((int64_t)(tok0 + r) * H + h) * V + col) : 0.f;
+      const float x = load_f32(dO + ((int64_t)(tok0 + (r < L ? r : 0)) * H + h) * V + col);
+      sO[r][lane] = r < L ? x : 0.f;
     }
     stage(sR, (const float*)a.Aqk + chb * C * C, C * C, NT);
     stage(sR + C * C, (const float*)a.Kb + chb * C * K, C * K, NT);
@@ -1090,10 +1091,11 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     const int r = rb2 + RSTEP2 * m;
     if (r < C) sZ[r][i2] = zv[m];
   }
+#pragma unroll
   for (int e = tid; e < C * K / 4; e += NT) {
     const int r = e / (K / 4), c4 = e % (K / 4);
-    ((float4*)&sQn[r][0])[c4] = r < L ? ((const float4*)(a.qn + th(r) * K))[c4]
-                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 x = ((const float4*)(a.qn + th(r < L ? r : 0) * K))[c4];
+    ((float4*)&sQn[r][0])[c4] = r < L ? x : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __syncthreads();
 
@@ -1117,10 +1119,11 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     const int r = rb2 + RSTEP2 * m;
     if (r < C) sY[r][i2] = dak[m];
   }
+#pragma unroll
   for (int e = tid; e < C * K / 4; e += NT) {
     const int r = e / (K / 4), c4 = e % (K / 4);
-    ((float4*)&sKn[r][0])[c4] = r < L ? ((const float4*)(a.kn + th(r) * K))[c4]
-                                      : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 x = ((const float4*)(a.kn + th(r < L ? r : 0) * K))[c4];
+    ((float4*)&sKn[r][0])[c4] = r < L ? x : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __syncthreads();
 

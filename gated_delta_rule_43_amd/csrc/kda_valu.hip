@@ -169,7 +169,10 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
         for (int e = 0; e < 4; ++e) sG[p / K][p % K + e] = gv[u][e];
     }
   }
-  for (int r = tid; r < C; r += kThreads) sB[r] = r < L ? a.bt[tok_off(r)] : 0.f;
+  for (int r = tid; r < C; r += kThreads) {
+    const float x = a.bt[tok_off(r < L ? r : 0)];
+    sB[r] = r < L ? x : 0.f;
+  }
   __syncthreads();
   for (int c = tid; c < K; c += kThreads) {
     float acc = 0.f;
