@@ -445,7 +445,19 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
   static_assert(C * C / 4 == NT && C * K / 4 <= 2 * NT, "one Aqk piece, one or two of the others");
   constexpr bool TWO = C * K / 4 == 2 * NT;
   float4 pa, pk0, pk1, pq0, pq1, pw0, pw1;
-  auto fetch = [&](int64_t chb) __attribute__((always_inline)) {
+  // dO of the prefetched chunk, raw (rows past its end are masked when staged)
+  constexpr int NO = C * VT / NT;
+  static_assert(NO * NT == C * VT, "whole dO tiles per thread");
+  const Tin* dO = (const Tin*)b.d_o;
+  float po[NO];
+  auto fetch = [&](int jn) __attribute__((always_inline)) {
+    const int64_t chb = (int64_t)jn * H + h;
+    const int tokn = a.chunk_tok[jn], Ln = a.chunk_len[jn];
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+      const int e = tid + u * NT, r = e / VT, cc = e % VT;
+      po[u] = load_f32(dO + ((int64_t)(tokn + (r < Ln ? r : 0)) * H + h) * V + col0 + cc);
+    }
     const float4* A4 = (const float4*)((const float*)a.Aqk + chb * C * C);
     const float4* K4 = (const float4*)((const float*)a.Kb + chb * C * K);
     const float4* Q4 = (const float4*)((const float*)a.Qt + chb * C * K);
@@ -477,15 +489,14 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
     }
   }
   const int drt = w >> 2, dct = w & 3;  // this wave's dDelta tile
-  const Tin* dO = (const Tin*)b.d_o;
   const int jc0 = a.seq_chunk0[n], jc1 = a.seq_chunk0[n + 1];
-  if (jc0 < jc1) fetch((int64_t)(jc1 - 1) * H + h);
+  if (jc0 < jc1) fetch(jc1 - 1);
   for (int j = jc1 - 1; j >= jc0; --j) {
     const int64_t chb = (int64_t)j * H + h;
     const float* gL = a.gL + chb * K;
     float* dhc = b.dhc + chb * K * V;
     float* dDc = b.dDc + chb * C * V;
-    const int tok0 = a.chunk_tok[j], L = a.chunk_len[j];
+    const int L = a.chunk_len[j];
     __syncthreads();  // the previous chunk is done with sR, sO, sD, sS
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
@@ -497,13 +508,10 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
         sS[c][cc] = st[t][e];
       }
     }
-    // (a clamped, valid row and the select after the load: a load under a
-    // condition of its own is waited for on the spot)
 #pragma unroll
-    for (int e = tid; e < C * VT; e += NT) {
-      const int r = e / VT, cc = e % VT;
-      const float x = load_f32(dO + ((int64_t)(tok0 + (r < L ? r : 0)) * H + h) * V + col0 + cc);
-      sO[r][cc] = r < L ? x : 0.f;
+    for (int u = 0; u < NO; ++u) {
+      const int e = tid + u * NT, r = e / VT, cc = e % VT;
+      sO[r][cc] = r < L ? po[u] : 0.f;
     }
     *(float4*)&sA[tid / (C / 4)][4 * (tid % (C / 4))] = pa;
     put_k(sKb, pk0, pk1);
@@ -532,12 +540,12 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) gl[t][e] = gL[16 * ((w * TPW + t) >> 2) + 4 * lg + e];
-    // The previous chunk of this sequence, issued after gL's loads (held there
-    // by the scheduling barrier) so that waiting for gL leaves it in flight;
-    // unconditional (the first chunk reads itself again, unused) so that the
-    // wait can count it.
+    // The previous chunk of this sequence (its operands and its dO tile),
+    // issued after gL's loads (held there by the scheduling barrier) so that
+    // waiting for gL leaves it in flight; unconditional (the first chunk reads
+    // itself again, unused) so that the wait can count it.
     __builtin_amdgcn_sched_barrier(0);
-    fetch(j - 1 >= jc0 ? chb - H : chb);
+    fetch(j - 1 >= jc0 ? j - 1 : j);
     __syncthreads();
     // dS0 = Diag(gL) dS_L + Qt_s^T dO - W^T dDelta (rows past the chunk end are zero)
 #pragma unroll
