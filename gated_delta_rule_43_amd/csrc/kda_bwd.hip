@@ -209,7 +209,18 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_mfma(BwdArgs b) {
   constexpr int NF4 = C * K / 4 / NT;
   static_assert(NF4 * NT * 4 == C * K && NF4 <= 2, "one or two float4 pieces per thread");
   float4 pw0, pw1, pk0, pk1;  // named, so that they stay in registers
+  f32x4 pu;                   // the chunk's U tile of this wave's Delta tile
+  float pgl[TPW][4];          // its gL entries of this wave's state tiles
+  const int drt = w >> 2, dct = w & 3;  // this wave's Delta tile
   auto fetch_wk = [&](int64_t chb) __attribute__((always_inline)) {
+    const float* U = (const float*)a.U + chb * C * V;
+    const float* gL = a.gL + chb * K;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pu[e] = U[(int64_t)(16 * drt + 4 * lg + e) * V + col0 + 16 * dct + ln];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pgl[t][e] = gL[16 * ((w * TPW + t) >> 2) + 4 * lg + e];
     const float4* W4 = (const float4*)((const float*)a.W + chb * C * K);
     const float4* K4 = (const float4*)((const float*)a.Kb + chb * C * K);
     pw0 = W4[tid];
@@ -230,27 +241,19 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_mfma(BwdArgs b) {
       st[t][e] = a.init ? a.init[sbase + (int64_t)c * V + col] : 0.f;
     }
   }
-  const int drt = w >> 2, dct = w & 3;  // this wave's Delta tile
   const int jc0 = a.seq_chunk0[n], jc1 = a.seq_chunk0[n + 1];
   if (jc0 < jc1) fetch_wk((int64_t)jc0 * H + h);
   for (int j = jc0; j < jc1; ++j) {
     const int64_t chb = (int64_t)j * H + h;
-    const float* U = (const float*)a.U + chb * C * V;
-    const float* gL = a.gL + chb * K;
     float* hc = b.hc + chb * K * V;
     float* Dc = b.Dc + chb * C * V;
-    // This chunk's U tile and gL are loaded before the next chunk's W and
-    // Kbar (the scheduling barriers hold that order), so that waiting for
-    // them leaves the prefetch in flight.
-    f32x4 acc;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) acc[e] = U[(int64_t)(16 * drt + 4 * lg + e) * V + col0 + 16 * dct + ln];
+    // this chunk's U tile and gL came with its W and Kbar, a chunk ahead
+    f32x4 acc = pu;
     float gl[TPW][4];
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) gl[t][e] = gL[16 * ((w * TPW + t) >> 2) + 4 * lg + e];
-    __builtin_amdgcn_sched_barrier(0);
+      for (int e = 0; e < 4; ++e) gl[t][e] = pgl[t][e];
     __syncthreads();  // the previous chunk is done with sW, sKb, sS, sD
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
