@@ -12,6 +12,9 @@
 //                 accumulators; per chunk
 //                     X = W S,  Y = Qt S,  Delta = U - X,
 //                     O = Y + Aqk Delta,  S <- Diag(gL) S + Kbar^T Delta.
+//                 S and Delta enter W S and Kbar^T Delta as bf16 hi + lo pairs
+//                 (about 16 significant bits), so the carried state, the final
+//                 state and the slice summaries keep fp32-level accuracy.
 //
 // Chunk algebra (derived from the token recurrence, see kda_valu.hip):
 //   Akk[r,i] = sum_c k^_rc k^_ic e^{gamma_rc-gamma_ic} (i<r), Aqk likewise with
@@ -96,6 +99,15 @@ __device__ __forceinline__ void split4(f32x4 x, f32x4& hi, f32x4& lo) {
     hi[e] = (float)(__bf16)x[e];
     lo[e] = x[e] - hi[e];
   }
+}
+// Two accumulator tiles as one B operand in bf16 hi + lo parts: hi = bf16(x),
+// lo = bf16(x - hi), so hi + lo carries about 16 significant bits of x.
+__device__ __forceinline__ void split_frag(f32x4 a, f32x4 b, bf16x8& hi, bf16x8& lo) {
+  f32x4 ah, al, bh, bl;
+  split4(a, ah, al);
+  split4(b, bh, bl);
+  hi = pair_frag(ah, bh);
+  lo = pair_frag(al, bl);
 }
 __device__ __forceinline__ void unpack4(uint2 u, float* out) {
   out[0] = bf16_to_f32((bf16)(u.x & 0xffff));
@@ -881,26 +893,8 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
     const bf16x8* sW = (const bf16x8*)(cur + R::oW);
     const bf16x8* sKbar = (const bf16x8*)(cur + R::oKbar);
     const float* sGL = (const float*)(cur + R::oGL);
-    // every staged A-operand fragment of this chunk, read up front
-    bf16x8 fW[4][NKJ], fQ[4][NKJ], fK[NKT][2];
-#pragma unroll
-    for (int t = 0; t < 4; ++t)
-#pragma unroll
-      for (int j = 0; j < NKJ; ++j) {
-        fW[t][j] = sW[(t * NKJ + j) * 64 + lane];
-        if (!SUM) fQ[t][j] = sQt[(t * NKJ + j) * 64 + lane];
-      }
-#pragma unroll
-    for (int at = 0; at < NKT; ++at) {
-      fK[at][0] = sKbar[(at * 2 + 0) * 64 + lane];
-      fK[at][1] = sKbar[(at * 2 + 1) * 64 + lane];
-    }
-    float gl[NKT][4];
-#pragma unroll
-    for (int at = 0; at < NKT; ++at) {
-      const float4 v4 = *(const float4*)&sGL[16 * at + 4 * g];
-      gl[at][0] = v4.x; gl[at][1] = v4.y; gl[at][2] = v4.z; gl[at][3] = v4.w;
-    }
+    // the staged A-operand fragments are read from LDS where each product
+    // needs them (W, then Qt, then Kbar^T), so that one set is live at a time
 #pragma unroll
     for (int ct = 0; ct < NCT; ++ct) {
       f32x4 Ut[4];
@@ -912,29 +906,40 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
         Ut[t][2] = bf16_to_f32((bf16)(u.y & 0xffff));
         Ut[t][3] = bf16_to_f32((bf16)(u.y >> 16));
       }
-      // S as B operand (k = key channel in sigma order)
-      bf16x8 sb[NKJ];
+      // S as B operand (k = key channel in sigma order), as bf16 hi + lo parts:
+      // the state's own products (W S here, Kbar^T Delta below) see about 16
+      // significant bits of it, so the carried state keeps fp32-level accuracy
+      // over long sequences; the output product Qt S uses the hi part alone
+      bf16x8 sb[NKJ], sl[NKJ];
 #pragma unroll
-      for (int j = 0; j < NKJ; ++j) sb[j] = pair_frag(S[2 * j][ct], S[2 * j + 1][ct]);
+      for (int j = 0; j < NKJ; ++j) split_frag(S[2 * j][ct], S[2 * j + 1][ct], sb[j], sl[j]);
       // X = W S (rows r, column n); Yt = (Qt S)^T = S^T Qt^T: the same fragments
       // with the operands swapped, giving lane (g, n) row 16t+n, columns 4g..4g+3
       f32x4 X[4], Y[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         X[t] = zero4();
-        Y[t] = zero4();
 #pragma unroll
         for (int j = 0; j < NKJ; ++j) {
-          X[t] = mfma(fW[t][j], sb[j], X[t]);
-          if (!SUM) Y[t] = mfma(sb[j], fQ[t][j], Y[t]);
+          const bf16x8 fw = sW[(t * NKJ + j) * 64 + lane];
+          X[t] = mfma(fw, sb[j], X[t]);
+          X[t] = mfma(fw, sl[j], X[t]);
+        }
+      }
+      if (!SUM) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          Y[t] = zero4();
+#pragma unroll
+          for (int j = 0; j < NKJ; ++j) Y[t] = mfma(sb[j], sQt[(t * NKJ + j) * 64 + lane], Y[t]);
         }
       }
       f32x4 D[4];
 #pragma unroll
       for (int t = 0; t < 4; ++t) D[t] = Ut[t] - X[t];
-      bf16x8 db[2];
-      db[0] = pair_frag(D[0], D[1]);
-      db[1] = pair_frag(D[2], D[3]);
+      bf16x8 db[2], dl[2];
+      split_frag(D[0], D[1], db[0], dl[0]);
+      split_frag(D[2], D[3], db[1], dl[1]);
       if (!SUM) {
 #pragma unroll
         for (int t = 0; t < 4; ++t) {
@@ -945,20 +950,15 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
       }
 #pragma unroll
       for (int at = 0; at < NKT; ++at) {
-        f32x4 acc;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[e] = gl[at][e] * S[at][ct][e];
-        acc = mfma(fK[at][0], db[0], acc);
-        acc = mfma(fK[at][1], db[1], acc);
+        const float4 gl = *(const float4*)&sGL[16 * at + 4 * g];
+        const bf16x8 fk0 = sKbar[(at * 2 + 0) * 64 + lane], fk1 = sKbar[(at * 2 + 1) * 64 + lane];
+        f32x4 acc = {gl.x * S[at][ct][0], gl.y * S[at][ct][1], gl.z * S[at][ct][2], gl.w * S[at][ct][3]};
+        acc = mfma(fk0, db[0], acc);
+        acc = mfma(fk1, db[1], acc);
+        acc = mfma(fk0, dl[0], acc);
+        acc = mfma(fk1, dl[1], acc);
         S[at][ct] = acc;
       }
-    }
-    // spread the LDS reads and memory instructions over the matrix-core stream
-#pragma unroll
-    for (int i = 0; i < 14; ++i) {
-      __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);  // LDS reads
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);  // MFMA
-      __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);  // global memory
     }
     otok = tok_cur;
     olen = len_cur;
