@@ -21,9 +21,16 @@ Besides the throughput it reports
     summary of every slice (kda_state_summary, one call) and their composition
     from the initial state (kda_apply_state_summary, slice by slice), compared
     with the forward's final state;
-  * "roofline": the dominant kernel's algorithmic bytes per launch divided by
-    its average duration, timed live with HIP events recorded by the library
-    around each stage on the kernel's own stream (kda_fwd_profiled);
+  * "roofline": the whole forward's algorithmic bytes (1,282 B per token-head
+    at dk=dv=128 bf16: q, k, gate, v, beta read and o written once, plus the
+    fp32 states) divided by the dominant kernel's duration, timed live with HIP
+    events recorded by the library around each stage on the kernel's own
+    stream (kda_fwd_profiled); "traffic" is the counter-measured HBM bytes of
+    that kernel and "design_bytes_per_launch" the bytes it must move given
+    this design's intermediates;
+  * timing: per-step events with 1 GiB of scratch written between steps (the
+    256 MB last-level cache evicted) for the headline and every workload,
+    and the same steps back to back as warm_*;
   * "cpu_baseline": the CPU oracle, as it stands, timed on this host on a
     bounded sample of the same workload (a few heads of one row).
 Only one GPU is used: --gpus above 1 exits with a message.
@@ -45,59 +52,12 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from gated_delta_rule_43_amd import kda, synthetic  # noqa: E402
+from gated_delta_rule_43_amd.timing import StageEvents, evict_caches  # noqa: E402
 
 METRIC = "KDA chunked fwd Mtokens/s at H=32,dk=dv=128 bf16; MFMA util % of peak"
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, TFLOP/s
 FP32_VECTOR_PEAK_TFLOPS = 157.3  # MI355X fp32 vector ALU, TFLOP/s
-
-
-def _hip():
-    """The HIP runtime torch already loaded (same soname as libkda.so's)."""
-    try:
-        return ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
-    except OSError:
-        return ctypes.CDLL(os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so"))
-
-
-class StageEvents:
-    """2*nstages hipEvents per timed step, read back after the timed region."""
-
-    def __init__(self, steps, nstages=None):
-        self.nstages = kda.NUM_STAGES if nstages is None else nstages
-        self.hip = _hip()
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
-        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
-                                                 ctypes.c_void_p]
-        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
-        n = 2 * self.nstages
-        self.arrays = []
-        for _ in range(steps):
-            arr = (ctypes.c_void_p * n)()
-            for i in range(n):
-                ev = ctypes.c_void_p()
-                rc = self.hip.hipEventCreate(ctypes.byref(ev))
-                if rc != 0:
-                    raise RuntimeError("hipEventCreate failed (%d)" % rc)
-                arr[i] = ev.value
-            self.arrays.append(arr)
-
-    def stage_ms(self):
-        """Average duration (ms) of each stage over the recorded steps."""
-        out = np.zeros(self.nstages)
-        for arr in self.arrays:
-            for s in range(self.nstages):
-                ms = ctypes.c_float(0.0)
-                rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), arr[2 * s], arr[2 * s + 1])
-                if rc != 0:
-                    raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
-                out[s] += ms.value
-        return out / max(1, len(self.arrays))
-
-    def close(self):
-        for arr in self.arrays:
-            for ev in arr:
-                self.hip.hipEventDestroy(ev)
 
 
 def algorithmic(w):
@@ -146,6 +106,17 @@ def measured_conv_traffic():
     return None if k is None else int(k["traffic_bytes"])
 
 
+def path_algorithmic_bytes(w, N):
+    """Algorithmic HBM bytes of one whole forward (the measurement notes'
+    figure): per token-head q, k, gate, v and beta read once and o written
+    once, plus per (sequence, head) the fp32 state read (initial_state) and
+    written (final_state) when present."""
+    bytes_th, _ = algorithmic(w)
+    states = N * w.H * w.K * w.V * 4 * ((1 if w.init_std is not None else 0)
+                                        + (1 if w.output_final_state else 0))
+    return int(w.B * w.T * w.H * bytes_th + states)
+
+
 def record_bytes(K, V):
     """Bytes of one chunk record of the MFMA path (per chunk-head): Qt, W and
     Kbar^T fragments (C*K bf16 each), Aqk fragments (C*C bf16), gL (K fp32) and
@@ -155,8 +126,10 @@ def record_bytes(K, V):
 
 
 def stage_bytes(w, stage, NT, N):
-    """Algorithmic (unique) HBM bytes one launch of a stage must move: every
-    input element read once, every output element written once."""
+    """Design bytes of one launch of a stage: the unique bytes it must move
+    given this design's chunk records (every input element read once, every
+    record and output element written once).  Not the path's algorithmic
+    bytes: the records are the design's own intermediate."""
     B, T, H, K, V = w.B, w.T, w.H, w.K, w.V
     ein = 2 if w.dtype == "bf16" else 4
     tokh = B * T * H
@@ -194,20 +167,42 @@ def fwd_runner(w, inp, dev):
 
 
 def time_fwd(step, steps, warmup):
-    """W untimed runs, then `steps` timed runs between two synchronisations:
-    (wall ms per step, mean ms of each stage from the library's events)."""
+    """W untimed runs, then two timed passes of `steps` runs each:
+
+    * evicted (the headline, as the measurement notes prescribe): before each
+      run 1 GiB of scratch is written (outside the run's events), so every
+      run reads its inputs from HBM; the step time is the median over runs of
+      the library's own events (first stage start to last stage end);
+    * warm: the runs back to back between two synchronisations (wall clock),
+      so small workloads may find their inputs in the 256 MB last-level cache.
+
+    Returns {"ms": evicted median, "stage_ms": evicted median per stage,
+    "warm_ms": ..., "warm_stage_ms": ...}."""
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
+    ev = StageEvents(steps)
+    for i in range(steps):
+        evict_caches()
+        step(ev.arrays[i])
+    torch.cuda.synchronize()
+    per_step = ev.per_step_ms()
+    per_stage = ev.per_step_stage_ms()
+    ev.close()
     ev = StageEvents(steps)
     t0 = time.perf_counter()
     for i in range(steps):
         step(ev.arrays[i])
     torch.cuda.synchronize()
-    ms = (time.perf_counter() - t0) * 1e3 / steps
-    stage_ms = ev.stage_ms()
+    warm = (time.perf_counter() - t0) * 1e3 / steps
+    warm_stage = ev.stage_ms()
     ev.close()
-    return ms, stage_ms
+    return {"ms": float(np.median(per_step)), "stage_ms": np.median(per_stage, axis=0),
+            "warm_ms": warm, "warm_stage_ms": warm_stage}
+
+
+def _stage_dict(x):
+    return dict(zip(kda.STAGE_NAMES, [round(float(v), 4) for v in x]))
 
 
 def bench_state_summary(w, inp, fin_fwd, steps, warmup, slices=8):
@@ -273,12 +268,18 @@ def bench_other_workloads(skip, steps, warmup, dev):
         w = synthetic.WORKLOADS[wid]
         print("[bench] workload %s" % w.name, file=sys.stderr, flush=True)
         inp = synthetic.make_inputs(w, dev)
-        step, res, N, _ = fwd_runner(w, inp, dev)
-        ms, stage_ms = time_fwd(step, steps, warmup)
+        step, res, N, cu_host = fwd_runner(w, inp, dev)
+        t = time_fwd(step, steps, warmup)
+        ms = t["ms"]
+        path_bytes = path_algorithmic_bytes(w, N)
         out[w.name] = {"value": round(w.B * w.T / (ms / 1e3) / 1e6, 4), "unit": "Mtokens/s",
                        "ms_per_step": round(ms, 4), "dtype": w.dtype, "sequences": N,
-                       "stage_ms": dict(zip(kda.STAGE_NAMES, [round(float(x), 4)
-                                                             for x in stage_ms]))}
+                       "stage_ms": _stage_dict(t["stage_ms"]),
+                       "warm_value": round(w.B * w.T / (t["warm_ms"] / 1e3) / 1e6, 4),
+                       "warm_ms_per_step": round(t["warm_ms"], 4),
+                       "warm_stage_ms": _stage_dict(t["warm_stage_ms"]),
+                       "path_algorithmic_bytes": path_bytes,
+                       "path_hbm_frac": round(path_bytes / (ms / 1e3) / 1e9 / HBM_PEAK_GBS, 5)}
         if w.init_std is not None and N == 1:
             print("[bench] slice summaries of %s" % w.name, file=sys.stderr, flush=True)
             out["state_summary"] = bench_state_summary(w, inp, res["fin"], steps, warmup)
@@ -533,10 +534,11 @@ def main():
         step()
         torch.cuda.synchronize()
         print("[bench] warmup %d/%d done" % (i + 1, args.warmup), file=sys.stderr, flush=True)
-    ms_per_step, stage_ms = time_fwd(step, args.steps, 0)
-    print("[bench] timed %d steps: %.3f ms/step; stages (ms) %s" % (
-        args.steps, ms_per_step, dict(zip(kda.STAGE_NAMES, np.round(stage_ms, 4).tolist()))),
-        file=sys.stderr, flush=True)
+    t = time_fwd(step, args.steps, 0)
+    ms_per_step, stage_ms = t["ms"], t["stage_ms"]
+    print("[bench] timed %d steps: %.3f ms/step (caches evicted), %.3f ms/step (back to back); "
+          "stages (ms) %s" % (args.steps, ms_per_step, t["warm_ms"], _stage_dict(stage_ms)),
+          file=sys.stderr, flush=True)
 
     tokens = w.B * w.T
     value = tokens / (ms_per_step / 1e3) / 1e6
@@ -544,15 +546,20 @@ def main():
     tokh = tokens * w.H
     NT = w.B * math.ceil(w.T / w.chunk_size) if cu is None else int(
         sum(math.ceil(int(b - a) / w.chunk_size) for a, b in zip(cu_host[:-1], cu_host[1:])))
+    path_bytes = path_algorithmic_bytes(w, N)
     dom = int(np.argmax(stage_ms))
-    dom_bytes = stage_bytes(w, dom, NT, N)
-    achieved = dom_bytes / (stage_ms[dom] / 1e3) / 1e9 if stage_ms[dom] > 0 else 0.0
+    dom_ms = float(stage_ms[dom])
+    achieved = path_bytes / (dom_ms / 1e3) / 1e9 if dom_ms > 0 else 0.0
     traffic = measured_traffic(kda.STAGE_NAMES[dom]) if args.workload == 3 else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": traffic,
-                "kernel": kda.STAGE_NAMES[dom], "kernel_ms": round(float(stage_ms[dom]), 4),
-                "bytes_per_launch": dom_bytes}
-    path_gbs = tokh * bytes_th / (ms_per_step / 1e3) / 1e9
+                "kernel": kda.STAGE_NAMES[dom], "kernel_ms": round(dom_ms, 4),
+                "bytes_per_launch": path_bytes,
+                "bytes_note": "the whole forward's algorithmic bytes (1282 B per token-head at "
+                              "dk=dv=128 bf16, plus fp32 states) over the dominant kernel's time",
+                "traffic_over_algorithmic": None if traffic is None else round(traffic / path_bytes, 3),
+                "design_bytes_per_launch": stage_bytes(w, dom, NT, N)}
+    path_gbs = path_bytes / (ms_per_step / 1e3) / 1e9
     mfma_util = tokh * flops_th / (ms_per_step / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS * 100
     out = {
         "metric": METRIC, "value": round(value, 4), "unit": "Mtokens/s", "n_gpus": 1,
@@ -562,7 +569,13 @@ def main():
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "dk": w.K, "dv": w.V,
                    "chunk_size": w.chunk_size, "lower_bound": w.lower_bound,
                    "documents": N, "initial_state": w.init_std is not None},
-        "stage_ms": dict(zip(kda.STAGE_NAMES, [round(float(x), 4) for x in stage_ms])),
+        "timing": "median of per-step HIP events with 1 GiB written between steps "
+                  "(last-level cache evicted); warm_* = the same steps back to back",
+        "stage_ms": _stage_dict(stage_ms),
+        "warm_value": round(tokens / (t["warm_ms"] / 1e3) / 1e6, 4),
+        "warm_ms_per_step": round(t["warm_ms"], 4),
+        "warm_stage_ms": _stage_dict(t["warm_stage_ms"]),
+        "path_algorithmic_bytes": path_bytes,
         "path_algorithmic_GBps": round(path_gbs, 2),
         "path_hbm_frac": round(path_gbs / HBM_PEAK_GBS, 5),
         "mfma_util_pct_useful_flops": round(mfma_util, 3),

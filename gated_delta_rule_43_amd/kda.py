@@ -186,28 +186,34 @@ def _workspace(nbytes: int, device):
 
 
 def _check_inputs(q, k, v, gate, beta, a_log, dt_bias):
-    """The projected-tensor contract (`_validate_projected_inputs` on the hyper_parallel page)."""
-    for name, t, r in (("query", q, 4), ("key", k, 4), ("value", v, 4), ("gate", gate, 4)):
-        if not isinstance(t, torch.Tensor) or t.dim() != r:
-            raise ValueError("query, key, value, and gate must be rank-4 tensors.")
-    if not isinstance(beta, torch.Tensor) or beta.dim() != 3:
-        raise ValueError("beta must be a rank-3 tensor.")
-    if q.shape != k.shape:
-        raise ValueError("query and key must have identical shapes.")
+    """Shapes of the projected inputs, against one table derived from q and v.
+
+    The contract is the one the hyper_parallel coverage page checks in
+    `_validate_projected_inputs`: q and k [B, T, H, K], v [B, T, HV, V],
+    gate [B, T, HV, K], beta [B, T, HV], a_log HV values and dt_bias HV*K
+    values, with HV a multiple of H.  Returns (B, T, H, K, V, HV)."""
+    for name, t, rank in (("q", q, 4), ("k", k, 4), ("v", v, 4), ("gate", gate, 4),
+                          ("beta", beta, 3)):
+        if not isinstance(t, torch.Tensor) or t.dim() != rank:
+            got = tuple(t.shape) if isinstance(t, torch.Tensor) else type(t).__name__
+            raise ValueError("%s: expected a rank-%d tensor, got %s" % (name, rank, got))
     B, T, H, K = q.shape
-    if tuple(v.shape[:2]) != (B, T):
-        raise ValueError("value batch and sequence dimensions must match query.")
     HV, V = v.shape[2], v.shape[3]
-    if tuple(gate.shape) != (B, T, HV, K):
-        raise ValueError("gate must have shape [B, S_local, num_v_heads, k_head_dim].")
-    if tuple(beta.shape) != (B, T, HV):
-        raise ValueError("beta must have shape [B, S_local, num_v_heads].")
+    expected = (("k", k.shape, (B, T, H, K)),
+                ("v (rows, tokens)", v.shape[:2], (B, T)),
+                ("gate", gate.shape, (B, T, HV, K)),
+                ("beta", beta.shape, (B, T, HV)))
+    for name, got, want in expected:
+        if tuple(got) != want:
+            raise ValueError("%s: shape %s does not fit q %s and v %s (expected %s)"
+                             % (name, tuple(got), tuple(q.shape), tuple(v.shape), want))
     if HV % H != 0:
-        raise ValueError("num_v_heads must be divisible by num_k_heads.")
-    if a_log.numel() != HV:
-        raise ValueError("a_log must contain %d elements, got %d." % (HV, a_log.numel()))
-    if dt_bias.numel() != HV * K:
-        raise ValueError("dt_bias must contain %d elements, got %d." % (HV * K, dt_bias.numel()))
+        raise ValueError("v has %d value heads, not a multiple of the %d key heads of q and k"
+                         % (HV, H))
+    for name, t, count in (("a_log", a_log, HV), ("dt_bias", dt_bias, HV * K)):
+        if not isinstance(t, torch.Tensor) or t.numel() != count:
+            got = t.numel() if isinstance(t, torch.Tensor) else type(t).__name__
+            raise ValueError("%s: expected %d values (%d value heads), got %s" % (name, count, HV, got))
     dt = q.dtype
     for name, t in (("q", q), ("k", k), ("v", v), ("gate", gate), ("beta", beta)):
         _dev(t, name, dtype=dt)
@@ -226,14 +232,13 @@ def _cu_args(cu_seqlens, cu_seqlens_host, T):
     if cu_seqlens.dim() != 1 or cu_seqlens.numel() < 1:
         raise ValueError("cu_seqlens must be a 1-D int32 tensor of N+1 offsets")
     N = cu_seqlens.numel() - 1
-    if cu_seqlens_host is False:   # caller vouches for the device offsets
+    if cu_seqlens_host is None or cu_seqlens_host is False:
+        # device offsets only: nothing waits for the GPU; the library sizes the
+        # launch from an upper bound of the chunk count and clamps the offsets
         return cu_seqlens, None, N, None
-    if cu_seqlens_host is None:
-        host = cu_seqlens.to("cpu")
-    else:
-        host = torch.as_tensor(cu_seqlens_host, dtype=torch.int32, device="cpu").contiguous()
-        if host.numel() != N + 1:
-            raise ValueError("cu_seqlens_host must hold the same N+1 offsets as cu_seqlens")
+    host = torch.as_tensor(cu_seqlens_host, dtype=torch.int32, device="cpu").contiguous()
+    if host.numel() != N + 1:
+        raise ValueError("cu_seqlens_host must hold the same N+1 offsets as cu_seqlens")
     return cu_seqlens, host, N, host.data_ptr()
 
 
@@ -265,8 +270,11 @@ def kda_fwd(q, k, v, gate, beta, a_log, dt_bias, *, scale=None, lower_bound=None
     on the GPU with B == 1; initial_state float32 [N,HV,K,V].
     ``lower_bound_form`` ("sigmoid" or "clamp") picks the form of the
     lower-bounded gate when lower_bound is given.  ``cu_seqlens_host`` may
-    carry a CPU copy of the offsets (otherwise one is made, which waits for the
-    GPU); pass ``False`` to skip the host-side check.  ``stage_events`` is an
+    carry a CPU copy of the offsets: they are then validated on the host and
+    the launch is sized exactly.  Without it (None, or False) nothing waits
+    for the GPU: the launch is sized from an upper bound of the chunk count
+    and the library clamps malformed device offsets into range (results are
+    then unspecified).  ``stage_events`` is an
     optional ctypes array of 2*NUM_STAGES hipEvent_t handles recorded around
     each stage (see kda_fwd_profiled in include/kda.h).
     """

@@ -181,7 +181,7 @@ def test_bwd_device_only_offsets_match_host_checked():
 def test_bwd_profiled_same_bits_and_stage_times():
     """kda_bwd_profiled does exactly kda_bwd's work: identical bits, and every
     stage's pair of events is recorded in order on the launch stream."""
-    import bench
+    from gated_delta_rule_43_amd.timing import StageEvents
     _banner("bwd profiled")
     inp = to_device(synthetic.random_problem(40, 1, 300, 2, 128, 128, dtype=torch.bfloat16,
                                              lengths=[100, 200], init_std=0.5))
@@ -190,7 +190,7 @@ def test_bwd_profiled_same_bits_and_stage_times():
             d_o, d_fin)
     kw = dict(cu_seqlens=inp["cu_seqlens"], initial_state=inp["initial_state"])
     a = kda.kda_bwd(*args, **kw)
-    ev = bench.StageEvents(1, kda.BWD_NUM_STAGES)
+    ev = StageEvents(1, kda.BWD_NUM_STAGES)
     b = kda.kda_bwd(*args, stage_events=ev.arrays[0], **kw)
     torch.cuda.synchronize()
     ms = ev.stage_ms()

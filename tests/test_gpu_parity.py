@@ -108,8 +108,8 @@ def test_varlen_without_host_copy_matches():
     inp = synthetic.random_problem(13, 1, sum(lengths), 2, 128, 128, dtype=torch.bfloat16,
                                    device=DEV, lengths=lengths)
     inp.update(scale=None, lower_bound=None, chunk_size=64)
-    o1, f1 = gpu_fwd(inp)
-    o2, f2 = gpu_fwd(inp, cu_seqlens_host=False)
+    o1, f1 = gpu_fwd(inp, cu_seqlens_host=inp["cu_seqlens"].cpu())
+    o2, f2 = gpu_fwd(inp)
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
 
 
@@ -155,7 +155,7 @@ def _expected_table(cu, C):
 def test_chunk_table_bit_exact(lengths, C, host):
     cu = synthetic.cu_from_lengths(lengths)
     cu_dev = torch.from_numpy(cu).to(DEV)
-    tok, ln, seq0 = kda.chunk_table(int(cu[-1]), C, cu_dev, cu_seqlens_host=None if host else False)
+    tok, ln, seq0 = kda.chunk_table(int(cu[-1]), C, cu_dev, cu_seqlens_host=cu if host else None)
     et, el, es = _expected_table(list(cu), C)
     assert tok.tolist() == et and ln.tolist() == el and seq0.tolist() == es
 
