@@ -99,18 +99,31 @@ kda_status validate_problem(const kda_problem* p, bool summary) {
   return validate_rows(p, summary);
 }
 
-// Which kernels run: the MFMA path for bf16 with 64-token chunks, the fp32
-// VALU path otherwise.  KDA_PATH=valu forces the VALU path (for comparisons).
-bool use_mfma(const kda_problem* p) {
+// Which kernels run.  fp32 inputs and chunk sizes 16 and 32: the VALU path.
+// bf16 with 64-token chunks: the matrix-core kernels, either fused (one
+// workgroup per (sequence, head) computes and consumes each chunk's factors
+// in LDS) or in two passes (all chunk-heads' factors in parallel as records in
+// the workspace, then the sequential state pass over them).  Summaries take
+// the two-pass kernels.  KDA_PATH=valu|mfma|fused forces a path where it
+// applies (for comparisons).
+enum Path { kPathValu = 0, kPathMfma = 1, kPathFused = 2 };
+
+int choose_path(const kda_problem* p, bool summary) {
+  const bool mfma_ok = p->dtype == KDA_BF16 && p->chunk_size == 64;
   const char* env = std::getenv("KDA_PATH");
-  if (env && std::strcmp(env, "valu") == 0) return false;
-  return p->dtype == KDA_BF16 && p->chunk_size == 64;
+  if (env && std::strcmp(env, "valu") == 0) return kPathValu;
+  if (!mfma_ok) return kPathValu;
+  if (env && std::strcmp(env, "mfma") == 0) return kPathMfma;
+  if (summary) return kPathMfma;
+  if (env && std::strcmp(env, "fused") == 0) return kPathFused;
+  return kPathMfma;
 }
 
 struct Layout {
   int NT = 0;
   int exact = 1;
-  bool mfma = false;
+  int path = kPathValu;
+  bool mfma = false;  // chunk records in the workspace (two-pass matrix-core path)
   size_t off_tok = 0, off_len = 0, off_seq0 = 0, off_nt = 0;
   size_t off_qn = 0, off_kn = 0, off_g = 0, off_bt = 0;
   size_t off_W = 0, off_U = 0, off_Qt = 0, off_Kb = 0, off_Aqk = 0, off_gL = 0;
@@ -134,10 +147,11 @@ int chunk_count(const kda_problem* p, int* exact) {
   return p->T / C + p->N;
 }
 
-Layout layout_for(const kda_problem* p, bool mfma) {
+Layout layout_for(const kda_problem* p, int path) {
   Layout L;
   L.NT = chunk_count(p, &L.exact);
-  L.mfma = mfma;
+  L.path = path;
+  L.mfma = path == kPathMfma;
   const size_t NT = (size_t)L.NT, H = value_heads(p), K = p->K, V = p->V, C = p->chunk_size, N = p->N;
   const size_t tokh = (size_t)p->B * p->T * H;
   size_t o = 0;
@@ -156,7 +170,7 @@ Layout layout_for(const kda_problem* p, bool mfma) {
     L.off_sink = take(kSinkBytes);
     L.off_xcount = take(4);
     L.off_xlist = take(NT * H * 4);
-  } else {
+  } else if (path == kPathValu) {
     L.off_qn = take(tokh * K * 4);
     L.off_kn = take(tokh * K * 4);
     L.off_g = take(tokh * K * 4);
@@ -173,7 +187,7 @@ Layout layout_for(const kda_problem* p, bool mfma) {
   return L;
 }
 
-Layout layout(const kda_problem* p) { return layout_for(p, use_mfma(p)); }
+Layout layout(const kda_problem* p, bool summary) { return layout_for(p, choose_path(p, summary)); }
 
 // The backward's workspace: the VALU forward's (recomputed factors) followed by
 // Akk and Tm, per-chunk states and their gradients, the per-value-head
@@ -188,7 +202,7 @@ struct BwdLayout {
 
 BwdLayout bwd_layout(const kda_problem* p) {
   BwdLayout B;
-  B.f = layout_for(p, false);
+  B.f = layout_for(p, kPathValu);
   const size_t NT = (size_t)B.f.NT, H = value_heads(p), K = p->K, V = p->V, C = p->chunk_size;
   const size_t tokh = (size_t)p->B * p->T * H;
   size_t o = B.f.total;
@@ -227,7 +241,9 @@ kda::FwdArgs make_args(const kda_problem* p, const Layout& L, void* ws) {
   a.chunk_len = (int32_t*)(w + L.off_len);
   a.seq_chunk0 = (int32_t*)(w + L.off_seq0);
   a.nt_dev = (int32_t*)(w + L.off_nt);
-  if (L.mfma) {
+  if (L.path == kPathFused) {
+    // the fused kernel needs the chunk table only
+  } else if (L.mfma) {
     a.rec = w + L.off_rec;
     a.sink = w + L.off_sink;
     a.exact_count = (int32_t*)(w + L.off_xcount);
@@ -250,6 +266,7 @@ kda::FwdArgs make_args(const kda_problem* p, const Layout& L, void* ws) {
 hipError_t launch(const kda::FwdArgs& a, const Layout& L, hipStream_t s) {
   hipError_t e = kda::launch_chunk_table(a, s);
   if (e != hipSuccess) return e;
+  if (L.path == kPathFused) return kda::launch_fused_path(a, s);
   return L.mfma ? kda::launch_mfma_path(a, s) : kda::launch_valu_path(a, s);
 }
 
@@ -333,7 +350,7 @@ kda_status fwd_impl(const kda_problem* p, const kda_short_conv* conv, const void
   if (initial_state && !aligned(initial_state, 4)) return fail(KDA_EINVAL, "initial_state misaligned");
   if (final_state && !aligned(final_state, 4)) return fail(KDA_EINVAL, "final_state misaligned");
   if (o && !aligned(o, p->dtype == KDA_BF16 ? 2 : 4)) return fail(KDA_EINVAL, "o misaligned");
-  const Layout L = layout(p);
+  const Layout L = layout(p, false);
   ConvBuffers cb;
   if (conv) {
     st = check_conv(p, conv, q, k, v);
@@ -342,7 +359,7 @@ kda_status fwd_impl(const kda_problem* p, const kda_short_conv* conv, const void
   }
   st = check_ws(conv ? cb.total : L.total, workspace, workspace_bytes);
   if (st != KDA_OK) return st;
-  if (L.mfma) {
+  if (L.path != kPathValu) {
     const void* vec[] = {q, k, v, gate, o};
     for (const void* ptr : vec)
       if (ptr && !aligned(ptr, 16))
@@ -389,13 +406,19 @@ kda_status kda_validate(const kda_problem* p) {
 size_t kda_fwd_workspace_size(const kda_problem* p, kda_status* status) {
   kda_status st = validate_problem(p, false);
   if (status) *status = st;
-  return st == KDA_OK ? layout(p).total : 0;
+  return st == KDA_OK ? layout(p, false).total : 0;
 }
 
 size_t kda_state_summary_workspace_size(const kda_problem* p, kda_status* status) {
   kda_status st = validate_problem(p, true);
   if (status) *status = st;
-  return st == KDA_OK ? layout(p).total : 0;
+  return st == KDA_OK ? layout(p, true).total : 0;
+}
+
+int32_t kda_fwd_path(const kda_problem* p) {
+  if (validate_problem(p, false) != KDA_OK) return -1;
+  g_last_error.clear();
+  return choose_path(p, false);
 }
 
 kda_status kda_fwd_profiled(const kda_problem* p, const void* q, const void* k, const void* v,
@@ -418,7 +441,7 @@ kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const voi
 size_t kda_fwd_short_conv_workspace_size(const kda_problem* p, kda_status* status) {
   kda_status st = validate_problem(p, false);
   if (status) *status = st;
-  return st == KDA_OK ? conv_buffers(p, layout(p).total).total : 0;
+  return st == KDA_OK ? conv_buffers(p, layout(p, false).total).total : 0;
 }
 
 kda_status kda_fwd_short_conv(const kda_problem* p, const kda_short_conv* conv, const void* q,
@@ -474,7 +497,7 @@ kda_status kda_state_summary(const kda_problem* p, const void* q, const void* k,
   if (st != KDA_OK) return st;
   if (!state_ext || !transition) return fail(KDA_EINVAL, "state_ext and transition must be non-NULL");
   if (!aligned(state_ext, 4) || !aligned(transition, 4)) return fail(KDA_EINVAL, "summary outputs misaligned");
-  const Layout L = layout(p);
+  const Layout L = layout(p, true);
   st = check_ws(L.total, workspace, workspace_bytes);
   if (st != KDA_OK) return st;
   if (L.mfma) {

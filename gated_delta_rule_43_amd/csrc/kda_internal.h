@@ -153,6 +153,7 @@ hipError_t launch_valu_path(const FwdArgs& a, hipStream_t s);
 hipError_t launch_valu_prep(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_mfma_path(const FwdArgs& a, hipStream_t s);
+hipError_t launch_fused_path(const FwdArgs& a, hipStream_t s);
 hipError_t launch_short_conv(const ConvArgs& a, hipStream_t s);
 hipError_t launch_gated_rms_norm(const NormArgs& a, hipStream_t s);
 size_t mfma_record_bytes(int K, int V);

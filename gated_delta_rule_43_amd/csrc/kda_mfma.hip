@@ -203,7 +203,7 @@ enum {
 // path on such blocks.  GATE: the gate form (FwdArgs::gate_form).
 template <int K, int V, bool EXACT, int GATE>
 __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, const int h,
-                                           const int tok0, const int L) {
+                                           const int tok0, const int L, char* const rec) {
   using R = Rec<K, V>;
   constexpr int NKJ = K / 32, NVJ = V / 32, NVT = V / 16, KL = K / 4;
   const int H = a.H;
@@ -214,7 +214,6 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
   const int64_t th = (int64_t)(tok0 + (valid ? row : 0)) * H + h;  // token-head index
   // the same token at the key head this value head reads (grouped value heads)
   const int64_t thk = (int64_t)(tok0 + (valid ? row : 0)) * a.HK + h / (H / a.HK);
-  char* rec = (char*)a.rec + ((int64_t)jchunk * H + h) * R::kBytes;
   // beta and a_log are issued with the row loads so that their latency is not
   // paid again after them
   const bf16 braw = ((const bf16*)a.beta)[th];
@@ -666,7 +665,8 @@ __global__ __launch_bounds__(kThreads, 3) void k_chunk_mfma(FwdArgs a) {
   const int tok0 = a.chunk_tok[jchunk], L = a.chunk_len[jchunk];
   asm volatile("" ::"s"(tok0), "s"(L));
   if (jchunk >= nt) return;
-  chunk_body<K, V, false, GATE>(a, jchunk, h, tok0, L);
+  chunk_body<K, V, false, GATE>(a, jchunk, h, tok0, L,
+                                (char*)a.rec + ((int64_t)jchunk * a.H + h) * Rec<K, V>::kBytes);
 }
 
 // Fix-up pass: recomputes the listed chunk-heads with the exact diagonal path.
@@ -676,8 +676,132 @@ __global__ __launch_bounds__(kThreads) void k_chunk_mfma_exact(FwdArgs a) {
   for (int i = blockIdx.x; i < count; i += gridDim.x) {
     const int ch = a.exact_list[i];
     const int jchunk = ch / a.H;
-    chunk_body<K, V, true, GATE>(a, jchunk, ch % a.H, a.chunk_tok[jchunk], a.chunk_len[jchunk]);
+    chunk_body<K, V, true, GATE>(a, jchunk, ch % a.H, a.chunk_tok[jchunk], a.chunk_len[jchunk],
+                                 (char*)a.rec + (int64_t)ch * Rec<K, V>::kBytes);
     __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Kernel F: the whole forward of one (sequence, head) in one workgroup.
+// ---------------------------------------------------------------------------
+// For each of the sequence's chunks in order, the four waves first compute the
+// chunk's factors exactly as k_chunk_mfma does, but into a record that stays
+// in LDS, and then consume it: wave w owns V/64 16-column tiles of the fp32
+// state (MFMA accumulators) and forms
+//   X = W S,  Delta = U - X,  O = Qt S + Aqk Delta,  S <- Diag(gL) S + Kbar^T Delta
+// with S and Delta as bf16 hi + lo pairs in the state's own products.  Nothing
+// but q, k, v, gate, beta, the states and o touches HBM.  Blocks whose decay
+// leaves the factorised range take the exact per-pair path in place.
+template <int K, int V, int GATE>
+__global__ __launch_bounds__(kThreads, 1) void k_fused(FwdArgs a) {
+  using R = Rec<K, V>;
+  constexpr int NKJ = K / 32, NKT = K / 16, NVT = V / 16;
+  constexpr int NCT = NVT / 4;  // column tiles per wave
+  static_assert(NCT >= 1 && NVT % 4 == 0, "four waves share the value columns");
+  const int H = a.H;
+  const int64_t nh = blockIdx.x;
+  if (nh >= (int64_t)a.N * H) return;
+  const int h = (int)(nh % H), seq = (int)(nh / H);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  __shared__ __attribute__((aligned(16))) char sRec[R::kBytes];
+  const int jc0 = a.seq_chunk0[seq], jc1 = a.seq_chunk0[seq + 1];
+  const int64_t sbase = ((int64_t)seq * H + h) * K * V;
+
+  f32x4 S[NKT][NCT];
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int col = 16 * (w * NCT + ct) + n;
+#pragma unroll
+    for (int at = 0; at < NKT; ++at)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        S[at][ct][e] = a.init ? a.init[sbase + (int64_t)(16 * at + 4 * g + e) * V + col] : 0.f;
+  }
+
+  const bf16x8* rQt = (const bf16x8*)(sRec + R::oQt);
+  const bf16x8* rW = (const bf16x8*)(sRec + R::oW);
+  const bf16x8* rKb = (const bf16x8*)(sRec + R::oKbar);
+  const float* rGL = (const float*)(sRec + R::oGL);
+  const bf16x8* rA = (const bf16x8*)(sRec + R::oAqk);
+  const uint2* rU = (const uint2*)(sRec + R::oU);
+  bf16* const o = (bf16*)a.o;
+
+  for (int jc = jc0; jc < jc1; ++jc) {
+    const int tok0 = a.chunk_tok[jc], L = a.chunk_len[jc];
+    chunk_body<K, V, true, GATE>(a, jc, h, tok0, L, sRec);
+    __syncthreads();
+    bf16x8 fA[4][2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      fA[t][0] = rA[(t * 2 + 0) * 64 + lane];
+      fA[t][1] = t >= 2 ? rA[(t * 2 + 1) * 64 + lane] : fA[t][0];
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int ctg = w * NCT + ct;
+      bf16x8 sb[NKJ], sl[NKJ];
+#pragma unroll
+      for (int j = 0; j < NKJ; ++j) split_frag(S[2 * j][ct], S[2 * j + 1][ct], sb[j], sl[j]);
+      f32x4 X[4], Y[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        X[t] = zero4();
+        Y[t] = zero4();
+#pragma unroll
+        for (int j = 0; j < NKJ; ++j) {
+          const bf16x8 fw = rW[(t * NKJ + j) * 64 + lane];
+          X[t] = mfma(fw, sb[j], X[t]);
+          X[t] = mfma(fw, sl[j], X[t]);
+          Y[t] = mfma(sb[j], rQt[(t * NKJ + j) * 64 + lane], Y[t]);
+        }
+      }
+      f32x4 D[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float u[4];
+        unpack4(rU[(t * NVT + ctg) * 64 + lane], u);
+        D[t] = f32x4{u[0], u[1], u[2], u[3]} - X[t];
+      }
+      bf16x8 db[2], dl[2];
+      split_frag(D[0], D[1], db[0], dl[0]);
+      split_frag(D[2], D[3], db[1], dl[1]);
+      // output rows 16t+n, columns 16ctg+4g..+3 (transposed tiles), rows
+      // past the chunk end are not stored
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        Y[t] = mfma(db[0], fA[t][0], Y[t]);
+        if (t >= 2) Y[t] = mfma(db[1], fA[t][1], Y[t]);
+        const int r = 16 * t + n;
+        if (r < L) *(uint2*)(o + ((int64_t)(tok0 + r) * H + h) * V + 16 * ctg + 4 * g) = pk4(Y[t]);
+      }
+#pragma unroll
+      for (int at = 0; at < NKT; ++at) {
+        const float4 gl = *(const float4*)&rGL[16 * at + 4 * g];
+        const bf16x8 fk0 = rKb[(at * 2 + 0) * 64 + lane], fk1 = rKb[(at * 2 + 1) * 64 + lane];
+        f32x4 acc = {gl.x * S[at][ct][0], gl.y * S[at][ct][1], gl.z * S[at][ct][2], gl.w * S[at][ct][3]};
+        acc = mfma(fk0, db[0], acc);
+        acc = mfma(fk1, db[1], acc);
+        acc = mfma(fk0, dl[0], acc);
+        acc = mfma(fk1, dl[1], acc);
+        S[at][ct] = acc;
+      }
+    }
+    // every wave is done with this chunk's record before the next overwrites it
+    __syncthreads();
+  }
+
+  if (a.fin) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int col = 16 * (w * NCT + ct) + n;
+#pragma unroll
+      for (int at = 0; at < NKT; ++at)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          a.fin[sbase + (int64_t)(16 * at + 4 * g + e) * V + col] = S[at][ct][e];
+    }
   }
 }
 
@@ -1068,7 +1192,35 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
   return hipSuccess;
 }
 
+template <int K, int V>
+hipError_t run_fused(const FwdArgs& a, hipStream_t s) {
+  // the chunk factors are folded into the fused kernel: their stage's events
+  // are recorded back to back
+  mark(a, kStagePrologue, 0, s);
+  mark(a, kStagePrologue, 1, s);
+  mark(a, kStageChunk, 0, s);
+  mark(a, kStageChunk, 1, s);
+  mark(a, kStageState, 0, s);
+  const int64_t wgs = (int64_t)a.N * a.H;
+  if (wgs > 0) {
+    const dim3 grid((unsigned)wgs), block(kThreads);
+    if (a.gate_form == 1) hipLaunchKernelGGL((k_fused<K, V, 1>), grid, block, 0, s, a);
+    else if (a.gate_form == 2) hipLaunchKernelGGL((k_fused<K, V, 2>), grid, block, 0, s, a);
+    else hipLaunchKernelGGL((k_fused<K, V, 0>), grid, block, 0, s, a);
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  }
+  mark(a, kStageState, 1, s);
+  return hipSuccess;
+}
+
 }  // namespace
+
+hipError_t launch_fused_path(const FwdArgs& a, hipStream_t s) {
+  if (a.K == 128 && a.V == 128) return run_fused<128, 128>(a, s);
+  if (a.K == 128 && a.V == 64) return run_fused<128, 64>(a, s);
+  if (a.K == 64 && a.V == 128) return run_fused<64, 128>(a, s);
+  return run_fused<64, 64>(a, s);
+}
 
 size_t mfma_record_bytes(int K, int V) {
   if (K == 128 && V == 128) return Rec<128, 128>::kBytes;

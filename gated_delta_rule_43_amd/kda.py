@@ -38,7 +38,7 @@ EXPORTED = ("kda_validate", "kda_fwd_workspace_size", "kda_fwd", "kda_fwd_profil
             "kda_apply_state_summary", "kda_chunk_capacity", "kda_chunk_table",
             "kda_short_conv_silu", "kda_fwd_short_conv_workspace_size", "kda_fwd_short_conv",
             "kda_bwd_workspace_size", "kda_bwd", "kda_bwd_profiled", "kda_gated_rms_norm",
-            "kda_last_error", "kda_version")
+            "kda_last_error", "kda_version", "kda_fwd_path")
 MAX_CONV_WIDTH = 4
 
 
@@ -111,6 +111,8 @@ def load_library(path: Optional[str] = None):
     lib.kda_gated_rms_norm.restype = ctypes.c_int
     lib.kda_last_error.argtypes = []
     lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_fwd_path.argtypes = [PP]
+    lib.kda_fwd_path.restype = I32
     lib.kda_version.argtypes = []
     lib.kda_version.restype = I32
     if path == LIB_PATH:
@@ -240,6 +242,21 @@ def _cu_args(cu_seqlens, cu_seqlens_host, T):
     if host.numel() != N + 1:
         raise ValueError("cu_seqlens_host must hold the same N+1 offsets as cu_seqlens")
     return cu_seqlens, host, N, host.data_ptr()
+
+
+PATH_NAMES = {0: "valu", 1: "mfma", 2: "fused"}
+
+
+def fwd_path(q_shape, V, dtype=torch.bfloat16, chunk_size=64, N=None, HV=0, cu_seqlens=False) -> str:
+    """Name of the kernel path kda_fwd takes for this problem: "valu",
+    "mfma" (two passes with workspace records) or "fused"."""
+    B, T, H, K = q_shape
+    p = make_problem(B, T, H, K, V, KDA_F32 if dtype == torch.float32 else KDA_BF16,
+                     chunk_size=chunk_size, N=N, cu_seqlens_ptr=1 if cu_seqlens else None, HV=HV)
+    r = load_library().kda_fwd_path(ctypes.byref(p))
+    if r < 0:
+        _raise(EINVAL, "kda_fwd_path")
+    return PATH_NAMES[r]
 
 
 def fwd_workspace_size(q_shape, V, dtype=torch.bfloat16, chunk_size=64, lower_bound=None,

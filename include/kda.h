@@ -149,6 +149,22 @@ kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const voi
                    float* final_state, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Which kernels kda_fwd runs for this problem (host only, launches nothing):
+ *   KDA_PATH_VALU   fp32 inputs or chunk sizes 16/32: vector-ALU kernels;
+ *   KDA_PATH_MFMA   bf16, chunk 64: all chunk-heads' factors in parallel into
+ *                   workspace records, then the sequential state pass;
+ *   KDA_PATH_FUSED  bf16, chunk 64: one workgroup per (sequence, head) that
+ *                   computes and consumes each chunk's factors in on-chip
+ *                   memory (no records in the workspace).
+ * Both matrix-core paths compute the same algebra; their results agree to
+ * rounding.  Returns -1 (message in kda_last_error) for an invalid problem.
+ */
+#define KDA_PATH_VALU 0
+#define KDA_PATH_MFMA 1
+#define KDA_PATH_FUSED 2
+int32_t kda_fwd_path(const kda_problem* p);
+
+/*
  * kda_fwd with per-stage timing hooks, for measurement.  It does exactly the
  * work of kda_fwd; in addition, when stage_events is not NULL it must hold
  * 2 * KDA_NUM_STAGES hipEvent_t handles created by the caller (entries may be
