@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "kda_internal.h"
@@ -336,12 +337,13 @@ kda_status check_conv(const kda_problem* p, const kda_short_conv* conv, const vo
   return KDA_OK;
 }
 
-// kda_fwd, optionally after the short convolution of q, k and v.
+// kda_fwd, optionally after the short convolution of q, k and v.  path < 0:
+// the library's choice; otherwise the path whose workspace the caller sized.
 kda_status fwd_impl(const kda_problem* p, const kda_short_conv* conv, const void* q, const void* k,
                     const void* v, const void* gate, const void* beta, const float* a_log,
                     const float* dt_bias, const float* initial_state, void* o,
                     float* final_state, void* workspace, size_t workspace_bytes, void* stream,
-                    void* const* stage_events) {
+                    void* const* stage_events, int path = -1) {
   kda_status st = validate_problem(p, false);
   if (st != KDA_OK) return st;
   st = check_inputs(p, q, k, v, gate, beta, a_log, dt_bias);
@@ -350,7 +352,7 @@ kda_status fwd_impl(const kda_problem* p, const kda_short_conv* conv, const void
   if (initial_state && !aligned(initial_state, 4)) return fail(KDA_EINVAL, "initial_state misaligned");
   if (final_state && !aligned(final_state, 4)) return fail(KDA_EINVAL, "final_state misaligned");
   if (o && !aligned(o, p->dtype == KDA_BF16 ? 2 : 4)) return fail(KDA_EINVAL, "o misaligned");
-  const Layout L = layout(p, false);
+  const Layout L = path < 0 ? layout(p, false) : layout_for(p, path);
   ConvBuffers cb;
   if (conv) {
     st = check_conv(p, conv, q, k, v);
@@ -394,6 +396,82 @@ kda_status fwd_impl(const kda_problem* p, const kda_short_conv* conv, const void
 }
 
 }  // namespace
+
+// ---------------------------------------------------------------------------
+// Allocation-free forward.  Its workspace is `scratch`, a device array of
+// kNoAllocScratchBytes that every GPU the library runs on holds until the
+// process ends.  In host code the array's name is only a stand-in: its device
+// address comes from hipGetSymbolAddress, once per device (with that device
+// current), and only that address is handed to kernels.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The scratch array's device address on the current device (looked up once).
+kda_status scratch_address(void* stream, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(KDA_EHIP, "no current HIP device (%s)", hipGetErrorString(e));
+  if (stream) {
+    int sdev = -1;
+    e = hipStreamGetDevice((hipStream_t)stream, &sdev);
+    if (e != hipSuccess) return fail(KDA_EHIP, "hipStreamGetDevice failed: %s", hipGetErrorString(e));
+    if (sdev != dev)
+      return fail(KDA_EINVAL, "the stream belongs to device %d but device %d is current", sdev, dev);
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(KDA_EHIP, "hipGetSymbolAddress of the scratch array failed on device %d: %s", dev,
+                  hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KDA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_fwd_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+kda_status kda_fwd_noalloc(const kda_problem* p, const void* q, const void* k, const void* v,
+                           const void* gate, const void* beta, const float* a_log,
+                           const float* dt_bias, const float* initial_state, void* o,
+                           float* final_state, void* stream) {
+  kda_status st = validate_problem(p, false);
+  if (st != KDA_OK) return st;
+  // the library's path when its workspace fits the scratch array, else the
+  // fused path, whose workspace is only the chunk table
+  int path = choose_path(p, false);
+  size_t need = layout_for(p, path).total;
+  if (need > kNoAllocScratchBytes && path == kPathMfma) {
+    path = kPathFused;
+    need = layout_for(p, path).total;
+  }
+  if (need > kNoAllocScratchBytes)
+    return fail(KDA_EWORKSPACE,
+                "this problem needs %zu bytes of workspace; the allocation-free entry point has "
+                "%zu (use kda_fwd with a caller-provided workspace)",
+                need, kNoAllocScratchBytes);
+  void* ws = nullptr;
+  st = scratch_address(stream, &ws);
+  if (st != KDA_OK) return st;
+  return fwd_impl(p, nullptr, q, k, v, gate, beta, a_log, dt_bias, initial_state, o, final_state,
+                  ws, kNoAllocScratchBytes, stream, nullptr, path);
+}
+
+}  // extern "C"
 
 extern "C" {
 

@@ -38,7 +38,8 @@ EXPORTED = ("kda_validate", "kda_fwd_workspace_size", "kda_fwd", "kda_fwd_profil
             "kda_apply_state_summary", "kda_chunk_capacity", "kda_chunk_table",
             "kda_short_conv_silu", "kda_fwd_short_conv_workspace_size", "kda_fwd_short_conv",
             "kda_bwd_workspace_size", "kda_bwd", "kda_bwd_profiled", "kda_gated_rms_norm",
-            "kda_last_error", "kda_version", "kda_fwd_path")
+            "kda_last_error", "kda_version", "kda_fwd_path", "kda_fwd_noalloc",
+            "kda_fwd_noalloc_scratch_bytes")
 MAX_CONV_WIDTH = 4
 
 
@@ -111,6 +112,10 @@ def load_library(path: Optional[str] = None):
     lib.kda_gated_rms_norm.restype = ctypes.c_int
     lib.kda_last_error.argtypes = []
     lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_fwd_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P]
+    lib.kda_fwd_noalloc.restype = ctypes.c_int
+    lib.kda_fwd_noalloc_scratch_bytes.argtypes = []
+    lib.kda_fwd_noalloc_scratch_bytes.restype = S
     lib.kda_fwd_path.argtypes = [PP]
     lib.kda_fwd_path.restype = I32
     lib.kda_version.argtypes = []
@@ -298,6 +303,39 @@ def kda_fwd(q, k, v, gate, beta, a_log, dt_bias, *, scale=None, lower_bound=None
     return _fwd(q, k, v, gate, beta, a_log, dt_bias, None, scale, lower_bound, chunk_size,
                 cu_seqlens, cu_seqlens_host, initial_state, output_final_state, out, workspace,
                 stage_events, lower_bound_form)
+
+
+def kda_fwd_noalloc(q, k, v, gate, beta, a_log, dt_bias, *, scale=None, lower_bound=None,
+                    chunk_size=64, cu_seqlens=None, cu_seqlens_host=None, initial_state=None,
+                    out=None, final_state_out=None, lower_bound_form="sigmoid"):
+    """kda_fwd through the allocation-free entry point (kda_fwd_noalloc).
+
+    The library allocates nothing; the caller passes the outputs: ``out``
+    (o, [B,T,HV,V], required) and ``final_state_out`` (float32 [N,HV,K,V] or
+    None).  Returns (out, final_state_out).  The library's device scratch
+    array is shared by every call on one GPU: calls that overlap on one GPU race."""
+    B, T, H, K, V, HV = _check_inputs(q, k, v, gate, beta, a_log, dt_bias)
+    cu, host, N, host_ptr = _cu_args(cu_seqlens, cu_seqlens_host, T)
+    if N is None:
+        N = B
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", dtype=torch.float32, shape=(N, HV, K, V))
+    if scale is not None and not scale > 0:
+        raise ValueError("scale must be positive, got %r" % (scale,))
+    if out is None:
+        raise ValueError("kda_fwd_noalloc needs the output tensor `out` (it allocates nothing)")
+    _dev(out, "out", dtype=q.dtype, shape=(B, T, HV, V))
+    if final_state_out is not None:
+        _dev(final_state_out, "final_state_out", dtype=torch.float32, shape=(N, HV, K, V))
+    p = make_problem(B, T, H, K, V, _dtype_code(q), scale, lower_bound, chunk_size, N,
+                     None if cu is None else cu.data_ptr(), host_ptr, lower_bound_form, HV)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = load_library().kda_fwd_noalloc(ctypes.byref(p), ptr(q), ptr(k), ptr(v), ptr(gate),
+                                        ptr(beta), ptr(a_log), ptr(dt_bias), ptr(initial_state),
+                                        ptr(out), ptr(final_state_out), _stream_ptr(q.device))
+    if st:
+        _raise(st, "kda_fwd_noalloc")
+    return out, final_state_out
 
 
 def kda_fwd_short_conv(q, k, v, gate, beta, a_log, dt_bias, conv_weights=None, conv_biases=None,

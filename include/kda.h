@@ -182,6 +182,28 @@ kda_status kda_fwd_profiled(const kda_problem* p, const void* q, const void* k, 
                             float* final_state, void* workspace, size_t workspace_bytes,
                             void* stream, void* const* stage_events);
 
+/*
+ * kda_fwd for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments and results as kda_fwd, without the workspace: the library uses a
+ * device array of kda_fwd_noalloc_scratch_bytes() (64 MiB) that it holds on
+ * every GPU it runs on until the process ends.  The entry point calls no
+ * hipMalloc, hipFree or other allocating routine.
+ *  - It runs kda_fwd's kernels: the path kda_fwd_path reports when that path's
+ *    workspace fits the array, otherwise the fused path (which needs only the
+ *    chunk table, about 8 bytes per chunk).  Problems whose workspace still
+ *    exceeds the array return KDA_EWORKSPACE.
+ *  - The stream must belong to the current device (KDA_EINVAL otherwise).
+ *  - Every call on one GPU shares that GPU's array: calls that overlap on one
+ *    GPU (concurrent streams, or threads) race and give undefined results.
+ *    Calls in one stream order are safe; each call rewrites what it reads.
+ */
+size_t kda_fwd_noalloc_scratch_bytes(void);
+kda_status kda_fwd_noalloc(const kda_problem* p, const void* q, const void* k, const void* v,
+                           const void* gate, const void* beta, const float* a_log,
+                           const float* dt_bias, const float* initial_state, void* o,
+                           float* final_state, void* stream);
+
 /* Workspace bytes for kda_state_summary. */
 size_t kda_state_summary_workspace_size(const kda_problem* p, kda_status* status);
 
