@@ -1133,6 +1133,277 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   }
 }
 
+// ---------------------------------------------------------------------------
+// Kernel B2: state pass with the key dimension split across waves.
+// ---------------------------------------------------------------------------
+// CT column tiles per workgroup, each shared by KS compute waves: wave
+// (tile, kq) holds rows [kq K/KS, (kq+1) K/KS) of that 16-column tile of the
+// fp32 state, so a chunk's dependent chain of matrix products per wave is KS
+// times shorter than with one wave per tile.  Per chunk:
+//   1. each wave forms its partial X_kq = W[:, rows] S[rows] (S as bf16 hi + lo)
+//      and puts it, and its rows of S (hi part), in LDS; barrier;
+//   2. every wave of the tile sums the KS partials in the same order (so all
+//      hold the same X), forms Delta = U - X (bf16 hi + lo), updates its rows
+//      S[rows] <- Diag(gL) S[rows] + Kbar[:, rows]^T Delta, and computes the
+//      output row tiles t = kq, kq + KS, ... as Qt S_hi + Aqk Delta_hi from
+//      the exchanged S rows.
+// One more wave streams W, Kbar^T and gL of each chunk into one of three LDS
+// stage buffers two chunks ahead; the compute waves read U, the Aqk and the
+// Qt fragments of their output rows straight into registers one chunk ahead.
+template <int K, int V, int CT, int KS, bool SUM>
+__global__ __launch_bounds__(64 * (CT * KS + 1)) void k_state_ks(FwdArgs a) {
+  using R = Rec<K, V>;
+  constexpr int CW = CT * KS;  // compute waves
+  constexpr int NKJ = K / 32, NKT = K / 16, NVT = V / 16;
+  constexpr int JW = NKJ / KS;  // k-steps (32 rows) per wave
+  constexpr int TW = NKT / KS;  // accumulator tiles (16 rows) per wave
+  constexpr int NTO = 4 / KS;   // output row tiles per wave
+  static_assert(JW >= 1 && NKJ % KS == 0 && 4 % KS == 0, "key split");
+  constexpr int ncols = SUM ? V + K : V;
+  constexpr int nct_total = ncols / 16;
+  static_assert(nct_total % CT == 0, "every workgroup owns whole column tiles");
+  constexpr int ntile_wg = nct_total / CT;
+  // the stage: W, Kbar^T and gL, contiguous in the record
+  constexpr int kStageOff = R::oW;
+  constexpr int kStageCopies = (R::kStage - kStageOff + 1023) / 1024;
+  static_assert(kStageOff + kStageCopies * 1024 <= R::kBytes, "stage inside the record");
+  constexpr int sW = R::oW - kStageOff, sKb = R::oKbar - kStageOff, sGLo = R::oGL - kStageOff;
+  const int H = a.H;
+  const int64_t bid = blockIdx.x;
+  const int xcd = (int)(bid % kXcds);
+  const int64_t q8 = bid / kXcds;
+  const int tileg = (int)(q8 % ntile_wg);
+  const int64_t nh = (q8 / ntile_wg) * kXcds + xcd;
+  if (nh >= (int64_t)a.N * H) return;
+  const int h = (int)(nh % H), seq = (int)(nh / H);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+  constexpr int kStageBytes = kStageCopies * 1024;
+  __shared__ __attribute__((aligned(16))) char sStage0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) char sStage1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) char sStage2[kStageBytes];
+  // exchange: each compute wave's partial X (4 row tiles) and its S rows (hi)
+  __shared__ f32x4 xX[CW][4][64];
+  __shared__ bf16x8 xS[CW][JW][64];
+  const int jc0 = a.seq_chunk0[seq], jc1 = a.seq_chunk0[seq + 1];
+  const char* recbase = (const char*)a.rec;
+
+  if (w == CW) {
+    // loader wave: as in k_state_mfma, but every chunk has two barriers
+    static_assert(kStageCopies < 64, "wait count field");
+    auto stage = [&](int jc, auto bufc) {
+      constexpr int B = decltype(bufc)::value;
+      char* const dst = B == 0 ? sStage0 : (B == 1 ? sStage1 : sStage2);
+      const char* rec = recbase + ((int64_t)jc * H + h) * R::kBytes + kStageOff;
+#pragma unroll
+      for (int i = 0; i < kStageCopies; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(rec + (lane + 64 * i) * 16),
+                                         (lds_void*)(&dst[(64 * i) * 16]), 16, 0, 0);
+    };
+    auto barrier_one_pending = [&]() { asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(kStageCopies) : "memory"); };
+    auto barrier_none_pending = [&]() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); };
+    auto mid_barrier = [&]() { asm volatile("s_barrier" ::: "memory"); };
+    auto step = [&](int jc, auto nbufc) {
+      mid_barrier();
+      if (jc + 2 < jc1) {
+        __builtin_amdgcn_s_sleep(2);
+        stage(jc + 2, nbufc);
+        barrier_one_pending();
+      } else {
+        barrier_none_pending();
+      }
+    };
+    if (jc0 < jc1) stage(jc0, std::integral_constant<int, 0>{});
+    if (jc0 + 1 < jc1) {
+      stage(jc0 + 1, std::integral_constant<int, 1>{});
+      barrier_one_pending();
+    } else {
+      barrier_none_pending();
+    }
+    for (int jc = jc0; jc < jc1; jc += 3) {
+      step(jc, std::integral_constant<int, 2>{});
+      if (jc + 1 < jc1) step(jc + 1, std::integral_constant<int, 0>{});
+      if (jc + 2 < jc1) step(jc + 2, std::integral_constant<int, 1>{});
+    }
+    __builtin_amdgcn_s_waitcnt(0);
+    return;
+  }
+
+  const int ct = w / KS, kq = w % KS;
+  const int ctg = tileg * CT + ct;
+  const int col = 16 * ctg + n;
+  const bool vcol = col < V;
+  const bool vt = !SUM || 16 * ctg < V;  // transition columns carry no values
+  const int ut = vt ? ctg : 0;
+  const int64_t sbase = ((int64_t)seq * H + h) * K * V;
+
+  // this wave's rows of S: accumulator tiles a = kq*TW .. kq*TW+TW-1
+  f32x4 S[TW];
+#pragma unroll
+  for (int i = 0; i < TW; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = 16 * (kq * TW + i) + 4 * g + e;
+      float sv = 0.f;
+      if (!SUM && a.init && vcol) sv = a.init[sbase + (int64_t)c * V + col];
+      if (SUM && !vcol) sv = (c == col - V) ? 1.f : 0.f;
+      S[i][e] = sv;
+    }
+
+  // operands read straight to registers one chunk ahead: U tile, and (output
+  // only) the Aqk and Qt fragments of this wave's output row tiles
+  uint2 ucur[4], unext[4];
+  bf16x8 aC[NTO][2], aN[NTO][2], qC[NTO][NKJ], qN[NTO][NKJ];
+  auto load_ops = [&](int jc, uint2 (&u)[4], bf16x8 (&aq)[NTO][2], bf16x8 (&qt)[NTO][NKJ]) {
+    const char* rec = recbase + ((int64_t)jc * H + h) * R::kBytes;
+    const uint2* ug = (const uint2*)(rec + R::oU);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const uint2 uu = ug[(t * NVT + ut) * 64 + lane];
+      u[t] = vt ? uu : make_uint2(0u, 0u);
+    }
+    if (!SUM) {
+      const bf16x8* ga = (const bf16x8*)(rec + R::oAqk);
+      const bf16x8* gq = (const bf16x8*)(rec + R::oQt);
+#pragma unroll
+      for (int i = 0; i < NTO; ++i) {
+        const int t = kq + KS * i;
+        aq[i][0] = ga[(t * 2 + 0) * 64 + lane];
+        aq[i][1] = ga[(t * 2 + 1) * 64 + lane];
+#pragma unroll
+        for (int j = 0; j < NKJ; ++j) qt[i][j] = gq[(t * NKJ + j) * 64 + lane];
+      }
+    }
+  };
+  int tok_cur = 0, len_cur = 0, tok_nxt = 0, len_nxt = 0;
+  if (jc0 < jc1) {
+    load_ops(jc0, ucur, aC, qC);
+    tok_cur = a.chunk_tok[jc0];
+    len_cur = a.chunk_len[jc0];
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  bf16* const o = (bf16*)a.o;
+
+  auto chunk_step = [&](int jc, auto bufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    const char* const cur = BUF == 0 ? sStage0 : (BUF == 1 ? sStage1 : sStage2);
+    const int jn = (jc + 1 < jc1) ? jc + 1 : jc;
+    load_ops(jn, unext, aN, qN);
+    tok_nxt = a.chunk_tok[jn];
+    len_nxt = a.chunk_len[jn];
+    const bf16x8* rW = (const bf16x8*)(cur + sW);
+    const bf16x8* rKb = (const bf16x8*)(cur + sKb);
+    const float* rGL = (const float*)(cur + sGLo);
+    // 1. partial X over this wave's rows; S rows (hi) to the exchange
+    bf16x8 sb[JW], sl[JW];
+#pragma unroll
+    for (int jj = 0; jj < JW; ++jj) {
+      split_frag(S[2 * jj], S[2 * jj + 1], sb[jj], sl[jj]);
+      if (!SUM) xS[w][jj][lane] = sb[jj];
+    }
+    f32x4 Xp[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      Xp[t] = zero4();
+#pragma unroll
+      for (int jj = 0; jj < JW; ++jj) {
+        const bf16x8 fw = rW[(t * NKJ + kq * JW + jj) * 64 + lane];
+        Xp[t] = mfma(fw, sb[jj], Xp[t]);
+        Xp[t] = mfma(fw, sl[jj], Xp[t]);
+      }
+      if (KS > 1) xX[w][t][lane] = Xp[t];
+    }
+    __syncthreads();
+    // 2. X summed over the tile's KS waves in rank order (the same in each)
+    f32x4 D[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      f32x4 X = KS > 1 ? xX[ct * KS][t][lane] : Xp[t];
+#pragma unroll
+      for (int r = 1; r < KS; ++r) X += xX[ct * KS + r][t][lane];
+      float u[4];
+      unpack4(ucur[t], u);
+      D[t] = f32x4{u[0], u[1], u[2], u[3]} - X;
+    }
+    bf16x8 db[2], dl[2];
+    split_frag(D[0], D[1], db[0], dl[0]);
+    split_frag(D[2], D[3], db[1], dl[1]);
+    // this wave's rows of S
+#pragma unroll
+    for (int i = 0; i < TW; ++i) {
+      const int at = kq * TW + i;
+      const float4 gl = *(const float4*)&rGL[16 * at + 4 * g];
+      const bf16x8 fk0 = rKb[(at * 2 + 0) * 64 + lane], fk1 = rKb[(at * 2 + 1) * 64 + lane];
+      f32x4 acc = {gl.x * S[i][0], gl.y * S[i][1], gl.z * S[i][2], gl.w * S[i][3]};
+      acc = mfma(fk0, db[0], acc);
+      acc = mfma(fk1, db[1], acc);
+      acc = mfma(fk0, dl[0], acc);
+      acc = mfma(fk1, dl[1], acc);
+      S[i] = acc;
+    }
+    // output row tiles t = kq + KS i: Yt = (Qt S_hi)^T + (Aqk Delta_hi)^T,
+    // lane (g, n) row 16t+n, columns 4g..4g+3; rows past the chunk end are
+    // not stored
+    if (!SUM) {
+#pragma unroll
+      for (int i = 0; i < NTO; ++i) {
+        const int t = kq + KS * i;
+        f32x4 Y = zero4();
+#pragma unroll
+        for (int j = 0; j < NKJ; ++j) {
+          const int src = ct * KS + j / JW;  // the wave holding k-step j
+          const bf16x8 sj = (j / JW == kq) ? sb[j % JW] : xS[src][j % JW][lane];
+          Y = mfma(sj, qC[i][j], Y);
+        }
+        Y = mfma(db[0], aC[i][0], Y);
+        if (t >= 2) Y = mfma(db[1], aC[i][1], Y);
+        const int r = 16 * t + n;
+        if (r < len_cur)
+          *(uint2*)(o + ((int64_t)(tok_cur + r) * H + h) * V + 16 * ctg + 4 * g) = pk4(Y);
+      }
+    }
+    // the next record's stage has landed and every wave is done with this
+    // chunk's stage and exchange
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) ucur[t] = unext[t];
+    if (!SUM) {
+#pragma unroll
+      for (int i = 0; i < NTO; ++i) {
+        aC[i][0] = aN[i][0];
+        aC[i][1] = aN[i][1];
+#pragma unroll
+        for (int j = 0; j < NKJ; ++j) qC[i][j] = qN[i][j];
+      }
+    }
+    tok_cur = tok_nxt;
+    len_cur = len_nxt;
+  };
+  for (int jc = jc0; jc < jc1; jc += 3) {
+    chunk_step(jc, std::integral_constant<int, 0>{});
+    if (jc + 1 < jc1) chunk_step(jc + 1, std::integral_constant<int, 1>{});
+    if (jc + 2 < jc1) chunk_step(jc + 2, std::integral_constant<int, 2>{});
+  }
+
+#pragma unroll
+  for (int i = 0; i < TW; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = 16 * (kq * TW + i) + 4 * g + e;
+      const float sv = S[i][e];
+      if (!SUM) {
+        if (a.fin) a.fin[sbase + (int64_t)c * V + col] = sv;
+      } else if (col < V) {
+        a.state_ext[sbase + (int64_t)c * V + col] = sv;
+      } else {
+        a.transition[((int64_t)seq * H + h) * K * K + (int64_t)c * K + (col - V)] = sv;
+      }
+    }
+}
+
 // compute units of the current device (cached per device)
 inline int device_cus() {
   static int cache[64] = {0};
@@ -1175,8 +1446,26 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
   const int cus = device_cus();
   int cw = 4;
   while (cw > 1 && heads * (ncols / 16 / cw) < cus) cw /= 2;
-  const int64_t wgs = heads * (ncols / 16 / cw);
-  if (wgs > 0 && (a.summary || a.fin || a.NT > 0)) {
+  int64_t wgs = heads * (ncols / 16 / cw);
+  // key split: when even one 16-column tile per workgroup leaves CUs idle,
+  // the chains are few and long and each chunk's latency bounds the pass;
+  // then KS waves share each tile's rows
+  int ks = (cw == 1 && heads * (ncols / 16) <= cus && K == 128) ? 4 : 1;
+  if (const char* env = std::getenv("KDA_STATE_KS")) ks = std::atoi(env);
+  if (ks != 1 && ks != 2 && ks != 4) ks = 1;
+  if (K == 64 && ks == 4) ks = 2;
+  if (ks > 1 && wgs > 0 && (a.summary || a.fin || a.NT > 0)) {
+    wgs = heads * (ncols / 16);
+    const dim3 grid((unsigned)wgs), block(64 * (ks + 1));
+    auto launch_ks = [&](auto ksc) {
+      constexpr int KSc = decltype(ksc)::value;
+      if (a.summary) hipLaunchKernelGGL((k_state_ks<K, V, 1, KSc, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((k_state_ks<K, V, 1, KSc, false>), grid, block, 0, s, a);
+    };
+    if (ks == 4) launch_ks(std::integral_constant<int, (K == 128 ? 4 : 2)>{});
+    else launch_ks(std::integral_constant<int, 2>{});
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  } else if (wgs > 0 && (a.summary || a.fin || a.NT > 0)) {
     const dim3 grid((unsigned)wgs), block(64 * (cw + 1));
     auto launch_cw = [&](auto cwc) {
       constexpr int CW = decltype(cwc)::value;

@@ -40,13 +40,19 @@ def test_fused_matches_two_pass_bitwise_and_oracle(case, monkeypatch):
     print("[gpu-test] fused path " + case[0], flush=True)
     inp = _problem(case, 500 + CASES.index(case))
     monkeypatch.setenv("KDA_PATH", "mfma")
-    o2, f2 = gpu_fwd(inp)
+    o3, f3 = gpu_fwd(inp)           # the launcher's own choice of state pass
+    monkeypatch.setenv("KDA_STATE_KS", "1")
+    o2, f2 = gpu_fwd(inp)           # one wave per column tile, as the fused kernel
+    monkeypatch.delenv("KDA_STATE_KS")
     monkeypatch.setenv("KDA_PATH", "fused")
     B, T, H, K = inp["q"].shape
     assert kda.fwd_path((B, T, H, K), inp["v"].shape[-1]) == "fused"
     o1, f1 = gpu_fwd(inp)
     assert torch.equal(o1, o2), "fused vs two-pass output differs"
     assert torch.equal(f1, f2), "fused vs two-pass final state differs"
+    # a key-split state pass sums the partial products in another order
+    assert_close(to_np(o3), to_np(o1), torch.bfloat16, "o, two-pass state pass of the launcher's choice")
+    assert float((f3 - f1).abs().max()) <= 1e-4
     if case[-1] is None:
         o_ref, f_ref = oracle_fwd(inp)
         assert_close(to_np(o1), o_ref, torch.bfloat16, "o")
@@ -69,5 +75,6 @@ def test_fused_extreme_gates(monkeypatch):
     assert_close(to_np(o1), o_ref, torch.bfloat16, "o")
     assert_close(to_np(f1), f_ref, torch.bfloat16, "final_state")
     monkeypatch.setenv("KDA_PATH", "mfma")
+    monkeypatch.setenv("KDA_STATE_KS", "1")
     o2, f2 = gpu_fwd(inp)
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
