@@ -1404,6 +1404,131 @@ __global__ __launch_bounds__(64 * (CT * KS + 1)) void k_state_ks(FwdArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// Kernel B3: state pass for short sequences.
+// ---------------------------------------------------------------------------
+// With many sequences of a few chunks each (documents shorter than a few
+// chunks), the staged pass above spends most of a workgroup's life filling its
+// pipeline.  Here one workgroup of four waves takes one (sequence, head); wave
+// w owns V/64 16-column tiles of the state and reads each chunk's fragments
+// straight from the record into registers (no LDS, no loader wave), so many
+// workgroups share a CU and hide each other's memory latency.  While the
+// state is still zero (the sequence's first chunk without an initial state)
+// the products with S are skipped: Delta = U, O = Aqk U, S = Kbar^T U.
+template <int K, int V>
+__global__ __launch_bounds__(256) void k_state_light(FwdArgs a) {
+  using R = Rec<K, V>;
+  constexpr int NKJ = K / 32, NKT = K / 16, NVT = V / 16;
+  constexpr int NCT = NVT / 4;
+  static_assert(NCT >= 1 && NVT % 4 == 0, "four waves share the value columns");
+  const int H = a.H;
+  const int64_t nh = blockIdx.x;
+  if (nh >= (int64_t)a.N * H) return;
+  const int h = (int)(nh % H), seq = (int)(nh / H);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int jc0 = a.seq_chunk0[seq], jc1 = a.seq_chunk0[seq + 1];
+  const int64_t sbase = ((int64_t)seq * H + h) * K * V;
+  const char* recbase = (const char*)a.rec;
+  bf16* const o = (bf16*)a.o;
+
+  f32x4 S[NKT][NCT];
+  bool zero = a.init == nullptr;  // S is exactly zero (wave-uniform)
+#pragma unroll
+  for (int ct = 0; ct < NCT; ++ct) {
+    const int col = 16 * (w * NCT + ct) + n;
+#pragma unroll
+    for (int at = 0; at < NKT; ++at)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        S[at][ct][e] = zero ? 0.f : a.init[sbase + (int64_t)(16 * at + 4 * g + e) * V + col];
+  }
+
+  for (int jc = jc0; jc < jc1; ++jc) {
+    const int tok0 = a.chunk_tok[jc], L = a.chunk_len[jc];
+    const char* rec = recbase + ((int64_t)jc * H + h) * R::kBytes;
+    const bf16x8* gW = (const bf16x8*)(rec + R::oW);
+    const bf16x8* gQ = (const bf16x8*)(rec + R::oQt);
+    const bf16x8* gK = (const bf16x8*)(rec + R::oKbar);
+    const float* gG = (const float*)(rec + R::oGL);
+    const bf16x8* gA = (const bf16x8*)(rec + R::oAqk);
+    const uint2* gU = (const uint2*)(rec + R::oU);
+    bf16x8 fA[4][2];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      fA[t][0] = gA[(t * 2 + 0) * 64 + lane];
+      fA[t][1] = gA[(t * 2 + 1) * 64 + lane];
+    }
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int ctg = w * NCT + ct;
+      f32x4 D[4], Y[4];
+      uint2 uraw[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) uraw[t] = gU[(t * NVT + ctg) * 64 + lane];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float u[4];
+        unpack4(uraw[t], u);
+        D[t] = f32x4{u[0], u[1], u[2], u[3]};
+        Y[t] = zero4();
+      }
+      if (!zero) {
+        bf16x8 sb[NKJ], sl[NKJ];
+#pragma unroll
+        for (int j = 0; j < NKJ; ++j) split_frag(S[2 * j][ct], S[2 * j + 1][ct], sb[j], sl[j]);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          f32x4 X = zero4();
+#pragma unroll
+          for (int j = 0; j < NKJ; ++j) {
+            const bf16x8 fw = gW[(t * NKJ + j) * 64 + lane];
+            X = mfma(fw, sb[j], X);
+            X = mfma(fw, sl[j], X);
+            Y[t] = mfma(sb[j], gQ[(t * NKJ + j) * 64 + lane], Y[t]);
+          }
+          D[t] -= X;
+        }
+      }
+      bf16x8 db[2], dl[2];
+      split_frag(D[0], D[1], db[0], dl[0]);
+      split_frag(D[2], D[3], db[1], dl[1]);
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        Y[t] = mfma(db[0], fA[t][0], Y[t]);
+        if (t >= 2) Y[t] = mfma(db[1], fA[t][1], Y[t]);
+        const int r = 16 * t + n;
+        if (r < L) *(uint2*)(o + ((int64_t)(tok0 + r) * H + h) * V + 16 * ctg + 4 * g) = pk4(Y[t]);
+      }
+#pragma unroll
+      for (int at = 0; at < NKT; ++at) {
+        const float4 gl = *(const float4*)&gG[16 * at + 4 * g];
+        const bf16x8 fk0 = gK[(at * 2 + 0) * 64 + lane], fk1 = gK[(at * 2 + 1) * 64 + lane];
+        f32x4 acc = zero4();
+        if (!zero) acc = f32x4{gl.x * S[at][ct][0], gl.y * S[at][ct][1], gl.z * S[at][ct][2], gl.w * S[at][ct][3]};
+        acc = mfma(fk0, db[0], acc);
+        acc = mfma(fk1, db[1], acc);
+        acc = mfma(fk0, dl[0], acc);
+        acc = mfma(fk1, dl[1], acc);
+        S[at][ct] = acc;
+      }
+    }
+    zero = false;
+  }
+
+  if (a.fin) {
+#pragma unroll
+    for (int ct = 0; ct < NCT; ++ct) {
+      const int col = 16 * (w * NCT + ct) + n;
+#pragma unroll
+      for (int at = 0; at < NKT; ++at)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          a.fin[sbase + (int64_t)(16 * at + 4 * g + e) * V + col] = S[at][ct][e];
+    }
+  }
+}
+
 // compute units of the current device (cached per device)
 inline int device_cus() {
   static int cache[64] = {0};
@@ -1447,6 +1572,18 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
   int cw = 4;
   while (cw > 1 && heads * (ncols / 16 / cw) < cus) cw /= 2;
   int64_t wgs = heads * (ncols / 16 / cw);
+  // many short sequences (at most four chunks each on average): the light pass
+  bool light = !a.summary && (int64_t)a.NT <= 4 * (int64_t)a.N;
+  if (const char* env = std::getenv("KDA_STATE_LIGHT")) light = !a.summary && std::atoi(env) != 0;
+  if (light) {
+    const int64_t nwg = (int64_t)a.N * a.H;
+    if (nwg > 0) {
+      hipLaunchKernelGGL((k_state_light<K, V>), dim3((unsigned)nwg), dim3(256), 0, s, a);
+      if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
+    mark(a, kStageState, 1, s);
+    return hipSuccess;
+  }
   // key split: when even one 16-column tile per workgroup leaves CUs idle,
   // the chains are few and long and each chunk's latency bounds the pass;
   // then KS waves share each tile's rows
