@@ -125,7 +125,7 @@ struct Layout {
   int exact = 1;
   int path = kPathValu;
   bool mfma = false;  // chunk records in the workspace (two-pass matrix-core path)
-  size_t off_tok = 0, off_len = 0, off_seq0 = 0, off_nt = 0;
+  size_t off_tok = 0, off_len = 0, off_seq0 = 0, off_nt = 0, off_cseq = 0, off_done = 0;
   size_t off_qn = 0, off_kn = 0, off_g = 0, off_bt = 0;
   size_t off_W = 0, off_U = 0, off_Qt = 0, off_Kb = 0, off_Aqk = 0, off_gL = 0;
   size_t off_rec = 0, off_sink = 0, off_xcount = 0, off_xlist = 0;
@@ -165,12 +165,14 @@ Layout layout_for(const kda_problem* p, int path) {
   L.off_len = take(NT * 4);
   L.off_seq0 = take((N + 1) * 4);
   L.off_nt = take(4);
+  L.off_cseq = take(NT * 4);
   if (L.mfma) {
     // one record of MFMA-ready chunk factors per chunk-head
     L.off_rec = take(NT * H * kda::mfma_record_bytes(p->K, p->V));
     L.off_sink = take(kSinkBytes);
     L.off_xcount = take(4);
     L.off_xlist = take(NT * H * 4);
+    L.off_done = take(NT * H * 4);
   } else if (path == kPathValu) {
     L.off_qn = take(tokh * K * 4);
     L.off_kn = take(tokh * K * 4);
@@ -242,6 +244,7 @@ kda::FwdArgs make_args(const kda_problem* p, const Layout& L, void* ws) {
   a.chunk_len = (int32_t*)(w + L.off_len);
   a.seq_chunk0 = (int32_t*)(w + L.off_seq0);
   a.nt_dev = (int32_t*)(w + L.off_nt);
+  a.chunk_seq = (int32_t*)(w + L.off_cseq);
   if (L.path == kPathFused) {
     // the fused kernel needs the chunk table only
   } else if (L.mfma) {
@@ -249,6 +252,7 @@ kda::FwdArgs make_args(const kda_problem* p, const Layout& L, void* ws) {
     a.sink = w + L.off_sink;
     a.exact_count = (int32_t*)(w + L.off_xcount);
     a.exact_list = (int32_t*)(w + L.off_xlist);
+    a.done = (int32_t*)(w + L.off_done);
   } else {
     a.qn = (float*)(w + L.off_qn);
     a.kn = (float*)(w + L.off_kn);

@@ -61,6 +61,7 @@ struct FwdArgs {
   int32_t* chunk_len;  // [NT] tokens in the chunk (1..C)
   int32_t* seq_chunk0; // [N+1] first chunk of each sequence
   int32_t* nt_dev;     // [1] actual number of chunks
+  int32_t* chunk_seq;  // [NT] sequence (row or document) of each chunk
   // workspace: per-token prologue results (VALU path)
   float *qn, *kn, *g, *bt;
   // workspace: per chunk-head factors, element type ws_dtype
@@ -76,6 +77,9 @@ struct FwdArgs {
   void* sink;
   int32_t* exact_count;  // [1] chunk-heads listed for the exact fix-up pass
   int32_t* exact_list;   // [NT*H]
+  // [NT*H] written by the chunk-factor kernel for every chunk-head: 1 when it
+  // finished the chunk's sequence itself (a one-chunk sequence), 0 otherwise
+  int32_t* done;
   // optional stage timing: hipEvent_t handles, [2 * kNumStages], entries may be null
   void* const* events;
 };

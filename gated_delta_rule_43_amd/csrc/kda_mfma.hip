@@ -203,7 +203,8 @@ enum {
 // path on such blocks.  GATE: the gate form (FwdArgs::gate_form).
 template <int K, int V, bool EXACT, int GATE>
 __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, const int h,
-                                           const int tok0, const int L, char* const rec) {
+                                           const int tok0, const int L, char* const rec,
+                                           const bool keep_ok = false) {
   using R = Rec<K, V>;
   constexpr int NKJ = K / 32, NVJ = V / 32, NVT = V / 16, KL = K / 4;
   const int H = a.H;
@@ -320,10 +321,40 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
     out[4] = hi.x; out[5] = hi.y; out[6] = hi.z; out[7] = hi.w;
   };
 
+  // ---- the block totals decide the exact diagonal path ----
+  float negmax = 0.f;
+#pragma unroll
+  for (int j = 0; j < NKJ; ++j) {
+    float lt[8];
+    fac8(kF_LAM + w, j, lt);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) negmax = fmaxf(negmax, -lt[e]);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) negmax = fmaxf(negmax, __shfl_xor(negmax, off));
+  const bool exact_diag = EXACT && negmax > kDiagSafe;  // wave-uniform
+  // keep: a sequence of this one chunk, starting from a zero state, is
+  // finished here (keep_ok), unless the chunk-head needs the exact fix-up.
+  // Then nothing goes to the record: Kbar^T fragments go to sX (whose W
+  // operands are not needed), U to sU1, the Aqk fragments stay in registers.
+  bool keep = false;
+  if (!EXACT) {
+    __shared__ int sNeedExact;
+    if (tid == 0) sNeedExact = 0;
+    __syncthreads();
+    if (negmax > kDiagSafe && lane == 0) sNeedExact = 1;
+    __syncthreads();
+    const bool need = sNeedExact != 0;
+    if (tid == 0 && need) {
+      const int slot = atomicAdd(a.exact_count, 1);
+      a.exact_list[slot] = jchunk * H + h;  // slot < NT*H: each chunk-head appends once
+    }
+    keep = keep_ok && !need;
+  }
+
   // ---- 4. per-element factors; fragments to LDS and to the record ----
   const bf16x8 sel0 = select_frag(g, n, 0), sel1 = select_frag(g, n, 1);
   bf16x8 qrow[NKJ], krow[NKJ], kdiag[NKJ];
-  float negmax = 0.f;
   {
     const float scale = a.scale;
 #pragma unroll
@@ -339,7 +370,6 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
         const float l = lam[8 * j + e];
         const float ef = fexp(l);            // e^{gamma_r - Gam_w}
         const float F = fexp(lt[e] - l);     // e^{Gam_{w+1} - gamma_r}
-        negmax = fmaxf(negmax, -lt[e]);
         fqr[e] = qv[8 * j + e] * ef;
         fk[e] = kv[8 * j + e] * ef;
         fq[e] = scale * fqr[e] * eg[e];
@@ -353,8 +383,10 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
       kdiag[j] = pack8(fkd);
       // keep the packed fragments (not their fp32 sources) live into step 5
       asm volatile("" : "+v"(qrow[j]), "+v"(krow[j]), "+v"(kdiag[j]));
-      ((bf16x8*)(rec + R::oQt))[(w * NKJ + j) * 64 + lane] = pack8(fq);
-      sX[w][j][lane] = pack8(fx);
+      if (!keep) {
+        ((bf16x8*)(rec + R::oQt))[(w * NKJ + j) * 64 + lane] = pack8(fq);
+        sX[w][j][lane] = pack8(fx);
+      }
       sKb[w][j][lane] = pack8(fkb);
       // Kbar^T fragments (a, w/2): this block's rows transposed on the matrix
       // cores, written as the (w%2) half of each lane's 16 bytes
@@ -365,28 +397,16 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
           const f32x4 d = mfma(kb8, a2 ? sel1 : sel0, zero4());
           const uint2 u = pk4(d);
           const int at = 2 * j + a2;
-          *(uint2*)(rec + R::oKbar + ((at * 2 + (w >> 1)) * 64 + lane) * 16 + 8 * (w & 1)) = u;
+          const int off = ((at * 2 + (w >> 1)) * 64 + lane) * 16 + 8 * (w & 1);
+          if (keep) *(uint2*)((char*)&sX[0][0][0] + off) = u;
+          else *(uint2*)(rec + R::oKbar + off) = u;
         }
       }
     }
   }
-  for (int c = tid; c < K; c += kThreads) ((float*)(rec + R::oGL))[c] = sFac[kF_GL][c];
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) negmax = fmaxf(negmax, __shfl_xor(negmax, off));
-  const bool exact_diag = EXACT && negmax > kDiagSafe;  // wave-uniform
-  if (!EXACT) {
-    __shared__ int sNeedExact;
-    if (tid == 0) sNeedExact = 0;
-    __syncthreads();
-    if (negmax > kDiagSafe && lane == 0) sNeedExact = 1;
-    __syncthreads();
-    if (tid == 0 && sNeedExact) {
-      const int slot = atomicAdd(a.exact_count, 1);
-      a.exact_list[slot] = jchunk * H + h;  // slot < NT*H: each chunk-head appends once
-    }
-  } else {
-    __syncthreads();
-  }
+  if (!keep)
+    for (int c = tid; c < K; c += kThreads) ((float*)(rec + R::oGL))[c] = sFac[kF_GL][c];
+  __syncthreads();
 
   // ---- 5. decayed key/query products, blocks (I <= R = w), transposed tiles ----
   f32x4 dq[4], dk[4];
@@ -453,6 +473,7 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
   // masks: Akk strictly lower -> LDS (bf16, row r = 16w+n; the diagonal block
   // also in fp32 after the barrier), Aqk lower incl. diagonal -> record
   float4 dgv;
+  bf16x8 fA0, fA1;  // this row block's Aqk fragments (kept for a finished sequence)
   {
     const int r = 16 * w + n;
 #pragma unroll
@@ -467,9 +488,13 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
       *(uint2*)&sA[r][16 * I + 4 * g] = pk4(vv[0], vv[1], vv[2], vv[3]);
       if (I == w) dgv = make_float4(vv[0], vv[1], vv[2], vv[3]);
     }
-    bf16x8* aq = (bf16x8*)(rec + R::oAqk);
-    aq[(w * 2 + 0) * 64 + lane] = pair_frag(dq[0], dq[1]);
-    aq[(w * 2 + 1) * 64 + lane] = pair_frag(dq[2], dq[3]);
+    fA0 = pair_frag(dq[0], dq[1]);
+    fA1 = pair_frag(dq[2], dq[3]);
+    if (!keep) {
+      bf16x8* aq = (bf16x8*)(rec + R::oAqk);
+      aq[(w * 2 + 0) * 64 + lane] = fA0;
+      aq[(w * 2 + 1) * 64 + lane] = fA1;
+    }
   }
   __syncthreads();
 
@@ -593,8 +618,11 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
       float f[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
       tfrag[t][j] = pack8(f);
     }
+  // a finished sequence puts U where Tm was (sU1): every wave has read Tm first
+  if (keep) __syncthreads();
   for (int job = w; job < NJOBS; job += 4) {
     if (job < NKJ) {
+      if (keep) continue;  // W multiplies the state, which is zero here
       const int p = job;
       f32x4 did[4][2];
 #pragma unroll
@@ -649,9 +677,53 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
         for (int a2 = 0; a2 < 2; ++a2) {
           f32x4 acc = mfma(tfrag[t][0], vb[0][a2], zero4());
           if (t >= 2) acc = mfma(tfrag[t][1], vb[1][a2], acc);
-          uout[(t * NVT + 2 * p + a2) * 64 + lane] = pk4(acc);
+          const int at = (t * NVT + 2 * p + a2) * 64 + lane;
+          if (keep) ((uint2*)sU1)[at] = pk4(acc);
+          else uout[at] = pk4(acc);
         }
     }
+  }
+
+  // ---- 8. a one-chunk sequence from a zero state, finished here ----
+  // Delta = U, O = Aqk U (wave w: output row tile w of every column tile),
+  // final state S = Kbar^T U (wave w: key row tiles w, w+4, ...).  The same
+  // products, in the same order, as the state pass for such a chunk.
+  if (!EXACT) {
+    if (keep) {
+      __syncthreads();
+      const int seq = a.chunk_seq[jchunk];
+      const int64_t sbase = ((int64_t)seq * H + h) * K * V;
+      const uint2* sUk = (const uint2*)sU1;
+      const bf16x8* sKk = (const bf16x8*)&sX[0][0][0];
+      bf16* const o = (bf16*)a.o;
+#pragma unroll
+      for (int ct = 0; ct < NVT; ++ct) {
+        f32x4 D[4];
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          float u[4];
+          unpack4(sUk[(t * NVT + ct) * 64 + lane], u);
+          D[t] = f32x4{u[0], u[1], u[2], u[3]};
+        }
+        const bf16x8 db0 = pair_frag(D[0], D[1]), db1 = pair_frag(D[2], D[3]);
+        f32x4 Y = mfma(db0, fA0, zero4());
+        if (w >= 2) Y = mfma(db1, fA1, Y);
+        const int r = 16 * w + n;
+        if (r < L) *(uint2*)(o + ((int64_t)(tok0 + r) * H + h) * V + 16 * ct + 4 * g) = pk4(Y);
+        if (a.fin) {
+#pragma unroll
+          for (int at = w; at < K / 16; at += 4) {
+            const bf16x8 fk0 = sKk[(at * 2 + 0) * 64 + lane], fk1 = sKk[(at * 2 + 1) * 64 + lane];
+            f32x4 acc = mfma(fk0, db0, zero4());
+            acc = mfma(fk1, db1, acc);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              a.fin[sbase + (int64_t)(16 * at + 4 * g + e) * V + 16 * ct + n] = acc[e];
+          }
+        }
+      }
+    }
+    if (tid == 0) a.done[jchunk * H + h] = keep ? 1 : 0;
   }
 }
 
@@ -665,8 +737,13 @@ __global__ __launch_bounds__(kThreads, 3) void k_chunk_mfma(FwdArgs a) {
   const int tok0 = a.chunk_tok[jchunk], L = a.chunk_len[jchunk];
   asm volatile("" ::"s"(tok0), "s"(L));
   if (jchunk >= nt) return;
+  // a sequence of this one chunk that starts from a zero state is finished here
+  const int sq = a.chunk_seq[jchunk];
+  const bool keep_ok = !a.summary && a.init == nullptr &&
+                       a.seq_chunk0[sq + 1] - a.seq_chunk0[sq] == 1;
   chunk_body<K, V, false, GATE>(a, jchunk, h, tok0, L,
-                                (char*)a.rec + ((int64_t)jchunk * a.H + h) * Rec<K, V>::kBytes);
+                                (char*)a.rec + ((int64_t)jchunk * a.H + h) * Rec<K, V>::kBytes,
+                                keep_ok);
 }
 
 // Fix-up pass: recomputes the listed chunk-heads with the exact diagonal path.
@@ -847,6 +924,8 @@ __global__ __launch_bounds__(320) __attribute__((amdgpu_waves_per_eu(2, 2))) voi
   __shared__ __attribute__((aligned(16))) char sStage1[kStageBytes];
   __shared__ __attribute__((aligned(16))) char sStage2[kStageBytes];
   const int jc0 = a.seq_chunk0[seq], jc1 = a.seq_chunk0[seq + 1];
+  // a one-chunk sequence the chunk-factor kernel finished itself
+  if (!SUM && jc1 - jc0 == 1 && a.done[(int64_t)jc0 * H + h]) return;
   const char* recbase = (const char*)a.rec;
 
   if (w == CW) {
@@ -1187,6 +1266,7 @@ __global__ __launch_bounds__(64 * (CT * KS + 1)) void k_state_ks(FwdArgs a) {
   __shared__ f32x4 xX[CW][4][64];
   __shared__ bf16x8 xS[CW][JW][64];
   const int jc0 = a.seq_chunk0[seq], jc1 = a.seq_chunk0[seq + 1];
+  if (!SUM && jc1 - jc0 == 1 && a.done[(int64_t)jc0 * H + h]) return;
   const char* recbase = (const char*)a.rec;
 
   if (w == CW) {
@@ -1428,6 +1508,7 @@ __global__ __launch_bounds__(256) void k_state_light(FwdArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int jc0 = a.seq_chunk0[seq], jc1 = a.seq_chunk0[seq + 1];
+  if (jc1 - jc0 == 1 && a.done[(int64_t)jc0 * H + h]) return;
   const int64_t sbase = ((int64_t)seq * H + h) * K * V;
   const char* recbase = (const char*)a.rec;
   bf16* const o = (bf16*)a.o;

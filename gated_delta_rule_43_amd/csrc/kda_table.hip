@@ -36,7 +36,8 @@ __global__ __launch_bounds__(kTableThreads) void k_chunk_table(const int32_t* __
                                                                int32_t* __restrict__ len,
                                                                int32_t* __restrict__ seq0,
                                                                int32_t* __restrict__ nt_out,
-                                                               int32_t* __restrict__ zero_out) {
+                                                               int32_t* __restrict__ zero_out,
+                                                               int32_t* __restrict__ cseq) {
   __shared__ int sh[kTableThreads];
   const int tid = threadIdx.x;
   if (zero_out && tid == 0) *zero_out = 0;  // counter the later kernels append to
@@ -47,6 +48,7 @@ __global__ __launch_bounds__(kTableThreads) void k_chunk_table(const int32_t* __
       int b = j / nc, t0 = (j - b * nc) * C;
       tok[j] = b * T + t0;
       len[j] = min(C, T - t0);
+      if (cseq) cseq[j] = b;
     }
     if (tid == 0) *nt_out = B * nc;
     return;
@@ -89,6 +91,7 @@ __global__ __launch_bounds__(kTableThreads) void k_chunk_table(const int32_t* __
         if (j < nt_max) {
           tok[j] = t0;
           len[j] = min(C, m - t0);
+          if (cseq) cseq[j] = e - 1;
         }
       }
       m_prev = m;
@@ -125,7 +128,8 @@ __global__ __launch_bounds__(256) void k_apply_summary(int64_t total, int K, int
 hipError_t launch_chunk_table(const FwdArgs& a, hipStream_t s) {
   mark(a, kStageTable, 0, s);
   hipLaunchKernelGGL(k_chunk_table, dim3(1), dim3(kTableThreads), 0, s, a.cu, a.N, a.B, a.T, a.C,
-                     a.NT, a.chunk_tok, a.chunk_len, a.seq_chunk0, a.nt_dev, a.exact_count);
+                     a.NT, a.chunk_tok, a.chunk_len, a.seq_chunk0, a.nt_dev, a.exact_count,
+                     a.chunk_seq);
   hipError_t e = hipGetLastError();
   mark(a, kStageTable, 1, s);
   return e;

@@ -22,6 +22,10 @@ CASES = [
     ("docs_k128_v64_clamp", 128, 64, 0, 2, [100, 28, 200], -3.0, "clamp", 0.2, None),
     ("rows_k64_v128_init", 64, 128, 193, 2, None, None, "sigmoid", 0.3, None),
     ("grouped_heads", 128, 128, 150, 2, None, None, "sigmoid", 0.1, 4),
+    # one-chunk documents from a zero state: the two-pass path finishes them
+    # inside the chunk-factor kernel
+    ("short_docs_d128_no_init", 128, 128, 0, 3, [5, 64, 1, 70, 0, 33, 128, 64], None, "sigmoid", None, None),
+    ("short_docs_d64_no_init_lb", 64, 64, 0, 2, [64, 17, 1, 2, 100, 63], -5.0, "sigmoid", None, None),
 ]
 
 
