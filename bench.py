@@ -90,6 +90,13 @@ def measured_traffic(stage_name):
     return None if k is None else int(k["traffic_bytes"])
 
 
+def measured_path_traffic():
+    """HBM bytes of one whole forward (every kernel of the throughput workload's
+    call) from the same committed summary, or None when stale/absent."""
+    info = _current_profile("traffic_throughput_bf16_B4_T16384_H32_d128.json")
+    return None if info is None else int(sum(k["traffic_bytes"] for k in info.get("kernels", {}).values()))
+
+
 def measured_mfma_util(workload):
     """Per-kernel MFMA busy % (SQ_VALU_MFMA_BUSY_CYCLES over the SIMDs' active
     cycles) from the committed counter summary, or None when stale/absent."""
@@ -551,6 +558,7 @@ def main():
     dom_ms = float(stage_ms[dom])
     achieved = path_bytes / (dom_ms / 1e3) / 1e9 if dom_ms > 0 else 0.0
     traffic = measured_traffic(kda.STAGE_NAMES[dom]) if args.workload == 3 else None
+    path_traffic = measured_path_traffic() if args.workload == 3 else None
     roofline = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": traffic,
                 "kernel": kda.STAGE_NAMES[dom], "kernel_ms": round(dom_ms, 4),
@@ -558,6 +566,8 @@ def main():
                 "bytes_note": "the whole forward's algorithmic bytes (1282 B per token-head at "
                               "dk=dv=128 bf16, plus fp32 states) over the dominant kernel's time",
                 "traffic_over_algorithmic": None if traffic is None else round(traffic / path_bytes, 3),
+                "path_traffic": path_traffic,
+                "path_traffic_over_algorithmic": None if path_traffic is None else round(path_traffic / path_bytes, 3),
                 "design_bytes_per_launch": stage_bytes(w, dom, NT, N)}
     path_gbs = path_bytes / (ms_per_step / 1e3) / 1e9
     mfma_util = tokh * flops_th / (ms_per_step / 1e3) / 1e12 / MFMA_BF16_PEAK_TFLOPS * 100

@@ -337,9 +337,11 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
   // finished here (keep_ok), unless the chunk-head needs the exact fix-up.
   // Then nothing goes to the record: Kbar^T fragments go to sX (whose W
   // operands are not needed), U to sU1, the Aqk fragments stay in registers.
-  bool keep = false;
-  if (!EXACT) {
-    __shared__ int sNeedExact;
+  // The workgroup's decision takes two barriers; it is made here only when
+  // the chunk may be kept, else after step 4, where its first barrier is the
+  // one step 4 needs anyway.
+  __shared__ int sNeedExact;
+  auto decide_exact = [&]() {
     if (tid == 0) sNeedExact = 0;
     __syncthreads();
     if (negmax > kDiagSafe && lane == 0) sNeedExact = 1;
@@ -349,8 +351,10 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
       const int slot = atomicAdd(a.exact_count, 1);
       a.exact_list[slot] = jchunk * H + h;  // slot < NT*H: each chunk-head appends once
     }
-    keep = keep_ok && !need;
-  }
+    return need;
+  };
+  bool keep = false;
+  if (!EXACT && keep_ok) keep = !decide_exact();
 
   // ---- 4. per-element factors; fragments to LDS and to the record ----
   const bf16x8 sel0 = select_frag(g, n, 0), sel1 = select_frag(g, n, 1);
@@ -406,7 +410,8 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
   }
   if (!keep)
     for (int c = tid; c < K; c += kThreads) ((float*)(rec + R::oGL))[c] = sFac[kF_GL][c];
-  __syncthreads();
+  if (!EXACT && !keep_ok) decide_exact();
+  else __syncthreads();
 
   // ---- 5. decayed key/query products, blocks (I <= R = w), transposed tiles ----
   f32x4 dq[4], dk[4];
