@@ -343,11 +343,30 @@ kda_status check_conv(const kda_problem* p, const kda_short_conv* conv, const vo
 
 // kda_fwd, optionally after the short convolution of q, k and v.  path < 0:
 // the library's choice; otherwise the path whose workspace the caller sized.
+// The gated output norm needs whole output rows: the fused kernel's consumer
+// waves split them, so a normed forward takes the two-pass kernels instead.
+int norm_path(const kda_problem* p) {
+  const int path = choose_path(p, false);
+  return path == kPathFused ? kPathMfma : path;
+}
+
+kda_status check_norm(const kda_problem* p, const kda_output_norm* nrm) {
+  if (!nrm->gate) return fail(KDA_EINVAL, "the output norm's gate must be non-NULL");
+  if (!aligned(nrm->gate, 16)) return fail(KDA_EINVAL, "the output norm's gate must be 16-byte aligned");
+  if (nrm->weight && !aligned(nrm->weight, 16)) return fail(KDA_EINVAL, "the output norm's weight must be 16-byte aligned");
+  if (!std::isfinite(nrm->eps) || nrm->eps < 0.f) return fail(KDA_EINVAL, "eps must be finite and >= 0");
+  if (nrm->activation != KDA_NORM_SIGMOID && nrm->activation != KDA_NORM_SILU)
+    return fail(KDA_EINVAL, "activation must be KDA_NORM_SIGMOID or KDA_NORM_SILU");
+  (void)p;
+  return KDA_OK;
+}
+
 kda_status fwd_impl(const kda_problem* p, const kda_short_conv* conv, const void* q, const void* k,
                     const void* v, const void* gate, const void* beta, const float* a_log,
                     const float* dt_bias, const float* initial_state, void* o,
                     float* final_state, void* workspace, size_t workspace_bytes, void* stream,
-                    void* const* stage_events, int path = -1) {
+                    void* const* stage_events, int path = -1,
+                    const kda_output_norm* nrm = nullptr) {
   kda_status st = validate_problem(p, false);
   if (st != KDA_OK) return st;
   st = check_inputs(p, q, k, v, gate, beta, a_log, dt_bias);
@@ -356,6 +375,11 @@ kda_status fwd_impl(const kda_problem* p, const kda_short_conv* conv, const void
   if (initial_state && !aligned(initial_state, 4)) return fail(KDA_EINVAL, "initial_state misaligned");
   if (final_state && !aligned(final_state, 4)) return fail(KDA_EINVAL, "final_state misaligned");
   if (o && !aligned(o, p->dtype == KDA_BF16 ? 2 : 4)) return fail(KDA_EINVAL, "o misaligned");
+  if (nrm) {
+    st = check_norm(p, nrm);
+    if (st != KDA_OK) return st;
+    if (path < 0) path = norm_path(p);
+  }
   const Layout L = path < 0 ? layout(p, false) : layout_for(p, path);
   ConvBuffers cb;
   if (conv) {
@@ -393,7 +417,37 @@ kda_status fwd_impl(const kda_problem* p, const kda_short_conv* conv, const void
   a.a_log = a_log; a.dt_bias = dt_bias; a.init = initial_state;
   a.o = o; a.fin = final_state; a.summary = 0;
   a.events = stage_events;
+  // The norm applied inside the state pass needs one workgroup per (sequence,
+  // head) holding whole rows; on every measured shape that costs the pass
+  // more than a separate pass over o costs (throughput shape 2.52 vs 1.97 ms,
+  // packed varlen 0.36 vs 0.22, short documents 1.57 vs 1.20), so by default
+  // the output is normalised in place right after the forward.
+  // KDA_NORM_IN_PASS=1 selects the in-pass form.
+  bool in_pass = false;
+  if (nrm && L.path != kPathValu) {
+    if (const char* env = std::getenv("KDA_NORM_IN_PASS")) in_pass = std::atoi(env) != 0;
+  }
+  if (in_pass) {
+    a.norm = 1;
+    a.norm_act = nrm->activation;
+    a.norm_eps = nrm->eps;
+    a.norm_gate = nrm->gate;
+    a.norm_w = nrm->weight;
+  }
   hipError_t e = launch(a, L, s);
+  if (e == hipSuccess && nrm && !in_pass && (long long)p->B * p->T > 0) {
+    kda::NormArgs na{};
+    na.rows = (int64_t)p->B * p->T * value_heads(p);
+    na.V = p->V;
+    na.dtype = p->dtype == KDA_BF16 ? 1 : 0;
+    na.act = nrm->activation;
+    na.eps = nrm->eps;
+    na.o = o;
+    na.gate = nrm->gate;
+    na.w = nrm->weight;
+    na.y = o;
+    e = kda::launch_gated_rms_norm(na, s);
+  }
   if (e != hipSuccess) return fail(KDA_EHIP, "kernel launch failed: %s", hipGetErrorString(e));
   g_last_error.clear();
   return KDA_OK;
@@ -448,6 +502,22 @@ kda_status scratch_address(void* stream, void** out) {
 extern "C" {
 
 size_t kda_fwd_noalloc_scratch_bytes(void) { return kNoAllocScratchBytes; }
+
+size_t kda_fwd_gated_norm_workspace_size(const kda_problem* p, kda_status* status) {
+  kda_status st = validate_problem(p, false);
+  if (status) *status = st;
+  return st == KDA_OK ? layout_for(p, norm_path(p)).total : 0;
+}
+
+kda_status kda_fwd_gated_norm(const kda_problem* p, const kda_output_norm* norm, const void* q,
+                              const void* k, const void* v, const void* gate, const void* beta,
+                              const float* a_log, const float* dt_bias,
+                              const float* initial_state, void* y, float* final_state,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  if (!norm) return fail(KDA_EINVAL, "output norm description is NULL");
+  return fwd_impl(p, nullptr, q, k, v, gate, beta, a_log, dt_bias, initial_state, y, final_state,
+                  workspace, workspace_bytes, stream, nullptr, -1, norm);
+}
 
 kda_status kda_fwd_noalloc(const kda_problem* p, const void* q, const void* k, const void* v,
                            const void* gate, const void* beta, const float* a_log,

@@ -80,6 +80,14 @@ struct FwdArgs {
   // [NT*H] written by the chunk-factor kernel for every chunk-head: 1 when it
   // finished the chunk's sequence itself (a one-chunk sequence), 0 otherwise
   int32_t* done;
+  // optional gated output norm fused into the output store (norm != 0): o then
+  // receives y = o / sqrt(mean_V(o^2) + eps) * weight * act(gate_o) per
+  // (token, value head) row, o rounded to the input dtype first
+  int norm;
+  int norm_act;          // 0 sigmoid, 1 SiLU
+  float norm_eps;
+  const void* norm_gate; // [B,T,H,V], dtype as q
+  const float* norm_w;   // [V] or null for ones
   // optional stage timing: hipEvent_t handles, [2 * kNumStages], entries may be null
   void* const* events;
 };

@@ -744,7 +744,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_chunk_mfma(FwdArgs a) {
   if (jchunk >= nt) return;
   // a sequence of this one chunk that starts from a zero state is finished here
   const int sq = a.chunk_seq[jchunk];
-  const bool keep_ok = !a.summary && a.init == nullptr &&
+  const bool keep_ok = !a.summary && !a.norm && a.init == nullptr &&
                        a.seq_chunk0[sq + 1] - a.seq_chunk0[sq] == 1;
   chunk_body<K, V, false, GATE>(a, jchunk, h, tok0, L,
                                 (char*)a.rec + ((int64_t)jchunk * a.H + h) * Rec<K, V>::kBytes,
@@ -1615,6 +1615,236 @@ __global__ __launch_bounds__(256) void k_state_light(FwdArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Kernel B4: state pass with one workgroup per (sequence, head).
+// ---------------------------------------------------------------------------
+// V/16 waves each own one 16-column tile, so a workgroup holds whole output
+// rows and can apply the gated output norm before storing them (NORM).  There
+// is no separate loader wave: every wave issues its share of the next-but-one
+// chunk's stage copy (Qt, W, Kbar^T, gL into one of three LDS buffers) at the
+// start of a chunk and waits for its own copies at the end, so each copy has
+// one chunk's time to land.  The output of chunk c is stored at the start of
+// chunk c+1, after the barrier that makes every wave's per-row sum of squares
+// of chunk c visible (two LDS slots, by chunk parity).
+template <int K, int V, bool NORM, int ACT>
+__global__ __launch_bounds__(64 * (V / 16)) void k_state_row(FwdArgs a) {
+  using R = Rec<K, V>;
+  constexpr int NW = V / 16;  // waves = column tiles
+  constexpr int NKJ = K / 32, NKT = K / 16, NVT = V / 16;
+  constexpr int kStageBytes = R::kStageCopies * 1024;
+  const int H = a.H;
+  const int64_t nh = blockIdx.x;
+  if (nh >= (int64_t)a.N * H) return;
+  const int h = (int)(nh % H), seq = (int)(nh / H);
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4, n = lane & 15;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int jc0 = a.seq_chunk0[seq], jc1 = a.seq_chunk0[seq + 1];
+  if (!NORM && jc1 - jc0 == 1 && a.done[(int64_t)jc0 * H + h]) return;
+  __shared__ __attribute__((aligned(16))) char sStage0[kStageBytes];
+  __shared__ __attribute__((aligned(16))) char sStage1[kStageBytes];
+  __shared__ __attribute__((aligned(16))) char sStage2[kStageBytes];
+  __shared__ float sSS[2][NW][4][16];  // per-row sums of squares, by chunk parity
+  const char* recbase = (const char*)a.rec;
+  const int ctg = w, col = 16 * w + n;
+  const int64_t sbase = ((int64_t)seq * H + h) * K * V;
+
+  auto stage = [&](int jc, auto bufc) {
+    constexpr int B = decltype(bufc)::value;
+    char* const dst = B == 0 ? sStage0 : (B == 1 ? sStage1 : sStage2);
+    const char* rec = recbase + ((int64_t)jc * H + h) * R::kBytes;
+    for (int i = w; i < R::kStageCopies; i += NW)
+      __builtin_amdgcn_global_load_lds((const void*)(rec + (lane + 64 * i) * 16),
+                                       (lds_void*)(&dst[(64 * i) * 16]), 16, 0, 0);
+  };
+
+  f32x4 S[NKT];
+#pragma unroll
+  for (int at = 0; at < NKT; ++at)
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      S[at][e] = a.init ? a.init[sbase + (int64_t)(16 * at + 4 * g + e) * V + col] : 0.f;
+
+  uint2 ucur[4], unext[4], gcur[4], gnext[4];
+  bf16x8 fA[4][2], fAn[4][2];
+  auto load_ops = [&](int jc, uint2 (&u)[4], bf16x8 (&aq)[4][2]) {
+    const char* rec = recbase + ((int64_t)jc * H + h) * R::kBytes;
+    const uint2* ug = (const uint2*)(rec + R::oU);
+    const bf16x8* ga = (const bf16x8*)(rec + R::oAqk);
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      u[t] = ug[(t * NVT + ctg) * 64 + lane];
+      aq[t][0] = ga[(t * 2 + 0) * 64 + lane];
+      aq[t][1] = ga[(t * 2 + 1) * 64 + lane];
+    }
+  };
+  // the output gate of rows 16t+n, columns 16w+4g..+3 (rows past the chunk
+  // end read the chunk's first row; their results are not stored)
+  auto load_gate = [&](int tok, int len, uint2 (&gg)[4]) {
+    if (NORM) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const int r = 16 * t + n < len ? 16 * t + n : 0;
+        gg[t] = *(const uint2*)((const bf16*)a.norm_gate + ((int64_t)(tok + r) * H + h) * V + 16 * w + 4 * g);
+      }
+    }
+  };
+  float wn[4] = {1.f, 1.f, 1.f, 1.f};
+  if (NORM && a.norm_w) {
+    const float4 w4 = *(const float4*)&a.norm_w[16 * w + 4 * g];
+    wn[0] = w4.x; wn[1] = w4.y; wn[2] = w4.z; wn[3] = w4.w;
+  }
+  int tok_cur = 0, len_cur = 0;
+  if (jc0 < jc1) {
+    stage(jc0, std::integral_constant<int, 0>{});
+    if (jc0 + 1 < jc1) stage(jc0 + 1, std::integral_constant<int, 1>{});
+    load_ops(jc0, ucur, fA);
+    tok_cur = a.chunk_tok[jc0];
+    len_cur = a.chunk_len[jc0];
+    load_gate(tok_cur, len_cur, gnext);
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+
+  uint2 opend[4];
+  int otok = 0, olen = 0;
+  bf16* const o = (bf16*)a.o;
+  // stores chunk (otok, olen)'s output rows, normalised with the sums of
+  // squares in slot par
+  auto store_out = [&](int par) {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int r = 16 * t + n;
+      uint2 val = opend[t];
+      if (NORM) {
+        float ss = 0.f;
+#pragma unroll
+        for (int ww = 0; ww < NW; ++ww) ss += sSS[par][ww][t][n];
+        const float inv = 1.f / sqrtf(ss / V + a.norm_eps);
+        float x[4], gt[4], y[4];
+        unpack4(val, x);
+        unpack4(gcur[t], gt);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float sg = __builtin_amdgcn_rcpf(1.f + __expf(-gt[e]));
+          const float act = ACT == 0 ? sg : gt[e] * sg;
+          y[e] = x[e] * inv * wn[e] * act;
+        }
+        val = pk4(y[0], y[1], y[2], y[3]);
+      }
+      if (r < olen) *(uint2*)(o + ((int64_t)(otok + r) * H + h) * V + 16 * w + 4 * g) = val;
+    }
+  };
+
+  auto chunk_step = [&](int jc, auto bufc, auto nbufc) {
+    constexpr int BUF = decltype(bufc)::value;
+    const char* const cur = BUF == 0 ? sStage0 : (BUF == 1 ? sStage1 : sStage2);
+    if (jc + 2 < jc1) stage(jc + 2, nbufc);
+    const int jn = (jc + 1 < jc1) ? jc + 1 : jc;
+    load_ops(jn, unext, fAn);
+    const int tok_n = a.chunk_tok[jn], len_n = a.chunk_len[jn];
+    // the previous chunk's output (its gate values are in gcur); then gcur
+    // takes this chunk's gate values and gnext starts loading the next's
+    if (jc > jc0) store_out((jc - 1 - jc0) & 1);
+    if (NORM) {
+#pragma unroll
+      for (int t = 0; t < 4; ++t) gcur[t] = gnext[t];
+    }
+    load_gate(tok_n, len_n, gnext);
+    const bf16x8* sQt = (const bf16x8*)(cur + R::oQt);
+    const bf16x8* sW = (const bf16x8*)(cur + R::oW);
+    const bf16x8* sKbar = (const bf16x8*)(cur + R::oKbar);
+    const float* sGL = (const float*)(cur + R::oGL);
+    f32x4 Ut[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      float u[4];
+      unpack4(ucur[t], u);
+      Ut[t] = f32x4{u[0], u[1], u[2], u[3]};
+    }
+    bf16x8 sb[NKJ], sl[NKJ];
+#pragma unroll
+    for (int j = 0; j < NKJ; ++j) split_frag(S[2 * j], S[2 * j + 1], sb[j], sl[j]);
+    f32x4 X[4], Y[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      X[t] = zero4();
+#pragma unroll
+      for (int j = 0; j < NKJ; ++j) {
+        const bf16x8 fw = sW[(t * NKJ + j) * 64 + lane];
+        X[t] = mfma(fw, sb[j], X[t]);
+        X[t] = mfma(fw, sl[j], X[t]);
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      Y[t] = zero4();
+#pragma unroll
+      for (int j = 0; j < NKJ; ++j) Y[t] = mfma(sb[j], sQt[(t * NKJ + j) * 64 + lane], Y[t]);
+    }
+    f32x4 D[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) D[t] = Ut[t] - X[t];
+    bf16x8 db[2], dl[2];
+    split_frag(D[0], D[1], db[0], dl[0]);
+    split_frag(D[2], D[3], db[1], dl[1]);
+    const int par = (jc - jc0) & 1;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      Y[t] = mfma(db[0], fA[t][0], Y[t]);
+      if (t >= 2) Y[t] = mfma(db[1], fA[t][1], Y[t]);
+      opend[t] = pk4(Y[t]);
+      if (NORM) {
+        // this wave's 16 columns of row 16t+n, as the stored (rounded) values
+        float x[4];
+        unpack4(opend[t], x);
+        float ss = x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+        ss += __shfl_xor(ss, 16);
+        ss += __shfl_xor(ss, 32);
+        if (g == 0) sSS[par][w][t][n] = ss;
+      }
+    }
+#pragma unroll
+    for (int at = 0; at < NKT; ++at) {
+      const float4 gl = *(const float4*)&sGL[16 * at + 4 * g];
+      const bf16x8 fk0 = sKbar[(at * 2 + 0) * 64 + lane], fk1 = sKbar[(at * 2 + 1) * 64 + lane];
+      f32x4 acc = {gl.x * S[at][0], gl.y * S[at][1], gl.z * S[at][2], gl.w * S[at][3]};
+      acc = mfma(fk0, db[0], acc);
+      acc = mfma(fk1, db[1], acc);
+      acc = mfma(fk0, dl[0], acc);
+      acc = mfma(fk1, dl[1], acc);
+      S[at] = acc;
+    }
+    otok = tok_cur;
+    olen = len_cur;
+    // this wave's stage copies for chunk c+1 (issued a chunk ago) and its
+    // prefetched operands have landed; after the barrier every wave's copies
+    // have, and every wave is done with this chunk's buffer
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      ucur[t] = unext[t];
+      fA[t][0] = fAn[t][0];
+      fA[t][1] = fAn[t][1];
+    }
+    tok_cur = tok_n;
+    len_cur = len_n;
+  };
+  for (int jc = jc0; jc < jc1; jc += 3) {
+    chunk_step(jc, std::integral_constant<int, 0>{}, std::integral_constant<int, 2>{});
+    if (jc + 1 < jc1) chunk_step(jc + 1, std::integral_constant<int, 1>{}, std::integral_constant<int, 0>{});
+    if (jc + 2 < jc1) chunk_step(jc + 2, std::integral_constant<int, 2>{}, std::integral_constant<int, 1>{});
+  }
+  if (jc1 > jc0) store_out((jc1 - 1 - jc0) & 1);
+  if (a.fin) {
+#pragma unroll
+    for (int at = 0; at < NKT; ++at)
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        a.fin[sbase + (int64_t)(16 * at + 4 * g + e) * V + col] = S[at][e];
+  }
+}
+
 // compute units of the current device (cached per device)
 inline int device_cus() {
   static int cache[64] = {0};
@@ -1658,6 +1888,21 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
   int cw = 4;
   while (cw > 1 && heads * (ncols / 16 / cw) < cus) cw /= 2;
   int64_t wgs = heads * (ncols / 16 / cw);
+  // whole output rows per workgroup: needed by the fused output norm
+  bool rowk = a.norm != 0;
+  if (const char* env = std::getenv("KDA_STATE_ROW")) rowk = rowk || std::atoi(env) != 0;
+  if (rowk && !a.summary) {
+    const int64_t nwg = (int64_t)a.N * a.H;
+    if (nwg > 0) {
+      const dim3 grid((unsigned)nwg), block(64 * (V / 16));
+      if (!a.norm) hipLaunchKernelGGL((k_state_row<K, V, false, 0>), grid, block, 0, s, a);
+      else if (a.norm_act == 0) hipLaunchKernelGGL((k_state_row<K, V, true, 0>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((k_state_row<K, V, true, 1>), grid, block, 0, s, a);
+      if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+    }
+    mark(a, kStageState, 1, s);
+    return hipSuccess;
+  }
   // many short sequences (at most four chunks each on average): the light pass
   bool light = !a.summary && (int64_t)a.NT <= 4 * (int64_t)a.N;
   if (const char* env = std::getenv("KDA_STATE_LIGHT")) light = !a.summary && std::atoi(env) != 0;

@@ -39,7 +39,8 @@ EXPORTED = ("kda_validate", "kda_fwd_workspace_size", "kda_fwd", "kda_fwd_profil
             "kda_short_conv_silu", "kda_fwd_short_conv_workspace_size", "kda_fwd_short_conv",
             "kda_bwd_workspace_size", "kda_bwd", "kda_bwd_profiled", "kda_gated_rms_norm",
             "kda_last_error", "kda_version", "kda_fwd_path", "kda_fwd_noalloc",
-            "kda_fwd_noalloc_scratch_bytes")
+            "kda_fwd_noalloc_scratch_bytes", "kda_fwd_gated_norm",
+            "kda_fwd_gated_norm_workspace_size")
 MAX_CONV_WIDTH = 4
 
 
@@ -56,6 +57,11 @@ class KdaShortConv(ctypes.Structure):
                 ("q_weight", ctypes.c_void_p), ("k_weight", ctypes.c_void_p),
                 ("v_weight", ctypes.c_void_p), ("q_bias", ctypes.c_void_p),
                 ("k_bias", ctypes.c_void_p), ("v_bias", ctypes.c_void_p)]
+
+
+class KdaOutputNorm(ctypes.Structure):
+    _fields_ = [("gate", ctypes.c_void_p), ("weight", ctypes.c_void_p), ("eps", ctypes.c_float),
+                ("activation", ctypes.c_int32)]
 
 
 # form of the lower-bounded gate (kda_lower_bound_form)
@@ -112,6 +118,10 @@ def load_library(path: Optional[str] = None):
     lib.kda_gated_rms_norm.restype = ctypes.c_int
     lib.kda_last_error.argtypes = []
     lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_fwd_gated_norm.argtypes = [PP, ctypes.POINTER(KdaOutputNorm)] + [P] * 11 + [S, P]
+    lib.kda_fwd_gated_norm.restype = ctypes.c_int
+    lib.kda_fwd_gated_norm_workspace_size.argtypes = [PP, PI]
+    lib.kda_fwd_gated_norm_workspace_size.restype = S
     lib.kda_fwd_noalloc.argtypes = [PP, P, P, P, P, P, P, P, P, P, P, P]
     lib.kda_fwd_noalloc.restype = ctypes.c_int
     lib.kda_fwd_noalloc_scratch_bytes.argtypes = []
@@ -303,6 +313,61 @@ def kda_fwd(q, k, v, gate, beta, a_log, dt_bias, *, scale=None, lower_bound=None
     return _fwd(q, k, v, gate, beta, a_log, dt_bias, None, scale, lower_bound, chunk_size,
                 cu_seqlens, cu_seqlens_host, initial_state, output_final_state, out, workspace,
                 stage_events, lower_bound_form)
+
+
+def kda_fwd_gated_norm(q, k, v, gate, beta, a_log, dt_bias, norm_gate, norm_weight=None, *,
+                       eps=1e-5, activation="sigmoid", scale=None, lower_bound=None,
+                       chunk_size=64, cu_seqlens=None, cu_seqlens_host=None, initial_state=None,
+                       output_final_state=False, out=None, workspace=None,
+                       lower_bound_form="sigmoid"):
+    """The forward followed by the gated output norm, in one call
+    (kda_fwd_gated_norm): returns (y, final_state or None) with
+    y = o / sqrt(mean_V(o^2) + eps) * norm_weight * act(norm_gate) per
+    (token, value head) row, o being kda_fwd's output (never stored).
+    norm_gate [B,T,HV,V] in the inputs' dtype; norm_weight float32 [V] or None;
+    activation "sigmoid" or "silu".  Other arguments as kda_fwd."""
+    if activation not in NORM_ACTIVATIONS:
+        raise ValueError("activation must be one of %s, got %r" % (sorted(NORM_ACTIVATIONS), activation))
+    B, T, H, K, V, HV = _check_inputs(q, k, v, gate, beta, a_log, dt_bias)
+    _dev(norm_gate, "norm_gate", dtype=q.dtype, shape=(B, T, HV, V))
+    if norm_weight is not None:
+        _dev(norm_weight, "norm_weight", dtype=torch.float32, shape=(V,))
+    nrm = KdaOutputNorm()
+    nrm.gate = norm_gate.data_ptr()
+    nrm.weight = None if norm_weight is None else norm_weight.data_ptr()
+    nrm.eps = float(eps)
+    nrm.activation = NORM_ACTIVATIONS[activation]
+    lib = load_library()
+    device = q.device
+    cu, host, N, host_ptr = _cu_args(cu_seqlens, cu_seqlens_host, T)
+    if N is None:
+        N = B
+    if initial_state is not None:
+        _dev(initial_state, "initial_state", dtype=torch.float32, shape=(N, HV, K, V))
+    if scale is not None and not scale > 0:
+        raise ValueError("scale must be positive, got %r" % (scale,))
+    p = make_problem(B, T, H, K, V, _dtype_code(q), scale, lower_bound, chunk_size, N,
+                     None if cu is None else cu.data_ptr(), host_ptr, lower_bound_form, HV)
+    st = ctypes.c_int(0)
+    need = lib.kda_fwd_gated_norm_workspace_size(ctypes.byref(p), ctypes.byref(st))
+    if st.value:
+        _raise(st.value, "kda_fwd_gated_norm")
+    y = out if out is not None else torch.empty((B, T, HV, V), dtype=q.dtype, device=device)
+    _dev(y, "out", dtype=q.dtype, shape=(B, T, HV, V))
+    fin = torch.empty((N, HV, K, V), dtype=torch.float32, device=device) if output_final_state else None
+    if workspace is None:
+        ws, nbytes = _workspace(need, device)
+    else:
+        _dev(workspace, "workspace", dtype=torch.uint8)
+        ws, nbytes = workspace, workspace.numel()
+    ptr = lambda t: None if t is None else t.data_ptr()
+    st = lib.kda_fwd_gated_norm(ctypes.byref(p), ctypes.byref(nrm), ptr(q), ptr(k), ptr(v),
+                                ptr(gate), ptr(beta), ptr(a_log), ptr(dt_bias),
+                                ptr(initial_state), ptr(y), ptr(fin), ptr(ws), nbytes,
+                                _stream_ptr(device))
+    if st:
+        _raise(st, "kda_fwd_gated_norm")
+    return y, fin
 
 
 def kda_fwd_noalloc(q, k, v, gate, beta, a_log, dt_bias, *, scale=None, lower_bound=None,

@@ -393,6 +393,36 @@ kda_status kda_gated_rms_norm(const kda_problem* p, const void* o, const void* g
                               const float* weight, float eps, int32_t activation, void* y,
                               void* stream);
 
+/*
+ * The forward followed by the gated output norm in one call (the layer's
+ * chunk_kda then o_norm(o, output_gate), as above): writes
+ *     y = o / sqrt(mean_V(o^2) + eps) * weight * act(norm->gate)
+ * per (token, value head) row, where o is kda_fwd's output rounded to
+ * p->dtype.  The forward writes o into y and kda_gated_rms_norm's kernel
+ * normalises it in place on the same stream.  (The matrix-core state pass can
+ * also apply the norm before storing the rows, with one workgroup holding
+ * whole rows; that is slower on every measured shape and is used only when
+ * the environment sets KDA_NORM_IN_PASS=1.)
+ *  norm->gate     [B,T,HV,V], p->dtype, 16-byte aligned (not NULL).
+ *  norm->weight   fp32 [V] or NULL for ones.
+ *  norm->eps      finite, >= 0.   norm->activation  KDA_NORM_SIGMOID / _SILU.
+ *  y              [B,T,HV,V], p->dtype (takes kda_fwd's o argument's place).
+ * Everything else as kda_fwd; the workspace is
+ * kda_fwd_gated_norm_workspace_size(p) bytes.
+ */
+typedef struct kda_output_norm {
+  const void* gate;
+  const float* weight;
+  float eps;
+  int32_t activation;
+} kda_output_norm;
+size_t kda_fwd_gated_norm_workspace_size(const kda_problem* p, kda_status* status);
+kda_status kda_fwd_gated_norm(const kda_problem* p, const kda_output_norm* norm, const void* q,
+                              const void* k, const void* v, const void* gate, const void* beta,
+                              const float* a_log, const float* dt_bias,
+                              const float* initial_state, void* y, float* final_state,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
 /* Message for the last non-OK status returned on the calling thread ("" if none). */
 const char* kda_last_error(void);
 

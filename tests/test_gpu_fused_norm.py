@@ -1,0 +1,127 @@
+"""The forward with the gated output norm (kda_fwd_gated_norm) against the
+oracle (forward, then norm, in fp64) and against the two-step GPU path
+(kda_fwd, then kda_gated_rms_norm on its output), with the norm applied in the
+state pass (KDA_NORM_IN_PASS=1) and after it (=0).
+
+The call normalises kda_fwd's output as rounded to the input dtype, so it
+equals the two-step path up to the order of the sum of squares over V.
+Against the oracle the bar is the output tolerance scaled to the normalised
+output's magnitude: max-abs <= 2e-2 * max(1, max|y|) and relative Frobenius
+<= 1e-2 (bf16), 1e-4 * max(1, max|y|) (fp32).  Normalising divides by the
+row's RMS, which scales the forward's absolute error by the same factor."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gated_delta_rule_43_amd import kda, synthetic
+from kda_testlib import assert_close, oracle_fwd, to_np
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+CASES = [
+    # (name, dtype, K, V, T, H, lengths, init_std, activation, weight, chunk)
+    ("rows_d128_sigmoid", torch.bfloat16, 128, 128, 300, 2, None, None, "sigmoid", True, 64),
+    ("docs_d128_silu_init", torch.bfloat16, 128, 128, 0, 2, [64, 1, 130, 0, 70], 0.2, "silu", True, 64),
+    ("docs_d64_no_weight", torch.bfloat16, 64, 64, 0, 3, [5, 64, 100, 33], None, "sigmoid", False, 64),
+    ("k128_v64", torch.bfloat16, 128, 64, 190, 2, None, 0.1, "silu", True, 64),
+    ("fp32_valu_path", torch.float32, 64, 64, 150, 2, None, 0.1, "sigmoid", True, 64),
+    ("bf16_chunk32_valu_path", torch.bfloat16, 128, 128, 100, 2, None, None, "silu", True, 32),
+]
+
+
+def _problem(case, seed):
+    name, dtype, K, V, T, H, lengths, init_std, act, weight, chunk = case
+    if lengths is not None:
+        T = sum(lengths)
+    inp = synthetic.random_problem(seed, 1 if lengths else 2, T, H, K, V, dtype=dtype, device=DEV,
+                                   init_std=init_std, lengths=lengths)
+    inp.update(scale=None, lower_bound=None, chunk_size=chunk)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(seed + 1)
+    ng = torch.randn(inp["v"].shape, generator=gen, device=DEV).to(dtype)
+    w = (torch.rand(V, generator=gen, device=DEV) + 0.5) if weight else None
+    return inp, ng, w, act
+
+
+def _fused(inp, ng, w, act):
+    y, fin = kda.kda_fwd_gated_norm(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"],
+                                    inp["a_log"], inp["dt_bias"], ng, w, eps=1e-5, activation=act,
+                                    chunk_size=inp["chunk_size"], cu_seqlens=inp["cu_seqlens"],
+                                    initial_state=inp["initial_state"], output_final_state=True)
+    torch.cuda.synchronize()
+    return y, fin
+
+
+def _close_scaled(got, ref, dtype, what):
+    scale = max(1.0, float(np.max(np.abs(ref))))
+    maxabs = float(np.max(np.abs(np.asarray(got, np.float64) - ref)))
+    relf = float(np.linalg.norm(np.asarray(got, np.float64) - ref) / max(1e-30, np.linalg.norm(ref)))
+    if dtype == torch.float32:
+        assert maxabs <= 1e-4 * scale, "%s: max-abs %.3g (scale %.3g)" % (what, maxabs, scale)
+    else:
+        assert maxabs <= 2e-2 * scale and relf <= 1e-2, "%s: max-abs %.3g (scale %.3g), rel-F %.3g" % (what, maxabs, scale, relf)
+
+
+@pytest.mark.parametrize("in_pass", ["1", "0"])
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_fused_norm_matches_oracle_and_two_step(case, in_pass, monkeypatch):
+    print("[gpu-test] fused output norm %s in_pass=%s" % (case[0], in_pass), flush=True)
+    monkeypatch.setenv("KDA_NORM_IN_PASS", in_pass)
+    inp, ng, w, act = _problem(case, 800 + CASES.index(case))
+    dtype = case[1]
+    y, fin = _fused(inp, ng, w, act)
+    # two steps on the GPU
+    o, fin2 = kda.kda_fwd(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"], inp["a_log"],
+                          inp["dt_bias"], chunk_size=inp["chunk_size"], cu_seqlens=inp["cu_seqlens"],
+                          initial_state=inp["initial_state"], output_final_state=True)
+    y2 = kda.gated_rms_norm(o, ng, w, eps=1e-5, activation=act)
+    torch.cuda.synchronize()
+    assert float((fin - fin2).abs().max()) <= 1e-4
+    if dtype == torch.float32:
+        assert float((y - y2).abs().max()) <= 1e-4
+    else:
+        assert_close(to_np(y), to_np(y2), torch.bfloat16, "fused vs two-step")
+        same = float((y == y2).float().mean())
+        assert same >= 0.97, "only %.3f of the outputs equal the two-step path's" % same
+    # the oracle: fp64 forward, then the norm of its output
+    o_ref, f_ref = oracle_fwd(inp)
+    y_ref = oracle.gated_rms_norm(o_ref, to_np(ng), None if w is None else to_np(w), 1e-5, act)
+    _close_scaled(to_np(y), y_ref, dtype, "y vs oracle")
+    assert_close(to_np(fin), f_ref, dtype, "final state vs oracle")
+
+
+def test_fused_norm_with_fused_path_forced(monkeypatch):
+    """KDA_PATH=fused: the normed forward takes the two-pass kernels (the fused
+    kernel splits output rows over waves); results as without the override."""
+    monkeypatch.setenv("KDA_NORM_IN_PASS", "1")
+    inp, ng, w, act = _problem(CASES[0], 900)
+    y1, f1 = _fused(inp, ng, w, act)
+    monkeypatch.setenv("KDA_PATH", "fused")
+    y2, f2 = _fused(inp, ng, w, act)
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("in_pass", ["1", "0"])
+def test_fused_norm_throughput_shape_sampled(in_pass, monkeypatch):
+    """Workload 3 at full size with the norm against the two-step path (the
+    norm in the state pass and after it)."""
+    monkeypatch.setenv("KDA_NORM_IN_PASS", in_pass)
+    w3 = synthetic.WORKLOADS[3]
+    print("[gpu-test] fused output norm, " + w3.name, flush=True)
+    inp = synthetic.make_inputs(w3, DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(11)
+    ng = torch.randn(inp["v"].shape, generator=gen, device=DEV).to(torch.bfloat16)
+    w = torch.rand(w3.V, generator=gen, device=DEV) + 0.5
+    y, _ = kda.kda_fwd_gated_norm(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"],
+                                  inp["a_log"], inp["dt_bias"], ng, w)
+    o, _ = kda.kda_fwd(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"], inp["a_log"],
+                       inp["dt_bias"])
+    y2 = kda.gated_rms_norm(o, ng, w)
+    torch.cuda.synchronize()
+    d = (y.float() - y2.float()).abs()
+    print("workload 3 fused vs two-step: max %.3g, equal %.4f" % (float(d.max()), float((y == y2).float().mean())), flush=True)
+    assert float((y == y2).float().mean()) >= 0.97
+    assert_close(to_np(y[:, :2048]), to_np(y2[:, :2048]), torch.bfloat16, "fused vs two-step")
