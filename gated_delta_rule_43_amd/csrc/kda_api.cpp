@@ -100,8 +100,11 @@ kda_status validate_problem(const kda_problem* p, bool summary) {
   return validate_rows(p, summary);
 }
 
-// Which kernels run.  fp32 inputs and chunk sizes 16 and 32: the VALU path.
-// bf16 with 64-token chunks: the matrix-core kernels, either fused (one
+// Which kernels run.  fp32 inputs: the VALU path.  bf16: the matrix-core
+// kernels, whose tiles hold 64 rows; chunks of 16 or 32 tokens fill the first
+// rows of a tile and the rest is masked exactly as past a sequence's end (zero
+// beta, q^, k^ and log-decay), so the tile computes those chunks' algebra.
+// The matrix-core kernels run either fused (one
 // workgroup per (sequence, head) computes and consumes each chunk's factors
 // in LDS) or in two passes (all chunk-heads' factors in parallel as records in
 // the workspace, then the sequential state pass over them).  Summaries take
@@ -110,7 +113,8 @@ kda_status validate_problem(const kda_problem* p, bool summary) {
 enum Path { kPathValu = 0, kPathMfma = 1, kPathFused = 2 };
 
 int choose_path(const kda_problem* p, bool summary) {
-  const bool mfma_ok = p->dtype == KDA_BF16 && p->chunk_size == 64;
+  const bool mfma_ok = p->dtype == KDA_BF16 &&
+                       (p->chunk_size == 64 || p->chunk_size == 32 || p->chunk_size == 16);
   const char* env = std::getenv("KDA_PATH");
   if (env && std::strcmp(env, "valu") == 0) return kPathValu;
   if (!mfma_ok) return kPathValu;

@@ -150,14 +150,16 @@ kda_status kda_fwd(const kda_problem* p, const void* q, const void* k, const voi
 
 /*
  * Which kernels kda_fwd runs for this problem (host only, launches nothing):
- *   KDA_PATH_VALU   fp32 inputs or chunk sizes 16/32: vector-ALU kernels;
- *   KDA_PATH_MFMA   bf16, chunk 64: all chunk-heads' factors in parallel into
+ *   KDA_PATH_VALU   fp32 inputs: vector-ALU kernels;
+ *   KDA_PATH_MFMA   bf16: all chunk-heads' factors in parallel into
  *                   workspace records, then the sequential state pass;
- *   KDA_PATH_FUSED  bf16, chunk 64: one workgroup per (sequence, head) that
+ *   KDA_PATH_FUSED  bf16: one workgroup per (sequence, head) that
  *                   computes and consumes each chunk's factors in on-chip
  *                   memory (no records in the workspace).
  * Both matrix-core paths compute the same algebra; their results agree to
- * rounding.  Returns -1 (message in kda_last_error) for an invalid problem.
+ * rounding.  Their tiles hold 64 rows: a chunk of 16 or 32 tokens fills the
+ * first rows and the rest is masked as past a sequence's end, so the tile
+ * computes that chunk size's algebra (with the masked rows' products wasted).  Returns -1 (message in kda_last_error) for an invalid problem.
  */
 #define KDA_PATH_VALU 0
 #define KDA_PATH_MFMA 1

@@ -82,3 +82,24 @@ def test_fused_extreme_gates(monkeypatch):
     monkeypatch.setenv("KDA_STATE_KS", "1")
     o2, f2 = gpu_fwd(inp)
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("C", [16, 32])
+def test_short_chunks_on_matrix_cores(C, monkeypatch):
+    """bf16 with 16- and 32-token chunks runs on the matrix-core kernels (the
+    chunk fills the first rows of a 64-row tile); documents of every length
+    class against the oracle, on both matrix-core paths (equal bit for bit)."""
+    print("[gpu-test] chunk %d on matrix cores" % C, flush=True)
+    lengths = [1, C - 1, C, C + 1, 3 * C + 5, 0, 64, 2 * C]
+    inp = synthetic.random_problem(600 + C, 1, sum(lengths), 2, 128, 64, dtype=torch.bfloat16,
+                                   device=DEV, init_std=0.2, lengths=lengths)
+    inp.update(scale=None, lower_bound=None, chunk_size=C)
+    assert kda.fwd_path((1, sum(lengths), 2, 128), 64, chunk_size=C, cu_seqlens=True) == "mfma"
+    monkeypatch.setenv("KDA_STATE_KS", "1")
+    o2, f2 = gpu_fwd(inp)
+    monkeypatch.setenv("KDA_PATH", "fused")
+    o1, f1 = gpu_fwd(inp)
+    assert torch.equal(o1, o2) and torch.equal(f1, f2)
+    o_ref, f_ref = oracle_fwd(inp)
+    assert_close(to_np(o1), o_ref, torch.bfloat16, "o")
+    assert_close(to_np(f1), f_ref, torch.bfloat16, "final_state")

@@ -27,7 +27,7 @@ CASES = [
     ("docs_d64_no_weight", torch.bfloat16, 64, 64, 0, 3, [5, 64, 100, 33], None, "sigmoid", False, 64),
     ("k128_v64", torch.bfloat16, 128, 64, 190, 2, None, 0.1, "silu", True, 64),
     ("fp32_valu_path", torch.float32, 64, 64, 150, 2, None, 0.1, "sigmoid", True, 64),
-    ("bf16_chunk32_valu_path", torch.bfloat16, 128, 128, 100, 2, None, None, "silu", True, 32),
+    ("bf16_chunk32", torch.bfloat16, 128, 128, 100, 2, None, None, "silu", True, 32),
 ]
 
 
