@@ -31,7 +31,8 @@ constexpr size_t kAlign = 256;
 constexpr size_t kSinkBytes = 16384;  // 256 threads x 2 column tiles x 8 B, with room
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
-bool head_dim_ok(int d) { return d == 64 || d == 128; }
+bool head_dim_ok(int d) { return d == 64 || d == 128 || d == 256; }
+bool wide(const kda_problem* p) { return p->K == 256 || p->V == 256; }
 
 // value heads (HV, 0 meaning H)
 int value_heads(const kda_problem* p) { return p->HV > 0 ? p->HV : p->H; }
@@ -93,7 +94,9 @@ kda_status validate_problem(const kda_problem* p, bool summary) {
     return fail(KDA_EINVAL, "value heads HV=%d must be a positive multiple of the key heads H=%d (or 0)",
                 p->HV, p->H);
   if (!head_dim_ok(p->K) || !head_dim_ok(p->V))
-    return fail(KDA_EUNSUPPORTED, "head dims K=%d V=%d are not supported (64 or 128)", p->K, p->V);
+    return fail(KDA_EUNSUPPORTED, "head dims K=%d V=%d are not supported (64, 128 or 256)", p->K, p->V);
+  if (wide(p) && p->chunk_size == 64)
+    return fail(KDA_EUNSUPPORTED, "head dim 256 runs with chunk_size 16 or 32, got 64");
   const long long BT = (long long)p->B * p->T;
   if (BT >= (1LL << 31) || BT * value_heads(p) >= (1LL << 31))
     return fail(KDA_EUNSUPPORTED, "B*T*HV = %lld token-heads exceeds 2^31", BT * value_heads(p));
@@ -113,7 +116,7 @@ kda_status validate_problem(const kda_problem* p, bool summary) {
 enum Path { kPathValu = 0, kPathMfma = 1, kPathFused = 2 };
 
 int choose_path(const kda_problem* p, bool summary) {
-  const bool mfma_ok = p->dtype == KDA_BF16 &&
+  const bool mfma_ok = p->dtype == KDA_BF16 && !wide(p) &&
                        (p->chunk_size == 64 || p->chunk_size == 32 || p->chunk_size == 16);
   const char* env = std::getenv("KDA_PATH");
   if (env && std::strcmp(env, "valu") == 0) return kPathValu;
@@ -717,8 +720,16 @@ kda_status kda_chunk_table(const kda_problem* p, int32_t* tok, int32_t* len, int
   return KDA_OK;
 }
 
-size_t kda_bwd_workspace_size(const kda_problem* p, kda_status* status) {
+// The backward keeps head dims 64 and 128 (its chunk kernel's LDS is sized for 128).
+kda_status validate_bwd(const kda_problem* p) {
   kda_status st = validate_problem(p, false);
+  if (st == KDA_OK && wide(p))
+    return fail(KDA_EUNSUPPORTED, "the backward supports head dims 64 and 128, got K=%d V=%d", p->K, p->V);
+  return st;
+}
+
+size_t kda_bwd_workspace_size(const kda_problem* p, kda_status* status) {
+  kda_status st = validate_bwd(p);
   if (status) *status = st;
   return st == KDA_OK ? bwd_layout(p).total : 0;
 }
@@ -741,7 +752,7 @@ kda_status kda_bwd_profiled(const kda_problem* p, const void* q, const void* k, 
                             void* dgate, void* dbeta, float* da_log, float* ddt_bias,
                             float* d_initial_state, void* workspace, size_t workspace_bytes,
                             void* stream, void* const* stage_events) {
-  kda_status st = validate_problem(p, false);
+  kda_status st = validate_bwd(p);
   if (st != KDA_OK) return st;
   st = check_inputs(p, q, k, v, gate, beta, a_log, dt_bias);
   if (st != KDA_OK) return st;
@@ -787,7 +798,7 @@ kda_status kda_gated_rms_norm(const kda_problem* p, const void* o, const void* g
   if (st != KDA_OK) return st;
   if (p->H < 1 || p->HV < 0 || (p->HV > 0 && p->HV % p->H != 0))
     return fail(KDA_EINVAL, "bad heads H=%d HV=%d", p->H, p->HV);
-  if (!head_dim_ok(p->V)) return fail(KDA_EUNSUPPORTED, "value head dim V=%d is not supported (64 or 128)", p->V);
+  if (!head_dim_ok(p->V)) return fail(KDA_EUNSUPPORTED, "value head dim V=%d is not supported (64, 128 or 256)", p->V);
   if (activation != KDA_NORM_SIGMOID && activation != KDA_NORM_SILU)
     return fail(KDA_EINVAL, "activation must be KDA_NORM_SIGMOID or KDA_NORM_SILU, got %d", activation);
   if (!(eps >= 0.f) || !std::isfinite(eps)) return fail(KDA_EINVAL, "eps must be finite and >= 0, got %g", (double)eps);

@@ -101,8 +101,12 @@ hipError_t launch_gated_rms_norm(const NormArgs& a, hipStream_t s) {
   const int nv = a.dtype == 1 ? 8 : 4;
   const int64_t rows_per_block = (int64_t)(kNormThreads / (a.V / nv)) * kNormRows;
   const dim3 grid((unsigned)((a.rows + rows_per_block - 1) / rows_per_block));
-  if (a.dtype == 1) return a.V == 64 ? launch_v<bf16, 64>(a, grid, s) : launch_v<bf16, 128>(a, grid, s);
-  return a.V == 64 ? launch_v<float, 64>(a, grid, s) : launch_v<float, 128>(a, grid, s);
+  if (a.dtype == 1) {
+    if (a.V == 64) return launch_v<bf16, 64>(a, grid, s);
+    return a.V == 128 ? launch_v<bf16, 128>(a, grid, s) : launch_v<bf16, 256>(a, grid, s);
+  }
+  if (a.V == 64) return launch_v<float, 64>(a, grid, s);
+  return a.V == 128 ? launch_v<float, 128>(a, grid, s) : launch_v<float, 256>(a, grid, s);
 }
 
 }  // namespace kda

@@ -36,7 +36,8 @@ constexpr int kThreads = 256;
 // The chunk-factor kernel's workgroup: its LDS (about 50 KB for C = 64) leaves
 // room for three workgroups per CU, so 512 threads give each SIMD six waves.
 constexpr int kChunkThreads = 512;
-constexpr int kMaxD = 128;  // largest head dimension
+constexpr int kMaxD = 128;  // largest head dimension of the default instantiations
+constexpr int kWideD = 256; // the wide instantiations (head dim 256, chunks of 16 or 32)
 
 __device__ inline float wave_sum(float x) {
 #pragma unroll
@@ -64,7 +65,7 @@ __device__ inline float gate_value(float x, float A, int gate, float lb) {
 // bound by the bytes in flight per CU, not by its arithmetic).
 constexpr int kProTPW = 4;
 
-template <typename Tin>
+template <typename Tin, int KM>
 __global__ __launch_bounds__(kThreads) void k_prologue_valu(
     const Tin* __restrict__ q, const Tin* __restrict__ k, const Tin* __restrict__ gate,
     const Tin* __restrict__ beta, const float* __restrict__ a_log,
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(kThreads) void k_prologue_valu(
   const int lane = threadIdx.x & 63;
   const int64_t th0 = ((int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * kProTPW;
   if (th0 >= n_th) return;
-  constexpr int M = kMaxD / 64;
+  constexpr int M = KM / 64;
   float vq[kProTPW][M], vk[kProTPW][M], vx[kProTPW][M], bl[kProTPW];
   // every load of the wave's token-heads is issued up front (past the end,
   // the last token-head is read again and nothing is stored)
@@ -126,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void k_prologue_valu(
 // One workgroup per chunk-head (flattened j*H + h).  The decay factors use the
 // hardware exponential (__expf, about one ulp; all arguments are <= 0).  gamma's rows are padded
 // to K+1 floats: the pairwise products read gamma of row i with lanes over i.
-template <typename Tin, int C>
+template <typename Tin, int C, int KM>
 __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
   constexpr int kThreads = kChunkThreads;  // the loops below stride by the workgroup
   const int H = a.H, K = a.K, V = a.V;
@@ -136,10 +137,10 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
   const int tid = threadIdx.x;
   const int tok0 = a.chunk_tok[j], L = a.chunk_len[j];
 
-  __shared__ float sG[C][kMaxD + 1];  // gamma, later X = beta k^ exp(gamma)
+  __shared__ float sG[C][KM + 1];  // gamma, later X = beta k^ exp(gamma)
   __shared__ float sA[C][C + 1];   // Akk, then Tm in place
   __shared__ float sB[C];
-  __shared__ float sGL[kMaxD];     // gamma_L, the chunk's last row of gamma
+  __shared__ float sGL[KM];     // gamma_L, the chunk's last row of gamma
   __shared__ float sDg[2][C == 64 ? C : 1];  // halves of the diagonal Aqk sums
   const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
@@ -416,7 +417,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
   float* Qt = (float*)a.Qt + chb * C * K;
   float* Kb = (float*)a.Kb + chb * C * K;
   {
-    constexpr int NP = (C * kMaxD / 4 + kThreads - 1) / kThreads;
+    constexpr int NP = (C * KM / 4 + kThreads - 1) / kThreads;
     f32x4 q4[NP], k4[NP];
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
@@ -481,7 +482,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_chunk_valu(FwdArgs a) {
   // Diag(beta) V to LDS in X's place (every load issued before the first
   // store), then U's rows read it from there
   const Tin* v = (const Tin*)a.v;
-  constexpr int NV = (C * kMaxD + kThreads - 1) / kThreads;
+  constexpr int NV = (C * KM + kThreads - 1) / kThreads;
   float vv[NV];
 #pragma unroll
   for (int u = 0; u < NV; ++u) {
@@ -697,27 +698,29 @@ hipError_t run_prep(const FwdArgs& a, hipStream_t s) {
   if (n_th > 0) {
     const int64_t per_block = (kThreads / 64) * kProTPW;
     const int64_t blocks = (n_th + per_block - 1) / per_block;
-    hipLaunchKernelGGL(k_prologue_valu<Tin>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((k_prologue_valu<Tin, kMaxD>), dim3((unsigned)blocks), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.gate, (const Tin*)a.beta,
                        a.a_log, a.dt_bias, n_th, a.H, a.HK, a.K, a.gate_form, a.lb, a.qn, a.kn, a.g, a.bt);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   if (a.NT > 0) {
-    hipLaunchKernelGGL((k_chunk_valu<Tin, C>), dim3((unsigned)((int64_t)a.NT * a.H)),
+    hipLaunchKernelGGL((k_chunk_valu<Tin, C, kMaxD>), dim3((unsigned)((int64_t)a.NT * a.H)),
                        dim3(kChunkThreads), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   return hipSuccess;
 }
 
-template <typename Tin, int C>
+// KM: the widest head dimension the instantiation handles (kMaxD, or kWideD
+// for head dim 256 with chunks of 16 or 32, whose state pass stages fit LDS)
+template <typename Tin, int C, int KM>
 hipError_t run(const FwdArgs& a, hipStream_t s) {
   const int64_t n_th = (int64_t)a.B * a.T * a.H;
   mark(a, kStagePrologue, 0, s);
   if (n_th > 0) {
     const int64_t per_block = (kThreads / 64) * kProTPW;
     const int64_t blocks = (n_th + per_block - 1) / per_block;
-    hipLaunchKernelGGL(k_prologue_valu<Tin>, dim3((unsigned)blocks), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL((k_prologue_valu<Tin, KM>), dim3((unsigned)blocks), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.gate, (const Tin*)a.beta,
                        a.a_log, a.dt_bias, n_th, a.H, a.HK, a.K, a.gate_form, a.lb, a.qn, a.kn, a.g, a.bt);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
@@ -725,7 +728,7 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
   mark(a, kStagePrologue, 1, s);
   mark(a, kStageChunk, 0, s);
   if (a.NT > 0) {
-    hipLaunchKernelGGL((k_chunk_valu<Tin, C>), dim3((unsigned)((int64_t)a.NT * a.H)),
+    hipLaunchKernelGGL((k_chunk_valu<Tin, C, KM>), dim3((unsigned)((int64_t)a.NT * a.H)),
                        dim3(kChunkThreads), 0, s, a);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
@@ -741,10 +744,17 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
     };
     using K64 = std::integral_constant<int, 64>;
     using K128 = std::integral_constant<int, 128>;
+    using K256 = std::integral_constant<int, 256>;
     using S0 = std::false_type;
     using S1 = std::true_type;
-    if (a.K == 64) a.summary ? launch(K64{}, S1{}) : launch(K64{}, S0{});
-    else a.summary ? launch(K128{}, S1{}) : launch(K128{}, S0{});
+    if constexpr (KM == kWideD) {
+      if (a.K == 256) a.summary ? launch(K256{}, S1{}) : launch(K256{}, S0{});
+      else if (a.K == 64) a.summary ? launch(K64{}, S1{}) : launch(K64{}, S0{});
+      else a.summary ? launch(K128{}, S1{}) : launch(K128{}, S0{});
+    } else {
+      if (a.K == 64) a.summary ? launch(K64{}, S1{}) : launch(K64{}, S0{});
+      else a.summary ? launch(K128{}, S1{}) : launch(K128{}, S0{});
+    }
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   mark(a, kStageState, 1, s);
@@ -753,10 +763,15 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
 
 template <typename Tin>
 hipError_t run_c(const FwdArgs& a, hipStream_t s) {
+  if (a.K > kMaxD || a.V > kMaxD) {
+    // head dim 256: chunks of 16 or 32 only (the host rejects 64)
+    if (a.C == 16) return run<Tin, 16, kWideD>(a, s);
+    return run<Tin, 32, kWideD>(a, s);
+  }
   switch (a.C) {
-    case 16: return run<Tin, 16>(a, s);
-    case 32: return run<Tin, 32>(a, s);
-    default: return run<Tin, 64>(a, s);
+    case 16: return run<Tin, 16, kMaxD>(a, s);
+    case 32: return run<Tin, 32, kMaxD>(a, s);
+    default: return run<Tin, 64, kMaxD>(a, s);
   }
 }
 

@@ -57,6 +57,9 @@ def _status(lib, p):
     (dict(lower_bound=-math.inf), kda.EINVAL, "lower_bound must be negative"),
     (dict(K=96), kda.EUNSUPPORTED, "head dims"),
     (dict(V=32), kda.EUNSUPPORTED, "head dims"),
+    (dict(K=512), kda.EUNSUPPORTED, "head dims"),
+    (dict(K=256), kda.EUNSUPPORTED, "head dim 256 runs with chunk_size 16 or 32"),
+    (dict(V=256, chunk_size=64), kda.EUNSUPPORTED, "head dim 256 runs with chunk_size 16 or 32"),
     (dict(B=0), kda.EINVAL, "bad shape"),
     (dict(T=-1), kda.EINVAL, "bad shape"),
     (dict(H=0), kda.EINVAL, "bad shape"),
@@ -348,3 +351,15 @@ def test_python_norm_binding_checks_shapes():
         kda.gated_rms_norm(o, o)
     with pytest.raises(ValueError, match="activation"):
         kda.gated_rms_norm(o, o, activation="tanh")
+
+
+def test_head_dim_256_paths_and_backward(lib):
+    """Head dim 256 runs the vector-ALU kernels (chunks of 16 or 32); the
+    matrix-core paths and the backward keep head dims 64 and 128."""
+    for kw in (dict(K=256, chunk_size=32), dict(V=256, chunk_size=16), dict(K=256, V=256, chunk_size=32)):
+        assert _status(lib, _p(**kw))[0] == kda.OK, kw
+        assert lib.kda_fwd_path(ctypes.byref(_p(**kw))) == 0, kw   # KDA_PATH_VALU
+    assert lib.kda_fwd_path(ctypes.byref(_p(chunk_size=32))) == 1  # bf16, d=64: matrix cores
+    st = ctypes.c_int(0)
+    assert lib.kda_bwd_workspace_size(ctypes.byref(_p(K=256, chunk_size=32)), ctypes.byref(st)) == 0
+    assert st.value == kda.EUNSUPPORTED and "backward" in lib.kda_last_error().decode()
