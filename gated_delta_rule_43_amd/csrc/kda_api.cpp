@@ -348,6 +348,28 @@ kda_status check_conv(const kda_problem* p, const kda_short_conv* conv, const vo
   return KDA_OK;
 }
 
+// By default the standalone pass convolves q, k and v into the workspace and
+// the forward reads the results.  KDA_CONV_FUSED=1 makes the matrix-core
+// kernels apply a width-4 convolution as they load q, k and v instead (bf16,
+// weights and biases 16-byte aligned); both round each convolved value to the
+// input dtype in the same order of operations, so the results are identical.
+// Measured slower: on the throughput shape (B=4, T=16384, H=32, d=128) the
+// forward with the convolution takes 3.04 ms on load against 2.24 ms with the
+// standalone pass (1.65 ms without any convolution), on short documents (d=64)
+// 2.45 against 1.51 ms: in the chunk kernel's row layout every lane reloads its
+// channels' weights and the convolution adds about 17 VALU operations per
+// element to a kernel that is already mostly VALU-busy, while the standalone pass
+// streams at HBM speed.
+bool conv_on_load(const kda_problem* p, const kda_short_conv* conv, int path) {
+  if (!conv || conv->width != 4 || path == kPathValu || p->dtype != KDA_BF16) return false;
+  const float* fp[] = {conv->q_weight, conv->k_weight, conv->v_weight,
+                       conv->q_bias, conv->k_bias, conv->v_bias};
+  for (const float* f : fp)
+    if (f && !aligned(f, 16)) return false;
+  const char* env = std::getenv("KDA_CONV_FUSED");
+  return env && std::atoi(env) != 0;
+}
+
 // kda_fwd, optionally after the short convolution of q, k and v.  path < 0:
 // the library's choice; otherwise the path whose workspace the caller sized.
 // The gated output norm needs whole output rows: the fused kernel's consumer
@@ -389,12 +411,14 @@ kda_status fwd_impl(const kda_problem* p, const kda_short_conv* conv, const void
   }
   const Layout L = path < 0 ? layout(p, false) : layout_for(p, path);
   ConvBuffers cb;
+  bool on_load = false;
   if (conv) {
     st = check_conv(p, conv, q, k, v);
     if (st != KDA_OK) return st;
-    cb = conv_buffers(p, L.total);
+    on_load = conv_on_load(p, conv, L.path);
+    if (!on_load) cb = conv_buffers(p, L.total);
   }
-  st = check_ws(conv ? cb.total : L.total, workspace, workspace_bytes);
+  st = check_ws(conv && !on_load ? cb.total : L.total, workspace, workspace_bytes);
   if (st != KDA_OK) return st;
   if (L.path != kPathValu) {
     const void* vec[] = {q, k, v, gate, o};
@@ -403,7 +427,7 @@ kda_status fwd_impl(const kda_problem* p, const kda_short_conv* conv, const void
         return fail(KDA_EINVAL, "bf16 q, k, v, gate and o must be 16-byte aligned");
   }
   hipStream_t s = (hipStream_t)stream;
-  if (conv && (long long)p->B * p->T > 0) {
+  if (conv && !on_load && (long long)p->B * p->T > 0) {
     char* w = (char*)workspace;
     kda::ConvArgs c{};
     c.B = p->B; c.T = p->T; c.N = p->N; c.dtype = p->dtype; c.width = conv->width;
@@ -424,6 +448,11 @@ kda_status fwd_impl(const kda_problem* p, const kda_short_conv* conv, const void
   a.a_log = a_log; a.dt_bias = dt_bias; a.init = initial_state;
   a.o = o; a.fin = final_state; a.summary = 0;
   a.events = stage_events;
+  if (on_load) {
+    a.conv = 1;
+    a.conv_wq = conv->q_weight; a.conv_wk = conv->k_weight; a.conv_wv = conv->v_weight;
+    a.conv_bq = conv->q_bias; a.conv_bk = conv->k_bias; a.conv_bv = conv->v_bias;
+  }
   // The norm applied inside the state pass needs one workgroup per (sequence,
   // head) holding whole rows; on every measured shape that costs the pass
   // more than a separate pass over o costs (throughput shape 2.52 vs 1.97 ms,

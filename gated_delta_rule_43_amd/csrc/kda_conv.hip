@@ -49,7 +49,10 @@ __device__ __forceinline__ void store16(bf16* p, const float* v) {
   *(uint4*)p = make_uint4(u[0], u[1], u[2], u[3]);
 }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.f + __expf(-z)); }
+// z sigmoid(z) with the hardware exponential and reciprocal (each about 1 ulp
+// in fp32; the result is rounded to the input dtype).  The matrix-core forward
+// that convolves on load computes the same expression, so both agree bit for bit.
+__device__ __forceinline__ float silu(float z) { return z * __builtin_amdgcn_rcpf(1.f + __expf(-z)); }
 
 // Sequence bounds of flat token t: [s0, s1) is the part of t's sequence from
 // its first token on.  Packed rows search cu_seqlens (largest n with

@@ -88,6 +88,13 @@ struct FwdArgs {
   float norm_eps;
   const void* norm_gate; // [B,T,H,V], dtype as q
   const float* norm_w;   // [V] or null for ones
+  // optional short convolution of width 4 + SiLU of q, k and v applied as the
+  // matrix-core kernels load them (conv != 0; q, k, v are then the raw
+  // projections): weights [C, 4] fp32 (tap 3 weights the current token),
+  // biases [C] fp32 or null; C = HK*K for q and k, H*V for v.  Each convolved
+  // value is rounded to the input dtype, as the standalone convolution stores it.
+  int conv;
+  const float *conv_wq, *conv_wk, *conv_wv, *conv_bq, *conv_bk, *conv_bv;
   // optional stage timing: hipEvent_t handles, [2 * kNumStages], entries may be null
   void* const* events;
 };

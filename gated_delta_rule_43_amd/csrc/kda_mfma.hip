@@ -159,6 +159,58 @@ __device__ __forceinline__ bf16x8 select_frag(int g, int n, int half) {
 }
 
 // ---------------------------------------------------------------------------
+// Short convolution of width 4 + SiLU applied as q, k and v are loaded
+// (FwdArgs::conv).  The lanes 16g + n of a 16-lane row group hold the same
+// channels of token rows r0 + n; the inputs of rows r - 1, r - 2 and r - 3
+// come from the lanes below (DPP row shifts) and, for the group's first three
+// rows, from hx: each lane's copy of row r0 + n - 3.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void window3(uint32_t x, uint32_t hx, uint32_t& r1, uint32_t& r2,
+                                        uint32_t& r3) {
+  const int xi = (int)x, hi = (int)hx;
+  // lane n < s takes row r0 + n - s from the halo copy of lane n - s + 3
+  const int h2 = __builtin_amdgcn_update_dpp(0, hi, 0x102, 0xF, 0xF, false);  // row_shl:2
+  const int h1 = __builtin_amdgcn_update_dpp(0, hi, 0x101, 0xF, 0xF, false);  // row_shl:1
+  // lane n >= s takes lane n - s (row_shr:s); the others keep the halo value
+  r1 = (uint32_t)__builtin_amdgcn_update_dpp(h2, xi, 0x111, 0xF, 0xF, false);
+  r2 = (uint32_t)__builtin_amdgcn_update_dpp(h1, xi, 0x112, 0xF, 0xF, false);
+  r3 = (uint32_t)__builtin_amdgcn_update_dpp(hi, xi, 0x113, 0xF, 0xF, false);
+}
+// row r0 + n - 3 from the previous 16-row block of the same lanes (row_shl:13)
+__device__ __forceinline__ uint2 halo_from_block(uint2 prev) {
+  return make_uint2((uint32_t)__builtin_amdgcn_update_dpp(0, (int)prev.x, 0x10D, 0xF, 0xF, false),
+                    (uint32_t)__builtin_amdgcn_update_dpp(0, (int)prev.y, 0x10D, 0xF, 0xF, false));
+}
+// Four channels of one row (x: 4 bf16; hx its halo as above):
+//   y = silu(b + w3 x_r + w2 x_{r-1} + w1 x_{r-2} + w0 x_{r-3}),
+// with w = wt[4 e .. 4 e + 3] the taps of channel e and b = bias[e] (0 without
+// a bias), in the standalone convolution's order of operations and with its
+// SiLU (z times the hardware reciprocal of 1 + e^-z), rounded to bf16 as it
+// stores it (f32_to_bf16).  Returns the four results as 4 bf16.
+__device__ __forceinline__ uint2 conv4_silu_bf16(uint2 x, uint2 hx, const float* wt, const float* bias) {
+  uint32_t a1, a2, a3, c1, c2, c3;
+  window3(x.x, hx.x, a1, a2, a3);
+  window3(x.y, hx.y, c1, c2, c3);
+  const uint32_t back[4][2] = {{x.x, x.y}, {a1, c1}, {a2, c2}, {a3, c3}};  // rows r - s
+  uint32_t outw[2] = {0u, 0u};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float4 w4 = *(const float4*)(wt + 4 * e);
+    auto xs = [&](int sb) {
+      const uint32_t u = back[sb][e >> 1];
+      return __uint_as_float((e & 1) ? (u & 0xffff0000u) : (u << 16));
+    };
+    float acc = fmaf(w4.w, xs(0), bias ? bias[e] : 0.f);
+    acc = fmaf(w4.z, xs(1), acc);
+    acc = fmaf(w4.y, xs(2), acc);
+    acc = fmaf(w4.x, xs(3), acc);
+    const float yy = acc * __builtin_amdgcn_rcpf(1.f + __expf(-acc));
+    outw[e >> 1] |= (uint32_t)f32_to_bf16(yy) << (16 * (e & 1));
+  }
+  return make_uint2(outw[0], outw[1]);
+}
+
+// ---------------------------------------------------------------------------
 // Chunk record layout (bytes, per chunk-head), shared by both kernels.
 // ---------------------------------------------------------------------------
 template <int K, int V>
@@ -200,8 +252,9 @@ enum {
 // One chunk-head.  EXACT = false: the common kernel; a 16-row block whose
 // decay exceeds the factorised range makes the workgroup append the chunk-head
 // to a fix-up list instead.  EXACT = true: the fix-up, with the exact per-pair
-// path on such blocks.  GATE: the gate form (FwdArgs::gate_form).
-template <int K, int V, bool EXACT, int GATE>
+// path on such blocks.  GATE: the gate form (FwdArgs::gate_form).  CONV: q, k
+// and v are the raw projections, convolved on load (FwdArgs::conv).
+template <int K, int V, bool EXACT, int GATE, bool CONV>
 __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, const int h,
                                            const int tok0, const int L, char* const rec,
                                            const bool keep_ok = false) {
@@ -219,6 +272,10 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
   // paid again after them
   const bf16 braw = ((const bf16*)a.beta)[th];
   const float alog = a.a_log[h];
+  // the convolution's window reaches back into the previous chunk unless this
+  // chunk starts its sequence (then the inputs before it count as zero)
+  const bool first = CONV && (jchunk == 0 || a.chunk_seq[jchunk - 1] != a.chunk_seq[jchunk]);
+  const int hk = h / (H / a.HK);  // the key head of q and k
 
   // the factor table (steps 3-5) and the diagonal Akk blocks (step 6) share storage
   __shared__ __attribute__((aligned(16))) float sFacMem[kNF * K];
@@ -241,20 +298,43 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
   // Loads q, k, gate of the lane's row at channels 32j + sig(g, e), normalises
   // q and k, applies the gate and scans it over the 16 rows of the block.
   // Used once up front and again by the exact diagonal path.
-  auto row_prologue = [&](float* qv, float* kv, float* lam) {
+  auto row_prologue = [&](float* qv, float* kv, float* lam) __attribute__((always_inline)) {
     const bf16* q = (const bf16*)a.q + thk * K;
     const bf16* k = (const bf16*)a.k + thk * K;
     const bf16* gt = (const bf16*)a.gate + th * K;
     const float* db = a.dt_bias + (int64_t)h * K;
+    // CONV: the halo row 16w + n - 3 (used by lanes n < 3): zero before the
+    // sequence start; rows past the chunk end read row 0 (they only feed rows
+    // past the chunk end)
+    const int hr = row - 3;
+    const bool hok = hr < 0 ? !first : hr < L;
+    const int64_t thh = (int64_t)(tok0 + (hok ? hr : 0)) * a.HK + hk;
+    auto conv_piece = [&](const bf16* xrow, const bf16* xhalo, const float* w, const float* b, int c,
+                          float* out) __attribute__((always_inline)) {
+      uint2 hx = *(const uint2*)(xhalo + c);
+      if (!hok) hx = make_uint2(0u, 0u);
+      const uint2 y = conv4_silu_bf16(*(const uint2*)(xrow + c), hx, w + ((int64_t)hk * K + c) * 4,
+                                      b ? b + (int64_t)hk * K + c : nullptr);
+      unpack4(y, out);
+    };
     // rows past the chunk end read the chunk's first row (th is clamped) and
     // are zeroed below through the norm scale and the gate select
 #pragma unroll
     for (int j = 0; j < NKJ; ++j) {
       const int c0 = 32 * j + 4 * g, c1 = c0 + 16;
-      load4_bf16(q + c0, qv + 8 * j);
-      load4_bf16(q + c1, qv + 8 * j + 4);
-      load4_bf16(k + c0, kv + 8 * j);
-      load4_bf16(k + c1, kv + 8 * j + 4);
+      if (CONV) {
+        const bf16* qh = (const bf16*)a.q + thh * K;
+        const bf16* kh = (const bf16*)a.k + thh * K;
+        conv_piece(q, qh, a.conv_wq, a.conv_bq, c0, qv + 8 * j);
+        conv_piece(q, qh, a.conv_wq, a.conv_bq, c1, qv + 8 * j + 4);
+        conv_piece(k, kh, a.conv_wk, a.conv_bk, c0, kv + 8 * j);
+        conv_piece(k, kh, a.conv_wk, a.conv_bk, c1, kv + 8 * j + 4);
+      } else {
+        load4_bf16(q + c0, qv + 8 * j);
+        load4_bf16(q + c1, qv + 8 * j + 4);
+        load4_bf16(k + c0, kv + 8 * j);
+        load4_bf16(k + c1, kv + 8 * j + 4);
+      }
       load4_bf16(gt + c0, lam + 8 * j);
       load4_bf16(gt + c1, lam + 8 * j + 4);
       const float4 d0 = *(const float4*)(db + c0), d1 = *(const float4*)(db + c1);
@@ -506,7 +586,7 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
   // this wave's value-pair job (at most one): its V rows are fetched now, so
   // that the triangular solve hides their latency
   // (rows past the chunk end read row 0 and are zeroed by their beta = 0)
-  uint2 vraw[4][2];
+  uint2 vraw[4][2], vhalo[2];
   if (upair >= 0) {
 #pragma unroll
     for (int I = 0; I < 4; ++I) {
@@ -514,6 +594,14 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
       const bf16* vp = (const bf16*)a.v + ((int64_t)(tok0 + ri) * H + h) * V + 32 * upair + 4 * g;
       vraw[I][0] = *(const uint2*)vp;
       vraw[I][1] = *(const uint2*)(vp + 16);
+    }
+    if (CONV) {
+      // the rows before the chunk (lanes n < 3), zero before the sequence start
+      const int hr = n - 3;
+      const bool hok = hr < 0 ? !first : hr < L;
+      const bf16* vp = (const bf16*)a.v + ((int64_t)(tok0 + (hok ? hr : 0)) * H + h) * V + 32 * upair + 4 * g;
+      vhalo[0] = hok ? *(const uint2*)vp : make_uint2(0u, 0u);
+      vhalo[1] = hok ? *(const uint2*)(vp + 16) : make_uint2(0u, 0u);
     }
   }
 
@@ -657,6 +745,21 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
       }
     } else {
       const int p = job - NKJ;
+      if (CONV) {
+        // convolve the V rows in place, last block first: block I's halo is
+        // block I - 1's raw rows
+#pragma unroll
+        for (int q2 = 0; q2 < 2; ++q2) {
+          const int64_t c = (int64_t)h * V + 32 * p + 16 * q2 + 4 * g;
+          const float* wv = a.conv_wv + c * 4;
+          const float* bv = a.conv_bv ? a.conv_bv + c : nullptr;
+#pragma unroll
+          for (int I = 3; I >= 0; --I) {
+            const uint2 hx = I > 0 ? halo_from_block(vraw[I - 1][q2]) : vhalo[q2];
+            vraw[I][q2] = conv4_silu_bf16(vraw[I][q2], hx, wv, bv);
+          }
+        }
+      }
       f32x4 did[4][2];
 #pragma unroll
       for (int I = 0; I < 4; ++I) {
@@ -732,7 +835,7 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
   }
 }
 
-template <int K, int V, int GATE>
+template <int K, int V, int GATE, bool CONV>
 __global__ __launch_bounds__(kThreads, 3) void k_chunk_mfma(FwdArgs a) {
   const unsigned wid = blockIdx.x, H = (unsigned)a.H;
   const int jchunk = (int)(wid / H), h = (int)(wid % H);
@@ -746,19 +849,19 @@ __global__ __launch_bounds__(kThreads, 3) void k_chunk_mfma(FwdArgs a) {
   const int sq = a.chunk_seq[jchunk];
   const bool keep_ok = !a.summary && !a.norm && a.init == nullptr &&
                        a.seq_chunk0[sq + 1] - a.seq_chunk0[sq] == 1;
-  chunk_body<K, V, false, GATE>(a, jchunk, h, tok0, L,
+  chunk_body<K, V, false, GATE, CONV>(a, jchunk, h, tok0, L,
                                 (char*)a.rec + ((int64_t)jchunk * a.H + h) * Rec<K, V>::kBytes,
                                 keep_ok);
 }
 
 // Fix-up pass: recomputes the listed chunk-heads with the exact diagonal path.
-template <int K, int V, int GATE>
+template <int K, int V, int GATE, bool CONV>
 __global__ __launch_bounds__(kThreads) void k_chunk_mfma_exact(FwdArgs a) {
   const int count = *a.exact_count;
   for (int i = blockIdx.x; i < count; i += gridDim.x) {
     const int ch = a.exact_list[i];
     const int jchunk = ch / a.H;
-    chunk_body<K, V, true, GATE>(a, jchunk, ch % a.H, a.chunk_tok[jchunk], a.chunk_len[jchunk],
+    chunk_body<K, V, true, GATE, CONV>(a, jchunk, ch % a.H, a.chunk_tok[jchunk], a.chunk_len[jchunk],
                                  (char*)a.rec + (int64_t)ch * Rec<K, V>::kBytes);
     __syncthreads();
   }
@@ -775,7 +878,7 @@ __global__ __launch_bounds__(kThreads) void k_chunk_mfma_exact(FwdArgs a) {
 // with S and Delta as bf16 hi + lo pairs in the state's own products.  Nothing
 // but q, k, v, gate, beta, the states and o touches HBM.  Blocks whose decay
 // leaves the factorised range take the exact per-pair path in place.
-template <int K, int V, int GATE>
+template <int K, int V, int GATE, bool CONV>
 __global__ __launch_bounds__(kThreads, 1) void k_fused(FwdArgs a) {
   using R = Rec<K, V>;
   constexpr int NKJ = K / 32, NKT = K / 16, NVT = V / 16;
@@ -812,7 +915,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_fused(FwdArgs a) {
 
   for (int jc = jc0; jc < jc1; ++jc) {
     const int tok0 = a.chunk_tok[jc], L = a.chunk_len[jc];
-    chunk_body<K, V, true, GATE>(a, jc, h, tok0, L, sRec);
+    chunk_body<K, V, true, GATE, CONV>(a, jc, h, tok0, L, sRec);
     __syncthreads();
     bf16x8 fA[4][2];
 #pragma unroll
@@ -1868,14 +1971,19 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
     // chunk-heads whose in-block decay left the factorised range go to a fix-up
     // pass (rare; its grid is fixed and exits at once when the list is empty)
     const dim3 fix_grid((unsigned)std::min<int64_t>((int64_t)a.NT * a.H, 256));
-    auto launch_gate = [&](auto gc) {
+    auto launch_gate = [&](auto gc, auto cc) {
       constexpr int GATE = decltype(gc)::value;
-      hipLaunchKernelGGL((k_chunk_mfma<K, V, GATE>), grid, block, 0, s, a);
-      hipLaunchKernelGGL((k_chunk_mfma_exact<K, V, GATE>), fix_grid, block, 0, s, a);
+      constexpr bool CONV = decltype(cc)::value;
+      hipLaunchKernelGGL((k_chunk_mfma<K, V, GATE, CONV>), grid, block, 0, s, a);
+      hipLaunchKernelGGL((k_chunk_mfma_exact<K, V, GATE, CONV>), fix_grid, block, 0, s, a);
     };
-    if (a.gate_form == 1) launch_gate(std::integral_constant<int, 1>{});
-    else if (a.gate_form == 2) launch_gate(std::integral_constant<int, 2>{});
-    else launch_gate(std::integral_constant<int, 0>{});
+    auto launch_conv = [&](auto gc) {
+      if (a.conv) launch_gate(gc, std::true_type{});
+      else launch_gate(gc, std::false_type{});
+    };
+    if (a.gate_form == 1) launch_conv(std::integral_constant<int, 1>{});
+    else if (a.gate_form == 2) launch_conv(std::integral_constant<int, 2>{});
+    else launch_conv(std::integral_constant<int, 0>{});
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   mark(a, kStageChunk, 1, s);
@@ -1961,9 +2069,14 @@ hipError_t run_fused(const FwdArgs& a, hipStream_t s) {
   const int64_t wgs = (int64_t)a.N * a.H;
   if (wgs > 0) {
     const dim3 grid((unsigned)wgs), block(kThreads);
-    if (a.gate_form == 1) hipLaunchKernelGGL((k_fused<K, V, 1>), grid, block, 0, s, a);
-    else if (a.gate_form == 2) hipLaunchKernelGGL((k_fused<K, V, 2>), grid, block, 0, s, a);
-    else hipLaunchKernelGGL((k_fused<K, V, 0>), grid, block, 0, s, a);
+    auto launch_gate = [&](auto gc) {
+      constexpr int GATE = decltype(gc)::value;
+      if (a.conv) hipLaunchKernelGGL((k_fused<K, V, GATE, true>), grid, block, 0, s, a);
+      else hipLaunchKernelGGL((k_fused<K, V, GATE, false>), grid, block, 0, s, a);
+    };
+    if (a.gate_form == 1) launch_gate(std::integral_constant<int, 1>{});
+    else if (a.gate_form == 2) launch_gate(std::integral_constant<int, 2>{});
+    else launch_gate(std::integral_constant<int, 0>{});
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   mark(a, kStageState, 1, s);

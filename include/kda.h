@@ -363,7 +363,10 @@ size_t kda_fwd_short_conv_workspace_size(const kda_problem* p, kda_status* statu
  * q, k, v are the raw projections; the convolved tensors live in the
  * workspace (p->dtype, rounded once), and the forward then runs on them
  * exactly as kda_fwd.  All other arguments are those of kda_fwd; q, k and v
- * must be 16-byte aligned.
+ * must be 16-byte aligned.  (With the environment variable KDA_CONV_FUSED=1, a
+ * bf16 matrix-core forward with width 4 and 16-byte aligned weights convolves
+ * q, k and v as it loads them instead, with identical results; measured
+ * slower, so not the default.)
  */
 kda_status kda_fwd_short_conv(const kda_problem* p, const kda_short_conv* conv, const void* q,
                               const void* k, const void* v, const void* gate, const void* beta,

@@ -170,3 +170,107 @@ def test_fwd_short_conv_matches_conv_then_fwd():
                          cu_seqlens=cu, output_final_state=True)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(f1, f2)
+
+
+# KDA_CONV_FUSED=1: the matrix-core kernels apply a width-4 convolution as they
+# load q, k and v (by default, and with =0, the standalone pass runs first).
+# Both round each convolved value to bf16 in the same order of operations, so
+# the outputs must agree bit for bit.
+ON_LOAD_CASES = [
+    # (name, K, V, H, HV, B, T, lengths, chunk, lower_bound, init_std, bias, gate_shift)
+    ("rows_d128_init", 128, 128, 2, 2, 2, 300, None, 64, None, 0.3, True, 0.0),
+    ("short_docs_d64_zero_state", 64, 64, 2, 2, 1, 0, [1, 2, 3, 64, 65, 0, 130, 17], 64, None, None, False, 0.0),
+    ("k128_v64_grouped_chunk32", 128, 64, 2, 4, 2, 150, None, 32, None, 0.2, True, 0.0),
+    ("docs_d128_chunk16_lb", 128, 128, 2, 2, 1, 0, [40, 3, 77, 16, 15], 16, -5.0, None, True, 0.0),
+    ("k64_v128_rows", 64, 128, 3, 3, 1, 200, None, 64, None, 0.1, False, 0.0),
+    ("extreme_gates_exact_path", 128, 128, 2, 2, 1, 256, None, 64, None, 0.1, True, 40.0),
+]
+
+
+def _on_load_problem(case, seed):
+    name, K, V, H, HV, B, T, lengths, C, lb, init_std, bias, shift = case
+    if lengths is not None:
+        T = sum(lengths)
+    inp = _to_dev_problem(seed, B, T, H, K, V, HV, lengths, init_std)
+    if shift:
+        g = inp["gate"].float()
+        g[:, ::7] += shift      # single steps decaying by tens of nats
+        inp["gate"] = g.to(torch.bfloat16)
+        inp["a_log"] = torch.full_like(inp["a_log"], 0.5)
+    ws, bs = synthetic.short_conv_params(seed + 1, (H * K, H * K, HV * V), 4, bias)
+    ws = tuple(w.to(DEV) for w in ws)
+    bs = None if bs is None else tuple(None if b is None else b.to(DEV) for b in bs)
+    return inp, ws, bs, C, lb
+
+
+def _to_dev_problem(seed, B, T, H, K, V, HV, lengths, init_std):
+    inp = synthetic.random_problem(seed, B, T, H, K, V, dtype=torch.bfloat16, lengths=lengths,
+                                   HV=HV, init_std=init_std)
+    return to_device(inp)
+
+
+def _conv_fwd(inp, ws, bs, C, lb, workspace=None):
+    o, fin = kda.kda_fwd_short_conv(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"],
+                                    inp["a_log"], inp["dt_bias"], ws, bs, chunk_size=C,
+                                    lower_bound=lb, cu_seqlens=inp["cu_seqlens"],
+                                    initial_state=inp["initial_state"], output_final_state=True,
+                                    workspace=workspace)
+    torch.cuda.synchronize()
+    return o, fin
+
+
+@pytest.mark.parametrize("case", ON_LOAD_CASES, ids=[c[0] for c in ON_LOAD_CASES])
+def test_fwd_short_conv_on_load_matches_standalone(case, monkeypatch):
+    _banner("conv on load " + case[0])
+    inp, ws, bs, C, lb = _on_load_problem(case, 300 + ON_LOAD_CASES.index(case))
+    monkeypatch.setenv("KDA_CONV_FUSED", "0")
+    o0, f0 = _conv_fwd(inp, ws, bs, C, lb)
+    monkeypatch.setenv("KDA_CONV_FUSED", "1")
+    o1, f1 = _conv_fwd(inp, ws, bs, C, lb)
+    assert torch.equal(o1, o0), "output differs: max %.3g" % float((o1.float() - o0.float()).abs().max())
+    assert torch.equal(f1, f0), "final state differs: max %.3g" % float((f1 - f0).abs().max())
+    # the fused kernel (one workgroup per sequence and head) convolves on load too
+    monkeypatch.setenv("KDA_PATH", "fused")
+    o2, f2 = _conv_fwd(inp, ws, bs, C, lb)
+    monkeypatch.setenv("KDA_STATE_KS", "1")
+    monkeypatch.setenv("KDA_PATH", "mfma")
+    o3, f3 = _conv_fwd(inp, ws, bs, C, lb)
+    assert torch.equal(o2, o3) and torch.equal(f2, f3)
+
+
+def test_fwd_short_conv_on_load_needs_no_conv_buffers(monkeypatch):
+    """With the convolution applied on load the forward's own workspace is
+    enough; the standalone pass needs room for the convolved tensors."""
+    case = ON_LOAD_CASES[0]
+    inp, ws, bs, C, lb = _on_load_problem(case, 399)
+    monkeypatch.setenv("KDA_CONV_FUSED", "1")
+    B, T, H, K = inp["q"].shape
+    HV, V = inp["v"].shape[2], inp["v"].shape[3]
+    n = kda.fwd_workspace_size((B, T, H, K), V, chunk_size=C, HV=HV)
+    small = torch.empty(n, dtype=torch.uint8, device=DEV)
+    o1, f1 = _conv_fwd(inp, ws, bs, C, lb, workspace=small)
+    monkeypatch.setenv("KDA_CONV_FUSED", "0")
+    with pytest.raises(ValueError, match="workspace"):
+        _conv_fwd(inp, ws, bs, C, lb, workspace=small)
+    o0, f0 = _conv_fwd(inp, ws, bs, C, lb)
+    assert torch.equal(o1, o0) and torch.equal(f1, f0)
+
+
+def test_fwd_short_conv_on_load_throughput_shape_sampled(monkeypatch):
+    """Workload 3's shape at full size, width 4 with bias, convolved on load,
+    against the standalone convolution then kda_fwd (bit for bit)."""
+    monkeypatch.setenv("KDA_CONV_FUSED", "1")
+    w3 = synthetic.WORKLOADS[3]
+    _banner("conv on load, " + w3.name)
+    inp = synthetic.make_inputs(w3, DEV)
+    ws, bs = synthetic.short_conv_params(33, (w3.H * w3.K, w3.H * w3.K, w3.H * w3.V), 4, True)
+    ws = tuple(w.to(DEV) for w in ws)
+    bs = tuple(b.to(DEV) for b in bs)
+    args = (inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"], inp["a_log"], inp["dt_bias"], ws, bs)
+    o1, _ = kda.kda_fwd_short_conv(*args)
+    qc = kda.short_conv_silu(inp["q"], ws[0], bs[0])
+    kc = kda.short_conv_silu(inp["k"], ws[1], bs[1])
+    vc = kda.short_conv_silu(inp["v"], ws[2], bs[2])
+    o2, _ = kda.kda_fwd(qc, kc, vc, inp["gate"], inp["beta"], inp["a_log"], inp["dt_bias"])
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
