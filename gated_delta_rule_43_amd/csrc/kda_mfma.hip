@@ -843,12 +843,18 @@ __global__ __launch_bounds__(kThreads, 3) void k_chunk_mfma(FwdArgs a) {
   // bounds; they are issued together with the count, ahead of its test
   const int nt = *a.nt_dev;
   const int tok0 = a.chunk_tok[jchunk], L = a.chunk_len[jchunk];
+  // the sequences of this chunk and of its neighbours in the table, read with
+  // the entries above so that one memory latency covers them all (a chain
+  // through seq_chunk0 would cost a second one before the first barrier)
+  const int sq = a.chunk_seq[jchunk];
+  const int sq_prev = jchunk > 0 ? a.chunk_seq[jchunk - 1] : -1;
+  const int sq_next = a.chunk_seq[jchunk + 1 < a.NT ? jchunk + 1 : jchunk];
   asm volatile("" ::"s"(tok0), "s"(L));
   if (jchunk >= nt) return;
-  // a sequence of this one chunk that starts from a zero state is finished here
-  const int sq = a.chunk_seq[jchunk];
-  const bool keep_ok = !a.summary && !a.norm && a.init == nullptr &&
-                       a.seq_chunk0[sq + 1] - a.seq_chunk0[sq] == 1;
+  // a sequence of this one chunk that starts from a zero state is finished
+  // here (chunks of a sequence are consecutive in the table)
+  const bool single = sq_prev != sq && (jchunk + 1 >= nt || sq_next != sq);
+  const bool keep_ok = !a.summary && !a.norm && a.init == nullptr && single;
   chunk_body<K, V, false, GATE, CONV>(a, jchunk, h, tok0, L,
                                 (char*)a.rec + ((int64_t)jchunk * a.H + h) * Rec<K, V>::kBytes,
                                 keep_ok);
