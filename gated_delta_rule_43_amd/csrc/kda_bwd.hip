@@ -1139,6 +1139,84 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   __syncthreads();
 
   // ---- phase F: per element (r, c), the gradients of q^, k^ and gamma ----
+  // The pairwise sums over the chunk:
+  //   r1 = sum_{i<=r} P[r][i] k^_ic e^{g_rc - g_ic},  r2 likewise with Y,
+  //   c12 = sum_{rr>=r} (P[rr][r] q^_rr,c + Y[rr][r] k^_rr,c) e^{g_rr,c - g_rc}.
+  // C = 64: pairs inside a 16-row block take their exact per-pair factor (a
+  // split through the block boundary could overflow there); the blocks before
+  // and after run on the fp32 matrix cores with every factor referenced to a
+  // block boundary (G_R = g at row 16R-1 for the blocks before row block R,
+  // G'_R = g at its last row for the blocks after), so that all are <= 1:
+  //   r1 += e^{g_r - G_R} (P[R rows, <16R] (k^ e^{G_R - g}))
+  //   c12 += e^{G'_R - g_r} (P[>R, R cols]^T (q^ e^{g - G'_R}) + Y^T (k^ e^{g - G'_R})).
+  // Their tiles reach the element owners through the LDS that Tm used.
+  // The blocks' terms are summed first (per owner: x1 = r1, x2 = r2 + c12,
+  // x3 = q^ r1 + k^ (r2 - c12) of the off-diagonal blocks), then the in-block
+  // pairs, and each element's outputs
+  //   dq^ = e^g dq~ + r1,  dk^ = ekt + e^{g_L - g} dkb + r2 + c12,
+  //   dg = k^ ekt + q^ e^g dq~ - tkb + q^ r1 + k^ (r2 - c12).
+  float ox1[NE1], ox2[NE1], ox3[NE1];
+#pragma unroll
+  for (int m = 0; m < NE1; ++m) ox1[m] = ox2[m] = ox3[m] = 0.f;
+  if constexpr (C == 64) {
+    static_assert(RSTEP1 == 8 && NE1 == 8, "rows rb1 + 8m: two rows of each 16-row block per owner");
+    constexpr int NW = NT / 64, CG = K < 64 ? K : 64, NGRP = K / CG, CTG = CG / 16;
+    float (*stg)[16][CG + 1] = (float(*)[16][CG + 1])&sT[0][0];  // Tm is dead
+    static_assert(3 * 16 * (CG + 1) <= C * (C + 1), "the staged tiles fit where Tm was");
+    const int lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
+#pragma unroll 1
+    for (int R = 0; R < 4; ++R) {
+#pragma unroll 1
+      for (int grp = 0; grp < NGRP; ++grp) {
+        // jobs 0..CTG-1: r1 tiles, then r2, then c12, of this row block and column group
+        for (int job = w; job < 3 * CTG; job += NW) {
+          const int kind = job / CTG, ctl = job % CTG, col = 16 * (grp * CTG + ctl) + ln;
+          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+          float rowf[4] = {0.f, 0.f, 0.f, 0.f};
+          if (kind < 2) {
+            if (R > 0 && 16 * R < L) {  // rows before 16R are all inside the chunk
+              const float gR = sGam[16 * R - 1][col];
+              for (int kk = 0; kk < 16 * R; kk += 4) {
+                const int i = kk + lg;
+                const float bk = sKn[i][col] * __expf(gR - sGam[i][col]);
+                acc = mfma_f32(kind == 0 ? sP[16 * R + ln][i] : sY[16 * R + ln][i], bk, acc);
+              }
+#pragma unroll
+              for (int e = 0; e < 4; ++e) rowf[e] = __expf(sGam[16 * R + 4 * lg + e][col] - gR);
+            }
+          } else if (R < 3 && 16 * (R + 1) < L) {
+            // g is constant past the chunk end, and q^, k^ are zero there
+            const float gE = sGam[16 * R + 15][col];
+            for (int kk = 16 * (R + 1); kk < C; kk += 4) {
+              const int rr = kk + lg;
+              const float f = __expf(sGam[rr][col] - gE);
+              acc = mfma_f32(sP[rr][16 * R + ln], sQn[rr][col] * f, acc);
+              acc = mfma_f32(sY[rr][16 * R + ln], sKn[rr][col] * f, acc);
+            }
+#pragma unroll
+            for (int e = 0; e < 4; ++e) rowf[e] = __expf(gE - sGam[16 * R + 4 * lg + e][col]);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) stg[kind][4 * lg + e][16 * ctl + ln] = rowf[e] * acc[e];
+        }
+        __syncthreads();
+        // the owners of this block's rows (m = 2R, 2R+1) in this column group
+        // (both conditions wave-uniform; m stays a compile-time index)
+        if (c1 / CG == grp) {
+#pragma unroll
+          for (int m = 0; m < NE1; ++m) {
+            if ((m >> 1) != R) continue;
+            const int rl = rb1 + 8 * (m & 1), cl = c1 - grp * CG, r = 16 * R + rl;
+            const float x1 = stg[0][rl][cl], x2 = stg[1][rl][cl], x3 = stg[2][rl][cl];
+            ox1[m] = x1;
+            ox2[m] = x2 + x3;
+            ox3[m] = sQn[r][c1] * x1 + sKn[r][c1] * (x2 - x3);
+          }
+        }
+        __syncthreads();
+      }
+    }
+  }
   float dgm[NE1], tkm[NE1];
 #pragma unroll
   for (int m = 0; m < NE1; ++m) {
@@ -1147,25 +1225,27 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     const int r = __builtin_amdgcn_readfirstlane(rb1 + RSTEP1 * m), c = c1;
     dgm[m] = tkm[m] = 0.f;
     if (r >= L) continue;
+    const int i0 = C == 64 ? (r & ~15) : 0;              // first column summed here
+    const int rr1 = C == 64 ? min((r | 15) + 1, L) : L;  // past the last row summed here
     const float q = sQn[r][c], kk = sKn[r][c];
     const float gm = sGam[r][c], egm = __expf(gm), ekb = __expf(sGam[L - 1][c] - gm);
     float r1 = 0.f, r2 = 0.f;
 #pragma unroll 4
-    for (int i = 0; i <= r; ++i) {
+    for (int i = i0; i <= r; ++i) {
       const float ke = sKn[i][c] * __expf(gm - sGam[i][c]);
       r1 = fmaf(sP[r][i], ke, r1);
       r2 = fmaf(sY[r][i], ke, r2);
     }
     float c12 = 0.f;
 #pragma unroll 4
-    for (int rr = r; rr < L; ++rr) {
+    for (int rr = r; rr < rr1; ++rr) {
       const float e = __expf(sGam[rr][c] - gm);
       c12 = fmaf(sP[rr][r] * sQn[rr][c] + sY[rr][r] * sKn[rr][c], e, c12);
     }
     const float tkb = kk * ekb * dkb[m];
-    b.dqh[th(r) * K + c] = egm * dqs[m] + r1;
-    b.dkh[th(r) * K + c] = ekt[m] + ekb * dkb[m] + r2 + c12;
-    dgm[m] = kk * ekt[m] + q * egm * dqs[m] - tkb + q * r1 + kk * r2 - kk * c12;
+    b.dqh[th(r) * K + c] = egm * dqs[m] + r1 + ox1[m];
+    b.dkh[th(r) * K + c] = ekt[m] + ekb * dkb[m] + r2 + c12 + ox2[m];
+    dgm[m] = kk * ekt[m] + q * egm * dqs[m] - tkb + q * r1 + kk * r2 - kk * c12 + ox3[m];
     tkm[m] = tkb;
   }
   __syncthreads();  // q^, k^ are dead
