@@ -1051,19 +1051,23 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
 
   // ---- phase D: dbeta (first part), Z = Tm^T dT (bb < r), and through dW the
   //      K~ term of k^ and gamma (kept in the element owner's registers) ----
-  for (int r = tid; r < L; r += NT) {
-    float acc = 0.f;
-    for (int aa = r; aa < L; ++aa) acc = fmaf(sT[aa][r], sY[aa][r], acc);
-    sDb[r] = acc;
-  }
+  // (C = 64: dbeta's first part and Z come from one product on the matrix
+  // cores below, once K~ and dW are dead)
   float zv[NE2];
+  if constexpr (C != 64) {
+    for (int r = tid; r < L; r += NT) {
+      float acc = 0.f;
+      for (int aa = r; aa < L; ++aa) acc = fmaf(sT[aa][r], sY[aa][r], acc);
+      sDb[r] = acc;
+    }
 #pragma unroll
-  for (int m = 0; m < NE2; ++m) {
-    const int r = rb2 + RSTEP2 * m;
-    float acc = 0.f;
-    if (r < L && i2 < r)
-      for (int aa = r; aa < L; ++aa) acc = fmaf(sT[aa][r], sY[aa][i2], acc);
-    zv[m] = sB[i2] * acc;
+    for (int m = 0; m < NE2; ++m) {
+      const int r = rb2 + RSTEP2 * m;
+      float acc = 0.f;
+      if (r < L && i2 < r)
+        for (int aa = r; aa < L; ++aa) acc = fmaf(sT[aa][r], sY[aa][i2], acc);
+      zv[m] = sB[i2] * acc;
+    }
   }
   float ekt[NE1];  // e^gamma beta (Tm^T dW): the K~ term of dk^ (and, times k^, of dgamma)
   if constexpr (C == 64) {
@@ -1097,10 +1101,33 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     }
   }
   __syncthreads();  // K~ and dW are dead: Z and q^ take their places
+  if constexpr (C == 64) {
+    // (Tm^T Y) on fp32 matrix cores, one 16 x 16 tile per wave and step:
+    // Tm[aa][r] is zero for aa < r, so a row tile's k-steps start at its own
+    // block; rows aa past the chunk end are masked.  Z = (Tm^T Y)[r][i] beta_i
+    // for i < r (zero elsewhere), dbeta's first part is the diagonal.
+    const int lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
+    for (int t = w; t < 16; t += NT / 64) {
+      const int rt = t / 4, it = t % 4;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (it <= rt)
+        for (int aa = 16 * rt; aa < C; aa += 4) {
+          const int ak = aa + lg;
+          acc = mfma_f32(sT[ak][16 * rt + ln], ak < L ? sY[ak][16 * it + ln] : 0.f, acc);
+        }
 #pragma unroll
-  for (int m = 0; m < NE2; ++m) {
-    const int r = rb2 + RSTEP2 * m;
-    if (r < C) sZ[r][i2] = zv[m];
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * lg + e, i = 16 * it + ln;
+        sZ[r][i] = (i < r && r < L) ? sB[i] * acc[e] : 0.f;
+        if (i == r && r < L) sDb[r] = acc[e];
+      }
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < NE2; ++m) {
+      const int r = rb2 + RSTEP2 * m;
+      if (r < C) sZ[r][i2] = zv[m];
+    }
   }
 #pragma unroll
   for (int e = tid; e < C * K / 4; e += NT) {
@@ -1111,13 +1138,35 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   __syncthreads();
 
   // ---- phase E: dN = -Z Tm^T (i < r), dAkk = beta_r dN -> sY; dbeta (second part) ----
+  if constexpr (C == 64) {
+    // (Z Tm^T)[r][i] on fp32 matrix cores (Tm[i][bb] is zero for bb > i, so a
+    // column tile's k-steps end with its own block), into Y's place, which
+    // nothing reads any more; each element's owner takes it from there
+    const int lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
+    for (int t = w; t < 16; t += NT / 64) {
+      const int rt = t / 4, it = t % 4;
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (it <= rt)
+        for (int bb = 0; bb < 16 * (it + 1); bb += 4)
+          acc = mfma_f32(sZ[16 * rt + ln][bb + lg], sT[16 * it + ln][bb + lg], acc);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * lg + e, i = 16 * it + ln;
+        sY[r][i] = (i < r && r < L) ? -acc[e] : 0.f;
+      }
+    }
+    __syncthreads();
+  }
   float dak[NE2];
 #pragma unroll
   for (int m = 0; m < NE2; ++m) {
     const int r = rb2 + RSTEP2 * m;
     float dn = 0.f;
-    if (r < L && i2 < r)
+    if constexpr (C == 64) {
+      if (r < C) dn = sY[r][i2];
+    } else if (r < L && i2 < r) {
       for (int bb = 0; bb <= i2; ++bb) dn = fmaf(-sZ[r][bb], sT[i2][bb], dn);
+    }
     float part = (r < L && i2 < r) ? dn * Akk[(int64_t)r * C + i2] : 0.f;
 #pragma unroll
     for (int off = C / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
