@@ -207,6 +207,7 @@ struct BwdLayout {
   Layout f;
   size_t off_akk = 0, off_tm = 0, off_hc = 0, off_dhc = 0, off_dc = 0, off_ddc = 0;
   size_t off_dqh = 0, off_dkh = 0, off_da = 0, off_ddt = 0;
+  size_t off_xcount = 0, off_xlist = 0;  // bf16: the recomputation's fix-up list
   size_t total = 0;
 };
 
@@ -231,6 +232,10 @@ BwdLayout bwd_layout(const kda_problem* p) {
   B.off_dkh = take(tokh * K * 4);
   B.off_da = take(NT * H * 4);
   B.off_ddt = take(NT * H * K * 4);
+  if (p->dtype == KDA_BF16) {
+    B.off_xcount = take(4);
+    B.off_xlist = take(NT * H * 4);
+  }
   B.total = o;
   return B;
 }
@@ -806,6 +811,13 @@ kda_status kda_bwd_profiled(const kda_problem* p, const void* q, const void* k, 
   b.f.a_log = a_log; b.f.dt_bias = dt_bias; b.f.init = initial_state;
   b.f.Akk_out = (float*)(w + L.off_akk);
   b.f.Tm_out = (float*)(w + L.off_tm);
+  // bf16: the chunk factors are recomputed on the matrix-core chunk kernel
+  // (KDA_BWD_RECOMPUTE=valu keeps the fp32 vector-ALU kernels, for comparisons)
+  const char* rc = std::getenv("KDA_BWD_RECOMPUTE");
+  if (p->dtype == KDA_BF16 && !(rc && std::strcmp(rc, "valu") == 0)) {
+    b.f.exact_count = (int32_t*)(w + L.off_xcount);
+    b.f.exact_list = (int32_t*)(w + L.off_xlist);
+  }
   b.d_o = d_o; b.d_fin = d_final_state;
   b.hc = (float*)(w + L.off_hc); b.dhc = (float*)(w + L.off_dhc);
   b.Dc = (float*)(w + L.off_dc); b.dDc = (float*)(w + L.off_ddc);

@@ -6,14 +6,18 @@
 // tests forward and backward together, whose state gradient the hyper_parallel
 // coverage page routes between slices (the backward of _RecvKDAInitialState).
 //
-// fp32 arithmetic for both input dtypes.  For 64-token chunks the dense
+// fp32 arithmetic after the recomputation.  For 64-token chunks the dense
 // per-chunk products (the two state passes, and the value-dimension, Y and
 // Tm^T dW products of the chunk kernel) run on fp32 matrix cores
 // (v_mfma_f32_16x16x4f32: fp32 operands, fp32 accumulation); the pairwise,
 // triangular and per-element work, and chunks of 16 or 32, stay on VALU.  The
 // decay factors and the gate's derivative use the hardware exponential,
-// logarithm and reciprocal (about one ulp on the result).  The forward's chunk factors are recomputed first
-// (the fp32 prologue and chunk kernels, which here also keep Akk and Tm); then,
+// logarithm and reciprocal (about one ulp on the result).  The forward's chunk
+// factors are recomputed first, with Akk and Tm kept: for fp32 inputs by the
+// fp32 prologue and chunk kernels; for bf16 inputs by the forward's
+// matrix-core chunk kernel (bf16 operands, fp32 accumulation, as in the
+// forward) writing the same fp32 arrays, or by the fp32 kernels when
+// KDA_BWD_RECOMPUTE=valu.  Then,
 // per chunk of L rows entering with state
 // S0 and with Q~ = q^ e^gamma, K~ = k^ e^gamma, Kbar = k^ e^(gamma_L - gamma),
 // Aqk_s = scale Aqk, Qt_s = scale Q~ (the forward's stored operands):
@@ -1472,7 +1476,9 @@ template <typename Tin, int C>
 hipError_t run(const BwdArgs& b, hipStream_t s) {
   const FwdArgs& a = b.f;
   bmark(b, kBwdRecompute, 0, s);
-  hipError_t e = launch_valu_prep(a, s);
+  // bf16 inputs: the matrix-core chunk kernel when its fix-up list is given
+  const bool mfma = std::is_same<Tin, bf16>::value && a.exact_list != nullptr;
+  hipError_t e = mfma ? launch_mfma_recompute(a, s) : launch_valu_prep(a, s);
   if (e != hipSuccess) return e;
   bmark(b, kBwdRecompute, 1, s);
   const int64_t wgs = (int64_t)a.N * a.H * (a.V / 64);

@@ -172,6 +172,10 @@ hipError_t launch_valu_path(const FwdArgs& a, hipStream_t s);
 hipError_t launch_valu_prep(const FwdArgs& a, hipStream_t s);
 hipError_t launch_bwd(const BwdArgs& a, hipStream_t s);
 hipError_t launch_mfma_path(const FwdArgs& a, hipStream_t s);
+// The backward's recomputation of the chunk factors for bf16 inputs on the
+// matrix-core chunk kernel, into the fp32 arrays that launch_valu_prep fills
+// (needs exact_count and exact_list for its fix-up pass).
+hipError_t launch_mfma_recompute(const FwdArgs& a, hipStream_t s);
 hipError_t launch_fused_path(const FwdArgs& a, hipStream_t s);
 hipError_t launch_short_conv(const ConvArgs& a, hipStream_t s);
 hipError_t launch_gated_rms_norm(const NormArgs& a, hipStream_t s);

@@ -253,8 +253,11 @@ enum {
 // decay exceeds the factorised range makes the workgroup append the chunk-head
 // to a fix-up list instead.  EXACT = true: the fix-up, with the exact per-pair
 // path on such blocks.  GATE: the gate form (FwdArgs::gate_form).  CONV: q, k
-// and v are the raw projections, convolved on load (FwdArgs::conv).
-template <int K, int V, bool EXACT, int GATE, bool CONV>
+// and v are the raw projections, convolved on load (FwdArgs::conv).  OUT32:
+// the backward's recomputation; instead of a record, the factors go to the
+// fp32 row-major arrays the backward reads (qn, kn, g, bt per token-head; Qt,
+// Kb, W, U, Aqk, Akk_out, Tm_out, gL per chunk-head with C = FwdArgs::C rows).
+template <int K, int V, bool EXACT, int GATE, bool CONV, bool OUT32 = false>
 __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, const int h,
                                            const int tok0, const int L, char* const rec,
                                            const bool keep_ok = false) {
@@ -298,7 +301,7 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
   // Loads q, k, gate of the lane's row at channels 32j + sig(g, e), normalises
   // q and k, applies the gate and scans it over the 16 rows of the block.
   // Used once up front and again by the exact diagonal path.
-  auto row_prologue = [&](float* qv, float* kv, float* lam) __attribute__((always_inline)) {
+  auto row_prologue = [&](float* qv, float* kv, float* lam, bool emit) __attribute__((always_inline)) {
     const bf16* q = (const bf16*)a.q + thk * K;
     const bf16* k = (const bf16*)a.k + thk * K;
     const bf16* gt = (const bf16*)a.gate + th * K;
@@ -361,11 +364,32 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
       kv[s2] *= rk;
     }
 #pragma unroll
-    for (int s2 = 0; s2 < KL; ++s2) lam[s2] = row_scan16(vmask * fgate<GATE>(lam[s2], A, a.lb));
+    for (int s2 = 0; s2 < KL; ++s2) lam[s2] = vmask * fgate<GATE>(lam[s2], A, a.lb);
+    if constexpr (OUT32) {
+      // q^, k^ and the per-token gate of a valid row, channels 32j + 4g.. and 32j + 16 + 4g..
+      if (emit && valid) {
+#pragma unroll
+        for (int j = 0; j < NKJ; ++j)
+#pragma unroll
+          for (int hf = 0; hf < 2; ++hf) {
+            const int64_t o = th * K + 32 * j + 16 * hf + 4 * g;
+            const int e0 = 8 * j + 4 * hf;
+            *(float4*)(a.qn + o) = make_float4(qv[e0], qv[e0 + 1], qv[e0 + 2], qv[e0 + 3]);
+            *(float4*)(a.kn + o) = make_float4(kv[e0], kv[e0 + 1], kv[e0 + 2], kv[e0 + 3]);
+            *(float4*)(a.g + o) = make_float4(lam[e0], lam[e0 + 1], lam[e0 + 2], lam[e0 + 3]);
+          }
+      }
+    }
+#pragma unroll
+    for (int s2 = 0; s2 < KL; ++s2) lam[s2] = row_scan16(lam[s2]);
   };
   float qv[KL], kv[KL], lam[KL];
-  row_prologue(qv, kv, lam);
+  row_prologue(qv, kv, lam, true);
   const float beta_r = valid ? fsigmoid(bf16_to_f32(braw)) : 0.f;
+  // OUT32: rows and columns of the chunk-head's C x C, C x K and C x V arrays
+  const int C = a.C;
+  const int64_t chb = (int64_t)jchunk * H + h;
+  if (OUT32 && g == 0 && valid) a.bt[th] = beta_r;
   if (n == 15) {
 #pragma unroll
     for (int j = 0; j < NKJ; ++j)
@@ -467,14 +491,24 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
       kdiag[j] = pack8(fkd);
       // keep the packed fragments (not their fp32 sources) live into step 5
       asm volatile("" : "+v"(qrow[j]), "+v"(krow[j]), "+v"(kdiag[j]));
-      if (!keep) {
+      if (OUT32) {
+        // Qt and Kbar rows in fp32 (zero past the chunk end: q^ = k^ = 0 there)
+        sX[w][j][lane] = pack8(fx);
+        if (row < C) {
+          const int64_t o = (chb * C + row) * K + 32 * j + 4 * g;
+          *(float4*)(((float*)a.Qt) + o) = make_float4(fq[0], fq[1], fq[2], fq[3]);
+          *(float4*)(((float*)a.Qt) + o + 16) = make_float4(fq[4], fq[5], fq[6], fq[7]);
+          *(float4*)(((float*)a.Kb) + o) = make_float4(fkbar[0], fkbar[1], fkbar[2], fkbar[3]);
+          *(float4*)(((float*)a.Kb) + o + 16) = make_float4(fkbar[4], fkbar[5], fkbar[6], fkbar[7]);
+        }
+      } else if (!keep) {
         ((bf16x8*)(rec + R::oQt))[(w * NKJ + j) * 64 + lane] = pack8(fq);
         sX[w][j][lane] = pack8(fx);
       }
       sKb[w][j][lane] = pack8(fkb);
       // Kbar^T fragments (a, w/2): this block's rows transposed on the matrix
       // cores, written as the (w%2) half of each lane's 16 bytes
-      {
+      if (!OUT32) {
         const bf16x8 kb8 = pack8(fkbar);
 #pragma unroll
         for (int a2 = 0; a2 < 2; ++a2) {
@@ -488,7 +522,9 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
       }
     }
   }
-  if (!keep)
+  if (OUT32)
+    for (int c = tid; c < K; c += kThreads) a.gL[chb * K + c] = sFac[kF_GL][c];
+  else if (!keep)
     for (int c = tid; c < K; c += kThreads) ((float*)(rec + R::oGL))[c] = sFac[kF_GL][c];
   if (!EXACT && !keep_ok) decide_exact();
   else __syncthreads();
@@ -527,7 +563,7 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
     // four g-lanes sum their channels and lane g keeps the sums for i = 4g..4g+3,
     // which are its entries of the transposed tile.  q^, k^ and lambda are
     // recomputed so that they need not stay live until here.
-    row_prologue(qv, kv, lam);
+    row_prologue(qv, kv, lam, false);
     f32x4 eq = zero4(), ek = zero4();
 #pragma unroll 1
     for (int i = 0; i < 16; ++i) {
@@ -572,10 +608,16 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
       }
       *(uint2*)&sA[r][16 * I + 4 * g] = pk4(vv[0], vv[1], vv[2], vv[3]);
       if (I == w) dgv = make_float4(vv[0], vv[1], vv[2], vv[3]);
+      if (OUT32 && r < C && 16 * I < C) {
+        // Akk strictly lower, Aqk (scaled) lower with the diagonal
+        const int64_t o = (chb * C + r) * C + 16 * I + 4 * g;
+        *(float4*)(a.Akk_out + o) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+        *(float4*)(((float*)a.Aqk) + o) = make_float4(dq[I][0], dq[I][1], dq[I][2], dq[I][3]);
+      }
     }
     fA0 = pair_frag(dq[0], dq[1]);
     fA1 = pair_frag(dq[2], dq[3]);
-    if (!keep) {
+    if (!keep && !OUT32) {
       bf16x8* aq = (bf16x8*)(rec + R::oAqk);
       aq[(w * 2 + 0) * 64 + lane] = fA0;
       aq[(w * 2 + 1) * 64 + lane] = fA1;
@@ -699,6 +741,11 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
     else if (w == 2) colblock(std::integral_constant<int, 2>{});
   }
   __syncthreads();
+  if (OUT32)
+    for (int p = 4 * tid; p < C * C; p += 4 * kThreads) {
+      const int r = p / C, i = p % C;
+      *(float4*)(a.Tm_out + chb * C * C + p) = *(const float4*)&sT[r][i];
+    }
 
   // ---- 7. jobs: W (channel pairs), U (value pairs) ----
   bf16x8 tfrag[4][2];
@@ -740,7 +787,16 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
             acc[a2] = mfma(xt[a2][0], tfrag[t][0], zero4());
             if (t >= 2) acc[a2] = mfma(xt[a2][1], tfrag[t][1], acc[a2]);
           }
-          wout[(t * NKJ + p) * 64 + lane] = pair_frag(acc[0], acc[1]);
+          if (OUT32) {
+            // lane (g, n): W[16t + n][32p + 16a2 + 4g + e]
+            const int r = 16 * t + n;
+            if (r < C)
+#pragma unroll
+              for (int a2 = 0; a2 < 2; ++a2)
+                *(f32x4*)(((float*)a.W) + (chb * C + r) * K + 32 * p + 16 * a2 + 4 * g) = acc[a2];
+          } else {
+            wout[(t * NKJ + p) * 64 + lane] = pair_frag(acc[0], acc[1]);
+          }
         }
       }
     } else {
@@ -786,8 +842,18 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
           f32x4 acc = mfma(tfrag[t][0], vb[0][a2], zero4());
           if (t >= 2) acc = mfma(tfrag[t][1], vb[1][a2], acc);
           const int at = (t * NVT + 2 * p + a2) * 64 + lane;
-          if (keep) ((uint2*)sU1)[at] = pk4(acc);
-          else uout[at] = pk4(acc);
+          if (OUT32) {
+            // lane (g, n): U[16t + 4g + e][32p + 16a2 + n]
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const int r = 16 * t + 4 * g + e;
+              if (r < C) ((float*)a.U)[(chb * C + r) * V + 32 * p + 16 * a2 + n] = acc[e];
+            }
+          } else if (keep) {
+            ((uint2*)sU1)[at] = pk4(acc);
+          } else {
+            uout[at] = pk4(acc);
+          }
         }
     }
   }
@@ -796,7 +862,7 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
   // Delta = U, O = Aqk U (wave w: output row tile w of every column tile),
   // final state S = Kbar^T U (wave w: key row tiles w, w+4, ...).  The same
   // products, in the same order, as the state pass for such a chunk.
-  if (!EXACT) {
+  if (!EXACT && !OUT32) {
     if (keep) {
       __syncthreads();
       const int seq = a.chunk_seq[jchunk];
@@ -869,6 +935,34 @@ __global__ __launch_bounds__(kThreads) void k_chunk_mfma_exact(FwdArgs a) {
     const int jchunk = ch / a.H;
     chunk_body<K, V, true, GATE, CONV>(a, jchunk, ch % a.H, a.chunk_tok[jchunk], a.chunk_len[jchunk],
                                  (char*)a.rec + (int64_t)ch * Rec<K, V>::kBytes);
+    __syncthreads();
+  }
+}
+
+// The backward's recomputation for bf16 inputs: every chunk-head's factors in
+// the fp32 row-major arrays the backward reads (chunk_body's OUT32 mode), the
+// chunk-heads that need the exact diagonal path listed for the fix-up pass.
+// The products take bf16 operands with fp32 accumulation, as in the forward.
+template <int K, int V, int GATE>
+__global__ __launch_bounds__(kThreads, 3) void k_chunk_recompute(FwdArgs a) {
+  const unsigned wid = blockIdx.x, H = (unsigned)a.H;
+  const int jchunk = (int)(wid / H), h = (int)(wid % H);
+  // the table holds at least gridDim.x / H entries
+  const int nt = *a.nt_dev;
+  const int tok0 = a.chunk_tok[jchunk], L = a.chunk_len[jchunk];
+  asm volatile("" ::"s"(tok0), "s"(L));
+  if (jchunk >= nt) return;
+  chunk_body<K, V, false, GATE, false, true>(a, jchunk, h, tok0, L, nullptr);
+}
+
+template <int K, int V, int GATE>
+__global__ __launch_bounds__(kThreads) void k_chunk_recompute_exact(FwdArgs a) {
+  const int count = *a.exact_count;
+  for (int i = blockIdx.x; i < count; i += gridDim.x) {
+    const int ch = a.exact_list[i];
+    const int jchunk = ch / a.H;
+    chunk_body<K, V, true, GATE, false, true>(a, jchunk, ch % a.H, a.chunk_tok[jchunk],
+                                              a.chunk_len[jchunk], nullptr);
     __syncthreads();
   }
 }
@@ -2096,6 +2190,31 @@ hipError_t launch_fused_path(const FwdArgs& a, hipStream_t s) {
   if (a.K == 128 && a.V == 64) return run_fused<128, 64>(a, s);
   if (a.K == 64 && a.V == 128) return run_fused<64, 128>(a, s);
   return run_fused<64, 64>(a, s);
+}
+
+namespace {
+template <int K, int V>
+hipError_t run_recompute(const FwdArgs& a, hipStream_t s) {
+  if (a.NT == 0) return hipSuccess;
+  const dim3 grid((unsigned)((int64_t)a.NT * a.H)), block(kThreads);
+  const dim3 fix_grid((unsigned)std::min<int64_t>((int64_t)a.NT * a.H, 256));
+  auto launch_gate = [&](auto gc) {
+    constexpr int GATE = decltype(gc)::value;
+    hipLaunchKernelGGL((k_chunk_recompute<K, V, GATE>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((k_chunk_recompute_exact<K, V, GATE>), fix_grid, block, 0, s, a);
+  };
+  if (a.gate_form == 1) launch_gate(std::integral_constant<int, 1>{});
+  else if (a.gate_form == 2) launch_gate(std::integral_constant<int, 2>{});
+  else launch_gate(std::integral_constant<int, 0>{});
+  return hipGetLastError() == hipSuccess ? hipSuccess : hipErrorLaunchFailure;
+}
+}  // namespace
+
+hipError_t launch_mfma_recompute(const FwdArgs& a, hipStream_t s) {
+  if (a.K == 128 && a.V == 128) return run_recompute<128, 128>(a, s);
+  if (a.K == 128 && a.V == 64) return run_recompute<128, 64>(a, s);
+  if (a.K == 64 && a.V == 128) return run_recompute<64, 128>(a, s);
+  return run_recompute<64, 64>(a, s);
 }
 
 size_t mfma_record_bytes(int K, int V) {

@@ -272,9 +272,14 @@ kda_status kda_chunk_table(const kda_problem* p, int32_t* tok, int32_t* len, int
  *                   document it equals that document's d_final_state.
  *  workspace        at least kda_bwd_workspace_size() bytes, 256-byte aligned.
  * Where the forward floors the log-decay at -110 or clamps it at the bound,
- * the gate's gradient is zero.  Computed in fp32 for both dtypes; the forward's
- * factors are recomputed, not read from a forward call.  Results are
- * deterministic (fixed summation orders, no atomics).
+ * the gate's gradient is zero.  The forward's chunk factors are recomputed,
+ * not read from a forward call: in fp32 for fp32 inputs; for bf16 inputs on
+ * the forward's matrix-core chunk kernel (bf16 operands, fp32 accumulation,
+ * as in the forward), or in fp32 when the environment sets
+ * KDA_BWD_RECOMPUTE=valu (slower; fp32 parameter and state gradients then
+ * about 1e-6 instead of 1e-3 relative).  Everything after the recomputation
+ * is fp32.  Results are deterministic (fixed summation orders; the one atomic
+ * counter only lists chunk-heads for a fix-up pass, each recomputed whole).
  */
 size_t kda_bwd_workspace_size(const kda_problem* p, kda_status* status);
 kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const void* v,

@@ -216,3 +216,43 @@ def test_bwd_fp32_extreme_gates():
     inp["a_log"] = torch.full_like(inp["a_log"], 0.5)
     d_o, d_fin = _upstream(inp, 12)
     _run(inp, d_o, d_fin, torch.float32, "fp32 extreme gates")
+
+
+# bf16 inputs recompute the chunk factors on the matrix-core chunk kernel
+# (bf16 operands, fp32 accumulation); KDA_BWD_RECOMPUTE=valu keeps the fp32
+# vector-ALU kernels.  Both are held to the bf16 tolerance above.
+@pytest.mark.parametrize("C", [32, 16])
+def test_bwd_bf16_short_chunks(C):
+    _banner("bwd bf16 chunk %d" % C)
+    inp = to_device(synthetic.random_problem(43, 1, 200, 2, 128, 128, dtype=torch.bfloat16,
+                                             lengths=[77, 123], init_std=0.5))
+    d_o, d_fin = _upstream(inp, 13)
+    _run(inp, d_o, d_fin, torch.bfloat16, "bf16 chunk %d" % C, chunk_size=C)
+
+
+def test_bwd_bf16_extreme_gates_exact_path():
+    """The fp32 test's gate spikes in bf16: chunk-heads whose in-block decay
+    leaves the factorised range go through the recomputation's exact fix-up."""
+    _banner("bwd bf16 extreme gates")
+    inp = to_device(synthetic.random_problem(42, 1, 260, 2, 128, 128, dtype=torch.bfloat16,
+                                             init_std=0.5, lengths=[150, 110]))
+    gen = torch.Generator(device="cpu").manual_seed(8)
+    spikes = torch.rand(inp["gate"].shape, generator=gen) < 0.1
+    gate = inp["gate"].float().cpu()
+    gate[spikes] = 30.0
+    inp["gate"] = gate.to(torch.bfloat16).to(DEV)
+    inp["a_log"] = torch.full_like(inp["a_log"], 0.5)
+    d_o, d_fin = _upstream(inp, 14)
+    _run(inp, d_o, d_fin, torch.bfloat16, "bf16 extreme gates")
+
+
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 128)])
+def test_bwd_bf16_both_recomputations(monkeypatch, K, V):
+    _banner("bwd bf16 recomputation kernels K=%d V=%d" % (K, V))
+    inp = to_device(synthetic.random_problem(44, 1, 300, 2, K, V, dtype=torch.bfloat16,
+                                             lengths=[64, 1, 129, 106], init_std=0.5))
+    d_o, d_fin = _upstream(inp, 15)
+    monkeypatch.delenv("KDA_BWD_RECOMPUTE", raising=False)
+    _run(inp, d_o, d_fin, torch.bfloat16, "bf16 matrix-core recomputation", lower_bound=-4.0)
+    monkeypatch.setenv("KDA_BWD_RECOMPUTE", "valu")
+    _run(inp, d_o, d_fin, torch.bfloat16, "bf16 vector-ALU recomputation", lower_bound=-4.0)
