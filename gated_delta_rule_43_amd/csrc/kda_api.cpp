@@ -812,11 +812,15 @@ kda_status kda_bwd_profiled(const kda_problem* p, const void* q, const void* k, 
   b.f.Akk_out = (float*)(w + L.off_akk);
   b.f.Tm_out = (float*)(w + L.off_tm);
   // bf16: the chunk factors are recomputed on the matrix-core chunk kernel
-  // (KDA_BWD_RECOMPUTE=valu keeps the fp32 vector-ALU kernels, for comparisons)
+  // (for comparisons, KDA_BWD_RECOMPUTE=valu keeps the fp32 vector-ALU kernels
+  // and =mfma32 keeps every recomputed array in fp32)
   const char* rc = std::getenv("KDA_BWD_RECOMPUTE");
   if (p->dtype == KDA_BF16 && !(rc && std::strcmp(rc, "valu") == 0)) {
     b.f.exact_count = (int32_t*)(w + L.off_xcount);
     b.f.exact_list = (int32_t*)(w + L.off_xlist);
+    // the matrix-core state passes (64-token chunks) read W, U, Qt, Kbar and
+    // Aqk as bf16, like the forward's records
+    b.f.ws_bf16 = p->chunk_size == 64 && !(rc && std::strcmp(rc, "mfma32") == 0) ? 1 : 0;
   }
   b.d_o = d_o; b.d_fin = d_final_state;
   b.hc = (float*)(w + L.off_hc); b.dhc = (float*)(w + L.off_dhc);

@@ -86,15 +86,44 @@ __device__ inline void gate_grad(float x, float A, int form, float lb, float* dg
 }
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // fp32 matrix-core product of one 16 x 4 by 4 x 16 step into a 16 x 16 tile
 __device__ __forceinline__ f32x4 mfma_f32(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
+// bf16 matrix-core product of one 16 x 32 by 32 x 16 step into a 16 x 16 fp32
+// tile: lane l holds A[l%16][8(l/16) .. +7] and B[8(l/16) .. +7][l%16]
+__device__ __forceinline__ f32x4 mfma_bf16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+// x = hi + lo: hi = bf16(x), lo = bf16(x - hi); hi + lo is within 2^-17 |x|
+// of x, and a product of two such pairs without the lo * lo term within about
+// 2^-16 of the fp32 product
+__device__ __forceinline__ void split_bf16(float x, bf16& hi, bf16& lo) {
+  const __bf16 h = (__bf16)x;
+  hi = __builtin_bit_cast(bf16, h);
+  lo = __builtin_bit_cast(bf16, (__bf16)(x - (float)h));
+}
+__device__ __forceinline__ bf16 to_bf16(float x) { return __builtin_bit_cast(bf16, (__bf16)x); }
+// 8 consecutive bf16 of an LDS row (16-byte aligned)
+__device__ __forceinline__ bf16x8 frag8(const bf16* p) { return *(const bf16x8*)p; }
 
 __device__ inline float wave_sum(float x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
   return x;
+}
+
+// Element type of the recomputed W, U, Qt, Kbar and Aqk that the matrix-core
+// state passes read: fp32, or bf16 (FwdArgs::ws_bf16, bf16 inputs with 64-token
+// chunks), four elements held as one piece (float4, or two 32-bit words).
+template <bool WS16> struct Ws;
+template <> struct Ws<false> { typedef float E; typedef float4 P4; };
+template <> struct Ws<true> { typedef bf16 E; typedef uint2 P4; };
+__device__ inline float4 widen4(float4 v) { return v; }
+__device__ inline float4 widen4(uint2 u) {
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
+                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
 }
 
 // Copy n floats (n a multiple of 4, 16-byte aligned) from global memory to LDS
@@ -189,9 +218,12 @@ __global__ __launch_bounds__(64 * state_waves(C)) void k_bwd_fstate(BwdArgs b) {
 // The forward state pass for 64-token chunks on fp32 matrix cores, same
 // arithmetic as k_bwd_fstate up to the order of additions: the state (K x 64
 // columns) lives in accumulator tiles, K/64 per wave; per chunk, wave w
-// computes one 16 x 16 tile of Delta (row tile w/4, column tile w%4).
-template <int K>
+// computes one 16 x 16 tile of Delta (row tile w/4, column tile w%4).  WS16:
+// W, Kbar and U are stored as bf16 and widened to fp32 on their way to LDS.
+template <int K, bool WS16>
 __global__ __launch_bounds__(1024) void k_bwd_fstate_mfma(BwdArgs b) {
+  typedef typename Ws<WS16>::E E;
+  typedef typename Ws<WS16>::P4 P4;
   constexpr int C = 64, NT = 1024, VT = 64;
   constexpr int TPW = K / 64;
   constexpr int SP = VT + 16, KP = K + 4;
@@ -212,21 +244,21 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_mfma(BwdArgs b) {
   // in flight while the previous chunk's products run)
   constexpr int NF4 = C * K / 4 / NT;
   static_assert(NF4 * NT * 4 == C * K && NF4 <= 2, "one or two float4 pieces per thread");
-  float4 pw0, pw1, pk0, pk1;  // named, so that they stay in registers
+  P4 pw0, pw1, pk0, pk1;      // named, so that they stay in registers
   f32x4 pu;                   // the chunk's U tile of this wave's Delta tile
   float pgl[TPW][4];          // its gL entries of this wave's state tiles
   const int drt = w >> 2, dct = w & 3;  // this wave's Delta tile
   auto fetch_wk = [&](int64_t chb) __attribute__((always_inline)) {
-    const float* U = (const float*)a.U + chb * C * V;
+    const E* U = (const E*)a.U + chb * C * V;
     const float* gL = a.gL + chb * K;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pu[e] = U[(int64_t)(16 * drt + 4 * lg + e) * V + col0 + 16 * dct + ln];
+    for (int e = 0; e < 4; ++e) pu[e] = load_f32(U + (int64_t)(16 * drt + 4 * lg + e) * V + col0 + 16 * dct + ln);
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) pgl[t][e] = gL[16 * ((w * TPW + t) >> 2) + 4 * lg + e];
-    const float4* W4 = (const float4*)((const float*)a.W + chb * C * K);
-    const float4* K4 = (const float4*)((const float*)a.Kb + chb * C * K);
+    const P4* W4 = (const P4*)((const E*)a.W + chb * C * K);
+    const P4* K4 = (const P4*)((const E*)a.Kb + chb * C * K);
     pw0 = W4[tid];
     pk0 = K4[tid];
     if constexpr (NF4 == 2) {
@@ -271,12 +303,12 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_mfma(BwdArgs b) {
     }
     {
       const int r0 = tid / (K / 4), c0 = 4 * (tid % (K / 4));
-      *(float4*)&sW[r0][c0] = pw0;
-      *(float4*)&sKb[r0][c0] = pk0;
+      *(float4*)&sW[r0][c0] = widen4(pw0);
+      *(float4*)&sKb[r0][c0] = widen4(pk0);
       if constexpr (NF4 == 2) {
         const int r1 = (tid + NT) / (K / 4), c1 = 4 * ((tid + NT) % (K / 4));
-        *(float4*)&sW[r1][c1] = pw1;
-        *(float4*)&sKb[r1][c1] = pk1;
+        *(float4*)&sW[r1][c1] = widen4(pw1);
+        *(float4*)&sKb[r1][c1] = widen4(pk1);
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -422,9 +454,12 @@ __global__ __launch_bounds__(64 * state_waves(C)) void k_bwd_dstate(BwdArgs b) {
 // row tile (w*TPW+t)/4, column tile (w*TPW+t)%4); per chunk, wave w computes
 // one 16 x 16 tile of dDelta (row tile w/4, column tile w%4).  Operands come
 // from LDS rows padded so that the 16 lanes of a fragment column hit
-// different banks.
-template <typename Tin, int K>
+// different banks.  WS16: Aqk, Kbar, Qt and W are stored as bf16 and widened
+// to fp32 on their way to LDS.
+template <typename Tin, int K, bool WS16>
 __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
+  typedef typename Ws<WS16>::E E;
+  typedef typename Ws<WS16>::P4 P4;
   constexpr int C = 64, NT = 1024, VT = 64;
   constexpr int TPW = K / 64;                     // state tiles per wave
   constexpr int SP = VT + 16, AP = C + 4, KP = K + 4;
@@ -451,7 +486,7 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
   // previous chunk's products run
   static_assert(C * C / 4 == NT && C * K / 4 <= 2 * NT, "one Aqk piece, one or two of the others");
   constexpr bool TWO = C * K / 4 == 2 * NT;
-  float4 pa, pk0, pk1, pq0, pq1, pw0, pw1;
+  P4 pa, pk0, pk1, pq0, pq1, pw0, pw1;
   // dO of the prefetched chunk, raw (rows past its end are masked when staged)
   constexpr int NO = C * VT / NT;
   static_assert(NO * NT == C * VT, "whole dO tiles per thread");
@@ -465,10 +500,10 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
       const int e = tid + u * NT, r = e / VT, cc = e % VT;
       po[u] = load_f32(dO + ((int64_t)(tokn + (r < Ln ? r : 0)) * H + h) * V + col0 + cc);
     }
-    const float4* A4 = (const float4*)((const float*)a.Aqk + chb * C * C);
-    const float4* K4 = (const float4*)((const float*)a.Kb + chb * C * K);
-    const float4* Q4 = (const float4*)((const float*)a.Qt + chb * C * K);
-    const float4* W4 = (const float4*)((const float*)a.W + chb * C * K);
+    const P4* A4 = (const P4*)((const E*)a.Aqk + chb * C * C);
+    const P4* K4 = (const P4*)((const E*)a.Kb + chb * C * K);
+    const P4* Q4 = (const P4*)((const E*)a.Qt + chb * C * K);
+    const P4* W4 = (const P4*)((const E*)a.W + chb * C * K);
     pa = A4[tid];
     pk0 = K4[tid];
     pq0 = Q4[tid];
@@ -480,9 +515,9 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
     }
   };
   // a [C][K] matrix held as pieces tid (and tid + NT) into LDS rows of stride KP
-  auto put_k = [&](float (*dst)[KP], const float4& v0, const float4& v1) __attribute__((always_inline)) {
-    *(float4*)&dst[tid / (K / 4)][4 * (tid % (K / 4))] = v0;
-    if constexpr (TWO) *(float4*)&dst[(tid + NT) / (K / 4)][4 * ((tid + NT) % (K / 4))] = v1;
+  auto put_k = [&](float (*dst)[KP], const P4& v0, const P4& v1) __attribute__((always_inline)) {
+    *(float4*)&dst[tid / (K / 4)][4 * (tid % (K / 4))] = widen4(v0);
+    if constexpr (TWO) *(float4*)&dst[(tid + NT) / (K / 4)][4 * ((tid + NT) % (K / 4))] = widen4(v1);
   };
   const int64_t sbase = ((int64_t)n * H + h) * K * V;
   f32x4 st[TPW];
@@ -520,7 +555,7 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
       const int e = tid + u * NT, r = e / VT, cc = e % VT;
       sO[r][cc] = r < L ? po[u] : 0.f;
     }
-    *(float4*)&sA[tid / (C / 4)][4 * (tid % (C / 4))] = pa;
+    *(float4*)&sA[tid / (C / 4)][4 * (tid % (C / 4))] = widen4(pa);
     put_k(sKb, pk0, pk1);
     __syncthreads();
     // dDelta = Aqk_s^T dO + Kbar dS_L (Aqk_s is zero above the diagonal, so
@@ -596,6 +631,9 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   constexpr int NE1 = C * K / NT, NE2 = (C * C + NT - 1) / NT;
   constexpr int RSTEP1 = NT / K, RSTEP2 = NT / C;
   constexpr int NEV = (C * VTL + NT - 1) / NT;  // dV elements per thread and tile
+  // bf16 inputs at 64-token chunks: the value-dimension products on bf16
+  // matrix cores with split operands (see phase B)
+  constexpr bool BF = std::is_same<Tin, bf16>::value && C == 64;
   const FwdArgs& a = b.f;
   const int H = a.H, V = a.V;
   const int64_t wid = blockIdx.x;
@@ -709,11 +747,17 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     constexpr int NS = K * VTL / NT, NR = C * VTL / NT;
     static_assert(NS * NT == K * VTL && NR * NT == C * VTL, "whole tiles per thread");
     float ps[NS], pd[NR], po[NR];
+    // bf16 inputs: dS_L too, for rowsum(S0 . dS_L) from the registers the
+    // tiles are staged from (row (tid + NT u) / VTL, column tid % VTL)
+    float pl[BF ? NS : 1], sdp[BF ? NS : 1];
+#pragma unroll
+    for (int u = 0; u < (BF ? NS : 1); ++u) sdp[u] = 0.f;
     auto fetch1 = [&](int j0) {
 #pragma unroll
       for (int u = 0; u < NS; ++u) {
         const int e = tid + NT * u, c = e / VTL, jj = e % VTL;
         ps[u] = S0[(int64_t)c * V + j0 + jj];
+        if constexpr (BF) pl[u] = dSL[(int64_t)c * V + j0 + jj];
       }
 #pragma unroll
       for (int u = 0; u < NR; ++u) {
@@ -723,31 +767,83 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
         po[u] = r < L ? x : 0.f;
       }
     };
+    // bf16 inputs: the tiles go to LDS as bf16, S0, Delta, dDelta and dS_L
+    // as hi + lo pairs (dO and V are exact), and each 32-column tile is one
+    // k-step of the bf16 products: hi*hi + hi*lo + lo*hi per pair of split
+    // operands, fp32 accumulation.  Rows padded to BP (16-byte aligned).
+    constexpr int BP = VTL + 8;
+    bf16 (*hS0)[BP] = (bf16(*)[BP])sReg;
+    bf16 (*lS0)[BP] = hS0 + K;
+    bf16 (*hdD)[BP] = lS0 + K;
+    bf16 (*ldD)[BP] = hdD + C;
+    bf16 (*hdO)[BP] = ldD + C;
+    static_assert(VTL == 32, "one bf16 k-step per value tile");
+    static_assert((2 * K + 3 * C) * BP * 2 <= kRegion * 4, "sweep 1 bf16 tiles fit the region");
     fetch1(0);
     for (int j0 = 0; j0 < V; j0 += VTL) {
       __syncthreads();
+      if constexpr (BF) {
 #pragma unroll
-      for (int u = 0; u < NS; ++u) {
-        const int e = tid + NT * u;
-        tS0[e / VTL][e % VTL] = ps[u];
-      }
+        for (int u = 0; u < NS; ++u) {
+          const int e = tid + NT * u;
+          split_bf16(ps[u], hS0[e / VTL][e % VTL], lS0[e / VTL][e % VTL]);
+          sdp[u] = fmaf(ps[u], pl[u], sdp[u]);
+        }
 #pragma unroll
-      for (int u = 0; u < NR; ++u) {
-        const int e = tid + NT * u;
-        tdD[e / VTL][e % VTL] = pd[u];
-        tdO[e / VTL][e % VTL] = po[u];
+        for (int u = 0; u < NR; ++u) {
+          const int e = tid + NT * u;
+          split_bf16(pd[u], hdD[e / VTL][e % VTL], ldD[e / VTL][e % VTL]);
+          hdO[e / VTL][e % VTL] = to_bf16(po[u]);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+          const int e = tid + NT * u;
+          tS0[e / VTL][e % VTL] = ps[u];
+        }
+#pragma unroll
+        for (int u = 0; u < NR; ++u) {
+          const int e = tid + NT * u;
+          tdD[e / VTL][e % VTL] = pd[u];
+          tdO[e / VTL][e % VTL] = po[u];
+        }
       }
       if (j0 + VTL < V) fetch1(j0 + VTL);
       __syncthreads();
-#pragma unroll
-      for (int jj = 0; jj < VTL; jj += 4) {
-        const float ad = tdD[16 * rt + ln][jj + lg], ao = tdO[16 * rt + ln][jj + lg];
+      if constexpr (BF) {
+        const bf16x8 ah = frag8(&hdD[16 * rt + ln][8 * lg]), al = frag8(&ldD[16 * rt + ln][8 * lg]);
+        const bf16x8 ao = frag8(&hdO[16 * rt + ln][8 * lg]);
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const float bs = tS0[16 * (ct0 + t) + ln][jj + lg];
-          m1[t] = mfma_f32(ad, bs, m1[t]);
-          m2[t] = mfma_f32(ao, bs, m2[t]);
+          const bf16x8 bh = frag8(&hS0[16 * (ct0 + t) + ln][8 * lg]);
+          const bf16x8 bl = frag8(&lS0[16 * (ct0 + t) + ln][8 * lg]);
+          m1[t] = mfma_bf16(ah, bh, m1[t]);
+          m1[t] = mfma_bf16(ah, bl, m1[t]);
+          m1[t] = mfma_bf16(al, bh, m1[t]);
+          m2[t] = mfma_bf16(ao, bh, m2[t]);
+          m2[t] = mfma_bf16(ao, bl, m2[t]);
         }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < VTL; jj += 4) {
+          const float ad = tdD[16 * rt + ln][jj + lg], ao = tdO[16 * rt + ln][jj + lg];
+#pragma unroll
+          for (int t = 0; t < 2; ++t) {
+            const float bs = tS0[16 * (ct0 + t) + ln][jj + lg];
+            m1[t] = mfma_f32(ad, bs, m1[t]);
+            m2[t] = mfma_f32(ao, bs, m2[t]);
+          }
+        }
+      }
+    }
+    if constexpr (BF) {
+      // each row's 32 columns sit in one half-wave
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        float x = sdp[u];
+#pragma unroll
+        for (int off = 16; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+        if (tid % VTL == 0) sSd[(tid + NT * u) / VTL] = x;
       }
     }
     __syncthreads();  // the tiles are dead: dW, and dQ~ on its way to registers
@@ -787,12 +883,22 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     const bool has_dv = w < 8;
     const int vrt = (w >> 1) & 3, vct = w & 1;
     float qs[NS], ql[NS], qd[NR], qD[NR], qo[NR], qv[NR];
+    // bf16 inputs: sweep 2's tiles, as in sweep 1 (S0 is not read again)
+    bf16 (*hSL)[BP] = (bf16(*)[BP])sReg2;
+    bf16 (*lSL)[BP] = hSL + K;
+    bf16 (*hD2)[BP] = lSL + K;
+    bf16 (*lD2)[BP] = hD2 + C;
+    bf16 (*hdO2)[BP] = lD2 + C;
+    bf16 (*hdD2)[BP] = hdO2 + C;
+    bf16 (*ldD2)[BP] = hdD2 + C;
+    bf16 (*hv2)[BP] = ldD2 + C;
+    static_assert((2 * K + 6 * C) * BP * 2 <= (kRegion - C * K) * 4, "sweep 2 bf16 tiles fit");
     auto fetch2 = [&](int j0) {
 #pragma unroll
       for (int u = 0; u < NS; ++u) {
         const int e = tid + NT * u, c = e / VTL, jj = e % VTL;
         ql[u] = dSL[(int64_t)c * V + j0 + jj];
-        qs[u] = S0[(int64_t)c * V + j0 + jj];
+        if constexpr (!BF) qs[u] = S0[(int64_t)c * V + j0 + jj];
       }
 #pragma unroll
       for (int u = 0; u < NR; ++u) {
@@ -809,22 +915,77 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     fetch2(0);
     for (int j0 = 0; j0 < V; j0 += VTL) {
       __syncthreads();
+      if constexpr (BF) {
 #pragma unroll
-      for (int u = 0; u < NS; ++u) {
-        const int e = tid + NT * u;
-        tdSL2[e / VTL][e % VTL] = ql[u];
-        tS02[e / VTL][e % VTL] = qs[u];
-      }
+        for (int u = 0; u < NS; ++u) {
+          const int e = tid + NT * u;
+          split_bf16(ql[u], hSL[e / VTL][e % VTL], lSL[e / VTL][e % VTL]);
+        }
 #pragma unroll
-      for (int u = 0; u < NR; ++u) {
-        const int e = tid + NT * u;
-        tdD2[e / VTL][e % VTL] = qd[u];
-        tD2[e / VTL][e % VTL] = qD[u];
-        tdO2[e / VTL][e % VTL] = qo[u];
-        tv2[e / VTL][e % VTL] = qv[u];
+        for (int u = 0; u < NR; ++u) {
+          const int e = tid + NT * u, r = e / VTL, jj = e % VTL;
+          split_bf16(qd[u], hdD2[r][jj], ldD2[r][jj]);
+          split_bf16(qD[u], hD2[r][jj], lD2[r][jj]);
+          hdO2[r][jj] = to_bf16(qo[u]);
+          hv2[r][jj] = to_bf16(qv[u]);
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+          const int e = tid + NT * u;
+          tdSL2[e / VTL][e % VTL] = ql[u];
+          tS02[e / VTL][e % VTL] = qs[u];
+        }
+#pragma unroll
+        for (int u = 0; u < NR; ++u) {
+          const int e = tid + NT * u;
+          tdD2[e / VTL][e % VTL] = qd[u];
+          tD2[e / VTL][e % VTL] = qD[u];
+          tdO2[e / VTL][e % VTL] = qo[u];
+          tv2[e / VTL][e % VTL] = qv[u];
+        }
       }
       if (j0 + VTL < V) fetch2(j0 + VTL);
       __syncthreads();
+      if constexpr (BF) {
+        const bf16x8 ah = frag8(&hD2[16 * rt + ln][8 * lg]), al = frag8(&lD2[16 * rt + ln][8 * lg]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const bf16x8 bh = frag8(&hSL[16 * (ct0 + t) + ln][8 * lg]);
+          const bf16x8 bl = frag8(&lSL[16 * (ct0 + t) + ln][8 * lg]);
+          m3[t] = mfma_bf16(ah, bh, m3[t]);
+          m3[t] = mfma_bf16(ah, bl, m3[t]);
+          m3[t] = mfma_bf16(al, bh, m3[t]);
+        }
+#pragma unroll
+        for (int u = 0; u < NPY; ++u) {
+          const int t = w + NW * u;
+          if (t < NTRI) {
+            int R, I;
+            tri_tile(t, R, I);
+            const bf16x8 o8 = frag8(&hdO2[16 * R + ln][8 * lg]);
+            pt[u] = mfma_bf16(o8, frag8(&hD2[16 * I + ln][8 * lg]), pt[u]);
+            pt[u] = mfma_bf16(o8, frag8(&lD2[16 * I + ln][8 * lg]), pt[u]);
+            const bf16x8 v8 = frag8(&hv2[16 * I + ln][8 * lg]);
+            yt[u] = mfma_bf16(frag8(&hdD2[16 * R + ln][8 * lg]), v8, yt[u]);
+            yt[u] = mfma_bf16(frag8(&ldD2[16 * R + ln][8 * lg]), v8, yt[u]);
+          }
+        }
+        if (has_dv) {
+          // dV as below, dDelta from its hi + lo pair, fp32 products
+          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+          for (int a0 = 16 * vrt; a0 < C; a0 += 4) {
+            const int ar = a0 + lg, ac = 16 * vct + ln;
+            acc = mfma_f32(sT[ar][16 * vrt + ln], bf16_to_f32(hdD2[ar][ac]) + bf16_to_f32(ldD2[ar][ac]), acc);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 16 * vrt + 4 * lg + e;
+            if (r < L) store_as(dv + th(r) * V + j0 + 16 * vct + ln, sB[r] * acc[e]);
+          }
+        }
+        continue;
+      }
       if (tid < K) {
         const int c = tid;
 #pragma unroll 8
@@ -894,7 +1055,9 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
         }
       }
     }
-    if (tid < K) sSd[tid] = sd;
+    if constexpr (!BF) {
+      if (tid < K) sSd[tid] = sd;
+    }
     __syncthreads();
   } else {
   {
@@ -1486,8 +1649,14 @@ hipError_t run(const BwdArgs& b, hipStream_t s) {
   if (wgs > 0 && a.NT > 0) {
     constexpr int NTS = 64 * state_waves(C);
     if constexpr (C == 64) {
-      if (a.K == 64) hipLaunchKernelGGL((k_bwd_fstate_mfma<64>), dim3((unsigned)wgs), dim3(1024), 0, s, b);
-      else hipLaunchKernelGGL((k_bwd_fstate_mfma<128>), dim3((unsigned)wgs), dim3(1024), 0, s, b);
+      const dim3 g((unsigned)wgs), t(1024);
+      if (a.ws_bf16) {
+        if (a.K == 64) hipLaunchKernelGGL((k_bwd_fstate_mfma<64, true>), g, t, 0, s, b);
+        else hipLaunchKernelGGL((k_bwd_fstate_mfma<128, true>), g, t, 0, s, b);
+      } else {
+        if (a.K == 64) hipLaunchKernelGGL((k_bwd_fstate_mfma<64, false>), g, t, 0, s, b);
+        else hipLaunchKernelGGL((k_bwd_fstate_mfma<128, false>), g, t, 0, s, b);
+      }
     } else {
       if (a.K == 64) hipLaunchKernelGGL((k_bwd_fstate<C, 64>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
       else hipLaunchKernelGGL((k_bwd_fstate<C, 128>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
@@ -1499,8 +1668,14 @@ hipError_t run(const BwdArgs& b, hipStream_t s) {
   if (wgs > 0) {
     constexpr int NTS = 64 * state_waves(C);
     if constexpr (C == 64) {
-      if (a.K == 64) hipLaunchKernelGGL((k_bwd_dstate_mfma<Tin, 64>), dim3((unsigned)wgs), dim3(1024), 0, s, b);
-      else hipLaunchKernelGGL((k_bwd_dstate_mfma<Tin, 128>), dim3((unsigned)wgs), dim3(1024), 0, s, b);
+      const dim3 g((unsigned)wgs), t(1024);
+      if (a.ws_bf16) {
+        if (a.K == 64) hipLaunchKernelGGL((k_bwd_dstate_mfma<Tin, 64, true>), g, t, 0, s, b);
+        else hipLaunchKernelGGL((k_bwd_dstate_mfma<Tin, 128, true>), g, t, 0, s, b);
+      } else {
+        if (a.K == 64) hipLaunchKernelGGL((k_bwd_dstate_mfma<Tin, 64, false>), g, t, 0, s, b);
+        else hipLaunchKernelGGL((k_bwd_dstate_mfma<Tin, 128, false>), g, t, 0, s, b);
+      }
     } else {
       if (a.K == 64) hipLaunchKernelGGL((k_bwd_dstate<Tin, C, 64>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
       else hipLaunchKernelGGL((k_bwd_dstate<Tin, C, 128>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);

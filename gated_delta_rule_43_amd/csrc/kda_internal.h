@@ -64,7 +64,8 @@ struct FwdArgs {
   int32_t* chunk_seq;  // [NT] sequence (row or document) of each chunk
   // workspace: per-token prologue results (VALU path)
   float *qn, *kn, *g, *bt;
-  // workspace: per chunk-head factors, element type ws_dtype
+  // workspace: per chunk-head factors, fp32; with ws_bf16 set, W, U, Qt, Kb
+  // and Aqk are bf16 (the backward's matrix-core recomputation, 64-token chunks)
   int ws_bf16;
   void *W, *U, *Qt, *Kb, *Aqk;
   float* gL;

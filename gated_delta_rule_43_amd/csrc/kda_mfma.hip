@@ -256,7 +256,8 @@ enum {
 // and v are the raw projections, convolved on load (FwdArgs::conv).  OUT32:
 // the backward's recomputation; instead of a record, the factors go to the
 // fp32 row-major arrays the backward reads (qn, kn, g, bt per token-head; Qt,
-// Kb, W, U, Aqk, Akk_out, Tm_out, gL per chunk-head with C = FwdArgs::C rows).
+// Kb, W, U, Aqk, Akk_out, Tm_out, gL per chunk-head with C = FwdArgs::C rows;
+// Qt, Kb, W, U and Aqk as bf16 when FwdArgs::ws_bf16 is set).
 template <int K, int V, bool EXACT, int GATE, bool CONV, bool OUT32 = false>
 __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, const int h,
                                            const int tok0, const int L, char* const rec,
@@ -496,10 +497,17 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
         sX[w][j][lane] = pack8(fx);
         if (row < C) {
           const int64_t o = (chb * C + row) * K + 32 * j + 4 * g;
-          *(float4*)(((float*)a.Qt) + o) = make_float4(fq[0], fq[1], fq[2], fq[3]);
-          *(float4*)(((float*)a.Qt) + o + 16) = make_float4(fq[4], fq[5], fq[6], fq[7]);
-          *(float4*)(((float*)a.Kb) + o) = make_float4(fkbar[0], fkbar[1], fkbar[2], fkbar[3]);
-          *(float4*)(((float*)a.Kb) + o + 16) = make_float4(fkbar[4], fkbar[5], fkbar[6], fkbar[7]);
+          if (a.ws_bf16) {
+            *(uint2*)((bf16*)a.Qt + o) = pk4(fq[0], fq[1], fq[2], fq[3]);
+            *(uint2*)((bf16*)a.Qt + o + 16) = pk4(fq[4], fq[5], fq[6], fq[7]);
+            *(uint2*)((bf16*)a.Kb + o) = pk4(fkbar[0], fkbar[1], fkbar[2], fkbar[3]);
+            *(uint2*)((bf16*)a.Kb + o + 16) = pk4(fkbar[4], fkbar[5], fkbar[6], fkbar[7]);
+          } else {
+            *(float4*)(((float*)a.Qt) + o) = make_float4(fq[0], fq[1], fq[2], fq[3]);
+            *(float4*)(((float*)a.Qt) + o + 16) = make_float4(fq[4], fq[5], fq[6], fq[7]);
+            *(float4*)(((float*)a.Kb) + o) = make_float4(fkbar[0], fkbar[1], fkbar[2], fkbar[3]);
+            *(float4*)(((float*)a.Kb) + o + 16) = make_float4(fkbar[4], fkbar[5], fkbar[6], fkbar[7]);
+          }
         }
       } else if (!keep) {
         ((bf16x8*)(rec + R::oQt))[(w * NKJ + j) * 64 + lane] = pack8(fq);
@@ -612,7 +620,8 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
         // Akk strictly lower, Aqk (scaled) lower with the diagonal
         const int64_t o = (chb * C + r) * C + 16 * I + 4 * g;
         *(float4*)(a.Akk_out + o) = make_float4(vv[0], vv[1], vv[2], vv[3]);
-        *(float4*)(((float*)a.Aqk) + o) = make_float4(dq[I][0], dq[I][1], dq[I][2], dq[I][3]);
+        if (a.ws_bf16) *(uint2*)((bf16*)a.Aqk + o) = pk4(dq[I]);
+        else *(float4*)(((float*)a.Aqk) + o) = make_float4(dq[I][0], dq[I][1], dq[I][2], dq[I][3]);
       }
     }
     fA0 = pair_frag(dq[0], dq[1]);
@@ -792,8 +801,11 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
             const int r = 16 * t + n;
             if (r < C)
 #pragma unroll
-              for (int a2 = 0; a2 < 2; ++a2)
-                *(f32x4*)(((float*)a.W) + (chb * C + r) * K + 32 * p + 16 * a2 + 4 * g) = acc[a2];
+              for (int a2 = 0; a2 < 2; ++a2) {
+                const int64_t o = (chb * C + r) * K + 32 * p + 16 * a2 + 4 * g;
+                if (a.ws_bf16) *(uint2*)((bf16*)a.W + o) = pk4(acc[a2]);
+                else *(f32x4*)(((float*)a.W) + o) = acc[a2];
+              }
           } else {
             wout[(t * NKJ + p) * 64 + lane] = pair_frag(acc[0], acc[1]);
           }
@@ -847,7 +859,10 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
               const int r = 16 * t + 4 * g + e;
-              if (r < C) ((float*)a.U)[(chb * C + r) * V + 32 * p + 16 * a2 + n] = acc[e];
+              const int64_t o = (chb * C + r) * V + 32 * p + 16 * a2 + n;
+              if (r >= C) continue;
+              if (a.ws_bf16) ((bf16*)a.U)[o] = f32_to_bf16(acc[e]);
+              else ((float*)a.U)[o] = acc[e];
             }
           } else if (keep) {
             ((uint2*)sU1)[at] = pk4(acc);
