@@ -814,8 +814,13 @@ kda_status kda_bwd_profiled(const kda_problem* p, const void* q, const void* k, 
   // bf16: the chunk factors are recomputed on the matrix-core chunk kernel
   // (for comparisons, KDA_BWD_RECOMPUTE=valu keeps the fp32 vector-ALU kernels
   // and =mfma32 keeps every recomputed array in fp32)
+  // (it reads q, k, v and gate in 8-byte pieces: they must be 16-byte aligned,
+  // else the vector-ALU kernels run)
   const char* rc = std::getenv("KDA_BWD_RECOMPUTE");
-  if (p->dtype == KDA_BF16 && !(rc && std::strcmp(rc, "valu") == 0)) {
+  bool vec_ok = true;
+  for (const void* ptr : {q, k, v, gate})
+    if (ptr && !aligned(ptr, 16)) vec_ok = false;
+  if (p->dtype == KDA_BF16 && vec_ok && !(rc && std::strcmp(rc, "valu") == 0)) {
     b.f.exact_count = (int32_t*)(w + L.off_xcount);
     b.f.exact_list = (int32_t*)(w + L.off_xlist);
     // the matrix-core state passes (64-token chunks) read W, U, Qt, Kbar and

@@ -1543,59 +1543,81 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
 }
 
 // dq, dk: sum over the value heads of a group, then the L2 norm's Jacobian.
-// One wave per (token, key head).
-template <typename Tin>
+// One wave per TPW (token, key head) pairs; lane l holds channels
+// CPL l .. CPL l + CPL - 1 (one 8-byte or 4-byte piece per row), and every load
+// of the wave's pairs is issued before the first reduction.
+template <typename Tin, int K>
 __global__ __launch_bounds__(kThreads) void k_bwd_qk(BwdArgs b) {
+  constexpr int CPL = K / 64, TPW = 4;
+  static_assert(CPL == 1 || CPL == 2, "head dims 64 and 128");
   const FwdArgs& a = b.f;
-  const int H = a.H, HK = a.HK, K = a.K, G = H / HK;
-  const int lane = threadIdx.x & 63;
-  const int64_t tk = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
-  if (tk >= (int64_t)a.B * a.T * HK) return;
-  const int64_t tok = tk / HK;
-  const int hk = (int)(tk % HK);
-  // q and k together: every load is issued before the first reduction
-  constexpr int M = kMaxD / 64;
-  const Tin* xq = (const Tin*)a.q + tk * K;
-  const Tin* xk = (const Tin*)a.k + tk * K;
-  float dq[M], dk[M], vq[M], vk[M];
-  float ssq = 0.f, dotq = 0.f, ssk = 0.f, dotk = 0.f;
-#pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int c = lane + 64 * m;
-    if (c >= K) break;
-    float sq = 0.f, sk = 0.f;
-    for (int gi = 0; gi < G; ++gi) {
-      const int64_t row = (tok * H + (int64_t)hk * G + gi) * K + c;
-      sq += b.dqh[row];
-      sk += b.dkh[row];
+  const int H = a.H, HK = a.HK, G = H / HK;
+  const int lane = threadIdx.x & 63, c0 = CPL * lane;
+  const int64_t n_tk = (int64_t)a.B * a.T * HK;
+  const int64_t tk0 = ((int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * TPW;
+  if (tk0 >= n_tk) return;
+  float dq[TPW][CPL], dk[TPW][CPL], vq[TPW][CPL], vk[TPW][CPL];
+  auto ld = [&](const float* p, float* out) __attribute__((always_inline)) {
+    if constexpr (CPL == 2) {
+      const float2 x = *(const float2*)p;
+      out[0] = x.x;
+      out[1] = x.y;
+    } else {
+      out[0] = *p;
     }
-    dq[m] = sq;
-    dk[m] = sk;
-    vq[m] = load_f32(xq + c);
-    vk[m] = load_f32(xk + c);
+  };
+  // q and k need only their element alignment: one load per element
+  auto ldt = [&](const Tin* p, float* out) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) out[e] = load_f32(p + e);
+  };
+  // past the last pair, the last one is read again and nothing is stored
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int64_t tk = tk0 + t < n_tk ? tk0 + t : n_tk - 1;
+    const int64_t tok = tk / HK;
+    const int hk = (int)(tk % HK);
+    const int64_t row0 = (tok * H + (int64_t)hk * G) * K + c0;
+    ld(b.dqh + row0, dq[t]);
+    ld(b.dkh + row0, dk[t]);
+    for (int gi = 1; gi < G; ++gi) {
+      float xq[CPL], xk[CPL];
+      ld(b.dqh + row0 + (int64_t)gi * K, xq);
+      ld(b.dkh + row0 + (int64_t)gi * K, xk);
+#pragma unroll
+      for (int e = 0; e < CPL; ++e) {
+        dq[t][e] += xq[e];
+        dk[t][e] += xk[e];
+      }
+    }
+    ldt((const Tin*)a.q + tk * K + c0, vq[t]);
+    ldt((const Tin*)a.k + tk * K + c0, vk[t]);
   }
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    if (lane + 64 * m >= K) break;
-    ssq = fmaf(vq[m], vq[m], ssq);
-    dotq = fmaf(vq[m], dq[m], dotq);
-    ssk = fmaf(vk[m], vk[m], ssk);
-    dotk = fmaf(vk[m], dk[m], dotk);
-  }
-  ssq = wave_sum(ssq);
-  dotq = wave_sum(dotq);
-  ssk = wave_sum(ssk);
-  dotk = wave_sum(dotk);
-  const float rq = 1.f / sqrtf(ssq + 1e-6f), rk = 1.f / sqrtf(ssk + 1e-6f);
-  const float r3q = rq * rq * rq, r3k = rk * rk * rk;
-  Tin* oq = (Tin*)b.dq + tk * K;
-  Tin* ok = (Tin*)b.dk + tk * K;
+  for (int t = 0; t < TPW; ++t) {
+    const int64_t tk = tk0 + t;
+    if (tk >= n_tk) break;
+    float ssq = 0.f, dotq = 0.f, ssk = 0.f, dotk = 0.f;
 #pragma unroll
-  for (int m = 0; m < M; ++m) {
-    const int c = lane + 64 * m;
-    if (c >= K) break;
-    store_as(oq + c, dq[m] * rq - vq[m] * dotq * r3q);
-    store_as(ok + c, dk[m] * rk - vk[m] * dotk * r3k);
+    for (int e = 0; e < CPL; ++e) {
+      ssq = fmaf(vq[t][e], vq[t][e], ssq);
+      dotq = fmaf(vq[t][e], dq[t][e], dotq);
+      ssk = fmaf(vk[t][e], vk[t][e], ssk);
+      dotk = fmaf(vk[t][e], dk[t][e], dotk);
+    }
+    ssq = wave_sum(ssq);
+    dotq = wave_sum(dotq);
+    ssk = wave_sum(ssk);
+    dotk = wave_sum(dotk);
+    const float rq = 1.f / sqrtf(ssq + 1e-6f), rk = 1.f / sqrtf(ssk + 1e-6f);
+    const float r3q = rq * rq * rq, r3k = rk * rk * rk;
+    Tin* oq = (Tin*)b.dq + tk * K + c0;
+    Tin* ok = (Tin*)b.dk + tk * K + c0;
+#pragma unroll
+    for (int e = 0; e < CPL; ++e) {
+      store_as(oq + e, dq[t][e] * rq - vq[t][e] * dotq * r3q);
+      store_as(ok + e, dk[t][e] * rk - vk[t][e] * dotk * r3k);
+    }
   }
 }
 
@@ -1695,7 +1717,9 @@ hipError_t run(const BwdArgs& b, hipStream_t s) {
   const int64_t tk = (int64_t)a.B * a.T * a.HK;
   bmark(b, kBwdQK, 0, s);
   if (tk > 0) {
-    hipLaunchKernelGGL((k_bwd_qk<Tin>), dim3((unsigned)((tk + 3) / 4)), dim3(kThreads), 0, s, b);
+    const dim3 grid((unsigned)((tk + 15) / 16));  // 4 waves of 4 pairs
+    if (a.K == 64) hipLaunchKernelGGL((k_bwd_qk<Tin, 64>), grid, dim3(kThreads), 0, s, b);
+    else hipLaunchKernelGGL((k_bwd_qk<Tin, 128>), grid, dim3(kThreads), 0, s, b);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   bmark(b, kBwdQK, 1, s);

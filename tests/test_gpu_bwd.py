@@ -256,3 +256,29 @@ def test_bwd_bf16_both_recomputations(monkeypatch, K, V):
     _run(inp, d_o, d_fin, torch.bfloat16, "bf16 matrix-core recomputation", lower_bound=-4.0)
     monkeypatch.setenv("KDA_BWD_RECOMPUTE", "valu")
     _run(inp, d_o, d_fin, torch.bfloat16, "bf16 vector-ALU recomputation", lower_bound=-4.0)
+
+
+def test_bwd_bf16_element_aligned_inputs(monkeypatch):
+    """bf16 inputs that are 2-byte but not 16-byte aligned: the recomputation
+    falls back to the vector-ALU kernels (the matrix-core one reads 8-byte
+    pieces), bit for bit what KDA_BWD_RECOMPUTE=valu gives on aligned copies."""
+    _banner("bwd bf16 element-aligned inputs")
+    inp = to_device(synthetic.random_problem(45, 1, 150, 2, 128, 128, dtype=torch.bfloat16,
+                                             lengths=[70, 80], init_std=0.5))
+    d_o, d_fin = _upstream(inp, 16)
+
+    def shifted(t):
+        buf = torch.empty(t.numel() + 1, dtype=t.dtype, device=t.device)
+        out = buf[1:].view(t.shape)
+        out.copy_(t)
+        assert out.data_ptr() % 16 != 0
+        return out
+
+    mis = dict(inp)
+    for n in ("q", "k", "v", "gate", "beta"):
+        mis[n] = shifted(inp[n])
+    got, _ = _run(mis, shifted(d_o), d_fin, torch.bfloat16, "bf16 element-aligned")
+    monkeypatch.setenv("KDA_BWD_RECOMPUTE", "valu")
+    ref, _ = _run(inp, d_o, d_fin, torch.bfloat16, "bf16 aligned, vector-ALU recomputation")
+    for n in NAMES:
+        assert torch.equal(got[n], ref[n]), n
