@@ -8,9 +8,12 @@
 //
 // fp32 arithmetic after the recomputation.  For 64-token chunks the dense
 // per-chunk products (the two state passes, and the value-dimension, Y and
-// Tm^T dW products of the chunk kernel) run on fp32 matrix cores
-// (v_mfma_f32_16x16x4f32: fp32 operands, fp32 accumulation); the pairwise,
-// triangular and per-element work, and chunks of 16 or 32, stay on VALU.  The
+// Tm^T dW products of the chunk kernel) run on matrix cores: for fp32 inputs
+// on fp32 ones (v_mfma_f32_16x16x4f32); for bf16 inputs the state passes and
+// the value-dimension products on bf16 ones (v_mfma_f32_16x16x32_bf16) with
+// every fp32 operand split into bf16 hi + lo (within about 2^-16 of the fp32
+// product), fp32 accumulation throughout; the pairwise, triangular and
+// per-element work, and chunks of 16 or 32, stay on VALU.  The
 // decay factors and the gate's derivative use the hardware exponential,
 // logarithm and reciprocal (about one ulp on the result).  The forward's chunk
 // factors are recomputed first, with Akk and Tm kept: for fp32 inputs by the
@@ -114,18 +117,6 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
-// Element type of the recomputed W, U, Qt, Kbar and Aqk that the matrix-core
-// state passes read: fp32, or bf16 (FwdArgs::ws_bf16, bf16 inputs with 64-token
-// chunks), four elements held as one piece (float4, or two 32-bit words).
-template <bool WS16> struct Ws;
-template <> struct Ws<false> { typedef float E; typedef float4 P4; };
-template <> struct Ws<true> { typedef bf16 E; typedef uint2 P4; };
-__device__ inline float4 widen4(float4 v) { return v; }
-__device__ inline float4 widen4(uint2 u) {
-  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u),
-                     __uint_as_float(u.y << 16), __uint_as_float(u.y & 0xffff0000u));
-}
-
 // Copy n floats (n a multiple of 4, 16-byte aligned) from global memory to LDS
 // with a workgroup of nt threads.
 __device__ inline void stage(float* dst, const float* src, int n, int nt) {
@@ -218,12 +209,9 @@ __global__ __launch_bounds__(64 * state_waves(C)) void k_bwd_fstate(BwdArgs b) {
 // The forward state pass for 64-token chunks on fp32 matrix cores, same
 // arithmetic as k_bwd_fstate up to the order of additions: the state (K x 64
 // columns) lives in accumulator tiles, K/64 per wave; per chunk, wave w
-// computes one 16 x 16 tile of Delta (row tile w/4, column tile w%4).  WS16:
-// W, Kbar and U are stored as bf16 and widened to fp32 on their way to LDS.
-template <int K, bool WS16>
+// computes one 16 x 16 tile of Delta (row tile w/4, column tile w%4).
+template <int K>
 __global__ __launch_bounds__(1024) void k_bwd_fstate_mfma(BwdArgs b) {
-  typedef typename Ws<WS16>::E E;
-  typedef typename Ws<WS16>::P4 P4;
   constexpr int C = 64, NT = 1024, VT = 64;
   constexpr int TPW = K / 64;
   constexpr int SP = VT + 16, KP = K + 4;
@@ -244,21 +232,21 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_mfma(BwdArgs b) {
   // in flight while the previous chunk's products run)
   constexpr int NF4 = C * K / 4 / NT;
   static_assert(NF4 * NT * 4 == C * K && NF4 <= 2, "one or two float4 pieces per thread");
-  P4 pw0, pw1, pk0, pk1;      // named, so that they stay in registers
+  float4 pw0, pw1, pk0, pk1;  // named, so that they stay in registers
   f32x4 pu;                   // the chunk's U tile of this wave's Delta tile
   float pgl[TPW][4];          // its gL entries of this wave's state tiles
   const int drt = w >> 2, dct = w & 3;  // this wave's Delta tile
   auto fetch_wk = [&](int64_t chb) __attribute__((always_inline)) {
-    const E* U = (const E*)a.U + chb * C * V;
+    const float* U = (const float*)a.U + chb * C * V;
     const float* gL = a.gL + chb * K;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pu[e] = load_f32(U + (int64_t)(16 * drt + 4 * lg + e) * V + col0 + 16 * dct + ln);
+    for (int e = 0; e < 4; ++e) pu[e] = U[(int64_t)(16 * drt + 4 * lg + e) * V + col0 + 16 * dct + ln];
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
       for (int e = 0; e < 4; ++e) pgl[t][e] = gL[16 * ((w * TPW + t) >> 2) + 4 * lg + e];
-    const P4* W4 = (const P4*)((const E*)a.W + chb * C * K);
-    const P4* K4 = (const P4*)((const E*)a.Kb + chb * C * K);
+    const float4* W4 = (const float4*)((const float*)a.W + chb * C * K);
+    const float4* K4 = (const float4*)((const float*)a.Kb + chb * C * K);
     pw0 = W4[tid];
     pk0 = K4[tid];
     if constexpr (NF4 == 2) {
@@ -303,12 +291,12 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_mfma(BwdArgs b) {
     }
     {
       const int r0 = tid / (K / 4), c0 = 4 * (tid % (K / 4));
-      *(float4*)&sW[r0][c0] = widen4(pw0);
-      *(float4*)&sKb[r0][c0] = widen4(pk0);
+      *(float4*)&sW[r0][c0] = pw0;
+      *(float4*)&sKb[r0][c0] = pk0;
       if constexpr (NF4 == 2) {
         const int r1 = (tid + NT) / (K / 4), c1 = 4 * ((tid + NT) % (K / 4));
-        *(float4*)&sW[r1][c1] = widen4(pw1);
-        *(float4*)&sKb[r1][c1] = widen4(pk1);
+        *(float4*)&sW[r1][c1] = pw1;
+        *(float4*)&sKb[r1][c1] = pk1;
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -454,12 +442,9 @@ __global__ __launch_bounds__(64 * state_waves(C)) void k_bwd_dstate(BwdArgs b) {
 // row tile (w*TPW+t)/4, column tile (w*TPW+t)%4); per chunk, wave w computes
 // one 16 x 16 tile of dDelta (row tile w/4, column tile w%4).  Operands come
 // from LDS rows padded so that the 16 lanes of a fragment column hit
-// different banks.  WS16: Aqk, Kbar, Qt and W are stored as bf16 and widened
-// to fp32 on their way to LDS.
-template <typename Tin, int K, bool WS16>
+// different banks.
+template <typename Tin, int K>
 __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
-  typedef typename Ws<WS16>::E E;
-  typedef typename Ws<WS16>::P4 P4;
   constexpr int C = 64, NT = 1024, VT = 64;
   constexpr int TPW = K / 64;                     // state tiles per wave
   constexpr int SP = VT + 16, AP = C + 4, KP = K + 4;
@@ -486,7 +471,7 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
   // previous chunk's products run
   static_assert(C * C / 4 == NT && C * K / 4 <= 2 * NT, "one Aqk piece, one or two of the others");
   constexpr bool TWO = C * K / 4 == 2 * NT;
-  P4 pa, pk0, pk1, pq0, pq1, pw0, pw1;
+  float4 pa, pk0, pk1, pq0, pq1, pw0, pw1;
   // dO of the prefetched chunk, raw (rows past its end are masked when staged)
   constexpr int NO = C * VT / NT;
   static_assert(NO * NT == C * VT, "whole dO tiles per thread");
@@ -500,10 +485,10 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
       const int e = tid + u * NT, r = e / VT, cc = e % VT;
       po[u] = load_f32(dO + ((int64_t)(tokn + (r < Ln ? r : 0)) * H + h) * V + col0 + cc);
     }
-    const P4* A4 = (const P4*)((const E*)a.Aqk + chb * C * C);
-    const P4* K4 = (const P4*)((const E*)a.Kb + chb * C * K);
-    const P4* Q4 = (const P4*)((const E*)a.Qt + chb * C * K);
-    const P4* W4 = (const P4*)((const E*)a.W + chb * C * K);
+    const float4* A4 = (const float4*)((const float*)a.Aqk + chb * C * C);
+    const float4* K4 = (const float4*)((const float*)a.Kb + chb * C * K);
+    const float4* Q4 = (const float4*)((const float*)a.Qt + chb * C * K);
+    const float4* W4 = (const float4*)((const float*)a.W + chb * C * K);
     pa = A4[tid];
     pk0 = K4[tid];
     pq0 = Q4[tid];
@@ -515,9 +500,9 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
     }
   };
   // a [C][K] matrix held as pieces tid (and tid + NT) into LDS rows of stride KP
-  auto put_k = [&](float (*dst)[KP], const P4& v0, const P4& v1) __attribute__((always_inline)) {
-    *(float4*)&dst[tid / (K / 4)][4 * (tid % (K / 4))] = widen4(v0);
-    if constexpr (TWO) *(float4*)&dst[(tid + NT) / (K / 4)][4 * ((tid + NT) % (K / 4))] = widen4(v1);
+  auto put_k = [&](float (*dst)[KP], const float4& v0, const float4& v1) __attribute__((always_inline)) {
+    *(float4*)&dst[tid / (K / 4)][4 * (tid % (K / 4))] = v0;
+    if constexpr (TWO) *(float4*)&dst[(tid + NT) / (K / 4)][4 * ((tid + NT) % (K / 4))] = v1;
   };
   const int64_t sbase = ((int64_t)n * H + h) * K * V;
   f32x4 st[TPW];
@@ -555,7 +540,7 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
       const int e = tid + u * NT, r = e / VT, cc = e % VT;
       sO[r][cc] = r < L ? po[u] : 0.f;
     }
-    *(float4*)&sA[tid / (C / 4)][4 * (tid % (C / 4))] = widen4(pa);
+    *(float4*)&sA[tid / (C / 4)][4 * (tid % (C / 4))] = pa;
     put_k(sKb, pk0, pk1);
     __syncthreads();
     // dDelta = Aqk_s^T dO + Kbar dS_L (Aqk_s is zero above the diagonal, so
@@ -601,6 +586,329 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
         const int s = w * TPW + t, srt = s >> 2, sct = s & 3;
         st[t] = mfma_f32(sQt[r + lg][16 * srt + ln], sO[r + lg][16 * sct + ln], st[t]);
         st[t] = mfma_f32(-sW[r + lg][16 * srt + ln], sD[r + lg][16 * sct + ln], st[t]);
+      }
+    }
+  }
+  if (b.dinit) {
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int s = w * TPW + t, srt = s >> 2, sct = s & 3;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        b.dinit[sbase + (int64_t)(16 * srt + 4 * lg + e) * V + col0 + 16 * sct + ln] = st[t][e];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// State passes on bf16 matrix cores (FwdArgs::ws_bf16: W, U, Qt, Kbar and Aqk
+// recomputed as bf16).  Those operands enter the products exactly; the fp32
+// state (or state gradient) and Delta (or dDelta) enter as bf16 hi + lo pairs
+// (hi = bf16(x), lo = bf16(x - hi): within 2^-17 of x), so each product is
+// two v_mfma_f32_16x16x32_bf16 per 32-long k-step with fp32 accumulation,
+// against eight fp32 steps of 4.  Operands are staged in LDS so that every
+// lane's 8 k-consecutive elements are one 16-byte read: row-major where the
+// k index runs along a row, transposed otherwise.  Layout as in the fp32
+// passes: one workgroup of 16 waves per (sequence, head, 64 columns), the
+// K x 64 state in accumulator tiles (K/64 per wave: state row tile
+// (w*TPW+t)/4, column tile (w*TPW+t)%4), wave w owning the (w/4, w%4) tile of
+// the chunk's Delta.
+// ---------------------------------------------------------------------------
+// 4 fp32 -> 4 bf16 hi and 4 bf16 lo (as two 32-bit words each)
+__device__ __forceinline__ void split4_bf16(f32x4 x, uint2& hi, uint2& lo) {
+  typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  bf16x4_t h, l;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    h[e] = (__bf16)x[e];
+    l[e] = (__bf16)(x[e] - (float)h[e]);
+  }
+  const u32x2 hu = __builtin_bit_cast(u32x2, h), lu = __builtin_bit_cast(u32x2, l);
+  hi = make_uint2(hu.x, hu.y);
+  lo = make_uint2(lu.x, lu.y);
+}
+// element q of 4 bf16 held as two 32-bit words
+__device__ __forceinline__ bf16 elem4(uint2 u, int q) {
+  return (bf16)(((q < 2 ? u.x : u.y) >> (16 * (q & 1))) & 0xffffu);
+}
+
+template <int K>
+__global__ __launch_bounds__(1024) void k_bwd_fstate_bf(BwdArgs b) {
+  constexpr int C = 64, NT = 1024, VT = 64;
+  constexpr int TPW = K / 64;
+  constexpr int WP = K + 8, TP = C + 8;  // bf16 row strides, multiples of 16 bytes
+  const FwdArgs& a = b.f;
+  const int H = a.H, V = a.V;
+  const int ntile = V / VT;
+  const int64_t wid = blockIdx.x;
+  const int tile = (int)(wid % ntile);
+  const int64_t nh = wid / ntile;
+  const int h = (int)(nh % H), n = (int)(nh / H);
+  const int col0 = tile * VT;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
+  __shared__ __attribute__((aligned(16))) bf16 sWn[C][WP];             // -W
+  __shared__ __attribute__((aligned(16))) bf16 sKbT[K][TP];            // Kbar^T
+  __shared__ __attribute__((aligned(16))) bf16 sSh[VT][WP], sSl[VT][WP];  // S^T hi, lo
+  __shared__ __attribute__((aligned(16))) bf16 sDh[VT][TP], sDl[VT][TP];  // Delta^T hi, lo
+  // W and Kbar (4 bf16 per piece, two pieces per thread), this wave's U tile
+  // and gL entries: one chunk ahead, in named registers
+  constexpr int NP = C * K / 4 / NT;
+  static_assert(NP == 1 || NP == 2, "one or two pieces per thread");
+  uint2 pw0, pw1, pk0, pk1;
+  f32x4 pu;
+  float pgl[TPW][4];
+  const int drt = w >> 2, dct = w & 3;
+  auto fetch = [&](int64_t chb) __attribute__((always_inline)) {
+    const bf16* U = (const bf16*)a.U + chb * C * V;
+    const float* gL = a.gL + chb * K;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) pu[e] = load_f32(U + (int64_t)(16 * drt + 4 * lg + e) * V + col0 + 16 * dct + ln);
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) pgl[t][e] = gL[16 * ((w * TPW + t) >> 2) + 4 * lg + e];
+    const uint2* W4 = (const uint2*)((const bf16*)a.W + chb * C * K);
+    const uint2* K4 = (const uint2*)((const bf16*)a.Kb + chb * C * K);
+    pw0 = W4[tid];
+    pk0 = K4[tid];
+    if constexpr (NP == 2) {
+      pw1 = W4[tid + NT];
+      pk1 = K4[tid + NT];
+    }
+  };
+  auto put = [&](int p, uint2 wv, uint2 kv) __attribute__((always_inline)) {
+    const int r = p / (K / 4), c = 4 * (p % (K / 4));
+    *(uint2*)&sWn[r][c] = make_uint2(wv.x ^ 0x80008000u, wv.y ^ 0x80008000u);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) sKbT[c + q][r] = elem4(kv, q);
+  };
+  const int64_t sbase = ((int64_t)n * H + h) * K * V;
+  f32x4 st[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int s = w * TPW + t, srt = s >> 2, sct = s & 3;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = 16 * srt + 4 * lg + e, col = col0 + 16 * sct + ln;
+      st[t][e] = a.init ? a.init[sbase + (int64_t)c * V + col] : 0.f;
+    }
+  }
+  const int jc0 = a.seq_chunk0[n], jc1 = a.seq_chunk0[n + 1];
+  if (jc0 < jc1) fetch((int64_t)jc0 * H + h);
+  for (int j = jc0; j < jc1; ++j) {
+    const int64_t chb = (int64_t)j * H + h;
+    float* hc = b.hc + chb * K * V;
+    float* Dc = b.Dc + chb * C * V;
+    f32x4 acc = pu;
+    float gl[TPW][4];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gl[t][e] = pgl[t][e];
+    __syncthreads();  // the previous chunk is done with the LDS operands
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int s = w * TPW + t, srt = s >> 2, sct = s & 3;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        hc[(int64_t)(16 * srt + 4 * lg + e) * V + col0 + 16 * sct + ln] = st[t][e];
+      uint2 hi, lo;
+      split4_bf16(st[t], hi, lo);
+      *(uint2*)&sSh[16 * sct + ln][16 * srt + 4 * lg] = hi;
+      *(uint2*)&sSl[16 * sct + ln][16 * srt + 4 * lg] = lo;
+    }
+    put(tid, pw0, pk0);
+    if constexpr (NP == 2) put(tid + NT, pw1, pk1);
+    __builtin_amdgcn_sched_barrier(0);
+    // the next chunk of this sequence (the last chunk reads itself again, unused)
+    fetch(j + 1 < jc1 ? chb + H : chb);
+    __syncthreads();
+    // Delta = U - W S
+#pragma unroll
+    for (int c0 = 0; c0 < K; c0 += 32) {
+      const bf16x8 wa = frag8(&sWn[16 * drt + ln][c0 + 8 * lg]);
+      acc = mfma_bf16(wa, frag8(&sSh[16 * dct + ln][c0 + 8 * lg]), acc);
+      acc = mfma_bf16(wa, frag8(&sSl[16 * dct + ln][c0 + 8 * lg]), acc);
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Dc[(int64_t)(16 * drt + 4 * lg + e) * V + col0 + 16 * dct + ln] = acc[e];
+    {
+      uint2 hi, lo;
+      split4_bf16(acc, hi, lo);
+      *(uint2*)&sDh[16 * dct + ln][16 * drt + 4 * lg] = hi;
+      *(uint2*)&sDl[16 * dct + ln][16 * drt + 4 * lg] = lo;
+    }
+    __syncthreads();
+    // S = Diag(gL) S + Kbar^T Delta (rows past the chunk end are zero)
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st[t][e] *= gl[t][e];
+#pragma unroll
+    for (int r0 = 0; r0 < C; r0 += 32) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int s = w * TPW + t, srt = s >> 2, sct = s & 3;
+        const bf16x8 ka = frag8(&sKbT[16 * srt + ln][r0 + 8 * lg]);
+        st[t] = mfma_bf16(ka, frag8(&sDh[16 * sct + ln][r0 + 8 * lg]), st[t]);
+        st[t] = mfma_bf16(ka, frag8(&sDl[16 * sct + ln][r0 + 8 * lg]), st[t]);
+      }
+    }
+  }
+}
+
+template <int K>
+__global__ __launch_bounds__(1024) void k_bwd_dstate_bf(BwdArgs b) {
+  constexpr int C = 64, NT = 1024, VT = 64;
+  constexpr int TPW = K / 64;
+  constexpr int WP = K + 8, TP = C + 8;
+  const FwdArgs& a = b.f;
+  const int H = a.H, V = a.V;
+  const int ntile = V / VT;
+  const int64_t wid = blockIdx.x;
+  const int tile = (int)(wid % ntile);
+  const int64_t nh = wid / ntile;
+  const int h = (int)(nh % H), n = (int)(nh / H);
+  const int col0 = tile * VT;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
+  __shared__ __attribute__((aligned(16))) bf16 sAT[C][TP];   // Aqk_s^T
+  __shared__ __attribute__((aligned(16))) bf16 sKb[C][WP];   // Kbar
+  __shared__ __attribute__((aligned(16))) bf16 sQT[K][TP];   // Qt_s^T
+  __shared__ __attribute__((aligned(16))) bf16 sWT[K][TP];   // -W^T
+  __shared__ __attribute__((aligned(16))) bf16 sOT[VT][TP];  // dO^T (rows past the chunk end zero)
+  __shared__ __attribute__((aligned(16))) bf16 sSh[VT][WP], sSl[VT][WP];  // dS^T hi, lo
+  __shared__ __attribute__((aligned(16))) bf16 sDh[VT][TP], sDl[VT][TP];  // dDelta^T hi, lo
+  constexpr int NP = C * K / 4 / NT;
+  static_assert(NP == 1 || NP == 2, "one or two pieces per thread");
+  static_assert(C * C / 4 == NT, "one Aqk piece per thread");
+  uint2 pa, pk0, pk1, pq0, pq1, pw0, pw1;
+  constexpr int NO = C * VT / NT;
+  static_assert(NO * NT == C * VT, "whole dO tiles per thread");
+  const bf16* dO = (const bf16*)b.d_o;
+  bf16 po[NO];
+  auto fetch = [&](int jn) __attribute__((always_inline)) {
+    const int64_t chb = (int64_t)jn * H + h;
+    const int tokn = a.chunk_tok[jn], Ln = a.chunk_len[jn];
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+      const int e = tid + u * NT, r = e / VT, cc = e % VT;
+      po[u] = dO[((int64_t)(tokn + (r < Ln ? r : 0)) * H + h) * V + col0 + cc];
+    }
+    const uint2* A4 = (const uint2*)((const bf16*)a.Aqk + chb * C * C);
+    const uint2* K4 = (const uint2*)((const bf16*)a.Kb + chb * C * K);
+    const uint2* Q4 = (const uint2*)((const bf16*)a.Qt + chb * C * K);
+    const uint2* W4 = (const uint2*)((const bf16*)a.W + chb * C * K);
+    pa = A4[tid];
+    pk0 = K4[tid];
+    pq0 = Q4[tid];
+    pw0 = W4[tid];
+    if constexpr (NP == 2) {
+      pk1 = K4[tid + NT];
+      pq1 = Q4[tid + NT];
+      pw1 = W4[tid + NT];
+    }
+  };
+  auto put = [&](int p, uint2 kv, uint2 qv, uint2 wv) __attribute__((always_inline)) {
+    const int r = p / (K / 4), c = 4 * (p % (K / 4));
+    *(uint2*)&sKb[r][c] = kv;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      sQT[c + q][r] = elem4(qv, q);
+      sWT[c + q][r] = elem4(wv, q) ^ 0x8000u;
+    }
+  };
+  const int64_t sbase = ((int64_t)n * H + h) * K * V;
+  f32x4 st[TPW];
+#pragma unroll
+  for (int t = 0; t < TPW; ++t) {
+    const int s = w * TPW + t, srt = s >> 2, sct = s & 3;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int c = 16 * srt + 4 * lg + e, col = col0 + 16 * sct + ln;
+      st[t][e] = b.d_fin ? b.d_fin[sbase + (int64_t)c * V + col] : 0.f;
+    }
+  }
+  const int drt = w >> 2, dct = w & 3;
+  const int jc0 = a.seq_chunk0[n], jc1 = a.seq_chunk0[n + 1];
+  if (jc0 < jc1) fetch(jc1 - 1);
+  for (int j = jc1 - 1; j >= jc0; --j) {
+    const int64_t chb = (int64_t)j * H + h;
+    const float* gL = a.gL + chb * K;
+    float* dhc = b.dhc + chb * K * V;
+    float* dDc = b.dDc + chb * C * V;
+    const int L = a.chunk_len[j];
+    __syncthreads();  // the previous chunk is done with the LDS operands
+#pragma unroll
+    for (int t = 0; t < TPW; ++t) {
+      const int s = w * TPW + t, srt = s >> 2, sct = s & 3;
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+        dhc[(int64_t)(16 * srt + 4 * lg + e) * V + col0 + 16 * sct + ln] = st[t][e];
+      uint2 hi, lo;
+      split4_bf16(st[t], hi, lo);
+      *(uint2*)&sSh[16 * sct + ln][16 * srt + 4 * lg] = hi;
+      *(uint2*)&sSl[16 * sct + ln][16 * srt + 4 * lg] = lo;
+    }
+#pragma unroll
+    for (int u = 0; u < NO; ++u) {
+      const int e = tid + u * NT, r = e / VT, cc = e % VT;
+      sOT[cc][r] = r < L ? po[u] : (bf16)0;
+    }
+    {
+      const int rr = tid / (C / 4), i = 4 * (tid % (C / 4));
+#pragma unroll
+      for (int q = 0; q < 4; ++q) sAT[i + q][rr] = elem4(pa, q);
+    }
+    put(tid, pk0, pq0, pw0);
+    if constexpr (NP == 2) put(tid + NT, pk1, pq1, pw1);
+    float gl[TPW][4];
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) gl[t][e] = gL[16 * ((w * TPW + t) >> 2) + 4 * lg + e];
+    // the previous chunk of this sequence, after gL's loads (held there by the
+    // scheduling barrier) so that waiting for gL leaves it in flight; the
+    // first chunk reads itself again, unused
+    __builtin_amdgcn_sched_barrier(0);
+    fetch(j - 1 >= jc0 ? j - 1 : j);
+    __syncthreads();
+    // dDelta = Aqk_s^T dO + Kbar dS_L (Aqk_s[rr][r] is zero for rr < r: the
+    // row tiles from 32 on skip the first k-step)
+    {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int r0 = 0; r0 < C; r0 += 32)
+        if (16 * drt < r0 + 32)
+          acc = mfma_bf16(frag8(&sAT[16 * drt + ln][r0 + 8 * lg]), frag8(&sOT[16 * dct + ln][r0 + 8 * lg]), acc);
+#pragma unroll
+      for (int c0 = 0; c0 < K; c0 += 32) {
+        const bf16x8 ka = frag8(&sKb[16 * drt + ln][c0 + 8 * lg]);
+        acc = mfma_bf16(ka, frag8(&sSh[16 * dct + ln][c0 + 8 * lg]), acc);
+        acc = mfma_bf16(ka, frag8(&sSl[16 * dct + ln][c0 + 8 * lg]), acc);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dDc[(int64_t)(16 * drt + 4 * lg + e) * V + col0 + 16 * dct + ln] = acc[e];
+      uint2 hi, lo;
+      split4_bf16(acc, hi, lo);
+      *(uint2*)&sDh[16 * dct + ln][16 * drt + 4 * lg] = hi;
+      *(uint2*)&sDl[16 * dct + ln][16 * drt + 4 * lg] = lo;
+    }
+    __syncthreads();
+    // dS0 = Diag(gL) dS_L + Qt_s^T dO - W^T dDelta (rows past the chunk end are zero)
+#pragma unroll
+    for (int t = 0; t < TPW; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) st[t][e] *= gl[t][e];
+#pragma unroll
+    for (int r0 = 0; r0 < C; r0 += 32) {
+#pragma unroll
+      for (int t = 0; t < TPW; ++t) {
+        const int s = w * TPW + t, srt = s >> 2, sct = s & 3;
+        st[t] = mfma_bf16(frag8(&sQT[16 * srt + ln][r0 + 8 * lg]), frag8(&sOT[16 * sct + ln][r0 + 8 * lg]), st[t]);
+        const bf16x8 wa = frag8(&sWT[16 * srt + ln][r0 + 8 * lg]);
+        st[t] = mfma_bf16(wa, frag8(&sDh[16 * sct + ln][r0 + 8 * lg]), st[t]);
+        st[t] = mfma_bf16(wa, frag8(&sDl[16 * sct + ln][r0 + 8 * lg]), st[t]);
       }
     }
   }
@@ -1673,11 +1981,11 @@ hipError_t run(const BwdArgs& b, hipStream_t s) {
     if constexpr (C == 64) {
       const dim3 g((unsigned)wgs), t(1024);
       if (a.ws_bf16) {
-        if (a.K == 64) hipLaunchKernelGGL((k_bwd_fstate_mfma<64, true>), g, t, 0, s, b);
-        else hipLaunchKernelGGL((k_bwd_fstate_mfma<128, true>), g, t, 0, s, b);
+        if (a.K == 64) hipLaunchKernelGGL((k_bwd_fstate_bf<64>), g, t, 0, s, b);
+        else hipLaunchKernelGGL((k_bwd_fstate_bf<128>), g, t, 0, s, b);
       } else {
-        if (a.K == 64) hipLaunchKernelGGL((k_bwd_fstate_mfma<64, false>), g, t, 0, s, b);
-        else hipLaunchKernelGGL((k_bwd_fstate_mfma<128, false>), g, t, 0, s, b);
+        if (a.K == 64) hipLaunchKernelGGL((k_bwd_fstate_mfma<64>), g, t, 0, s, b);
+        else hipLaunchKernelGGL((k_bwd_fstate_mfma<128>), g, t, 0, s, b);
       }
     } else {
       if (a.K == 64) hipLaunchKernelGGL((k_bwd_fstate<C, 64>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
@@ -1692,11 +2000,11 @@ hipError_t run(const BwdArgs& b, hipStream_t s) {
     if constexpr (C == 64) {
       const dim3 g((unsigned)wgs), t(1024);
       if (a.ws_bf16) {
-        if (a.K == 64) hipLaunchKernelGGL((k_bwd_dstate_mfma<Tin, 64, true>), g, t, 0, s, b);
-        else hipLaunchKernelGGL((k_bwd_dstate_mfma<Tin, 128, true>), g, t, 0, s, b);
+        if (a.K == 64) hipLaunchKernelGGL((k_bwd_dstate_bf<64>), g, t, 0, s, b);
+        else hipLaunchKernelGGL((k_bwd_dstate_bf<128>), g, t, 0, s, b);
       } else {
-        if (a.K == 64) hipLaunchKernelGGL((k_bwd_dstate_mfma<Tin, 64, false>), g, t, 0, s, b);
-        else hipLaunchKernelGGL((k_bwd_dstate_mfma<Tin, 128, false>), g, t, 0, s, b);
+        if (a.K == 64) hipLaunchKernelGGL((k_bwd_dstate_mfma<Tin, 64>), g, t, 0, s, b);
+        else hipLaunchKernelGGL((k_bwd_dstate_mfma<Tin, 128>), g, t, 0, s, b);
       }
     } else {
       if (a.K == 64) hipLaunchKernelGGL((k_bwd_dstate<Tin, C, 64>), dim3((unsigned)wgs), dim3(NTS), 0, s, b);
