@@ -254,6 +254,9 @@ def test_bwd_bf16_both_recomputations(monkeypatch, K, V):
     d_o, d_fin = _upstream(inp, 15)
     monkeypatch.delenv("KDA_BWD_RECOMPUTE", raising=False)
     _run(inp, d_o, d_fin, torch.bfloat16, "bf16 matrix-core recomputation", lower_bound=-4.0)
+    monkeypatch.setenv("KDA_BWD_RECOMPUTE", "mfma32")
+    _run(inp, d_o, d_fin, torch.bfloat16, "bf16 matrix-core recomputation, fp32 arrays",
+         lower_bound=-4.0)
     monkeypatch.setenv("KDA_BWD_RECOMPUTE", "valu")
     _run(inp, d_o, d_fin, torch.bfloat16, "bf16 vector-ALU recomputation", lower_bound=-4.0)
 

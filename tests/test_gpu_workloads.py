@@ -158,6 +158,45 @@ def test_workload3_backward_sampled():
         assert err <= 2e-2 * scale_ and rf <= 1e-2, n
 
 
+def test_workload5_backward_sampled():
+    """The backward on the short-documents workload at full size (644 packed
+    documents of 1-100 tokens, d = 64, sigmoid-bounded gate): every document of
+    two heads against the oracle's reverse mode, to the same bf16 tolerance."""
+    import oracle
+    w = synthetic.WORKLOADS[5]
+    _banner("workload 5 backward")
+    inp = synthetic.make_inputs(w, DEV)
+    gen = torch.Generator(device=DEV)
+    gen.manual_seed(7)
+    d_o = torch.randn(w.B, w.T, w.H, w.V, generator=gen, device=DEV).to(w.torch_dtype)
+    cu = inp["cu_seqlens"]
+    got = kda.kda_bwd(inp["q"], inp["k"], inp["v"], inp["gate"], inp["beta"], inp["a_log"],
+                      inp["dt_bias"], d_o, None, scale=w.scale, lower_bound=w.lower_bound,
+                      cu_seqlens=cu, cu_seqlens_host=cu.cpu(), initial_state=inp["initial_state"])
+    torch.cuda.synchronize()
+    heads = [0, w.H - 1]
+    cut = lambda t: to_np(t[:, :, heads])
+    init = inp["initial_state"]
+    ref = oracle.kda_bwd(cut(inp["q"]), cut(inp["k"]), cut(inp["v"]), cut(inp["gate"]),
+                         cut(inp["beta"]), to_np(inp["a_log"][heads]),
+                         to_np(inp["dt_bias"][heads]), cut(d_o), None, scale=w.scale,
+                         lower_bound=w.lower_bound, gate_mode="sigmoid",
+                         cu_seqlens=to_np(cu).astype(np.int32),
+                         initial_state=None if init is None else to_np(init[:, heads]), threads=8)
+    sel = {"dq": cut(got["dq"]), "dk": cut(got["dk"]), "dv": cut(got["dv"]),
+           "dgate": cut(got["dgate"]), "dbeta": to_np(got["dbeta"][:, :, heads]),
+           "da_log": to_np(got["da_log"][heads]), "ddt_bias": to_np(got["ddt_bias"][heads]),
+           "dinit": to_np(got["dinit"][:, heads])}
+    for n, g in sel.items():
+        r = ref[n]
+        scale_ = max(1.0, float(np.abs(r).max()))
+        err = float(np.abs(g - r).max())
+        rf = float(np.linalg.norm(g - r) / max(1e-30, np.linalg.norm(r)))
+        print("workload 5 backward %s: max-abs %.3g (scale %.3g) rel-F %.3g" % (n, err, scale_, rf),
+              flush=True)
+        assert err <= 2e-2 * scale_ and rf <= 1e-2, n
+
+
 def test_workload3_output_norm_sampled():
     """The gated output norm on the forward output's full shape (the benchmark's
     output_norm configuration); sampled rows against the oracle, each within one
