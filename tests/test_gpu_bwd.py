@@ -246,7 +246,7 @@ def test_bwd_bf16_extreme_gates_exact_path():
     _run(inp, d_o, d_fin, torch.bfloat16, "bf16 extreme gates")
 
 
-@pytest.mark.parametrize("K,V", [(128, 128), (64, 128)])
+@pytest.mark.parametrize("K,V", [(128, 128), (64, 128), (128, 64)])
 def test_bwd_bf16_both_recomputations(monkeypatch, K, V):
     _banner("bwd bf16 recomputation kernels K=%d V=%d" % (K, V))
     inp = to_device(synthetic.random_problem(44, 1, 300, 2, K, V, dtype=torch.bfloat16,
