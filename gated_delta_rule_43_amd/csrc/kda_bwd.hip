@@ -1028,19 +1028,221 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     }
   }
 
-  // ---- phase B: products over the value dimension, and dV, in two sweeps over
-  //      32-column value tiles staged in LDS (dW and dQ~; then dKbar, P, the V
-  //      half of Y and dV).  For C = 64 the products run on the matrix cores in
-  //      fp32 (v_mfma_f32_16x16x4f32, one 16 x 16 output tile per accumulator;
-  //      lane l holds A[l%16][l/16], B[l/16][l%16] and D[4(l/16)+e][l%16]),
-  //      each wave owning fixed output tiles; results reach the thread layouts
-  //      below through LDS.  Smaller chunks keep per-thread VALU accumulators.
+  // ---- phase B: products over the value dimension, and dV, over 32-column
+  //      value tiles staged in LDS (dW, dQ~, dKbar, P, the V half of Y and
+  //      dV).  For C = 64 the products run on the matrix cores, each wave
+  //      owning fixed 16 x 16 output tiles, the results reaching the thread
+  //      layouts below through LDS: for bf16 inputs in one sweep on bf16
+  //      matrix cores with split operands (below); for fp32 inputs in two
+  //      sweeps (dW and dQ~; then dKbar, P, Y and dV) in fp32
+  //      (v_mfma_f32_16x16x4f32: lane l holds A[l%16][l/16], B[l/16][l%16] and
+  //      D[4(l/16)+e][l%16]).  Smaller chunks keep per-thread VALU accumulators.
   const int c1 = tid % K, rb1 = tid / K;       // C x K layout
   const int i2 = tid % C, rb2 = tid / C;       // C x C layout
   Tin* dv = (Tin*)b.dv;
   float dqs[NE1];  // scale dO S0^T, kept until phase F
   float dkb[NE1], sd = 0.f;
-  if constexpr (C == 64) {
+  if constexpr (BF) {
+    // bf16 inputs: one sweep over 32-column value tiles.  Each tile of S0,
+    // dS_L, Delta and dDelta reaches LDS as bf16 hi + lo pairs (dO and V
+    // exactly), rows padded to BP (16-byte fragment reads), and is one k-step
+    // of every product on the bf16 matrix cores (hi*hi + hi*lo + lo*hi per
+    // pair of split operands, fp32 accumulation):
+    //   M1 = dDelta S0^T (-> -dW), M2 = dO S0^T (-> dQ~), M3 = Delta dS_L^T (-> dKbar),
+    //   P = dO Delta^T and Yv = dDelta V^T (lower tiles); dV = Diag(beta) Tm^T dDelta
+    //   on the fp32 matrix cores with dDelta from its pair.
+    // Each tile reaches registers one tile ahead of its products;
+    // rowsum(S0 . dS_L) comes from those registers (row (tid + NT u) / VTL,
+    // column tid % VTL).
+    constexpr int NW = NT / 64;
+    const int lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
+    static_assert(2 * NW * 16 * 16 == C * K, "two output tiles per wave and product");
+    static_assert(VTL == 32, "one bf16 k-step per value tile");
+    const int rt = w & 3, ct0 = 2 * (w >> 2);  // M1..M3 tiles: row tile rt, column tiles ct0, ct0 + 1
+    constexpr int NS = K * VTL / NT, NR = C * VTL / NT;
+    static_assert(NS * NT == K * VTL && NR * NT == C * VTL, "whole tiles per thread");
+    constexpr int BP = VTL + 8;
+    bf16 (*hS0)[BP] = (bf16(*)[BP])sReg;
+    bf16 (*lS0)[BP] = hS0 + K;
+    bf16 (*hSL)[BP] = lS0 + K;
+    bf16 (*lSL)[BP] = hSL + K;
+    bf16 (*hD)[BP] = lSL + K;
+    bf16 (*lD)[BP] = hD + C;
+    bf16 (*hdD)[BP] = lD + C;
+    bf16 (*ldD)[BP] = hdD + C;
+    bf16 (*hdO)[BP] = ldD + C;
+    bf16 (*hv)[BP] = hdO + C;
+    static_assert((4 * K + 6 * C) * BP * 2 <= kRegion * 4, "the tiles fit the region");
+    constexpr int NTRI = 10;                  // lower 16 x 16 tiles (rt >= it) of a 64 x 64 matrix
+    constexpr int NPY = (NTRI + NW - 1) / NW;  // P and Yv tile pairs per wave
+    auto tri_tile = [](int t, int& r, int& i) {  // t = R (R + 1) / 2 + I, I <= R
+      r = t >= 6 ? 3 : t >= 3 ? 2 : t >= 1 ? 1 : 0;
+      i = t - r * (r + 1) / 2;
+    };
+    // dV tile of this wave (waves 0..7): row tile w / 2, column tile w % 2 of the value tile
+    const bool has_dv = w < 8;
+    const int vrt = (w >> 1) & 3, vct = w & 1;
+    f32x4 m1[2], m2[2], m3[2], pt[NPY], yt[NPY];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) m1[t] = m2[t] = m3[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < NPY; ++u) pt[u] = yt[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float ps[NS], pl[NS], pD[NR], pd[NR], po[NR], pv[NR], sdp[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) sdp[u] = 0.f;
+    auto fetch = [&](int j0) __attribute__((always_inline)) {
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        const int e = tid + NT * u, c = e / VTL, jj = e % VTL;
+        ps[u] = S0[(int64_t)c * V + j0 + jj];
+        pl[u] = dSL[(int64_t)c * V + j0 + jj];
+      }
+#pragma unroll
+      for (int u = 0; u < NR; ++u) {
+        const int e = tid + NT * u, r = e / VTL, jj = e % VTL;
+        const bool in = r < L;
+        pd[u] = dDl[(int64_t)r * V + j0 + jj];
+        pD[u] = Dl[(int64_t)r * V + j0 + jj];
+        const int64_t rv = th(in ? r : 0) * V + j0 + jj;
+        const float xo = load_f32(dO + rv), xv = load_f32(v + rv);
+        po[u] = in ? xo : 0.f;
+        pv[u] = in ? xv : 0.f;
+      }
+    };
+    fetch(0);
+    for (int j0 = 0; j0 < V; j0 += VTL) {
+      __syncthreads();  // the previous tile's products are done
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        const int e = tid + NT * u, c = e / VTL, jj = e % VTL;
+        split_bf16(ps[u], hS0[c][jj], lS0[c][jj]);
+        split_bf16(pl[u], hSL[c][jj], lSL[c][jj]);
+        sdp[u] = fmaf(ps[u], pl[u], sdp[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < NR; ++u) {
+        const int e = tid + NT * u, r = e / VTL, jj = e % VTL;
+        split_bf16(pd[u], hdD[r][jj], ldD[r][jj]);
+        split_bf16(pD[u], hD[r][jj], lD[r][jj]);
+        hdO[r][jj] = to_bf16(po[u]);
+        hv[r][jj] = to_bf16(pv[u]);
+      }
+      if (j0 + VTL < V) fetch(j0 + VTL);
+      __syncthreads();
+      {
+        const int ar = 16 * rt + ln;
+        const bf16x8 dh = frag8(&hdD[ar][8 * lg]), dl = frag8(&ldD[ar][8 * lg]);
+        const bf16x8 o8 = frag8(&hdO[ar][8 * lg]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int cr = 16 * (ct0 + t) + ln;
+          const bf16x8 sh = frag8(&hS0[cr][8 * lg]), sl = frag8(&lS0[cr][8 * lg]);
+          m1[t] = mfma_bf16(dh, sh, m1[t]);
+          m1[t] = mfma_bf16(dh, sl, m1[t]);
+          m1[t] = mfma_bf16(dl, sh, m1[t]);
+          m2[t] = mfma_bf16(o8, sh, m2[t]);
+          m2[t] = mfma_bf16(o8, sl, m2[t]);
+        }
+      }
+      {
+        const int ar = 16 * rt + ln;
+        const bf16x8 Dh = frag8(&hD[ar][8 * lg]), Dl8 = frag8(&lD[ar][8 * lg]);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int cr = 16 * (ct0 + t) + ln;
+          const bf16x8 Lh = frag8(&hSL[cr][8 * lg]), Ll = frag8(&lSL[cr][8 * lg]);
+          m3[t] = mfma_bf16(Dh, Lh, m3[t]);
+          m3[t] = mfma_bf16(Dh, Ll, m3[t]);
+          m3[t] = mfma_bf16(Dl8, Lh, m3[t]);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < NPY; ++u) {
+        const int t = w + NW * u;
+        if (t < NTRI) {
+          int R, I;
+          tri_tile(t, R, I);
+          const bf16x8 o8 = frag8(&hdO[16 * R + ln][8 * lg]);
+          pt[u] = mfma_bf16(o8, frag8(&hD[16 * I + ln][8 * lg]), pt[u]);
+          pt[u] = mfma_bf16(o8, frag8(&lD[16 * I + ln][8 * lg]), pt[u]);
+          const bf16x8 v8 = frag8(&hv[16 * I + ln][8 * lg]);
+          yt[u] = mfma_bf16(frag8(&hdD[16 * R + ln][8 * lg]), v8, yt[u]);
+          yt[u] = mfma_bf16(frag8(&ldD[16 * R + ln][8 * lg]), v8, yt[u]);
+        }
+      }
+      if (has_dv) {
+        // dV rows 16 vrt .. + 15, value columns j0 + 16 vct .. + 15: the sum over
+        // a >= r of Tm[a][r] dDelta[a][j] (Tm is lower triangular)
+        f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int a0 = 16 * vrt; a0 < C; a0 += 4) {
+          const int ar = a0 + lg, ac = 16 * vct + ln;
+          acc = mfma_f32(sT[ar][16 * vrt + ln], bf16_to_f32(hdD[ar][ac]) + bf16_to_f32(ldD[ar][ac]), acc);
+        }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * vrt + 4 * lg + e;
+          if (r < L) store_as(dv + th(r) * V + j0 + 16 * vct + ln, sB[r] * acc[e]);
+        }
+      }
+    }
+    // rowsum(S0 . dS_L): each row's 32 columns sit in one half-wave
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      float x = sdp[u];
+#pragma unroll
+      for (int off = 16; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+      if (tid % VTL == 0) sSd[(tid + NT * u) / VTL] = x;
+    }
+    __syncthreads();  // the tiles are dead: dW, then dQ~ and dKbar on their way to registers
+    float (*sX)[K] = (float(*)[K])(sReg + C * K);
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int r = 16 * rt + 4 * lg + e, c = 16 * (ct0 + t) + ln;
+        sDW[r][c] = -m1[t][e];
+        sX[r][c] = scale * m2[t][e];
+      }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NE1; ++m) dqs[m] = sX[rb1 + RSTEP1 * m][c1];
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sX[16 * rt + 4 * lg + e][16 * (ct0 + t) + ln] = m3[t][e];
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < NE1; ++m) dkb[m] = sX[rb1 + RSTEP1 * m][c1];
+    __syncthreads();  // sX is dead: P, Y and K~^T take its place
+#pragma unroll
+    for (int m = 0; m < NE1; ++m) {
+      const int r = rb1 + RSTEP1 * m;
+      const float x = a.kn[th(r < L ? r : 0) * K + c1];
+      sKtT[c1][r] = r < L ? x * __expf(sGam[r][c1]) : 0.f;
+    }
+    // P (scaled) and the V half of Y, lower triangle i <= r < L; zero elsewhere
+    for (int e = tid; e < C * C; e += NT) {
+      const int r = e / C, i = e % C;
+      if ((i >> 4) > (r >> 4)) sP[r][i] = sY[r][i] = 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < NPY; ++u) {
+      const int t = w + NW * u;
+      if (t < NTRI) {
+        int R, I;
+        tri_tile(t, R, I);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 16 * R + 4 * lg + e, i = 16 * I + ln;
+          const bool low = i <= r && r < L;
+          sP[r][i] = low ? scale * pt[u][e] : 0.f;
+          sY[r][i] = low ? yt[u][e] : 0.f;
+        }
+      }
+    }
+    __syncthreads();
+  } else if constexpr (C == 64) {
     constexpr int NW = NT / 64;
     const int lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
     // dW, dQ~ and dKbar tiles: row tile rt, column tiles 2 (w / 4) + {0, 1}
@@ -1055,17 +1257,11 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     constexpr int NS = K * VTL / NT, NR = C * VTL / NT;
     static_assert(NS * NT == K * VTL && NR * NT == C * VTL, "whole tiles per thread");
     float ps[NS], pd[NR], po[NR];
-    // bf16 inputs: dS_L too, for rowsum(S0 . dS_L) from the registers the
-    // tiles are staged from (row (tid + NT u) / VTL, column tid % VTL)
-    float pl[BF ? NS : 1], sdp[BF ? NS : 1];
-#pragma unroll
-    for (int u = 0; u < (BF ? NS : 1); ++u) sdp[u] = 0.f;
     auto fetch1 = [&](int j0) {
 #pragma unroll
       for (int u = 0; u < NS; ++u) {
         const int e = tid + NT * u, c = e / VTL, jj = e % VTL;
         ps[u] = S0[(int64_t)c * V + j0 + jj];
-        if constexpr (BF) pl[u] = dSL[(int64_t)c * V + j0 + jj];
       }
 #pragma unroll
       for (int u = 0; u < NR; ++u) {
@@ -1075,83 +1271,31 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
         po[u] = r < L ? x : 0.f;
       }
     };
-    // bf16 inputs: the tiles go to LDS as bf16, S0, Delta, dDelta and dS_L
-    // as hi + lo pairs (dO and V are exact), and each 32-column tile is one
-    // k-step of the bf16 products: hi*hi + hi*lo + lo*hi per pair of split
-    // operands, fp32 accumulation.  Rows padded to BP (16-byte aligned).
-    constexpr int BP = VTL + 8;
-    bf16 (*hS0)[BP] = (bf16(*)[BP])sReg;
-    bf16 (*lS0)[BP] = hS0 + K;
-    bf16 (*hdD)[BP] = lS0 + K;
-    bf16 (*ldD)[BP] = hdD + C;
-    bf16 (*hdO)[BP] = ldD + C;
-    static_assert(VTL == 32, "one bf16 k-step per value tile");
-    static_assert((2 * K + 3 * C) * BP * 2 <= kRegion * 4, "sweep 1 bf16 tiles fit the region");
     fetch1(0);
     for (int j0 = 0; j0 < V; j0 += VTL) {
       __syncthreads();
-      if constexpr (BF) {
 #pragma unroll
-        for (int u = 0; u < NS; ++u) {
-          const int e = tid + NT * u;
-          split_bf16(ps[u], hS0[e / VTL][e % VTL], lS0[e / VTL][e % VTL]);
-          sdp[u] = fmaf(ps[u], pl[u], sdp[u]);
-        }
+      for (int u = 0; u < NS; ++u) {
+        const int e = tid + NT * u;
+        tS0[e / VTL][e % VTL] = ps[u];
+      }
 #pragma unroll
-        for (int u = 0; u < NR; ++u) {
-          const int e = tid + NT * u;
-          split_bf16(pd[u], hdD[e / VTL][e % VTL], ldD[e / VTL][e % VTL]);
-          hdO[e / VTL][e % VTL] = to_bf16(po[u]);
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < NS; ++u) {
-          const int e = tid + NT * u;
-          tS0[e / VTL][e % VTL] = ps[u];
-        }
-#pragma unroll
-        for (int u = 0; u < NR; ++u) {
-          const int e = tid + NT * u;
-          tdD[e / VTL][e % VTL] = pd[u];
-          tdO[e / VTL][e % VTL] = po[u];
-        }
+      for (int u = 0; u < NR; ++u) {
+        const int e = tid + NT * u;
+        tdD[e / VTL][e % VTL] = pd[u];
+        tdO[e / VTL][e % VTL] = po[u];
       }
       if (j0 + VTL < V) fetch1(j0 + VTL);
       __syncthreads();
-      if constexpr (BF) {
-        const bf16x8 ah = frag8(&hdD[16 * rt + ln][8 * lg]), al = frag8(&ldD[16 * rt + ln][8 * lg]);
-        const bf16x8 ao = frag8(&hdO[16 * rt + ln][8 * lg]);
+#pragma unroll
+      for (int jj = 0; jj < VTL; jj += 4) {
+        const float ad = tdD[16 * rt + ln][jj + lg], ao = tdO[16 * rt + ln][jj + lg];
 #pragma unroll
         for (int t = 0; t < 2; ++t) {
-          const bf16x8 bh = frag8(&hS0[16 * (ct0 + t) + ln][8 * lg]);
-          const bf16x8 bl = frag8(&lS0[16 * (ct0 + t) + ln][8 * lg]);
-          m1[t] = mfma_bf16(ah, bh, m1[t]);
-          m1[t] = mfma_bf16(ah, bl, m1[t]);
-          m1[t] = mfma_bf16(al, bh, m1[t]);
-          m2[t] = mfma_bf16(ao, bh, m2[t]);
-          m2[t] = mfma_bf16(ao, bl, m2[t]);
+          const float bs = tS0[16 * (ct0 + t) + ln][jj + lg];
+          m1[t] = mfma_f32(ad, bs, m1[t]);
+          m2[t] = mfma_f32(ao, bs, m2[t]);
         }
-      } else {
-#pragma unroll
-        for (int jj = 0; jj < VTL; jj += 4) {
-          const float ad = tdD[16 * rt + ln][jj + lg], ao = tdO[16 * rt + ln][jj + lg];
-#pragma unroll
-          for (int t = 0; t < 2; ++t) {
-            const float bs = tS0[16 * (ct0 + t) + ln][jj + lg];
-            m1[t] = mfma_f32(ad, bs, m1[t]);
-            m2[t] = mfma_f32(ao, bs, m2[t]);
-          }
-        }
-      }
-    }
-    if constexpr (BF) {
-      // each row's 32 columns sit in one half-wave
-#pragma unroll
-      for (int u = 0; u < NS; ++u) {
-        float x = sdp[u];
-#pragma unroll
-        for (int off = 16; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-        if (tid % VTL == 0) sSd[(tid + NT * u) / VTL] = x;
       }
     }
     __syncthreads();  // the tiles are dead: dW, and dQ~ on its way to registers
@@ -1191,22 +1335,12 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     const bool has_dv = w < 8;
     const int vrt = (w >> 1) & 3, vct = w & 1;
     float qs[NS], ql[NS], qd[NR], qD[NR], qo[NR], qv[NR];
-    // bf16 inputs: sweep 2's tiles, as in sweep 1 (S0 is not read again)
-    bf16 (*hSL)[BP] = (bf16(*)[BP])sReg2;
-    bf16 (*lSL)[BP] = hSL + K;
-    bf16 (*hD2)[BP] = lSL + K;
-    bf16 (*lD2)[BP] = hD2 + C;
-    bf16 (*hdO2)[BP] = lD2 + C;
-    bf16 (*hdD2)[BP] = hdO2 + C;
-    bf16 (*ldD2)[BP] = hdD2 + C;
-    bf16 (*hv2)[BP] = ldD2 + C;
-    static_assert((2 * K + 6 * C) * BP * 2 <= (kRegion - C * K) * 4, "sweep 2 bf16 tiles fit");
     auto fetch2 = [&](int j0) {
 #pragma unroll
       for (int u = 0; u < NS; ++u) {
         const int e = tid + NT * u, c = e / VTL, jj = e % VTL;
         ql[u] = dSL[(int64_t)c * V + j0 + jj];
-        if constexpr (!BF) qs[u] = S0[(int64_t)c * V + j0 + jj];
+        qs[u] = S0[(int64_t)c * V + j0 + jj];
       }
 #pragma unroll
       for (int u = 0; u < NR; ++u) {
@@ -1223,77 +1357,22 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     fetch2(0);
     for (int j0 = 0; j0 < V; j0 += VTL) {
       __syncthreads();
-      if constexpr (BF) {
 #pragma unroll
-        for (int u = 0; u < NS; ++u) {
-          const int e = tid + NT * u;
-          split_bf16(ql[u], hSL[e / VTL][e % VTL], lSL[e / VTL][e % VTL]);
-        }
+      for (int u = 0; u < NS; ++u) {
+        const int e = tid + NT * u;
+        tdSL2[e / VTL][e % VTL] = ql[u];
+        tS02[e / VTL][e % VTL] = qs[u];
+      }
 #pragma unroll
-        for (int u = 0; u < NR; ++u) {
-          const int e = tid + NT * u, r = e / VTL, jj = e % VTL;
-          split_bf16(qd[u], hdD2[r][jj], ldD2[r][jj]);
-          split_bf16(qD[u], hD2[r][jj], lD2[r][jj]);
-          hdO2[r][jj] = to_bf16(qo[u]);
-          hv2[r][jj] = to_bf16(qv[u]);
-        }
-      } else {
-#pragma unroll
-        for (int u = 0; u < NS; ++u) {
-          const int e = tid + NT * u;
-          tdSL2[e / VTL][e % VTL] = ql[u];
-          tS02[e / VTL][e % VTL] = qs[u];
-        }
-#pragma unroll
-        for (int u = 0; u < NR; ++u) {
-          const int e = tid + NT * u;
-          tdD2[e / VTL][e % VTL] = qd[u];
-          tD2[e / VTL][e % VTL] = qD[u];
-          tdO2[e / VTL][e % VTL] = qo[u];
-          tv2[e / VTL][e % VTL] = qv[u];
-        }
+      for (int u = 0; u < NR; ++u) {
+        const int e = tid + NT * u;
+        tdD2[e / VTL][e % VTL] = qd[u];
+        tD2[e / VTL][e % VTL] = qD[u];
+        tdO2[e / VTL][e % VTL] = qo[u];
+        tv2[e / VTL][e % VTL] = qv[u];
       }
       if (j0 + VTL < V) fetch2(j0 + VTL);
       __syncthreads();
-      if constexpr (BF) {
-        const bf16x8 ah = frag8(&hD2[16 * rt + ln][8 * lg]), al = frag8(&lD2[16 * rt + ln][8 * lg]);
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const bf16x8 bh = frag8(&hSL[16 * (ct0 + t) + ln][8 * lg]);
-          const bf16x8 bl = frag8(&lSL[16 * (ct0 + t) + ln][8 * lg]);
-          m3[t] = mfma_bf16(ah, bh, m3[t]);
-          m3[t] = mfma_bf16(ah, bl, m3[t]);
-          m3[t] = mfma_bf16(al, bh, m3[t]);
-        }
-#pragma unroll
-        for (int u = 0; u < NPY; ++u) {
-          const int t = w + NW * u;
-          if (t < NTRI) {
-            int R, I;
-            tri_tile(t, R, I);
-            const bf16x8 o8 = frag8(&hdO2[16 * R + ln][8 * lg]);
-            pt[u] = mfma_bf16(o8, frag8(&hD2[16 * I + ln][8 * lg]), pt[u]);
-            pt[u] = mfma_bf16(o8, frag8(&lD2[16 * I + ln][8 * lg]), pt[u]);
-            const bf16x8 v8 = frag8(&hv2[16 * I + ln][8 * lg]);
-            yt[u] = mfma_bf16(frag8(&hdD2[16 * R + ln][8 * lg]), v8, yt[u]);
-            yt[u] = mfma_bf16(frag8(&ldD2[16 * R + ln][8 * lg]), v8, yt[u]);
-          }
-        }
-        if (has_dv) {
-          // dV as below, dDelta from its hi + lo pair, fp32 products
-          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
-          for (int a0 = 16 * vrt; a0 < C; a0 += 4) {
-            const int ar = a0 + lg, ac = 16 * vct + ln;
-            acc = mfma_f32(sT[ar][16 * vrt + ln], bf16_to_f32(hdD2[ar][ac]) + bf16_to_f32(ldD2[ar][ac]), acc);
-          }
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const int r = 16 * vrt + 4 * lg + e;
-            if (r < L) store_as(dv + th(r) * V + j0 + 16 * vct + ln, sB[r] * acc[e]);
-          }
-        }
-        continue;
-      }
       if (tid < K) {
         const int c = tid;
 #pragma unroll 8
@@ -1363,9 +1442,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
         }
       }
     }
-    if constexpr (!BF) {
-      if (tid < K) sSd[tid] = sd;
-    }
+    if (tid < K) sSd[tid] = sd;
     __syncthreads();
   } else {
   {
