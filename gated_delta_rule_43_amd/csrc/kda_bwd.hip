@@ -1087,48 +1087,51 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     for (int t = 0; t < 2; ++t) m1[t] = m2[t] = m3[t] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int u = 0; u < NPY; ++u) pt[u] = yt[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-    float ps[NS], pl[NS], pD[NR], pd[NR], po[NR], pv[NR], sdp[NS];
+    // 512-thread workgroups (K = 64) keep two tiles in flight: tile t's loads
+    // are issued two steps ahead of its products, into the register set of
+    // its parity
+    struct Tile { float s[NS], l[NS], D[NR], d[NR], o[NR], v[NR]; };
+    Tile ta, tb;
+    float sdp[NS];
 #pragma unroll
     for (int u = 0; u < NS; ++u) sdp[u] = 0.f;
-    auto fetch = [&](int j0) __attribute__((always_inline)) {
+    auto fetch = [&](Tile& x, int j0) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < NS; ++u) {
         const int e = tid + NT * u, c = e / VTL, jj = e % VTL;
-        ps[u] = S0[(int64_t)c * V + j0 + jj];
-        pl[u] = dSL[(int64_t)c * V + j0 + jj];
+        x.s[u] = S0[(int64_t)c * V + j0 + jj];
+        x.l[u] = dSL[(int64_t)c * V + j0 + jj];
       }
 #pragma unroll
       for (int u = 0; u < NR; ++u) {
         const int e = tid + NT * u, r = e / VTL, jj = e % VTL;
         const bool in = r < L;
-        pd[u] = dDl[(int64_t)r * V + j0 + jj];
-        pD[u] = Dl[(int64_t)r * V + j0 + jj];
+        x.d[u] = dDl[(int64_t)r * V + j0 + jj];
+        x.D[u] = Dl[(int64_t)r * V + j0 + jj];
         const int64_t rv = th(in ? r : 0) * V + j0 + jj;
         const float xo = load_f32(dO + rv), xv = load_f32(v + rv);
-        po[u] = in ? xo : 0.f;
-        pv[u] = in ? xv : 0.f;
+        x.o[u] = in ? xo : 0.f;
+        x.v[u] = in ? xv : 0.f;
       }
     };
-    fetch(0);
-    for (int j0 = 0; j0 < V; j0 += VTL) {
-      __syncthreads();  // the previous tile's products are done
+    auto stage = [&](const Tile& x) __attribute__((always_inline)) {
 #pragma unroll
       for (int u = 0; u < NS; ++u) {
         const int e = tid + NT * u, c = e / VTL, jj = e % VTL;
-        split_bf16(ps[u], hS0[c][jj], lS0[c][jj]);
-        split_bf16(pl[u], hSL[c][jj], lSL[c][jj]);
-        sdp[u] = fmaf(ps[u], pl[u], sdp[u]);
+        split_bf16(x.s[u], hS0[c][jj], lS0[c][jj]);
+        split_bf16(x.l[u], hSL[c][jj], lSL[c][jj]);
+        sdp[u] = fmaf(x.s[u], x.l[u], sdp[u]);
       }
 #pragma unroll
       for (int u = 0; u < NR; ++u) {
         const int e = tid + NT * u, r = e / VTL, jj = e % VTL;
-        split_bf16(pd[u], hdD[r][jj], ldD[r][jj]);
-        split_bf16(pD[u], hD[r][jj], lD[r][jj]);
-        hdO[r][jj] = to_bf16(po[u]);
-        hv[r][jj] = to_bf16(pv[u]);
+        split_bf16(x.d[u], hdD[r][jj], ldD[r][jj]);
+        split_bf16(x.D[u], hD[r][jj], lD[r][jj]);
+        hdO[r][jj] = to_bf16(x.o[u]);
+        hv[r][jj] = to_bf16(x.v[u]);
       }
-      if (j0 + VTL < V) fetch(j0 + VTL);
-      __syncthreads();
+    };
+    auto products = [&](const int j0) __attribute__((always_inline)) {
       {
         const int ar = 16 * rt + ln;
         const bf16x8 dh = frag8(&hdD[ar][8 * lg]), dl = frag8(&ldD[ar][8 * lg]);
@@ -1183,6 +1186,33 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
           const int r = 16 * vrt + 4 * lg + e;
           if (r < L) store_as(dv + th(r) * V + j0 + 16 * vct + ln, sB[r] * acc[e]);
         }
+      }
+    };
+    if constexpr (NT <= 512) {
+      static_assert(2 * VTL == 64, "V (64 or 128) is a whole number of tile pairs");
+      fetch(ta, 0);
+      fetch(tb, VTL);
+      for (int j0 = 0; j0 < V; j0 += 2 * VTL) {
+        __syncthreads();  // the previous tile's products are done
+        stage(ta);
+        if (j0 + 2 * VTL < V) fetch(ta, j0 + 2 * VTL);
+        __syncthreads();
+        products(j0);
+        __syncthreads();
+        stage(tb);
+        if (j0 + 3 * VTL < V) fetch(tb, j0 + 3 * VTL);
+        __syncthreads();
+        products(j0 + VTL);
+      }
+    } else {
+      // 1024 threads: 128 registers leave room for one tile in flight only
+      fetch(ta, 0);
+      for (int j0 = 0; j0 < V; j0 += VTL) {
+        __syncthreads();
+        stage(ta);
+        if (j0 + VTL < V) fetch(ta, j0 + VTL);
+        __syncthreads();
+        products(j0);
       }
     }
     // rowsum(S0 . dS_L): each row's 32 columns sit in one half-wave
