@@ -246,6 +246,16 @@ def test_bwd_bf16_extreme_gates_exact_path():
     _run(inp, d_o, d_fin, torch.bfloat16, "bf16 extreme gates")
 
 
+def test_bwd_bf16_clamped_gate():
+    """The hard-clamp gate form in bf16 (the matrix-core recomputation's clamp
+    instantiation), packed documents, no final-state gradient."""
+    _banner("bwd bf16 clamp gate")
+    inp = to_device(synthetic.random_problem(46, 1, 220, 2, 128, 128, dtype=torch.bfloat16,
+                                             gate_std=3.0, lengths=[90, 130], init_std=0.5))
+    d_o, _ = _upstream(inp, 17, with_final=False)
+    _run(inp, d_o, None, torch.bfloat16, "bf16 clamp", lower_bound=-0.5, lower_bound_form="clamp")
+
+
 @pytest.mark.parametrize("K,V", [(128, 128), (64, 128), (128, 64)])
 def test_bwd_bf16_both_recomputations(monkeypatch, K, V):
     _banner("bwd bf16 recomputation kernels K=%d V=%d" % (K, V))
