@@ -201,13 +201,15 @@ Layout layout(const kda_problem* p, bool summary) { return layout_for(p, choose_
 
 // The backward's workspace: the VALU forward's (recomputed factors) followed by
 // Akk and Tm, per-chunk states and their gradients, the per-value-head
-// gradients of q^ and k^, and per-chunk partial sums of the gate-parameter
-// gradients.
+// gradients of q^ and k^, per-chunk partial sums of the gate-parameter
+// gradients, the L2 norm's scales per token-head and (bf16) the fix-up list
+// of the matrix-core recomputation.
 struct BwdLayout {
   Layout f;
   size_t off_akk = 0, off_tm = 0, off_hc = 0, off_dhc = 0, off_dc = 0, off_ddc = 0;
   size_t off_dqh = 0, off_dkh = 0, off_da = 0, off_ddt = 0;
   size_t off_xcount = 0, off_xlist = 0;  // bf16: the recomputation's fix-up list
+  size_t off_rq = 0, off_rk = 0;         // the L2 norm's scales per token-head
   size_t total = 0;
 };
 
@@ -232,6 +234,8 @@ BwdLayout bwd_layout(const kda_problem* p) {
   B.off_dkh = take(tokh * K * 4);
   B.off_da = take(NT * H * 4);
   B.off_ddt = take(NT * H * K * 4);
+  B.off_rq = take(tokh * 4);
+  B.off_rk = take(tokh * 4);
   if (p->dtype == KDA_BF16) {
     B.off_xcount = take(4);
     B.off_xlist = take(NT * H * 4);
@@ -811,6 +815,8 @@ kda_status kda_bwd_profiled(const kda_problem* p, const void* q, const void* k, 
   b.f.a_log = a_log; b.f.dt_bias = dt_bias; b.f.init = initial_state;
   b.f.Akk_out = (float*)(w + L.off_akk);
   b.f.Tm_out = (float*)(w + L.off_tm);
+  b.f.rq = (float*)(w + L.off_rq);
+  b.f.rk = (float*)(w + L.off_rk);
   // bf16: the chunk factors are recomputed on the matrix-core chunk kernel
   // (for comparisons, KDA_BWD_RECOMPUTE=valu keeps the fp32 vector-ALU kernels
   // and =mfma32 keeps every recomputed array in fp32)

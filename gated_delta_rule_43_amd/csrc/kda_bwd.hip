@@ -951,6 +951,40 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   const int tok0 = a.chunk_tok[j], L = a.chunk_len[j];
   const int64_t chb = (int64_t)j * H + h;
   auto th = [&](int r) { return (int64_t)(tok0 + r) * H + h; };
+  // q^ and k^ rebuilt from the raw q and k of the key head this value head
+  // reads and the recomputation's norm scales (the same fp32 product as there):
+  // one element, or the 4 channels 4 c4 .. 4 c4 + 3 (one 8- or 16-byte load
+  // when the inputs allow it)
+  const int64_t hk = h / (H / a.HK);
+  auto thk = [&](int r) { return (int64_t)(tok0 + r) * a.HK + hk; };
+  auto khat = [&](int r, int c) { return load_f32((const Tin*)a.k + thk(r) * K + c) * a.rk[th(r)]; };
+  const bool vec_in = (((uintptr_t)a.q | (uintptr_t)a.k) % (4 * sizeof(Tin))) == 0;
+  auto hat4 = [&](const Tin* x, const float* rs, int r, int c4) {
+    const Tin* p = x + thk(r) * K + 4 * c4;
+    float f[4];
+    if constexpr (std::is_same<Tin, bf16>::value) {
+      if (vec_in) {
+        const uint2 u = *(const uint2*)p;
+        f[0] = __uint_as_float(u.x << 16);
+        f[1] = __uint_as_float(u.x & 0xffff0000u);
+        f[2] = __uint_as_float(u.y << 16);
+        f[3] = __uint_as_float(u.y & 0xffff0000u);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = load_f32(p + e);
+      }
+    } else {
+      if (vec_in) {
+        const float4 u = *(const float4*)p;
+        f[0] = u.x; f[1] = u.y; f[2] = u.z; f[3] = u.w;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) f[e] = p[e];
+      }
+    }
+    const float s = rs[th(r)];
+    return make_float4(f[0] * s, f[1] * s, f[2] * s, f[3] * s);
+  };
   const float* Akk = a.Akk_out + chb * C * C;
   const float* S0 = b.hc + chb * K * V;
   const float* dSL = b.dhc + chb * K * V;
@@ -1248,7 +1282,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
 #pragma unroll
     for (int m = 0; m < NE1; ++m) {
       const int r = rb1 + RSTEP1 * m;
-      const float x = a.kn[th(r < L ? r : 0) * K + c1];
+      const float x = khat(r < L ? r : 0, c1);
       sKtT[c1][r] = r < L ? x * __expf(sGam[r][c1]) : 0.f;
     }
     // P (scaled) and the V half of Y, lower triangle i <= r < L; zero elsewhere
@@ -1449,7 +1483,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
 #pragma unroll
   for (int m = 0; m < NE1; ++m) {
     const int r = rb1 + RSTEP1 * m;
-    const float x = a.kn[th(r < L ? r : 0) * K + c1];
+    const float x = khat(r < L ? r : 0, c1);
     sKtT[c1][r] = r < L ? x * __expf(sGam[r][c1]) : 0.f;
   }
     // P (scaled) and the V half of Y, lower triangle i <= r < L; zero elsewhere
@@ -1581,7 +1615,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
 #pragma unroll
   for (int m = 0; m < NE1; ++m) {
     const int r = rb1 + RSTEP1 * m;
-    const float x = a.kn[th(r < L ? r : 0) * K + c1];
+    const float x = khat(r < L ? r : 0, c1);
     sKtT[c1][r] = r < L ? x * __expf(sGam[r][c1]) : 0.f;
   }
 #pragma unroll
@@ -1714,7 +1748,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
 #pragma unroll
   for (int e = tid; e < C * K / 4; e += NT) {
     const int r = e / (K / 4), c4 = e % (K / 4);
-    const float4 x = ((const float4*)(a.qn + th(r < L ? r : 0) * K))[c4];
+    const float4 x = hat4((const Tin*)a.q, a.rq, r < L ? r : 0, c4);
     ((float4*)&sQn[r][0])[c4] = r < L ? x : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __syncthreads();
@@ -1764,7 +1798,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
 #pragma unroll
   for (int e = tid; e < C * K / 4; e += NT) {
     const int r = e / (K / 4), c4 = e % (K / 4);
-    const float4 x = ((const float4*)(a.kn + th(r < L ? r : 0) * K))[c4];
+    const float4 x = hat4((const Tin*)a.k, a.rk, r < L ? r : 0, c4);
     ((float4*)&sKn[r][0])[c4] = r < L ? x : make_float4(0.f, 0.f, 0.f, 0.f);
   }
   __syncthreads();

@@ -64,6 +64,9 @@ struct FwdArgs {
   int32_t* chunk_seq;  // [NT] sequence (row or document) of each chunk
   // workspace: per-token prologue results (VALU path)
   float *qn, *kn, *g, *bt;
+  // backward: the L2 norm's scales 1/||q||, 1/||k|| of each value-head
+  // token-head (q^ = q rq), written by the recomputation
+  float *rq, *rk;
   // workspace: per chunk-head factors, fp32; with ws_bf16 set, W, U, Qt, Kb
   // and Aqk are bf16 (the backward's matrix-core recomputation, 64-token chunks)
   int ws_bf16;

@@ -255,7 +255,7 @@ enum {
 // path on such blocks.  GATE: the gate form (FwdArgs::gate_form).  CONV: q, k
 // and v are the raw projections, convolved on load (FwdArgs::conv).  OUT32:
 // the backward's recomputation; instead of a record, the factors go to the
-// fp32 row-major arrays the backward reads (qn, kn, g, bt per token-head; Qt,
+// fp32 row-major arrays the backward reads (rq, rk, g, bt per token-head; Qt,
 // Kb, W, U, Aqk, Akk_out, Tm_out, gL per chunk-head with C = FwdArgs::C rows;
 // Qt, Kb, W, U and Aqk as bf16 when FwdArgs::ws_bf16 is set).
 template <int K, int V, bool EXACT, int GATE, bool CONV, bool OUT32 = false>
@@ -367,16 +367,19 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
 #pragma unroll
     for (int s2 = 0; s2 < KL; ++s2) lam[s2] = vmask * fgate<GATE>(lam[s2], A, a.lb);
     if constexpr (OUT32) {
-      // q^, k^ and the per-token gate of a valid row, channels 32j + 4g.. and 32j + 16 + 4g..
+      // the norm scales and the per-token gate of a valid row (channels
+      // 32j + 4g.. and 32j + 16 + 4g..); q^ = q rq is rebuilt from them
       if (emit && valid) {
+        if (g == 0) {
+          a.rq[th] = rq;
+          a.rk[th] = rk;
+        }
 #pragma unroll
         for (int j = 0; j < NKJ; ++j)
 #pragma unroll
           for (int hf = 0; hf < 2; ++hf) {
             const int64_t o = th * K + 32 * j + 16 * hf + 4 * g;
             const int e0 = 8 * j + 4 * hf;
-            *(float4*)(a.qn + o) = make_float4(qv[e0], qv[e0 + 1], qv[e0 + 2], qv[e0 + 3]);
-            *(float4*)(a.kn + o) = make_float4(kv[e0], kv[e0 + 1], kv[e0 + 2], kv[e0 + 3]);
             *(float4*)(a.g + o) = make_float4(lam[e0], lam[e0 + 1], lam[e0 + 2], lam[e0 + 3]);
           }
       }
@@ -453,8 +456,10 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
     __syncthreads();
     const bool need = sNeedExact != 0;
     if (tid == 0 && need) {
+      // each chunk-head appends once after the chunk table cleared the count,
+      // so slot < NT*H; the test keeps a stale count from writing past the list
       const int slot = atomicAdd(a.exact_count, 1);
-      a.exact_list[slot] = jchunk * H + h;  // slot < NT*H: each chunk-head appends once
+      if (slot < a.NT * H) a.exact_list[slot] = jchunk * H + h;
     }
     return need;
   };
@@ -944,7 +949,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_chunk_mfma(FwdArgs a) {
 // Fix-up pass: recomputes the listed chunk-heads with the exact diagonal path.
 template <int K, int V, int GATE, bool CONV>
 __global__ __launch_bounds__(kThreads) void k_chunk_mfma_exact(FwdArgs a) {
-  const int count = *a.exact_count;
+  const int count = min(*a.exact_count, a.NT * a.H);
   for (int i = blockIdx.x; i < count; i += gridDim.x) {
     const int ch = a.exact_list[i];
     const int jchunk = ch / a.H;
@@ -972,7 +977,7 @@ __global__ __launch_bounds__(kThreads, 3) void k_chunk_recompute(FwdArgs a) {
 
 template <int K, int V, int GATE>
 __global__ __launch_bounds__(kThreads) void k_chunk_recompute_exact(FwdArgs a) {
-  const int count = *a.exact_count;
+  const int count = min(*a.exact_count, a.NT * a.H);
   for (int i = blockIdx.x; i < count; i += gridDim.x) {
     const int ch = a.exact_list[i];
     const int jchunk = ch / a.H;

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(kThreads) void k_prologue_valu(
     const Tin* __restrict__ beta, const float* __restrict__ a_log,
     const float* __restrict__ dt_bias, int64_t n_th, int H, int HK, int K, int gate_form, float lb,
     float* __restrict__ qn, float* __restrict__ kn, float* __restrict__ g,
-    float* __restrict__ bt) {
+    float* __restrict__ bt, float* __restrict__ rqo, float* __restrict__ rko) {
   const int lane = threadIdx.x & 63;
   const int64_t th0 = ((int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6)) * kProTPW;
   if (th0 >= n_th) return;
@@ -120,7 +120,13 @@ __global__ __launch_bounds__(kThreads) void k_prologue_valu(
       kn[base + c] = vk[t][m] * rk;
       g[base + c] = gate_value(vx[t][m], A, gate_form, lb);
     }
-    if (lane == 0) bt[th] = sigmoid_f(bl[t]);
+    if (lane == 0) {
+      bt[th] = sigmoid_f(bl[t]);
+      if (rqo) {
+        rqo[th] = rq;
+        rko[th] = rk;
+      }
+    }
   }
 }
 
@@ -700,7 +706,8 @@ hipError_t run_prep(const FwdArgs& a, hipStream_t s) {
     const int64_t blocks = (n_th + per_block - 1) / per_block;
     hipLaunchKernelGGL((k_prologue_valu<Tin, kMaxD>), dim3((unsigned)blocks), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.gate, (const Tin*)a.beta,
-                       a.a_log, a.dt_bias, n_th, a.H, a.HK, a.K, a.gate_form, a.lb, a.qn, a.kn, a.g, a.bt);
+                       a.a_log, a.dt_bias, n_th, a.H, a.HK, a.K, a.gate_form, a.lb, a.qn, a.kn, a.g, a.bt,
+                       a.rq, a.rk);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   if (a.NT > 0) {
@@ -722,7 +729,8 @@ hipError_t run(const FwdArgs& a, hipStream_t s) {
     const int64_t blocks = (n_th + per_block - 1) / per_block;
     hipLaunchKernelGGL((k_prologue_valu<Tin, KM>), dim3((unsigned)blocks), dim3(kThreads), 0, s,
                        (const Tin*)a.q, (const Tin*)a.k, (const Tin*)a.gate, (const Tin*)a.beta,
-                       a.a_log, a.dt_bias, n_th, a.H, a.HK, a.K, a.gate_form, a.lb, a.qn, a.kn, a.g, a.bt);
+                       a.a_log, a.dt_bias, n_th, a.H, a.HK, a.K, a.gate_form, a.lb, a.qn, a.kn, a.g, a.bt,
+                       a.rq, a.rk);
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
   }
   mark(a, kStagePrologue, 1, s);
