@@ -111,6 +111,24 @@ __device__ __forceinline__ bf16 to_bf16(float x) { return __builtin_bit_cast(bf1
 // 8 consecutive bf16 of an LDS row (16-byte aligned)
 __device__ __forceinline__ bf16x8 frag8(const bf16* p) { return *(const bf16x8*)p; }
 
+// Sum over the 64 lanes on the VALU (DPP): inclusive prefix sums inside each
+// 16-lane row (row_shr 1, 2, 4, 8, zero fill), then row 0's total into row 1
+// and row 2's into row 3 (row_bcast:15), then row 1's into rows 2 and 3
+// (row_bcast:31); lane 63 then holds the total, which is broadcast.
+template <int CTRL, int ROWS, bool ZERO>
+__device__ __forceinline__ float dpp_f(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xF, ZERO));
+}
+__device__ inline float wave_sum_dpp(float x) {
+  x += dpp_f<0x111, 0xF, true>(x);
+  x += dpp_f<0x112, 0xF, true>(x);
+  x += dpp_f<0x114, 0xF, true>(x);
+  x += dpp_f<0x118, 0xF, true>(x);
+  x += dpp_f<0x142, 0xA, false>(x);
+  x += dpp_f<0x143, 0xC, false>(x);
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+
 __device__ inline float wave_sum(float x) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
@@ -1882,6 +1900,16 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
       }
     }
   }
+  // One key head per value head: the L2 norm's Jacobian is applied here,
+  // dq = rq (dq^ - q^ (q^ . dq^)) and likewise dk, the dot over the row's K
+  // channels as a wave sum per row and the K/64 waves of the row added through
+  // LDS (the dead Tm's place).  Grouped value heads leave dq^ and dk^ in the
+  // workspace for k_bwd_qk, which sums the group first.
+  const bool fuse_qk = a.H == a.HK;
+  constexpr int NWV = NT / 64, WPR = (K + 63) / 64;  // waves; waves per row
+  float* sPart = &sT[0][0];                          // [NWV][NE1][2]
+  static_assert(NWV * NE1 * 2 <= C * (C + 1), "the partial dots fit where Tm was");
+  float dqv[NE1], dkv[NE1];
   float dgm[NE1], tkm[NE1];
 #pragma unroll
   for (int m = 0; m < NE1; ++m) {
@@ -1908,10 +1936,42 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
       c12 = fmaf(sP[rr][r] * sQn[rr][c] + sY[rr][r] * sKn[rr][c], e, c12);
     }
     const float tkb = kk * ekb * dkb[m];
-    b.dqh[th(r) * K + c] = egm * dqs[m] + r1 + ox1[m];
-    b.dkh[th(r) * K + c] = ekt[m] + ekb * dkb[m] + r2 + c12 + ox2[m];
+    const float dqh = egm * dqs[m] + r1 + ox1[m];
+    const float dkh = ekt[m] + ekb * dkb[m] + r2 + c12 + ox2[m];
+    if (fuse_qk) {
+      dqv[m] = dqh;
+      dkv[m] = dkh;
+      const float pq = wave_sum_dpp(q * dqh), pk = wave_sum_dpp(kk * dkh);
+      if ((tid & 63) == 0) {
+        sPart[((tid >> 6) * NE1 + m) * 2] = pq;
+        sPart[((tid >> 6) * NE1 + m) * 2 + 1] = pk;
+      }
+    } else {
+      b.dqh[th(r) * K + c] = dqh;
+      b.dkh[th(r) * K + c] = dkh;
+    }
     dgm[m] = kk * ekt[m] + q * egm * dqs[m] - tkb + q * r1 + kk * r2 - kk * c12 + ox3[m];
     tkm[m] = tkb;
+  }
+  if (fuse_qk) {
+    __syncthreads();  // the partial dots are in LDS
+    Tin* dqo = (Tin*)b.dq;
+    Tin* dko = (Tin*)b.dk;
+#pragma unroll
+    for (int m = 0; m < NE1; ++m) {
+      const int r = __builtin_amdgcn_readfirstlane(rb1 + RSTEP1 * m);
+      if (r >= L) continue;
+      float dq_dot = 0.f, dk_dot = 0.f;
+#pragma unroll
+      for (int u = 0; u < WPR; ++u) {
+        const int wv = WPR * rb1 + u;
+        dq_dot += sPart[(wv * NE1 + m) * 2];
+        dk_dot += sPart[(wv * NE1 + m) * 2 + 1];
+      }
+      const int64_t o = th(r) * K + c1;  // one key head per value head: thk(r) = th(r)
+      store_as(dqo + o, a.rq[th(r)] * (dqv[m] - sQn[r][c1] * dq_dot));
+      store_as(dko + o, a.rk[th(r)] * (dkv[m] - sKn[r][c1] * dk_dot));
+    }
   }
   __syncthreads();  // q^, k^ are dead
 #pragma unroll
@@ -2165,7 +2225,8 @@ hipError_t run(const BwdArgs& b, hipStream_t s) {
   bmark(b, kBwdChunk, 1, s);
   const int64_t tk = (int64_t)a.B * a.T * a.HK;
   bmark(b, kBwdQK, 0, s);
-  if (tk > 0) {
+  // (one key head per value head: done inside k_bwd_chunk)
+  if (tk > 0 && a.H != a.HK) {
     const dim3 grid((unsigned)((tk + 15) / 16));  // 4 waves of 4 pairs
     if (a.K == 64) hipLaunchKernelGGL((k_bwd_qk<Tin, 64>), grid, dim3(kThreads), 0, s, b);
     else hipLaunchKernelGGL((k_bwd_qk<Tin, 128>), grid, dim3(kThreads), 0, s, b);
