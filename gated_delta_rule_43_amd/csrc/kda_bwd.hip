@@ -129,11 +129,6 @@ __device__ inline float wave_sum_dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
-__device__ inline float wave_sum(float x) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-  return x;
-}
 
 // Copy n floats (n a multiple of 4, 16-byte aligned) from global memory to LDS
 // with a workgroup of nt threads.
@@ -2114,10 +2109,10 @@ __global__ __launch_bounds__(kThreads) void k_bwd_qk(BwdArgs b) {
       ssk = fmaf(vk[t][e], vk[t][e], ssk);
       dotk = fmaf(vk[t][e], dk[t][e], dotk);
     }
-    ssq = wave_sum(ssq);
-    dotq = wave_sum(dotq);
-    ssk = wave_sum(ssk);
-    dotk = wave_sum(dotk);
+    ssq = wave_sum_dpp(ssq);
+    dotq = wave_sum_dpp(dotq);
+    ssk = wave_sum_dpp(ssk);
+    dotk = wave_sum_dpp(dotk);
     const float rq = 1.f / sqrtf(ssq + 1e-6f), rk = 1.f / sqrtf(ssk + 1e-6f);
     const float r3q = rq * rq * rq, r3k = rk * rk * rk;
     Tin* oq = (Tin*)b.dq + tk * K + c0;
