@@ -119,6 +119,18 @@ template <int CTRL, int ROWS, bool ZERO>
 __device__ __forceinline__ float dpp_f(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xF, ZERO));
 }
+// Sums over each 32-lane half of the wave on the VALU: row prefix sums, then
+// rows 0 and 2 into rows 1 and 3; lanes 31 and 63 hold the two halves' sums
+// (returned as lo and hi to every lane).
+__device__ inline void half_sums_dpp(float x, float& lo, float& hi) {
+  x += dpp_f<0x111, 0xF, true>(x);
+  x += dpp_f<0x112, 0xF, true>(x);
+  x += dpp_f<0x114, 0xF, true>(x);
+  x += dpp_f<0x118, 0xF, true>(x);
+  x += dpp_f<0x142, 0xA, false>(x);
+  lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
+  hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
 __device__ inline float wave_sum_dpp(float x) {
   x += dpp_f<0x111, 0xF, true>(x);
   x += dpp_f<0x112, 0xF, true>(x);
@@ -1265,10 +1277,9 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     // rowsum(S0 . dS_L): each row's 32 columns sit in one half-wave
 #pragma unroll
     for (int u = 0; u < NS; ++u) {
-      float x = sdp[u];
-#pragma unroll
-      for (int off = 16; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
-      if (tid % VTL == 0) sSd[(tid + NT * u) / VTL] = x;
+      float lo, hi;
+      half_sums_dpp(sdp[u], lo, hi);
+      if (tid % VTL == 0) sSd[(tid + NT * u) / VTL] = (tid & 32) ? hi : lo;
     }
     __syncthreads();  // the tiles are dead: dW, then dQ~ and dKbar on their way to registers
     float (*sX)[K] = (float(*)[K])(sReg + C * K);
@@ -1797,8 +1808,12 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
       for (int bb = 0; bb <= i2; ++bb) dn = fmaf(-sZ[r][bb], sT[i2][bb], dn);
     }
     float part = (r < L && i2 < r) ? dn * Akk[(int64_t)r * C + i2] : 0.f;
+    if constexpr (C == 64) {
+      part = wave_sum_dpp(part);  // a row's 64 columns are one wave
+    } else {
 #pragma unroll
-    for (int off = C / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+      for (int off = C / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+    }
     if (r < C && i2 == 0) sDb[r] += part;
     dak[m] = (r < C) ? sB[r < C ? r : 0] * dn : 0.f;
   }
