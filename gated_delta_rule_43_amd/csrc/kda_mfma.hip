@@ -126,14 +126,30 @@ __device__ __forceinline__ void load4_bf16(const bf16* p, float* out) {
 // Hardware transcendentals (v_exp_f32 / v_log_f32 are base 2, ~1 ulp): the
 // bf16 path's tolerance is far above their error.
 __device__ __forceinline__ float fexp(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
-__device__ __forceinline__ float flog(float x) { return __builtin_amdgcn_logf(x) * 0.6931471805599453f; }
 __device__ __forceinline__ float fsigmoid(float x) { return __builtin_amdgcn_rcpf(1.f + fexp(-x)); }
-__device__ __forceinline__ float fsoftplus(float x) { return fmaxf(x, 0.f) + flog(1.f + fexp(-fabsf(x))); }
-// In-kernel gate, GATE as in FwdArgs::gate_form (see kda_valu.hip for the floor at -110).
+// In-kernel gate, GATE as in FwdArgs::gate_form (see kda_valu.hip for the floor
+// at -110), computed in base-2 units.  x2 = x log2(e) and lb2 = lb log2(e) in,
+// the log-decay times log2(e) out, so that the decays are plain exp2 (no
+// scaling multiply per element): softplus(x) log2(e) = max(x2, 0) +
+// log2(1 + 2^-|x2|) and sigmoid(A x) = 1 / (1 + 2^(-A x2)).  A = 0 (GATE 0, 2)
+// or lb2 = 0 (GATE 1) gives a zero gate, which masks rows past the chunk end.
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
 template <int GATE>
-__device__ __forceinline__ float fgate(float x, float A, float lb) {
-  const float g = GATE == 1 ? lb * fsigmoid(A * x) : -A * fsoftplus(x);
-  return fmaxf(GATE == 2 ? fmaxf(g, lb) : g, kGateFloor);
+__device__ __forceinline__ float fgate2(float x2, float A, float lb2) {
+  float g;
+  if (GATE == 1) {
+    g = lb2 * __builtin_amdgcn_rcpf(1.f + __builtin_amdgcn_exp2f(-A * x2));
+  } else {
+    g = -A * (fmaxf(x2, 0.f) + __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(-fabsf(x2))));
+    if (GATE == 2) g = fmaxf(g, lb2);
+  }
+  return fmaxf(g, kGateFloor * kLog2e);
+}
+// Sum over the four 16-lane rows of the wave, in every lane.
+__device__ __forceinline__ float rows_sum4(float x) {
+  x += __shfl_xor(x, 16);
+  return x + __shfl_xor(x, 32);
 }
 // Row shift right by N inside each 16-lane row (DPP row_shr), zero fill.
 template <int N>
@@ -344,6 +360,8 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
       const float4 d0 = *(const float4*)(db + c0), d1 = *(const float4*)(db + c1);
       lam[8 * j + 0] += d0.x; lam[8 * j + 1] += d0.y; lam[8 * j + 2] += d0.z; lam[8 * j + 3] += d0.w;
       lam[8 * j + 4] += d1.x; lam[8 * j + 5] += d1.y; lam[8 * j + 6] += d1.z; lam[8 * j + 7] += d1.w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) lam[8 * j + e] *= kLog2e;
     }
     float ssq = 0.f, ssk = 0.f;
 #pragma unroll
@@ -351,21 +369,22 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
       ssq = fmaf(qv[s2], qv[s2], ssq);
       ssk = fmaf(kv[s2], kv[s2], ssk);
     }
-    ssq += __shfl_xor(ssq, 16);
-    ssq += __shfl_xor(ssq, 32);
-    ssk += __shfl_xor(ssk, 16);
-    ssk += __shfl_xor(ssk, 32);
+    ssq = rows_sum4(ssq);
+    ssk = rows_sum4(ssk);
     const float rq = valid ? __builtin_amdgcn_rsqf(ssq + 1e-6f) : 0.f;
     const float rk = valid ? __builtin_amdgcn_rsqf(ssk + 1e-6f) : 0.f;
-    const float A = fexp(alog);
-    const float vmask = valid ? 1.f : 0.f;  // the gate is finite (floored), so masking multiplies
+    // q^ carries the attention scale from here on (Qt and Aqk are scaled)
+    const float rqs = rq * a.scale;
+    // a zero coefficient zeroes the gate of a row past the chunk end
+    const float A = valid ? fexp(alog) : 0.f;
+    const float lb2 = valid ? a.lb * kLog2e : 0.f;
 #pragma unroll
     for (int s2 = 0; s2 < KL; ++s2) {
-      qv[s2] *= rq;
+      qv[s2] *= rqs;
       kv[s2] *= rk;
     }
 #pragma unroll
-    for (int s2 = 0; s2 < KL; ++s2) lam[s2] = vmask * fgate<GATE>(lam[s2], A, a.lb);
+    for (int s2 = 0; s2 < KL; ++s2) lam[s2] = fgate2<GATE>(lam[s2], A, GATE == 1 ? lb2 : a.lb * kLog2e);
     if constexpr (OUT32) {
       // the norm scales and the per-token gate of a valid row (channels
       // 32j + 4g.. and 32j + 16 + 4g..); q^ = q rq is rebuilt from them
@@ -380,7 +399,8 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
           for (int hf = 0; hf < 2; ++hf) {
             const int64_t o = th * K + 32 * j + 16 * hf + 4 * g;
             const int e0 = 8 * j + 4 * hf;
-            *(float4*)(a.g + o) = make_float4(lam[e0], lam[e0 + 1], lam[e0 + 2], lam[e0 + 3]);
+            *(float4*)(a.g + o) = make_float4(kLn2 * lam[e0], kLn2 * lam[e0 + 1], kLn2 * lam[e0 + 2],
+                                              kLn2 * lam[e0 + 3]);
           }
       }
     }
@@ -410,14 +430,14 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
     const float lamb[4] = {l0, l1, l2, l3};
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      sFac[kF_EG + b][c] = fexp(gam[b]);
-      sFac[kF_EL + b][c] = fexp(gam[4] - gam[b + 1]);
-      sFac[kF_EML + b][c] = fexp(-lamb[b]);
+      sFac[kF_EG + b][c] = __builtin_amdgcn_exp2f(gam[b]);
+      sFac[kF_EL + b][c] = __builtin_amdgcn_exp2f(gam[4] - gam[b + 1]);
+      sFac[kF_EML + b][c] = __builtin_amdgcn_exp2f(-lamb[b]);
     }
-    sFac[kF_M20][c] = fexp(l1);
-    sFac[kF_M30][c] = fexp(l1 + l2);
-    sFac[kF_M31][c] = fexp(l2);
-    sFac[kF_GL][c] = fexp(gam[4]);
+    sFac[kF_M20][c] = __builtin_amdgcn_exp2f(l1);
+    sFac[kF_M30][c] = __builtin_amdgcn_exp2f(l1 + l2);
+    sFac[kF_M31][c] = __builtin_amdgcn_exp2f(l2);
+    sFac[kF_GL][c] = __builtin_amdgcn_exp2f(gam[4]);
   }
   __syncthreads();
 
@@ -438,9 +458,9 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
 #pragma unroll
     for (int e = 0; e < 8; ++e) negmax = fmaxf(negmax, -lt[e]);
   }
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) negmax = fmaxf(negmax, __shfl_xor(negmax, off));
-  const bool exact_diag = EXACT && negmax > kDiagSafe;  // wave-uniform
+  // (log-decays are in base-2 units here)
+  const bool over = __builtin_amdgcn_ballot_w64(negmax > kDiagSafe * kLog2e) != 0;  // wave-uniform
+  const bool exact_diag = EXACT && over;
   // keep: a sequence of this one chunk, starting from a zero state, is
   // finished here (keep_ok), unless the chunk-head needs the exact fix-up.
   // Then nothing goes to the record: Kbar^T fragments go to sX (whose W
@@ -452,7 +472,7 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
   auto decide_exact = [&]() {
     if (tid == 0) sNeedExact = 0;
     __syncthreads();
-    if (negmax > kDiagSafe && lane == 0) sNeedExact = 1;
+    if (over && lane == 0) sNeedExact = 1;
     __syncthreads();
     const bool need = sNeedExact != 0;
     if (tid == 0 && need) {
@@ -470,7 +490,6 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
   const bf16x8 sel0 = select_frag(g, n, 0), sel1 = select_frag(g, n, 1);
   bf16x8 qrow[NKJ], krow[NKJ], kdiag[NKJ];
   {
-    const float scale = a.scale;
 #pragma unroll
     for (int j = 0; j < NKJ; ++j) {
       float lt[8], eg[8], el[8], eml[8];
@@ -482,11 +501,11 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const float l = lam[8 * j + e];
-        const float ef = fexp(l);            // e^{gamma_r - Gam_w}
-        const float F = fexp(lt[e] - l);     // e^{Gam_{w+1} - gamma_r}
+        const float ef = __builtin_amdgcn_exp2f(l);          // e^{gamma_r - Gam_w}
+        const float F = __builtin_amdgcn_exp2f(lt[e] - l);   // e^{Gam_{w+1} - gamma_r}
         fqr[e] = qv[8 * j + e] * ef;
         fk[e] = kv[8 * j + e] * ef;
-        fq[e] = scale * fqr[e] * eg[e];
+        fq[e] = fqr[e] * eg[e];
         fx[e] = beta_r * fk[e] * eg[e];
         fkb[e] = kv[8 * j + e] * F;
         fkbar[e] = fkb[e] * el[e];
@@ -585,14 +604,12 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
       for (int s2 = 0; s2 < KL; ++s2) {
         const float ki = __shfl(kv[s2], 16 * g + i);
         const float li = __shfl(lam[s2], 16 * g + i);
-        const float d = (i <= n) ? fexp(lam[s2] - li) : 0.f;
+        const float d = (i <= n) ? __builtin_amdgcn_exp2f(lam[s2] - li) : 0.f;
         pq = fmaf(qv[s2] * ki, d, pq);
         pk = fmaf(kv[s2] * ki, d, pk);
       }
-      pq += __shfl_xor(pq, 16);
-      pq += __shfl_xor(pq, 32);
-      pk += __shfl_xor(pk, 16);
-      pk += __shfl_xor(pk, 32);
+      pq = rows_sum4(pq);
+      pk = rows_sum4(pk);
       const bool mine = (i >> 2) == g;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -617,7 +634,7 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
       for (int e = 0; e < 4; ++e) {
         const int i = 16 * I + 4 * g + e;
         vv[e] = (i < r) ? dk[I][e] : 0.f;
-        dq[I][e] = (i <= r) ? a.scale * dq[I][e] : 0.f;
+        dq[I][e] = (i <= r) ? dq[I][e] : 0.f;
       }
       *(uint2*)&sA[r][16 * I + 4 * g] = pk4(vv[0], vv[1], vv[2], vv[3]);
       if (I == w) dgv = make_float4(vv[0], vv[1], vv[2], vv[3]);
