@@ -156,14 +156,6 @@ template <int N>
 __device__ __forceinline__ float row_shr(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x110 + N, 0xF, 0xF, true));
 }
-// Inclusive prefix sum over the 16 lanes of each row.
-__device__ __forceinline__ float row_scan16(float x) {
-  x += row_shr<1>(x);
-  x += row_shr<2>(x);
-  x += row_shr<4>(x);
-  x += row_shr<8>(x);
-  return x;
-}
 
 // 0/1 selection fragment: as a B operand it picks logical column 16*half + n
 // of a 32-wide k-step laid out in sigma order.
@@ -404,8 +396,16 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
           }
       }
     }
+    // the block scan, one shift step over all channels at a time (no DPP
+    // read waits on the add just before it)
 #pragma unroll
-    for (int s2 = 0; s2 < KL; ++s2) lam[s2] = row_scan16(lam[s2]);
+    for (int s2 = 0; s2 < KL; ++s2) lam[s2] += row_shr<1>(lam[s2]);
+#pragma unroll
+    for (int s2 = 0; s2 < KL; ++s2) lam[s2] += row_shr<2>(lam[s2]);
+#pragma unroll
+    for (int s2 = 0; s2 < KL; ++s2) lam[s2] += row_shr<4>(lam[s2]);
+#pragma unroll
+    for (int s2 = 0; s2 < KL; ++s2) lam[s2] += row_shr<8>(lam[s2]);
   };
   float qv[KL], kv[KL], lam[KL];
   row_prologue(qv, kv, lam, true);
@@ -422,8 +422,10 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
   }
   if (g == 0) sBeta[row] = beta_r;
   __syncthreads();
-  // per-channel factor table
-  for (int c = tid; c < K; c += kThreads) {
+  // per-channel factor table, on waves 2 and 3 (wave 0 carries the longest
+  // part of the triangular inverse below)
+  static_assert(K <= kThreads - 128, "one factor-table channel per thread of waves 2 and 3");
+  if (const int c = tid - 128; c >= 0 && c < K) {
     const float l0 = sFac[kF_LAM + 0][c], l1 = sFac[kF_LAM + 1][c];
     const float l2 = sFac[kF_LAM + 2][c], l3 = sFac[kF_LAM + 3][c];
     const float gam[5] = {0.f, l0, l0 + l1, l0 + l1 + l2, l0 + l1 + l2 + l3};
