@@ -65,6 +65,22 @@ __device__ inline void softplus_sigmoid(float x, float* sp, float* sg) {
   *sg = x >= 0.f ? r : e * r;
 }
 
+// The in-kernel gate at x = gate + dt_bias (A = e^a_log), the same arithmetic
+// as gate_grad's value: -A softplus(x) (form 0), lb sigmoid(A x) (form 1),
+// max(lb, -A softplus(x)) (form 2), floored at -110.
+__device__ inline float gate_value(float x, float A, int form, float lb) {
+  float sp, s, g;
+  if (form == 1) {
+    softplus_sigmoid(A * x, &sp, &s);
+    g = lb * s;
+  } else {
+    softplus_sigmoid(x, &sp, &s);
+    g = -A * sp;
+    if (form == 2) g = fmaxf(g, lb);
+  }
+  return fmaxf(g, kGateFloor);
+}
+
 // dg/dx and dg/da_log of the in-kernel gate at x = gate + dt_bias (A = e^a_log);
 // zero where the forward clamped g at the bound or floored it at -110.
 __device__ inline void gate_grad(float x, float A, int form, float lb, float* dgdx, float* dgda) {
@@ -1046,20 +1062,50 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   float (*sTk)[K] = (float(*)[K])sR4;
 
   // ---- phase A: gamma, beta, Tm ----
-  // The chunk's g reaches LDS first, every thread loading its 16-byte pieces
-  // (rows past the chunk end are zero); then each channel's thread adds down
-  // its column.  Loads under a row condition read a clamped, valid row and
-  // select afterwards: a load under a condition of its own is waited for on
-  // the spot.
+  // The chunk's gate g = gate(x + dt_bias) reaches LDS first, every thread
+  // taking 4-channel pieces of the raw gate (rows past the chunk end are zero);
+  // then each channel's thread adds down its column.  Loads under a row
+  // condition read a clamped, valid row and select afterwards: a load under a
+  // condition of its own is waited for on the spot.
   {
     constexpr int NP = (C * K / 4 + NT - 1) / NT;
+    const float Ag = expf(a.a_log[h]);  // as in the gate's derivative below
+    const float* dbh = a.dt_bias + (int64_t)h * K;
+    const bool vec_g = ((uintptr_t)a.gate % (4 * sizeof(Tin))) == 0 && ((uintptr_t)dbh % 16) == 0;
     float4 gq[NP];
 #pragma unroll
     for (int u = 0; u < NP; ++u) {
       const int p = 4 * (tid + u * NT), r = p / K, c = p % K;
       const bool in = p < C * K && r < L;
-      const float4 x = *(const float4*)(a.g + th(in ? r : 0) * K + (in ? c : 0));
-      gq[u] = in ? x : make_float4(0.f, 0.f, 0.f, 0.f);
+      const Tin* gp = (const Tin*)a.gate + th(in ? r : 0) * K + (in ? c : 0);
+      float x[4];
+      if constexpr (std::is_same<Tin, bf16>::value) {
+        if (vec_g) {
+          const uint2 w = *(const uint2*)gp;
+          x[0] = __uint_as_float(w.x << 16);
+          x[1] = __uint_as_float(w.x & 0xffff0000u);
+          x[2] = __uint_as_float(w.y << 16);
+          x[3] = __uint_as_float(w.y & 0xffff0000u);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = load_f32(gp + e);
+        }
+      } else {
+        if (vec_g) {
+          const float4 w = *(const float4*)gp;
+          x[0] = w.x; x[1] = w.y; x[2] = w.z; x[3] = w.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = gp[e];
+        }
+      }
+      const int cc = in ? c : 0;
+      const float4 db = vec_g ? *(const float4*)(dbh + cc) : make_float4(dbh[cc], dbh[cc + 1], dbh[cc + 2], dbh[cc + 3]);
+      gq[u] = in ? make_float4(gate_value(x[0] + db.x, Ag, a.gate_form, a.lb),
+                               gate_value(x[1] + db.y, Ag, a.gate_form, a.lb),
+                               gate_value(x[2] + db.z, Ag, a.gate_form, a.lb),
+                               gate_value(x[3] + db.w, Ag, a.gate_form, a.lb))
+                 : make_float4(0.f, 0.f, 0.f, 0.f);
     }
     for (int r = tid; r < C; r += NT) {
       const float x = a.bt[th(r < L ? r : 0)];

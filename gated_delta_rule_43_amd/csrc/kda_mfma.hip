@@ -134,7 +134,6 @@ __device__ __forceinline__ float fsigmoid(float x) { return __builtin_amdgcn_rcp
 // log2(1 + 2^-|x2|) and sigmoid(A x) = 1 / (1 + 2^(-A x2)).  A = 0 (GATE 0, 2)
 // or lb2 = 0 (GATE 1) gives a zero gate, which masks rows past the chunk end.
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kLn2 = 0.6931471805599453f;
 template <int GATE>
 __device__ __forceinline__ float fgate2(float x2, float A, float lb2) {
   float g;
@@ -263,7 +262,7 @@ enum {
 // path on such blocks.  GATE: the gate form (FwdArgs::gate_form).  CONV: q, k
 // and v are the raw projections, convolved on load (FwdArgs::conv).  OUT32:
 // the backward's recomputation; instead of a record, the factors go to the
-// fp32 row-major arrays the backward reads (rq, rk, g, bt per token-head; Qt,
+// fp32 row-major arrays the backward reads (rq, rk, bt per token-head; Qt,
 // Kb, W, U, Aqk, Akk_out, Tm_out, gL per chunk-head with C = FwdArgs::C rows;
 // Qt, Kb, W, U and Aqk as bf16 when FwdArgs::ws_bf16 is set).
 template <int K, int V, bool EXACT, int GATE, bool CONV, bool OUT32 = false>
@@ -378,22 +377,10 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
 #pragma unroll
     for (int s2 = 0; s2 < KL; ++s2) lam[s2] = fgate2<GATE>(lam[s2], A, GATE == 1 ? lb2 : a.lb * kLog2e);
     if constexpr (OUT32) {
-      // the norm scales and the per-token gate of a valid row (channels
-      // 32j + 4g.. and 32j + 16 + 4g..); q^ = q rq is rebuilt from them
-      if (emit && valid) {
-        if (g == 0) {
-          a.rq[th] = rq;
-          a.rk[th] = rk;
-        }
-#pragma unroll
-        for (int j = 0; j < NKJ; ++j)
-#pragma unroll
-          for (int hf = 0; hf < 2; ++hf) {
-            const int64_t o = th * K + 32 * j + 16 * hf + 4 * g;
-            const int e0 = 8 * j + 4 * hf;
-            *(float4*)(a.g + o) = make_float4(kLn2 * lam[e0], kLn2 * lam[e0 + 1], kLn2 * lam[e0 + 2],
-                                              kLn2 * lam[e0 + 3]);
-          }
+      // the norm scales of a valid row; q^ = q rq is rebuilt from them
+      if (emit && valid && g == 0) {
+        a.rq[th] = rq;
+        a.rk[th] = rk;
       }
     }
     // the block scan, one shift step over all channels at a time (no DPP
