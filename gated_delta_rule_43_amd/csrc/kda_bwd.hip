@@ -1824,6 +1824,24 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   __syncthreads();
 
   // ---- phase E: dN = -Z Tm^T (i < r), dAkk = beta_r dN -> sY; dbeta (second part) ----
+  // this thread's Akk elements for dbeta, issued ahead of the products below
+  // (one uniform branch around each loop: a select between two loads per
+  // element would branch and wait on every load)
+  float akk[NE2];
+  if (a.ws_bf16) {
+    const bf16* akb = (const bf16*)a.Akk_out + chb * C * C;
+#pragma unroll
+    for (int m = 0; m < NE2; ++m) {
+      const int r = rb2 + RSTEP2 * m;
+      akk[m] = bf16_to_f32(akb[(int64_t)(r < C ? r : 0) * C + i2]);
+    }
+  } else {
+#pragma unroll
+    for (int m = 0; m < NE2; ++m) {
+      const int r = rb2 + RSTEP2 * m;
+      akk[m] = Akk[(int64_t)(r < C ? r : 0) * C + i2];
+    }
+  }
   if constexpr (C == 64) {
     // (Z Tm^T)[r][i] on fp32 matrix cores (Tm[i][bb] is zero for bb > i, so a
     // column tile's k-steps end with its own block), into Y's place, which
@@ -1853,7 +1871,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     } else if (r < L && i2 < r) {
       for (int bb = 0; bb <= i2; ++bb) dn = fmaf(-sZ[r][bb], sT[i2][bb], dn);
     }
-    float part = (r < L && i2 < r) ? dn * Akk[(int64_t)r * C + i2] : 0.f;
+    float part = (r < L && i2 < r) ? dn * akk[m] : 0.f;
     if constexpr (C == 64) {
       part = wave_sum_dpp(part);  // a row's 64 columns are one wave
     } else {

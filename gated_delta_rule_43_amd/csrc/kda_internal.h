@@ -67,8 +67,9 @@ struct FwdArgs {
   // backward: the L2 norm's scales 1/||q||, 1/||k|| of each value-head
   // token-head (q^ = q rq), written by the recomputation
   float *rq, *rk;
-  // workspace: per chunk-head factors, fp32; with ws_bf16 set, W, U, Qt, Kb
-  // and Aqk are bf16 (the backward's matrix-core recomputation, 64-token chunks)
+  // workspace: per chunk-head factors, fp32; with ws_bf16 set, W, U, Qt, Kb,
+  // Aqk and Akk_out are bf16 (the backward's matrix-core recomputation,
+  // 64-token chunks)
   int ws_bf16;
   void *W, *U, *Qt, *Kb, *Aqk;
   float* gL;

@@ -264,7 +264,7 @@ enum {
 // the backward's recomputation; instead of a record, the factors go to the
 // fp32 row-major arrays the backward reads (rq, rk, bt per token-head; Qt,
 // Kb, W, U, Aqk, Akk_out, Tm_out, gL per chunk-head with C = FwdArgs::C rows;
-// Qt, Kb, W, U and Aqk as bf16 when FwdArgs::ws_bf16 is set).
+// Qt, Kb, W, U, Aqk and Akk_out as bf16 when FwdArgs::ws_bf16 is set).
 template <int K, int V, bool EXACT, int GATE, bool CONV, bool OUT32 = false>
 __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, const int h,
                                            const int tok0, const int L, char* const rec,
@@ -630,9 +630,14 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
       if (OUT32 && r < C && 16 * I < C) {
         // Akk strictly lower, Aqk (scaled) lower with the diagonal
         const int64_t o = (chb * C + r) * C + 16 * I + 4 * g;
-        *(float4*)(a.Akk_out + o) = make_float4(vv[0], vv[1], vv[2], vv[3]);
-        if (a.ws_bf16) *(uint2*)((bf16*)a.Aqk + o) = pk4(dq[I]);
-        else *(float4*)(((float*)a.Aqk) + o) = make_float4(dq[I][0], dq[I][1], dq[I][2], dq[I][3]);
+        // (bf16 Akk with ws_bf16: the operand Tm was solved from, as in sA)
+        if (a.ws_bf16) {
+          *(uint2*)((bf16*)a.Akk_out + o) = pk4(vv[0], vv[1], vv[2], vv[3]);
+          *(uint2*)((bf16*)a.Aqk + o) = pk4(dq[I]);
+        } else {
+          *(float4*)(a.Akk_out + o) = make_float4(vv[0], vv[1], vv[2], vv[3]);
+          *(float4*)(((float*)a.Aqk) + o) = make_float4(dq[I][0], dq[I][1], dq[I][2], dq[I][3]);
+        }
       }
     }
     fA0 = pair_frag(dq[0], dq[1]);
