@@ -2028,6 +2028,15 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     tkm[m] = tkb;
   }
   if (fuse_qk) {
+    // the rows' norm scales (a row is one wave's: scalar loads), all issued
+    // before the barrier
+    float rqm[NE1], rkm[NE1];
+#pragma unroll
+    for (int m = 0; m < NE1; ++m) {
+      const int r = __builtin_amdgcn_readfirstlane(rb1 + RSTEP1 * m);
+      rqm[m] = a.rq[th(r < L ? r : 0)];
+      rkm[m] = a.rk[th(r < L ? r : 0)];
+    }
     __syncthreads();  // the partial dots are in LDS
     Tin* dqo = (Tin*)b.dq;
     Tin* dko = (Tin*)b.dk;
@@ -2043,8 +2052,8 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
         dk_dot += sPart[(wv * NE1 + m) * 2 + 1];
       }
       const int64_t o = th(r) * K + c1;  // one key head per value head: thk(r) = th(r)
-      store_as(dqo + o, a.rq[th(r)] * (dqv[m] - sQn[r][c1] * dq_dot));
-      store_as(dko + o, a.rk[th(r)] * (dkv[m] - sKn[r][c1] * dk_dot));
+      store_as(dqo + o, rqm[m] * (dqv[m] - sQn[r][c1] * dq_dot));
+      store_as(dko + o, rkm[m] * (dkv[m] - sKn[r][c1] * dk_dot));
     }
   }
   __syncthreads();  // q^, k^ are dead
@@ -2065,6 +2074,14 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   Tin* dgate = (Tin*)b.dgate;
   const Tin* gate = (const Tin*)a.gate;
   const bool segok = sS_ * RSEG < C;
+  // the raw gate of this thread's segment rows, issued before the barriers
+  // below (the loop that uses them walks its rows one after another)
+  float gin[RSEG];
+#pragma unroll
+  for (int u = 0; u < RSEG; ++u) {
+    const int r = sS_ * RSEG + u;
+    gin[u] = load_f32(gate + th(segok && r < L ? r : 0) * K + cS);
+  }
   if (segok) {
     float sdg = 0.f, stk = 0.f;
 #pragma unroll
@@ -2086,13 +2103,13 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
       if (s2 > sS_) run += sSeg[s2][cS];
     }
     const float Aexp = expf(a.a_log[h]), db = a.dt_bias[(int64_t)h * K + cS];
-#pragma unroll 1
+#pragma unroll
     for (int u = RSEG - 1; u >= 0; --u) {
       const int r = sS_ * RSEG + u;
       if (r >= L) continue;
       run += sDg[r][cS];
       float gx, ga;
-      gate_grad(load_f32(gate + th(r) * K + cS) + db, Aexp, a.gate_form, a.lb, &gx, &ga);
+      gate_grad(gin[u] + db, Aexp, a.gate_form, a.lb, &gx, &ga);
       const float dg = run * gx;
       store_as(dgate + th(r) * K + cS, dg);
       ddt += dg;
