@@ -1787,6 +1787,36 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     }
   }
   __syncthreads();  // K~ and dW are dead: Z and q^ take their places
+  // q^ of the chunk (rebuilt from q and its norm scale) and below k^: loaded
+  // ahead of the products of phases D and E and stored to LDS after them
+  // where the registers allow it (not in the 1024-thread kernel, whose
+  // spills grow with them)
+  constexpr bool early_hat = NT < 1024;
+  constexpr int NHAT = (C * K / 4 + NT - 1) / NT;
+  float4 hat_pre[early_hat ? NHAT : 1];
+  auto hat_load = [&](const Tin* x, const float* rs) {
+#pragma unroll
+    for (int u = 0; u < NHAT; ++u) {
+      const int e = tid + u * NT, r = e / (K / 4), c4 = e % (K / 4);
+      hat_pre[u] = hat4(x, rs, e < C * K / 4 && r < L ? r : 0, c4);
+    }
+  };
+  auto hat_store = [&](float (*dst)[K]) {
+#pragma unroll
+    for (int u = 0; u < NHAT; ++u) {
+      const int e = tid + u * NT, r = e / (K / 4), c4 = e % (K / 4);
+      if (e < C * K / 4) ((float4*)&dst[r][0])[c4] = r < L ? hat_pre[u] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  auto hat_direct = [&](const Tin* x, const float* rs, float (*dst)[K]) {
+#pragma unroll
+    for (int e = tid; e < C * K / 4; e += NT) {
+      const int r = e / (K / 4), c4 = e % (K / 4);
+      const float4 v = hat4(x, rs, r < L ? r : 0, c4);
+      ((float4*)&dst[r][0])[c4] = r < L ? v : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+  };
+  if constexpr (early_hat) hat_load((const Tin*)a.q, a.rq);
   if constexpr (C == 64) {
     // (Tm^T Y) on fp32 matrix cores, one 16 x 16 tile per wave and step:
     // Tm[aa][r] is zero for aa < r, so a row tile's k-steps start at its own
@@ -1815,12 +1845,8 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
       if (r < C) sZ[r][i2] = zv[m];
     }
   }
-#pragma unroll
-  for (int e = tid; e < C * K / 4; e += NT) {
-    const int r = e / (K / 4), c4 = e % (K / 4);
-    const float4 x = hat4((const Tin*)a.q, a.rq, r < L ? r : 0, c4);
-    ((float4*)&sQn[r][0])[c4] = r < L ? x : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  if constexpr (early_hat) hat_store(sQn);
+  else hat_direct((const Tin*)a.q, a.rq, sQn);
   __syncthreads();
 
   // ---- phase E: dN = -Z Tm^T (i < r), dAkk = beta_r dN -> sY; dbeta (second part) ----
@@ -1828,6 +1854,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   // (one uniform branch around each loop: a select between two loads per
   // element would branch and wait on every load)
   float akk[NE2];
+  if constexpr (early_hat) hat_load((const Tin*)a.k, a.rk);
   if (a.ws_bf16) {
     const bf16* akb = (const bf16*)a.Akk_out + chb * C * C;
 #pragma unroll
@@ -1887,12 +1914,8 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     const int r = rb2 + RSTEP2 * m;
     if (r < C) sY[r][i2] = dak[m];
   }
-#pragma unroll
-  for (int e = tid; e < C * K / 4; e += NT) {
-    const int r = e / (K / 4), c4 = e % (K / 4);
-    const float4 x = hat4((const Tin*)a.k, a.rk, r < L ? r : 0, c4);
-    ((float4*)&sKn[r][0])[c4] = r < L ? x : make_float4(0.f, 0.f, 0.f, 0.f);
-  }
+  if constexpr (early_hat) hat_store(sKn);
+  else hat_direct((const Tin*)a.k, a.rk, sKn);
   __syncthreads();
 
   // ---- phase F: per element (r, c), the gradients of q^, k^ and gamma ----
