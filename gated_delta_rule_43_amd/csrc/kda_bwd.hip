@@ -104,6 +104,29 @@ __device__ inline void gate_grad(float x, float A, int form, float lb, float* dg
   *dgda = ga;
 }
 
+// The (sequence, head) chain and value-column tile of a state-pass workgroup.
+// Workgroups go to the chip's eight XCDs in turn (id % 8), each XCD with its
+// own L2, and the column tiles of one chain read the same per-chunk K-side
+// operands at about the same time: so all tiles of a chain take ids on one
+// XCD, 8 apart.  Ids past the last whole group of 8 chains map in order.
+__device__ __forceinline__ void chain_tile(int64_t wid, int64_t wgs, int ntile, int& tile, int64_t& nh) {
+  constexpr int kX = 8;
+  if (ntile == 1) {
+    tile = 0;
+    nh = wid;
+    return;
+  }
+  const int64_t full = wgs / (kX * ntile) * (kX * ntile);
+  if (wid < full) {
+    const int64_t x = wid % kX, q = wid / kX;
+    tile = (int)(q % ntile);
+    nh = (q / ntile) * kX + x;
+  } else {
+    tile = (int)(wid % ntile);
+    nh = wid / ntile;
+  }
+}
+
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 // fp32 matrix-core product of one 16 x 4 by 4 x 16 step into a 16 x 16 tile
@@ -179,9 +202,9 @@ __global__ __launch_bounds__(64 * state_waves(C)) void k_bwd_fstate(BwdArgs b) {
   const FwdArgs& a = b.f;
   const int H = a.H, V = a.V;
   const int ntile = V / VT;
-  const int64_t wid = blockIdx.x;
-  const int tile = (int)(wid % ntile);
-  const int64_t nh = wid / ntile;
+  int tile;
+  int64_t nh;
+  chain_tile(blockIdx.x, gridDim.x, ntile, tile, nh);
   const int h = (int)(nh % H), n = (int)(nh / H);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = tile * VT + lane;
@@ -259,9 +282,9 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_mfma(BwdArgs b) {
   const FwdArgs& a = b.f;
   const int H = a.H, V = a.V;
   const int ntile = V / VT;
-  const int64_t wid = blockIdx.x;
-  const int tile = (int)(wid % ntile);
-  const int64_t nh = wid / ntile;
+  int tile;
+  int64_t nh;
+  chain_tile(blockIdx.x, gridDim.x, ntile, tile, nh);
   const int h = (int)(nh % H), n = (int)(nh / H);
   const int col0 = tile * VT;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
@@ -382,9 +405,9 @@ __global__ __launch_bounds__(64 * state_waves(C)) void k_bwd_dstate(BwdArgs b) {
   const FwdArgs& a = b.f;
   const int H = a.H, V = a.V;
   const int ntile = V / VT;
-  const int64_t wid = blockIdx.x;
-  const int tile = (int)(wid % ntile);
-  const int64_t nh = wid / ntile;
+  int tile;
+  int64_t nh;
+  chain_tile(blockIdx.x, gridDim.x, ntile, tile, nh);
   const int h = (int)(nh % H), n = (int)(nh / H);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int col = tile * VT + lane;
@@ -492,9 +515,9 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_mfma(BwdArgs b) {
   const FwdArgs& a = b.f;
   const int H = a.H, V = a.V;
   const int ntile = V / VT;
-  const int64_t wid = blockIdx.x;
-  const int tile = (int)(wid % ntile);
-  const int64_t nh = wid / ntile;
+  int tile;
+  int64_t nh;
+  chain_tile(blockIdx.x, gridDim.x, ntile, tile, nh);
   const int h = (int)(nh % H), n = (int)(nh / H);
   const int col0 = tile * VT;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
@@ -682,9 +705,9 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_bf(BwdArgs b) {
   const FwdArgs& a = b.f;
   const int H = a.H, V = a.V;
   const int ntile = V / VT;
-  const int64_t wid = blockIdx.x;
-  const int tile = (int)(wid % ntile);
-  const int64_t nh = wid / ntile;
+  int tile;
+  int64_t nh;
+  chain_tile(blockIdx.x, gridDim.x, ntile, tile, nh);
   const int h = (int)(nh % H), n = (int)(nh / H);
   const int col0 = tile * VT;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
@@ -807,9 +830,9 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_bf(BwdArgs b) {
   const FwdArgs& a = b.f;
   const int H = a.H, V = a.V;
   const int ntile = V / VT;
-  const int64_t wid = blockIdx.x;
-  const int tile = (int)(wid % ntile);
-  const int64_t nh = wid / ntile;
+  int tile;
+  int64_t nh;
+  chain_tile(blockIdx.x, gridDim.x, ntile, tile, nh);
   const int h = (int)(nh % H), n = (int)(nh / H);
   const int col0 = tile * VT;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
