@@ -488,9 +488,11 @@ def bench_backward(inp, w, steps, warmup):
     return {"workload": w.name + " backward (gradients of q, k, v, gate, beta, a_log, dt_bias)",
             "value": round(tokens / (ms / 1e3) / 1e6, 4), "unit": "Mtokens/s",
             "ms_per_step": round(ms, 3), "wall_ms_per_step": round(wall, 3),
-            "arith": ("bf16 matrix-core recomputation of the chunk factors (fp32 accumulation), "
-                      "then fp32 (VALU, and fp32 matrix cores for the state passes and the chunk "
-                      "kernel's dense products at chunk 64)" if w.torch_dtype == torch.bfloat16
+            "arith": ("bf16 matrix-core recomputation of the chunk factors (fp32 accumulation); "
+                      "state passes and the chunk kernel's value-dimension products on bf16 "
+                      "matrix cores with fp32 states split into bf16 hi + lo pairs; the other "
+                      "dense products on fp32 matrix cores, the per-element work fp32 VALU"
+                      if w.torch_dtype == torch.bfloat16
                       else "fp32 (VALU, and fp32 matrix cores for the state passes and the chunk "
                       "kernel's dense products at chunk 64)"),
             "stage_ms": dict(zip(kda.BWD_STAGE_NAMES, [round(float(x), 4) for x in stage_ms])),
