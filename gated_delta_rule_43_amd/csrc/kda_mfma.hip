@@ -557,6 +557,7 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
     dq[I] = zero4();
     dk[I] = zero4();
     if (I > w) continue;
+    if (16 * w >= L) continue;  // rows past the chunk end: q^ = k^ = 0, so the products are zero
     if (I == w && exact_diag) continue;  // filled by the exact path below
     // factor row e^{Gam_w - Gam_{I+1}} below the diagonal (the diagonal
     // operand already carries e^{-Lam_w})
@@ -693,20 +694,26 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
       bw[i4] = b4.x; bw[i4 + 1] = b4.y; bw[i4 + 2] = b4.z; bw[i4 + 3] = b4.w;
     }
     float tc[16];
+    if (b0 >= L) {
+      // a block past the chunk end (beta = 0): its inverse is the identity
 #pragma unroll
-    for (int rr = 0; rr < 16; ++rr) {
-      float acc[4] = {0.f, 0.f, 0.f, 0.f};
+      for (int rr = 0; rr < 16; ++rr) tc[rr] = (n == rr) ? 1.f : 0.f;
+    } else {
 #pragma unroll
-      for (int i4 = 0; i4 < rr; i4 += 4) {
-        const float4 a4 = *(const float4*)&sDg[w][rr][i4];
-        const float ar[4] = {a4.x, a4.y, a4.z, a4.w};
+      for (int rr = 0; rr < 16; ++rr) {
+        float acc[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (i4 + e < rr) acc[e] = fmaf(ar[e], tc[i4 + e], acc[e]);
+        for (int i4 = 0; i4 < rr; i4 += 4) {
+          const float4 a4 = *(const float4*)&sDg[w][rr][i4];
+          const float ar[4] = {a4.x, a4.y, a4.z, a4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (i4 + e < rr) acc[e] = fmaf(ar[e], tc[i4 + e], acc[e]);
+        }
+        const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
+        // 1 on the diagonal, -beta * sum below it, 0 above (sum is finite)
+        tc[rr] = fmaf((n < rr) ? -bw[rr] : 0.f, sum, (n == rr) ? 1.f : 0.f);
       }
-      const float sum = (acc[0] + acc[1]) + (acc[2] + acc[3]);
-      // 1 on the diagonal, -beta * sum below it, 0 above (sum is finite)
-      tc[rr] = fmaf((n < rr) ? -bw[rr] : 0.f, sum, (n == rr) ? 1.f : 0.f);
     }
     if (g == 0) {
 #pragma unroll
@@ -728,6 +735,15 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
       for (int e = 0; e < 4; ++e) tcol[Ib][e] = sT[16 * Ib + 4 * g + e][16 * Ib + n];
 #pragma unroll
       for (int Rb = Ib + 1; Rb < 4; ++Rb) {
+        if (16 * Rb >= L) {
+          // block rows past the chunk end (beta = 0): Tm_{R,Ib} = 0
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            tcol[Rb][e] = 0.f;
+            sT[16 * Rb + 4 * g + e][16 * Ib + n] = 0.f;
+          }
+          continue;
+        }
         f32x4 p = zero4();
 #pragma unroll
         for (int J0 = Ib; J0 < Rb; J0 += 2) {
