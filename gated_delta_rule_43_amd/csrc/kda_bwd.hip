@@ -52,6 +52,9 @@ constexpr int kThreads = 256;
 constexpr int chunk_threads(int C, int K) { return C == 64 ? (K == 128 ? 1024 : 512) : C == 32 ? 256 : 512; }
 constexpr int kMaxD = 128;
 constexpr float kGateFloor = -110.f;
+// Largest decay of a 16-row block (in a channel) for which the chunk-gradient
+// kernel splits in-block pair factors through the block boundary.
+constexpr float kBlockSafe = 80.f;
 
 // Hardware exponential and logarithm (v_exp_f32 / v_log_f32 after a scaling,
 // about one ulp) and reciprocal: the gate's derivatives enter sums whose fp32
@@ -1939,19 +1942,35 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   }
   if constexpr (early_hat) hat_store(sKn);
   else hat_direct((const Tin*)a.k, a.rk, sKn);
-  __syncthreads();
+  // C = 64: does any 16-row block decay by more than kBlockSafe in a channel?
+  // Then the pairs inside the blocks keep their exact per-pair factor (below).
+  bool exact_blocks = true;
+  if constexpr (C == 64) {
+    bool over = false;
+    if (tid < 4 * K) {
+      const int R = tid / K, c = tid % K;
+      over = (R > 0 ? sGam[16 * R - 1][c] : 0.f) - sGam[16 * R + 15][c] > kBlockSafe;
+    }
+    exact_blocks = __syncthreads_or(over) != 0;
+  } else {
+    __syncthreads();
+  }
 
   // ---- phase F: per element (r, c), the gradients of q^, k^ and gamma ----
   // The pairwise sums over the chunk:
   //   r1 = sum_{i<=r} P[r][i] k^_ic e^{g_rc - g_ic},  r2 likewise with Y,
   //   c12 = sum_{rr>=r} (P[rr][r] q^_rr,c + Y[rr][r] k^_rr,c) e^{g_rr,c - g_rc}.
-  // C = 64: pairs inside a 16-row block take their exact per-pair factor (a
-  // split through the block boundary could overflow there); the blocks before
-  // and after run on the fp32 matrix cores with every factor referenced to a
-  // block boundary (G_R = g at row 16R-1 for the blocks before row block R,
-  // G'_R = g at its last row for the blocks after), so that all are <= 1:
+  // C = 64: the blocks before and after run on the fp32 matrix cores with every
+  // factor referenced to a block boundary (G_R = g at row 16R-1 for the blocks
+  // before row block R, G'_R = g at its last row for the blocks after), so
+  // that all are <= 1:
   //   r1 += e^{g_r - G_R} (P[R rows, <16R] (k^ e^{G_R - g}))
   //   c12 += e^{G'_R - g_r} (P[>R, R cols]^T (q^ e^{g - G'_R}) + Y^T (k^ e^{g - G'_R})).
+  // The pairs inside a block join those products (k-steps 16R..16R+15, P and
+  // Y being zero above the diagonal) while no block decays by more than
+  // kBlockSafe: their inner factors e^{G_R - g_i} and e^{g_rr - G'_R} then stay
+  // below e^kBlockSafe.  Otherwise (exact_blocks) each in-block pair takes its
+  // exact factor e^{g_r - g_i} in the per-element loops.
   // Their tiles reach the element owners through the LDS that Tm used.
   // The blocks' terms are summed first (per owner: x1 = r1, x2 = r2 + c12,
   // x3 = q^ r1 + k^ (r2 - c12) of the off-diagonal blocks), then the in-block
@@ -1977,9 +1996,10 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
           f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
           float rowf[4] = {0.f, 0.f, 0.f, 0.f};
           if (kind < 2) {
-            if (R > 0 && 16 * R < L) {  // rows before 16R are all inside the chunk
-              const float gR = sGam[16 * R - 1][col];
-              for (int kk = 0; kk < 16 * R; kk += 4) {
+            const int kend = exact_blocks ? 16 * R : 16 * R + 16;
+            if (kend > 0 && 16 * R < L) {  // rows before 16R are all inside the chunk
+              const float gR = R > 0 ? sGam[16 * R - 1][col] : 0.f;
+              for (int kk = 0; kk < kend; kk += 4) {
                 const int i = kk + lg;
                 const float bk = sKn[i][col] * __expf(gR - sGam[i][col]);
                 acc = mfma_f32(kind == 0 ? sP[16 * R + ln][i] : sY[16 * R + ln][i], bk, acc);
@@ -1987,10 +2007,10 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
 #pragma unroll
               for (int e = 0; e < 4; ++e) rowf[e] = __expf(sGam[16 * R + 4 * lg + e][col] - gR);
             }
-          } else if (R < 3 && 16 * (R + 1) < L) {
+          } else if (const int kbeg = exact_blocks ? 16 * (R + 1) : 16 * R; kbeg < C && kbeg < L) {
             // g is constant past the chunk end, and q^, k^ are zero there
             const float gE = sGam[16 * R + 15][col];
-            for (int kk = 16 * (R + 1); kk < C; kk += 4) {
+            for (int kk = kbeg; kk < C; kk += 4) {
               const int rr = kk + lg;
               const float f = __expf(sGam[rr][col] - gE);
               acc = mfma_f32(sP[rr][16 * R + ln], sQn[rr][col] * f, acc);
@@ -2038,8 +2058,9 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     const int r = __builtin_amdgcn_readfirstlane(rb1 + RSTEP1 * m), c = c1;
     dgm[m] = tkm[m] = 0.f;
     if (r >= L) continue;
-    const int i0 = C == 64 ? (r & ~15) : 0;              // first column summed here
-    const int rr1 = C == 64 ? min((r | 15) + 1, L) : L;  // past the last row summed here
+    // (the in-block pairs ran on the matrix cores unless exact_blocks)
+    const int i0 = C == 64 ? (exact_blocks ? (r & ~15) : r + 1) : 0;   // first column summed here
+    const int rr1 = C == 64 ? (exact_blocks ? min((r | 15) + 1, L) : r) : L;  // past the last row summed here
     const float q = sQn[r][c], kk = sKn[r][c];
     const float gm = sGam[r][c], egm = __expf(gm), ekb = __expf(sGam[L - 1][c] - gm);
     float r1 = 0.f, r2 = 0.f;
