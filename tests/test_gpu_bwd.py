@@ -218,6 +218,42 @@ def test_bwd_fp32_extreme_gates():
     _run(inp, d_o, d_fin, torch.float32, "fp32 extreme gates")
 
 
+def _max_block_decay(inp, head):
+    """Largest decay of a 16-row block of 64-token chunks, over channels, for one
+    head (plain in-kernel gate, documents from position 0 of each sequence)."""
+    x = inp["gate"].float().cpu()[0, :, head] + inp["dt_bias"].float().cpu()[head]
+    g = -torch.exp(inp["a_log"].float().cpu()[head]) * torch.nn.functional.softplus(x)
+    g = torch.clamp(g, min=-110.0)
+    cu = to_np(inp["cu_seqlens"]).astype(np.int64)
+    worst = 0.0
+    for s0, s1 in zip(cu[:-1], cu[1:]):
+        for b in range(s0, s1, 16):
+            worst = max(worst, float(-g[b:min(b + 16, s1)].sum(0).min()))
+    return worst
+
+
+@pytest.mark.parametrize("K", [128, 64])
+def test_bwd_fp32_mixed_in_block_paths(K):
+    """One call in which some chunk-heads keep the exact per-pair factors for
+    the pairs inside 16-row blocks (a block decays by more than 80 nats in a
+    channel: head 0) and the others take them on the matrix cores through the
+    block boundary (head 1), at fp32 tolerance."""
+    _banner("bwd fp32 mixed in-block paths K=%d" % K)
+    inp = to_device(synthetic.random_problem(47, 1, 300, 2, K, 128, dtype=torch.float32,
+                                             init_std=0.5, lengths=[170, 93, 37]))
+    gen = torch.Generator(device="cpu").manual_seed(9)
+    gate = inp["gate"].cpu()
+    spikes = torch.rand(gate[:, :, 0].shape, generator=gen) < 0.15
+    g0 = gate[:, :, 0]
+    g0[spikes] = 30.0
+    gate[:, :, 0] = g0
+    inp["gate"] = gate.to(DEV)
+    inp["a_log"] = torch.tensor([0.5, -1.0], device=DEV)
+    assert _max_block_decay(inp, 0) > 80.0 and _max_block_decay(inp, 1) < 80.0
+    d_o, d_fin = _upstream(inp, 19)
+    _run(inp, d_o, d_fin, torch.float32, "fp32 mixed in-block paths")
+
+
 # bf16 inputs recompute the chunk factors on the matrix-core chunk kernel
 # (bf16 operands, fp32 accumulation); KDA_BWD_RECOMPUTE=valu keeps the fp32
 # vector-ALU kernels.  Both are held to the bf16 tolerance above.
