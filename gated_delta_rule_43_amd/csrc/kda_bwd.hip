@@ -161,18 +161,6 @@ template <int CTRL, int ROWS, bool ZERO>
 __device__ __forceinline__ float dpp_f(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xF, ZERO));
 }
-// Sums over each 32-lane half of the wave on the VALU: row prefix sums, then
-// rows 0 and 2 into rows 1 and 3; lanes 31 and 63 hold the two halves' sums
-// (returned as lo and hi to every lane).
-__device__ inline void half_sums_dpp(float x, float& lo, float& hi) {
-  x += dpp_f<0x111, 0xF, true>(x);
-  x += dpp_f<0x112, 0xF, true>(x);
-  x += dpp_f<0x114, 0xF, true>(x);
-  x += dpp_f<0x118, 0xF, true>(x);
-  x += dpp_f<0x142, 0xA, false>(x);
-  lo = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 31));
-  hi = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
-}
 __device__ inline float wave_sum_dpp(float x) {
   x += dpp_f<0x111, 0xF, true>(x);
   x += dpp_f<0x112, 0xF, true>(x);
@@ -1182,9 +1170,10 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     //   M1 = dDelta S0^T (-> -dW), M2 = dO S0^T (-> dQ~), M3 = Delta dS_L^T (-> dKbar),
     //   P = dO Delta^T and Yv = dDelta V^T (lower tiles); dV = Diag(beta) Tm^T dDelta
     //   on the fp32 matrix cores with dDelta from its pair.
-    // Each tile reaches registers one tile ahead of its products;
-    // rowsum(S0 . dS_L) comes from those registers (row (tid + NT u) / VTL,
-    // column tid % VTL).
+    // Each tile reaches registers one tile ahead of its products, every thread
+    // taking one 4-column piece of a row of S0 and dS_L and one NR-column piece
+    // of a row of Delta, dDelta, dO and V (16-, 8- and 4-byte loads, 8- and
+    // 4-byte LDS writes); rowsum(S0 . dS_L) comes from those registers.
     constexpr int NW = NT / 64;
     const int lane = tid & 63, w = tid >> 6, ln = lane & 15, lg = lane >> 4;
     static_assert(2 * NW * 16 * 16 == C * K, "two output tiles per wave and product");
@@ -1192,6 +1181,12 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     const int rt = w & 3, ct0 = 2 * (w >> 2);  // M1..M3 tiles: row tile rt, column tiles ct0, ct0 + 1
     constexpr int NS = K * VTL / NT, NR = C * VTL / NT;
     static_assert(NS * NT == K * VTL && NR * NT == C * VTL, "whole tiles per thread");
+    static_assert(NS == 4 && (NR == 2 || NR == 4), "one piece of each operand per thread");
+    // this thread's pieces: S0 / dS_L row sc, columns sj .. sj + 3; Delta,
+    // dDelta, dO, V row rr, columns rj .. rj + NR - 1 (of the value tile)
+    const int sc = tid / (VTL / 4), sj = 4 * (tid % (VTL / 4));
+    const int rr = tid / (VTL / NR), rj = NR * (tid % (VTL / NR));
+    const bool vec_ov = ((uintptr_t)dO % (NR * sizeof(Tin))) == 0 && ((uintptr_t)v % (NR * sizeof(Tin))) == 0;
     constexpr int BP = VTL + 8;
     bf16 (*hS0)[BP] = (bf16(*)[BP])sReg;
     bf16 (*lS0)[BP] = hS0 + K;
@@ -1221,46 +1216,93 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     // 512-thread workgroups (K = 64) keep two tiles in flight: tile t's loads
     // are issued two steps ahead of its products, into the register set of
     // its parity
-    struct Tile { float s[NS], l[NS], D[NR], d[NR], o[NR], v[NR]; };
+    struct Tile { f32x4 s, l; float D[NR], d[NR], o[NR], v[NR]; };
     Tile ta, tb;
-    float sdp[NS];
-#pragma unroll
-    for (int u = 0; u < NS; ++u) sdp[u] = 0.f;
+    float sdp = 0.f;
     auto fetch = [&](Tile& x, int j0) __attribute__((always_inline)) {
+      const float4 s4 = *(const float4*)(S0 + (int64_t)sc * V + j0 + sj);
+      const float4 l4 = *(const float4*)(dSL + (int64_t)sc * V + j0 + sj);
+      x.s = f32x4{s4.x, s4.y, s4.z, s4.w};
+      x.l = f32x4{l4.x, l4.y, l4.z, l4.w};
+      const int64_t dr = (int64_t)rr * V + j0 + rj;
+      if constexpr (NR == 2) {
+        const float2 d2 = *(const float2*)(dDl + dr), D2 = *(const float2*)(Dl + dr);
+        x.d[0] = d2.x; x.d[1] = d2.y;
+        x.D[0] = D2.x; x.D[1] = D2.y;
+      } else {
+        const float4 d4 = *(const float4*)(dDl + dr), D4 = *(const float4*)(Dl + dr);
+        x.d[0] = d4.x; x.d[1] = d4.y; x.d[2] = d4.z; x.d[3] = d4.w;
+        x.D[0] = D4.x; x.D[1] = D4.y; x.D[2] = D4.z; x.D[3] = D4.w;
+      }
+      // rows past the chunk end read row 0 and are zeroed after the loads
+      const bool in = rr < L;
+      const int64_t rv = th(in ? rr : 0) * V + j0 + rj;
+      float fo[NR], fv[NR];
+      if (vec_ov) {
+        uint32_t uo[NR / 2], uv[NR / 2];
+        if constexpr (NR == 2) {
+          uo[0] = *(const uint32_t*)(dO + rv);
+          uv[0] = *(const uint32_t*)(v + rv);
+        } else {
+          const uint2 o2 = *(const uint2*)(dO + rv), v2 = *(const uint2*)(v + rv);
+          uo[0] = o2.x; uo[1] = o2.y;
+          uv[0] = v2.x; uv[1] = v2.y;
+        }
 #pragma unroll
-      for (int u = 0; u < NS; ++u) {
-        const int e = tid + NT * u, c = e / VTL, jj = e % VTL;
-        x.s[u] = S0[(int64_t)c * V + j0 + jj];
-        x.l[u] = dSL[(int64_t)c * V + j0 + jj];
+        for (int q = 0; q < NR / 2; ++q) {
+          fo[2 * q] = __uint_as_float(uo[q] << 16);
+          fo[2 * q + 1] = __uint_as_float(uo[q] & 0xffff0000u);
+          fv[2 * q] = __uint_as_float(uv[q] << 16);
+          fv[2 * q + 1] = __uint_as_float(uv[q] & 0xffff0000u);
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < NR; ++e) {
+          fo[e] = load_f32(dO + rv + e);
+          fv[e] = load_f32(v + rv + e);
+        }
       }
 #pragma unroll
-      for (int u = 0; u < NR; ++u) {
-        const int e = tid + NT * u, r = e / VTL, jj = e % VTL;
-        const bool in = r < L;
-        x.d[u] = dDl[(int64_t)r * V + j0 + jj];
-        x.D[u] = Dl[(int64_t)r * V + j0 + jj];
-        const int64_t rv = th(in ? r : 0) * V + j0 + jj;
-        const float xo = load_f32(dO + rv), xv = load_f32(v + rv);
-        x.o[u] = in ? xo : 0.f;
-        x.v[u] = in ? xv : 0.f;
+      for (int e = 0; e < NR; ++e) {
+        x.o[e] = in ? fo[e] : 0.f;
+        x.v[e] = in ? fv[e] : 0.f;
       }
     };
+    // NR values as bf16 in LDS, NR / 2 words
+    auto put_bf16 = [&](bf16* dst, const float* f) __attribute__((always_inline)) {
+      uint32_t wds[NR / 2];
+#pragma unroll
+      for (int q = 0; q < NR / 2; ++q)
+        wds[q] = (uint32_t)__builtin_bit_cast(unsigned short, (__bf16)f[2 * q]) |
+                 ((uint32_t)__builtin_bit_cast(unsigned short, (__bf16)f[2 * q + 1]) << 16);
+      if constexpr (NR == 2) *(uint32_t*)dst = wds[0];
+      else *(uint2*)dst = make_uint2(wds[0], wds[1]);
+    };
+    // NR values as bf16 hi + lo parts (hi = bf16(x), lo = bf16(x - hi))
+    auto put_split = [&](bf16* dhi, bf16* dlo, const float* f) __attribute__((always_inline)) {
+      float hv_[NR], lv_[NR];
+#pragma unroll
+      for (int e = 0; e < NR; ++e) {
+        hv_[e] = (float)(__bf16)f[e];
+        lv_[e] = f[e] - hv_[e];
+      }
+      put_bf16(dhi, hv_);
+      put_bf16(dlo, lv_);
+    };
     auto stage = [&](const Tile& x) __attribute__((always_inline)) {
+      uint2 hi, lo;
+      split4_bf16(x.s, hi, lo);
+      *(uint2*)&hS0[sc][sj] = hi;
+      *(uint2*)&lS0[sc][sj] = lo;
+      split4_bf16(x.l, hi, lo);
+      *(uint2*)&hSL[sc][sj] = hi;
+      *(uint2*)&lSL[sc][sj] = lo;
 #pragma unroll
-      for (int u = 0; u < NS; ++u) {
-        const int e = tid + NT * u, c = e / VTL, jj = e % VTL;
-        split_bf16(x.s[u], hS0[c][jj], lS0[c][jj]);
-        split_bf16(x.l[u], hSL[c][jj], lSL[c][jj]);
-        sdp[u] = fmaf(x.s[u], x.l[u], sdp[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < NR; ++u) {
-        const int e = tid + NT * u, r = e / VTL, jj = e % VTL;
-        split_bf16(x.d[u], hdD[r][jj], ldD[r][jj]);
-        split_bf16(x.D[u], hD[r][jj], lD[r][jj]);
-        hdO[r][jj] = to_bf16(x.o[u]);
-        hv[r][jj] = to_bf16(x.v[u]);
-      }
+      for (int e = 0; e < 4; ++e) sdp = fmaf(x.s[e], x.l[e], sdp);
+      put_split(&hdD[rr][rj], &ldD[rr][rj], x.d);
+      put_split(&hD[rr][rj], &lD[rr][rj], x.D);
+      put_bf16(&hdO[rr][rj], x.o);
+      put_bf16(&hv[rr][rj], x.v);
     };
     auto products = [&](const int j0) __attribute__((always_inline)) {
       {
@@ -1346,13 +1388,11 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
         products(j0);
       }
     }
-    // rowsum(S0 . dS_L): each row's 32 columns sit in one half-wave
-#pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      float lo, hi;
-      half_sums_dpp(sdp[u], lo, hi);
-      if (tid % VTL == 0) sSd[(tid + NT * u) / VTL] = (tid & 32) ? hi : lo;
-    }
+    // rowsum(S0 . dS_L): each row's pieces sit in 8 consecutive lanes
+    sdp += __shfl_xor(sdp, 1);
+    sdp += __shfl_xor(sdp, 2);
+    sdp += __shfl_xor(sdp, 4);
+    if (sj == 0) sSd[sc] = sdp;
     __syncthreads();  // the tiles are dead: dW, then dQ~ and dKbar on their way to registers
     float (*sX)[K] = (float(*)[K])(sReg + C * K);
 #pragma unroll
