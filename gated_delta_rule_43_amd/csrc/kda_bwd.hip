@@ -171,7 +171,6 @@ __device__ inline float wave_sum_dpp(float x) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
 }
 
-
 // Copy n floats (n a multiple of 4, 16-byte aligned) from global memory to LDS
 // with a workgroup of nt threads.
 __device__ inline void stage(float* dst, const float* src, int n, int nt) {
