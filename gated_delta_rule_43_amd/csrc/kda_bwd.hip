@@ -714,10 +714,13 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_bf(BwdArgs b) {
   float pgl[TPW][4];
   const int drt = w >> 2, dct = w & 3;
   auto fetch = [&](int64_t chb) __attribute__((always_inline)) {
-    const bf16* U = (const bf16*)a.U + chb * C * V;
+    // U as 16 x 16 accumulator tiles of bf16 ([row tile][column tile][lane][4])
+    const uint2 u4 = ((const uint2*)a.U)[((chb * 4 + drt) * (V / 16) + col0 / 16 + dct) * 64 + lane];
     const float* gL = a.gL + chb * K;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) pu[e] = load_f32(U + (int64_t)(16 * drt + 4 * lg + e) * V + col0 + 16 * dct + ln);
+    pu[0] = __uint_as_float(u4.x << 16);
+    pu[1] = __uint_as_float(u4.x & 0xffff0000u);
+    pu[2] = __uint_as_float(u4.y << 16);
+    pu[3] = __uint_as_float(u4.y & 0xffff0000u);
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll

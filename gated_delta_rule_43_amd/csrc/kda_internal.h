@@ -69,7 +69,9 @@ struct FwdArgs {
   float *rq, *rk;
   // workspace: per chunk-head factors, fp32; with ws_bf16 set, W, U, Qt, Kb,
   // Aqk and Akk_out are bf16 (the backward's matrix-core recomputation,
-  // 64-token chunks)
+  // 64-token chunks), U then as 16 x 16 accumulator tiles
+  // ([C/16][V/16][64 lanes][4]: lane l holds rows 4 (l / 16) .. + 3 of column
+  // l % 16 of its tile)
   int ws_bf16;
   void *W, *U, *Qt, *Kb, *Aqk;
   float* gL;

@@ -264,7 +264,8 @@ enum {
 // the backward's recomputation; instead of a record, the factors go to the
 // fp32 row-major arrays the backward reads (rq, rk, bt per token-head; Qt,
 // Kb, W, U, Aqk, Akk_out, Tm_out, gL per chunk-head with C = FwdArgs::C rows;
-// Qt, Kb, W, U, Aqk and Akk_out as bf16 when FwdArgs::ws_bf16 is set).
+// Qt, Kb, W, U, Aqk and Akk_out as bf16 when FwdArgs::ws_bf16 is set, U then
+// as 16 x 16 accumulator tiles).
 template <int K, int V, bool EXACT, int GATE, bool CONV, bool OUT32 = false>
 __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, const int h,
                                            const int tok0, const int L, char* const rec,
@@ -887,14 +888,17 @@ __device__ __forceinline__ void chunk_body(const FwdArgs& a, const int jchunk, c
           if (t >= 2) acc = mfma(tfrag[t][1], vb[1][a2], acc);
           const int at = (t * NVT + 2 * p + a2) * 64 + lane;
           if (OUT32) {
-            // lane (g, n): U[16t + 4g + e][32p + 16a2 + n]
+            // lane (g, n): U[16t + 4g + e][32p + 16a2 + n].  bf16 (64-row
+            // chunks): as 16 x 16 accumulator tiles, [row tile][column tile]
+            // [lane][4], the layout the backward's state pass reads; fp32: row-major
+            if (a.ws_bf16) {
+              ((uint2*)a.U)[((chb * 4 + t) * NVT + 2 * p + a2) * 64 + lane] = pk4(acc);
+            } else {
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const int r = 16 * t + 4 * g + e;
-              const int64_t o = (chb * C + r) * V + 32 * p + 16 * a2 + n;
-              if (r >= C) continue;
-              if (a.ws_bf16) ((bf16*)a.U)[o] = f32_to_bf16(acc[e]);
-              else ((float*)a.U)[o] = acc[e];
+              for (int e = 0; e < 4; ++e) {
+                const int r = 16 * t + 4 * g + e;
+                if (r < C) ((float*)a.U)[(chb * C + r) * V + 32 * p + 16 * a2 + n] = acc[e];
+              }
             }
           } else if (keep) {
             ((uint2*)sU1)[at] = pk4(acc);
