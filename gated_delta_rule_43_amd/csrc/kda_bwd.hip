@@ -709,29 +709,24 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_bf(BwdArgs b) {
   // and gL entries: one chunk ahead, in named registers
   constexpr int NP = C * K / 4 / NT;
   static_assert(NP == 1 || NP == 2, "one or two pieces per thread");
-  uint2 pw0, pw1, pk0, pk1;
-  f32x4 pu;
-  float pgl[TPW][4];
+  struct Pre { uint2 pw0, pw1, pk0, pk1; uint2 u4; float pgl[TPW][4]; };
+  Pre P0, P1;
   const int drt = w >> 2, dct = w & 3;
-  auto fetch = [&](int64_t chb) __attribute__((always_inline)) {
+  auto fetch = [&](Pre& x, int64_t chb) __attribute__((always_inline)) {
     // U as 16 x 16 accumulator tiles of bf16 ([row tile][column tile][lane][4])
-    const uint2 u4 = ((const uint2*)a.U)[((chb * 4 + drt) * (V / 16) + col0 / 16 + dct) * 64 + lane];
+    x.u4 = ((const uint2*)a.U)[((chb * 4 + drt) * (V / 16) + col0 / 16 + dct) * 64 + lane];
     const float* gL = a.gL + chb * K;
-    pu[0] = __uint_as_float(u4.x << 16);
-    pu[1] = __uint_as_float(u4.x & 0xffff0000u);
-    pu[2] = __uint_as_float(u4.y << 16);
-    pu[3] = __uint_as_float(u4.y & 0xffff0000u);
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) pgl[t][e] = gL[16 * ((w * TPW + t) >> 2) + 4 * lg + e];
+      for (int e = 0; e < 4; ++e) x.pgl[t][e] = gL[16 * ((w * TPW + t) >> 2) + 4 * lg + e];
     const uint2* W4 = (const uint2*)((const bf16*)a.W + chb * C * K);
     const uint2* K4 = (const uint2*)((const bf16*)a.Kb + chb * C * K);
-    pw0 = W4[tid];
-    pk0 = K4[tid];
+    x.pw0 = W4[tid];
+    x.pk0 = K4[tid];
     if constexpr (NP == 2) {
-      pw1 = W4[tid + NT];
-      pk1 = K4[tid + NT];
+      x.pw1 = W4[tid + NT];
+      x.pk1 = K4[tid + NT];
     }
   };
   auto put = [&](int p, uint2 wv, uint2 kv) __attribute__((always_inline)) {
@@ -752,17 +747,17 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_bf(BwdArgs b) {
     }
   }
   const int jc0 = a.seq_chunk0[n], jc1 = a.seq_chunk0[n + 1];
-  if (jc0 < jc1) fetch((int64_t)jc0 * H + h);
-  for (int j = jc0; j < jc1; ++j) {
+  auto chunk = [&](Pre& cur, const int j) __attribute__((always_inline)) {
     const int64_t chb = (int64_t)j * H + h;
     float* hc = b.hc + chb * K * V;
     float* Dc = b.Dc + chb * C * V;
-    f32x4 acc = pu;
+    f32x4 acc = {__uint_as_float(cur.u4.x << 16), __uint_as_float(cur.u4.x & 0xffff0000u),
+                 __uint_as_float(cur.u4.y << 16), __uint_as_float(cur.u4.y & 0xffff0000u)};
     float gl[TPW][4];
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) gl[t][e] = pgl[t][e];
+      for (int e = 0; e < 4; ++e) gl[t][e] = cur.pgl[t][e];
     __syncthreads();  // the previous chunk is done with the LDS operands
 #pragma unroll
     for (int t = 0; t < TPW; ++t) {
@@ -775,11 +770,12 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_bf(BwdArgs b) {
       *(uint2*)&sSh[16 * sct + ln][16 * srt + 4 * lg] = hi;
       *(uint2*)&sSl[16 * sct + ln][16 * srt + 4 * lg] = lo;
     }
-    put(tid, pw0, pk0);
-    if constexpr (NP == 2) put(tid + NT, pw1, pk1);
+    put(tid, cur.pw0, cur.pk0);
+    if constexpr (NP == 2) put(tid + NT, cur.pw1, cur.pk1);
     __builtin_amdgcn_sched_barrier(0);
-    // the next chunk of this sequence (the last chunk reads itself again, unused)
-    fetch(j + 1 < jc1 ? chb + H : chb);
+    // the chunk two after this one (near the sequence end a chunk reads itself
+    // again, unused)
+    fetch(cur, j + 2 < jc1 ? chb + 2 * H : chb);
     __syncthreads();
     // Delta = U - W S
 #pragma unroll
@@ -812,7 +808,15 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_bf(BwdArgs b) {
         st[t] = mfma_bf16(ka, frag8(&sDl[16 * sct + ln][r0 + 8 * lg]), st[t]);
       }
     }
+  };
+  if (jc0 < jc1) fetch(P0, (int64_t)jc0 * H + h);
+  if (jc0 + 1 < jc1) fetch(P1, (int64_t)(jc0 + 1) * H + h);
+  int j = jc0;
+  for (; j + 1 < jc1; j += 2) {
+    chunk(P0, j);
+    chunk(P1, j + 1);
   }
+  if (j < jc1) chunk(P0, j);
 }
 
 template <int K>
