@@ -152,6 +152,12 @@ __device__ __forceinline__ void split_bf16(float x, bf16& hi, bf16& lo) {
 __device__ __forceinline__ bf16 to_bf16(float x) { return __builtin_bit_cast(bf16, (__bf16)x); }
 // 8 consecutive bf16 of an LDS row (16-byte aligned)
 __device__ __forceinline__ bf16x8 frag8(const bf16* p) { return *(const bf16x8*)p; }
+// Column of element (row, col) in a bf16 LDS array whose rows are read as
+// 16-byte chunks of 8 and written transposed (lanes stepping 4 rows, rows 72
+// or 136 bf16 long): the chunk index is XORed with bits 3..5 of the row, so
+// that 32 such lanes reach 8 of the 32 banks instead of 2, while a chunk stays
+// 16 contiguous bytes.  For columns below 64.
+__device__ __forceinline__ int swz8(int row, int col) { return (((col >> 3) ^ ((row >> 3) & 7)) << 3) | (col & 7); }
 
 // Sum over the 64 lanes on the VALU (DPP): inclusive prefix sums inside each
 // 16-lane row (row_shr 1, 2, 4, 8, zero fill), then row 0's total into row 1
@@ -733,7 +739,7 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_bf(BwdArgs b) {
     const int r = p / (K / 4), c = 4 * (p % (K / 4));
     *(uint2*)&sWn[r][c] = make_uint2(wv.x ^ 0x80008000u, wv.y ^ 0x80008000u);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) sKbT[c + q][r] = elem4(kv, q);
+    for (int q = 0; q < 4; ++q) sKbT[c + q][swz8(c + q, r)] = elem4(kv, q);
   };
   const int64_t sbase = ((int64_t)n * H + h) * K * V;
   f32x4 st[TPW];
@@ -803,7 +809,7 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_bf(BwdArgs b) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         const int s = w * TPW + t, srt = s >> 2, sct = s & 3;
-        const bf16x8 ka = frag8(&sKbT[16 * srt + ln][r0 + 8 * lg]);
+        const bf16x8 ka = frag8(&sKbT[16 * srt + ln][swz8(16 * srt + ln, r0 + 8 * lg)]);
         st[t] = mfma_bf16(ka, frag8(&sDh[16 * sct + ln][r0 + 8 * lg]), st[t]);
         st[t] = mfma_bf16(ka, frag8(&sDl[16 * sct + ln][r0 + 8 * lg]), st[t]);
       }
@@ -875,8 +881,8 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_bf(BwdArgs b) {
     *(uint2*)&sKb[r][c] = kv;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      sQT[c + q][r] = elem4(qv, q);
-      sWT[c + q][r] = elem4(wv, q) ^ 0x8000u;
+      sQT[c + q][swz8(c + q, r)] = elem4(qv, q);
+      sWT[c + q][swz8(c + q, r)] = elem4(wv, q) ^ 0x8000u;
     }
   };
   const int64_t sbase = ((int64_t)n * H + h) * K * V;
@@ -914,12 +920,12 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_bf(BwdArgs b) {
 #pragma unroll
     for (int u = 0; u < NO; ++u) {
       const int e = tid + u * NT, r = e / VT, cc = e % VT;
-      sOT[cc][r] = r < L ? po[u] : (bf16)0;
+      sOT[cc][swz8(cc, r)] = r < L ? po[u] : (bf16)0;
     }
     {
       const int rr = tid / (C / 4), i = 4 * (tid % (C / 4));
 #pragma unroll
-      for (int q = 0; q < 4; ++q) sAT[i + q][rr] = elem4(pa, q);
+      for (int q = 0; q < 4; ++q) sAT[i + q][swz8(i + q, rr)] = elem4(pa, q);
     }
     put(tid, pk0, pq0, pw0);
     if constexpr (NP == 2) put(tid + NT, pk1, pq1, pw1);
@@ -941,7 +947,8 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_bf(BwdArgs b) {
 #pragma unroll
       for (int r0 = 0; r0 < C; r0 += 32)
         if (16 * drt < r0 + 32)
-          acc = mfma_bf16(frag8(&sAT[16 * drt + ln][r0 + 8 * lg]), frag8(&sOT[16 * dct + ln][r0 + 8 * lg]), acc);
+          acc = mfma_bf16(frag8(&sAT[16 * drt + ln][swz8(16 * drt + ln, r0 + 8 * lg)]),
+                          frag8(&sOT[16 * dct + ln][swz8(16 * dct + ln, r0 + 8 * lg)]), acc);
 #pragma unroll
       for (int c0 = 0; c0 < K; c0 += 32) {
         const bf16x8 ka = frag8(&sKb[16 * drt + ln][c0 + 8 * lg]);
@@ -966,8 +973,9 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_bf(BwdArgs b) {
 #pragma unroll
       for (int t = 0; t < TPW; ++t) {
         const int s = w * TPW + t, srt = s >> 2, sct = s & 3;
-        st[t] = mfma_bf16(frag8(&sQT[16 * srt + ln][r0 + 8 * lg]), frag8(&sOT[16 * sct + ln][r0 + 8 * lg]), st[t]);
-        const bf16x8 wa = frag8(&sWT[16 * srt + ln][r0 + 8 * lg]);
+        st[t] = mfma_bf16(frag8(&sQT[16 * srt + ln][swz8(16 * srt + ln, r0 + 8 * lg)]),
+                          frag8(&sOT[16 * sct + ln][swz8(16 * sct + ln, r0 + 8 * lg)]), st[t]);
+        const bf16x8 wa = frag8(&sWT[16 * srt + ln][swz8(16 * srt + ln, r0 + 8 * lg)]);
         st[t] = mfma_bf16(wa, frag8(&sDh[16 * sct + ln][r0 + 8 * lg]), st[t]);
         st[t] = mfma_bf16(wa, frag8(&sDl[16 * sct + ln][r0 + 8 * lg]), st[t]);
       }
