@@ -157,6 +157,10 @@ __device__ __forceinline__ bf16x8 frag8(const bf16* p) { return *(const bf16x8*)
 // or 136 bf16 long): the chunk index is XORed with bits 3..5 of the row, so
 // that 32 such lanes reach 8 of the 32 banks instead of 2, while a chunk stays
 // 16 contiguous bytes.  For columns below 64.
+// With two 4-column pieces per thread (a C x K bf16 operand, K = 128, 1024
+// threads), the thread's pieces u = 0, 1: rows 2 (tid / 32) + u, columns
+// 4 (tid % 32) .. + 3, so that its transposed writes pair two adjacent rows.
+__device__ __forceinline__ int pair_piece(int tid, int u) { return (2 * (tid >> 5) + u) * 32 + (tid & 31); }
 __device__ __forceinline__ int swz8(int row, int col) { return (((col >> 3) ^ ((row >> 3) & 7)) << 3) | (col & 7); }
 
 // Sum over the 64 lanes on the VALU (DPP): inclusive prefix sums inside each
@@ -728,11 +732,14 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_bf(BwdArgs b) {
       for (int e = 0; e < 4; ++e) x.pgl[t][e] = gL[16 * ((w * TPW + t) >> 2) + 4 * lg + e];
     const uint2* W4 = (const uint2*)((const bf16*)a.W + chb * C * K);
     const uint2* K4 = (const uint2*)((const bf16*)a.Kb + chb * C * K);
-    x.pw0 = W4[tid];
-    x.pk0 = K4[tid];
     if constexpr (NP == 2) {
-      x.pw1 = W4[tid + NT];
-      x.pk1 = K4[tid + NT];
+      x.pw0 = W4[pair_piece(tid, 0)];
+      x.pk0 = K4[pair_piece(tid, 0)];
+      x.pw1 = W4[pair_piece(tid, 1)];
+      x.pk1 = K4[pair_piece(tid, 1)];
+    } else {
+      x.pw0 = W4[tid];
+      x.pk0 = K4[tid];
     }
   };
   auto put = [&](int p, uint2 wv, uint2 kv) __attribute__((always_inline)) {
@@ -740,6 +747,15 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_bf(BwdArgs b) {
     *(uint2*)&sWn[r][c] = make_uint2(wv.x ^ 0x80008000u, wv.y ^ 0x80008000u);
 #pragma unroll
     for (int q = 0; q < 4; ++q) sKbT[c + q][swz8(c + q, r)] = elem4(kv, q);
+  };
+  // two pieces of rows r (even) and r + 1: the transposed elements as pairs
+  auto put2 = [&](uint2 wv0, uint2 kv0, uint2 wv1, uint2 kv1) __attribute__((always_inline)) {
+    const int p = pair_piece(tid, 0), r = p / (K / 4), c = 4 * (p % (K / 4));
+    *(uint2*)&sWn[r][c] = make_uint2(wv0.x ^ 0x80008000u, wv0.y ^ 0x80008000u);
+    *(uint2*)&sWn[r + 1][c] = make_uint2(wv1.x ^ 0x80008000u, wv1.y ^ 0x80008000u);
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      *(uint32_t*)&sKbT[c + q][swz8(c + q, r)] = (uint32_t)elem4(kv0, q) | ((uint32_t)elem4(kv1, q) << 16);
   };
   const int64_t sbase = ((int64_t)n * H + h) * K * V;
   f32x4 st[TPW];
@@ -776,8 +792,8 @@ __global__ __launch_bounds__(1024) void k_bwd_fstate_bf(BwdArgs b) {
       *(uint2*)&sSh[16 * sct + ln][16 * srt + 4 * lg] = hi;
       *(uint2*)&sSl[16 * sct + ln][16 * srt + 4 * lg] = lo;
     }
-    put(tid, cur.pw0, cur.pk0);
-    if constexpr (NP == 2) put(tid + NT, cur.pw1, cur.pk1);
+    if constexpr (NP == 2) put2(cur.pw0, cur.pk0, cur.pw1, cur.pk1);
+    else put(tid, cur.pw0, cur.pk0);
     __builtin_amdgcn_sched_barrier(0);
     // the chunk two after this one (near the sequence end a chunk reads itself
     // again, unused)
@@ -867,13 +883,17 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_bf(BwdArgs b) {
     const uint2* Q4 = (const uint2*)((const bf16*)a.Qt + chb * C * K);
     const uint2* W4 = (const uint2*)((const bf16*)a.W + chb * C * K);
     pa = A4[tid];
-    pk0 = K4[tid];
-    pq0 = Q4[tid];
-    pw0 = W4[tid];
     if constexpr (NP == 2) {
-      pk1 = K4[tid + NT];
-      pq1 = Q4[tid + NT];
-      pw1 = W4[tid + NT];
+      pk0 = K4[pair_piece(tid, 0)];
+      pq0 = Q4[pair_piece(tid, 0)];
+      pw0 = W4[pair_piece(tid, 0)];
+      pk1 = K4[pair_piece(tid, 1)];
+      pq1 = Q4[pair_piece(tid, 1)];
+      pw1 = W4[pair_piece(tid, 1)];
+    } else {
+      pk0 = K4[tid];
+      pq0 = Q4[tid];
+      pw0 = W4[tid];
     }
   };
   auto put = [&](int p, uint2 kv, uint2 qv, uint2 wv) __attribute__((always_inline)) {
@@ -883,6 +903,17 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_bf(BwdArgs b) {
     for (int q = 0; q < 4; ++q) {
       sQT[c + q][swz8(c + q, r)] = elem4(qv, q);
       sWT[c + q][swz8(c + q, r)] = elem4(wv, q) ^ 0x8000u;
+    }
+  };
+  // two pieces of rows r (even) and r + 1: the transposed elements as pairs
+  auto put2 = [&](uint2 kv0, uint2 qv0, uint2 wv0, uint2 kv1, uint2 qv1, uint2 wv1) __attribute__((always_inline)) {
+    const int p = pair_piece(tid, 0), r = p / (K / 4), c = 4 * (p % (K / 4));
+    *(uint2*)&sKb[r][c] = kv0;
+    *(uint2*)&sKb[r + 1][c] = kv1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      *(uint32_t*)&sQT[c + q][swz8(c + q, r)] = (uint32_t)elem4(qv0, q) | ((uint32_t)elem4(qv1, q) << 16);
+      *(uint32_t*)&sWT[c + q][swz8(c + q, r)] = ((uint32_t)elem4(wv0, q) | ((uint32_t)elem4(wv1, q) << 16)) ^ 0x80008000u;
     }
   };
   const int64_t sbase = ((int64_t)n * H + h) * K * V;
@@ -927,8 +958,8 @@ __global__ __launch_bounds__(1024) void k_bwd_dstate_bf(BwdArgs b) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) sAT[i + q][swz8(i + q, rr)] = elem4(pa, q);
     }
-    put(tid, pk0, pq0, pw0);
-    if constexpr (NP == 2) put(tid + NT, pk1, pq1, pw1);
+    if constexpr (NP == 2) put2(pk0, pq0, pw0, pk1, pq1, pw1);
+    else put(tid, pk0, pq0, pw0);
     float gl[TPW][4];
 #pragma unroll
     for (int t = 0; t < TPW; ++t)
