@@ -278,8 +278,11 @@ kda_status kda_chunk_table(const kda_problem* p, int32_t* tok, int32_t* len, int
  * as in the forward), or in fp32 when the environment sets
  * KDA_BWD_RECOMPUTE=valu (slower; fp32 parameter and state gradients then
  * about 1e-6 instead of 1e-3 relative).  Everything after the recomputation
- * is fp32.  Results are deterministic (fixed summation orders; the one atomic
- * counter only lists chunk-heads for a fix-up pass, each recomputed whole).
+ * accumulates in fp32; for bf16 inputs with 64-token chunks the fp32 states
+ * and Delta enter the matrix-core products as bf16 hi + lo pairs (about 16
+ * significant bits).  Results are deterministic (fixed summation orders; the
+ * one atomic counter only lists chunk-heads for a fix-up pass, each
+ * recomputed whole).
  */
 size_t kda_bwd_workspace_size(const kda_problem* p, kda_status* status);
 kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const void* v,
@@ -297,7 +300,9 @@ kda_status kda_bwd(const kda_problem* p, const void* q, const void* k, const voi
  * stage i is enqueued and stage_events[2*i+1] just after.  Stages, in order:
  *   0 chunk table, 1 recomputation of the forward's chunk factors,
  *   2 forward state pass (state entering each chunk), 3 reverse state pass,
- *   4 chunk-local gradients, 5 dq/dk (group sums and the L2 norm's Jacobian),
+ *   4 chunk-local gradients, 5 dq/dk (with grouped value heads: the sums over
+ *   a key head's value heads and the L2 norm's Jacobian; with one key head per
+ *   value head nothing runs here, stage 4 applies the Jacobian),
  *   6 da_log and ddt_bias sums.
  * A stage with nothing to launch records both events back to back.
  */
