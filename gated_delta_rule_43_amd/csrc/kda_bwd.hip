@@ -7,13 +7,13 @@
 // coverage page routes between slices (the backward of _RecvKDAInitialState).
 //
 // fp32 arithmetic after the recomputation.  For 64-token chunks the dense
-// per-chunk products (the two state passes, and the value-dimension, Y and
-// Tm^T dW products of the chunk kernel) run on matrix cores: for fp32 inputs
-// on fp32 ones (v_mfma_f32_16x16x4f32); for bf16 inputs the state passes and
-// the value-dimension products on bf16 ones (v_mfma_f32_16x16x32_bf16) with
-// every fp32 operand split into bf16 hi + lo (within about 2^-16 of the fp32
-// product), fp32 accumulation throughout; the pairwise, triangular and
-// per-element work, and chunks of 16 or 32, stay on VALU.  The
+// per-chunk products (the two state passes, the value-dimension, Y, Z and dN
+// products and the pairwise sums of the chunk kernel) run on matrix cores:
+// for fp32 inputs on fp32 ones (v_mfma_f32_16x16x4f32); for bf16 inputs the
+// state passes and the value-dimension products on bf16 ones
+// (v_mfma_f32_16x16x32_bf16) with every fp32 operand split into bf16 hi + lo
+// (within about 2^-16 of the fp32 product), fp32 accumulation throughout;
+// the per-element work, and chunks of 16 or 32, stay on VALU.  The
 // decay factors and the gate's derivative use the hardware exponential,
 // logarithm and reciprocal (about one ulp on the result).  The forward's chunk
 // factors are recomputed first, with Akk and Tm kept: for fp32 inputs by the
@@ -35,7 +35,9 @@
 //                          dV = Diag(beta) Tm^T dDelta; P = scale dO Delta^T (lower);
 //                          then q^, k^, gamma through Q~ S0, Kbar, K~ and the two
 //                          pairwise products Akk, Aqk (exp(gamma_r - gamma_i) per pair,
-//                          never a factor larger than one), gamma -> g by a reverse
+//                          split through 16-row block boundaries while no block
+//                          decays by more than kBlockSafe, exact per pair inside
+//                          a block otherwise), gamma -> g by a reverse
 //                          cumulative sum, and g through the gate;
 //   reductions             dq, dk: sum over the value heads that share a key head,
 //                          then the L2 norm's Jacobian; da_log, ddt_bias: sums over
