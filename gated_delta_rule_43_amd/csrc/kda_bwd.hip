@@ -55,8 +55,12 @@ constexpr int chunk_threads(int C, int K) { return C == 64 ? (K == 128 ? 1024 : 
 constexpr int kMaxD = 128;
 constexpr float kGateFloor = -110.f;
 // Largest decay of a 16-row block (in a channel) for which the chunk-gradient
-// kernel splits in-block pair factors through the block boundary.
-constexpr float kBlockSafe = 80.f;
+// kernel splits in-block pair factors through the block boundary.  The inner
+// factor (up to e^kBlockSafe) multiplies P or dAkk before the sum is scaled
+// back, and those are not bounded by one as the forward's k^ k^ products are:
+// e^70 (about 2.5e30) leaves such a sum about eight orders of magnitude below
+// the fp32 range for any realistic P.
+constexpr float kBlockSafe = 70.f;
 
 // Hardware exponential and logarithm (v_exp_f32 / v_log_f32 after a scaling,
 // about one ulp) and reciprocal: the gate's derivatives enter sums whose fp32

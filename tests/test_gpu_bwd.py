@@ -235,7 +235,7 @@ def _max_block_decay(inp, head):
 @pytest.mark.parametrize("K", [128, 64])
 def test_bwd_fp32_mixed_in_block_paths(K):
     """One call in which some chunk-heads keep the exact per-pair factors for
-    the pairs inside 16-row blocks (a block decays by more than 80 nats in a
+    the pairs inside 16-row blocks (a block decays by more than 60 nats in a
     channel: head 0) and the others take them on the matrix cores through the
     block boundary (head 1), at fp32 tolerance."""
     _banner("bwd fp32 mixed in-block paths K=%d" % K)
@@ -249,7 +249,7 @@ def test_bwd_fp32_mixed_in_block_paths(K):
     gate[:, :, 0] = g0
     inp["gate"] = gate.to(DEV)
     inp["a_log"] = torch.tensor([0.5, -1.0], device=DEV)
-    assert _max_block_decay(inp, 0) > 80.0 and _max_block_decay(inp, 1) < 80.0
+    assert _max_block_decay(inp, 0) > 60.0 and _max_block_decay(inp, 1) < 60.0
     d_o, d_fin = _upstream(inp, 19)
     _run(inp, d_o, d_fin, torch.float32, "fp32 mixed in-block paths")
 
