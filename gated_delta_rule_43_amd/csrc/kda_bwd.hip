@@ -1190,10 +1190,16 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     }
   }
   __syncthreads();
+  // each channel's column: all C rows read first (independent LDS reads),
+  // then summed down in registers and written back
   for (int c = tid; c < K; c += NT) {
+    float col[C];
+#pragma unroll
+    for (int r = 0; r < C; ++r) col[r] = sGam[r][c];
     float acc = 0.f;
+#pragma unroll
     for (int r = 0; r < C; ++r) {
-      acc += sGam[r][c];
+      acc += col[r];
       sGam[r][c] = acc;
     }
   }
