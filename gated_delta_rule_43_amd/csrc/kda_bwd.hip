@@ -2299,10 +2299,12 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   Tin* dbeta = (Tin*)b.dbeta;
   for (int r = tid; r < L; r += NT) store_as(dbeta + th(r), sDb[r] * sB[r] * (1.f - sB[r]));
   __syncthreads();
-  if (tid == 0) {
+  if (tid < 64) {
+    // wave 0 sums the K channel partials (a fixed order: deterministic)
     float acc = 0.f;
-    for (int c = 0; c < K; ++c) acc += sRed[c];
-    b.da_part[chb] = acc;
+    for (int c = tid; c < K; c += 64) acc += sRed[c];
+    acc = wave_sum_dpp(acc);
+    if (tid == 0) b.da_part[chb] = acc;
   }
 }
 
