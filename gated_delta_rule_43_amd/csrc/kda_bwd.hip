@@ -1100,9 +1100,13 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   const Tin* v = (const Tin*)a.v;
   const float scale = a.scale;
 
-  // LDS: gamma and Tm for the whole kernel; one region reused by phase
-  constexpr int kTiles = C * K + 2 * K * (VTL + 1) + 4 * C * TS;
-  constexpr int kAfter = C * K + 2 * C * (C + 1) + K * (C + 1);
+  // LDS: gamma and Tm for the whole kernel; one region reused by phase.
+  // dW's rows are padded to DWS floats: phase C's matrix-core loop reads it
+  // down columns (16 rows per k-step), which a 128-float stride puts in one
+  // bank; 4 extra floats spread them and keep rows 16-byte aligned
+  constexpr int DWS = K + 4;
+  constexpr int kTiles = C * DWS + 2 * K * (VTL + 1) + 4 * C * TS;
+  constexpr int kAfter = C * DWS + 2 * C * (C + 1) + K * (C + 1);
   constexpr int kRegion = kTiles > kAfter ? kTiles : kAfter;
   __shared__ float sGam[C][K];
   __shared__ float sT[C][C + 1];
@@ -1115,10 +1119,10 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
   // after phase B: dW | P | Y (then dAkk) | K~ transposed (then Z); after phase
   // D, q^ takes dW's place; after phase E, k^ takes Z's; after phase F, dgamma
   // and the Kbar term take those two places
-  float (*sDW)[K] = (float(*)[K])sReg;
-  float (*sP)[C + 1] = (float(*)[C + 1])(sReg + C * K);
-  float (*sY)[C + 1] = (float(*)[C + 1])(sReg + C * K + C * (C + 1));
-  float* sR4 = sReg + C * K + 2 * C * (C + 1);
+  float (*sDW)[DWS] = (float(*)[DWS])sReg;
+  float (*sP)[C + 1] = (float(*)[C + 1])(sReg + C * DWS);
+  float (*sY)[C + 1] = (float(*)[C + 1])(sReg + C * DWS + C * (C + 1));
+  float* sR4 = sReg + C * DWS + 2 * C * (C + 1);
   float (*sKtT)[C + 1] = (float(*)[C + 1])sR4;
   float (*sZ)[C + 1] = (float(*)[C + 1])sR4;
   float (*sQn)[K] = (float(*)[K])sReg;
@@ -1451,7 +1455,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     sdp += __shfl_xor(sdp, 4);
     if (sj == 0) sSd[sc] = sdp;
     __syncthreads();  // the tiles are dead: dW, then dQ~ and dKbar on their way to registers
-    float (*sX)[K] = (float(*)[K])(sReg + C * K);
+    float (*sX)[K] = (float(*)[K])(sReg + C * DWS);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -1556,7 +1560,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
       }
     }
     __syncthreads();  // the tiles are dead: dW, and dQ~ on its way to registers
-    float (*sX)[K] = (float(*)[K])(sReg + C * K);
+    float (*sX)[K] = (float(*)[K])(sReg + C * DWS);
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -1570,7 +1574,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     for (int m = 0; m < NE1; ++m) dqs[m] = sX[rb1 + RSTEP1 * m][c1];
     // sweep 2: M3 = Delta dS_L^T (-> dKbar), P = dO Delta^T and Yv = dDelta V^T
     // (lower tiles only), dV = Diag(beta) Tm^T dDelta per value tile
-    float* sReg2 = sReg + C * K;
+    float* sReg2 = sReg + C * DWS;
     float (*tdSL2)[VTL + 1] = (float(*)[VTL + 1])sReg2;
     float (*tD2)[TS] = (float(*)[TS])(sReg2 + K * (VTL + 1));
     float (*tdO2)[TS] = (float(*)[TS])(sReg2 + K * (VTL + 1) + C * TS);
@@ -1740,7 +1744,7 @@ __global__ __launch_bounds__(NT) void k_bwd_chunk(BwdArgs b) {
     }
   }
   // second sweep: its tiles live in the part of the region above dW
-  float* sReg2 = sReg + C * K;
+  float* sReg2 = sReg + C * DWS;
   float (*tdSL2)[VTL + 1] = (float(*)[VTL + 1])sReg2;
   float (*tD2)[TS] = (float(*)[TS])(sReg2 + K * (VTL + 1));
   float (*tdO2)[TS] = (float(*)[TS])(sReg2 + K * (VTL + 1) + C * TS);
