@@ -48,7 +48,7 @@ namespace kda {
 namespace {
 
 constexpr int kThreads = 256;
-// Workgroup size of the chunk-gradient kernel per (C, K): its LDS (up to 159 KB)
+// Workgroup size of the chunk-gradient kernel per (C, K): its LDS (up to 160 KiB)
 // allows one workgroup per CU, so the widest size that compiles without
 // register spills gives the most waves to hide LDS latency.
 constexpr int chunk_threads(int C, int K) { return C == 64 ? (K == 128 ? 1024 : 512) : C == 32 ? 256 : 512; }
